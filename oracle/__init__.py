@@ -1,0 +1,300 @@
+"""Oracle for the compressed-KV decode path -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow CPU reference of what the GPU library computes.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import it; the
+product package never does.  The arithmetic lives in ``kvc_oracle.c`` (built by
+``oracle/build.py`` into ``oracle/libkvc_oracle.so``); this module only marshals numpy
+arrays, and places per-token records into the paged cache layout and gathers them back.
+
+Every function follows a passage of the pages (cited by title and section in the C file):
+keys are stored as the sign bits of a random rotation with a binary16 norm and correction
+("RaBitQCache" abstract; "H1B-KV" key design), values as per-group 4-bit linear codes
+("H1B-KV" key design), scores come from binary x INT4 dot products ("RaBitQCache" key
+design), an adaptive Top-p selects tokens ("RaBitQCache" abstract), and the output is the
+softmax-weighted sum of the decoded 4-bit values ("H1B-KV" technical framework).
+
+Parity pins: every function here is checked against something other than itself in
+``tests/test_oracle_*.py`` (brute force, closed forms, library routines, statistics).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+ROT_DENSE = 0
+ROT_HADAMARD = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvc_oracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.orc_f16_from_f64.argtypes = [ctypes.c_double]
+    lib.orc_f16_from_f64.restype = ctypes.c_uint16
+    lib.orc_f64_from_f16.argtypes = [ctypes.c_uint16]
+    lib.orc_f64_from_f16.restype = ctypes.c_double
+    lib.orc_rotate_f64.argtypes = [i32, i32, P, P, P, i64, P]
+    lib.orc_key_encode.argtypes = [i32, i32, P, P, P, i64, P, P]
+    lib.orc_value_encode.argtypes = [i32, i32, P, i64, P, P]
+    lib.orc_query_encode.argtypes = [i32, i32, P, P, P, i64, P, P, P, P]
+    lib.orc_scores.argtypes = [i32, P, P, i64, P, f32, f32, P, P, P]
+    lib.orc_kbin.argtypes = [i32]
+    lib.orc_kbin.restype = f32
+    lib.orc_bin.argtypes = [f32, f32]
+    lib.orc_bin.restype = i32
+    lib.orc_weight_table.argtypes = [P]
+    lib.orc_topp.argtypes = [i32, P, i64, f32, P, P, P, P, P]
+    lib.orc_topp.restype = i64
+    lib.orc_attend.argtypes = [i32, i32, P, P, P, i64, P, i64, P]
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------------------
+# Rotation description
+# ----------------------------------------------------------------------------------------
+class Rotation:
+    """A key/query rotation: dense binary16 D x D matrix, or randomized Hadamard signs.
+
+    dense:    ``R16`` (np.float16, D x D, row-major); k' = R k.
+    hadamard: ``signs`` (np.uint32, D/32 words); bit j set means sigma_j = -1;
+              k' = H diag(sigma) k / sqrt(D) with H the Sylvester-order Hadamard matrix.
+    """
+
+    def __init__(self, kind, D, R16=None, signs=None):
+        self.kind = kind
+        self.D = D
+        if kind == ROT_DENSE:
+            self.Rf = _c(np.asarray(R16, dtype=np.float16).astype(np.float32), np.float32)
+            self.signs = np.zeros(max(1, D // 32), dtype=np.uint32)
+        else:
+            self.Rf = np.zeros(1, dtype=np.float32)
+            self.signs = _c(signs, np.uint32)
+
+
+# ----------------------------------------------------------------------------------------
+# binary16
+# ----------------------------------------------------------------------------------------
+def f16_bits(x: float) -> int:
+    return int(_load().orc_f16_from_f64(float(x)))
+
+
+def f16_value(bits: int) -> float:
+    return float(_load().orc_f64_from_f16(int(bits)))
+
+
+def f16_bits_array(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64).ravel()
+    return np.array([lib.orc_f16_from_f64(float(v)) for v in x], dtype=np.uint16)
+
+
+# ----------------------------------------------------------------------------------------
+# Per-vector steps
+# ----------------------------------------------------------------------------------------
+def rotate_f64(rot: Rotation, x) -> np.ndarray:
+    x = _c(np.asarray(x, dtype=np.float32).reshape(-1, rot.D), np.float32)
+    y = np.empty(x.shape, dtype=np.float64)
+    _load().orc_rotate_f64(rot.D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(x), x.shape[0], _p(y))
+    return y
+
+
+def key_encode(rot: Rotation, k):
+    """k: (n, D) float -> bits (n, D/32) uint32, nc (n, 2) uint16 (norm, corr)."""
+    D = rot.D
+    k = _c(np.asarray(k).astype(np.float32).reshape(-1, D), np.float32)
+    n = k.shape[0]
+    bits = np.empty((n, D // 32), dtype=np.uint32)
+    nc = np.empty((n, 2), dtype=np.uint16)
+    _load().orc_key_encode(D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(k), n, _p(bits), _p(nc))
+    return bits, nc
+
+
+def value_encode(v, D: int, Gv: int):
+    """v: (n, D) float -> codes (n, D/2) uint8, sz (n, D/Gv, 2) uint16 (scale, zero)."""
+    v = _c(np.asarray(v).astype(np.float32).reshape(-1, D), np.float32)
+    n = v.shape[0]
+    codes = np.empty((n, D // 2), dtype=np.uint8)
+    sz = np.empty((n, D // Gv, 2), dtype=np.uint16)
+    _load().orc_value_encode(D, Gv, _p(v), n, _p(codes), _p(sz))
+    return codes, sz
+
+
+def query_encode(rot: Rotation, q):
+    """q: (m, D) float32 -> dict(u (m, D) uint8, vl, delta, c0, c1 (m,) f32, sumu (m,), qrot)."""
+    D = rot.D
+    q = _c(np.asarray(q, dtype=np.float32).reshape(-1, D), np.float32)
+    m = q.shape[0]
+    u = np.empty((m, D), dtype=np.uint8)
+    par = np.empty((m, 4), dtype=np.float32)
+    sumu = np.empty(m, dtype=np.int32)
+    qrot = np.empty((m, D), dtype=np.float32)
+    _load().orc_query_encode(D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(q), m, _p(u), _p(par),
+                             _p(sumu), _p(qrot))
+    return dict(u=u, vl=par[:, 0].copy(), delta=par[:, 1].copy(), c0=par[:, 2].copy(),
+                c1=par[:, 3].copy(), sumu=sumu, qrot=qrot)
+
+
+def scores(bits, nc, u, c0, c1, D: int):
+    """One encoded query against L encoded keys -> (A, P, score) arrays of length L."""
+    bits = _c(bits, np.uint32).reshape(-1, D // 32)
+    nc = _c(nc, np.uint16).reshape(-1, 2)
+    u = _c(u, np.uint8).reshape(D)
+    L = bits.shape[0]
+    A = np.empty(L, dtype=np.int32)
+    P = np.empty(L, dtype=np.int32)
+    s = np.empty(L, dtype=np.float32)
+    _load().orc_scores(D, _p(bits), _p(nc), L, _p(u), float(c0), float(c1), _p(A), _p(P), _p(s))
+    return A, P, s
+
+
+def kbin(D: int) -> float:
+    return float(_load().orc_kbin(D))
+
+
+def score_bin(s: float, D: int) -> int:
+    lib = _load()
+    return int(lib.orc_bin(float(s), lib.orc_kbin(D)))
+
+
+def weight_table() -> np.ndarray:
+    T = np.empty(256, dtype=np.uint64)
+    _load().orc_weight_table(_p(T))
+    return T
+
+
+def topp(s, p: float, D: int):
+    """Top-p over one head's scores -> dict(idx ascending int32, emax, bstar, Z, Tp)."""
+    s = _c(s, np.float32).ravel()
+    L = s.shape[0]
+    idx = np.empty(max(L, 1), dtype=np.int32)
+    emax = ctypes.c_int32(0)
+    bstar = ctypes.c_int32(0)
+    Z = ctypes.c_uint64(0)
+    Tp = ctypes.c_uint64(0)
+    n = _load().orc_topp(D, _p(s), L, float(p), _p(idx), ctypes.byref(emax), ctypes.byref(bstar),
+                         ctypes.byref(Z), ctypes.byref(Tp))
+    return dict(idx=idx[:n].copy(), emax=emax.value, bstar=bstar.value, Z=Z.value, Tp=Tp.value)
+
+
+def attend(s, codes, sz, D: int, Gv: int, idx=None) -> np.ndarray:
+    """Softmax(s/sqrt(D)) over all tokens (idx None) or over idx, times the decoded values."""
+    s = _c(s, np.float32).ravel()
+    codes = _c(codes, np.uint8).reshape(-1, D // 2)
+    sz = _c(sz, np.uint16).reshape(-1, D // Gv, 2)
+    L = s.shape[0]
+    out = np.empty(D, dtype=np.float64)
+    if idx is None:
+        _load().orc_attend(D, Gv, _p(s), _p(codes), _p(sz), L, None, 0, _p(out))
+    else:
+        idx = _c(idx, np.int32)
+        _load().orc_attend(D, Gv, _p(s), _p(codes), _p(sz), L, _p(idx), idx.shape[0], _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Paged cache: per (physical page, KV head) structure-of-arrays
+# ----------------------------------------------------------------------------------------
+class PagedCache:
+    """The paged packed cache.  Token t of sequence b lives in physical page
+    page_table[b][t // P], slot t % P.  Per (page, KV head):
+      key_bits  uint32 [P][D/32]     sign bits of the rotated key
+      key_nc    uint32 [P]           binary16 norm (low half) | binary16 corr (high half)
+      val_codes uint8  [P][D/2]      4-bit value codes, even dim in the low nibble
+      val_sz    uint32 [P][D/Gv]     binary16 scale (low half) | binary16 zero (high half)
+    """
+
+    def __init__(self, num_pages, Hkv, P, D, Gv):
+        self.num_pages, self.Hkv, self.P, self.D, self.Gv = num_pages, Hkv, P, D, Gv
+        self.key_bits = np.zeros((num_pages, Hkv, P, D // 32), dtype=np.uint32)
+        self.key_nc = np.zeros((num_pages, Hkv, P), dtype=np.uint32)
+        self.val_codes = np.zeros((num_pages, Hkv, P, D // 2), dtype=np.uint8)
+        self.val_sz = np.zeros((num_pages, Hkv, P, D // Gv), dtype=np.uint32)
+
+    def locate(self, b, t, page_table):
+        t = np.asarray(t)
+        return np.asarray(page_table)[b, t // self.P], t % self.P
+
+    def gather(self, b, kvh, L, page_table):
+        """Records of tokens 0..L-1 of sequence b, KV head kvh."""
+        pg, sl = self.locate(b, np.arange(L), page_table)
+        bits = self.key_bits[pg, kvh, sl]
+        ncw = self.key_nc[pg, kvh, sl]
+        nc = np.stack([(ncw & 0xFFFF).astype(np.uint16), (ncw >> 16).astype(np.uint16)], axis=-1)
+        codes = self.val_codes[pg, kvh, sl]
+        szw = self.val_sz[pg, kvh, sl]
+        sz = np.stack([(szw & 0xFFFF).astype(np.uint16), (szw >> 16).astype(np.uint16)], axis=-1)
+        return bits, nc, codes, sz
+
+
+def append(cache: PagedCache, rot: Rotation, k, v, start_pos, page_table):
+    """Encode k, v (B, n_new, Hkv, D) and write token start_pos[b] + i of sequence b."""
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, n_new, Hkv, D = k.shape
+    for b in range(B):
+        t = int(start_pos[b]) + np.arange(n_new)
+        pg, sl = cache.locate(b, t, page_table)
+        for h in range(Hkv):
+            bits, nc = key_encode(rot, k[b, :, h, :])
+            codes, sz = value_encode(v[b, :, h, :], D, cache.Gv)
+            cache.key_bits[pg, h, sl] = bits
+            cache.key_nc[pg, h, sl] = nc[:, 0].astype(np.uint32) | (nc[:, 1].astype(np.uint32) << 16)
+            cache.val_codes[pg, h, sl] = codes
+            cache.val_sz[pg, h, sl] = sz[..., 0].astype(np.uint32) | (sz[..., 1].astype(np.uint32) << 16)
+
+
+def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p):
+    """One (sequence, query head) decode step.  Query head h reads KV head h*Hkv//Hq."""
+    D, Gv = cache.D, cache.Gv
+    kvh = h * cache.Hkv // Hq
+    qe = query_encode(rot, q_h)
+    res = dict(u=qe["u"][0], vl=qe["vl"][0], delta=qe["delta"][0], c0=qe["c0"][0],
+               c1=qe["c1"][0], sumu=int(qe["sumu"][0]), kvh=kvh)
+    if L <= 0:
+        res.update(out=np.zeros(D), A=np.zeros(0, np.int32), score=np.zeros(0, np.float32),
+                   idx=None)
+        return res
+    bits, nc, codes, sz = cache.gather(b, kvh, L, page_table)
+    A, P, s = scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], D)
+    res.update(A=A, P=P, score=s)
+    if top_p < 1.0:
+        tp = topp(s, top_p, D)
+        res.update(idx=tp["idx"], emax=tp["emax"], bstar=tp["bstar"], Z=tp["Z"], Tp=tp["Tp"])
+        res["out"] = attend(s, codes, sz, D, Gv, tp["idx"])
+    else:
+        res["idx"] = None
+        res["out"] = attend(s, codes, sz, D, Gv)
+    return res
+
+
+def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None):
+    """Decode step for q (B, Hq, D).  Returns {(b, h): decode_head(...)} for the requested
+    (b, h) pairs (all by default)."""
+    q = np.asarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hq)]
+    return {(b, h): decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p)
+            for (b, h) in heads}
