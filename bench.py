@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the compressed-KV attention library on one MI355X.
+
+A step is the whole decode hot path for one batch: append the newest token of every
+sequence (key sign bits + norm/correction, 4-bit values) into the paged cache, then one
+decode attention over every cached token (query rotation and int4 codes, binary x INT4
+proxy scores, adaptive Top-p when the workload uses it, softmax and 4-bit value sums, merge).
+
+Default workload: 32 query / 8 KV heads, head_dim 128, batch 4, 131072-token context, fp16
+K/V N(0,1) with 1% query-correlated "spike" tokens, dense random rotation, value group 32,
+256-token pages, adaptive Top-p 0.9.  The cache is filled before timing (inputs resident
+in HBM); L2 and the 256 MB Infinity Cache are flushed between steps outside the timed
+events.  Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode: KV tokens*heads attended/s and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+# algorithmic bytes per unit: key sign words 16 B + norm/corr 4 B per
+# token-KV-head; 4-bit value codes 64 B + scale/zero 4 B per group
+KEY_BYTES = 20
+
+
+def value_bytes(Gv):
+    return 64 + 4 * (128 // Gv)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload index 0..4 (default 2: GQA 128k Top-p)")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many steps after setup (for rocprofv3), no JSON")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_compress_amd as kvc
+    import workloads as W
+
+    wl = W.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    D, Hq, Hkv, B, P, Gv = wl.D, wl.Hq, wl.Hkv, wl.B, wl.P, wl.Gv
+    lens = W.draw_seq_lens(wl)
+    Lmax = int(lens.max())
+    log(f"[bench] workload {wl.name}: B={B} Hq={Hq} Hkv={Hkv} L<={Lmax} top_p={wl.top_p} rot={wl.rot}")
+
+    t0 = time.time()
+    K, V, q = W.draw_device(wl, dev, L=Lmax)
+    pt_np, npages = W.page_layout(wl, lens)
+    kind, rot = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, Hkv, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    pt = torch.from_numpy(pt_np).to(dev)
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    # prefill tokens 0 .. len-2 of every sequence
+    if np.all(lens == Lmax):
+        kvc.append(cache, K[:, :Lmax - 1].contiguous(), V[:, :Lmax - 1].contiguous(),
+                   torch.zeros(B, dtype=torch.int32, device=dev), pt)
+    else:
+        for b in range(B):
+            n = int(lens[b]) - 1
+            if n > 0:
+                kvc.append(cache, K[b:b + 1, :n].contiguous(), V[b:b + 1, :n].contiguous(),
+                           torch.zeros(1, dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+    idx_last = torch.from_numpy(lens.astype(np.int64) - 1).to(dev)
+    ar = torch.arange(B, device=dev)
+    k_new = K[ar, idx_last].unsqueeze(1).contiguous()  # [B, 1, Hkv, D]
+    v_new = V[ar, idx_last].unsqueeze(1).contiguous()
+    start = (seq - 1).contiguous()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvc.decode_workspace_bytes(B, Hq, Hkv, Lmax, wl.top_p), dtype=torch.uint8, device=dev)
+    flush = torch.zeros(256 * 1024 * 1024, dtype=torch.int32, device=dev)  # 1 GiB
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.1f}s, cache {cache.nbytes() / 2**20:.0f} MiB, "
+        f"workspace {ws.numel() / 2**20:.1f} MiB")
+
+    def step(dbg=None):
+        kvc.append(cache, k_new, v_new, start, pt)
+        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
+                          debug_struct=dbg)
+
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            if not args.no_flush:
+                flush.add_(1)
+            step()
+        torch.cuda.synchronize()
+        log("[bench] profile steps done")
+        return
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.add_(1)
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, per-step HIP events (flush outside the events)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.add_(1)
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = statistics.mean(step_ms)
+    tokens_heads = int(lens.astype(np.int64).sum()) * Hkv
+    value = tokens_heads / (ms / 1e3)
+    log(f"[bench] step {ms * 1e3:.1f} us (median {statistics.median(step_ms) * 1e3:.1f}, "
+        f"p10 {np.percentile(step_ms, 10) * 1e3:.1f}, p90 {np.percentile(step_ms, 90) * 1e3:.1f}); "
+        f"{value:.3e} KV token-heads/s")
+
+    # ---- second timed region with per-stage events recorded by the library
+    timers = [kvc.StageTimer() for _ in range(args.steps)]
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.add_(1)
+        aev[i][0].record()
+        kvc.append(cache, k_new, v_new, start, pt)
+        aev[i][1].record()
+        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
+                          debug_struct=timers[i].struct())
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for t in timers:
+        for k, v in t.elapsed_ms().items():
+            stage_ms.setdefault(k, []).append(v)
+    stage_ms = {k: statistics.mean(v) for k, v in stage_ms.items()}
+    stage_ms["append"] = statistics.mean(a.elapsed_time(b) for a, b in aev)
+    log("[bench] stages (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in stage_ms.items()))
+
+    # ---- selection statistics (one untimed debug decode)
+    sel_union = None
+    if wl.top_p < 1.0:
+        dbg = kvc.DecodeDebug.allocate(B, Hq, Lmax, True, dev)
+        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, debug=dbg)
+        torch.cuda.synchronize()
+        G = Hq // Hkv
+        mask = torch.zeros((B, Hkv, Lmax), dtype=torch.bool, device=dev)
+        cnt = dbg.sel_count
+        for h in range(Hq):
+            idx = dbg.sel_idx[:, h].clamp(min=0).long()
+            valid = torch.arange(Lmax, device=dev)[None, :] < cnt[:, h:h + 1]
+            m = torch.zeros((B, Lmax), dtype=torch.bool, device=dev)
+            m.scatter_(1, idx * valid, valid)
+            mask[:, h // G] |= m
+        sel_union = int(mask.sum())
+        sel_frac = float(cnt.sum()) / float(tokens_heads * G)
+        log(f"[bench] Top-p kept {sel_frac * 100:.2f}% of (token, query head) pairs; "
+            f"union over GQA groups {sel_union} token-KV-heads")
+        del dbg, mask
+
+    # ---- roofline of the dominant kernel
+    per_launch = {"score": KEY_BYTES * tokens_heads,
+                  "attend": (value_bytes(Gv) * sel_union) if sel_union is not None
+                  else (KEY_BYTES + value_bytes(Gv)) * tokens_heads,
+                  "append": (2 * D * 2 + 16 + 4 + value_bytes(Gv)) * B * Hkv}
+    kernel_names = {"score": "k_score", "attend": "k_attend", "append": "k_append",
+                    "hist": "k_hist", "threshold": "k_threshold", "query": "k_qprep", "merge": "k_merge"}
+    dominant = max((k for k in stage_ms if k in per_launch), key=lambda k: stage_ms[k])
+    ach = per_launch[dominant] / (stage_ms[dominant] / 1e3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kernel_names[dominant], wl.name),
+                "algorithmic_bytes_per_launch": per_launch[dominant],
+                "avg_launch_us": round(stage_ms[dominant] * 1e3, 2)}
+    step_alg = per_launch["append"] + per_launch["attend"] + (per_launch["score"] if wl.top_p < 1.0 else 0)
+    log(f"[bench] dominant {dominant}: {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i32 (1-bit x int4 popcount) + f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": Lmax,
+                   "head_dim": D, "top_p": wl.top_p, "value_group": Gv, "page_size": P, "rotation": wl.rot,
+                   "kv_dtype": wl.kv_dtype, "step": "append 1 token per sequence + decode attention",
+                   "cache_flushed_between_steps": not args.no_flush},
+        "roofline": roofline,
+        "step_hbm_frac_algorithmic": round(step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "query_head_tokens_per_s": value * (Hq // Hkv),
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "step_us_median": round(statistics.median(step_ms) * 1e3, 2),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
+    }
+    if sel_union is not None:
+        result["topp_selected_union_token_kv_heads"] = sel_union
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, wl, K, V, q, lens, pt_np, kind, rot,
+                                                                      out, value)
+    print(json.dumps(result), flush=True)
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this kernel and
+    workload, when the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, "bit_kv_cache_compress_amd", "csrc", rec["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(args, wl, K, V, q, lens, pt_np, kind, rot, gpu_out, gpu_value):
+    """The oracle, untuned, on a bounded sample of the same workload: the decode step of a
+    few whole (sequence, KV head) units -- its G query heads over every cached token --
+    run on the host cores, one unit per thread."""
+    import numpy as np
+
+    import oracle
+
+    G = wl.Hq // wl.Hkv
+    cores = len(os.sched_getaffinity(0))
+    units = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)][:max(1, min(wl.B * wl.Hkv, cores))]
+    orot = oracle.Rotation(oracle.ROT_DENSE if kind == "dense" else oracle.ROT_HADAMARD, wl.D,
+                           R16=rot if kind == "dense" else None, signs=rot if kind != "dense" else None)
+    log(f"[cpu] encoding {len(units)} units with the oracle on {cores} cores")
+    t0 = time.time()
+
+    def encode(u):
+        b, h = u
+        n = int(lens[b])
+        k = K[b, :n, h].float().cpu().numpy()
+        v = V[b, :n, h].float().cpu().numpy()
+        bits, nc = oracle.key_encode(orot, k)
+        codes, sz = oracle.value_encode(v, wl.D, wl.Gv)
+        return bits, nc, codes, sz
+
+    with ThreadPoolExecutor(cores) as ex:
+        enc = list(ex.map(encode, units))
+    log(f"[cpu] oracle caches built in {time.time() - t0:.1f}s")
+    qn = q.cpu().numpy()
+
+    def decode_unit(i):
+        b, h = units[i]
+        bits, nc, codes, sz = enc[i]
+        outs = []
+        for hh in range(h * G, (h + 1) * G):
+            qe = oracle.query_encode(orot, qn[b, hh][None, :])
+            _, _, s = oracle.scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], wl.D)
+            if wl.top_p < 1.0:
+                sel = oracle.topp(s, wl.top_p, wl.D)["idx"]
+                outs.append(oracle.attend(s, codes, sz, wl.D, wl.Gv, sel))
+            else:
+                outs.append(oracle.attend(s, codes, sz, wl.D, wl.Gv))
+        return outs
+
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        while True:
+            res = list(ex.map(decode_unit, range(len(units))))
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed * (reps + 1) / reps > args.cpu_seconds or reps >= 50:
+                break
+    work = reps * sum(int(lens[b]) for b, _ in units)
+    cpu_value = work / elapsed
+    # parity of the same sample against the GPU step's output
+    go = gpu_out.cpu().numpy()
+    worst = 0.0
+    for (b, h), outs in zip(units, res):
+        for j, hh in enumerate(range(h * G, (h + 1) * G)):
+            ref = outs[j]
+            worst = max(worst, float(np.abs(go[b, hh] - ref).max() / np.abs(ref).max()))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    log(f"[cpu] oracle {cpu_value:.3e} KV token-heads/s on {cores} threads ({model}); "
+        f"GPU/CPU {gpu_value / cpu_value:.0f}x; sample max rel err {worst:.2e}")
+    base = {"value": cpu_value, "unit": "KV token-heads/s", "cores": min(cores, len(units)), "kind": "oracle",
+            "sample": f"{len(units)} (sequence, KV head) units x {reps} repetition(s): query encode, proxy "
+                      f"scores, Top-p and attention of their {G} query heads over {int(lens[units[0][0]])} "
+                      f"tokens (cache encoded untimed)", "cpu_model": model, "seconds": round(elapsed, 2)}
+    return base, {"units": len(units), "max_rel_err_vs_oracle": worst, "tolerance": 2e-3}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+"""PyTorch-facing wrappers of the C ABI: shape and dtype checks, device pointers, the
+current HIP stream, and allocation of outputs/workspace with torch.  Every step of the
+computation runs in the library's HIP kernels."""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+HEAD_DIM = 128
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class KVCache:
+    """Paged packed cache (device memory owned by torch tensors).
+
+    Token t of sequence b lives in physical page ``page_table[b][t // page_size]``, slot
+    ``t % page_size``.  Arrays (per page, KV head, slot): ``key_bits`` 4 x uint32 sign words,
+    ``key_nc`` binary16 norm | binary16 correction << 16, ``val_codes`` 64 bytes of 4-bit
+    codes, ``val_sz`` binary16 scale | binary16 zero << 16 per value group.
+
+    ``rotation``: dense -> float16 [128, 128] orthogonal matrix; hadamard -> 4 uint32 sign
+    words (given as an int32 or uint32 array/tensor).
+    """
+
+    def __init__(self, num_pages: int, num_kv_heads: int, rotation, rot_kind: str = "dense",
+                 page_size: int = 256, value_group: int = 32, device="cuda"):
+        device = torch.device(device)
+        if device.type == "cuda" and device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = device
+        D = HEAD_DIM
+        self.num_pages, self.num_kv_heads = int(num_pages), int(num_kv_heads)
+        self.page_size, self.value_group = int(page_size), int(value_group)
+        self.rot_kind = L.KV_ROT_DENSE if rot_kind == "dense" else L.KV_ROT_HADAMARD
+        if self.rot_kind == L.KV_ROT_DENSE:
+            r = torch.as_tensor(rotation)
+            if r.dtype != torch.float16 or tuple(r.shape) != (D, D):
+                raise ValueError("dense rotation must be a float16 [128, 128] matrix")
+            self.rot = r.to(device).contiguous()
+        else:
+            r = torch.as_tensor(rotation.astype("int64") if hasattr(rotation, "astype") else rotation)
+            r = r.to(torch.int64)
+            if r.numel() != D // 32:
+                raise ValueError("hadamard rotation must hold 4 sign words")
+            r = torch.where(r >= 2**31, r - 2**32, r).to(torch.int32)
+            self.rot = r.to(device).contiguous()
+        shp = (self.num_pages, self.num_kv_heads, self.page_size)
+        self.key_bits = torch.zeros(shp + (D // 32,), dtype=torch.int32, device=device)
+        self.key_nc = torch.zeros(shp, dtype=torch.int32, device=device)
+        self.val_codes = torch.zeros(shp + (D // 2,), dtype=torch.uint8, device=device)
+        self.val_sz = torch.zeros(shp + (D // self.value_group,), dtype=torch.int32, device=device)
+        self.desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
+                                  self.rot_kind, self.rot.data_ptr(), self.key_bits.data_ptr(),
+                                  self.key_nc.data_ptr(), self.val_codes.data_ptr(), self.val_sz.data_ptr())
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.key_bits, self.key_nc, self.val_codes, self.val_sz))
+
+
+def append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, start_pos: torch.Tensor,
+           page_table: torch.Tensor) -> None:
+    """Encodes k, v [B, n_new, Hkv, 128] (float16 or float32) at positions start_pos[b] + i."""
+    dev = cache.device
+    if k.dim() != 4 or k.shape[2] != cache.num_kv_heads or k.shape[3] != HEAD_DIM:
+        raise ValueError(f"k must be [B, n_new, {cache.num_kv_heads}, {HEAD_DIM}], got {tuple(k.shape)}")
+    dtype = {torch.float16: L.KV_F16, torch.float32: L.KV_F32}.get(k.dtype)
+    if dtype is None:
+        raise TypeError("k, v must be float16 or float32")
+    _need(k, "k", k.dtype, dev)
+    _need(v, "v", k.dtype, dev, k.shape)
+    B, n_new = int(k.shape[0]), int(k.shape[1])
+    _need(start_pos, "start_pos", torch.int32, dev, (B,))
+    _need(page_table, "page_table", torch.int32, dev)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    L.check(L.lib().kv_compress_append(ctypes.byref(cache.desc), dtype, _ptr(k), _ptr(v), B, n_new, _ptr(start_pos),
+                                       _ptr(page_table), int(page_table.shape[1]), _stream(dev)))
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, max_seq_len: int, top_p: float = 1.0) -> int:
+    n = L.lib().kv_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, HEAD_DIM, float(top_p))
+    if n == 0:
+        raise ValueError(L.last_error() or "invalid decode shape")
+    return int(n)
+
+
+@dataclass
+class DecodeDebug:
+    """Intermediate outputs of one decode step (stage-wise checks)."""
+    q_codes: torch.Tensor
+    q_params: torch.Tensor
+    q_sumu: torch.Tensor
+    iscores: torch.Tensor
+    scores: torch.Tensor
+    sel_count: Optional[torch.Tensor] = None
+    sel_idx: Optional[torch.Tensor] = None
+    sel_bins: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def allocate(B, Hq, ld, topp: bool, device) -> "DecodeDebug":
+        z = lambda *s, dt=torch.int32: torch.zeros(s, dtype=dt, device=device)
+        return DecodeDebug(q_codes=z(B, Hq, HEAD_DIM, dt=torch.uint8), q_params=z(B, Hq, 4, dt=torch.float32),
+                           q_sumu=z(B, Hq), iscores=z(B, Hq, ld), scores=z(B, Hq, ld, dt=torch.float32),
+                           sel_count=z(B, Hq) if topp else None, sel_idx=z(B, Hq, ld) - 1 if topp else None,
+                           sel_bins=z(B, Hq, 2) if topp else None)
+
+    def struct(self) -> L.KVDebug:
+        return L.KVDebug(*[None if t is None else t.data_ptr() for t in
+                           (self.q_codes, self.q_params, self.q_sumu, self.iscores, self.scores, self.sel_count,
+                            self.sel_idx, self.sel_bins)], None)
+
+
+class StageTimer:
+    """HIP events that the library records around each decode stage (kv_debug.stage_events).
+    Pass ``timer.struct()`` as ``debug_struct`` to decode_attend; read ``timer.elapsed_ms()``
+    after synchronizing."""
+
+    def __init__(self):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        n = 2 * len(L.STAGES)
+        self.events = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+        self._dbg = L.KVDebug(None, None, None, None, None, None, None, None,
+                              ctypes.cast(self.events, ctypes.c_void_p))
+
+    def struct(self) -> L.KVDebug:
+        return self._dbg
+
+    def elapsed_ms(self) -> dict:
+        out = {}
+        for s, name in enumerate(L.STAGES):
+            a, b = self.events[2 * s], self.events[2 * s + 1]
+            ms = ctypes.c_float(0.0)
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0:
+                out[name] = float(ms.value)
+        return out
+
+
+def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
+                  top_p: float = 1.0, max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
+                  debug_struct: Optional[L.KVDebug] = None) -> torch.Tensor:
+    """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32."""
+    dev = cache.device
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
+    _need(q, "q", torch.float32, dev)
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    _need(seq_lens, "seq_lens", torch.int32, dev, (B,))
+    _need(page_table, "page_table", torch.int32, dev)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    max_pages = int(page_table.shape[1])
+    if max_seq_len is None:
+        max_seq_len = max_pages * cache.page_size
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, (B, Hq, HEAD_DIM))
+    need = decode_workspace_bytes(B, Hq, cache.num_kv_heads, max_seq_len, top_p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if debug is not None:
+        debug_struct = debug.struct()
+    dbg = ctypes.byref(debug_struct) if debug_struct is not None else None
+    L.check(L.lib().kv_decode_attend(ctypes.byref(cache.desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
+                                     _ptr(page_table), max_pages, float(top_p), _ptr(out), dbg, _ptr(workspace),
+                                     workspace.numel(), _stream(dev)))
+    return out
+
+
+def topp_workspace_bytes(B: int, Hq: int, ld: int) -> int:
+    n = L.lib().kv_topp_workspace_bytes(B, Hq, ld)
+    if n == 0:
+        raise ValueError("invalid top-p shape")
+    return int(n)
+
+
+def topp_select(scores: torch.Tensor, seq_lens: torch.Tensor, top_p: float, head_dim: int = HEAD_DIM,
+                workspace: Optional[torch.Tensor] = None):
+    """Adaptive Top-p over scores [B, Hq, ld] -> (sel_idx [B, Hq, ld] ascending, padded
+    with -1; sel_count [B, Hq])."""
+    dev = scores.device
+    _need(scores, "scores", torch.float32, dev)
+    if scores.dim() != 3:
+        raise ValueError("scores must be [B, Hq, ld]")
+    B, Hq, ld = (int(x) for x in scores.shape)
+    _need(seq_lens, "seq_lens", torch.int32, dev, (B,))
+    sel_idx = torch.full((B, Hq, ld), -1, dtype=torch.int32, device=dev)
+    sel_count = torch.zeros((B, Hq), dtype=torch.int32, device=dev)
+    need = topp_workspace_bytes(B, Hq, ld)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    L.check(L.lib().kv_topp_select(_ptr(scores), ld, _ptr(seq_lens), B, Hq, head_dim, float(top_p), _ptr(sel_idx),
+                                   _ptr(sel_count), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return sel_idx, sel_count

@@ -1,0 +1,448 @@
+// C ABI of libkvcompress: argument validation (host only, before any HIP call), the decode
+// plan (chunk size, workspace layout) and the launch sequences.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kv_compress.h"
+#include "kvc_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(long x)
+{
+    int r = 0;
+    while ((1L << r) < x) ++r;
+    return r;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------------------
+// Decode plan
+// ---------------------------------------------------------------------------------------
+struct Plan {
+    kvc::DecodeGeom g;
+    bool topp;
+    int nsplit, cps;
+    size_t off_qpl, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po;
+    size_t total;
+};
+
+// Chunk size: the largest power of two CH in [256, cap] that still gives at least 2048
+// blocks (8 per compute unit) over (chunk, KV-head group, sequence); cap keeps the per-block
+// LDS score buffer (CH x GB floats) and Top-p entry list within 48 KB.
+void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
+{
+    int cap = 8192 / GB;
+    if (topp && cap > 4096) cap = 4096;
+    int CH = cap;
+    const long units = (long)B * rows_per_seq;
+    while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048) CH >>= 1;
+    pl.g.CH = CH;
+    pl.g.logCH = ilog2(CH);
+    pl.g.NC = (max_len + CH - 1) / CH;
+    if (pl.g.NC < 1) pl.g.NC = 1;
+    pl.g.Lpad = pl.g.NC * CH;
+    pl.g.ld = max_len;
+}
+
+void plan_layout(Plan &pl, int BH)
+{
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    const size_t NC = (size_t)pl.g.NC;
+    pl.off_qpl = take((size_t)BH * 16 * 4);
+    pl.off_qpar = take((size_t)BH * 16);
+    pl.off_pm = take((size_t)BH * NC * 4);
+    pl.off_pl = take((size_t)BH * NC * 4);
+    pl.off_po = take((size_t)BH * NC * 128 * 4);
+    if (pl.topp) {
+        // histogram splits: >= 256 blocks over (split, head, sequence), <= 1024 chunks each
+        int nsplit = (256 + BH - 1) / BH;
+        if (nsplit > pl.g.NC) nsplit = pl.g.NC;
+        if (nsplit < 1) nsplit = 1;
+        int cps = (pl.g.NC + nsplit - 1) / nsplit;
+        while (cps > 1024) {
+            ++nsplit;
+            cps = (pl.g.NC + nsplit - 1) / nsplit;
+        }
+        pl.nsplit = nsplit;
+        pl.cps = cps;
+        pl.off_lmax = take((size_t)BH * NC * 4);
+        pl.off_dl = take((size_t)BH * pl.g.Lpad * 2);
+        pl.off_hist = take((size_t)BH * nsplit * 8192 * 4);
+        pl.off_sel = take((size_t)BH * 4 * 4);
+        pl.off_cnt = take((size_t)BH * NC * 4);
+    } else {
+        pl.nsplit = pl.cps = 0;
+        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = 0;
+    }
+    pl.total = o;
+}
+
+int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, float top_p)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seq_len <= 0)
+        return fail(KV_ERR_ARG, "B, Hq, Hkv and max_seq_len must be positive (got %d, %d, %d, %d)", B, Hq,
+                    Hkv, max_seq_len);
+    if (head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", head_dim);
+    if (Hq % Hkv != 0) return fail(KV_ERR_ARG, "Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+    const int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(KV_ERR_UNSUPPORTED, "GQA group Hq/Hkv = %d: supported groups are 1, 2, 4, 8", G);
+    if (!(top_p > 0.0f)) return fail(KV_ERR_ARG, "top_p must be > 0 (got %g)", (double)top_p);
+    if (max_seq_len > (1 << 30)) return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above 2^30", max_seq_len);
+    return KV_OK;
+}
+
+void make_plan(Plan &pl, int B, int Hq, int Hkv, int max_seq_len, float top_p)
+{
+    memset(&pl, 0, sizeof(pl));
+    pl.topp = top_p < 1.0f;
+    const int G = Hq / Hkv;
+    const int GB = G < 4 ? G : 4;
+    pl.g.B = B;
+    pl.g.Hq = Hq;
+    pl.g.Hkv = Hkv;
+    pl.g.G = G;
+    pl.g.GB = GB;
+    pl.g.nsub = G / GB;
+    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, GB, pl.topp);
+    plan_layout(pl, B * Hq);
+}
+
+int check_cache(const kv_cache *c)
+{
+    if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
+    if (c->head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", c->head_dim);
+    if (c->num_kv_heads <= 0) return fail(KV_ERR_ARG, "num_kv_heads must be positive");
+    if (c->value_group != 32 && c->value_group != 64)
+        return fail(KV_ERR_UNSUPPORTED, "value_group %d: supported groups are 32 and 64", c->value_group);
+    if (!is_pow2(c->page_size) || c->page_size < 16)
+        return fail(KV_ERR_UNSUPPORTED, "page_size %d: must be a power of two >= 16", c->page_size);
+    if (c->num_pages <= 0) return fail(KV_ERR_ARG, "num_pages must be positive");
+    if (c->rot_kind != KV_ROT_DENSE && c->rot_kind != KV_ROT_HADAMARD)
+        return fail(KV_ERR_ARG, "rot_kind %d is not KV_ROT_DENSE or KV_ROT_HADAMARD", c->rot_kind);
+    if (!c->rot || !c->key_bits || !c->key_nc || !c->val_codes || !c->val_sz)
+        return fail(KV_ERR_ARG, "cache descriptor has a NULL array");
+    return KV_OK;
+}
+
+kvc::CacheView view_of(const kv_cache *c)
+{
+    kvc::CacheView v;
+    v.Hkv = c->num_kv_heads;
+    v.P = c->page_size;
+    v.logP = ilog2(c->page_size);
+    v.Gv = c->value_group;
+    v.key_bits = c->key_bits;
+    v.key_nc = c->key_nc;
+    v.val_codes = c->val_codes;
+    v.val_sz = c->val_sz;
+    return v;
+}
+
+// Records the stage's start (begin = true) or end event when the caller asked for them.
+void stage_mark(const kv_debug *dbg, int stage, bool begin, hipStream_t s)
+{
+    if (dbg && dbg->stage_events) (void)hipEventRecord(dbg->stage_events[2 * stage + (begin ? 0 : 1)], s);
+}
+
+template <typename T>
+T *at(void *ws, size_t off)
+{
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kv_last_error(void) { return g_err; }
+
+int kv_version(void) { return 10000; }
+
+int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const void *v, int32_t B,
+                       int32_t n_new, const int32_t *start_pos, const int32_t *page_table,
+                       int32_t max_pages, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_cache(c);
+    if (rc) return rc;
+    if (dtype != KV_F16 && dtype != KV_F32) return fail(KV_ERR_ARG, "dtype %d is not KV_F16 or KV_F32", dtype);
+    if (B <= 0 || n_new < 0 || max_pages <= 0)
+        return fail(KV_ERR_ARG, "B and max_pages must be positive and n_new >= 0 (got %d, %d, %d)", B, n_new,
+                    max_pages);
+    if (n_new == 0) return KV_OK;
+    if (!k || !v || !start_pos || !page_table) return fail(KV_ERR_ARG, "NULL k, v, start_pos or page_table");
+    kvc::AppendParams p;
+    p.c = view_of(c);
+    p.rot_kind = c->rot_kind;
+    p.rot = c->rot;
+    p.dtype = dtype;
+    p.k = k;
+    p.v = v;
+    p.B = B;
+    p.n_new = n_new;
+    p.start_pos = start_pos;
+    p.page_table = page_table;
+    p.max_pages = max_pages;
+    hipError_t e = kvc::launch_append(p, stream);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    return KV_OK;
+}
+
+size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t head_dim,
+                                 float top_p)
+{
+    if (check_decode_shapes(B, Hq, Hkv, max_seq_len, head_dim, top_p) != KV_OK) return 0;
+    Plan pl;
+    make_plan(pl, B, Hq, Hkv, max_seq_len, top_p);
+    return pl.total;
+}
+
+int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, const int32_t *seq_lens,
+                     int32_t max_seq_len, const int32_t *page_table, int32_t max_pages, float top_p,
+                     float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_cache(c);
+    if (rc) return rc;
+    rc = check_decode_shapes(B, Hq, c->num_kv_heads, max_seq_len, c->head_dim, top_p);
+    if (rc) return rc;
+    if (!q || !seq_lens || !page_table || !out) return fail(KV_ERR_ARG, "NULL q, seq_lens, page_table or out");
+    if (max_pages <= 0) return fail(KV_ERR_ARG, "max_pages must be positive");
+    if ((long)max_pages * c->page_size < (long)max_seq_len)
+        return fail(KV_ERR_ARG, "max_pages * page_size (%ld) < max_seq_len (%d)", (long)max_pages * c->page_size,
+                    max_seq_len);
+    Plan pl;
+    make_plan(pl, B, Hq, c->num_kv_heads, max_seq_len, top_p);
+    if (!workspace || workspace_bytes < pl.total)
+        return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes required", workspace_bytes,
+                    pl.total);
+    pl.g.seq_lens = seq_lens;
+    pl.g.page_table = page_table;
+    pl.g.max_pages = max_pages;
+    const kvc::CacheView cv = view_of(c);
+    const float isd = (float)(1.0 / sqrt((double)c->head_dim));
+    const float kbin = (float)(256.0 * 1.4426950408889634074 / sqrt((double)c->head_dim));
+    const float klog = (float)(1.4426950408889634074 / sqrt((double)c->head_dim));
+    (void)isd;
+    const int BH = B * Hq;
+    uint32_t *qpl = at<uint32_t>(workspace, pl.off_qpl);
+    float4 *qpar = at<float4>(workspace, pl.off_qpar);
+
+    kvc::QprepParams qp;
+    qp.rot_kind = c->rot_kind;
+    qp.rot = c->rot;
+    qp.q = q;
+    qp.BH = BH;
+    qp.qpl = qpl;
+    qp.qpar = qpar;
+    qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
+    qp.dbg_params = dbg ? dbg->q_params : nullptr;
+    qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
+    stage_mark(dbg, KV_STAGE_QUERY, true, stream);
+    hipError_t e = kvc::launch_qprep(qp, stream);
+    if (e != hipSuccess) return hip_fail(e, "query launch");
+    stage_mark(dbg, KV_STAGE_QUERY, false, stream);
+
+    kvc::ScoreParams sp;
+    sp.g = pl.g;
+    sp.c = cv;
+    sp.qpl = qpl;
+    sp.qpar = qpar;
+    sp.kbin = kbin;
+    sp.dl = pl.topp ? at<uint16_t>(workspace, pl.off_dl) : nullptr;
+    sp.lmax = pl.topp ? at<int32_t>(workspace, pl.off_lmax) : nullptr;
+    sp.dbg_scores = dbg ? dbg->scores : nullptr;
+    sp.dbg_iscores = dbg ? dbg->iscores : nullptr;
+    if (pl.topp || sp.dbg_scores || sp.dbg_iscores) {
+        stage_mark(dbg, KV_STAGE_SCORE, true, stream);
+        e = kvc::launch_score(sp, stream);
+        if (e != hipSuccess) return hip_fail(e, "score launch");
+        stage_mark(dbg, KV_STAGE_SCORE, false, stream);
+    }
+
+    if (pl.topp) {
+        kvc::HistParams hp;
+        hp.g = pl.g;
+        hp.nsplit = pl.nsplit;
+        hp.cps = pl.cps;
+        hp.dl = sp.dl;
+        hp.lmax = sp.lmax;
+        hp.hist = at<uint32_t>(workspace, pl.off_hist);
+        stage_mark(dbg, KV_STAGE_HIST, true, stream);
+        e = kvc::launch_hist(hp, stream);
+        if (e != hipSuccess) return hip_fail(e, "histogram launch");
+        stage_mark(dbg, KV_STAGE_HIST, false, stream);
+        kvc::ThresholdParams tp;
+        tp.g = pl.g;
+        tp.nsplit = pl.nsplit;
+        tp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
+        tp.lmax = sp.lmax;
+        tp.hist = hp.hist;
+        tp.sel = at<int32_t>(workspace, pl.off_sel);
+        tp.dbg_count = dbg ? dbg->sel_count : nullptr;
+        tp.dbg_bins = dbg ? dbg->sel_bins : nullptr;
+        stage_mark(dbg, KV_STAGE_THRESHOLD, true, stream);
+        e = kvc::launch_threshold(tp, stream);
+        if (e != hipSuccess) return hip_fail(e, "threshold launch");
+        stage_mark(dbg, KV_STAGE_THRESHOLD, false, stream);
+        if (dbg && dbg->sel_idx) {
+            kvc::SelectParams sel;
+            sel.g = pl.g;
+            sel.dl = sp.dl;
+            sel.lmax = sp.lmax;
+            sel.sel = tp.sel;
+            sel.cnt = at<int32_t>(workspace, pl.off_cnt);
+            sel.idx = dbg->sel_idx;
+            stage_mark(dbg, KV_STAGE_SELECT, true, stream);
+            e = kvc::launch_select(sel, stream);
+            if (e != hipSuccess) return hip_fail(e, "selection launch");
+            stage_mark(dbg, KV_STAGE_SELECT, false, stream);
+        }
+    }
+
+    kvc::AttendParams ap;
+    ap.g = pl.g;
+    ap.c = cv;
+    ap.qpl = qpl;
+    ap.qpar = qpar;
+    ap.klog = klog;
+    ap.dl = sp.dl;
+    ap.lmax = sp.lmax;
+    ap.sel = pl.topp ? at<int32_t>(workspace, pl.off_sel) : nullptr;
+    ap.pm = at<float>(workspace, pl.off_pm);
+    ap.pl = at<float>(workspace, pl.off_pl);
+    ap.po = at<float>(workspace, pl.off_po);
+    stage_mark(dbg, KV_STAGE_ATTEND, true, stream);
+    e = kvc::launch_attend(ap, pl.topp, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    stage_mark(dbg, KV_STAGE_ATTEND, false, stream);
+
+    kvc::MergeParams mp;
+    mp.g = pl.g;
+    mp.klog = klog;
+    mp.pm = ap.pm;
+    mp.pl = ap.pl;
+    mp.po = ap.po;
+    mp.out = out;
+    stage_mark(dbg, KV_STAGE_MERGE, true, stream);
+    e = kvc::launch_merge(mp, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    stage_mark(dbg, KV_STAGE_MERGE, false, stream);
+    return KV_OK;
+}
+
+size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld)
+{
+    if (B <= 0 || Hq <= 0 || ld <= 0 || ld > (1 << 30)) return 0;
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.topp = true;
+    pl.g.B = B;
+    pl.g.Hq = Hq;
+    pl.g.Hkv = Hq;
+    pl.g.G = pl.g.GB = pl.g.nsub = 1;
+    plan_geometry(pl, B, Hq, ld, 1, true);
+    plan_layout(pl, B * Hq);
+    return pl.total;
+}
+
+int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int32_t B, int32_t Hq,
+                   int32_t head_dim, float top_p, int32_t *sel_idx, int32_t *sel_count, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (B <= 0 || Hq <= 0 || ld <= 0)
+        return fail(KV_ERR_ARG, "B, Hq and ld must be positive (got %d, %d, %d)", B, Hq, ld);
+    if (ld > (1 << 30)) return fail(KV_ERR_UNSUPPORTED, "ld %d above 2^30", ld);
+    if (head_dim <= 0) return fail(KV_ERR_ARG, "head_dim must be positive");
+    if (!(top_p > 0.0f && top_p < 1.0f)) return fail(KV_ERR_ARG, "top_p must be in (0, 1) (got %g)", (double)top_p);
+    if (!scores || !seq_lens || !sel_idx || !sel_count)
+        return fail(KV_ERR_ARG, "NULL scores, seq_lens, sel_idx or sel_count");
+    const size_t need = kv_topp_workspace_bytes(B, Hq, ld);
+    if (!workspace || workspace_bytes < need)
+        return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes required", workspace_bytes,
+                    need);
+    Plan pl;
+    memset(&pl, 0, sizeof(pl));
+    pl.topp = true;
+    pl.g.B = B;
+    pl.g.Hq = Hq;
+    pl.g.Hkv = Hq;
+    pl.g.G = pl.g.GB = pl.g.nsub = 1;
+    plan_geometry(pl, B, Hq, ld, 1, true);
+    plan_layout(pl, B * Hq);
+    pl.g.seq_lens = seq_lens;
+    pl.g.page_table = nullptr;
+    pl.g.max_pages = 0;
+    const float kbin = (float)(256.0 * 1.4426950408889634074 / sqrt((double)head_dim));
+
+    kvc::BinScoresParams bp;
+    bp.g = pl.g;
+    bp.scores = scores;
+    bp.kbin = kbin;
+    bp.dl = at<uint16_t>(workspace, pl.off_dl);
+    bp.lmax = at<int32_t>(workspace, pl.off_lmax);
+    hipError_t e = kvc::launch_bin_scores(bp, stream);
+    if (e != hipSuccess) return hip_fail(e, "bin launch");
+    kvc::HistParams hp;
+    hp.g = pl.g;
+    hp.nsplit = pl.nsplit;
+    hp.cps = pl.cps;
+    hp.dl = bp.dl;
+    hp.lmax = bp.lmax;
+    hp.hist = at<uint32_t>(workspace, pl.off_hist);
+    e = kvc::launch_hist(hp, stream);
+    if (e != hipSuccess) return hip_fail(e, "histogram launch");
+    kvc::ThresholdParams tp;
+    tp.g = pl.g;
+    tp.nsplit = pl.nsplit;
+    tp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
+    tp.lmax = bp.lmax;
+    tp.hist = hp.hist;
+    tp.sel = at<int32_t>(workspace, pl.off_sel);
+    tp.dbg_count = sel_count;
+    tp.dbg_bins = nullptr;
+    e = kvc::launch_threshold(tp, stream);
+    if (e != hipSuccess) return hip_fail(e, "threshold launch");
+    kvc::SelectParams sel;
+    sel.g = pl.g;
+    sel.dl = bp.dl;
+    sel.lmax = bp.lmax;
+    sel.sel = tp.sel;
+    sel.cnt = at<int32_t>(workspace, pl.off_cnt);
+    sel.idx = sel_idx;
+    e = kvc::launch_select(sel, stream);
+    if (e != hipSuccess) return hip_fail(e, "selection launch");
+    return KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// Append kernels: encode new keys (sign bits of a random rotation + binary16 norm and
+// correction) and values (per-group 4-bit linear codes) into the paged cache.
+//
+// Method: "H1B-KV" (key design: 1-bit key sketch by random projection, 4-bit linear value
+// quantization) with the randomized rotation of "RaBitQCache" (abstract).  The sign of each
+// rotated coordinate is decided on the exact product: for binary16 (and, in practice,
+// binary32) inputs every partial sum of R k is exact in binary64, so the kernels rotate in
+// binary64 -- a butterfly for the randomized Hadamard rotation and binary64 MFMA for the
+// dense one -- and their sign bits do not depend on the summation order.
+#include "kvc_device.h"
+#include "kvc_launch.h"
+
+namespace kvc {
+
+namespace {
+
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+// Eight consecutive input elements of a row, widened to float.
+__device__ __forceinline__ void load8(const void *base, int dtype, size_t elem, float x[8])
+{
+    if (dtype == 0) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + elem);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = half_bits_to_float(w[e] & 0xFFFFu);
+            x[2 * e + 1] = half_bits_to_float(w[e] >> 16);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
+        const float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+
+// Physical slot of token-head n = (b * n_new + t) * Hkv + h.
+__device__ __forceinline__ size_t slot_of(const AppendParams &p, long n)
+{
+    const int h = (int)(n % p.c.Hkv);
+    const long bt = n / p.c.Hkv;
+    const int t = (int)(bt % p.n_new);
+    const int b = (int)(bt / p.n_new);
+    const int pos = p.start_pos[b] + t;
+    const int page = p.page_table[(size_t)b * p.max_pages + (pos >> p.c.logP)];
+    return ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
+}
+
+// Value encode of one token-head by 16 lanes (lane i holds dims 8i..8i+7):
+//   scale = fp16((max - min) / 15), zero = fp16(min) per group of Gv dims (binary32 ops),
+//   code  = clamp(rint((x - zero) / scale), 0, 15), 0 when scale == 0;
+//   byte m of the 64-byte row holds dim 2m in its low nibble, dim 2m+1 in its high nibble.
+__device__ __forceinline__ void encode_values(const float x[8], int i, int Gv, uint8_t *codes,
+                                              uint32_t *sz)
+{
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+    }
+    const int gl = Gv / 8;  // lanes per group
+    for (int o = 1; o < gl; o <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    const float range = mx - mn;
+    const float step = range / 15.0f;
+    const uint32_t s16 = float_to_half_bits(step);
+    const uint32_t z16 = float_to_half_bits(mn);
+    const float sf = half_bits_to_float(s16);
+    const float zf = half_bits_to_float(z16);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        int c = 0;
+        if (sf != 0.0f) {
+            float t = rintf((x[e] - zf) / sf);
+            t = fminf(fmaxf(t, 0.0f), 15.0f);
+            c = (int)t;
+        }
+        word |= (uint32_t)c << (4 * e);
+    }
+    reinterpret_cast<uint32_t *>(codes)[i] = word;
+    if ((i & (gl - 1)) == 0) sz[(8 * i) / Gv] = s16 | (z16 << 16);
+}
+
+// Sum over the 16 lanes of a token-head group.
+__device__ __forceinline__ double sum16(double v)
+{
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// key_nc word: binary16 |k| (low) and binary16 sum|k'| / (sqrt(D) |k|) (high; 1 if k = 0).
+__device__ __forceinline__ uint32_t norm_corr_word(double ss, double sabs_rot)
+{
+    const double nrm = sqrt(ss);
+    const double corr = (nrm == 0.0) ? 1.0 : sabs_rot / (sqrt((double)kD) * nrm);
+    return double_to_half_bits(nrm) | (double_to_half_bits(corr) << 16);
+}
+
+// ---------------------------------------------------------------------------------------
+// Randomized Hadamard rotation: k' = H diag(sigma) k / sqrt(D), in binary64 butterflies.
+// 16 lanes per token-head, 16 token-heads per 256-thread block.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_append_hadamard(AppendParams p, long N)
+{
+    const int i = threadIdx.x & 15;
+    const long n = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (n >= N) return;  // whole 16-lane groups exit together
+    const size_t row = (size_t)n * kD + 8 * i;
+    float xk[8], xv[8];
+    load8(p.k, p.dtype, row, xk);
+    load8(p.v, p.dtype, row, xv);
+    const size_t slot = slot_of(p, n);
+
+    // sigma, then the 7 butterfly levels (h = 1, 2, 4 inside the lane, 8..64 across lanes)
+    const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[i >> 2];
+    double y[8];
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double xe = (double)xk[e];
+        ss += xe * xe;
+        const int d = 8 * i + e;
+        y[e] = ((sgw >> (d & 31)) & 1u) ? -xe : xe;
+    }
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & h) == 0) {
+                const double a = y[e], b = y[e + h];
+                y[e] = a + b;
+                y[e + h] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double o = __shfl_xor(y[e], m);
+            y[e] = (i & m) ? (o - y[e]) : (y[e] + o);
+        }
+    // sign bits: byte i of the 16-byte key word vector
+    uint32_t byte = 0;
+    double sabs = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        byte |= (y[e] < 0.0 ? 0u : 1u) << e;
+        sabs += fabs(y[e]);
+    }
+    uint32_t word = byte << (8 * (i & 3));
+    word |= __shfl_xor(word, 1);
+    word |= __shfl_xor(word, 2);
+    if ((i & 3) == 0) p.c.key_bits[slot * kKeyWords + (i >> 2)] = word;
+    ss = sum16(ss);
+    sabs = sum16(sabs) / sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
+    if (i == 0) p.c.key_nc[slot] = norm_corr_word(ss, sabs);
+    encode_values(xv, i, p.c.Gv, p.c.val_codes + slot * (kD / 2),
+                  p.c.val_sz + slot * (kD / p.c.Gv));
+}
+
+// ---------------------------------------------------------------------------------------
+// Dense rotation k' = R k with binary64 MFMA (v_mfma_f64_16x16x4f64): each wave rotates 16
+// token-heads (A = 16 keys x 4 dims, B = 4 dims x 16 rows of R^T, 32 steps x 8 row blocks).
+// 128-thread blocks, 32 token-heads per tile, R staged once per block in LDS (binary16,
+// rows padded to 130 halves so the 16 rows read by one MFMA fall in distinct banks).
+// ---------------------------------------------------------------------------------------
+constexpr int kRStride = 130;
+
+__global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
+{
+    __shared__ uint16_t Rs[kD * kRStride];
+    __shared__ float Ks[32 * kD];       // key tile widened to float (exact for f16 and f32)
+    __shared__ double sabs_s[32];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const uint16_t *R = reinterpret_cast<const uint16_t *>(p.rot);
+    for (int c = tid; c < kD * kD / 8; c += 128) {
+        const uint4 raw = reinterpret_cast<const uint4 *>(R)[c];
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        const int r = c >> 4, j0 = (c & 15) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Rs[r * kRStride + j0 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+            Rs[r * kRStride + j0 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+        }
+    }
+
+    const long ntiles = (N + 31) / 32;
+    for (long tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        __syncthreads();  // R ready / previous tile finished with Ks, sabs_s
+        // stage the key tile: 32 rows x 128 dims, 8 dims per thread-iteration
+        for (int c = tid; c < 32 * 16; c += 128) {
+            const int r = c >> 4, i = c & 15;
+            const long n = tile * 32 + r;
+            float x[8];
+            if (n < N) {
+                load8(p.k, p.dtype, (size_t)n * kD + 8 * i, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Ks[r * kD + 8 * i + e] = x[e];
+        }
+        __syncthreads();
+
+        // MFMA: this wave's 16 rows are tile rows 16*wave .. 16*wave+15
+        double4_t acc[8];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) acc[rb] = (double4_t){0.0, 0.0, 0.0, 0.0};
+        const int arow = 16 * wave + (lane & 15);
+        const int kq = lane >> 4;
+        for (int js = 0; js < 32; ++js) {
+            const double a = (double)Ks[arow * kD + 4 * js + kq];
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) {
+                const double b = (double)half_bits_to_float(Rs[(16 * rb + (lane & 15)) * kRStride + 4 * js + kq]);
+                acc[rb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[rb], 0, 0, 0);
+            }
+        }
+        // accumulator v of lane l holds k'[row 4*v + l/16][dim 16*rb + l%16]
+        const int q = lane & 3;  // lanes 0..3 assemble rows 4v+q
+        uint32_t words[4][4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) words[v][w] = 0u;
+            double sa = 0.0;
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb) {
+                const double val = acc[rb][v];
+                sa += fabs(val);
+                const uint64_t m = __ballot(!(val < 0.0));
+                const uint32_t bits16 = (uint32_t)((m >> (16 * q)) & 0xFFFFull);
+                words[v][rb >> 1] |= bits16 << (16 * (rb & 1));
+            }
+            sa = sum16(sa);
+            if ((lane & 15) == 0) sabs_s[16 * wave + 4 * v + (lane >> 4)] = sa;
+        }
+        if (lane < 4) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const long n = tile * 32 + 16 * wave + 4 * v + q;
+                if (n < N) {
+                    const size_t slot = slot_of(p, n);
+                    reinterpret_cast<uint4 *>(p.c.key_bits)[slot] =
+                        make_uint4(words[v][0], words[v][1], words[v][2], words[v][3]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // norms, corrections and values: 16 lanes per token-head, 8 token-heads per pass
+        for (int pass = 0; pass < 4; ++pass) {
+            const int r = pass * 8 + (tid >> 4);
+            const int i = tid & 15;
+            const long n = tile * 32 + r;
+            if (n < N) {
+                double ss = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double xe = (double)Ks[r * kD + 8 * i + e];
+                    ss += xe * xe;
+                }
+                ss = sum16(ss);
+                const size_t slot = slot_of(p, n);
+                if (i == 0) p.c.key_nc[slot] = norm_corr_word(ss, sabs_s[r]);
+                float xv[8];
+                load8(p.v, p.dtype, (size_t)n * kD + 8 * i, xv);
+                encode_values(xv, i, p.c.Gv, p.c.val_codes + slot * (kD / 2),
+                              p.c.val_sz + slot * (kD / p.c.Gv));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams &p, hipStream_t s)
+{
+    const long N = (long)p.B * p.n_new * p.c.Hkv;
+    if (N == 0) return hipSuccess;
+    if (p.rot_kind == 1) {
+        const long blocks = (N + 15) / 16;
+        hipLaunchKernelGGL(k_append_hadamard, dim3((unsigned)blocks), dim3(256), 0, s, p, N);
+    } else {
+        const long tiles = (N + 31) / 32;
+        const long blocks = tiles < 2048 ? tiles : 2048;
+        hipLaunchKernelGGL(k_append_dense, dim3((unsigned)blocks), dim3(128), 0, s, p, N);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,143 @@
+// Kernel parameter blocks and launchers of libkvcompress (host <-> kernels interface).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// Device view of the paged cache: per (page, KV head) structure of arrays.
+struct CacheView {
+    int Hkv;
+    int P;       // page size (power of two)
+    int logP;
+    int Gv;      // value group (32 or 64)
+    uint32_t *key_bits;   // [pages][Hkv][P][4]
+    uint32_t *key_nc;     // [pages][Hkv][P]
+    uint8_t *val_codes;   // [pages][Hkv][P][64]
+    uint32_t *val_sz;     // [pages][Hkv][P][128/Gv]
+};
+
+struct AppendParams {
+    CacheView c;
+    int rot_kind;          // 0 dense, 1 hadamard
+    const void *rot;       // dense: binary16 [128][128]; hadamard: uint32 [4]
+    int dtype;             // 0 f16, 1 f32
+    const void *k, *v;     // [B][n_new][Hkv][128]
+    int B, n_new;
+    const int32_t *start_pos;
+    const int32_t *page_table;
+    int max_pages;
+};
+
+// Query preparation: rotate, quantize, bit-planes.
+struct QprepParams {
+    int rot_kind;
+    const void *rot;
+    const float *q;        // [B*Hq][128]
+    int BH;
+    uint32_t *qpl;         // [B*Hq][16]
+    float4 *qpar;          // [B*Hq]
+    uint8_t *dbg_codes;    // nullable [B*Hq][128]
+    float *dbg_params;     // nullable [B*Hq][4]
+    int32_t *dbg_sumu;     // nullable [B*Hq]
+};
+
+// Chunked decode geometry shared by the decode kernels.
+struct DecodeGeom {
+    int B, Hq, Hkv;
+    int G;        // Hq / Hkv
+    int GB;       // query heads per block (<= 4)
+    int nsub;     // G / GB
+    int CH;       // tokens per chunk (power of two, multiple of 256)
+    int logCH;
+    int NC;       // chunks per sequence (max)
+    int Lpad;     // NC * CH
+    int ld;       // max_seq_len (row stride of debug/score/index arrays)
+    const int32_t *seq_lens;
+    const int32_t *page_table;
+    int max_pages;
+};
+
+struct ScoreParams {
+    DecodeGeom g;
+    CacheView c;
+    const uint32_t *qpl;
+    const float4 *qpar;
+    float kbin;
+    uint16_t *dl;          // nullable [B*Hq][Lpad]: bin distance to the chunk's top bin
+    int32_t *lmax;         // nullable [B*Hq][NC]: chunk top bin
+    float *dbg_scores;     // nullable [B*Hq][ld]
+    int32_t *dbg_iscores;  // nullable [B*Hq][ld]
+};
+
+// Bins from caller-supplied scores (kv_topp_select).
+struct BinScoresParams {
+    DecodeGeom g;          // Hq used as rows; GB = 1
+    const float *scores;   // [B*Hq][ld]
+    float kbin;
+    uint16_t *dl;
+    int32_t *lmax;
+};
+
+struct HistParams {
+    DecodeGeom g;
+    int nsplit, cps;       // splits per (b,h), chunks per split
+    const uint16_t *dl;
+    const int32_t *lmax;
+    uint32_t *hist;        // [B*Hq][nsplit][8192]
+};
+
+struct ThresholdParams {
+    DecodeGeom g;
+    int nsplit;
+    uint32_t pfx;          // rint(p * 2^24)
+    const int32_t *lmax;
+    const uint32_t *hist;
+    int32_t *sel;          // [B*Hq][4] = (e_max, b*, count, 0)
+    int32_t *dbg_count;    // nullable [B*Hq]
+    int32_t *dbg_bins;     // nullable [B*Hq][2]
+};
+
+struct SelectParams {
+    DecodeGeom g;
+    const uint16_t *dl;
+    const int32_t *lmax;
+    const int32_t *sel;
+    int32_t *cnt;          // [B*Hq][NC]
+    int32_t *idx;          // [B*Hq][ld]
+};
+
+struct AttendParams {
+    DecodeGeom g;
+    CacheView c;
+    const uint32_t *qpl;
+    const float4 *qpar;
+    float klog;            // log2(e) / sqrt(D)
+    // Top-p selection (select mode only)
+    const uint16_t *dl;
+    const int32_t *lmax;
+    const int32_t *sel;
+    // partial results per (b, h, chunk)
+    float *pm;             // [B*Hq][NC] running max score
+    float *pl;             // [B*Hq][NC] sum of weights
+    float *po;             // [B*Hq][NC][128] weighted value sums
+};
+
+struct MergeParams {
+    DecodeGeom g;
+    float klog;
+    const float *pm, *pl, *po;
+    float *out;            // [B*Hq][128]
+};
+
+hipError_t launch_append(const AppendParams &p, hipStream_t s);
+hipError_t launch_qprep(const QprepParams &p, hipStream_t s);
+hipError_t launch_score(const ScoreParams &p, hipStream_t s);
+hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s);
+hipError_t launch_hist(const HistParams &p, hipStream_t s);
+hipError_t launch_threshold(const ThresholdParams &p, hipStream_t s);
+hipError_t launch_select(const SelectParams &p, hipStream_t s);
+hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s);
+hipError_t launch_merge(const MergeParams &p, hipStream_t s);
+
+}  // namespace kvc

@@ -1,0 +1,193 @@
+/*
+ * kv_compress.h -- C ABI of the MI355X (gfx950) compressed-KV decode-attention library
+ * (libkvcompress.so).
+ *
+ * The method (from the pages "H1B-KV: Hybrid One-Bit Caches for Memory-Efficient Large
+ * Language Model Inference" and "RaBitQCache: Rotated Binary Quantization for KVCache in
+ * Long Context LLM Inference"):
+ *   - each cached key is stored as the sign bits of a seeded random rotation of the key
+ *     (H1B-KV key design: 1-bit sketch by random projection; RaBitQCache abstract:
+ *     randomized rotated binary quantization), plus a binary16 norm and a binary16
+ *     correction scalar <sign(k')/sqrt(D), k'/|k|>;
+ *   - each cached value is stored as per-group 4-bit linear codes with a binary16 scale and
+ *     zero point per group (H1B-KV key design);
+ *   - at decode the query is rotated and quantized to int4, and the proxy score of every
+ *     cached token is formed by binary x INT4 arithmetic (RaBitQCache key design);
+ *   - an optional adaptive Top-p keeps the smallest set of tokens whose softmax mass reaches
+ *     p (RaBitQCache abstract), and the output is the softmax-weighted sum of the decoded
+ *     4-bit values (H1B-KV technical framework: weights from the sketch, output from the
+ *     4-bit values).
+ *
+ * Conventions for every call:
+ *   - Pointers are device memory unless marked [host].  The caller allocates and frees all
+ *     memory and keeps it alive until the work enqueued on `stream` has completed.  The
+ *     library allocates nothing, keeps no pointer after returning, and never synchronizes.
+ *   - Each call validates its arguments on the host first.  On a bad argument it returns a
+ *     negative code, records a message for kv_last_error(), and enqueues nothing.  A failed
+ *     kernel launch returns KV_ERR_HIP with the HIP error string.
+ *   - Device-side preconditions are not checked: sequence lengths within the pages the page
+ *     table maps, page ids < num_pages, finite inputs, and (for append) positions that stay
+ *     inside the mapped pages.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null stream).
+ *   - head_dim D must be 128; value_group must be 32 or 64; page_size must be a power of
+ *     two >= 16; the GQA group Hq/Hkv must be 1, 2, 4 or 8.
+ */
+#ifndef KV_COMPRESS_H
+#define KV_COMPRESS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KV_OK = 0,
+    KV_ERR_ARG = -1,          /* NULL pointer, non-positive size, inconsistent shapes, bad p */
+    KV_ERR_UNSUPPORTED = -2,  /* a head_dim, value group, page size or GQA group with no kernel */
+    KV_ERR_WORKSPACE = -3,    /* workspace smaller than the *_workspace_bytes() figure */
+    KV_ERR_HIP = -4           /* a HIP launch failed; kv_last_error() has the HIP message */
+};
+
+enum { KV_ROT_DENSE = 0, KV_ROT_HADAMARD = 1 };
+enum { KV_F16 = 0, KV_F32 = 1 };
+
+/* Paged packed cache ([host] struct describing device arrays).
+ * Token t of sequence b lives in physical page page_table[b][t / page_size], slot
+ * t % page_size.  For each (physical page p, KV head h) the four arrays hold, slot by slot:
+ *   key_bits  [num_pages][Hkv][page_size][D/32] uint32: bit r of the rotated key k' = R k is
+ *             bit r%32 of word r/32, set when k'_r >= 0.  Read as little-endian bytes this is
+ *             byte r/8, bit r%8, set = +1: the bitmap order of the H1IB-KV page, section 二.3.
+ *   key_nc    [num_pages][Hkv][page_size] uint32: binary16 |k| in the low half, binary16
+ *             correction sum_r |k'_r| / (sqrt(D) |k|) in the high half (1.0 for k = 0).
+ *   val_codes [num_pages][Hkv][page_size][D/2] uint8: 4-bit codes, dim 2m in the low nibble
+ *             of byte m and dim 2m+1 in the high nibble.
+ *   val_sz    [num_pages][Hkv][page_size][D/value_group] uint32: binary16 scale in the low
+ *             half, binary16 zero point in the high half; value = code * scale + zero.
+ * rot: KV_ROT_DENSE -> binary16 [D][D] row-major orthogonal matrix R (k' = R k);
+ *      KV_ROT_HADAMARD -> uint32 [D/32] random signs (bit j set: sigma_j = -1), and
+ *      R = H diag(sigma) / sqrt(D) with H the Sylvester-order Hadamard matrix.
+ * The same rotation must be used for appends and decodes of one cache. */
+typedef struct kv_cache {
+    int32_t head_dim;      /* D */
+    int32_t num_kv_heads;  /* Hkv */
+    int32_t value_group;   /* 32 or 64 dims per scale/zero pair */
+    int32_t page_size;     /* tokens per page */
+    int32_t num_pages;     /* physical pages in the pool */
+    int32_t rot_kind;      /* KV_ROT_DENSE or KV_ROT_HADAMARD */
+    const void *rot;       /* device: see above */
+    uint32_t *key_bits;
+    uint32_t *key_nc;
+    uint8_t *val_codes;
+    uint32_t *val_sz;
+} kv_cache;
+
+/* Optional intermediate outputs of kv_decode_attend ([host] struct; every member is a
+ * nullable device pointer).  Used by tests to compare each stage with the oracle; passing
+ * NULL (or NULL members) skips the extra work.  ld = max_seq_len.
+ *   q_codes  uint8 [B][Hq][D]       int4 codes u of the rotated query
+ *   q_params float [B][Hq][4]       v_l, delta, c0 = v_l/sqrt(D), c1 = delta/sqrt(D)
+ *   q_sumu   int32 [B][Hq]          sum of the codes
+ *   iscores  int32 [B][Hq][ld]      A = sum_r s_r u_r, s_r = +-1 from the key bits
+ *   scores   float [B][Hq][ld]      proxy scores (estimates of <k, q>)
+ *   sel_count int32 [B][Hq]         Top-p only: number of selected tokens
+ *   sel_idx  int32 [B][Hq][ld]      Top-p only: selected token indices, ascending
+ *   sel_bins int32 [B][Hq][2]       Top-p only: top bin e_max and threshold bin distance b*
+ *   stage_events [host] array of 2 * KV_NUM_STAGES hipEvent_t (nullable): the call records
+ *            stage_events[2s] on `stream` before the kernels of stage s and
+ *            stage_events[2s+1] after them, for each stage s it runs (others are left
+ *            alone), so a caller can time every stage with hipEventElapsedTime. */
+enum {
+    KV_STAGE_QUERY = 0,      /* query rotation, int4 codes, bit-planes */
+    KV_STAGE_SCORE = 1,      /* Top-p: proxy scores of all tokens -> bin distances */
+    KV_STAGE_HIST = 2,       /* Top-p: per-bin token counts */
+    KV_STAGE_THRESHOLD = 3,  /* Top-p: threshold bin */
+    KV_STAGE_SELECT = 4,     /* Top-p, only when sel_idx is requested: ordered index lists */
+    KV_STAGE_ATTEND = 5,     /* scores of the attended tokens, softmax, 4-bit value sums */
+    KV_STAGE_MERGE = 6,      /* merge of the per-chunk partial results */
+    KV_NUM_STAGES = 7
+};
+typedef struct kv_debug {
+    uint8_t *q_codes;
+    float *q_params;
+    int32_t *q_sumu;
+    int32_t *iscores;
+    float *scores;
+    int32_t *sel_count;
+    int32_t *sel_idx;
+    int32_t *sel_bins;
+    hipEvent_t *stage_events;
+} kv_debug;
+
+/* kv_compress_append -- encode n_new new tokens per sequence into the cache.
+ * Defines: H1B-KV key design (1-bit key sketch by random projection, 4-bit linear values)
+ * with RaBitQCache's randomized rotation (abstract).
+ *   c          [host] cache descriptor
+ *   dtype      KV_F16 or KV_F32: element type of k and v
+ *   k, v       [B][n_new][Hkv][D] row-major
+ *   start_pos  int32 [B]: token index of the first new token of each sequence
+ *   page_table int32 [B][max_pages]
+ * Token i of sequence b is written at position start_pos[b] + i.  Appending a sequence in
+ * several calls gives the same bytes as one call. */
+int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const void *v, int32_t B,
+                       int32_t n_new, const int32_t *start_pos, const int32_t *page_table,
+                       int32_t max_pages, hipStream_t stream);
+
+/* kv_decode_attend -- one decode step of attention over the compressed cache.
+ * Defines: H1B-KV technical framework (attention weights from the 1-bit sketch, output
+ * from the 4-bit values); RaBitQCache abstract and key design (int4 query, binary x INT4
+ * proxy score, adaptive Top-p).
+ *   q           float [B][Hq][D]; query head h attends KV head h * Hkv / Hq
+ *   seq_lens    int32 [B]: tokens 0..seq_lens[b]-1 of sequence b are attended; must be
+ *               <= max_seq_len; a zero length gives a zero output
+ *   max_seq_len [host] upper bound of seq_lens (sizes the grid and the workspace)
+ *   top_p       [host] >= 1: softmax over all tokens; in (0, 1): adaptive Top-p, then the
+ *               softmax renormalised over the selected tokens.  <= 0 or NaN is an error.
+ *   out         float [B][Hq][D]
+ *   dbg         [host] nullable, see kv_debug
+ *   workspace   device scratch of at least kv_decode_workspace_bytes(...) bytes; its
+ *               contents on entry do not matter
+ * Softmax weights are exp(score / sqrt(D)). */
+int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq,
+                     const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                     int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace size for kv_decode_attend with these arguments (0 on invalid arguments). */
+size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
+                                 int32_t head_dim, float top_p);
+
+/* kv_topp_select -- adaptive Top-p over caller-supplied proxy scores.
+ * Defines: RaBitQCache abstract (adaptive Top-p retrieval whose token budget follows the
+ * actual attention sparsity), read as the textbook nucleus evaluated on integer weights:
+ *   bin e_i = floor(s_i * kbin), kbin = fp32(256 log2(e) / sqrt(head_dim)), clamped to
+ *   [-2^29, 2^29]; d_i = max_j e_j - e_i; weight W(d) = T[d mod 256] >> (d / 256) for
+ *   d < 8192 and 0 beyond, T[j] = round(2^(32 - j/256)); Z = sum_i W(d_i);
+ *   T_p = ceil(Z * rint(p * 2^24) / 2^24); b* = min { b : sum_{d_i <= b} W(d_i) >= T_p };
+ *   selected set S = { i : d_i <= b* }.
+ *   scores    float [B][Hq][ld]; tokens 0..seq_lens[b]-1 are used (seq_lens <= ld)
+ *   top_p     [host] in (0, 1)
+ *   sel_idx   int32 [B][Hq][ld]: S in ascending order; entries past the count are untouched
+ *   sel_count int32 [B][Hq]
+ *   workspace at least kv_topp_workspace_bytes(B, Hq, ld) bytes */
+int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int32_t B,
+                   int32_t Hq, int32_t head_dim, float top_p, int32_t *sel_idx,
+                   int32_t *sel_count, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Workspace size for kv_topp_select (0 on invalid arguments). */
+size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld);
+
+/* Message describing the last error of this thread (static storage; "" if none). */
+const char *kv_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV_COMPRESS_H */

@@ -1,0 +1,119 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/kv_compress.h declares, and rejects bad arguments on the host (negative code and a
+message, before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_kv_cache_compress_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kv_compress.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = _declared()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kv_version() == 10000
+
+
+def _desc(**kw):
+    d = dict(head_dim=128, num_kv_heads=8, value_group=32, page_size=256, num_pages=16, rot_kind=0,
+             rot=0x10000, key_bits=0x10000, key_nc=0x10000, val_codes=0x10000, val_sz=0x10000)
+    d.update(kw)
+    return L.KVCacheDesc(*[d[f] for f, _ in L.KVCacheDesc._fields_])
+
+
+def _decode(desc, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p=1.0, ws_bytes=None, q=FAKE, out=FAKE):
+    if ws_bytes is None:
+        ws_bytes = L.lib().kv_decode_workspace_bytes(B, Hq, desc.num_kv_heads, max_seq_len, 128, top_p)
+    return L.lib().kv_decode_attend(ctypes.byref(desc), q, B, Hq, FAKE, max_seq_len, FAKE, max_pages, top_p, out,
+                                    None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), L.KV_ERR_UNSUPPORTED),
+    (dict(value_group=16), L.KV_ERR_UNSUPPORTED),
+    (dict(page_size=100), L.KV_ERR_UNSUPPORTED),
+    (dict(page_size=8), L.KV_ERR_UNSUPPORTED),
+    (dict(num_pages=0), L.KV_ERR_ARG),
+    (dict(num_kv_heads=0), L.KV_ERR_ARG),
+    (dict(rot_kind=7), L.KV_ERR_ARG),
+    (dict(key_nc=0), L.KV_ERR_ARG),
+    (dict(rot=0), L.KV_ERR_ARG),
+])
+def test_bad_cache_descriptor(kw, code):
+    assert _decode(_desc(**kw)) == code
+    assert L.last_error()
+    rc = L.lib().kv_compress_append(ctypes.byref(_desc(**kw)), 0, FAKE, FAKE, 1, 4, FAKE, FAKE, 1, None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), L.KV_ERR_ARG),
+    (dict(Hq=12), L.KV_ERR_ARG),        # not a multiple of Hkv = 8
+    (dict(Hq=24), L.KV_ERR_UNSUPPORTED),  # group 3
+    (dict(Hq=128), L.KV_ERR_UNSUPPORTED),  # group 16
+    (dict(max_seq_len=0), L.KV_ERR_ARG),
+    (dict(max_seq_len=5000, max_pages=4), L.KV_ERR_ARG),  # pages cover only 1024 tokens
+    (dict(top_p=0.0), L.KV_ERR_ARG),
+    (dict(top_p=-0.5), L.KV_ERR_ARG),
+    (dict(top_p=float("nan")), L.KV_ERR_ARG),
+    (dict(q=None), L.KV_ERR_ARG),
+    (dict(out=None), L.KV_ERR_ARG),
+])
+def test_bad_decode_arguments(kw, code):
+    ws = kw.pop("ws_bytes", 1 << 30)
+    assert _decode(_desc(), ws_bytes=ws, **kw) == code
+    assert L.last_error()
+
+
+def test_workspace_too_small():
+    need = L.lib().kv_decode_workspace_bytes(2, 32, 8, 1000, 128, 0.9)
+    assert need > 0
+    assert _decode(_desc(), top_p=0.9, ws_bytes=need - 1) == L.KV_ERR_WORKSPACE
+    assert "workspace" in L.last_error()
+    tneed = L.lib().kv_topp_workspace_bytes(2, 32, 1000)
+    rc = L.lib().kv_topp_select(FAKE, 1000, FAKE, 2, 32, 128, 0.9, FAKE, FAKE, FAKE, tneed - 1, None)
+    assert rc == L.KV_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    lib = L.lib()
+    full = lib.kv_decode_workspace_bytes(4, 32, 8, 131072, 128, 1.0)
+    topp = lib.kv_decode_workspace_bytes(4, 32, 8, 131072, 128, 0.9)
+    assert 0 < full < topp
+    # the Top-p workspace holds at least a 16-bit bin distance per (sequence, head, token)
+    assert topp >= 4 * 32 * 131072 * 2
+    assert lib.kv_decode_workspace_bytes(4, 32, 8, 131072, 64, 0.9) == 0
+    assert lib.kv_decode_workspace_bytes(0, 32, 8, 131072, 128, 0.9) == 0
+    assert lib.kv_topp_workspace_bytes(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0, 1.5, -1.0, float("nan")])
+def test_topp_select_rejects_p(p):
+    rc = L.lib().kv_topp_select(FAKE, 100, FAKE, 1, 1, 128, p, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == L.KV_ERR_ARG
+
+
+def test_append_argument_errors():
+    lib = L.lib()
+    d = _desc()
+    assert lib.kv_compress_append(ctypes.byref(d), 2, FAKE, FAKE, 1, 4, FAKE, FAKE, 1, None) == L.KV_ERR_ARG
+    assert lib.kv_compress_append(ctypes.byref(d), 0, None, FAKE, 1, 4, FAKE, FAKE, 1, None) == L.KV_ERR_ARG
+    assert lib.kv_compress_append(ctypes.byref(d), 0, FAKE, FAKE, 0, 4, FAKE, FAKE, 1, None) == L.KV_ERR_ARG
+    assert lib.kv_compress_append(ctypes.byref(d), 0, FAKE, FAKE, 1, -1, FAKE, FAKE, 1, None) == L.KV_ERR_ARG
+    # zero new tokens is a no-op
+    assert lib.kv_compress_append(ctypes.byref(d), 0, None, None, 1, 0, None, None, 1, None) == L.KV_OK
+    assert lib.kv_compress_append(None, 0, FAKE, FAKE, 1, 4, FAKE, FAKE, 1, None) == L.KV_ERR_ARG
