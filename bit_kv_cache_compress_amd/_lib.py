@@ -49,7 +49,7 @@ class KVDebug(ctypes.Structure):
     ]
 
 
-STAGES = ("query", "score", "hist", "threshold", "select", "attend", "merge")
+STAGES = ("query", "score", "hist", "select", "attend", "merge")
 
 
 class KVCompressError(RuntimeError):
@@ -69,6 +69,10 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_kv_cache_compress_amd.build` "
                           "(there is no fallback path)")
+    # torch ships its own HIP runtime; loading torch first makes the library bind to that
+    # same runtime instance (one HIP runtime per process, shared streams and events)
+    import torch  # noqa: F401
+
     L = ctypes.CDLL(LIB_PATH)
     P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     L.kv_compress_append.argtypes = [ctypes.POINTER(KVCacheDesc), i32, P, P, i32, i32, P, P, i32, P]

@@ -10,6 +10,7 @@ from typing import Optional
 import torch
 
 from . import _lib as L
+from ._lib import lib
 
 HEAD_DIM = 128
 
@@ -135,16 +136,28 @@ class DecodeDebug:
                             self.sel_idx, self.sel_bins)], None)
 
 
+def _loaded_hip_runtime() -> str:
+    """Path of the HIP runtime already mapped into this process (the one torch and the
+    library use); opening another copy would create a second, separate runtime."""
+    lib().kv_version()  # make sure the library and its HIP runtime are loaded
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in path:
+                return path
+    raise RuntimeError("no HIP runtime is mapped in this process")
+
+
 class StageTimer:
     """HIP events that the library records around each decode stage (kv_debug.stage_events).
     Pass ``timer.struct()`` as ``debug_struct`` to decode_attend; read ``timer.elapsed_ms()``
     after synchronizing."""
 
     def __init__(self):
-        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip = ctypes.CDLL(_loaded_hip_runtime())
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self._hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        self._hip.hipGetLastError.argtypes = []
         n = 2 * len(L.STAGES)
         self.events = (ctypes.c_void_p * n)()
         for i in range(n):
@@ -158,13 +171,18 @@ class StageTimer:
     def struct(self) -> L.KVDebug:
         return self._dbg
 
-    def elapsed_ms(self) -> dict:
+    def elapsed_ms(self, stages=None) -> dict:
+        """Elapsed time of each recorded stage (pass the names of the stages the call ran;
+        events of stages that never ran must not be queried)."""
         out = {}
         for s, name in enumerate(L.STAGES):
+            if stages is not None and name not in stages:
+                continue
             a, b = self.events[2 * s], self.events[2 * s + 1]
             ms = ctypes.c_float(0.0)
             if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0:
                 out[name] = float(ms.value)
+        self._hip.hipGetLastError()  # leave no error state behind for the next HIP call
         return out
 
 

@@ -44,26 +44,45 @@ struct Plan {
     kvc::DecodeGeom g;
     bool topp;
     int nsplit, cps;
-    size_t off_qpl, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po;
+    size_t off_qpl, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_ctr, off_pm, off_pl, off_po;
     size_t total;
 };
 
-// Chunk size: the largest power of two CH in [256, cap] that still gives at least 2048
-// blocks (8 per compute unit) over (chunk, KV-head group, sequence); cap keeps the per-block
-// LDS score buffer (CH x GB floats) and Top-p entry list within 48 KB.
-void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
+// Largest chunk: the per-block LDS score buffer holds CH x GB floats (32 KB) and a Top-p
+// block lists up to CH token offsets in 16 bits.
+int chunk_cap(int GB, bool topp)
 {
     int cap = 8192 / GB;
     if (topp && cap > 4096) cap = 4096;
+    return cap;
+}
+
+// At most this many chunks per sequence (the merge keeps one weight per chunk in LDS).
+constexpr int kMaxChunks = 4096;
+
+// Chunk size: the largest power of two CH in [256, cap] that still gives at least 2048
+// blocks (8 per compute unit) over (chunk, KV-head group, sequence), and no fewer than
+// max_len / 4096 tokens.
+void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
+{
+    const int cap = chunk_cap(GB, topp);
     int CH = cap;
     const long units = (long)B * rows_per_seq;
-    while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048) CH >>= 1;
+    while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048 && (long)(CH >> 1) * kMaxChunks >= max_len) CH >>= 1;
     pl.g.CH = CH;
     pl.g.logCH = ilog2(CH);
     pl.g.NC = (max_len + CH - 1) / CH;
     if (pl.g.NC < 1) pl.g.NC = 1;
     pl.g.Lpad = pl.g.NC * CH;
     pl.g.ld = max_len;
+    // Top-p attention blocks cover KA score chunks (at most 8192 tokens, the entry list of
+    // a block), as long as that still leaves >= 512 blocks: most of their tokens are skipped,
+    // so fewer, larger blocks cost fewer dependent memory rounds.
+    int KA = 1;
+    if (topp)
+        while (KA < 4 && (long)CH * KA * 2 <= 8192 && units * ((pl.g.NC + 2 * KA - 1) / (2 * KA)) >= 512) KA *= 2;
+    pl.g.KA = KA;
+    pl.g.NCA = (pl.g.NC + KA - 1) / KA;
 }
 
 void plan_layout(Plan &pl, int BH)
@@ -74,19 +93,22 @@ void plan_layout(Plan &pl, int BH)
         o = align_up(o + bytes);
         return at;
     };
-    const size_t NC = (size_t)pl.g.NC;
+    const size_t NC = (size_t)pl.g.NC, NCA = (size_t)pl.g.NCA;
     pl.off_qpl = take((size_t)BH * 16 * 4);
     pl.off_qpar = take((size_t)BH * 16);
-    pl.off_pm = take((size_t)BH * NC * 4);
-    pl.off_pl = take((size_t)BH * NC * 4);
-    pl.off_po = take((size_t)BH * NC * 128 * 4);
+    pl.off_pm = take((size_t)BH * NCA * 4);
+    pl.off_pl = take((size_t)BH * NCA * 4);
+    pl.off_po = take((size_t)BH * NCA * 128 * 4);
     if (pl.topp) {
-        // histogram splits: >= 256 blocks over (split, head, sequence), <= 1024 chunks each
-        int nsplit = (256 + BH - 1) / BH;
+        // histogram splits: >= 512 blocks over (split, head, sequence); a split holds fewer
+        // than 65536 tokens (16-bit partial counts) and at most 1024 chunks
+        int nsplit = (512 + BH - 1) / BH;
+        const int min_split = (int)(((long)pl.g.Lpad + 32767) / 32768);
+        if (nsplit < min_split) nsplit = min_split;
         if (nsplit > pl.g.NC) nsplit = pl.g.NC;
         if (nsplit < 1) nsplit = 1;
         int cps = (pl.g.NC + nsplit - 1) / nsplit;
-        while (cps > 1024) {
+        while (cps > 1024 || (long)cps * pl.g.CH > 65535) {
             ++nsplit;
             cps = (pl.g.NC + nsplit - 1) / nsplit;
         }
@@ -94,12 +116,13 @@ void plan_layout(Plan &pl, int BH)
         pl.cps = cps;
         pl.off_lmax = take((size_t)BH * NC * 4);
         pl.off_dl = take((size_t)BH * pl.g.Lpad * 2);
-        pl.off_hist = take((size_t)BH * nsplit * 8192 * 4);
+        pl.off_hist = take((size_t)BH * nsplit * 8192 * 2);
         pl.off_sel = take((size_t)BH * 4 * 4);
         pl.off_cnt = take((size_t)BH * NC * 4);
+        pl.off_ctr = take((size_t)BH * 4);
     } else {
         pl.nsplit = pl.cps = 0;
-        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = 0;
+        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = pl.off_ctr = 0;
     }
     pl.total = o;
 }
@@ -115,7 +138,10 @@ int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, f
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(KV_ERR_UNSUPPORTED, "GQA group Hq/Hkv = %d: supported groups are 1, 2, 4, 8", G);
     if (!(top_p > 0.0f)) return fail(KV_ERR_ARG, "top_p must be > 0 (got %g)", (double)top_p);
-    if (max_seq_len > (1 << 30)) return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above 2^30", max_seq_len);
+    const int GB = G < 4 ? G : 4;
+    const long limit = (long)chunk_cap(GB, top_p < 1.0f) * kMaxChunks;
+    if (max_seq_len > limit)
+        return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld for this head grouping", max_seq_len, limit);
     return KV_OK;
 }
 
@@ -254,7 +280,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     const float klog = (float)(1.4426950408889634074 / sqrt((double)c->head_dim));
     (void)isd;
     const int BH = B * Hq;
-    uint32_t *qpl = at<uint32_t>(workspace, pl.off_qpl);
+    uint32_t *qnib = at<uint32_t>(workspace, pl.off_qpl);
     float4 *qpar = at<float4>(workspace, pl.off_qpar);
 
     kvc::QprepParams qp;
@@ -262,8 +288,9 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     qp.rot = c->rot;
     qp.q = q;
     qp.BH = BH;
-    qp.qpl = qpl;
+    qp.qnib = qnib;
     qp.qpar = qpar;
+    qp.counters = pl.topp ? at<int32_t>(workspace, pl.off_ctr) : nullptr;
     qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
@@ -275,7 +302,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     kvc::ScoreParams sp;
     sp.g = pl.g;
     sp.c = cv;
-    sp.qpl = qpl;
+    sp.qnib = qnib;
     sp.qpar = qpar;
     sp.kbin = kbin;
     sp.dl = pl.topp ? at<uint16_t>(workspace, pl.off_dl) : nullptr;
@@ -294,32 +321,24 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
         hp.g = pl.g;
         hp.nsplit = pl.nsplit;
         hp.cps = pl.cps;
+        hp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
         hp.dl = sp.dl;
         hp.lmax = sp.lmax;
-        hp.hist = at<uint32_t>(workspace, pl.off_hist);
+        hp.hist = at<uint16_t>(workspace, pl.off_hist);
+        hp.counters = at<int32_t>(workspace, pl.off_ctr);
+        hp.sel = at<int32_t>(workspace, pl.off_sel);
+        hp.dbg_count = dbg ? dbg->sel_count : nullptr;
+        hp.dbg_bins = dbg ? dbg->sel_bins : nullptr;
         stage_mark(dbg, KV_STAGE_HIST, true, stream);
         e = kvc::launch_hist(hp, stream);
         if (e != hipSuccess) return hip_fail(e, "histogram launch");
         stage_mark(dbg, KV_STAGE_HIST, false, stream);
-        kvc::ThresholdParams tp;
-        tp.g = pl.g;
-        tp.nsplit = pl.nsplit;
-        tp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
-        tp.lmax = sp.lmax;
-        tp.hist = hp.hist;
-        tp.sel = at<int32_t>(workspace, pl.off_sel);
-        tp.dbg_count = dbg ? dbg->sel_count : nullptr;
-        tp.dbg_bins = dbg ? dbg->sel_bins : nullptr;
-        stage_mark(dbg, KV_STAGE_THRESHOLD, true, stream);
-        e = kvc::launch_threshold(tp, stream);
-        if (e != hipSuccess) return hip_fail(e, "threshold launch");
-        stage_mark(dbg, KV_STAGE_THRESHOLD, false, stream);
         if (dbg && dbg->sel_idx) {
             kvc::SelectParams sel;
             sel.g = pl.g;
             sel.dl = sp.dl;
             sel.lmax = sp.lmax;
-            sel.sel = tp.sel;
+            sel.sel = hp.sel;
             sel.cnt = at<int32_t>(workspace, pl.off_cnt);
             sel.idx = dbg->sel_idx;
             stage_mark(dbg, KV_STAGE_SELECT, true, stream);
@@ -332,7 +351,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     kvc::AttendParams ap;
     ap.g = pl.g;
     ap.c = cv;
-    ap.qpl = qpl;
+    ap.qnib = qnib;
     ap.qpar = qpar;
     ap.klog = klog;
     ap.dl = sp.dl;
@@ -417,27 +436,23 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     hp.g = pl.g;
     hp.nsplit = pl.nsplit;
     hp.cps = pl.cps;
+    hp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
     hp.dl = bp.dl;
     hp.lmax = bp.lmax;
-    hp.hist = at<uint32_t>(workspace, pl.off_hist);
+    hp.hist = at<uint16_t>(workspace, pl.off_hist);
+    hp.counters = at<int32_t>(workspace, pl.off_ctr);
+    hp.sel = at<int32_t>(workspace, pl.off_sel);
+    hp.dbg_count = sel_count;
+    hp.dbg_bins = nullptr;
+    e = kvc::launch_zero(hp.counters, B * Hq, stream);
+    if (e != hipSuccess) return hip_fail(e, "zero launch");
     e = kvc::launch_hist(hp, stream);
     if (e != hipSuccess) return hip_fail(e, "histogram launch");
-    kvc::ThresholdParams tp;
-    tp.g = pl.g;
-    tp.nsplit = pl.nsplit;
-    tp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
-    tp.lmax = bp.lmax;
-    tp.hist = hp.hist;
-    tp.sel = at<int32_t>(workspace, pl.off_sel);
-    tp.dbg_count = sel_count;
-    tp.dbg_bins = nullptr;
-    e = kvc::launch_threshold(tp, stream);
-    if (e != hipSuccess) return hip_fail(e, "threshold launch");
     kvc::SelectParams sel;
     sel.g = pl.g;
     sel.dl = bp.dl;
     sel.lmax = bp.lmax;
-    sel.sel = tp.sel;
+    sel.sel = hp.sel;
     sel.cnt = at<int32_t>(workspace, pl.off_cnt);
     sel.idx = sel_idx;
     e = kvc::launch_select(sel, stream);

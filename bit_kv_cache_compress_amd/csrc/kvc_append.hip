@@ -280,6 +280,71 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Dense rotation for few token-heads (the per-step append of a decode loop): one wave per
+// token-head, lane l computes rows l and l + 64 of k' = R k as a binary64 fused chain over
+// j ascending (each product of a binary16 and a binary16/binary32 is exact, so each step is
+// the rounded sum).  Many small blocks instead of one MFMA tile keep the latency low.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_append_dense_small(AppendParams p, long N)
+{
+    __shared__ double kd[4][kD];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long n = (long)blockIdx.x * 4 + w;
+    const bool active = n < N;  // uniform per wave
+    if (active && lane < 16) {
+        float x[8];
+        load8(p.k, p.dtype, (size_t)n * kD + 8 * lane, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kd[w][8 * lane + e] = (double)x[e];
+    }
+    __syncthreads();
+    if (!active) return;
+    const uint4 *R0 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + lane * kD);
+    const uint4 *R1 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + (lane + 64) * kD);
+    double y0 = 0.0, y1 = 0.0;
+    for (int half = 0; half < 2; ++half) {
+        uint4 a[8], c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[i] = R0[8 * half + i];
+            c[i] = R1[8 * half + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t wa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
+            const uint32_t wc[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 64 * half + 8 * i + e;
+                const double kj = kd[w][j];
+                y0 = fma((double)half_bits_to_float((wa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), kj, y0);
+                y1 = fma((double)half_bits_to_float((wc[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), kj, y1);
+            }
+        }
+    }
+    const uint64_t m0 = __ballot(!(y0 < 0.0));  // rows 0..63
+    const uint64_t m1 = __ballot(!(y1 < 0.0));  // rows 64..127
+    double sabs = fabs(y0) + fabs(y1);
+    double ss = kd[w][2 * lane] * kd[w][2 * lane] + kd[w][2 * lane + 1] * kd[w][2 * lane + 1];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sabs += __shfl_xor(sabs, o);
+        ss += __shfl_xor(ss, o);
+    }
+    const size_t slot = slot_of(p, n);
+    if (lane == 0) {
+        reinterpret_cast<uint4 *>(p.c.key_bits)[slot] =
+            make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
+        p.c.key_nc[slot] = norm_corr_word(ss, sabs);
+    }
+    if (lane < 16) {
+        float xv[8];
+        load8(p.v, p.dtype, (size_t)n * kD + 8 * lane, xv);
+        encode_values(xv, lane, p.c.Gv, p.c.val_codes + slot * (kD / 2), p.c.val_sz + slot * (kD / p.c.Gv));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendParams &p, hipStream_t s)
@@ -289,6 +354,8 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
     if (p.rot_kind == 1) {
         const long blocks = (N + 15) / 16;
         hipLaunchKernelGGL(k_append_hadamard, dim3((unsigned)blocks), dim3(256), 0, s, p, N);
+    } else if (N <= 8192) {
+        hipLaunchKernelGGL(k_append_dense_small, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, p, N);
     } else {
         const long tiles = (N + 31) / 32;
         const long blocks = tiles < 2048 ? tiles : 2048;

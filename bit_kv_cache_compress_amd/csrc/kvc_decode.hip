@@ -1,5 +1,5 @@
 // Decode kernels: query preparation, binary x INT4 proxy scores, adaptive Top-p (bin
-// distances, histogram, threshold, ordered selection), chunked attention over the 4-bit
+// distances, histogram and threshold, ordered selection), chunked attention over the 4-bit
 // values, and the split-K merge.
 //
 // Method: "RaBitQCache" (abstract and key design: int4 query, binary x INT4 proxy score,
@@ -9,7 +9,9 @@
 // Work decomposition.  A sequence is cut into chunks of CH tokens (CH a power of two,
 // 256..8192).  One 256-thread block works on one (chunk, KV head, sequence) and on GB <= 4
 // of the query heads that share the KV head (GQA), so every key word and value byte it
-// streams from HBM serves all GB heads.  Partial results (max score, weight sum, weighted
+// streams from HBM serves all GB heads.  The page ids of a chunk are read once into LDS, and
+// each thread issues all of its loads of a pass before using any of them, so that a block
+// keeps several KB of HBM reads in flight.  Partial results (max score, weight sum, weighted
 // value sum) of all chunks are merged per (sequence, query head) at the end.
 #include "kvc_device.h"
 #include "kvc_launch.h"
@@ -17,6 +19,8 @@
 namespace kvc {
 
 namespace {
+
+constexpr int kMaxChunkPages = 513;  // CH / P + 1 with CH <= 8192, P >= 16
 
 // First query head of block (hb = kv head * nsub + sub) and its KV head.
 __device__ __forceinline__ void block_heads(const DecodeGeom &g, int hb, int &kvh, int &hq0)
@@ -26,14 +30,22 @@ __device__ __forceinline__ void block_heads(const DecodeGeom &g, int hb, int &kv
     hq0 = kvh * g.G + sub * g.GB;
 }
 
-__device__ __forceinline__ size_t token_slot(const DecodeGeom &g, const CacheView &c, int b, int kvh,
-                                             int t)
+// Page ids of the chunk [t0, t0 + n) into LDS; returns the first page index.
+__device__ __forceinline__ int load_chunk_pages(const DecodeGeom &g, int logP, int b, int t0, int n,
+                                                int *pages)
 {
-    const int page = g.page_table[(size_t)b * g.max_pages + (t >> c.logP)];
-    return ((size_t)page * c.Hkv + kvh) * c.P + (t & (c.P - 1));
+    const int p0 = t0 >> logP, p1 = (t0 + n - 1) >> logP;
+    for (int i = threadIdx.x; i <= p1 - p0; i += kBlock) pages[i] = g.page_table[(size_t)b * g.max_pages + p0 + i];
+    __syncthreads();
+    return p0;
 }
 
-// Block-wide max of GB ints per thread (256 threads); result broadcast through LDS.
+__device__ __forceinline__ size_t chunk_slot(const CacheView &c, const int *pages, int p0, int kvh, int t)
+{
+    return ((size_t)pages[(t >> c.logP) - p0] * c.Hkv + kvh) * c.P + (t & (c.P - 1));
+}
+
+// Block-wide reduction of GB values per thread (256 threads); result broadcast in LDS.
 template <int GB, typename T, typename Op>
 __device__ __forceinline__ void block_reduce(T (&v)[GB], T *red /* [4][GB] */, T *out /* [GB] */, Op op)
 {
@@ -54,6 +66,25 @@ __device__ __forceinline__ void block_reduce(T (&v)[GB], T *red /* [4][GB] */, T
     __syncthreads();
 }
 
+// Exclusive prefix sum over the 256 threads of a block; *total gets the sum.
+__device__ __forceinline__ int block_exscan(int v, int *red /* [4] */, int *total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    int before = x - v;
+    for (int w = 0; w < wave; ++w) before += red[w];
+    *total = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return before;
+}
+
 struct MaxI { __device__ int operator()(int a, int b) const { return a > b ? a : b; } };
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
@@ -65,25 +96,30 @@ struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 //   hadamard: x = sigma * q, in-place fast Walsh-Hadamard butterflies h = 1..64 (binary32),
 //             q' = x * fp32(1/sqrt(D))
 //   v_l = min q', delta = (max q' - v_l) / 15, u = clamp(rint((q' - v_l) / delta), 0, 15)
-//   (u = 0 when delta == 0); bit-planes of u; c0 = v_l/sqrt(D), c1 = delta/sqrt(D).
+//   (u = 0 when delta == 0); the codes in dot8 order; c0 = v_l/sqrt(D), c1 = delta/sqrt(D).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
 {
     __shared__ float xs[kD];
+    __shared__ int us[kD];
     __shared__ float redf[4];
     __shared__ int redi[2];
     const int bh = blockIdx.x, r = threadIdx.x;
     const int lane = r & 63, wave = r >> 6;
     const float *q = p.q + (size_t)bh * kD;
+    if (p.counters && r == 0) p.counters[bh] = 0;
     float x;
     if (p.rot_kind == 0) {
+        const uint4 *Rr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + r * kD);
+        uint4 row[kD / 8];
+#pragma unroll
+        for (int c = 0; c < kD / 8; ++c) row[c] = Rr[c];
         xs[r] = q[r];
         __syncthreads();
-        const uint4 *Rr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + r * kD);
         float a = 0.0f;
+#pragma unroll
         for (int c = 0; c < kD / 8; ++c) {
-            const uint4 raw = Rr[c];
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint32_t w[4] = {row[c].x, row[c].y, row[c].z, row[c].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = 8 * c + e;
@@ -107,7 +143,6 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
         __syncthreads();
         x = xs[r] * isd;
     }
-    // min / max over the 128 rotated coordinates
     float mn = x, mx = x;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -130,15 +165,17 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
     }
     int su = wave_sum_i(u);
     if (lane == 0) redi[wave] = su;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint64_t m = __ballot((u >> j) & 1);
-        if (lane == 0) {
-            p.qpl[(size_t)bh * 16 + j * 4 + 2 * wave] = (uint32_t)m;
-            p.qpl[(size_t)bh * 16 + j * 4 + 2 * wave + 1] = (uint32_t)(m >> 32);
-        }
-    }
+    __syncthreads();  // everyone has read xs
+    us[r] = u;
     __syncthreads();
+    if (r < 16) {
+        // word 4w + k: nibble m holds the code of dim 32w + 4m + k
+        const int w = r >> 2, k = r & 3;
+        uint32_t word = 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) word |= (uint32_t)us[32 * w + 4 * m + k] << (4 * m);
+        p.qnib[(size_t)bh * 16 + r] = word;
+    }
     su = redi[0] + redi[1];
     if (r == 0) p.qpar[bh] = make_float4(vl * isd, delta * isd, __int_as_float(su), 0.0f);
     if (p.dbg_codes) p.dbg_codes[(size_t)bh * kD + r] = (uint8_t)u;
@@ -156,11 +193,16 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
 // the proxy score of every token of the chunk for GB query heads.  Writes the bin distance
 // to the chunk's top bin (uint16, saturated at 8192: no token that far below a chunk's top
 // can be selected, since the threshold distance is < 8192) and the chunk's top bin.
+// Thread t scores tokens t, t + 256, ... (coalesced 16-byte key loads, 8 in flight), then
+// stores the distances of 8 consecutive tokens per 16-byte store.
 // ---------------------------------------------------------------------------------------
-template <int GB>
+template <int GB, bool DEBUG>
 __global__ __launch_bounds__(256) void k_score(ScoreParams p)
 {
     __shared__ int ebuf[8192];
+    __shared__ int pages[kMaxChunkPages];
+    __shared__ uint32_t qsh[GB * 16];
+    __shared__ float4 qps[GB];
     __shared__ int red[4 * GB];
     __shared__ int emax_s[GB];
     const DecodeGeom &g = p.g;
@@ -171,38 +213,64 @@ __global__ __launch_bounds__(256) void k_score(ScoreParams p)
     const int t0 = chunk * g.CH;
     if (t0 >= L) return;
     const int n = min(g.CH, L - t0);
+    const int tid = threadIdx.x;
     const int bh0 = b * g.Hq + hq0;
+    stage_query<GB>(p.qnib, p.qpar, bh0, qsh, qps);
+    const int p0 = load_chunk_pages(g, p.c.logP, b, t0, n, pages);  // includes a barrier
     QueryState<GB> qs;
-    load_query<GB>(qs, p.qpl, p.qpar, bh0);
+    read_query<GB>(qs, qsh, qps);
     int lm[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) lm[h] = -kBinClamp;
     const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
-    for (int tl = threadIdx.x; tl < n; tl += kBlock) {
-        const int t = t0 + tl;
-        const size_t slot = token_slot(g, p.c, b, kvh, t);
-        const uint4 kb = kb4[slot];
-        const uint32_t nc = p.c.key_nc[slot];
-        float s[GB];
-        int A[GB];
-        score_key<GB>(kb, nc, qs, s, A);
+    const int nk = (n + kBlock - 1) / kBlock;
+    for (int k0 = 0; k0 < nk; k0 += 8) {
+        uint4 kb[8];
+        uint32_t nc[8];
 #pragma unroll
-        for (int h = 0; h < GB; ++h) {
-            const int e = score_bin(s[h], p.kbin);
-            ebuf[h * g.CH + tl] = e;
-            lm[h] = max(lm[h], e);
-            if (p.dbg_scores) p.dbg_scores[(size_t)(bh0 + h) * g.ld + t] = s[h];
-            if (p.dbg_iscores) p.dbg_iscores[(size_t)(bh0 + h) * g.ld + t] = A[h];
+        for (int u = 0; u < 8; ++u) {
+            const int tl = tid + kBlock * (k0 + u);
+            if (tl < n) {
+                const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
+                kb[u] = kb4[slot];
+                nc[u] = p.c.key_nc[slot];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int tl = tid + kBlock * (k0 + u);
+            if (tl < n) {
+                float s[GB];
+                int A[GB];
+                score_key<GB>(kb[u], nc[u], qs, s, A);
+#pragma unroll
+                for (int h = 0; h < GB; ++h) {
+                    const int e = score_bin(s[h], p.kbin);
+                    ebuf[h * g.CH + tl] = e;
+                    lm[h] = max(lm[h], e);
+                    if (DEBUG) {
+                        if (p.dbg_scores) p.dbg_scores[(size_t)(bh0 + h) * g.ld + t0 + tl] = s[h];
+                        if (p.dbg_iscores) p.dbg_iscores[(size_t)(bh0 + h) * g.ld + t0 + tl] = A[h];
+                    }
+                }
+            }
         }
     }
     if (!p.dl) return;
     block_reduce<GB>(lm, red, emax_s, MaxI());
-    if (threadIdx.x < GB) p.lmax[(size_t)(bh0 + threadIdx.x) * g.NC + chunk] = emax_s[threadIdx.x];
-    for (int tl = threadIdx.x; tl < n; tl += kBlock) {
+    if (tid < GB) p.lmax[(size_t)(bh0 + tid) * g.NC + chunk] = emax_s[tid];
+    for (int base = 8 * tid; base < n; base += 8 * kBlock) {
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-            const int d = emax_s[h] - ebuf[h * g.CH + tl];
-            p.dl[(size_t)(bh0 + h) * g.Lpad + t0 + tl] = (uint16_t)min(d, kBins);
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int a = base + 2 * q, c = a + 1;
+                const uint32_t da = a < n ? (uint32_t)min(emax_s[h] - ebuf[h * g.CH + a], kBins) : kBins;
+                const uint32_t dc = c < n ? (uint32_t)min(emax_s[h] - ebuf[h * g.CH + c], kBins) : kBins;
+                w[q] = da | (dc << 16);
+            }
+            *reinterpret_cast<uint4 *>(p.dl + (size_t)(bh0 + h) * g.Lpad + t0 + base) = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
 }
@@ -233,8 +301,8 @@ __global__ __launch_bounds__(256) void k_bin_scores(BinScoresParams p)
 }
 
 // Top bin of (b, h): max over the chunk top bins.
-__device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t *lmax, size_t bh,
-                                              int nch, int *red /* [4] */, int *out /* [1] */)
+__device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t *lmax, size_t bh, int nch,
+                                              int *red /* [4] */, int *out /* [1] */)
 {
     int m[1] = {-kBinClamp};
     for (int c = threadIdx.x; c < nch; c += kBlock) m[0] = max(m[0], lmax[bh * g.NC + c]);
@@ -242,107 +310,42 @@ __device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t
     return out[0];
 }
 
-// ---------------------------------------------------------------------------------------
-// Histogram pass: per (split, query head, sequence) block, counts of tokens per bin
-// distance d = (e_max - chunk top) + distance-to-chunk-top, for d < 8192.
-// ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_hist(HistParams p)
-{
-    __shared__ uint32_t hist[kBins];
-    __shared__ int delta[1024];
-    __shared__ int red[4];
-    __shared__ int top[1];
-    const DecodeGeom &g = p.g;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const size_t bh = (size_t)b * g.Hq + h;
-    const int L = g.seq_lens[b];
-    const int nch = (L + g.CH - 1) >> g.logCH;
-    for (int i = threadIdx.x; i < kBins; i += kBlock) hist[i] = 0u;
-    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
-    const int c0 = split * p.cps;
-    const int c1 = min(nch, c0 + p.cps);
-    for (int c = c0 + (int)threadIdx.x; c < c1; c += kBlock) delta[c - c0] = emax - p.lmax[bh * g.NC + c];
-    __syncthreads();
-    if (c0 < c1) {
-        const int tb = c0 << g.logCH;
-        const int te = min(L, c1 << g.logCH);
-        const uint16_t *row = p.dl + bh * g.Lpad;
-        // 8 tokens per thread-iteration (tb is a multiple of CH >= 256, so 16-byte aligned)
-        for (int t = tb + 8 * (int)threadIdx.x; t < te; t += 8 * kBlock) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(row + t);
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tt = t + e;
-                if (tt < te) {
-                    const int dloc = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                    const int d = delta[(tt >> g.logCH) - c0] + dloc;
-                    if (d < kBins) atomicAdd(&hist[d], 1u);
-                }
-            }
-        }
-    }
-    __syncthreads();
-    uint4 *dst = reinterpret_cast<uint4 *>(p.hist + (bh * p.nsplit + split) * kBins);
-    for (int i = threadIdx.x; i < kBins / 4; i += kBlock)
-        dst[i] = make_uint4(hist[4 * i], hist[4 * i + 1], hist[4 * i + 2], hist[4 * i + 3]);
-}
-
-// ---------------------------------------------------------------------------------------
-// Threshold: per (query head, sequence) block.  With W(d) = T[d mod 256] >> (d / 256),
-// T[j] = round(2^(32 - j/256)):  Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
-// b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p }, count = sum_{d <= b*} cnt[d].
-// Thread t owns bins 32t .. 32t+31.
-// ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_threshold(ThresholdParams p)
+// Top-p threshold of (b, h) from the per-split bin counts (256 threads, thread t owns bins
+// 32t .. 32t+31).  With W(d) = T[d mod 256] >> (d / 256), T[j] = round(2^(32 - j/256)):
+//   Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
+//   b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p },  count = sum_{d <= b*} cnt[d].
+__device__ void topp_threshold(const HistParams &p, size_t bh, int emax)
 {
     __shared__ uint64_t T[256];
     __shared__ uint64_t wsum[4];
-    __shared__ int red[4];
-    __shared__ int top[1];
     __shared__ int bstar_s;
     __shared__ int cnt_s[4];
-    const DecodeGeom &g = p.g;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const size_t bh = (size_t)b * g.Hq + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int L = g.seq_lens[b];
     T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
-    const int nch = (L + g.CH - 1) >> g.logCH;
-    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);  // includes barriers
-    if (L <= 0) {
-        if (tid == 0) {
-            p.sel[bh * 4 + 0] = 0;
-            p.sel[bh * 4 + 1] = -1;
-            p.sel[bh * 4 + 2] = 0;
-            if (p.dbg_count) p.dbg_count[bh] = 0;
-            if (p.dbg_bins) {
-                p.dbg_bins[bh * 2] = 0;
-                p.dbg_bins[bh * 2 + 1] = -1;
-            }
-        }
-        return;
-    }
     uint32_t cnt[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) cnt[k] = 0u;
     for (int s = 0; s < p.nsplit; ++s) {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + (bh * p.nsplit + s) * kBins + 32 * tid);
+        uint4 v[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint4 v = src[k];
-            cnt[4 * k] += v.x;
-            cnt[4 * k + 1] += v.y;
-            cnt[4 * k + 2] += v.z;
-            cnt[4 * k + 3] += v.w;
+        for (int k = 0; k < 4; ++k) v[k] = src[k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cnt[8 * k + 2 * q] += w[q] & 0xFFFFu;
+                cnt[8 * k + 2 * q + 1] += w[q] >> 16;
+            }
         }
     }
+    __syncthreads();  // T ready
     // d >> 8 is the same for all 32 bins of a thread
     const int shift = (32 * tid) >> 8;
     uint64_t mine = 0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) mine += (uint64_t)cnt[k] * (T[(32 * tid + k) & 255] >> shift);
-    // exclusive prefix of the per-thread masses
     uint64_t incl = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -396,10 +399,94 @@ __global__ __launch_bounds__(256) void k_threshold(ThresholdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Histogram pass: per (split, query head, sequence) block, counts of tokens per bin
+// distance d = (e_max - chunk top) + distance-to-chunk-top, d < 8192.  The last block of a
+// (b, h) to finish (arrival counter) computes the Top-p threshold from all splits.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_hist(HistParams p)
+{
+    __shared__ uint32_t hist[kBins];
+    __shared__ int delta[1024];
+    __shared__ int red[4];
+    __shared__ int top[1];
+    __shared__ int last;
+    const DecodeGeom &g = p.g;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const size_t bh = (size_t)b * g.Hq + h;
+    const int tid = threadIdx.x;
+    const int L = g.seq_lens[b];
+    const int nch = (L + g.CH - 1) >> g.logCH;
+    for (int i = tid; i < kBins; i += kBlock) hist[i] = 0u;
+    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
+    const int c0 = split * p.cps;
+    const int c1 = min(nch, c0 + p.cps);
+    for (int c = c0 + tid; c < c1; c += kBlock) delta[c - c0] = emax - p.lmax[bh * g.NC + c];
+    __syncthreads();
+    if (c0 < c1) {
+        const int tb = c0 << g.logCH;
+        const int te = min(L, c1 << g.logCH);
+        const uint16_t *row = p.dl + bh * g.Lpad;
+        // 8 tokens per 16-byte load, 4 loads in flight (tb is a multiple of CH >= 256)
+        for (int t = tb + 8 * tid; t < te; t += 32 * kBlock) {
+            uint4 raw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (t + 8 * kBlock * u < te) raw[u] = *reinterpret_cast<const uint4 *>(row + t + 8 * kBlock * u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int tu = t + 8 * kBlock * u;
+                if (tu < te) {
+                    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                    const int dc = delta[(tu >> g.logCH) - c0];  // 8 tokens share a chunk
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int d = dc + (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                        if (tu + e < te && d < kBins) atomicAdd(&hist[d], 1u);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    uint4 *dst = reinterpret_cast<uint4 *>(p.hist + (bh * p.nsplit + split) * kBins);
+    for (int i = tid; i < kBins / 8; i += kBlock) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = hist[8 * i + 2 * q] | (hist[8 * i + 2 * q + 1] << 16);
+        dst[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // publish this split, then let the last arriving block of (b, h) compute the threshold.
+    // After the barrier one thread's device-scope release (an L2 write-back) covers the
+    // whole block's stores; the last block's acquire (L1/L2 invalidate) precedes its reads.
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        last = (atomicAdd(&p.counters[bh], 1) == p.nsplit - 1);
+        if (last) __threadfence();
+    }
+    __syncthreads();
+    if (!last) return;
+    if (L <= 0) {
+        if (tid == 0) {
+            p.sel[bh * 4 + 0] = 0;
+            p.sel[bh * 4 + 1] = -1;
+            p.sel[bh * 4 + 2] = 0;
+            if (p.dbg_count) p.dbg_count[bh] = 0;
+            if (p.dbg_bins) {
+                p.dbg_bins[bh * 2] = 0;
+                p.dbg_bins[bh * 2 + 1] = -1;
+            }
+        }
+        return;
+    }
+    topp_threshold(p, bh, emax);
+}
+
 // Bin-distance threshold of a chunk: token kept when its distance to the chunk top bin is
 // <= b* - (e_max - chunk top).
-__device__ __forceinline__ int chunk_threshold(const int32_t *sel, const int32_t *lmax, size_t bh,
-                                               int NC, int chunk)
+__device__ __forceinline__ int chunk_threshold(const int32_t *sel, const int32_t *lmax, size_t bh, int NC,
+                                               int chunk)
 {
     const int emax = sel[bh * 4 + 0], bstar = sel[bh * 4 + 1];
     const long thr = (long)bstar - ((long)emax - (long)lmax[bh * NC + chunk]);
@@ -460,204 +547,309 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Attention over one chunk for GB query heads of one KV head.
+// Attention over one attention chunk (KA score chunks, KA * CH tokens) for GB query heads
+// of one KV head.
 //   SEL: tokens whose bin distance passes the head's Top-p threshold (Top-p decode);
 //   otherwise every token of the chunk (full softmax).
-// Phase 1 lists the chunk's tokens (SEL: ordered compaction of the kept ones), phase 2
-// scores them (binary x INT4), phase 3 turns scores into weights exp2((s - m) log2e/sqrt(D))
-// with the chunk max m, phase 4 accumulates weights x decoded 4-bit values (8 lanes per
-// token, 16 dims per lane; the zero point is accumulated once per group), and the block
-// writes (m, sum of weights, weighted sum) for the merge.
+// SEL first lists the kept tokens in order (one pass over the 16-bit bin distances, 8
+// tokens per thread).  Entries are then processed in batches: score them (binary x INT4),
+// update the running max m, turn scores into weights exp2((s - m) log2e/sqrt(D)) (earlier
+// batches are rescaled when m grows), and accumulate weights x decoded 4-bit values (16
+// lanes per entry, 8 dims per lane; the zero point is accumulated once per group).  The
+// block writes (m, sum of weights, weighted value sums) for the merge.
 // ---------------------------------------------------------------------------------------
 template <int GB, bool SEL>
 __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 {
-    __shared__ float wbuf[8192];               // scores, then weights: [entry][GB]
-    __shared__ uint32_t list[SEL ? 4096 : 1];  // entry -> token offset | head mask << 16
+    constexpr int kBatch = SEL ? 4096 / GB : 8192 / GB;  // entries per batch (scores in LDS)
+    __shared__ float wbuf[kBatch * GB];                   // scores, then weights: [entry][GB]
+    __shared__ uint32_t list[SEL ? 8192 : 1];             // entry -> token offset | head mask << 16
+    __shared__ int pages[kMaxChunkPages];
+    __shared__ uint32_t qsh[GB * 16];
+    __shared__ float4 qps[GB];
+    __shared__ int thr_s[SEL ? 4 * GB : 1];
     __shared__ float redf[4 * GB];
-    __shared__ float mh[GB], lh[GB];
-    __shared__ int wcnt[4];
+    __shared__ float mh[GB];
+    __shared__ int redi[4];
     const DecodeGeom &g = p.g;
-    const int chunk = blockIdx.x, b = blockIdx.z;
+    const int achunk = blockIdx.x, b = blockIdx.z;
     int kvh, hq0;
     block_heads(g, blockIdx.y, kvh, hq0);
     const int L = g.seq_lens[b];
-    const int t0 = chunk * g.CH;
+    const int CHa = g.CH * g.KA;
+    const int t0 = achunk * CHa;
     if (t0 >= L) return;
-    const int n = min(g.CH, L - t0);
+    const int n = min(CHa, L - t0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh0 = (size_t)b * g.Hq + hq0;
+    stage_query<GB>(p.qnib, p.qpar, (int)bh0, qsh, qps);
+    if (SEL && tid < g.KA * GB) {
+        const int sc = tid / GB, h = tid - sc * GB;
+        const int chunk = achunk * g.KA + sc;
+        thr_s[tid] = (chunk * g.CH < L) ? chunk_threshold(p.sel, p.lmax, bh0 + h, g.NC, chunk) : -1;
+    }
+    const int p0 = load_chunk_pages(g, p.c.logP, b, t0, n, pages);  // includes a barrier
+    QueryState<GB> qs;
+    read_query<GB>(qs, qsh, qps);
 
-    // ---- phase 1: entries
+    // ---- kept entries
     int nlist = n;
     if (SEL) {
-        int thr[GB];
-#pragma unroll
-        for (int h = 0; h < GB; ++h) thr[h] = chunk_threshold(p.sel, p.lmax, bh0 + h, g.NC, chunk);
         int base = 0;
-        for (int tb = 0; tb < n; tb += kBlock) {
-            const int tl = tb + tid;
-            uint32_t mask = 0;
-            if (tl < n) {
+        for (int c0 = 0; c0 < n; c0 += 8 * kBlock) {
+            const int tl0 = c0 + 8 * tid;
+            uint32_t m8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m8[e] = 0u;
+            if (tl0 < n) {
+                const int sc = tl0 >> g.logCH;  // the 8 tokens share a score chunk
+                uint4 raw[GB];
 #pragma unroll
                 for (int h = 0; h < GB; ++h)
-                    if ((int)p.dl[(bh0 + h) * g.Lpad + t0 + tl] <= thr[h]) mask |= 1u << h;
+                    raw[h] = *reinterpret_cast<const uint4 *>(p.dl + (bh0 + h) * g.Lpad + t0 + tl0);
+#pragma unroll
+                for (int h = 0; h < GB; ++h) {
+                    const int thr = thr_s[sc * GB + h];
+                    const uint32_t w[4] = {raw[h].x, raw[h].y, raw[h].z, raw[h].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int dloc = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                        if (tl0 + e < n && dloc <= thr) m8[e] |= 1u << h;
+                    }
+                }
             }
-            const uint64_t m = __ballot(mask != 0);
-            if (lane == 0) wcnt[wave] = __popcll(m);
-            __syncthreads();
-            int off = base;
-            for (int w = 0; w < wave; ++w) off += wcnt[w];
-            if (mask) list[off + __popcll(m & lanemask_lt())] = (uint32_t)tl | (mask << 16);
-            base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-            __syncthreads();
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cnt += m8[e] ? 1 : 0;
+            int total;
+            int off = base + block_exscan(cnt, redi, &total);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (m8[e]) list[off++] = (uint32_t)(tl0 + e) | (m8[e] << 16);
+            base += total;
         }
+        __syncthreads();
         nlist = base;
     }
 
-    // ---- phase 2: scores
-    QueryState<GB> qs;
-    load_query<GB>(qs, p.qpl, p.qpar, (int)bh0);
-    float mloc[GB];
-#pragma unroll
-    for (int h = 0; h < GB; ++h) mloc[h] = -INFINITY;
     const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
-    for (int e = tid; e < nlist; e += kBlock) {
-        int tl = e;
-        uint32_t mask = (1u << GB) - 1u;
-        if (SEL) {
-            const uint32_t ent = list[e];
-            tl = (int)(ent & 0xFFFFu);
-            mask = ent >> 16;
-        }
-        const size_t slot = token_slot(g, p.c, b, kvh, t0 + tl);
-        float s[GB];
-        int A[GB];
-        score_key<GB>(kb4[slot], p.c.key_nc[slot], qs, s, A);
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-            const float v = ((mask >> h) & 1u) ? s[h] : -INFINITY;
-            wbuf[e * GB + h] = v;
-            mloc[h] = fmaxf(mloc[h], v);
-        }
-    }
-    block_reduce<GB>(mloc, redf, mh, MaxF());
-
-    // ---- phase 3: weights
-    float lloc[GB];
-#pragma unroll
-    for (int h = 0; h < GB; ++h) lloc[h] = 0.0f;
-    for (int e = tid; e < nlist; e += kBlock) {
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-            const float v = wbuf[e * GB + h];
-            const float w = (v == -INFINITY) ? 0.0f : exp2f((v - mh[h]) * p.klog);
-            wbuf[e * GB + h] = w;
-            lloc[h] += w;
-        }
-    }
-    block_reduce<GB>(lloc, redf, lh, SumF());
-
-    // ---- phase 4: weighted sum of decoded values (8 lanes per entry, 16 dims per lane)
-    const int sub = lane & 7;        // dims 16*sub .. 16*sub+15
-    const int eg = lane >> 3;        // entry within the wave-iteration
-    float acc[GB][16];
-    float zacc[GB];
+    const int sub = lane & 15;  // dims 8*sub .. 8*sub+7
+    const int eg = lane >> 4;   // entry within the wave-iteration
+    const int gv = p.c.Gv;
+    const int grp = (8 * sub) / gv;
+    const int ngrp = kD / gv;
+    float acc[GB][8];
+    float zacc[GB], lloc[GB], mrun[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
         zacc[h] = 0.0f;
+        lloc[h] = 0.0f;
+        mrun[h] = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[h][j] = 0.0f;
+        for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
     }
-    const int gv = p.c.Gv;
-    const int grp = (16 * sub) / gv;
-    const int ngrp = kD / gv;
-    for (int e = wave * 8 + eg; e < nlist; e += 32) {
-        const int tl = SEL ? (int)(list[e] & 0xFFFFu) : e;
-        const size_t slot = token_slot(g, p.c, b, kvh, t0 + tl);
-        const uint2 cw = *reinterpret_cast<const uint2 *>(p.c.val_codes + slot * (kD / 2) + 8 * sub);
-        const uint32_t szw = p.c.val_sz[slot * ngrp + grp];
-        const float sf = half_bits_to_float(szw & 0xFFFFu);
-        const float zf = half_bits_to_float(szw >> 16);
-        float c[16];
-        const uint32_t lo0 = cw.x & 0x0F0F0F0Fu, hi0 = (cw.x >> 4) & 0x0F0F0F0Fu;
-        const uint32_t lo1 = cw.y & 0x0F0F0F0Fu, hi1 = (cw.y >> 4) & 0x0F0F0F0Fu;
+
+    for (int bs = 0; bs < nlist; bs += kBatch) {
+        const int nb = min(kBatch, nlist - bs);
+        // ---- scores of the batch, 8 keys in flight per thread
+        float mloc[GB];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            c[2 * m] = (float)((lo0 >> (8 * m)) & 0xFFu);
-            c[2 * m + 1] = (float)((hi0 >> (8 * m)) & 0xFFu);
-            c[8 + 2 * m] = (float)((lo1 >> (8 * m)) & 0xFFu);
-            c[8 + 2 * m + 1] = (float)((hi1 >> (8 * m)) & 0xFFu);
+        for (int h = 0; h < GB; ++h) mloc[h] = -INFINITY;
+        for (int e0 = tid; e0 < nb; e0 += 4 * kBlock) {
+            uint4 kb[4];
+            uint32_t nc[4], msk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + kBlock * u;
+                if (e < nb) {
+                    int tl = bs + e;
+                    msk[u] = (1u << GB) - 1u;
+                    if (SEL) {
+                        const uint32_t ent = list[bs + e];
+                        tl = (int)(ent & 0xFFFFu);
+                        msk[u] = ent >> 16;
+                    }
+                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
+                    kb[u] = kb4[slot];
+                    nc[u] = p.c.key_nc[slot];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + kBlock * u;
+                if (e < nb) {
+                    float sc[GB];
+                    int A[GB];
+                    score_key<GB>(kb[u], nc[u], qs, sc, A);
+#pragma unroll
+                    for (int h = 0; h < GB; ++h) {
+                        const float v = ((msk[u] >> h) & 1u) ? sc[h] : -INFINITY;
+                        wbuf[e * GB + h] = v;
+                        mloc[h] = fmaxf(mloc[h], v);
+                    }
+                }
+            }
         }
+        block_reduce<GB>(mloc, redf, mh, MaxF());
+        // ---- running max, rescale earlier batches, weights
+        float mnew[GB];
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-            const float w = wbuf[e * GB + h];
-            const float ws = w * sf;
-            zacc[h] = fmaf(w, zf, zacc[h]);
+            mnew[h] = fmaxf(mrun[h], mh[h]);
+            const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew[h]) * p.klog);
+            if (scale != 1.0f) {
+                zacc[h] *= scale;
+                lloc[h] *= scale;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[h][j] = fmaf(ws, c[j], acc[h][j]);
+                for (int j = 0; j < 8; ++j) acc[h][j] *= scale;
+            }
+            mrun[h] = mnew[h];
         }
-    }
-    // reduce over the 8 entry lanes (lane bits 3..5) of each wave
+        for (int e = tid; e < nb; e += kBlock) {
 #pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
+            for (int h = 0; h < GB; ++h) {
+                const float v = wbuf[e * GB + h];
+                const float w = (v == -INFINITY) ? 0.0f : exp2f((v - mnew[h]) * p.klog);
+                wbuf[e * GB + h] = w;
+                lloc[h] += w;
+            }
+        }
+        __syncthreads();
+        // ---- weighted sums of the decoded values, 4 entries in flight per lane group
+        constexpr int U = 4;
+        for (int e0 = wave * 4 + eg; e0 < nb; e0 += 16 * U) {
+            uint32_t cw[U], szw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + 16 * u;
+                if (e < nb) {
+                    const int tl = SEL ? (int)(list[bs + e] & 0xFFFFu) : bs + e;
+                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
+                    cw[u] = *reinterpret_cast<const uint32_t *>(p.c.val_codes + slot * (kD / 2) + 4 * sub);
+                    szw[u] = p.c.val_sz[slot * ngrp + grp];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + 16 * u;
+                if (e < nb) {
+                    const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
+                    const float zf = half_bits_to_float(szw[u] >> 16);
+                    float c[8];
+                    const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        c[2 * m] = (float)((lo >> (8 * m)) & 0xFFu);
+                        c[2 * m + 1] = (float)((hi >> (8 * m)) & 0xFFu);
+                    }
+#pragma unroll
+                    for (int h = 0; h < GB; ++h) {
+                        const float w = wbuf[e * GB + h];
+                        const float ws = w * sf;
+                        zacc[h] = fmaf(w, zf, zacc[h]);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(ws, c[j], acc[h][j]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // wbuf is rewritten by the next batch
+    }
+
+    // ---- weight sums, then the value sums reduced over entry lanes and waves
+    __shared__ float lsum[GB];
+    block_reduce<GB>(lloc, redf, lsum, SumF());
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             zacc[h] += __shfl_xor(zacc[h], o);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[h][j] += __shfl_xor(acc[h][j], o);
+            for (int j = 0; j < 8; ++j) acc[h][j] += __shfl_xor(acc[h][j], o);
         }
     }
-    __syncthreads();  // wbuf reused for the cross-wave reduction
     if (eg == 0) {
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) wbuf[((wave * GB + h) * 8 + sub) * 17 + j] = acc[h][j];
-            wbuf[((wave * GB + h) * 8 + sub) * 17 + 16] = zacc[h];
+            for (int j = 0; j < 8; ++j) wbuf[((wave * GB + h) * 16 + sub) * 9 + j] = acc[h][j];
+            wbuf[((wave * GB + h) * 16 + sub) * 9 + 8] = zacc[h];
         }
     }
     __syncthreads();
+    const size_t pidx = (bh0 * g.NCA + achunk);  // partial of head bh0 (+ h * NCA)
     for (int o = tid; o < GB * kD; o += kBlock) {
         const int h = o / kD, d = o - h * kD;
-        const int sb = d >> 4, j = d & 15;
+        const int sb = d >> 3, j = d & 7;
         float v = 0.0f, z = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            v += wbuf[((w * GB + h) * 8 + sb) * 17 + j];
-            z += wbuf[((w * GB + h) * 8 + sb) * 17 + 16];
+            v += wbuf[((w * GB + h) * 16 + sb) * 9 + j];
+            z += wbuf[((w * GB + h) * 16 + sb) * 9 + 8];
         }
-        p.po[((bh0 + h) * g.NC + chunk) * kD + d] = v + z;
+        p.po[(pidx + (size_t)h * g.NCA) * kD + d] = v + z;
     }
     if (tid < GB) {
-        p.pm[(bh0 + tid) * g.NC + chunk] = mh[tid];
-        p.pl[(bh0 + tid) * g.NC + chunk] = lh[tid];
+        p.pm[pidx + (size_t)tid * g.NCA] = mrun[tid];
+        p.pl[pidx + (size_t)tid * g.NCA] = lsum[tid];
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Split-K merge: out = sum_c a_c o_c / sum_c a_c l_c, a_c = exp2((m_c - M) log2e/sqrt(D)).
+// Split-K merge, one 256-thread block per (query head, sequence):
+//   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
+// Thread (d, half) sums the chunks of one parity for dim d; loads are independent.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void k_merge(MergeParams p)
+__global__ __launch_bounds__(256) void k_merge(MergeParams p)
 {
+    __shared__ float alpha[4096];
+    __shared__ float redf[4];
+    __shared__ float outm[1];
+    __shared__ float part[kD];
     const DecodeGeom &g = p.g;
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const size_t bh = (size_t)b * g.Hq + h;
     const int L = g.seq_lens[b];
-    const int nch = L > 0 ? (L + g.CH - 1) >> g.logCH : 0;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, p.pm[bh * g.NC + c]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-        for (int c = 0; c < nch; ++c) {
-            const float m = p.pm[bh * g.NC + c];
-            if (m == -INFINITY) continue;
-            const float a = exp2f((m - M) * p.klog);
-            num = fmaf(a, p.po[(bh * g.NC + c) * kD + d], num);
-            den = fmaf(a, p.pl[bh * g.NC + c], den);
-        }
+    const int CHa = g.CH * g.KA;
+    const int nch = L > 0 ? (L + CHa - 1) / CHa : 0;
+    float m[1] = {-INFINITY};
+    for (int c = tid; c < nch; c += kBlock) m[0] = fmaxf(m[0], p.pm[bh * g.NCA + c]);
+    block_reduce<1>(m, redf, outm, MaxF());
+    const float M = outm[0];
+    float den[1] = {0.0f};
+    for (int c = tid; c < nch; c += kBlock) {
+        const float mc = p.pm[bh * g.NCA + c];
+        const float a = (mc == -INFINITY) ? 0.0f : exp2f((mc - M) * p.klog);
+        alpha[c] = a;
+        den[0] = fmaf(a, p.pl[bh * g.NCA + c], den[0]);
     }
-    p.out[bh * kD + d] = den > 0.0f ? num / den : 0.0f;
+    block_reduce<1>(den, redf, outm, SumF());  // barriers also publish alpha
+    const float D = outm[0];
+    const int d = tid & (kD - 1), half = tid >> 7;
+    float num = 0.0f;
+    const float *po = p.po + bh * g.NCA * kD + d;
+    int c = half;
+    for (; c + 6 < nch; c += 8) {
+        const float v0 = po[(size_t)c * kD], v1 = po[(size_t)(c + 2) * kD];
+        const float v2 = po[(size_t)(c + 4) * kD], v3 = po[(size_t)(c + 6) * kD];
+        num = fmaf(alpha[c], v0, num);
+        num = fmaf(alpha[c + 2], v1, num);
+        num = fmaf(alpha[c + 4], v2, num);
+        num = fmaf(alpha[c + 6], v3, num);
+    }
+    for (; c < nch; c += 2) num = fmaf(alpha[c], po[(size_t)c * kD], num);
+    if (half == 1) part[d] = num;
+    __syncthreads();
+    if (half == 0) {
+        num += part[d];
+        p.out[bh * kD + d] = D > 0.0f ? num / D : 0.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_zero(int32_t *p, int n)
+{
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
 }  // namespace
@@ -675,10 +867,20 @@ hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
 hipError_t launch_score(const ScoreParams &p, hipStream_t s)
 {
     const dim3 grid(p.g.NC, p.g.Hkv * p.g.nsub, p.g.B);
+    const bool dbg = p.dbg_scores || p.dbg_iscores;
     switch (p.g.GB) {
-    case 1: hipLaunchKernelGGL(k_score<1>, grid, dim3(kBlock), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(k_score<2>, grid, dim3(kBlock), 0, s, p); break;
-    default: hipLaunchKernelGGL(k_score<4>, grid, dim3(kBlock), 0, s, p); break;
+    case 1:
+        if (dbg) hipLaunchKernelGGL((k_score<1, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((k_score<1, false>), grid, dim3(kBlock), 0, s, p);
+        break;
+    case 2:
+        if (dbg) hipLaunchKernelGGL((k_score<2, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((k_score<2, false>), grid, dim3(kBlock), 0, s, p);
+        break;
+    default:
+        if (dbg) hipLaunchKernelGGL((k_score<4, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((k_score<4, false>), grid, dim3(kBlock), 0, s, p);
+        break;
     }
     return hipGetLastError();
 }
@@ -695,12 +897,6 @@ hipError_t launch_hist(const HistParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_threshold(const ThresholdParams &p, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_threshold, dim3(p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
-    return hipGetLastError();
-}
-
 hipError_t launch_select(const SelectParams &p, hipStream_t s)
 {
     const dim3 grid(p.g.NC, p.g.Hq, p.g.B);
@@ -713,7 +909,7 @@ hipError_t launch_select(const SelectParams &p, hipStream_t s)
 
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 {
-    const dim3 grid(p.g.NC, p.g.Hkv * p.g.nsub, p.g.B);
+    const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
     const dim3 blk(kBlock);
     if (select) {
         switch (p.g.GB) {
@@ -731,9 +927,15 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_zero(int32_t *p, int n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_zero, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_merge, dim3(p.g.Hq, p.g.B), dim3(kD), 0, s, p);
+    hipLaunchKernelGGL(k_merge, dim3(p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -87,35 +87,46 @@ __device__ __forceinline__ uint64_t lanemask_lt()
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int score_bin(float s, float kbin)
 {
-    float x = s * kbin;
-    if (!(x >= -(float)kBinClamp)) return -kBinClamp;
-    if (x >= (float)kBinClamp) return kBinClamp;
+    const float x = fminf(fmaxf(s * kbin, -(float)kBinClamp), (float)kBinClamp);  // NaN -> bottom
     return (int)floorf(x);
 }
 
 // ---------------------------------------------------------------------------------------
-// Encoded query of up to GB heads that share one KV head: 4 bit-planes x 4 words of the
-// int4 codes per head, c0 = v_l/sqrt(D), c1 = delta/sqrt(D), and the code sum.
+// Encoded query of up to GB heads that share one KV head.  The int4 codes are kept as
+// 16 words per head in the order the 8 x 4-bit dot product (v_dot8_u32_u4) consumes them:
+// nib[4w + k] holds, in nibble m = 0..7, the code of dim 32w + 4m + k.  A key word w
+// spread with (w >> k) & 0x11111111 puts the sign bit of the same dims in the same nibbles,
+// so  sum_{w,k} dot8(spread(w, k), nib[4w + k]) = sum_r bit_r u_r.
+// c0 = v_l/sqrt(D), c1 = delta/sqrt(D), sumu = sum of the codes.
 // ---------------------------------------------------------------------------------------
 template <int GB>
 struct QueryState {
-    uint32_t plane[GB][4][kKeyWords];
+    uint32_t nib[GB][16];
     float c0[GB], c1[GB];
     int sumu[GB];
 };
 
-// qpl: [B*Hq][16] words (plane-major), qpar: [B*Hq][4] = (c0, c1, sumu bits, 0).
+// Block-wide staging of the GB heads' query state through LDS (qsh: GB*16 words, qps: GB
+// float4).  Reading it back from LDS keeps one copy per lane in vector registers; as
+// uniform scalar loads the 64 words of 4 heads would overflow the scalar register file.
+// Caller synchronizes between stage_query and read_query.
 template <int GB>
-__device__ __forceinline__ void load_query(QueryState<GB> &qs, const uint32_t *__restrict__ qpl,
-                                           const float4 *__restrict__ qpar, int bh0)
+__device__ __forceinline__ void stage_query(const uint32_t *__restrict__ qnib, const float4 *__restrict__ qpar,
+                                            int bh0, uint32_t *qsh, float4 *qps)
+{
+    const int t = threadIdx.x;
+    if (t < GB * 16) qsh[t] = qnib[(size_t)(bh0 + t / 16) * 16 + (t & 15)];
+    if (t < GB) qps[t] = qpar[bh0 + t];
+}
+
+template <int GB>
+__device__ __forceinline__ void read_query(QueryState<GB> &qs, const uint32_t *qsh, const float4 *qps)
 {
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int w = 0; w < kKeyWords; ++w) qs.plane[h][j][w] = qpl[(bh0 + h) * 16 + j * 4 + w];
-        float4 p = qpar[bh0 + h];
+        for (int i = 0; i < 16; ++i) qs.nib[h][i] = qsh[h * 16 + i];
+        const float4 p = qps[h];
         qs.c0[h] = p.x;
         qs.c1[h] = p.y;
         qs.sumu[h] = __float_as_int(p.z);
@@ -123,28 +134,34 @@ __device__ __forceinline__ void load_query(QueryState<GB> &qs, const uint32_t *_
 }
 
 // Proxy score of one cached key against GB query heads (binary x INT4, then the binary32
-// combine):  A = 2 * sum_j 2^j popcount(bits & plane_j) - sumu  (= sum_r s_r u_r),
+// combine):  A = 2 * sum_r bit_r u_r - sumu  (= sum_r s_r u_r, s_r = +-1),
 // P = 2 * popcount(bits) - D  (= sum_r s_r),  score = fmaf(c1, A, c0 * P) * (norm / corr).
 template <int GB>
 __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const QueryState<GB> &qs,
                                           float *s, int *A)
 {
     const uint32_t w[4] = {kb.x, kb.y, kb.z, kb.w};
+    uint32_t x[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * i + k] = (w[i] >> k) & 0x11111111u;
     const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                    __builtin_popcount(w[3]);
     const float fP = (float)(2 * pc - kD);
     const float r = half_bits_to_float(nc & 0xFFFFu) / half_bits_to_float(nc >> 16);
+    // the GB accumulation chains are interleaved so that consecutive dot products are
+    // independent
+    uint32_t ip[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) ip[h] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int h = 0; h < GB; ++h) ip[h] = __builtin_amdgcn_udot8(x[i], qs.nib[h][i], ip[h], false);
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
-        int ip = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int t = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) t += __builtin_popcount(w[q] & qs.plane[h][j][q]);
-            ip += t << j;
-        }
-        const int a = 2 * ip - qs.sumu[h];
+        const int a = 2 * (int)ip[h] - qs.sumu[h];
         A[h] = a;
         const float cp = qs.c0[h] * fP;
         s[h] = fmaf(qs.c1[h], (float)a, cp) * r;

@@ -35,8 +35,9 @@ struct QprepParams {
     const void *rot;
     const float *q;        // [B*Hq][128]
     int BH;
-    uint32_t *qpl;         // [B*Hq][16]
+    uint32_t *qnib;        // [B*Hq][16] int4 codes in dot8 order
     float4 *qpar;          // [B*Hq]
+    int32_t *counters;     // nullable [B*Hq]: zeroed here (arrival counters of later kernels)
     uint8_t *dbg_codes;    // nullable [B*Hq][128]
     float *dbg_params;     // nullable [B*Hq][4]
     int32_t *dbg_sumu;     // nullable [B*Hq]
@@ -52,6 +53,8 @@ struct DecodeGeom {
     int logCH;
     int NC;       // chunks per sequence (max)
     int Lpad;     // NC * CH
+    int KA;       // score chunks per attention block (Top-p), 1 for full softmax
+    int NCA;      // attention chunks per sequence (max) = ceil(NC / KA)
     int ld;       // max_seq_len (row stride of debug/score/index arrays)
     const int32_t *seq_lens;
     const int32_t *page_table;
@@ -61,7 +64,7 @@ struct DecodeGeom {
 struct ScoreParams {
     DecodeGeom g;
     CacheView c;
-    const uint32_t *qpl;
+    const uint32_t *qnib;
     const float4 *qpar;
     float kbin;
     uint16_t *dl;          // nullable [B*Hq][Lpad]: bin distance to the chunk's top bin
@@ -79,20 +82,15 @@ struct BinScoresParams {
     int32_t *lmax;
 };
 
+// Histogram of bin distances, then (last block of each (b, h)) the Top-p threshold.
 struct HistParams {
     DecodeGeom g;
     int nsplit, cps;       // splits per (b,h), chunks per split
+    uint32_t pfx;          // rint(p * 2^24)
     const uint16_t *dl;
     const int32_t *lmax;
-    uint32_t *hist;        // [B*Hq][nsplit][8192]
-};
-
-struct ThresholdParams {
-    DecodeGeom g;
-    int nsplit;
-    uint32_t pfx;          // rint(p * 2^24)
-    const int32_t *lmax;
-    const uint32_t *hist;
+    uint16_t *hist;        // [B*Hq][nsplit][8192] per-split counts (a split has < 65536 tokens)
+    int32_t *counters;     // [B*Hq] arrival counters, zero on entry
     int32_t *sel;          // [B*Hq][4] = (e_max, b*, count, 0)
     int32_t *dbg_count;    // nullable [B*Hq]
     int32_t *dbg_bins;     // nullable [B*Hq][2]
@@ -110,7 +108,7 @@ struct SelectParams {
 struct AttendParams {
     DecodeGeom g;
     CacheView c;
-    const uint32_t *qpl;
+    const uint32_t *qnib;
     const float4 *qpar;
     float klog;            // log2(e) / sqrt(D)
     // Top-p selection (select mode only)
@@ -118,9 +116,9 @@ struct AttendParams {
     const int32_t *lmax;
     const int32_t *sel;
     // partial results per (b, h, chunk)
-    float *pm;             // [B*Hq][NC] running max score
-    float *pl;             // [B*Hq][NC] sum of weights
-    float *po;             // [B*Hq][NC][128] weighted value sums
+    float *pm;             // [B*Hq][NCA] max score of the chunk's attended tokens
+    float *pl;             // [B*Hq][NCA] sum of weights
+    float *po;             // [B*Hq][NCA][128] weighted value sums
 };
 
 struct MergeParams {
@@ -135,9 +133,10 @@ hipError_t launch_qprep(const QprepParams &p, hipStream_t s);
 hipError_t launch_score(const ScoreParams &p, hipStream_t s);
 hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s);
 hipError_t launch_hist(const HistParams &p, hipStream_t s);
-hipError_t launch_threshold(const ThresholdParams &p, hipStream_t s);
 hipError_t launch_select(const SelectParams &p, hipStream_t s);
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, hipStream_t s);
+// n int32 zeros (a fill kernel, so that the call stays free of memset nodes under capture)
+hipError_t launch_zero(int32_t *p, int n, hipStream_t s);
 
 }  // namespace kvc

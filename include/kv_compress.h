@@ -101,14 +101,13 @@ typedef struct kv_cache {
  *            stage_events[2s+1] after them, for each stage s it runs (others are left
  *            alone), so a caller can time every stage with hipEventElapsedTime. */
 enum {
-    KV_STAGE_QUERY = 0,      /* query rotation, int4 codes, bit-planes */
-    KV_STAGE_SCORE = 1,      /* Top-p: proxy scores of all tokens -> bin distances */
-    KV_STAGE_HIST = 2,       /* Top-p: per-bin token counts */
-    KV_STAGE_THRESHOLD = 3,  /* Top-p: threshold bin */
-    KV_STAGE_SELECT = 4,     /* Top-p, only when sel_idx is requested: ordered index lists */
-    KV_STAGE_ATTEND = 5,     /* scores of the attended tokens, softmax, 4-bit value sums */
-    KV_STAGE_MERGE = 6,      /* merge of the per-chunk partial results */
-    KV_NUM_STAGES = 7
+    KV_STAGE_QUERY = 0,   /* query rotation, int4 codes, bit-planes */
+    KV_STAGE_SCORE = 1,   /* Top-p: proxy scores of all tokens -> bin distances */
+    KV_STAGE_HIST = 2,    /* Top-p: per-bin token counts, then the threshold bin */
+    KV_STAGE_SELECT = 3,  /* Top-p, only when sel_idx is requested: ordered index lists */
+    KV_STAGE_ATTEND = 4,  /* scores of the attended tokens, softmax, 4-bit value sums */
+    KV_STAGE_MERGE = 5,   /* merge of the per-chunk partial results */
+    KV_NUM_STAGES = 6
 };
 typedef struct kv_debug {
     uint8_t *q_codes;
