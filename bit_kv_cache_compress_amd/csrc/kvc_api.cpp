@@ -37,6 +37,9 @@ int ilog2(long x)
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Tokens per Top-p score chunk (one wave of the score kernel, 8 tokens per lane).
+constexpr int kTopPChunk = 512;
+
 // ---------------------------------------------------------------------------------------
 // Decode plan
 // ---------------------------------------------------------------------------------------
@@ -48,39 +51,45 @@ struct Plan {
     size_t total;
 };
 
-// Largest chunk: the per-block LDS score buffer holds CH x GB floats (32 KB) and a Top-p
-// block lists up to CH token offsets in 16 bits.
+// Largest chunk of a full-softmax attention block: its LDS score buffer holds CH x GB
+// floats (32 KB).
 int chunk_cap(int GB, bool topp)
 {
-    int cap = 8192 / GB;
-    if (topp && cap > 4096) cap = 4096;
-    return cap;
+    return topp ? kTopPChunk * 16 : 8192 / GB;
 }
 
-// At most this many chunks per sequence (the merge keeps one weight per chunk in LDS).
+// At most this many attention chunks per sequence (the merge keeps one weight per chunk in
+// LDS).
 constexpr int kMaxChunks = 4096;
 
-// Chunk size: the largest power of two CH in [256, cap] that still gives at least 2048
-// blocks (8 per compute unit) over (chunk, KV-head group, sequence), and no fewer than
-// max_len / 4096 tokens.
-void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
+// Geometry.
+//  Full softmax: chunks of CH tokens, the largest power of two in [256, 8192/GB] that still
+//  gives at least 2048 blocks (8 per compute unit) over (chunk, KV-head group, sequence) and
+//  no more than 4096 chunks; one attention block per chunk (KA = 1).
+//  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention block
+//  (one query head, Top-p keeps few tokens per head) covers KA <= 16 score chunks, as many
+//  as still give >= 1024 blocks.
+void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp, int Hq)
 {
-    const int cap = chunk_cap(GB, topp);
-    int CH = cap;
-    const long units = (long)B * rows_per_seq;
-    while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048 && (long)(CH >> 1) * kMaxChunks >= max_len) CH >>= 1;
+    int CH, KA = 1;
+    if (topp) {
+        CH = kTopPChunk;
+        const int NC = (max_len + CH - 1) / CH;
+        const long heads = (long)B * Hq;
+        while (KA < 16 && heads * ((NC + 2 * KA - 1) / (2 * KA)) >= 1024) KA *= 2;
+        while ((long)(NC + KA - 1) / KA > kMaxChunks) KA *= 2;
+    } else {
+        CH = chunk_cap(GB, false);
+        const long units = (long)B * rows_per_seq;
+        while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048 && (long)(CH >> 1) * kMaxChunks >= max_len)
+            CH >>= 1;
+    }
     pl.g.CH = CH;
     pl.g.logCH = ilog2(CH);
     pl.g.NC = (max_len + CH - 1) / CH;
     if (pl.g.NC < 1) pl.g.NC = 1;
     pl.g.Lpad = pl.g.NC * CH;
     pl.g.ld = max_len;
-    // Top-p attention blocks cover KA score chunks (at most 8192 tokens, the entry list of
-    // a block), as long as that still leaves >= 512 blocks: most of their tokens are skipped,
-    // so fewer, larger blocks cost fewer dependent memory rounds.
-    int KA = 1;
-    if (topp)
-        while (KA < 4 && (long)CH * KA * 2 <= 8192 && units * ((pl.g.NC + 2 * KA - 1) / (2 * KA)) >= 512) KA *= 2;
     pl.g.KA = KA;
     pl.g.NCA = (pl.g.NC + KA - 1) / KA;
 }
@@ -139,7 +148,7 @@ int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, f
         return fail(KV_ERR_UNSUPPORTED, "GQA group Hq/Hkv = %d: supported groups are 1, 2, 4, 8", G);
     if (!(top_p > 0.0f)) return fail(KV_ERR_ARG, "top_p must be > 0 (got %g)", (double)top_p);
     const int GB = G < 4 ? G : 4;
-    const long limit = (long)chunk_cap(GB, top_p < 1.0f) * kMaxChunks;
+    const long limit = (long)chunk_cap(GB, top_p < 1.0f) * kMaxChunks;  // merge weights fit in LDS
     if (max_seq_len > limit)
         return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld for this head grouping", max_seq_len, limit);
     return KV_OK;
@@ -157,7 +166,7 @@ void make_plan(Plan &pl, int B, int Hq, int Hkv, int max_seq_len, float top_p)
     pl.g.G = G;
     pl.g.GB = GB;
     pl.g.nsub = G / GB;
-    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, GB, pl.topp);
+    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, GB, pl.topp, Hq);
     plan_layout(pl, B * Hq);
 }
 
@@ -350,6 +359,11 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
 
     kvc::AttendParams ap;
     ap.g = pl.g;
+    if (pl.topp) {
+        // Top-p keeps a different small set of tokens per query head: one head per block
+        ap.g.GB = 1;
+        ap.g.nsub = ap.g.G;
+    }
     ap.c = cv;
     ap.qnib = qnib;
     ap.qpar = qpar;
@@ -389,7 +403,7 @@ size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld)
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, 1, true);
+    plan_geometry(pl, B, Hq, ld, 1, true, Hq);
     plan_layout(pl, B * Hq);
     return pl.total;
 }
@@ -417,7 +431,7 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, 1, true);
+    plan_geometry(pl, B, Hq, ld, 1, true, Hq);
     plan_layout(pl, B * Hq);
     pl.g.seq_lens = seq_lens;
     pl.g.page_table = nullptr;

@@ -189,22 +189,21 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
 }
 
 // ---------------------------------------------------------------------------------------
-// Score pass (Top-p first pass, and debug scores): per (chunk, KV head, sequence) block,
-// the proxy score of every token of the chunk for GB query heads.  Writes the bin distance
-// to the chunk's top bin (uint16, saturated at 8192: no token that far below a chunk's top
-// can be selected, since the threshold distance is < 8192) and the chunk's top bin.
-// Thread t scores tokens t, t + 256, ... (coalesced 16-byte key loads, 8 in flight), then
-// stores the distances of 8 consecutive tokens per 16-byte store.
+// Score pass (Top-p first pass, and debug scores): one wave per (chunk, KV head, sequence)
+// computes the proxy score of every token of the chunk for GB query heads.  Writes the bin
+// distance to the chunk's top bin (uint16, saturated at 8192: no token that far below a
+// chunk's top can be selected, since the threshold distance is < 8192) and the chunk's top
+// bin.  Lane l scores tokens l, l + 64, ... (coalesced 16-byte key loads, 8 in flight), then
+// stores the distances of 8 consecutive tokens per 16-byte store.  One-wave blocks need no
+// block barrier, so the load, compute and store phases of different waves overlap freely.
 // ---------------------------------------------------------------------------------------
-template <int GB, bool DEBUG>
-__global__ __launch_bounds__(256) void k_score(ScoreParams p)
+template <int GB, bool DEBUG, int CHMAX>
+__global__ __launch_bounds__(64) void k_score(ScoreParams p)
 {
-    __shared__ int ebuf[8192];
-    __shared__ int pages[kMaxChunkPages];
+    __shared__ int ebuf[GB * CHMAX];
+    __shared__ int pages[CHMAX / 16 + 1];
     __shared__ uint32_t qsh[GB * 16];
     __shared__ float4 qps[GB];
-    __shared__ int red[4 * GB];
-    __shared__ int emax_s[GB];
     const DecodeGeom &g = p.g;
     const int chunk = blockIdx.x, b = blockIdx.z;
     int kvh, hq0;
@@ -213,23 +212,26 @@ __global__ __launch_bounds__(256) void k_score(ScoreParams p)
     const int t0 = chunk * g.CH;
     if (t0 >= L) return;
     const int n = min(g.CH, L - t0);
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const int bh0 = b * g.Hq + hq0;
-    stage_query<GB>(p.qnib, p.qpar, bh0, qsh, qps);
-    const int p0 = load_chunk_pages(g, p.c.logP, b, t0, n, pages);  // includes a barrier
+    if (lane < GB * 16) qsh[lane] = p.qnib[(size_t)(bh0 + lane / 16) * 16 + (lane & 15)];
+    if (lane < GB) qps[lane] = p.qpar[bh0 + lane];
+    const int p0 = t0 >> p.c.logP;
+    const int np = ((t0 + n - 1) >> p.c.logP) - p0 + 1;
+    for (int i = lane; i < np; i += 64) pages[i] = g.page_table[(size_t)b * g.max_pages + p0 + i];
+    __syncthreads();
     QueryState<GB> qs;
     read_query<GB>(qs, qsh, qps);
     int lm[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) lm[h] = -kBinClamp;
     const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
-    const int nk = (n + kBlock - 1) / kBlock;
-    for (int k0 = 0; k0 < nk; k0 += 8) {
+    for (int k0 = 0; k0 < n; k0 += 8 * 64) {
         uint4 kb[8];
         uint32_t nc[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int tl = tid + kBlock * (k0 + u);
+            const int tl = k0 + lane + 64 * u;
             if (tl < n) {
                 const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
                 kb[u] = kb4[slot];
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreParams p)
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int tl = tid + kBlock * (k0 + u);
+            const int tl = k0 + lane + 64 * u;
             if (tl < n) {
                 float s[GB];
                 int A[GB];
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreParams p)
 #pragma unroll
                 for (int h = 0; h < GB; ++h) {
                     const int e = score_bin(s[h], p.kbin);
-                    ebuf[h * g.CH + tl] = e;
+                    ebuf[h * CHMAX + tl] = e;
                     lm[h] = max(lm[h], e);
                     if (DEBUG) {
                         if (p.dbg_scores) p.dbg_scores[(size_t)(bh0 + h) * g.ld + t0 + tl] = s[h];
@@ -257,17 +259,22 @@ __global__ __launch_bounds__(256) void k_score(ScoreParams p)
         }
     }
     if (!p.dl) return;
-    block_reduce<GB>(lm, red, emax_s, MaxI());
-    if (tid < GB) p.lmax[(size_t)(bh0 + tid) * g.NC + chunk] = emax_s[tid];
-    for (int base = 8 * tid; base < n; base += 8 * kBlock) {
+#pragma unroll
+    for (int h = 0; h < GB; ++h) lm[h] = wave_max_i(lm[h]);
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GB; ++h) p.lmax[(size_t)(bh0 + h) * g.NC + chunk] = lm[h];
+    }
+    __syncthreads();  // ebuf written by other lanes
+    for (int base = 8 * lane; base < n; base += 8 * 64) {
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int a = base + 2 * q, c = a + 1;
-                const uint32_t da = a < n ? (uint32_t)min(emax_s[h] - ebuf[h * g.CH + a], kBins) : kBins;
-                const uint32_t dc = c < n ? (uint32_t)min(emax_s[h] - ebuf[h * g.CH + c], kBins) : kBins;
+                const uint32_t da = a < n ? (uint32_t)min(lm[h] - ebuf[h * CHMAX + a], kBins) : kBins;
+                const uint32_t dc = c < n ? (uint32_t)min(lm[h] - ebuf[h * CHMAX + c], kBins) : kBins;
                 w[q] = da | (dc << 16);
             }
             *reinterpret_cast<uint4 *>(p.dl + (size_t)(bh0 + h) * g.Lpad + t0 + base) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -427,14 +434,15 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
         const int tb = c0 << g.logCH;
         const int te = min(L, c1 << g.logCH);
         const uint16_t *row = p.dl + bh * g.Lpad;
-        // 8 tokens per 16-byte load, 4 loads in flight (tb is a multiple of CH >= 256)
-        for (int t = tb + 8 * tid; t < te; t += 32 * kBlock) {
-            uint4 raw[4];
+        // 8 tokens per 16-byte load, 16 loads in flight (tb is a multiple of CH >= 256)
+        constexpr int U = 16;
+        for (int t = tb + 8 * tid; t < te; t += 8 * kBlock * U) {
+            uint4 raw[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < U; ++u)
                 if (t + 8 * kBlock * u < te) raw[u] = *reinterpret_cast<const uint4 *>(row + t + 8 * kBlock * u);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int tu = t + 8 * kBlock * u;
                 if (tu < te) {
                     const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
@@ -567,7 +575,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
     __shared__ int pages[kMaxChunkPages];
     __shared__ uint32_t qsh[GB * 16];
     __shared__ float4 qps[GB];
-    __shared__ int thr_s[SEL ? 4 * GB : 1];
+    __shared__ int thr_s[SEL ? 16 * GB : 1];
     __shared__ float redf[4 * GB];
     __shared__ float mh[GB];
     __shared__ int redi[4];
@@ -867,20 +875,22 @@ hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
 hipError_t launch_score(const ScoreParams &p, hipStream_t s)
 {
     const dim3 grid(p.g.NC, p.g.Hkv * p.g.nsub, p.g.B);
+    const dim3 blk(64);
     const bool dbg = p.dbg_scores || p.dbg_iscores;
-    switch (p.g.GB) {
-    case 1:
-        if (dbg) hipLaunchKernelGGL((k_score<1, true>), grid, dim3(kBlock), 0, s, p);
-        else hipLaunchKernelGGL((k_score<1, false>), grid, dim3(kBlock), 0, s, p);
-        break;
-    case 2:
-        if (dbg) hipLaunchKernelGGL((k_score<2, true>), grid, dim3(kBlock), 0, s, p);
-        else hipLaunchKernelGGL((k_score<2, false>), grid, dim3(kBlock), 0, s, p);
-        break;
-    default:
-        if (dbg) hipLaunchKernelGGL((k_score<4, true>), grid, dim3(kBlock), 0, s, p);
-        else hipLaunchKernelGGL((k_score<4, false>), grid, dim3(kBlock), 0, s, p);
-        break;
+    // Top-p chunks are 512 tokens (8 per lane); the debug pass of a full-softmax decode runs
+    // on that decode's larger chunks
+    if (!dbg && p.g.CH <= 512) {
+        switch (p.g.GB) {
+        case 1: hipLaunchKernelGGL((k_score<1, false, 512>), grid, blk, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_score<2, false, 512>), grid, blk, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_score<4, false, 512>), grid, blk, 0, s, p); break;
+        }
+    } else {
+        switch (p.g.GB) {
+        case 1: hipLaunchKernelGGL((k_score<1, true, 8192>), grid, blk, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_score<2, true, 4096>), grid, blk, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_score<4, true, 2048>), grid, blk, 0, s, p); break;
+        }
     }
     return hipGetLastError();
 }
