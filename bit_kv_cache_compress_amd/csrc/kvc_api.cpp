@@ -37,9 +37,6 @@ int ilog2(long x)
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Tokens per Top-p score chunk (one wave of the score kernel, 8 tokens per lane).
-constexpr int kTopPChunk = 512;
-
 // ---------------------------------------------------------------------------------------
 // Decode plan
 // ---------------------------------------------------------------------------------------
@@ -47,7 +44,7 @@ struct Plan {
     kvc::DecodeGeom g;
     bool topp;
     int nsplit, cps;
-    size_t off_qpl, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_ctr, off_pm, off_pl, off_po;
+    size_t off_qpl, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po;
     size_t total;
 };
 
@@ -55,7 +52,7 @@ struct Plan {
 // floats (32 KB).
 int chunk_cap(int GB, bool topp)
 {
-    return topp ? kTopPChunk * 16 : 8192 / GB;
+    return topp ? kvc::kTopPChunk * 16 : 8192 / GB;
 }
 
 // At most this many attention chunks per sequence (the merge keeps one weight per chunk in
@@ -73,7 +70,7 @@ void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool 
 {
     int CH, KA = 1;
     if (topp) {
-        CH = kTopPChunk;
+        CH = kvc::kTopPChunk;
         const int NC = (max_len + CH - 1) / CH;
         const long heads = (long)B * Hq;
         while (KA < 16 && heads * ((NC + 2 * KA - 1) / (2 * KA)) >= 1024) KA *= 2;
@@ -128,10 +125,9 @@ void plan_layout(Plan &pl, int BH)
         pl.off_hist = take((size_t)BH * nsplit * 8192 * 2);
         pl.off_sel = take((size_t)BH * 4 * 4);
         pl.off_cnt = take((size_t)BH * NC * 4);
-        pl.off_ctr = take((size_t)BH * 4);
     } else {
         pl.nsplit = pl.cps = 0;
-        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = pl.off_ctr = 0;
+        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = 0;
     }
     pl.total = o;
 }
@@ -180,6 +176,8 @@ int check_cache(const kv_cache *c)
     if (!is_pow2(c->page_size) || c->page_size < 16)
         return fail(KV_ERR_UNSUPPORTED, "page_size %d: must be a power of two >= 16", c->page_size);
     if (c->num_pages <= 0) return fail(KV_ERR_ARG, "num_pages must be positive");
+    if ((long)c->num_pages * c->num_kv_heads * c->page_size > 0xFFFFFFFFL)
+        return fail(KV_ERR_UNSUPPORTED, "num_pages * num_kv_heads * page_size above 2^32 - 1 slots");
     if (c->rot_kind != KV_ROT_DENSE && c->rot_kind != KV_ROT_HADAMARD)
         return fail(KV_ERR_ARG, "rot_kind %d is not KV_ROT_DENSE or KV_ROT_HADAMARD", c->rot_kind);
     if (!c->rot || !c->key_bits || !c->key_nc || !c->val_codes || !c->val_sz)
@@ -299,7 +297,6 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     qp.BH = BH;
     qp.qnib = qnib;
     qp.qpar = qpar;
-    qp.counters = pl.topp ? at<int32_t>(workspace, pl.off_ctr) : nullptr;
     qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
@@ -334,7 +331,6 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
         hp.dl = sp.dl;
         hp.lmax = sp.lmax;
         hp.hist = at<uint16_t>(workspace, pl.off_hist);
-        hp.counters = at<int32_t>(workspace, pl.off_ctr);
         hp.sel = at<int32_t>(workspace, pl.off_sel);
         hp.dbg_count = dbg ? dbg->sel_count : nullptr;
         hp.dbg_bins = dbg ? dbg->sel_bins : nullptr;
@@ -454,12 +450,9 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     hp.dl = bp.dl;
     hp.lmax = bp.lmax;
     hp.hist = at<uint16_t>(workspace, pl.off_hist);
-    hp.counters = at<int32_t>(workspace, pl.off_ctr);
     hp.sel = at<int32_t>(workspace, pl.off_sel);
     hp.dbg_count = sel_count;
     hp.dbg_bins = nullptr;
-    e = kvc::launch_zero(hp.counters, B * Hq, stream);
-    if (e != hipSuccess) return hip_fail(e, "zero launch");
     e = kvc::launch_hist(hp, stream);
     if (e != hipSuccess) return hip_fail(e, "histogram launch");
     kvc::SelectParams sel;

@@ -20,7 +20,8 @@ namespace kvc {
 
 namespace {
 
-constexpr int kMaxChunkPages = 513;  // CH / P + 1 with CH <= 8192, P >= 16
+constexpr int kMaxAttendChunk = 8192;  // tokens of an attention chunk
+constexpr int kMaxChunkPages = kMaxAttendChunk / 16 + 1;  // page ids of a chunk (P >= 16)
 
 // First query head of block (hb = kv head * nsub + sub) and its KV head.
 __device__ __forceinline__ void block_heads(const DecodeGeom &g, int hb, int &kvh, int &hq0)
@@ -66,25 +67,6 @@ __device__ __forceinline__ void block_reduce(T (&v)[GB], T *red /* [4][GB] */, T
     __syncthreads();
 }
 
-// Exclusive prefix sum over the 256 threads of a block; *total gets the sum.
-__device__ __forceinline__ int block_exscan(int v, int *red /* [4] */, int *total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) red[wave] = x;
-    __syncthreads();
-    int before = x - v;
-    for (int w = 0; w < wave; ++w) before += red[w];
-    *total = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    return before;
-}
-
 struct MaxI { __device__ int operator()(int a, int b) const { return a > b ? a : b; } };
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 struct SumF { __device__ float operator()(float a, float b) const { return a + b; } };
@@ -107,7 +89,6 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
     const int bh = blockIdx.x, r = threadIdx.x;
     const int lane = r & 63, wave = r >> 6;
     const float *q = p.q + (size_t)bh * kD;
-    if (p.counters && r == 0) p.counters[bh] = 0;
     float x;
     if (p.rot_kind == 0) {
         const uint4 *Rr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + r * kD);
@@ -282,6 +263,97 @@ __global__ __launch_bounds__(64) void k_score(ScoreParams p)
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Top-p score pass (no debug output): one wave per 512-token chunk, KV head and sequence.
+// Lane l scores tokens l + 64 u (u < 8; 16-byte key loads coalesce over the wave).  Page ids
+// are turned into 32-bit slot bases in LDS once, so a token's slot is one LDS read and an
+// add.  There is no per-token branch: past the sequence end a lane re-reads the last token
+// and its bin is forced below every real one.  The bins stay in registers; after the wave
+// max, each lane stores its tokens' 16-bit distances (128-byte coalesced stores), and every
+// position of the chunk is written (kBins past the end).
+// ---------------------------------------------------------------------------------------
+template <int GB>
+__global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
+{
+    constexpr int CH = kTopPChunk;
+    constexpr int U = CH / 64;  // tokens per lane
+    constexpr int kNone = -2 * kBinClamp;
+    __shared__ uint32_t pbase[CH / 16 + 1];
+    __shared__ uint32_t qsh[GB * 16];
+    __shared__ float4 qps[GB];
+    const DecodeGeom &g = p.g;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    int kvh, hq0;
+    block_heads(g, blockIdx.y, kvh, hq0);
+    const int L = g.seq_lens[b];
+    const int t0 = chunk * CH;
+    if (t0 >= L) return;
+    const int n = min(CH, L - t0);
+    const int lane = threadIdx.x;
+    const int bh0 = b * g.Hq + hq0;
+    if (lane < GB * 16) qsh[lane] = p.qnib[(size_t)(bh0 + lane / 16) * 16 + (lane & 15)];
+    if (lane < GB) qps[lane] = p.qpar[bh0 + lane];
+    const int logP = p.c.logP;
+    const int p0 = t0 >> logP;
+    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
+    for (int i = lane; i < np; i += 64)
+        pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
+                   << logP;
+    __syncthreads();
+    QueryState<GB> qs;
+    read_query<GB>(qs, qsh, qps);
+    uint32_t slot[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int t = t0 + min(lane + 64 * u, n - 1);
+        slot[u] = pbase[(t >> logP) - p0] + (uint32_t)(t & ((1 << logP) - 1));
+    }
+    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
+    int e[U][GB];
+    int lm[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) lm[h] = kNone;
+    // two halves of U/2 tokens: the second half's loads overlap the first half's arithmetic
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        uint4 kb[U / 2];
+        uint32_t nc[U / 2];
+#pragma unroll
+        for (int v = 0; v < U / 2; ++v) {
+            kb[v] = kb4[slot[half * (U / 2) + v]];
+            nc[v] = p.c.key_nc[slot[half * (U / 2) + v]];
+        }
+#pragma unroll
+        for (int v = 0; v < U / 2; ++v) {
+            const int u = half * (U / 2) + v;
+            float s[GB];
+            int A[GB];
+            score_key<GB>(kb[v], nc[v], qs, s, A);
+            // min() rather than a select, so that the score is computed on every lane
+            // instead of behind a branch
+            const int lim = lane + 64 * u < n ? INT_MAX : kNone;
+#pragma unroll
+            for (int h = 0; h < GB; ++h) {
+                const int ev = min(score_bin(s[h], p.kbin), lim);
+                e[u][h] = ev;
+                lm[h] = max(lm[h], ev);
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h) lm[h] = wave_max_i(lm[h]);
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GB; ++h) p.lmax[(size_t)(bh0 + h) * g.NC + chunk] = lm[h];
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        uint16_t *row = p.dl + (size_t)(bh0 + h) * g.Lpad + t0 + lane;
+#pragma unroll
+        for (int u = 0; u < U; ++u) row[64 * u] = (uint16_t)min(lm[h] - e[u][h], kBins);
+    }
+}
+
 // Bins of caller-supplied scores (kv_topp_select): one block per (chunk, query head, seq).
 __global__ __launch_bounds__(256) void k_bin_scores(BinScoresParams p)
 {
@@ -321,7 +393,7 @@ __device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t
 // 32t .. 32t+31).  With W(d) = T[d mod 256] >> (d / 256), T[j] = round(2^(32 - j/256)):
 //   Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
 //   b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p },  count = sum_{d <= b*} cnt[d].
-__device__ void topp_threshold(const HistParams &p, size_t bh, int emax)
+__device__ void topp_threshold(const HistParams &p, size_t bh, int emax, int nsplit_used)
 {
     __shared__ uint64_t T[256];
     __shared__ uint64_t wsum[4];
@@ -332,18 +404,21 @@ __device__ void topp_threshold(const HistParams &p, size_t bh, int emax)
     uint32_t cnt[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) cnt[k] = 0u;
-    for (int s = 0; s < p.nsplit; ++s) {
+    for (int s = 0; s < nsplit_used; s += 2) {
         const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + (bh * p.nsplit + s) * kBins + 32 * tid);
-        uint4 v[4];
+        const bool two = s + 1 < nsplit_used;
+        uint4 v[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = src[k];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 4; k < 8; ++k) v[k] = two ? src[kBins / 8 + k - 4] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
             const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                cnt[8 * k + 2 * q] += w[q] & 0xFFFFu;
-                cnt[8 * k + 2 * q + 1] += w[q] >> 16;
+                cnt[8 * (k & 3) + 2 * q] += w[q] & 0xFFFFu;
+                cnt[8 * (k & 3) + 2 * q + 1] += w[q] >> 16;
             }
         }
     }
@@ -413,24 +488,24 @@ __device__ void topp_threshold(const HistParams &p, size_t bh, int emax)
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_hist(HistParams p)
 {
-    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t hist[kBins + 1];  // + a bin for tokens that are not counted
     __shared__ int delta[1024];
     __shared__ int red[4];
     __shared__ int top[1];
-    __shared__ int last;
     const DecodeGeom &g = p.g;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t bh = (size_t)b * g.Hq + h;
     const int tid = threadIdx.x;
     const int L = g.seq_lens[b];
-    const int nch = (L + g.CH - 1) >> g.logCH;
-    for (int i = tid; i < kBins; i += kBlock) hist[i] = 0u;
-    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
+    const int nch = L > 0 ? (L + g.CH - 1) >> g.logCH : 0;
     const int c0 = split * p.cps;
+    if (c0 >= nch) return;  // the threshold pass reads only the splits that hold tokens
     const int c1 = min(nch, c0 + p.cps);
+    for (int i = tid; i <= kBins; i += kBlock) hist[i] = 0u;
+    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
     for (int c = c0 + tid; c < c1; c += kBlock) delta[c - c0] = emax - p.lmax[bh * g.NC + c];
     __syncthreads();
-    if (c0 < c1) {
+    {
         const int tb = c0 << g.logCH;
         const int te = min(L, c1 << g.logCH);
         const uint16_t *row = p.dl + bh * g.Lpad;
@@ -450,7 +525,7 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int d = dc + (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                        if (tu + e < te && d < kBins) atomicAdd(&hist[d], 1u);
+                        atomicAdd(&hist[(tu + e < te && d < kBins) ? d : kBins], 1u);
                     }
                 }
             }
@@ -464,17 +539,19 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
         for (int q = 0; q < 4; ++q) w[q] = hist[8 * i + 2 * q] | (hist[8 * i + 2 * q + 1] << 16);
         dst[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    // publish this split, then let the last arriving block of (b, h) compute the threshold.
-    // After the barrier one thread's device-scope release (an L2 write-back) covers the
-    // whole block's stores; the last block's acquire (L1/L2 invalidate) precedes its reads.
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        last = (atomicAdd(&p.counters[bh], 1) == p.nsplit - 1);
-        if (last) __threadfence();
-    }
-    __syncthreads();
-    if (!last) return;
+}
+
+// Top-p threshold of each (b, h) from the split counts: one block per (query head, sequence).
+// A kernel of its own, so that the split counts reach it through the kernel boundary rather
+// than through device-scope fences in every histogram block.
+__global__ __launch_bounds__(256) void k_thresh(HistParams p)
+{
+    __shared__ int red[4];
+    __shared__ int top[1];
+    const DecodeGeom &g = p.g;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const size_t bh = (size_t)b * g.Hq + h;
+    const int L = g.seq_lens[b];
     if (L <= 0) {
         if (tid == 0) {
             p.sel[bh * 4 + 0] = 0;
@@ -488,7 +565,9 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
         }
         return;
     }
-    topp_threshold(p, bh, emax);
+    const int nch = (L + g.CH - 1) >> g.logCH;
+    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
+    topp_threshold(p, bh, emax, (nch + p.cps - 1) / p.cps);
 }
 
 // Bin-distance threshold of a chunk: token kept when its distance to the chunk top bin is
@@ -555,94 +634,41 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Attention over one attention chunk (KA score chunks, KA * CH tokens) for GB query heads
-// of one KV head.
-//   SEL: tokens whose bin distance passes the head's Top-p threshold (Top-p decode);
-//   otherwise every token of the chunk (full softmax).
-// SEL first lists the kept tokens in order (one pass over the 16-bit bin distances, 8
-// tokens per thread).  Entries are then processed in batches: score them (binary x INT4),
-// update the running max m, turn scores into weights exp2((s - m) log2e/sqrt(D)) (earlier
-// batches are rescaled when m grows), and accumulate weights x decoded 4-bit values (16
-// lanes per entry, 8 dims per lane; the zero point is accumulated once per group).  The
-// block writes (m, sum of weights, weighted value sums) for the merge.
+// Full-softmax attention over one chunk of CH tokens for GB query heads of one KV head.
+// Keys are processed in batches: score them (binary x INT4), update the running max m,
+// turn scores into weights exp2((s - m) log2e/sqrt(D)) (earlier batches are rescaled when
+// m grows), and accumulate weights x decoded 4-bit values (16 lanes per key, 8 dims per
+// lane; the zero point is accumulated once per group).  The block writes (m, sum of
+// weights, weighted value sums) for the merge.
 // ---------------------------------------------------------------------------------------
-template <int GB, bool SEL>
+template <int GB>
 __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 {
-    constexpr int kBatch = SEL ? 4096 / GB : 8192 / GB;  // entries per batch (scores in LDS)
-    __shared__ float wbuf[kBatch * GB];                   // scores, then weights: [entry][GB]
-    __shared__ uint32_t list[SEL ? 8192 : 1];             // entry -> token offset | head mask << 16
+    constexpr int kBatch = 8192 / GB;  // keys per batch (scores in LDS)
+    __shared__ float wbuf[kBatch * GB];  // scores, then weights: [key][GB]
     __shared__ int pages[kMaxChunkPages];
     __shared__ uint32_t qsh[GB * 16];
     __shared__ float4 qps[GB];
-    __shared__ int thr_s[SEL ? 16 * GB : 1];
     __shared__ float redf[4 * GB];
     __shared__ float mh[GB];
-    __shared__ int redi[4];
     const DecodeGeom &g = p.g;
     const int achunk = blockIdx.x, b = blockIdx.z;
     int kvh, hq0;
     block_heads(g, blockIdx.y, kvh, hq0);
     const int L = g.seq_lens[b];
-    const int CHa = g.CH * g.KA;
-    const int t0 = achunk * CHa;
+    const int t0 = achunk * g.CH;
     if (t0 >= L) return;
-    const int n = min(CHa, L - t0);
+    const int n = min(g.CH, L - t0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh0 = (size_t)b * g.Hq + hq0;
     stage_query<GB>(p.qnib, p.qpar, (int)bh0, qsh, qps);
-    if (SEL && tid < g.KA * GB) {
-        const int sc = tid / GB, h = tid - sc * GB;
-        const int chunk = achunk * g.KA + sc;
-        thr_s[tid] = (chunk * g.CH < L) ? chunk_threshold(p.sel, p.lmax, bh0 + h, g.NC, chunk) : -1;
-    }
     const int p0 = load_chunk_pages(g, p.c.logP, b, t0, n, pages);  // includes a barrier
     QueryState<GB> qs;
     read_query<GB>(qs, qsh, qps);
 
-    // ---- kept entries
-    int nlist = n;
-    if (SEL) {
-        int base = 0;
-        for (int c0 = 0; c0 < n; c0 += 8 * kBlock) {
-            const int tl0 = c0 + 8 * tid;
-            uint32_t m8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m8[e] = 0u;
-            if (tl0 < n) {
-                const int sc = tl0 >> g.logCH;  // the 8 tokens share a score chunk
-                uint4 raw[GB];
-#pragma unroll
-                for (int h = 0; h < GB; ++h)
-                    raw[h] = *reinterpret_cast<const uint4 *>(p.dl + (bh0 + h) * g.Lpad + t0 + tl0);
-#pragma unroll
-                for (int h = 0; h < GB; ++h) {
-                    const int thr = thr_s[sc * GB + h];
-                    const uint32_t w[4] = {raw[h].x, raw[h].y, raw[h].z, raw[h].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int dloc = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                        if (tl0 + e < n && dloc <= thr) m8[e] |= 1u << h;
-                    }
-                }
-            }
-            int cnt = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cnt += m8[e] ? 1 : 0;
-            int total;
-            int off = base + block_exscan(cnt, redi, &total);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (m8[e]) list[off++] = (uint32_t)(tl0 + e) | (m8[e] << 16);
-            base += total;
-        }
-        __syncthreads();
-        nlist = base;
-    }
-
     const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
     const int sub = lane & 15;  // dims 8*sub .. 8*sub+7
-    const int eg = lane >> 4;   // entry within the wave-iteration
+    const int eg = lane >> 4;   // key within the wave-iteration
     const int gv = p.c.Gv;
     const int grp = (8 * sub) / gv;
     const int ngrp = kD / gv;
@@ -657,27 +683,20 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
         for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
     }
 
-    for (int bs = 0; bs < nlist; bs += kBatch) {
-        const int nb = min(kBatch, nlist - bs);
-        // ---- scores of the batch, 8 keys in flight per thread
+    for (int bs = 0; bs < n; bs += kBatch) {
+        const int nb = min(kBatch, n - bs);
+        // ---- scores of the batch, 4 keys in flight per thread
         float mloc[GB];
 #pragma unroll
         for (int h = 0; h < GB; ++h) mloc[h] = -INFINITY;
         for (int e0 = tid; e0 < nb; e0 += 4 * kBlock) {
             uint4 kb[4];
-            uint32_t nc[4], msk[4];
+            uint32_t nc[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = e0 + kBlock * u;
                 if (e < nb) {
-                    int tl = bs + e;
-                    msk[u] = (1u << GB) - 1u;
-                    if (SEL) {
-                        const uint32_t ent = list[bs + e];
-                        tl = (int)(ent & 0xFFFFu);
-                        msk[u] = ent >> 16;
-                    }
-                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
+                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + bs + e);
                     kb[u] = kb4[slot];
                     nc[u] = p.c.key_nc[slot];
                 }
@@ -691,9 +710,8 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
                     score_key<GB>(kb[u], nc[u], qs, sc, A);
 #pragma unroll
                     for (int h = 0; h < GB; ++h) {
-                        const float v = ((msk[u] >> h) & 1u) ? sc[h] : -INFINITY;
-                        wbuf[e * GB + h] = v;
-                        mloc[h] = fmaxf(mloc[h], v);
+                        wbuf[e * GB + h] = sc[h];
+                        mloc[h] = fmaxf(mloc[h], sc[h]);
                     }
                 }
             }
@@ -723,7 +741,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
             }
         }
         __syncthreads();
-        // ---- weighted sums of the decoded values, 4 entries in flight per lane group
+        // ---- weighted sums of the decoded values, 4 keys in flight per lane group
         constexpr int U = 4;
         for (int e0 = wave * 4 + eg; e0 < nb; e0 += 16 * U) {
             uint32_t cw[U], szw[U];
@@ -731,8 +749,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
             for (int u = 0; u < U; ++u) {
                 const int e = e0 + 16 * u;
                 if (e < nb) {
-                    const int tl = SEL ? (int)(list[bs + e] & 0xFFFFu) : bs + e;
-                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
+                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + bs + e);
                     cw[u] = *reinterpret_cast<const uint32_t *>(p.c.val_codes + slot * (kD / 2) + 4 * sub);
                     szw[u] = p.c.val_sz[slot * ngrp + grp];
                 }
@@ -764,7 +781,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
         __syncthreads();  // wbuf is rewritten by the next batch
     }
 
-    // ---- weight sums, then the value sums reduced over entry lanes and waves
+    // ---- weight sums, then the value sums reduced over key lanes and waves
     __shared__ float lsum[GB];
     block_reduce<GB>(lloc, redf, lsum, SumF());
 #pragma unroll
@@ -800,6 +817,212 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
     if (tid < GB) {
         p.pm[pidx + (size_t)tid * g.NCA] = mrun[tid];
         p.pl[pidx + (size_t)tid * g.NCA] = lsum[tid];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Top-p attention over one attention chunk (KA score chunks, at most 8192 tokens) for one
+// query head.  Top-p keeps a small, head-specific set of tokens, so the block first lists
+// the kept tokens of its chunk in ascending order (one pass over the 16-bit bin distances,
+// 32 tokens per thread, a single block-wide scan of four packed 16-bit counts), then works
+// through the list in batches of 256 entries.  For a batch every load is issued up front:
+// one key per thread (sign words and norm/correction word) and, per 16-lane group, the
+// value words of 16 entries (4 bytes of codes, i.e. 8 dims, and the group's scale/zero word
+// per lane).  Scores, the running max and the weights follow, then the weighted value sums
+// from registers.  The chunk costs two dependent rounds of HBM reads (distances with the
+// query and page ids, then the kept entries) when it keeps at most 256 tokens.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_attend_topp(AttendParams p)
+{
+    constexpr int kNB = 256;  // entries per batch
+    constexpr int kVU = kNB / 16;  // entries per 16-lane group and batch
+    __shared__ uint16_t list[kMaxAttendChunk];
+    __shared__ float wbuf[kNB];
+    __shared__ int pages[kMaxChunkPages];
+    __shared__ uint32_t qsh[16];
+    __shared__ float4 qps[1];
+    __shared__ int thr_s[16];
+    __shared__ uint64_t scan_s[4];
+    __shared__ float redf[4];
+    __shared__ float accs[4][16][9];
+    const DecodeGeom &g = p.g;
+    const int achunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int kvh = h / g.G;
+    const int L = g.seq_lens[b];
+    const int CHa = g.CH * g.KA;
+    const int t0 = achunk * CHa;
+    if (t0 >= L) return;
+    const int n = min(CHa, L - t0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)b * g.Hq + h;
+
+    // ---- round 1: distances (tokens 8 tid + 2048 j .. + 7), query, thresholds, page ids
+    uint4 raw[4];
+    const uint16_t *row = p.dl + bh * g.Lpad + t0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tl = 8 * tid + 2048 * j;
+        if (tl < n) raw[j] = *reinterpret_cast<const uint4 *>(row + tl);
+    }
+    stage_query<1>(p.qnib, p.qpar, (int)bh, qsh, qps);
+    if (tid < g.KA) {
+        const int chunk = achunk * g.KA + tid;
+        thr_s[tid] = (chunk * g.CH < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
+    }
+    const int p0 = t0 >> p.c.logP;
+    const int np = ((t0 + n - 1) >> p.c.logP) - p0 + 1;
+    for (int i = tid; i < np; i += kBlock) pages[i] = g.page_table[(size_t)b * g.max_pages + p0 + i];
+    __syncthreads();
+
+    // ---- kept tokens, listed in ascending order
+    uint32_t keep[4];
+    uint64_t cnt4 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tl = 8 * tid + 2048 * j;
+        uint32_t m = 0u;
+        if (tl < n) {
+            const int thr = thr_s[tl >> g.logCH];  // the 8 tokens share a score chunk
+            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                m |= (tl + e < n && d <= thr) ? (1u << e) : 0u;
+            }
+        }
+        keep[j] = m;
+        cnt4 |= (uint64_t)__builtin_popcount(m) << (16 * j);
+    }
+    // block-wide exclusive scan of the four 16-bit counts (a field never exceeds 2048)
+    uint64_t incl = cnt4;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) scan_s[wave] = incl;
+    __syncthreads();
+    uint64_t before = incl - cnt4;
+    for (int w = 0; w < wave; ++w) before += scan_s[w];
+    const uint64_t total = scan_s[0] + scan_s[1] + scan_s[2] + scan_s[3];
+    int nlist = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int off = nlist + (int)((before >> (16 * j)) & 0xFFFFu);
+        uint32_t m = keep[j];
+        while (m) {
+            const int e = __builtin_ctz(m);
+            m &= m - 1u;
+            list[off++] = (uint16_t)(8 * tid + 2048 * j + e);
+        }
+        nlist += (int)((total >> (16 * j)) & 0xFFFFu);
+    }
+    __syncthreads();
+
+    QueryState<1> qs;
+    read_query<1>(qs, qsh, qps);
+    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
+    const int sub = tid & 15;  // dims 8*sub .. 8*sub+7
+    const int eg = tid >> 4;   // entries eg + 16 u of a batch
+    const int gv = p.c.Gv;
+    const int grp = (8 * sub) / gv;
+    const int ngrp = kD / gv;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    float zacc = 0.0f, lloc = 0.0f, mrun = -INFINITY;
+
+    for (int bs = 0; bs < nlist; bs += kNB) {
+        const int nb = min(kNB, nlist - bs);
+        // ---- round 2: the batch's keys and value words
+        uint4 kb = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t nc = 0u;
+        if (tid < nb) {
+            const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + (int)list[bs + tid]);
+            kb = kb4[slot];
+            nc = p.c.key_nc[slot];
+        }
+        uint32_t cw[kVU], szw[kVU];
+#pragma unroll
+        for (int u = 0; u < kVU; ++u) {
+            const int e = eg + 16 * u;
+            if (e < nb) {
+                const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + (int)list[bs + e]);
+                cw[u] = *reinterpret_cast<const uint32_t *>(p.c.val_codes + slot * (kD / 2) + 4 * sub);
+                szw[u] = p.c.val_sz[slot * ngrp + grp];
+            }
+        }
+        float s = -INFINITY;
+        if (tid < nb) {
+            int A;
+            score_key<1>(kb, nc, qs, &s, &A);
+        }
+        const float wm = wave_max(s);
+        if (lane == 0) redf[wave] = wm;
+        __syncthreads();
+        const float mb = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+        const float mnew = fmaxf(mrun, mb);
+        const float scale = (mrun == -INFINITY) ? 0.0f : exp2f((mrun - mnew) * p.klog);
+        if (scale != 1.0f) {
+            zacc *= scale;
+            lloc *= scale;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] *= scale;
+        }
+        mrun = mnew;
+        const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
+        lloc += w;
+        wbuf[tid] = w;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kVU; ++u) {
+            const int e = eg + 16 * u;
+            if (e < nb) {
+                const float we = wbuf[e];
+                const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
+                const float zf = half_bits_to_float(szw[u] >> 16);
+                const float ws = we * sf;
+                zacc = fmaf(we, zf, zacc);
+                const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    acc[2 * m] = fmaf(ws, (float)((lo >> (8 * m)) & 0xFFu), acc[2 * m]);
+                    acc[2 * m + 1] = fmaf(ws, (float)((hi >> (8 * m)) & 0xFFu), acc[2 * m + 1]);
+                }
+            }
+        }
+        __syncthreads();  // wbuf and redf are rewritten by the next batch
+    }
+
+    // ---- weight sum, then the value sums reduced over the 16 entry groups
+    const float lw = wave_sum(lloc);
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        zacc += __shfl_xor(zacc, o);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += __shfl_xor(acc[j], o);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) accs[wave][lane][j] = acc[j];
+        accs[wave][lane][8] = zacc;
+    }
+    if (lane == 0) redf[wave] = lw;
+    __syncthreads();
+    const size_t pidx = bh * g.NCA + achunk;
+    if (tid < kD) {
+        const int sb = tid >> 3, j = tid & 7;
+        float v = 0.0f, z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v += accs[w][sb][j];
+            z += accs[w][sb][8];
+        }
+        p.po[pidx * kD + tid] = v + z;
+    }
+    if (tid == 0) {
+        p.pm[pidx] = mrun;
+        p.pl[pidx] = (redf[0] + redf[1]) + (redf[2] + redf[3]);
     }
 }
 
@@ -854,12 +1077,6 @@ __global__ __launch_bounds__(256) void k_merge(MergeParams p)
     }
 }
 
-__global__ __launch_bounds__(256) void k_zero(int32_t *p, int n)
-{
-    const int i = blockIdx.x * kBlock + threadIdx.x;
-    if (i < n) p[i] = 0;
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -877,15 +1094,14 @@ hipError_t launch_score(const ScoreParams &p, hipStream_t s)
     const dim3 grid(p.g.NC, p.g.Hkv * p.g.nsub, p.g.B);
     const dim3 blk(64);
     const bool dbg = p.dbg_scores || p.dbg_iscores;
-    // Top-p chunks are 512 tokens (8 per lane); the debug pass of a full-softmax decode runs
-    // on that decode's larger chunks
-    if (!dbg && p.g.CH <= 512) {
+    if (!dbg && p.dl && p.g.CH == kTopPChunk) {
         switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_score<1, false, 512>), grid, blk, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_score<2, false, 512>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_score<4, false, 512>), grid, blk, 0, s, p); break;
+        case 1: hipLaunchKernelGGL((k_score_topp<1>), grid, blk, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_score_topp<2>), grid, blk, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_score_topp<4>), grid, blk, 0, s, p); break;
         }
     } else {
+        // debug scores: the Top-p chunks, or the larger chunks of a full-softmax decode
         switch (p.g.GB) {
         case 1: hipLaunchKernelGGL((k_score<1, true, 8192>), grid, blk, 0, s, p); break;
         case 2: hipLaunchKernelGGL((k_score<2, true, 4096>), grid, blk, 0, s, p); break;
@@ -904,6 +1120,9 @@ hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s)
 hipError_t launch_hist(const HistParams &p, hipStream_t s)
 {
     hipLaunchKernelGGL(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_thresh, dim3(p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
     return hipGetLastError();
 }
 
@@ -919,27 +1138,18 @@ hipError_t launch_select(const SelectParams &p, hipStream_t s)
 
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 {
-    const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
     const dim3 blk(kBlock);
     if (select) {
-        switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_attend<1, true>), grid, blk, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_attend<2, true>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_attend<4, true>), grid, blk, 0, s, p); break;
-        }
+        if (p.g.CH * p.g.KA > kMaxAttendChunk) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_attend_topp, dim3(p.g.NCA, p.g.Hq, p.g.B), blk, 0, s, p);
     } else {
+        const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
         switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_attend<1, false>), grid, blk, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_attend<2, false>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_attend<4, false>), grid, blk, 0, s, p); break;
+        case 1: hipLaunchKernelGGL((k_attend<1>), grid, blk, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_attend<2>), grid, blk, 0, s, p); break;
+        default: hipLaunchKernelGGL((k_attend<4>), grid, blk, 0, s, p); break;
         }
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_zero(int32_t *p, int n, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_zero, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p, n);
     return hipGetLastError();
 }
 

@@ -95,8 +95,8 @@ __device__ __forceinline__ int score_bin(float s, float kbin)
 // Encoded query of up to GB heads that share one KV head.  The int4 codes are kept as
 // 16 words per head in the order the 8 x 4-bit dot product (v_dot8_u32_u4) consumes them:
 // nib[4w + k] holds, in nibble m = 0..7, the code of dim 32w + 4m + k.  A key word w
-// spread with (w >> k) & 0x11111111 puts the sign bit of the same dims in the same nibbles,
-// so  sum_{w,k} dot8(spread(w, k), nib[4w + k]) = sum_r bit_r u_r.
+// spread to nibbles (spread_key) puts twice the sign bit of the same dims in the same
+// nibbles, so  sum_{w,k} dot8(spread_key(w, k), nib[4w + k]) = 2 sum_r bit_r u_r.
 // c0 = v_l/sqrt(D), c1 = delta/sqrt(D), sumu = sum of the codes.
 // ---------------------------------------------------------------------------------------
 template <int GB>
@@ -133,9 +133,17 @@ __device__ __forceinline__ void read_query(QueryState<GB> &qs, const uint32_t *q
     }
 }
 
+// Key word w spread for the dot8 products: nibble m of spread_key(w, k) is 2 * bit (4m + k)
+// of w.  With the query word nib[4w + k] this gives 2 * sum_r bit_r u_r.
+__device__ __forceinline__ uint32_t spread_key(uint32_t w, int k)
+{
+    return (k == 0 ? (w << 1) : k == 1 ? w : (w >> (k - 1))) & 0x22222222u;
+}
+
 // Proxy score of one cached key against GB query heads (binary x INT4, then the binary32
-// combine):  A = 2 * sum_r bit_r u_r - sumu  (= sum_r s_r u_r, s_r = +-1),
-// P = 2 * popcount(bits) - D  (= sum_r s_r),  score = fmaf(c1, A, c0 * P) * (norm / corr).
+// combine):  A = 2 * sum_r bit_r u_r - sumu  (= sum_r s_r u_r, s_r = +-1; the dot8 chain
+// starts at -sumu and wraps modulo 2^32), P = 2 * popcount(bits) - D  (= sum_r s_r),
+// score = fmaf(c1, A, c0 * P) * (norm / corr).
 template <int GB>
 __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const QueryState<GB> &qs,
                                           float *s, int *A)
@@ -145,7 +153,7 @@ __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const Que
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[4 * i + k] = (w[i] >> k) & 0x11111111u;
+        for (int k = 0; k < 4; ++k) x[4 * i + k] = spread_key(w[i], k);
     const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                    __builtin_popcount(w[3]);
     const float fP = (float)(2 * pc - kD);
@@ -154,14 +162,14 @@ __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const Que
     // independent
     uint32_t ip[GB];
 #pragma unroll
-    for (int h = 0; h < GB; ++h) ip[h] = 0u;
+    for (int h = 0; h < GB; ++h) ip[h] = (uint32_t)(-qs.sumu[h]);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
         for (int h = 0; h < GB; ++h) ip[h] = __builtin_amdgcn_udot8(x[i], qs.nib[h][i], ip[h], false);
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
-        const int a = 2 * (int)ip[h] - qs.sumu[h];
+        const int a = (int)ip[h];
         A[h] = a;
         const float cp = qs.c0[h] * fP;
         s[h] = fmaf(qs.c1[h], (float)a, cp) * r;

@@ -5,6 +5,9 @@
 
 namespace kvc {
 
+// Tokens per Top-p score chunk (one wave of the score kernel, 8 tokens per lane).
+constexpr int kTopPChunk = 512;
+
 // Device view of the paged cache: per (page, KV head) structure of arrays.
 struct CacheView {
     int Hkv;
@@ -37,7 +40,6 @@ struct QprepParams {
     int BH;
     uint32_t *qnib;        // [B*Hq][16] int4 codes in dot8 order
     float4 *qpar;          // [B*Hq]
-    int32_t *counters;     // nullable [B*Hq]: zeroed here (arrival counters of later kernels)
     uint8_t *dbg_codes;    // nullable [B*Hq][128]
     float *dbg_params;     // nullable [B*Hq][4]
     int32_t *dbg_sumu;     // nullable [B*Hq]
@@ -82,15 +84,15 @@ struct BinScoresParams {
     int32_t *lmax;
 };
 
-// Histogram of bin distances, then (last block of each (b, h)) the Top-p threshold.
+// Histogram of bin distances per split, then the Top-p threshold of each (b, h).
 struct HistParams {
     DecodeGeom g;
     int nsplit, cps;       // splits per (b,h), chunks per split
     uint32_t pfx;          // rint(p * 2^24)
     const uint16_t *dl;
     const int32_t *lmax;
-    uint16_t *hist;        // [B*Hq][nsplit][8192] per-split counts (a split has < 65536 tokens)
-    int32_t *counters;     // [B*Hq] arrival counters, zero on entry
+    uint16_t *hist;        // [B*Hq][nsplit][8192] per-split counts (a split has < 65536 tokens);
+                           // splits past a sequence's end are neither written nor read
     int32_t *sel;          // [B*Hq][4] = (e_max, b*, count, 0)
     int32_t *dbg_count;    // nullable [B*Hq]
     int32_t *dbg_bins;     // nullable [B*Hq][2]
@@ -136,7 +138,5 @@ hipError_t launch_hist(const HistParams &p, hipStream_t s);
 hipError_t launch_select(const SelectParams &p, hipStream_t s);
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, hipStream_t s);
-// n int32 zeros (a fill kernel, so that the call stays free of memset nodes under capture)
-hipError_t launch_zero(int32_t *p, int n, hipStream_t s);
 
 }  // namespace kvc

@@ -76,7 +76,8 @@ typedef struct kv_cache {
     int32_t num_kv_heads;  /* Hkv */
     int32_t value_group;   /* 32 or 64 dims per scale/zero pair */
     int32_t page_size;     /* tokens per page */
-    int32_t num_pages;     /* physical pages in the pool */
+    int32_t num_pages;     /* physical pages in the pool; num_pages * num_kv_heads * page_size
+                              must stay below 2^32 (KV_ERR_UNSUPPORTED otherwise) */
     int32_t rot_kind;      /* KV_ROT_DENSE or KV_ROT_HADAMARD */
     const void *rot;       /* device: see above */
     uint32_t *key_bits;
