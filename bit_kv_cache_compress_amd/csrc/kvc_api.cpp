@@ -63,17 +63,16 @@ constexpr int kMaxChunks = 4096;
 //  Full softmax: chunks of CH tokens, the largest power of two in [256, 8192/GB] that still
 //  gives at least 2048 blocks (8 per compute unit) over (chunk, KV-head group, sequence) and
 //  no more than 4096 chunks; one attention block per chunk (KA = 1).
-//  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention block
-//  (one query head, Top-p keeps few tokens per head) covers KA <= 16 score chunks, as many
-//  as still give >= 1024 blocks.
+//  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention wave
+//  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 4 score chunks,
+//  8 or 16 only where more than 4096 attention chunks would be needed.
 void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp, int Hq)
 {
     int CH, KA = 1;
     if (topp) {
         CH = kvc::kTopPChunk;
         const int NC = (max_len + CH - 1) / CH;
-        const long heads = (long)B * Hq;
-        while (KA < 16 && heads * ((NC + 2 * KA - 1) / (2 * KA)) >= 1024) KA *= 2;
+        KA = 4;  // 2048-token attention chunks, more only to stay within kMaxChunks
         while ((long)(NC + KA - 1) / KA > kMaxChunks) KA *= 2;
     } else {
         CH = chunk_cap(GB, false);

@@ -821,68 +821,70 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention over one attention chunk (KA score chunks, at most 8192 tokens) for one
-// query head.  Top-p keeps a small, head-specific set of tokens, so the block first lists
-// the kept tokens of its chunk in ascending order (one pass over the 16-bit bin distances,
-// 32 tokens per thread, a single block-wide scan of four packed 16-bit counts), then works
-// through the list in batches of 256 entries.  For a batch every load is issued up front:
-// one key per thread (sign words and norm/correction word) and, per 16-lane group, the
-// value words of 16 entries (4 bytes of codes, i.e. 8 dims, and the group's scale/zero word
-// per lane).  Scores, the running max and the weights follow, then the weighted value sums
-// from registers.  The chunk costs two dependent rounds of HBM reads (distances with the
-// query and page ids, then the kept entries) when it keeps at most 256 tokens.
+// Top-p attention: one wave per (attention chunk of 2048 * NSUB tokens, query head,
+// sequence).  Top-p keeps a small, head-specific set of tokens, so the wave first lists the
+// kept tokens of its chunk in ascending order (one pass over the 16-bit bin distances, 8
+// tokens per 16-byte load, one wave scan of packed 16-bit counts), then works through the
+// list in batches of 64 entries.  For a batch every load is issued up front: one key per
+// lane (sign words and the norm/correction word) and, per 4-lane group, the value words of
+// up to 4 entries (16 bytes of codes, i.e. 32 dims, and the group's scale/zero word per
+// lane).  Scores, the running max and the weights follow, then the weighted value sums
+// from registers.  Page ids become 32-bit slot bases in LDS, so an entry's slot is one LDS
+// read and an add.  A chunk that keeps at most 64 tokens costs two dependent rounds of HBM
+// reads: the distances (with the query, thresholds and page ids), then the kept entries.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_attend_topp(AttendParams p)
+template <int NSUB>
+__global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 {
-    constexpr int kNB = 256;  // entries per batch
-    constexpr int kVU = kNB / 16;  // entries per 16-lane group and batch
-    __shared__ uint16_t list[kMaxAttendChunk];
-    __shared__ float wbuf[kNB];
-    __shared__ int pages[kMaxChunkPages];
+    constexpr int CHA = 2048 * NSUB;  // tokens of the attention chunk
+    constexpr int NB = 64;            // entries per batch
+    constexpr int VU = NB / 16;       // value entries per 4-lane group and batch
+    __shared__ uint32_t list[CHA];  // slots of the kept tokens
+    __shared__ float wbuf[NB];
+    __shared__ uint32_t pbase[CHA / 16 + 1];
     __shared__ uint32_t qsh[16];
-    __shared__ float4 qps[1];
-    __shared__ int thr_s[16];
-    __shared__ uint64_t scan_s[4];
-    __shared__ float redf[4];
-    __shared__ float accs[4][16][9];
+    __shared__ int thr_s[CHA / kTopPChunk];
     const DecodeGeom &g = p.g;
     const int achunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int kvh = h / g.G;
     const int L = g.seq_lens[b];
-    const int CHa = g.CH * g.KA;
-    const int t0 = achunk * CHa;
+    const int t0 = achunk * CHA;
     if (t0 >= L) return;
-    const int n = min(CHa, L - t0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = min(CHA, L - t0);
+    const int lane = threadIdx.x;
     const size_t bh = (size_t)b * g.Hq + h;
 
-    // ---- round 1: distances (tokens 8 tid + 2048 j .. + 7), query, thresholds, page ids
-    uint4 raw[4];
+    // ---- round 1: distances (tokens 8 lane + 512 j .. + 7), query, thresholds, page ids
+    uint4 raw[4 * NSUB];
     const uint16_t *row = p.dl + bh * g.Lpad + t0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tl = 8 * tid + 2048 * j;
+    for (int j = 0; j < 4 * NSUB; ++j) {
+        const int tl = 8 * lane + 512 * j;
         if (tl < n) raw[j] = *reinterpret_cast<const uint4 *>(row + tl);
     }
-    stage_query<1>(p.qnib, p.qpar, (int)bh, qsh, qps);
-    if (tid < g.KA) {
-        const int chunk = achunk * g.KA + tid;
-        thr_s[tid] = (chunk * g.CH < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
+    if (lane < 16) qsh[lane] = p.qnib[bh * 16 + lane];
+    const float4 qp = p.qpar[bh];
+    if (lane < CHA / kTopPChunk) {
+        const int chunk = achunk * (CHA / kTopPChunk) + lane;
+        thr_s[lane] = (chunk * kTopPChunk < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
     }
-    const int p0 = t0 >> p.c.logP;
-    const int np = ((t0 + n - 1) >> p.c.logP) - p0 + 1;
-    for (int i = tid; i < np; i += kBlock) pages[i] = g.page_table[(size_t)b * g.max_pages + p0 + i];
+    const int logP = p.c.logP;
+    const int p0 = t0 >> logP;
+    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
+    for (int i = lane; i < np; i += 64)
+        pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
+                   << logP;
     __syncthreads();
 
     // ---- kept tokens, listed in ascending order
-    uint32_t keep[4];
-    uint64_t cnt4 = 0;
+    uint64_t cnt4[NSUB];
+    uint32_t keep[4 * NSUB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tl = 8 * tid + 2048 * j;
+    for (int j = 0; j < 4 * NSUB; ++j) {
+        const int tl = 8 * lane + 512 * j;
         uint32_t m = 0u;
         if (tl < n) {
-            const int thr = thr_s[tl >> g.logCH];  // the 8 tokens share a score chunk
+            const int thr = thr_s[j];  // 512 tokens of a score chunk per j
             const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -891,138 +893,142 @@ __global__ __launch_bounds__(256) void k_attend_topp(AttendParams p)
             }
         }
         keep[j] = m;
-        cnt4 |= (uint64_t)__builtin_popcount(m) << (16 * j);
     }
-    // block-wide exclusive scan of the four 16-bit counts (a field never exceeds 2048)
-    uint64_t incl = cnt4;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+    for (int s = 0; s < NSUB; ++s) {
+        cnt4[s] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt4[s] |= (uint64_t)__builtin_popcount(keep[4 * s + j]) << (16 * j);
     }
-    if (lane == 63) scan_s[wave] = incl;
-    __syncthreads();
-    uint64_t before = incl - cnt4;
-    for (int w = 0; w < wave; ++w) before += scan_s[w];
-    const uint64_t total = scan_s[0] + scan_s[1] + scan_s[2] + scan_s[3];
     int nlist = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        int off = nlist + (int)((before >> (16 * j)) & 0xFFFFu);
-        uint32_t m = keep[j];
-        while (m) {
-            const int e = __builtin_ctz(m);
-            m &= m - 1u;
-            list[off++] = (uint16_t)(8 * tid + 2048 * j + e);
+    for (int s = 0; s < NSUB; ++s) {
+        // wave-wide inclusive scan of four packed 16-bit counts (a field never exceeds 512)
+        uint64_t incl = cnt4[s];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
         }
-        nlist += (int)((total >> (16 * j)) & 0xFFFFu);
+        const uint64_t total = __shfl(incl, 63);
+        const uint64_t before = incl - cnt4[s];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int off = nlist + (int)((before >> (16 * j)) & 0xFFFFu);
+            uint32_t m = keep[4 * s + j];
+            if (m) {
+                // the 8 tokens of a 16-byte load share a page (P >= 16)
+                const int t = t0 + 8 * lane + 512 * (4 * s + j);
+                const uint32_t sb = pbase[(t >> logP) - p0] + (uint32_t)(t & ((1 << logP) - 1));
+                while (m) {
+                    const int e = __builtin_ctz(m);
+                    m &= m - 1u;
+                    list[off++] = sb + (uint32_t)e;
+                }
+            }
+            nlist += (int)((total >> (16 * j)) & 0xFFFFu);
+        }
     }
+    nlist = __builtin_amdgcn_readfirstlane(nlist);  // wave-uniform: scalar loop control
     __syncthreads();
 
     QueryState<1> qs;
-    read_query<1>(qs, qsh, qps);
-    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
-    const int sub = tid & 15;  // dims 8*sub .. 8*sub+7
-    const int eg = tid >> 4;   // entries eg + 16 u of a batch
-    const int gv = p.c.Gv;
-    const int grp = (8 * sub) / gv;
-    const int ngrp = kD / gv;
-    float acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int i = 0; i < 16; ++i) qs.nib[0][i] = qsh[i];
+    qs.c0[0] = qp.x;
+    qs.c1[0] = qp.y;
+    qs.sumu[0] = __float_as_int(qp.z);
+    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
+    const int q4 = lane & 3;   // dims 32*q4 .. 32*q4+31
+    const int eg = lane >> 2;  // entries eg + 16 u of a batch
+    const int lgv = p.c.Gv == 32 ? 5 : 6;
+    const int lngrp = 7 - lgv;  // log2 of the groups per token
+    const int grp = (32 * q4) >> lgv;
+    float acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
     float zacc = 0.0f, lloc = 0.0f, mrun = -INFINITY;
 
-    for (int bs = 0; bs < nlist; bs += kNB) {
-        const int nb = min(kNB, nlist - bs);
-        // ---- round 2: the batch's keys and value words
-        uint4 kb = make_uint4(0u, 0u, 0u, 0u);
-        uint32_t nc = 0u;
-        if (tid < nb) {
-            const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + (int)list[bs + tid]);
-            kb = kb4[slot];
-            nc = p.c.key_nc[slot];
-        }
-        uint32_t cw[kVU], szw[kVU];
+    for (int bs = 0; bs < nlist; bs += NB) {
+        const int nb = min(NB, nlist - bs);
+        const int nu = (nb + 15) >> 4;  // value rounds of this batch (uniform)
+        // ---- round 2: the batch's keys and value words (entries past nb re-read the last)
+        const uint32_t slot_k = list[bs + min(lane, nb - 1)];
+        uint32_t sl[VU];
 #pragma unroll
-        for (int u = 0; u < kVU; ++u) {
-            const int e = eg + 16 * u;
-            if (e < nb) {
-                const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + (int)list[bs + e]);
-                cw[u] = *reinterpret_cast<const uint32_t *>(p.c.val_codes + slot * (kD / 2) + 4 * sub);
-                szw[u] = p.c.val_sz[slot * ngrp + grp];
+        for (int u = 0; u < VU; ++u) sl[u] = list[bs + min(eg + 16 * u, nb - 1)];
+        const uint4 kb = kb4[slot_k];
+        const uint32_t nc = p.c.key_nc[slot_k];
+        uint4 cw[VU];
+        uint32_t szw[VU];
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            if (u < nu) {
+                cw[u] = *reinterpret_cast<const uint4 *>(p.c.val_codes + ((size_t)sl[u] << 6) + 16 * q4);
+                szw[u] = p.c.val_sz[((size_t)sl[u] << lngrp) + grp];
             }
         }
-        float s = -INFINITY;
-        if (tid < nb) {
+        float s;
+        {
             int A;
             score_key<1>(kb, nc, qs, &s, &A);
         }
-        const float wm = wave_max(s);
-        if (lane == 0) redf[wave] = wm;
-        __syncthreads();
-        const float mb = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
-        const float mnew = fmaxf(mrun, mb);
+        if (lane >= nb) s = -INFINITY;
+        const float mnew = fmaxf(mrun, wave_max(s));
         const float scale = (mrun == -INFINITY) ? 0.0f : exp2f((mrun - mnew) * p.klog);
         if (scale != 1.0f) {
             zacc *= scale;
             lloc *= scale;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] *= scale;
+            for (int j = 0; j < 32; ++j) acc[j] *= scale;
         }
         mrun = mnew;
         const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
         lloc += w;
-        wbuf[tid] = w;
+        wbuf[lane] = w;
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kVU; ++u) {
-            const int e = eg + 16 * u;
-            if (e < nb) {
-                const float we = wbuf[e];
+        for (int u = 0; u < VU; ++u) {
+            if (u < nu) {
+                const float we = wbuf[eg + 16 * u];  // 0 past nb
                 const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
                 const float zf = half_bits_to_float(szw[u] >> 16);
                 const float ws = we * sf;
                 zacc = fmaf(we, zf, zacc);
-                const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+                const uint32_t cwk[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    acc[2 * m] = fmaf(ws, (float)((lo >> (8 * m)) & 0xFFu), acc[2 * m]);
-                    acc[2 * m + 1] = fmaf(ws, (float)((hi >> (8 * m)) & 0xFFu), acc[2 * m + 1]);
+                for (int k = 0; k < 4; ++k) {
+                    // byte m of word k holds dims 32 q4 + 8k + 2m (low nibble) and + 1 (high)
+                    const uint32_t lo = cwk[k] & 0x0F0F0F0Fu, hi = (cwk[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        acc[8 * k + 2 * m] = fmaf(ws, (float)((lo >> (8 * m)) & 0xFFu), acc[8 * k + 2 * m]);
+                        acc[8 * k + 2 * m + 1] = fmaf(ws, (float)((hi >> (8 * m)) & 0xFFu), acc[8 * k + 2 * m + 1]);
+                    }
                 }
             }
         }
-        __syncthreads();  // wbuf and redf are rewritten by the next batch
+        __syncthreads();  // wbuf is rewritten by the next batch
     }
 
     // ---- weight sum, then the value sums reduced over the 16 entry groups
-    const float lw = wave_sum(lloc);
+    const float lsum = wave_sum(lloc);
 #pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
+    for (int o = 4; o < 64; o <<= 1) {
         zacc += __shfl_xor(zacc, o);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += __shfl_xor(acc[j], o);
+        for (int j = 0; j < 32; ++j) acc[j] += __shfl_xor(acc[j], o);
     }
-    if (lane < 16) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) accs[wave][lane][j] = acc[j];
-        accs[wave][lane][8] = zacc;
-    }
-    if (lane == 0) redf[wave] = lw;
-    __syncthreads();
     const size_t pidx = bh * g.NCA + achunk;
-    if (tid < kD) {
-        const int sb = tid >> 3, j = tid & 7;
-        float v = 0.0f, z = 0.0f;
+    if (lane < 4) {
+        float4 *dst = reinterpret_cast<float4 *>(p.po + pidx * kD + 32 * lane);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            v += accs[w][sb][j];
-            z += accs[w][sb][8];
-        }
-        p.po[pidx * kD + tid] = v + z;
+        for (int k = 0; k < 8; ++k)
+            dst[k] = make_float4(acc[4 * k] + zacc, acc[4 * k + 1] + zacc, acc[4 * k + 2] + zacc, acc[4 * k + 3] + zacc);
     }
-    if (tid == 0) {
+    if (lane == 0) {
         p.pm[pidx] = mrun;
-        p.pl[pidx] = (redf[0] + redf[1]) + (redf[2] + redf[3]);
+        p.pl[pidx] = lsum;
     }
 }
 
@@ -1140,8 +1146,15 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 {
     const dim3 blk(kBlock);
     if (select) {
-        if (p.g.CH * p.g.KA > kMaxAttendChunk) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_attend_topp, dim3(p.g.NCA, p.g.Hq, p.g.B), blk, 0, s, p);
+        // one wave per (attention chunk, query head, sequence)
+        const dim3 grid(p.g.NCA, p.g.Hq, p.g.B);
+        if (p.g.CH != kTopPChunk) return hipErrorInvalidValue;
+        switch (p.g.KA) {
+        case 4: hipLaunchKernelGGL((k_attend_topp<1>), grid, dim3(64), 0, s, p); break;
+        case 8: hipLaunchKernelGGL((k_attend_topp<2>), grid, dim3(64), 0, s, p); break;
+        case 16: hipLaunchKernelGGL((k_attend_topp<4>), grid, dim3(64), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+        }
     } else {
         const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
         switch (p.g.GB) {
