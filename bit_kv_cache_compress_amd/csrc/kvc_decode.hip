@@ -389,98 +389,6 @@ __device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t
     return out[0];
 }
 
-// Top-p threshold of (b, h) from the per-split bin counts (256 threads, thread t owns bins
-// 32t .. 32t+31).  With W(d) = T[d mod 256] >> (d / 256), T[j] = round(2^(32 - j/256)):
-//   Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
-//   b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p },  count = sum_{d <= b*} cnt[d].
-__device__ void topp_threshold(const HistParams &p, size_t bh, int emax, int nsplit_used)
-{
-    __shared__ uint64_t T[256];
-    __shared__ uint64_t wsum[4];
-    __shared__ int bstar_s;
-    __shared__ int cnt_s[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
-    uint32_t cnt[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k) cnt[k] = 0u;
-    for (int s = 0; s < nsplit_used; s += 2) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + (bh * p.nsplit + s) * kBins + 32 * tid);
-        const bool two = s + 1 < nsplit_used;
-        uint4 v[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = src[k];
-#pragma unroll
-        for (int k = 4; k < 8; ++k) v[k] = two ? src[kBins / 8 + k - 4] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                cnt[8 * (k & 3) + 2 * q] += w[q] & 0xFFFFu;
-                cnt[8 * (k & 3) + 2 * q + 1] += w[q] >> 16;
-            }
-        }
-    }
-    __syncthreads();  // T ready
-    // d >> 8 is the same for all 32 bins of a thread
-    const int shift = (32 * tid) >> 8;
-    uint64_t mine = 0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) mine += (uint64_t)cnt[k] * (T[(32 * tid + k) & 255] >> shift);
-    uint64_t incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint64_t before = incl - mine;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const uint64_t Z = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    const uint64_t lo = Z * (uint64_t)p.pfx;
-    uint64_t hi = __umul64hi(Z, (uint64_t)p.pfx);
-    const uint64_t lo2 = lo + ((1ull << 24) - 1);
-    hi += (lo2 < lo) ? 1 : 0;
-    const uint64_t Tp = (hi << 40) | (lo2 >> 24);
-    if (tid == 0) bstar_s = (Tp == 0) ? 0 : kBins - 1;
-    __syncthreads();
-    if (Tp > 0 && before < Tp && before + mine >= Tp) {
-        uint64_t F = before;
-        int bs = 32 * tid + 31;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            F += (uint64_t)cnt[k] * (T[(32 * tid + k) & 255] >> shift);
-            if (F >= Tp) {
-                bs = 32 * tid + k;
-                break;
-            }
-        }
-        bstar_s = bs;
-    }
-    __syncthreads();
-    const int bstar = bstar_s;
-    int c = 0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-        if (32 * tid + k <= bstar) c += (int)cnt[k];
-    c = wave_sum_i(c);
-    if (lane == 0) cnt_s[wave] = c;
-    __syncthreads();
-    if (tid == 0) {
-        const int count = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
-        p.sel[bh * 4 + 0] = emax;
-        p.sel[bh * 4 + 1] = bstar;
-        p.sel[bh * 4 + 2] = count;
-        if (p.dbg_count) p.dbg_count[bh] = count;
-        if (p.dbg_bins) {
-            p.dbg_bins[bh * 2] = emax;
-            p.dbg_bins[bh * 2 + 1] = bstar;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------------------
 // Histogram pass: per (split, query head, sequence) block, counts of tokens per bin
 // distance d = (e_max - chunk top) + distance-to-chunk-top, d < 8192.  The last block of a
@@ -541,15 +449,23 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
     }
 }
 
-// Top-p threshold of each (b, h) from the split counts: one block per (query head, sequence).
-// A kernel of its own, so that the split counts reach it through the kernel boundary rather
-// than through device-scope fences in every histogram block.
-__global__ __launch_bounds__(256) void k_thresh(HistParams p)
+// Top-p threshold of each (b, h) from the split counts: one 1024-thread block per (query
+// head, sequence), thread t owns bins 8t .. 8t+7.  A kernel of its own, so that the split
+// counts reach it through the kernel boundary rather than through device-scope fences in
+// every histogram block.  With W(d) = T[d mod 256] >> (d / 256), T[j] = round(2^(32 - j/256)):
+//   Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
+//   b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p },  count = sum_{d <= b*} cnt[d].
+// One block scan carries both the weighted sums and the counts, so the thread whose bins
+// hold b* writes the result without a further pass.
+__global__ __launch_bounds__(1024) void k_thresh(HistParams p)
 {
-    __shared__ int red[4];
-    __shared__ int top[1];
+    constexpr int kT = 1024;
+    __shared__ uint64_t T[256];
+    __shared__ uint64_t wsum[kT / 64];
+    __shared__ int csum[kT / 64];
+    __shared__ int imax[kT / 64];
     const DecodeGeom &g = p.g;
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)b * g.Hq + h;
     const int L = g.seq_lens[b];
     if (L <= 0) {
@@ -566,8 +482,103 @@ __global__ __launch_bounds__(256) void k_thresh(HistParams p)
         return;
     }
     const int nch = (L + g.CH - 1) >> g.logCH;
-    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
-    topp_threshold(p, bh, emax, (nch + p.cps - 1) / p.cps);
+    const int nsu = (nch + p.cps - 1) / p.cps;  // splits that hold tokens
+    // counts of bins 8 tid .. 8 tid + 7 summed over the splits (8 splits' loads in flight)
+    uint32_t cnt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cnt[k] = 0u;
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + bh * p.nsplit * kBins) + tid;
+    for (int s0 = 0; s0 < nsu; s0 += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (s0 + k < nsu) ? src[(size_t)(s0 + k) * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cnt[2 * q] += w[q] & 0xFFFFu;
+                cnt[2 * q + 1] += w[q] >> 16;
+            }
+        }
+    }
+    int m = -kBinClamp;
+    for (int c = tid; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
+    m = wave_max_i(m);
+    if (lane == 0) imax[wave] = m;
+    if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
+    __syncthreads();
+    // d >> 8 is the same for all 8 bins of a thread
+    const int shift = tid >> 5;
+    uint64_t mine = 0;
+    int cmine = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        mine += (uint64_t)cnt[k] * (T[(8 * tid + k) & 255] >> shift);
+        cmine += (int)cnt[k];
+    }
+    uint64_t incl = mine;
+    int cincl = cmine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        const int cy = __shfl_up(cincl, o);
+        if (lane >= o) {
+            incl += y;
+            cincl += cy;
+        }
+    }
+    if (lane == 63) {
+        wsum[wave] = incl;
+        csum[wave] = cincl;
+    }
+    __syncthreads();
+    uint64_t before = incl - mine, Z = 0;
+    int cbefore = cincl - cmine, emax = -kBinClamp;
+#pragma unroll
+    for (int w = 0; w < kT / 64; ++w) {
+        Z += wsum[w];
+        emax = max(emax, imax[w]);
+        if (w < wave) {
+            before += wsum[w];
+            cbefore += csum[w];
+        }
+    }
+    const uint64_t lo = Z * (uint64_t)p.pfx;
+    uint64_t hi = __umul64hi(Z, (uint64_t)p.pfx);
+    const uint64_t lo2 = lo + ((1ull << 24) - 1);
+    hi += (lo2 < lo) ? 1 : 0;
+    const uint64_t Tp = (hi << 40) | (lo2 >> 24);
+    int bstar = -1, count = 0;
+    if (Tp == 0) {
+        if (tid == 0) {
+            bstar = 0;
+            count = (int)cnt[0];
+        }
+    } else if (before < Tp && before + mine >= Tp) {
+        uint64_t F = before;
+        count = cbefore;
+        bstar = 8 * tid + 7;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            F += (uint64_t)cnt[k] * (T[(8 * tid + k) & 255] >> shift);
+            count += (int)cnt[k];
+            if (F >= Tp) {
+                bstar = 8 * tid + k;
+                break;
+            }
+        }
+    }
+    if (bstar >= 0) {
+        p.sel[bh * 4 + 0] = emax;
+        p.sel[bh * 4 + 1] = bstar;
+        p.sel[bh * 4 + 2] = count;
+        if (p.dbg_count) p.dbg_count[bh] = count;
+        if (p.dbg_bins) {
+            p.dbg_bins[bh * 2] = emax;
+            p.dbg_bins[bh * 2 + 1] = bstar;
+        }
+    }
 }
 
 // Bin-distance threshold of a chunk: token kept when its distance to the chunk top bin is
@@ -1035,46 +1046,53 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 // ---------------------------------------------------------------------------------------
 // Split-K merge, one 256-thread block per (query head, sequence):
 //   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
-// Thread (d, half) sums the chunks of one parity for dim d; loads are independent.
+// Thread (d, half) sums the chunks of one parity for dim d.  The value sums of the first 64
+// chunks are loaded first, so that their reads overlap the max and weight reductions.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_merge(MergeParams p)
 {
+    constexpr int PF = 32;  // chunks per thread loaded ahead
     __shared__ float alpha[4096];
-    __shared__ float redf[4];
-    __shared__ float outm[1];
+    __shared__ float redf[8];
     __shared__ float part[kD];
     const DecodeGeom &g = p.g;
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)b * g.Hq + h;
     const int L = g.seq_lens[b];
     const int CHa = g.CH * g.KA;
     const int nch = L > 0 ? (L + CHa - 1) / CHa : 0;
-    float m[1] = {-INFINITY};
-    for (int c = tid; c < nch; c += kBlock) m[0] = fmaxf(m[0], p.pm[bh * g.NCA + c]);
-    block_reduce<1>(m, redf, outm, MaxF());
-    const float M = outm[0];
-    float den[1] = {0.0f};
+    const int d = tid & (kD - 1), half = tid >> 7;
+    const float *po = p.po + bh * g.NCA * kD + d;
+    float v[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int c = half + 2 * i;
+        v[i] = c < nch ? po[(size_t)c * kD] : 0.0f;
+    }
+    float m = -INFINITY;
+    for (int c = tid; c < nch; c += kBlock) m = fmaxf(m, p.pm[bh * g.NCA + c]);
+    m = wave_max(m);
+    if (lane == 0) redf[wave] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+    float den = 0.0f;
     for (int c = tid; c < nch; c += kBlock) {
         const float mc = p.pm[bh * g.NCA + c];
         const float a = (mc == -INFINITY) ? 0.0f : exp2f((mc - M) * p.klog);
         alpha[c] = a;
-        den[0] = fmaf(a, p.pl[bh * g.NCA + c], den[0]);
+        den = fmaf(a, p.pl[bh * g.NCA + c], den);
     }
-    block_reduce<1>(den, redf, outm, SumF());  // barriers also publish alpha
-    const float D = outm[0];
-    const int d = tid & (kD - 1), half = tid >> 7;
+    den = wave_sum(den);
+    if (lane == 0) redf[4 + wave] = den;
+    __syncthreads();  // also publishes alpha
+    const float D = (redf[4] + redf[5]) + (redf[6] + redf[7]);
     float num = 0.0f;
-    const float *po = p.po + bh * g.NCA * kD + d;
-    int c = half;
-    for (; c + 6 < nch; c += 8) {
-        const float v0 = po[(size_t)c * kD], v1 = po[(size_t)(c + 2) * kD];
-        const float v2 = po[(size_t)(c + 4) * kD], v3 = po[(size_t)(c + 6) * kD];
-        num = fmaf(alpha[c], v0, num);
-        num = fmaf(alpha[c + 2], v1, num);
-        num = fmaf(alpha[c + 4], v2, num);
-        num = fmaf(alpha[c + 6], v3, num);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int c = half + 2 * i;
+        if (c < nch) num = fmaf(alpha[c], v[i], num);
     }
-    for (; c < nch; c += 2) num = fmaf(alpha[c], po[(size_t)c * kD], num);
+    for (int c = half + 2 * PF; c < nch; c += 2) num = fmaf(alpha[c], po[(size_t)c * kD], num);
     if (half == 1) part[d] = num;
     __syncthreads();
     if (half == 0) {
@@ -1128,7 +1146,7 @@ hipError_t launch_hist(const HistParams &p, hipStream_t s)
     hipLaunchKernelGGL(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_thresh, dim3(p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_thresh, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 
