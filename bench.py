@@ -26,9 +26,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "compressed-KV decode: KV tokens*heads attended/s and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
-# algorithmic bytes per unit: key sign words 16 B + norm/corr 4 B per
-# token-KV-head; 4-bit value codes 64 B + scale/zero 4 B per group
+# Algorithmic bytes per unit: a cached key is 16 B of sign words + a 4 B norm/correction
+# word per token-KV-head; a cached value is 64 B of 4-bit codes + a 4 B scale/zero word per
+# group.  Top-p adds a 2 B bin distance per (token, query head), written by the score pass
+# and read by the histogram and attention passes.
 KEY_BYTES = 20
+DIST_BYTES = 2
 
 
 def value_bytes(Gv):
@@ -50,6 +53,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many steps after setup (for rocprofv3), no JSON")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (a known-size kernel that "
+                         "calibrates the FETCH_SIZE/WRITE_SIZE counters), no JSON")
     return ap.parse_args()
 
 
@@ -62,6 +68,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2**20 // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB five times")
+        return
 
     import bit_kv_cache_compress_amd as kvc
     import workloads as W
@@ -171,7 +187,7 @@ def main():
     log("[bench] stages (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in stage_ms.items()))
 
     # ---- selection statistics (one untimed debug decode)
-    sel_union = None
+    sel_union = sel_entries = None
     if wl.top_p < 1.0:
         dbg = kvc.DecodeDebug.allocate(B, Hq, Lmax, True, dev)
         kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, debug=dbg)
@@ -186,18 +202,29 @@ def main():
             m.scatter_(1, idx * valid, valid)
             mask[:, h // G] |= m
         sel_union = int(mask.sum())
+        sel_entries = int(cnt.sum())
         sel_frac = float(cnt.sum()) / float(tokens_heads * G)
         log(f"[bench] Top-p kept {sel_frac * 100:.2f}% of (token, query head) pairs; "
             f"union over GQA groups {sel_union} token-KV-heads")
         del dbg, mask
 
     # ---- roofline of the dominant kernel
-    per_launch = {"score": KEY_BYTES * tokens_heads,
-                  "attend": (value_bytes(Gv) * sel_union) if sel_union is not None
-                  else (KEY_BYTES + value_bytes(Gv)) * tokens_heads,
-                  "append": (2 * D * 2 + 16 + 4 + value_bytes(Gv)) * B * Hkv}
-    kernel_names = {"score": "k_score", "attend": "k_attend", "append": "k_append",
-                    "hist": "k_hist", "query": "k_qprep", "merge": "k_merge"}
+    G = Hq // Hkv
+    kv_in = 2 if wl.kv_dtype == "f16" else 4
+    per_launch = {
+        # every key of the context, each scored for the G query heads of its KV head, and
+        # the bin distances written
+        "score": (KEY_BYTES + DIST_BYTES * G) * tokens_heads if wl.top_p < 1.0 else KEY_BYTES * tokens_heads,
+        # Top-p: the distances, then key and value of every kept (token, query head);
+        # full softmax: every key and value once per KV head
+        "attend": (DIST_BYTES * G * tokens_heads + (KEY_BYTES + value_bytes(Gv)) * sel_entries)
+        if sel_entries is not None else (KEY_BYTES + value_bytes(Gv)) * tokens_heads,
+        # the distances once
+        "hist": DIST_BYTES * G * tokens_heads,
+        "append": (2 * D * kv_in + KEY_BYTES + value_bytes(Gv)) * B * Hkv}
+    kernel_names = {"score": "k_score_topp" if wl.top_p < 1.0 else "k_score", "append": "k_append",
+                    "attend": "k_attend_topp" if wl.top_p < 1.0 else "k_attend", "hist": "k_hist",
+                    "query": "k_qprep", "merge": "k_merge"}
     dominant = max((k for k in stage_ms if k in per_launch), key=lambda k: stage_ms[k])
     ach = per_launch[dominant] / (stage_ms[dominant] / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": round(ach, 1),
@@ -205,7 +232,10 @@ def main():
                 "traffic": measured_traffic(kernel_names[dominant], wl.name),
                 "algorithmic_bytes_per_launch": per_launch[dominant],
                 "avg_launch_us": round(stage_ms[dominant] * 1e3, 2)}
-    step_alg = per_launch["append"] + per_launch["attend"] + (per_launch["score"] if wl.top_p < 1.0 else 0)
+    # whole step, algorithmic minimum: every key once, the values of the kept tokens once per
+    # KV head (the union over its query heads), the appended token
+    step_alg = per_launch["append"] + (KEY_BYTES * tokens_heads + value_bytes(Gv) * sel_union
+                                       if sel_union is not None else (KEY_BYTES + value_bytes(Gv)) * tokens_heads)
     log(f"[bench] dominant {dominant}: {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
 
     result = {
@@ -225,6 +255,7 @@ def main():
     }
     if sel_union is not None:
         result["topp_selected_union_token_kv_heads"] = sel_union
+        result["topp_selected_token_query_heads"] = sel_entries
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, wl, K, V, q, lens, pt_np, kind, rot,

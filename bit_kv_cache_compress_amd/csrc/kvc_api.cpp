@@ -52,32 +52,25 @@ struct Plan {
 // floats (32 KB).
 int chunk_cap(int GB, bool topp)
 {
-    return topp ? kvc::kTopPChunk * 16 : 8192 / GB;
+    return topp ? kvc::kTopPAttendChunk : 8192 / GB;
 }
-
-// At most this many attention chunks per sequence (the merge keeps one weight per chunk in
-// LDS).
-constexpr int kMaxChunks = 4096;
 
 // Geometry.
 //  Full softmax: chunks of CH tokens, the largest power of two in [256, 8192/GB] that still
 //  gives at least 2048 blocks (8 per compute unit) over (chunk, KV-head group, sequence) and
 //  no more than 4096 chunks; one attention block per chunk (KA = 1).
 //  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention wave
-//  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 4 score chunks,
-//  8 or 16 only where more than 4096 attention chunks would be needed.
-void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp, int Hq)
+//  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 4 score chunks.
+void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
 {
     int CH, KA = 1;
     if (topp) {
         CH = kvc::kTopPChunk;
-        const int NC = (max_len + CH - 1) / CH;
-        KA = 4;  // 2048-token attention chunks, more only to stay within kMaxChunks
-        while ((long)(NC + KA - 1) / KA > kMaxChunks) KA *= 2;
+        KA = kvc::kTopPAttendChunk / CH;
     } else {
         CH = chunk_cap(GB, false);
         const long units = (long)B * rows_per_seq;
-        while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048 && (long)(CH >> 1) * kMaxChunks >= max_len)
+        while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048 && (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
             CH >>= 1;
     }
     pl.g.CH = CH;
@@ -143,7 +136,7 @@ int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, f
         return fail(KV_ERR_UNSUPPORTED, "GQA group Hq/Hkv = %d: supported groups are 1, 2, 4, 8", G);
     if (!(top_p > 0.0f)) return fail(KV_ERR_ARG, "top_p must be > 0 (got %g)", (double)top_p);
     const int GB = G < 4 ? G : 4;
-    const long limit = (long)chunk_cap(GB, top_p < 1.0f) * kMaxChunks;  // merge weights fit in LDS
+    const long limit = (long)chunk_cap(GB, top_p < 1.0f) * kvc::kMaxChunks;  // merge weights fit in LDS
     if (max_seq_len > limit)
         return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld for this head grouping", max_seq_len, limit);
     return KV_OK;
@@ -161,7 +154,7 @@ void make_plan(Plan &pl, int B, int Hq, int Hkv, int max_seq_len, float top_p)
     pl.g.G = G;
     pl.g.GB = GB;
     pl.g.nsub = G / GB;
-    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, GB, pl.topp, Hq);
+    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, GB, pl.topp);
     plan_layout(pl, B * Hq);
 }
 
@@ -398,7 +391,7 @@ size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld)
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, 1, true, Hq);
+    plan_geometry(pl, B, Hq, ld, 1, true);
     plan_layout(pl, B * Hq);
     return pl.total;
 }
@@ -426,7 +419,7 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, 1, true, Hq);
+    plan_geometry(pl, B, Hq, ld, 1, true);
     plan_layout(pl, B * Hq);
     pl.g.seq_lens = seq_lens;
     pl.g.page_table = nullptr;

@@ -832,8 +832,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention: one wave per (attention chunk of 2048 * NSUB tokens, query head,
-// sequence).  Top-p keeps a small, head-specific set of tokens, so the wave first lists the
+// Top-p attention: one wave per (attention chunk of 2048 tokens, query head, sequence).  Top-p keeps a small, head-specific set of tokens, so the wave first lists the
 // kept tokens of its chunk in ascending order (one pass over the 16-bit bin distances, 8
 // tokens per 16-byte load, one wave scan of packed 16-bit counts), then works through the
 // list in batches of 64 entries.  For a batch every load is issued up front: one key per
@@ -844,10 +843,10 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 // read and an add.  A chunk that keeps at most 64 tokens costs two dependent rounds of HBM
 // reads: the distances (with the query, thresholds and page ids), then the kept entries.
 // ---------------------------------------------------------------------------------------
-template <int NSUB>
 __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 {
-    constexpr int CHA = 2048 * NSUB;  // tokens of the attention chunk
+    constexpr int NSUB = 1;
+    constexpr int CHA = kTopPAttendChunk;  // tokens of the attention chunk
     constexpr int NB = 64;            // entries per batch
     constexpr int VU = NB / 16;       // value entries per 4-lane group and batch
     __shared__ uint32_t list[CHA];  // slots of the kept tokens
@@ -1052,7 +1051,7 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 __global__ __launch_bounds__(256) void k_merge(MergeParams p)
 {
     constexpr int PF = 32;  // chunks per thread loaded ahead
-    __shared__ float alpha[4096];
+    __shared__ float alpha[kMaxChunks];
     __shared__ float redf[8];
     __shared__ float part[kD];
     const DecodeGeom &g = p.g;
@@ -1166,13 +1165,8 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
     if (select) {
         // one wave per (attention chunk, query head, sequence)
         const dim3 grid(p.g.NCA, p.g.Hq, p.g.B);
-        if (p.g.CH != kTopPChunk) return hipErrorInvalidValue;
-        switch (p.g.KA) {
-        case 4: hipLaunchKernelGGL((k_attend_topp<1>), grid, dim3(64), 0, s, p); break;
-        case 8: hipLaunchKernelGGL((k_attend_topp<2>), grid, dim3(64), 0, s, p); break;
-        case 16: hipLaunchKernelGGL((k_attend_topp<4>), grid, dim3(64), 0, s, p); break;
-        default: return hipErrorInvalidValue;
-        }
+        if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_attend_topp, grid, dim3(64), 0, s, p);
     } else {
         const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
         switch (p.g.GB) {

@@ -7,6 +7,10 @@ namespace kvc {
 
 // Tokens per Top-p score chunk (one wave of the score kernel, 8 tokens per lane).
 constexpr int kTopPChunk = 512;
+// Tokens per Top-p attention chunk (one wave of the attention kernel).
+constexpr int kTopPAttendChunk = 2048;
+// Most chunks per sequence (the merge keeps one weight per chunk in LDS).
+constexpr int kMaxChunks = 16384;
 
 // Device view of the paged cache: per (page, KV head) structure of arrays.
 struct CacheView {
