@@ -279,8 +279,6 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
     constexpr int U = CH / 64;  // tokens per lane
     constexpr int kNone = -2 * kBinClamp;
     __shared__ uint32_t pbase[CH / 16 + 1];
-    __shared__ uint32_t qsh[GB * 16];
-    __shared__ float4 qps[GB];
     const DecodeGeom &g = p.g;
     const int chunk = blockIdx.x, b = blockIdx.z;
     int kvh, hq0;
@@ -291,8 +289,6 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
     const int n = min(CH, L - t0);
     const int lane = threadIdx.x;
     const int bh0 = b * g.Hq + hq0;
-    if (lane < GB * 16) qsh[lane] = p.qnib[(size_t)(bh0 + lane / 16) * 16 + (lane & 15)];
-    if (lane < GB) qps[lane] = p.qpar[bh0 + lane];
     const int logP = p.c.logP;
     const int p0 = t0 >> logP;
     const int np = ((t0 + n - 1) >> logP) - p0 + 1;
@@ -300,8 +296,18 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
         pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
                    << logP;
     __syncthreads();
+    // the query state is wave-uniform: scalar loads keep it in SGPRs, which the dot8
+    // instructions read directly
     QueryState<GB> qs;
-    read_query<GB>(qs, qsh, qps);
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qs.nib[h][i] = p.qnib[(size_t)(bh0 + h) * 16 + i];
+        const float4 pq = p.qpar[bh0 + h];
+        qs.c0[h] = pq.x;
+        qs.c1[h] = pq.y;
+        qs.sumu[h] = __float_as_int(pq.z);
+    }
     uint32_t slot[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -852,7 +858,6 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     __shared__ uint32_t list[CHA];  // slots of the kept tokens
     __shared__ float wbuf[NB];
     __shared__ uint32_t pbase[CHA / 16 + 1];
-    __shared__ uint32_t qsh[16];
     __shared__ int thr_s[CHA / kTopPChunk];
     const DecodeGeom &g = p.g;
     const int achunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -872,8 +877,6 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         const int tl = 8 * lane + 512 * j;
         if (tl < n) raw[j] = *reinterpret_cast<const uint4 *>(row + tl);
     }
-    if (lane < 16) qsh[lane] = p.qnib[bh * 16 + lane];
-    const float4 qp = p.qpar[bh];
     if (lane < CHA / kTopPChunk) {
         const int chunk = achunk * (CHA / kTopPChunk) + lane;
         thr_s[lane] = (chunk * kTopPChunk < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
@@ -942,12 +945,15 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     nlist = __builtin_amdgcn_readfirstlane(nlist);  // wave-uniform: scalar loop control
     __syncthreads();
 
-    QueryState<1> qs;
+    QueryState<1> qs;  // wave-uniform: scalar loads into SGPRs
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qs.nib[0][i] = qsh[i];
-    qs.c0[0] = qp.x;
-    qs.c1[0] = qp.y;
-    qs.sumu[0] = __float_as_int(qp.z);
+    for (int i = 0; i < 16; ++i) qs.nib[0][i] = p.qnib[bh * 16 + i];
+    {
+        const float4 qp = p.qpar[bh];
+        qs.c0[0] = qp.x;
+        qs.c1[0] = qp.y;
+        qs.sumu[0] = __float_as_int(qp.z);
+    }
     const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
     const int q4 = lane & 3;   // dims 32*q4 .. 32*q4+31
     const int eg = lane >> 2;  // entries eg + 16 u of a batch
