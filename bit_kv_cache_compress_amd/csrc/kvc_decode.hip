@@ -319,31 +319,30 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
     int lm[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) lm[h] = kNone;
-    // two halves of U/2 tokens: the second half's loads overlap the first half's arithmetic
+    // every key load of the chunk is issued before any arithmetic (the scheduling barrier
+    // keeps the compiler from sinking loads next to their uses, which would serialize the
+    // round trips)
+    uint4 kb[U];
+    uint32_t nc[U];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        uint4 kb[U / 2];
-        uint32_t nc[U / 2];
+    for (int u = 0; u < U; ++u) {
+        kb[u] = kb4[slot[u]];
+        nc[u] = p.c.key_nc[slot[u]];
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int v = 0; v < U / 2; ++v) {
-            kb[v] = kb4[slot[half * (U / 2) + v]];
-            nc[v] = p.c.key_nc[slot[half * (U / 2) + v]];
-        }
+    for (int u = 0; u < U; ++u) {
+        float s[GB];
+        int A[GB];
+        score_key<GB>(kb[u], nc[u], qs, s, A);
+        // min() rather than a select, so that the score is computed on every lane
+        // instead of behind a branch
+        const int lim = lane + 64 * u < n ? INT_MAX : kNone;
 #pragma unroll
-        for (int v = 0; v < U / 2; ++v) {
-            const int u = half * (U / 2) + v;
-            float s[GB];
-            int A[GB];
-            score_key<GB>(kb[v], nc[v], qs, s, A);
-            // min() rather than a select, so that the score is computed on every lane
-            // instead of behind a branch
-            const int lim = lane + 64 * u < n ? INT_MAX : kNone;
-#pragma unroll
-            for (int h = 0; h < GB; ++h) {
-                const int ev = min(score_bin(s[h], p.kbin), lim);
-                e[u][h] = ev;
-                lm[h] = max(lm[h], ev);
-            }
+        for (int h = 0; h < GB; ++h) {
+            const int ev = min(score_bin(s[h], p.kbin), lim);
+            e[u][h] = ev;
+            lm[h] = max(lm[h], ev);
         }
     }
 #pragma unroll
