@@ -28,10 +28,8 @@ class KVCacheDesc(ctypes.Structure):
         ("num_pages", ctypes.c_int32),
         ("rot_kind", ctypes.c_int32),
         ("rot", ctypes.c_void_p),
-        ("key_bits", ctypes.c_void_p),
-        ("key_nc", ctypes.c_void_p),
-        ("val_codes", ctypes.c_void_p),
-        ("val_sz", ctypes.c_void_p),
+        ("keys", ctypes.c_void_p),
+        ("vals", ctypes.c_void_p),
     ]
 
 

@@ -40,9 +40,11 @@ class KVCache:
     """Paged packed cache (device memory owned by torch tensors).
 
     Token t of sequence b lives in physical page ``page_table[b][t // page_size]``, slot
-    ``t % page_size``.  Arrays (per page, KV head, slot): ``key_bits`` 4 x uint32 sign words,
-    ``key_nc`` binary16 norm | binary16 correction << 16, ``val_codes`` 64 bytes of 4-bit
-    codes, ``val_sz`` binary16 scale | binary16 zero << 16 per value group.
+    ``t % page_size``.  Two arrays of records (per page, KV head, slot): ``keys`` int32
+    [..., 5] = 4 sign words and the binary16 norm | binary16 correction << 16 word; ``vals``
+    uint8 [..., 64 + 4 * 128 / value_group] = 64 bytes of 4-bit codes, then one binary16
+    scale | binary16 zero << 16 word per value group.  ``key_bits``, ``key_nc``,
+    ``val_codes`` and ``val_sz`` are views of the fields.
 
     ``rotation``: dense -> float16 [128, 128] orthogonal matrix; hadamard -> 4 uint32 sign
     words (given as an int32 or uint32 array/tensor).
@@ -71,16 +73,29 @@ class KVCache:
             r = torch.where(r >= 2**31, r - 2**32, r).to(torch.int32)
             self.rot = r.to(device).contiguous()
         shp = (self.num_pages, self.num_kv_heads, self.page_size)
-        self.key_bits = torch.zeros(shp + (D // 32,), dtype=torch.int32, device=device)
-        self.key_nc = torch.zeros(shp, dtype=torch.int32, device=device)
-        self.val_codes = torch.zeros(shp + (D // 2,), dtype=torch.uint8, device=device)
-        self.val_sz = torch.zeros(shp + (D // self.value_group,), dtype=torch.int32, device=device)
+        self.keys = torch.zeros(shp + (D // 32 + 1,), dtype=torch.int32, device=device)
+        self.vals = torch.zeros(shp + (D // 2 + 4 * (D // self.value_group),), dtype=torch.uint8, device=device)
         self.desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
-                                  self.rot_kind, self.rot.data_ptr(), self.key_bits.data_ptr(),
-                                  self.key_nc.data_ptr(), self.val_codes.data_ptr(), self.val_sz.data_ptr())
+                                  self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(), self.vals.data_ptr())
+
+    @property
+    def key_bits(self) -> torch.Tensor:
+        return self.keys[..., :HEAD_DIM // 32]
+
+    @property
+    def key_nc(self) -> torch.Tensor:
+        return self.keys[..., HEAD_DIM // 32]
+
+    @property
+    def val_codes(self) -> torch.Tensor:
+        return self.vals[..., :HEAD_DIM // 2]
+
+    @property
+    def val_sz(self) -> torch.Tensor:
+        return self.vals[..., HEAD_DIM // 2:].view(torch.int32)
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.key_bits, self.key_nc, self.val_codes, self.val_sz))
+        return self.keys.numel() * 4 + self.vals.numel()
 
 
 def append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, start_pos: torch.Tensor,

@@ -172,7 +172,7 @@ int check_cache(const kv_cache *c)
         return fail(KV_ERR_UNSUPPORTED, "num_pages * num_kv_heads * page_size above 2^32 - 1 slots");
     if (c->rot_kind != KV_ROT_DENSE && c->rot_kind != KV_ROT_HADAMARD)
         return fail(KV_ERR_ARG, "rot_kind %d is not KV_ROT_DENSE or KV_ROT_HADAMARD", c->rot_kind);
-    if (!c->rot || !c->key_bits || !c->key_nc || !c->val_codes || !c->val_sz)
+    if (!c->rot || !c->keys || !c->vals)
         return fail(KV_ERR_ARG, "cache descriptor has a NULL array");
     return KV_OK;
 }
@@ -184,10 +184,9 @@ kvc::CacheView view_of(const kv_cache *c)
     v.P = c->page_size;
     v.logP = ilog2(c->page_size);
     v.Gv = c->value_group;
-    v.key_bits = c->key_bits;
-    v.key_nc = c->key_nc;
-    v.val_codes = c->val_codes;
-    v.val_sz = c->val_sz;
+    v.lngrp = ilog2(c->head_dim / c->value_group);
+    v.keys = c->keys;
+    v.vals = c->vals;
     return v;
 }
 

@@ -47,13 +47,15 @@ __device__ __forceinline__ size_t slot_of(const AppendParams &p, long n)
     return ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
 }
 
-// Value encode of one token-head by 16 lanes (lane i holds dims 8i..8i+7):
+// Value encode of one token-head by 16 lanes (lane i holds dims 8i..8i+7) into its record:
 //   scale = fp16((max - min) / 15), zero = fp16(min) per group of Gv dims (binary32 ops),
 //   code  = clamp(rint((x - zero) / scale), 0, 15), 0 when scale == 0;
-//   byte m of the 64-byte row holds dim 2m in its low nibble, dim 2m+1 in its high nibble.
-__device__ __forceinline__ void encode_values(const float x[8], int i, int Gv, uint8_t *codes,
-                                              uint32_t *sz)
+//   byte m of the 64 code bytes holds dim 2m in its low nibble, dim 2m+1 in its high nibble;
+//   the scale/zero words follow the codes.
+__device__ __forceinline__ void encode_values(const float x[8], int i, int Gv, uint8_t *rec)
 {
+    uint8_t *codes = rec;
+    uint32_t *sz = reinterpret_cast<uint32_t *>(rec + kD / 2);
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -155,12 +157,11 @@ __global__ __launch_bounds__(256) void k_append_hadamard(AppendParams p, long N)
     uint32_t word = byte << (8 * (i & 3));
     word |= __shfl_xor(word, 1);
     word |= __shfl_xor(word, 2);
-    if ((i & 3) == 0) p.c.key_bits[slot * kKeyWords + (i >> 2)] = word;
+    if ((i & 3) == 0) key_rec(p.c, slot)[i >> 2] = word;
     ss = sum16(ss);
     sabs = sum16(sabs) / sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
-    if (i == 0) p.c.key_nc[slot] = norm_corr_word(ss, sabs);
-    encode_values(xv, i, p.c.Gv, p.c.val_codes + slot * (kD / 2),
-                  p.c.val_sz + slot * (kD / p.c.Gv));
+    if (i == 0) key_rec(p.c, slot)[kKeyWords] = norm_corr_word(ss, sabs);
+    encode_values(xv, i, p.c.Gv, val_rec(p.c, slot));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -249,8 +250,9 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
                 const long n = tile * 32 + 16 * wave + 4 * v + q;
                 if (n < N) {
                     const size_t slot = slot_of(p, n);
-                    reinterpret_cast<uint4 *>(p.c.key_bits)[slot] =
-                        make_uint4(words[v][0], words[v][1], words[v][2], words[v][3]);
+                    uint32_t *kr = key_rec(p.c, slot);
+#pragma unroll
+                    for (int q2 = 0; q2 < kKeyWords; ++q2) kr[q2] = words[v][q2];
                 }
             }
         }
@@ -270,79 +272,76 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
                 }
                 ss = sum16(ss);
                 const size_t slot = slot_of(p, n);
-                if (i == 0) p.c.key_nc[slot] = norm_corr_word(ss, sabs_s[r]);
+                if (i == 0) key_rec(p.c, slot)[kKeyWords] = norm_corr_word(ss, sabs_s[r]);
                 float xv[8];
                 load8(p.v, p.dtype, (size_t)n * kD + 8 * i, xv);
-                encode_values(xv, i, p.c.Gv, p.c.val_codes + slot * (kD / 2),
-                              p.c.val_sz + slot * (kD / p.c.Gv));
+                encode_values(xv, i, p.c.Gv, val_rec(p.c, slot));
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// Dense rotation for few token-heads (the per-step append of a decode loop): one wave per
-// token-head, lane l computes rows l and l + 64 of k' = R k as a binary64 fused chain over
-// j ascending (each product of a binary16 and a binary16/binary32 is exact, so each step is
-// the rounded sum).  Many small blocks instead of one MFMA tile keep the latency low.
+// Dense rotation for few token-heads (the per-step append of a decode loop): one 256-thread
+// block per token-head.  Thread t computes half (t >> 5) & 1 of row 32 (t >> 6) + (t & 31) of
+// k' = R k as a binary64 fused chain over 64 columns, and the two halves are added.  Every
+// load (the key, the value, the 64 binary16 entries of the row half) is issued at the start,
+// so the block costs one round of memory latency plus the 64-step chain.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_append_dense_small(AppendParams p, long N)
 {
-    __shared__ double kd[4][kD];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const long n = (long)blockIdx.x * 4 + w;
-    const bool active = n < N;  // uniform per wave
-    if (active && lane < 16) {
-        float x[8];
-        load8(p.k, p.dtype, (size_t)n * kD + 8 * lane, x);
+    __shared__ double kd[kD];
+    __shared__ double red[8];
+    __shared__ uint32_t rows[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const long n = blockIdx.x;
+    if (n >= N) return;
+    const int hc = lane >> 5;
+    const int r = 32 * w + (lane & 31);
+    const uint4 *Rr = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + r * kD + 64 * hc);
+    uint4 a[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kd[w][8 * lane + e] = (double)x[e];
+    for (int i = 0; i < 8; ++i) a[i] = Rr[i];
+    float xk[8], xv[8];
+    if (t < 16) load8(p.k, p.dtype, (size_t)n * kD + 8 * t, xk);
+    if (t >= 64 && t < 80) load8(p.v, p.dtype, (size_t)n * kD + 8 * (t - 64), xv);
+    const size_t slot = slot_of(p, n);
+    if (t < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kd[8 * t + e] = (double)xk[e];
     }
     __syncthreads();
-    if (!active) return;
-    const uint4 *R0 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + lane * kD);
-    const uint4 *R1 = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.rot) + (lane + 64) * kD);
-    double y0 = 0.0, y1 = 0.0;
-    for (int half = 0; half < 2; ++half) {
-        uint4 a[8], c[8];
+    double y = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            a[i] = R0[8 * half + i];
-            c[i] = R1[8 * half + i];
-        }
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t wa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t wa[4] = {a[i].x, a[i].y, a[i].z, a[i].w};
-            const uint32_t wc[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = 64 * half + 8 * i + e;
-                const double kj = kd[w][j];
-                y0 = fma((double)half_bits_to_float((wa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), kj, y0);
-                y1 = fma((double)half_bits_to_float((wc[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), kj, y1);
-            }
-        }
+        for (int e = 0; e < 8; ++e)
+            y = fma((double)half_bits_to_float((wa[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), kd[64 * hc + 8 * i + e], y);
     }
-    const uint64_t m0 = __ballot(!(y0 < 0.0));  // rows 0..63
-    const uint64_t m1 = __ballot(!(y1 < 0.0));  // rows 64..127
-    double sabs = fabs(y0) + fabs(y1);
-    double ss = kd[w][2 * lane] * kd[w][2 * lane] + kd[w][2 * lane + 1] * kd[w][2 * lane + 1];
+    y += __shfl_xor(y, 32);  // both halves of the row
+    const uint64_t m = __ballot(!(y < 0.0));  // bit (lane & 31) = row 32 w + (lane & 31)
+    double sabs = hc == 0 ? fabs(y) : 0.0;
+    double ss = t < kD ? kd[t] * kd[t] : 0.0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         sabs += __shfl_xor(sabs, o);
         ss += __shfl_xor(ss, o);
     }
-    const size_t slot = slot_of(p, n);
     if (lane == 0) {
-        reinterpret_cast<uint4 *>(p.c.key_bits)[slot] =
-            make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
-        p.c.key_nc[slot] = norm_corr_word(ss, sabs);
+        red[w] = sabs;
+        red[4 + w] = ss;
+        rows[w] = (uint32_t)m;
     }
-    if (lane < 16) {
-        float xv[8];
-        load8(p.v, p.dtype, (size_t)n * kD + 8 * lane, xv);
-        encode_values(xv, lane, p.c.Gv, p.c.val_codes + slot * (kD / 2), p.c.val_sz + slot * (kD / p.c.Gv));
+    __syncthreads();
+    if (t == 0) {
+        uint32_t *kr = key_rec(p.c, slot);
+#pragma unroll
+        for (int q = 0; q < kKeyWords; ++q) kr[q] = rows[q];
+        kr[kKeyWords] = norm_corr_word((red[4] + red[5]) + (red[6] + red[7]), (red[0] + red[1]) + (red[2] + red[3]));
     }
+    if (t >= 64 && t < 80)
+        encode_values(xv, t - 64, p.c.Gv, val_rec(p.c, slot));
 }
 
 }  // namespace
@@ -355,7 +354,7 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
         const long blocks = (N + 15) / 16;
         hipLaunchKernelGGL(k_append_hadamard, dim3((unsigned)blocks), dim3(256), 0, s, p, N);
     } else if (N <= 8192) {
-        hipLaunchKernelGGL(k_append_dense_small, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, p, N);
+        hipLaunchKernelGGL(k_append_dense_small, dim3((unsigned)N), dim3(256), 0, s, p, N);
     } else {
         const long tiles = (N + 31) / 32;
         const long blocks = tiles < 2048 ? tiles : 2048;

@@ -46,6 +46,15 @@ __device__ __forceinline__ size_t chunk_slot(const CacheView &c, const int *page
     return ((size_t)pages[(t >> c.logP) - p0] * c.Hkv + kvh) * c.P + (t & (c.P - 1));
 }
 
+// Key record of a slot: the 16 sign bytes (one 16-byte load at 4-byte alignment) and the
+// norm/corr word.
+__device__ __forceinline__ void load_key(const CacheView &c, size_t slot, uint4 &kb, uint32_t &nc)
+{
+    const uint32_t *kr = key_rec(c, slot);
+    __builtin_memcpy(&kb, kr, 16);
+    nc = kr[kKeyWords];
+}
+
 // Block-wide reduction of GB values per thread (256 threads); result broadcast in LDS.
 template <int GB, typename T, typename Op>
 __device__ __forceinline__ void block_reduce(T (&v)[GB], T *red /* [4][GB] */, T *out /* [GB] */, Op op)
@@ -206,7 +215,6 @@ __global__ __launch_bounds__(64) void k_score(ScoreParams p)
     int lm[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) lm[h] = -kBinClamp;
-    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
     for (int k0 = 0; k0 < n; k0 += 8 * 64) {
         uint4 kb[8];
         uint32_t nc[8];
@@ -214,9 +222,7 @@ __global__ __launch_bounds__(64) void k_score(ScoreParams p)
         for (int u = 0; u < 8; ++u) {
             const int tl = k0 + lane + 64 * u;
             if (tl < n) {
-                const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + tl);
-                kb[u] = kb4[slot];
-                nc[u] = p.c.key_nc[slot];
+                load_key(p.c, chunk_slot(p.c, pages, p0, kvh, t0 + tl), kb[u], nc[u]);
             }
         }
 #pragma unroll
@@ -314,7 +320,6 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
         const int t = t0 + min(lane + 64 * u, n - 1);
         slot[u] = pbase[(t >> logP) - p0] + (uint32_t)(t & ((1 << logP) - 1));
     }
-    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
     int e[U][GB];
     int lm[GB];
 #pragma unroll
@@ -326,8 +331,7 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
     uint32_t nc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        kb[u] = kb4[slot[u]];
-        nc[u] = p.c.key_nc[slot[u]];
+        load_key(p.c, slot[u], kb[u], nc[u]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -682,12 +686,10 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
     QueryState<GB> qs;
     read_query<GB>(qs, qsh, qps);
 
-    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
     const int sub = lane & 15;  // dims 8*sub .. 8*sub+7
     const int eg = lane >> 4;   // key within the wave-iteration
     const int gv = p.c.Gv;
     const int grp = (8 * sub) / gv;
-    const int ngrp = kD / gv;
     float acc[GB][8];
     float zacc[GB], lloc[GB], mrun[GB];
 #pragma unroll
@@ -712,9 +714,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
             for (int u = 0; u < 4; ++u) {
                 const int e = e0 + kBlock * u;
                 if (e < nb) {
-                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + bs + e);
-                    kb[u] = kb4[slot];
-                    nc[u] = p.c.key_nc[slot];
+                    load_key(p.c, chunk_slot(p.c, pages, p0, kvh, t0 + bs + e), kb[u], nc[u]);
                 }
             }
 #pragma unroll
@@ -765,9 +765,9 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
             for (int u = 0; u < U; ++u) {
                 const int e = e0 + 16 * u;
                 if (e < nb) {
-                    const size_t slot = chunk_slot(p.c, pages, p0, kvh, t0 + bs + e);
-                    cw[u] = *reinterpret_cast<const uint32_t *>(p.c.val_codes + slot * (kD / 2) + 4 * sub);
-                    szw[u] = p.c.val_sz[slot * ngrp + grp];
+                    const uint8_t *vr = val_rec(p.c, chunk_slot(p.c, pages, p0, kvh, t0 + bs + e));
+                    cw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * sub);
+                    szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
                 }
             }
 #pragma unroll
@@ -953,11 +953,9 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         qs.c1[0] = qp.y;
         qs.sumu[0] = __float_as_int(qp.z);
     }
-    const uint4 *kb4 = reinterpret_cast<const uint4 *>(p.c.key_bits);
     const int q4 = lane & 3;   // dims 32*q4 .. 32*q4+31
     const int eg = lane >> 2;  // entries eg + 16 u of a batch
     const int lgv = p.c.Gv == 32 ? 5 : 6;
-    const int lngrp = 7 - lgv;  // log2 of the groups per token
     const int grp = (32 * q4) >> lgv;
     float acc[32];
 #pragma unroll
@@ -972,15 +970,17 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         uint32_t sl[VU];
 #pragma unroll
         for (int u = 0; u < VU; ++u) sl[u] = list[bs + min(eg + 16 * u, nb - 1)];
-        const uint4 kb = kb4[slot_k];
-        const uint32_t nc = p.c.key_nc[slot_k];
+        uint4 kb;
+        uint32_t nc;
+        load_key(p.c, slot_k, kb, nc);
         uint4 cw[VU];
         uint32_t szw[VU];
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             if (u < nu) {
-                cw[u] = *reinterpret_cast<const uint4 *>(p.c.val_codes + ((size_t)sl[u] << 6) + 16 * q4);
-                szw[u] = p.c.val_sz[((size_t)sl[u] << lngrp) + grp];
+                const uint8_t *vr = val_rec(p.c, sl[u]);
+                __builtin_memcpy(&cw[u], vr + 16 * q4, 16);  // 8-byte aligned when Gv = 64
+                szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
             }
         }
         float s;

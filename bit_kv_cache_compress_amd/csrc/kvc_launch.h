@@ -12,17 +12,24 @@ constexpr int kTopPAttendChunk = 2048;
 // Most chunks per sequence (the merge keeps one weight per chunk in LDS).
 constexpr int kMaxChunks = 16384;
 
-// Device view of the paged cache: per (page, KV head) structure of arrays.
+// Device view of the paged cache: one key record and one value record per slot.
 struct CacheView {
     int Hkv;
     int P;       // page size (power of two)
     int logP;
     int Gv;      // value group (32 or 64)
-    uint32_t *key_bits;   // [pages][Hkv][P][4]
-    uint32_t *key_nc;     // [pages][Hkv][P]
-    uint8_t *val_codes;   // [pages][Hkv][P][64]
-    uint32_t *val_sz;     // [pages][Hkv][P][128/Gv]
+    int lngrp;   // log2(128 / Gv)
+    uint32_t *keys;  // [pages][Hkv][P][5]: 4 sign words, norm/corr word
+    uint8_t *vals;   // [pages][Hkv][P][64 + 4 * 128/Gv]: codes, scale/zero words
 };
+
+// Key record of a slot (20 bytes: 4 sign words, then the norm/corr word).
+__device__ __forceinline__ uint32_t *key_rec(const CacheView &c, size_t slot) { return c.keys + slot * 5; }
+// Value record of a slot (64 bytes of codes, then 128/Gv scale/zero words).
+__device__ __forceinline__ uint8_t *val_rec(const CacheView &c, size_t slot)
+{
+    return c.vals + (slot << 6) + (slot << (2 + c.lngrp));
+}
 
 struct AppendParams {
     CacheView c;

@@ -57,16 +57,22 @@ enum { KV_F16 = 0, KV_F32 = 1 };
 
 /* Paged packed cache ([host] struct describing device arrays).
  * Token t of sequence b lives in physical page page_table[b][t / page_size], slot
- * t % page_size.  For each (physical page p, KV head h) the four arrays hold, slot by slot:
- *   key_bits  [num_pages][Hkv][page_size][D/32] uint32: bit r of the rotated key k' = R k is
- *             bit r%32 of word r/32, set when k'_r >= 0.  Read as little-endian bytes this is
- *             byte r/8, bit r%8, set = +1: the bitmap order of the H1IB-KV page, section 二.3.
- *   key_nc    [num_pages][Hkv][page_size] uint32: binary16 |k| in the low half, binary16
- *             correction sum_r |k'_r| / (sqrt(D) |k|) in the high half (1.0 for k = 0).
- *   val_codes [num_pages][Hkv][page_size][D/2] uint8: 4-bit codes, dim 2m in the low nibble
- *             of byte m and dim 2m+1 in the high nibble.
- *   val_sz    [num_pages][Hkv][page_size][D/value_group] uint32: binary16 scale in the low
- *             half, binary16 zero point in the high half; value = code * scale + zero.
+ * t % page_size; the record of (page p, KV head h, slot s) has index
+ * i = (p * num_kv_heads + h) * page_size + s in each of the two arrays:
+ *   keys  uint32 [num_pages][Hkv][page_size][D/32 + 1], a 20-byte record per key:
+ *         words 0..D/32-1: bit r of the rotated key k' = R k is bit r%32 of word r/32, set
+ *           when k'_r >= 0.  Read as little-endian bytes this is byte r/8, bit r%8, set = +1:
+ *           the bitmap order of the H1IB-KV page, section 二.3.
+ *         word D/32: binary16 |k| in the low half, binary16 correction
+ *           sum_r |k'_r| / (sqrt(D) |k|) in the high half (1.0 for k = 0).
+ *   vals  uint8 [num_pages][Hkv][page_size][D/2 + 4 D/value_group], a record per value:
+ *         bytes 0..D/2-1: 4-bit codes, dim 2m in the low nibble of byte m and dim 2m+1 in
+ *           the high nibble;
+ *         then one uint32 per group of value_group dims: binary16 scale in the low half,
+ *           binary16 zero point in the high half; value = code * scale + zero.
+ * A key and a value are each one contiguous record (20 and 80 or 72 bytes), so that a
+ * decode that gathers a few selected tokens touches one or two 128-byte lines per record
+ * rather than one per field.
  * rot: KV_ROT_DENSE -> binary16 [D][D] row-major orthogonal matrix R (k' = R k);
  *      KV_ROT_HADAMARD -> uint32 [D/32] random signs (bit j set: sigma_j = -1), and
  *      R = H diag(sigma) / sqrt(D) with H the Sylvester-order Hadamard matrix.
@@ -80,10 +86,8 @@ typedef struct kv_cache {
                               must stay below 2^32 (KV_ERR_UNSUPPORTED otherwise) */
     int32_t rot_kind;      /* KV_ROT_DENSE or KV_ROT_HADAMARD */
     const void *rot;       /* device: see above */
-    uint32_t *key_bits;
-    uint32_t *key_nc;
-    uint8_t *val_codes;
-    uint32_t *val_sz;
+    uint32_t *keys;        /* device, 4-byte aligned: see above */
+    uint8_t *vals;         /* device, 4-byte aligned: see above */
 } kv_cache;
 
 /* Optional intermediate outputs of kv_decode_attend ([host] struct; every member is a

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def _desc(**kw):
     d = dict(head_dim=128, num_kv_heads=8, value_group=32, page_size=256, num_pages=16, rot_kind=0,
-             rot=0x10000, key_bits=0x10000, key_nc=0x10000, val_codes=0x10000, val_sz=0x10000)
+             rot=0x10000, keys=0x10000, vals=0x10000)
     d.update(kw)
     return L.KVCacheDesc(*[d[f] for f, _ in L.KVCacheDesc._fields_])
 
@@ -48,9 +48,11 @@ def _decode(desc, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p=1.0, ws_bytes
     (dict(page_size=100), L.KV_ERR_UNSUPPORTED),
     (dict(page_size=8), L.KV_ERR_UNSUPPORTED),
     (dict(num_pages=0), L.KV_ERR_ARG),
+    (dict(num_pages=1 << 24), L.KV_ERR_UNSUPPORTED),  # 2^35 slots: above the 32-bit slot index
     (dict(num_kv_heads=0), L.KV_ERR_ARG),
     (dict(rot_kind=7), L.KV_ERR_ARG),
-    (dict(key_nc=0), L.KV_ERR_ARG),
+    (dict(keys=0), L.KV_ERR_ARG),
+    (dict(vals=0), L.KV_ERR_ARG),
     (dict(rot=0), L.KV_ERR_ARG),
 ])
 def test_bad_cache_descriptor(kw, code):
