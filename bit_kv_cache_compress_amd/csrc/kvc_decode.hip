@@ -837,27 +837,43 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention: one wave per (attention chunk of 2048 tokens, query head, sequence).  Top-p keeps a small, head-specific set of tokens, so the wave first lists the
-// kept tokens of its chunk in ascending order (one pass over the 16-bit bin distances, 8
-// tokens per 16-byte load, one wave scan of packed 16-bit counts), then works through the
-// list in batches of 64 entries.  For a batch every load is issued up front: one key per
-// lane (sign words and the norm/correction word) and, per 4-lane group, the value words of
-// up to 4 entries (16 bytes of codes, i.e. 32 dims, and the group's scale/zero word per
-// lane).  Scores, the running max and the weights follow, then the weighted value sums
-// from registers.  Page ids become 32-bit slot bases in LDS, so an entry's slot is one LDS
-// read and an add.  A chunk that keeps at most 64 tokens costs two dependent rounds of HBM
-// reads: the distances (with the query, thresholds and page ids), then the kept entries.
+// Top-p attention: one wave per (attention chunk of 2048 tokens, query head, sequence).
+// Top-p keeps a small, head-specific set of tokens, so the wave first lists the kept tokens
+// of its chunk in ascending order (one pass over the 16-bit bin distances, 8 tokens per
+// 16-byte load, one wave scan of packed 16-bit counts), then works through the list in
+// batches of 64 entries.  For a batch every load is issued up front: one key record per lane
+// and, per 4-lane group, the value records of up to 4 entries (16 bytes of codes, i.e. 32
+// dims, and the group's scale/zero word per lane).  Scores, the running max and the weights
+// follow, then the weighted value sums from registers.  A chunk that keeps at most 64 tokens
+// costs two dependent rounds of HBM reads: the distances (with the query, thresholds and
+// page ids), then the kept records.
+// Distances past a sequence's end (within its last 512-token score chunk) are 8192, above
+// every threshold, so only whole 16-byte groups need a bound check; a group whose smallest
+// distance is above the threshold (most of them) costs a few packed 16-bit ops.
 // ---------------------------------------------------------------------------------------
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dpp_ror(float v, int k)
+{
+    // row_ror:k within each 16-lane row (DPP control 0x120 + k); every lane has a source
+    const int r = k == 4 ? __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true)
+                         : __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true);
+    return __int_as_float(r);
+}
+
 __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 {
-    constexpr int NSUB = 1;
     constexpr int CHA = kTopPAttendChunk;  // tokens of the attention chunk
-    constexpr int NB = 64;            // entries per batch
-    constexpr int VU = NB / 16;       // value entries per 4-lane group and batch
-    __shared__ uint32_t list[CHA];  // slots of the kept tokens
-    __shared__ float wbuf[NB];
+    constexpr int NJ = CHA / 512;          // 16-byte distance loads per lane
+    constexpr int NB = 64;                 // entries per batch
+    constexpr int VU = NB / 16;            // value entries per 4-lane group and batch
+    __shared__ union {
+        uint16_t list[CHA];                // chunk offsets of the kept tokens
+        float4 red[4][4][9];               // final sums: [row][dim block][32 dims + zero term]
+    } sh;
+    __shared__ float wbuf[64];
     __shared__ uint32_t pbase[CHA / 16 + 1];
-    __shared__ int thr_s[CHA / kTopPChunk];
+    uint16_t *list = sh.list;
     const DecodeGeom &g = p.g;
     const int achunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int kvh = h / g.G;
@@ -869,16 +885,18 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     const size_t bh = (size_t)b * g.Hq + h;
 
     // ---- round 1: distances (tokens 8 lane + 512 j .. + 7), query, thresholds, page ids
-    uint4 raw[4 * NSUB];
+    uint4 raw[NJ];
     const uint16_t *row = p.dl + bh * g.Lpad + t0;
 #pragma unroll
-    for (int j = 0; j < 4 * NSUB; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int tl = 8 * lane + 512 * j;
         if (tl < n) raw[j] = *reinterpret_cast<const uint4 *>(row + tl);
     }
-    if (lane < CHA / kTopPChunk) {
-        const int chunk = achunk * (CHA / kTopPChunk) + lane;
-        thr_s[lane] = (chunk * kTopPChunk < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
+    int thr[NJ];  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int chunk = achunk * NJ + j;
+        thr[j] = (chunk * kTopPChunk < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
     }
     const int logP = p.c.logP;
     const int p0 = t0 >> logP;
@@ -886,64 +904,6 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     for (int i = lane; i < np; i += 64)
         pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
                    << logP;
-    __syncthreads();
-
-    // ---- kept tokens, listed in ascending order
-    uint64_t cnt4[NSUB];
-    uint32_t keep[4 * NSUB];
-#pragma unroll
-    for (int j = 0; j < 4 * NSUB; ++j) {
-        const int tl = 8 * lane + 512 * j;
-        uint32_t m = 0u;
-        if (tl < n) {
-            const int thr = thr_s[j];  // 512 tokens of a score chunk per j
-            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                m |= (tl + e < n && d <= thr) ? (1u << e) : 0u;
-            }
-        }
-        keep[j] = m;
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        cnt4[s] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cnt4[s] |= (uint64_t)__builtin_popcount(keep[4 * s + j]) << (16 * j);
-    }
-    int nlist = 0;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        // wave-wide inclusive scan of four packed 16-bit counts (a field never exceeds 512)
-        uint64_t incl = cnt4[s];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint64_t y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
-        const uint64_t total = __shfl(incl, 63);
-        const uint64_t before = incl - cnt4[s];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int off = nlist + (int)((before >> (16 * j)) & 0xFFFFu);
-            uint32_t m = keep[4 * s + j];
-            if (m) {
-                // the 8 tokens of a 16-byte load share a page (P >= 16)
-                const int t = t0 + 8 * lane + 512 * (4 * s + j);
-                const uint32_t sb = pbase[(t >> logP) - p0] + (uint32_t)(t & ((1 << logP) - 1));
-                while (m) {
-                    const int e = __builtin_ctz(m);
-                    m &= m - 1u;
-                    list[off++] = sb + (uint32_t)e;
-                }
-            }
-            nlist += (int)((total >> (16 * j)) & 0xFFFFu);
-        }
-    }
-    nlist = __builtin_amdgcn_readfirstlane(nlist);  // wave-uniform: scalar loop control
-    __syncthreads();
-
     QueryState<1> qs;  // wave-uniform: scalar loads into SGPRs
 #pragma unroll
     for (int i = 0; i < 16; ++i) qs.nib[0][i] = p.qnib[bh * 16 + i];
@@ -953,10 +913,56 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         qs.c1[0] = qp.y;
         qs.sumu[0] = __float_as_int(qp.z);
     }
+
+    // ---- kept tokens, listed in ascending order
+    uint32_t keep[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int tl = 8 * lane + 512 * j;
+        uint32_t m = 0u;
+        if (tl < n) {
+            u16x2 w2[4];
+            __builtin_memcpy(w2, &raw[j], 16);
+            const u16x2 mn = __builtin_elementwise_min(__builtin_elementwise_min(w2[0], w2[1]),
+                                                       __builtin_elementwise_min(w2[2], w2[3]));
+            if ((int)min(mn.x, mn.y) <= thr[j]) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m |= ((int)w2[e >> 1][e & 1] <= thr[j]) ? (1u << e) : 0u;
+            }
+        }
+        keep[j] = m;
+    }
+    uint64_t cnt4 = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cnt4 |= (uint64_t)__builtin_popcount(keep[j]) << (16 * j);
+    // wave-wide inclusive scan of the packed 16-bit counts (a field never exceeds 512)
+    uint64_t incl = cnt4;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const uint64_t total = __shfl(incl, 63);
+    const uint64_t before = incl - cnt4;
+    int nlist = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        int off = nlist + (int)((before >> (16 * j)) & 0xFFFFu);
+        uint32_t m = keep[j];
+        while (m) {
+            const int e = __builtin_ctz(m);
+            m &= m - 1u;
+            list[off++] = (uint16_t)(8 * lane + 512 * j + e);
+        }
+        nlist += (int)((total >> (16 * j)) & 0xFFFFu);
+    }
+    nlist = __builtin_amdgcn_readfirstlane(nlist);  // wave-uniform: scalar loop control
+    __syncthreads();
+
     const int q4 = lane & 3;   // dims 32*q4 .. 32*q4+31
     const int eg = lane >> 2;  // entries eg + 16 u of a batch
-    const int lgv = p.c.Gv == 32 ? 5 : 6;
-    const int grp = (32 * q4) >> lgv;
+    const int grp = (32 * q4) / p.c.Gv;
+    const uint32_t tmask = (1u << logP) - 1u;
     float acc[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
@@ -965,14 +971,16 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     for (int bs = 0; bs < nlist; bs += NB) {
         const int nb = min(NB, nlist - bs);
         const int nu = (nb + 15) >> 4;  // value rounds of this batch (uniform)
-        // ---- round 2: the batch's keys and value words (entries past nb re-read the last)
-        const uint32_t slot_k = list[bs + min(lane, nb - 1)];
-        uint32_t sl[VU];
+        // ---- round 2: the batch's key and value records (entries past nb re-read the last)
+        uint32_t sl[VU + 1];
 #pragma unroll
-        for (int u = 0; u < VU; ++u) sl[u] = list[bs + min(eg + 16 * u, nb - 1)];
+        for (int u = 0; u <= VU; ++u) {
+            const uint32_t t = (uint32_t)(t0 + list[bs + min(u < VU ? eg + 16 * u : lane, nb - 1)]);
+            sl[u] = pbase[(t >> logP) - p0] + (t & tmask);
+        }
         uint4 kb;
         uint32_t nc;
-        load_key(p.c, slot_k, kb, nc);
+        load_key(p.c, sl[VU], kb, nc);
         uint4 cw[VU];
         uint32_t szw[VU];
 #pragma unroll
@@ -1026,20 +1034,37 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         __syncthreads();  // wbuf is rewritten by the next batch
     }
 
-    // ---- weight sum, then the value sums reduced over the 16 entry groups
+    // ---- weight sum, then the value sums over the 16 entry groups: the 4 groups of a
+    // 16-lane row by DPP rotations, the 4 rows through LDS (the list's space: the last
+    // batch's barrier follows every read of the list)
     const float lsum = wave_sum(lloc);
 #pragma unroll
-    for (int o = 4; o < 64; o <<= 1) {
-        zacc += __shfl_xor(zacc, o);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) acc[j] += __shfl_xor(acc[j], o);
+    for (int j = 0; j < 32; ++j) {
+        acc[j] += dpp_ror(acc[j], 4);
+        acc[j] += dpp_ror(acc[j], 8);
     }
-    const size_t pidx = bh * g.NCA + achunk;
-    if (lane < 4) {
-        float4 *dst = reinterpret_cast<float4 *>(p.po + pidx * kD + 32 * lane);
+    zacc += dpp_ror(zacc, 4);
+    zacc += dpp_ror(zacc, 8);
+    if ((lane & 15) < 4) {
+        float4 *dst = sh.red[lane >> 4][q4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            dst[k] = make_float4(acc[4 * k] + zacc, acc[4 * k + 1] + zacc, acc[4 * k + 2] + zacc, acc[4 * k + 3] + zacc);
+        for (int k = 0; k < 8; ++k) dst[k] = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
+        dst[8].x = zacc;
+    }
+    __syncthreads();
+    const size_t pidx = bh * g.NCA + achunk;
+    {
+        // lane l: dims 2l, 2l + 1 (dim block l / 16, float4 (l & 15) / 2, half l & 1)
+        const int qb = lane >> 4, f4 = (lane & 15) >> 1, hf = lane & 1;
+        float v0 = 0.0f, v1 = 0.0f, z = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 a = sh.red[r][qb][f4];
+            v0 += hf ? a.z : a.x;
+            v1 += hf ? a.w : a.y;
+            z += sh.red[r][qb][8].x;
+        }
+        reinterpret_cast<float2 *>(p.po + pidx * kD)[lane] = make_float2(v0 + z, v1 + z);
     }
     if (lane == 0) {
         p.pm[pidx] = mrun;
