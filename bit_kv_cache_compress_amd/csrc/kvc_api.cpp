@@ -60,7 +60,7 @@ int chunk_cap(int GB, bool topp)
 //  gives at least 2048 blocks (8 per compute unit) over (chunk, KV-head group, sequence) and
 //  no more than 4096 chunks; one attention block per chunk (KA = 1).
 //  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention wave
-//  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 4 score chunks.
+//  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 2 score chunks.
 void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
 {
     int CH, KA = 1;

@@ -837,7 +837,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention: one wave per (attention chunk of 2048 tokens, query head, sequence).
+// Top-p attention: one wave per (attention chunk of 1024 tokens, query head, sequence).
 // Top-p keeps a small, head-specific set of tokens, so the wave first lists the kept tokens
 // of its chunk in ascending order (one pass over the 16-bit bin distances, 8 tokens per
 // 16-byte load, one wave scan of packed 16-bit counts), then works through the list in
@@ -1073,60 +1073,68 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Split-K merge, one 256-thread block per (query head, sequence):
+// Split-K merge, one 1024-thread block per (query head, sequence):
 //   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
-// Thread (d, half) sums the chunks of one parity for dim d.  The value sums of the first 64
-// chunks are loaded first, so that their reads overlap the max and weight reductions.
+// Thread (d, slice) sums the chunks c = slice (mod 8) for dim d.  The value sums of the
+// first 256 chunks are loaded first, so that their reads overlap the max and weight
+// reductions.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_merge(MergeParams p)
+__global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 {
-    constexpr int PF = 32;  // chunks per thread loaded ahead
+    constexpr int kT = 1024, NS = kT / kD;  // threads, chunk slices
+    constexpr int PF = 32;                  // chunks per thread loaded ahead
     __shared__ float alpha[kMaxChunks];
-    __shared__ float redf[8];
-    __shared__ float part[kD];
+    __shared__ float redf[2][kT / 64];
+    __shared__ float part[NS][kD];
     const DecodeGeom &g = p.g;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)b * g.Hq + h;
     const int L = g.seq_lens[b];
     const int CHa = g.CH * g.KA;
     const int nch = L > 0 ? (L + CHa - 1) / CHa : 0;
-    const int d = tid & (kD - 1), half = tid >> 7;
+    const int d = tid & (kD - 1), sl = tid >> 7;
     const float *po = p.po + bh * g.NCA * kD + d;
     float v[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-        const int c = half + 2 * i;
+        const int c = sl + NS * i;
         v[i] = c < nch ? po[(size_t)c * kD] : 0.0f;
     }
     float m = -INFINITY;
-    for (int c = tid; c < nch; c += kBlock) m = fmaxf(m, p.pm[bh * g.NCA + c]);
+    for (int c = tid; c < nch; c += kT) m = fmaxf(m, p.pm[bh * g.NCA + c]);
     m = wave_max(m);
-    if (lane == 0) redf[wave] = m;
+    if (lane == 0) redf[0][wave] = m;
     __syncthreads();
-    const float M = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+    float M = redf[0][0];
+#pragma unroll
+    for (int w = 1; w < kT / 64; ++w) M = fmaxf(M, redf[0][w]);
     float den = 0.0f;
-    for (int c = tid; c < nch; c += kBlock) {
+    for (int c = tid; c < nch; c += kT) {
         const float mc = p.pm[bh * g.NCA + c];
         const float a = (mc == -INFINITY) ? 0.0f : exp2f((mc - M) * p.klog);
         alpha[c] = a;
         den = fmaf(a, p.pl[bh * g.NCA + c], den);
     }
     den = wave_sum(den);
-    if (lane == 0) redf[4 + wave] = den;
+    if (lane == 0) redf[1][wave] = den;
     __syncthreads();  // also publishes alpha
-    const float D = (redf[4] + redf[5]) + (redf[6] + redf[7]);
+    float D = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kT / 64; ++w) D += redf[1][w];
     float num = 0.0f;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-        const int c = half + 2 * i;
+        const int c = sl + NS * i;
         if (c < nch) num = fmaf(alpha[c], v[i], num);
     }
-    for (int c = half + 2 * PF; c < nch; c += 2) num = fmaf(alpha[c], po[(size_t)c * kD], num);
-    if (half == 1) part[d] = num;
+    for (int c = sl + NS * PF; c < nch; c += NS) num = fmaf(alpha[c], po[(size_t)c * kD], num);
+    part[sl][d] = num;
     __syncthreads();
-    if (half == 0) {
-        num += part[d];
-        p.out[bh * kD + d] = D > 0.0f ? num / D : 0.0f;
+    if (tid < kD) {
+        float t = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) t += part[s2][d];
+        p.out[bh * kD + d] = D > 0.0f ? t / D : 0.0f;
     }
 }
 
@@ -1210,7 +1218,7 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_merge, dim3(p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_merge, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 

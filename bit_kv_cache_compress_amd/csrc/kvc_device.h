@@ -88,7 +88,9 @@ __device__ __forceinline__ uint64_t lanemask_lt()
 __device__ __forceinline__ int score_bin(float s, float kbin)
 {
     const float x = fminf(fmaxf(s * kbin, -(float)kBinClamp), (float)kBinClamp);  // NaN -> bottom
-    return (int)floorf(x);
+    int e;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(e) : "v"(x));  // floor, then to int32 (exact here)
+    return e;
 }
 
 // ---------------------------------------------------------------------------------------

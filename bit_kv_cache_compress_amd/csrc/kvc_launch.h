@@ -8,7 +8,7 @@ namespace kvc {
 // Tokens per Top-p score chunk (one wave of the score kernel, 8 tokens per lane).
 constexpr int kTopPChunk = 512;
 // Tokens per Top-p attention chunk (one wave of the attention kernel).
-constexpr int kTopPAttendChunk = 2048;
+constexpr int kTopPAttendChunk = 1024;
 // Most chunks per sequence (the merge keeps one weight per chunk in LDS).
 constexpr int kMaxChunks = 16384;
 
