@@ -48,29 +48,28 @@ struct Plan {
     size_t total;
 };
 
-// Largest chunk of a full-softmax attention block: its LDS score buffer holds CH x GB
-// floats (32 KB).
-int chunk_cap(int GB, bool topp)
+// Largest attention chunk (tokens of one attention wave).
+int chunk_cap(bool topp)
 {
-    return topp ? kvc::kTopPAttendChunk : 8192 / GB;
+    return topp ? kvc::kTopPAttendChunk : kvc::kMaxFullChunk;
 }
 
 // Geometry.
-//  Full softmax: chunks of CH tokens, the largest power of two in [256, 8192/GB] that still
-//  gives at least 2048 blocks (8 per compute unit) over (chunk, KV-head group, sequence) and
-//  no more than 4096 chunks; one attention block per chunk (KA = 1).
+//  Full softmax: chunks of CH tokens, the largest power of two in [256, 2048] that still
+//  gives at least 4096 waves (16 per compute unit) over (chunk, KV-head group, sequence)
+//  and no more than kMaxChunks chunks; one attention wave per chunk (KA = 1).
 //  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention wave
 //  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 2 score chunks.
-void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, int GB, bool topp)
+void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, bool topp)
 {
     int CH, KA = 1;
     if (topp) {
         CH = kvc::kTopPChunk;
         KA = kvc::kTopPAttendChunk / CH;
     } else {
-        CH = chunk_cap(GB, false);
+        CH = chunk_cap(false);
         const long units = (long)B * rows_per_seq;
-        while (CH > 256 && units * ((max_len + CH - 1) / CH) < 2048 && (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
+        while (CH > 256 && units * ((max_len + CH - 1) / CH) < 4096 && (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
             CH >>= 1;
     }
     pl.g.CH = CH;
@@ -135,10 +134,9 @@ int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, f
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(KV_ERR_UNSUPPORTED, "GQA group Hq/Hkv = %d: supported groups are 1, 2, 4, 8", G);
     if (!(top_p > 0.0f)) return fail(KV_ERR_ARG, "top_p must be > 0 (got %g)", (double)top_p);
-    const int GB = G < 4 ? G : 4;
-    const long limit = (long)chunk_cap(GB, top_p < 1.0f) * kvc::kMaxChunks;  // merge weights fit in LDS
+    const long limit = (long)chunk_cap(top_p < 1.0f) * kvc::kMaxChunks;  // merge weights fit in LDS
     if (max_seq_len > limit)
-        return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld for this head grouping", max_seq_len, limit);
+        return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld", max_seq_len, limit);
     return KV_OK;
 }
 
@@ -154,7 +152,7 @@ void make_plan(Plan &pl, int B, int Hq, int Hkv, int max_seq_len, float top_p)
     pl.g.G = G;
     pl.g.GB = GB;
     pl.g.nsub = G / GB;
-    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, GB, pl.topp);
+    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, pl.topp);
     plan_layout(pl, B * Hq);
 }
 
@@ -390,7 +388,7 @@ size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld)
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, 1, true);
+    plan_geometry(pl, B, Hq, ld, true);
     plan_layout(pl, B * Hq);
     return pl.total;
 }
@@ -418,7 +416,7 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, 1, true);
+    plan_geometry(pl, B, Hq, ld, true);
     plan_layout(pl, B * Hq);
     pl.g.seq_lens = seq_lens;
     pl.g.page_table = nullptr;

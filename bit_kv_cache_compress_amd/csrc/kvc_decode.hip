@@ -20,25 +20,12 @@ namespace kvc {
 
 namespace {
 
-constexpr int kMaxAttendChunk = 8192;  // tokens of an attention chunk
-constexpr int kMaxChunkPages = kMaxAttendChunk / 16 + 1;  // page ids of a chunk (P >= 16)
-
 // First query head of block (hb = kv head * nsub + sub) and its KV head.
 __device__ __forceinline__ void block_heads(const DecodeGeom &g, int hb, int &kvh, int &hq0)
 {
     kvh = hb / g.nsub;
     const int sub = hb - kvh * g.nsub;
     hq0 = kvh * g.G + sub * g.GB;
-}
-
-// Page ids of the chunk [t0, t0 + n) into LDS; returns the first page index.
-__device__ __forceinline__ int load_chunk_pages(const DecodeGeom &g, int logP, int b, int t0, int n,
-                                                int *pages)
-{
-    const int p0 = t0 >> logP, p1 = (t0 + n - 1) >> logP;
-    for (int i = threadIdx.x; i <= p1 - p0; i += kBlock) pages[i] = g.page_table[(size_t)b * g.max_pages + p0 + i];
-    __syncthreads();
-    return p0;
 }
 
 __device__ __forceinline__ size_t chunk_slot(const CacheView &c, const int *pages, int p0, int kvh, int t)
@@ -654,185 +641,148 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Full-softmax attention over one chunk of CH tokens for GB query heads of one KV head.
-// Keys are processed in batches: score them (binary x INT4), update the running max m,
-// turn scores into weights exp2((s - m) log2e/sqrt(D)) (earlier batches are rescaled when
-// m grows), and accumulate weights x decoded 4-bit values (16 lanes per key, 8 dims per
-// lane; the zero point is accumulated once per group).  The block writes (m, sum of
-// weights, weighted value sums) for the merge.
+// Full-softmax attention: one wave per (chunk of CH tokens, KV head, sequence) and GB <= 4
+// query heads of that KV head.  The chunk is walked in batches of 64 tokens.  For a batch
+// every load is issued up front: one key record per lane (the lane's token) and, per 16-lane
+// group, the value words of 16 tokens (4 bytes of codes, i.e. 8 dims, and the group's
+// scale/zero word per lane).  The lane scores its token for the GB heads (binary x INT4),
+// the running max of each head is updated with a wave reduction (earlier batches are
+// rescaled when it grows), the weights exp2((s - m) log2e/sqrt(D)) go through LDS, and each
+// lane accumulates weight x decoded value for its 8 dims (the zero point once per token).
+// The wave writes (m, sum of weights, weighted value sums) per head for the merge.
 // ---------------------------------------------------------------------------------------
 template <int GB>
-__global__ __launch_bounds__(256) void k_attend(AttendParams p)
+__global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 {
-    constexpr int kBatch = 8192 / GB;  // keys per batch (scores in LDS)
-    __shared__ float wbuf[kBatch * GB];  // scores, then weights: [key][GB]
-    __shared__ int pages[kMaxChunkPages];
-    __shared__ uint32_t qsh[GB * 16];
-    __shared__ float4 qps[GB];
-    __shared__ float redf[4 * GB];
-    __shared__ float mh[GB];
+    constexpr int NB = 64;        // tokens per batch
+    constexpr int VU = NB / 4;    // value tokens per 16-lane group and batch
+    __shared__ float wbuf[NB][GB];
+    __shared__ uint32_t pbase[kMaxFullChunk / 16 + 1];
     const DecodeGeom &g = p.g;
-    const int achunk = blockIdx.x, b = blockIdx.z;
+    const int chunk = blockIdx.x, b = blockIdx.z;
     int kvh, hq0;
     block_heads(g, blockIdx.y, kvh, hq0);
     const int L = g.seq_lens[b];
-    const int t0 = achunk * g.CH;
+    const int t0 = chunk * g.CH;
     if (t0 >= L) return;
     const int n = min(g.CH, L - t0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh0 = (size_t)b * g.Hq + hq0;
-    stage_query<GB>(p.qnib, p.qpar, (int)bh0, qsh, qps);
-    const int p0 = load_chunk_pages(g, p.c.logP, b, t0, n, pages);  // includes a barrier
-    QueryState<GB> qs;
-    read_query<GB>(qs, qsh, qps);
+    const int lane = threadIdx.x;
+    const int bh0 = b * g.Hq + hq0;
+    const int logP = p.c.logP;
+    const int p0 = t0 >> logP;
+    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
+    for (int i = lane; i < np; i += 64)
+        pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
+                   << logP;
+    QueryState<GB> qs;  // wave-uniform: scalar loads into SGPRs
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qs.nib[h][i] = p.qnib[(size_t)(bh0 + h) * 16 + i];
+        const float4 pq = p.qpar[bh0 + h];
+        qs.c0[h] = pq.x;
+        qs.c1[h] = pq.y;
+        qs.sumu[h] = __float_as_int(pq.z);
+    }
+    __syncthreads();
 
     const int sub = lane & 15;  // dims 8*sub .. 8*sub+7
-    const int eg = lane >> 4;   // key within the wave-iteration
-    const int gv = p.c.Gv;
-    const int grp = (8 * sub) / gv;
-    float acc[GB][8];
-    float zacc[GB], lloc[GB], mrun[GB];
+    const int eg = lane >> 4;   // value tokens eg + 4 u of a batch
+    const int grp = (8 * sub) / p.c.Gv;
+    const uint32_t tmask = (1u << logP) - 1u;
+    float acc[GB][8], zacc[GB], lsum[GB], mrun[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
         zacc[h] = 0.0f;
-        lloc[h] = 0.0f;
+        lsum[h] = 0.0f;
         mrun[h] = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
     }
 
-    for (int bs = 0; bs < n; bs += kBatch) {
-        const int nb = min(kBatch, n - bs);
-        // ---- scores of the batch, 4 keys in flight per thread
-        float mloc[GB];
-#pragma unroll
-        for (int h = 0; h < GB; ++h) mloc[h] = -INFINITY;
-        for (int e0 = tid; e0 < nb; e0 += 4 * kBlock) {
-            uint4 kb[4];
-            uint32_t nc[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + kBlock * u;
-                if (e < nb) {
-                    load_key(p.c, chunk_slot(p.c, pages, p0, kvh, t0 + bs + e), kb[u], nc[u]);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + kBlock * u;
-                if (e < nb) {
-                    float sc[GB];
-                    int A[GB];
-                    score_key<GB>(kb[u], nc[u], qs, sc, A);
-#pragma unroll
-                    for (int h = 0; h < GB; ++h) {
-                        wbuf[e * GB + h] = sc[h];
-                        mloc[h] = fmaxf(mloc[h], sc[h]);
-                    }
-                }
-            }
+    for (int bs = 0; bs < n; bs += NB) {
+        const int nb = min(NB, n - bs);
+        // ---- the batch's key and value records (tokens past nb re-read the last one)
+        uint4 kb;
+        uint32_t nc;
+        {
+            const uint32_t t = (uint32_t)(t0 + bs + min(lane, nb - 1));
+            load_key(p.c, pbase[(t >> logP) - p0] + (t & tmask), kb, nc);
         }
-        block_reduce<GB>(mloc, redf, mh, MaxF());
-        // ---- running max, rescale earlier batches, weights
-        float mnew[GB];
+        uint32_t cw[VU], szw[VU];
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            const uint32_t t = (uint32_t)(t0 + bs + min(eg + 4 * u, nb - 1));
+            const uint8_t *vr = val_rec(p.c, pbase[(t >> logP) - p0] + (t & tmask));
+            cw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * sub);
+            szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
+        }
+        float s[GB];
+        {
+            int A[GB];
+            score_key<GB>(kb, nc, qs, s, A);
+        }
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-            mnew[h] = fmaxf(mrun[h], mh[h]);
-            const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew[h]) * p.klog);
+            if (lane >= nb) s[h] = -INFINITY;
+            const float mnew = fmaxf(mrun[h], wave_max(s[h]));
+            const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
             if (scale != 1.0f) {
                 zacc[h] *= scale;
-                lloc[h] *= scale;
+                lsum[h] *= scale;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[h][j] *= scale;
             }
-            mrun[h] = mnew[h];
-        }
-        for (int e = tid; e < nb; e += kBlock) {
-#pragma unroll
-            for (int h = 0; h < GB; ++h) {
-                const float v = wbuf[e * GB + h];
-                const float w = (v == -INFINITY) ? 0.0f : exp2f((v - mnew[h]) * p.klog);
-                wbuf[e * GB + h] = w;
-                lloc[h] += w;
-            }
+            mrun[h] = mnew;
+            const float w = (s[h] == -INFINITY) ? 0.0f : exp2f((s[h] - mnew) * p.klog);
+            lsum[h] += w;
+            wbuf[lane][h] = w;
         }
         __syncthreads();
-        // ---- weighted sums of the decoded values, 4 keys in flight per lane group
-        constexpr int U = 4;
-        for (int e0 = wave * 4 + eg; e0 < nb; e0 += 16 * U) {
-            uint32_t cw[U], szw[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = e0 + 16 * u;
-                if (e < nb) {
-                    const uint8_t *vr = val_rec(p.c, chunk_slot(p.c, pages, p0, kvh, t0 + bs + e));
-                    cw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * sub);
-                    szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
-                }
+        for (int u = 0; u < VU; ++u) {
+            const int e = eg + 4 * u;  // weight 0 past nb
+            const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
+            const float zf = half_bits_to_float(szw[u] >> 16);
+            float c[8];
+            const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                c[2 * m] = (float)((lo >> (8 * m)) & 0xFFu);
+                c[2 * m + 1] = (float)((hi >> (8 * m)) & 0xFFu);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = e0 + 16 * u;
-                if (e < nb) {
-                    const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
-                    const float zf = half_bits_to_float(szw[u] >> 16);
-                    float c[8];
-                    const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
+            for (int h = 0; h < GB; ++h) {
+                const float w = wbuf[e][h];
+                const float ws = w * sf;
+                zacc[h] = fmaf(w, zf, zacc[h]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        c[2 * m] = (float)((lo >> (8 * m)) & 0xFFu);
-                        c[2 * m + 1] = (float)((hi >> (8 * m)) & 0xFFu);
-                    }
-#pragma unroll
-                    for (int h = 0; h < GB; ++h) {
-                        const float w = wbuf[e * GB + h];
-                        const float ws = w * sf;
-                        zacc[h] = fmaf(w, zf, zacc[h]);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(ws, c[j], acc[h][j]);
-                    }
-                }
+                for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(ws, c[j], acc[h][j]);
             }
         }
         __syncthreads();  // wbuf is rewritten by the next batch
     }
 
-    // ---- weight sums, then the value sums reduced over key lanes and waves
-    __shared__ float lsum[GB];
-    block_reduce<GB>(lloc, redf, lsum, SumF());
+    // ---- weight sums, then the value sums over the 4 token groups (lanes sub, sub + 16, ...)
+    const size_t pidx = (size_t)bh0 * g.NCA + chunk;  // partial of head bh0 (+ h * NCA)
 #pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
+    for (int h = 0; h < GB; ++h) {
+        const float l = wave_sum(lsum[h]);
 #pragma unroll
-        for (int h = 0; h < GB; ++h) {
+        for (int o = 16; o < 64; o <<= 1) {
             zacc[h] += __shfl_xor(zacc[h], o);
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[h][j] += __shfl_xor(acc[h][j], o);
         }
-    }
-    if (eg == 0) {
-#pragma unroll
-        for (int h = 0; h < GB; ++h) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) wbuf[((wave * GB + h) * 16 + sub) * 9 + j] = acc[h][j];
-            wbuf[((wave * GB + h) * 16 + sub) * 9 + 8] = zacc[h];
+        if (lane < 16) {
+            float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + 8 * lane);
+            dst[0] = make_float4(acc[h][0] + zacc[h], acc[h][1] + zacc[h], acc[h][2] + zacc[h], acc[h][3] + zacc[h]);
+            dst[1] = make_float4(acc[h][4] + zacc[h], acc[h][5] + zacc[h], acc[h][6] + zacc[h], acc[h][7] + zacc[h]);
         }
-    }
-    __syncthreads();
-    const size_t pidx = (bh0 * g.NCA + achunk);  // partial of head bh0 (+ h * NCA)
-    for (int o = tid; o < GB * kD; o += kBlock) {
-        const int h = o / kD, d = o - h * kD;
-        const int sb = d >> 3, j = d & 7;
-        float v = 0.0f, z = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            v += wbuf[((w * GB + h) * 16 + sb) * 9 + j];
-            z += wbuf[((w * GB + h) * 16 + sb) * 9 + 8];
+        if (lane == 0) {
+            p.pm[pidx + (size_t)h * g.NCA] = mrun[h];
+            p.pl[pidx + (size_t)h * g.NCA] = l;
         }
-        p.po[(pidx + (size_t)h * g.NCA) * kD + d] = v + z;
-    }
-    if (tid < GB) {
-        p.pm[pidx + (size_t)tid * g.NCA] = mrun[tid];
-        p.pl[pidx + (size_t)tid * g.NCA] = lsum[tid];
     }
 }
 
@@ -1199,18 +1149,19 @@ hipError_t launch_select(const SelectParams &p, hipStream_t s)
 
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 {
-    const dim3 blk(kBlock);
     if (select) {
         // one wave per (attention chunk, query head, sequence)
         const dim3 grid(p.g.NCA, p.g.Hq, p.g.B);
         if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_attend_topp, grid, dim3(64), 0, s, p);
     } else {
+        // one wave per (chunk, KV-head group, sequence)
         const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
+        if (p.g.CH > kMaxFullChunk || p.g.KA != 1) return hipErrorInvalidValue;
         switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_attend<1>), grid, blk, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_attend<2>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_attend<4>), grid, blk, 0, s, p); break;
+        case 1: hipLaunchKernelGGL((k_attend_full<1>), grid, dim3(64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_attend_full<2>), grid, dim3(64), 0, s, p); break;
+        default: hipLaunchKernelGGL((k_attend_full<4>), grid, dim3(64), 0, s, p); break;
         }
     }
     return hipGetLastError();

@@ -9,6 +9,8 @@ namespace kvc {
 constexpr int kTopPChunk = 512;
 // Tokens per Top-p attention chunk (one wave of the attention kernel).
 constexpr int kTopPAttendChunk = 1024;
+// Most tokens per full-softmax attention chunk (one wave of the attention kernel).
+constexpr int kMaxFullChunk = 2048;
 // Most chunks per sequence (the merge keeps one weight per chunk in LDS).
 constexpr int kMaxChunks = 16384;
 
