@@ -651,11 +651,12 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 // lane accumulates weight x decoded value for its 8 dims (the zero point once per token).
 // The wave writes (m, sum of weights, weighted value sums) per head for the merge.
 // ---------------------------------------------------------------------------------------
-template <int GB>
+template <int GB, int GV>
 __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 {
     constexpr int NB = 64;        // tokens per batch
     constexpr int VU = NB / 4;    // value tokens per 16-lane group and batch
+    constexpr int VREC = kD / 2 + 4 * (kD / GV);  // bytes of a value record
     __shared__ float wbuf[NB][GB];
     __shared__ uint32_t pbase[kMaxFullChunk / 16 + 1];
     const DecodeGeom &g = p.g;
@@ -688,8 +689,9 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 
     const int sub = lane & 15;  // dims 8*sub .. 8*sub+7
     const int eg = lane >> 4;   // value tokens eg + 4 u of a batch
-    const int grp = (8 * sub) / p.c.Gv;
+    const int grp = (8 * sub) / GV;
     const uint32_t tmask = (1u << logP) - 1u;
+    const int vw = 4 * sub, vz = kD / 2 + 4 * grp;  // offsets of the lane's code and scale/zero words
     float acc[GB][8], zacc[GB], lsum[GB], mrun[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
@@ -705,17 +707,30 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         // ---- the batch's key and value records (tokens past nb re-read the last one)
         uint4 kb;
         uint32_t nc;
-        {
-            const uint32_t t = (uint32_t)(t0 + bs + min(lane, nb - 1));
-            load_key(p.c, pbase[(t >> logP) - p0] + (t & tmask), kb, nc);
-        }
         uint32_t cw[VU], szw[VU];
+        if (nb == NB && logP >= 6) {
+            // a whole batch inside one page: consecutive slots
+            const uint32_t first = (uint32_t)(t0 + bs);
+            const uint32_t s0 = pbase[(first >> logP) - p0] + (first & tmask);
+            load_key(p.c, s0 + lane, kb, nc);
+            const uint8_t *vr = p.c.vals + (size_t)(s0 + eg) * VREC;
 #pragma unroll
-        for (int u = 0; u < VU; ++u) {
-            const uint32_t t = (uint32_t)(t0 + bs + min(eg + 4 * u, nb - 1));
-            const uint8_t *vr = val_rec(p.c, pbase[(t >> logP) - p0] + (t & tmask));
-            cw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * sub);
-            szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
+            for (int u = 0; u < VU; ++u) {
+                cw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * u * VREC + vw);
+                szw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * u * VREC + vz);
+            }
+        } else {
+            {
+                const uint32_t t = (uint32_t)(t0 + bs + min(lane, nb - 1));
+                load_key(p.c, pbase[(t >> logP) - p0] + (t & tmask), kb, nc);
+            }
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                const uint32_t t = (uint32_t)(t0 + bs + min(eg + 4 * u, nb - 1));
+                const uint8_t *vr = p.c.vals + (size_t)(pbase[(t >> logP) - p0] + (t & tmask)) * VREC;
+                cw[u] = *reinterpret_cast<const uint32_t *>(vr + vw);
+                szw[u] = *reinterpret_cast<const uint32_t *>(vr + vz);
+            }
         }
         float s[GB];
         {
@@ -725,7 +740,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             if (lane >= nb) s[h] = -INFINITY;
-            const float mnew = fmaxf(mrun[h], wave_max(s[h]));
+            const float mnew = fmaxf(mrun[h], wave_max_u(s[h]));
             const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
             if (scale != 1.0f) {
                 zacc[h] *= scale;
@@ -745,12 +760,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
             const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
             const float zf = half_bits_to_float(szw[u] >> 16);
             float c[8];
-            const uint32_t lo = cw[u] & 0x0F0F0F0Fu, hi = (cw[u] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                c[2 * m] = (float)((lo >> (8 * m)) & 0xFFu);
-                c[2 * m + 1] = (float)((hi >> (8 * m)) & 0xFFu);
-            }
+            unpack_codes(cw[u], c);
 #pragma unroll
             for (int h = 0; h < GB; ++h) {
                 const float w = wbuf[e][h];
@@ -971,13 +981,11 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
                 const uint32_t cwk[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    // byte m of word k holds dims 32 q4 + 8k + 2m (low nibble) and + 1 (high)
-                    const uint32_t lo = cwk[k] & 0x0F0F0F0Fu, hi = (cwk[k] >> 4) & 0x0F0F0F0Fu;
+                    // word k holds dims 32 q4 + 8k .. + 7
+                    float c[8];
+                    unpack_codes(cwk[k], c);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        acc[8 * k + 2 * m] = fmaf(ws, (float)((lo >> (8 * m)) & 0xFFu), acc[8 * k + 2 * m]);
-                        acc[8 * k + 2 * m + 1] = fmaf(ws, (float)((hi >> (8 * m)) & 0xFFu), acc[8 * k + 2 * m + 1]);
-                    }
+                    for (int j = 0; j < 8; ++j) acc[8 * k + j] = fmaf(ws, c[j], acc[8 * k + j]);
                 }
             }
         }
@@ -1158,10 +1166,20 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         // one wave per (chunk, KV-head group, sequence)
         const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
         if (p.g.CH > kMaxFullChunk || p.g.KA != 1) return hipErrorInvalidValue;
+        const bool g32 = p.c.Gv == 32;
         switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_attend_full<1>), grid, dim3(64), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_attend_full<2>), grid, dim3(64), 0, s, p); break;
-        default: hipLaunchKernelGGL((k_attend_full<4>), grid, dim3(64), 0, s, p); break;
+        case 1:
+            if (g32) hipLaunchKernelGGL((k_attend_full<1, 32>), grid, dim3(64), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_full<1, 64>), grid, dim3(64), 0, s, p);
+            break;
+        case 2:
+            if (g32) hipLaunchKernelGGL((k_attend_full<2, 32>), grid, dim3(64), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_full<2, 64>), grid, dim3(64), 0, s, p);
+            break;
+        default:
+            if (g32) hipLaunchKernelGGL((k_attend_full<4, 32>), grid, dim3(64), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_full<4, 64>), grid, dim3(64), 0, s, p);
+            break;
         }
     }
     return hipGetLastError();

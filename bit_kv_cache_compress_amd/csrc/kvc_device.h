@@ -81,6 +81,48 @@ __device__ __forceinline__ uint64_t lanemask_lt()
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Byte K of x as a float (v_cvt_f32_ubyteK: one instruction, where the compiler would
+// otherwise extract the field first).
+template <int K>
+__device__ __forceinline__ float ubyte_to_float(uint32_t x)
+{
+    float f;
+    if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
+    else if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+    else if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
+    return f;
+}
+
+// The 8 codes of a 32-bit code word (dims 2m in the low, 2m+1 in the high nibble of byte m)
+// as floats, c[0..7] in dim order.
+__device__ __forceinline__ void unpack_codes(uint32_t w, float c[8])
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    c[0] = ubyte_to_float<0>(lo);
+    c[1] = ubyte_to_float<0>(hi);
+    c[2] = ubyte_to_float<1>(lo);
+    c[3] = ubyte_to_float<1>(hi);
+    c[4] = ubyte_to_float<2>(lo);
+    c[5] = ubyte_to_float<2>(hi);
+    c[6] = ubyte_to_float<3>(lo);
+    c[7] = ubyte_to_float<3>(hi);
+}
+
+// Wave-wide max, uniform result: DPP within each 16-lane row, then the four row maxima.
+__device__ __forceinline__ float wave_max_u(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad_perm 1,0,3,2
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));   // quad_perm 2,3,0,1
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true)));  // row_ror 4
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true)));  // row_ror 8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // ---------------------------------------------------------------------------------------
 // Top-p bin of a proxy score: floor(s * kbin) in binary32, clamped to [-2^29, 2^29];
 // a NaN goes to the bottom.
