@@ -1,9 +1,16 @@
-"""Full-size parity: the 128k-context GQA Top-p workload (batch 4, 32 query / 8 KV heads,
-131072 tokens, 1% spike tokens, Top-p 0.9) in the launch configuration the benchmark
-times.  Inputs are drawn on the device by torch's seeded generator.  The oracle checks
-sampled (sequence, KV head) units one by one: the unit's cache bytes, then the library's
-scores, Top-p sets and outputs for the unit's query heads.  Properties that hold at any
-size are checked on every head."""
+"""Full-size parity on the workloads' real shapes, inputs drawn on the device by torch's
+seeded generator:
+
+- the 128k-context GQA Top-p workload (batch 4, 32 query / 8 KV heads, 131072 tokens, 1%
+  spike tokens, Top-p 0.9) in the launch configuration the benchmark times;
+- 32 sequences x 32 heads of lengths 1k..32k on shuffled 256-token pages, value group 64,
+  full softmax;
+- the 32768-token x 32-head prefill append with a randomized Hadamard rotation, then a
+  1,048,576-token decode over 8 KV heads at Top-p 0.95 whose cache 32 appends built.
+
+The oracle checks sampled (sequence, KV head) units one by one: the unit's cache bytes,
+then the library's scores, Top-p sets and outputs for the unit's query heads.  Properties
+that hold at any size are checked on every head."""
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
@@ -103,3 +110,155 @@ def test_gqa_128k_topp_full_size():
             assert rel_err(o[b, hh], r["out"]) <= 2e-3
             assert rel_err(of[b, hh], r["out_full"]) <= 2e-3
         _say(f"[full] unit {(b, h)} ok: cache identical={same}, kept {cnt[b, h * G:(h + 1) * G].tolist()}")
+
+
+def _check_unit_cache(kb, kn, vc, vs, pg, sl, h, bits, nc, codes, sz):
+    """Cache bytes of one unit: sign words and norms exact, correction within one binary16
+    ulp (its binary64 sum runs in another order), value codes and scale/zero exact.
+    Returns whether the corrections are identical too."""
+    np.testing.assert_array_equal(kb[pg, h, sl], bits)
+    np.testing.assert_array_equal(kn[pg, h, sl] & 0xFFFF, nc[:, 0])
+    assert np.all(np.abs((kn[pg, h, sl] >> 16).astype(np.int64) - nc[:, 1].astype(np.int64)) <= 1)
+    np.testing.assert_array_equal(vc[pg, h, sl], codes)
+    np.testing.assert_array_equal(vs[pg, h, sl], sz[..., 0].astype(np.uint32) | (sz[..., 1].astype(np.uint32) << 16))
+    return bool(np.array_equal(kn[pg, h, sl] >> 16, nc[:, 1]))
+
+
+def _oracle_encode(orot, k, v, D, Gv, threads=16):
+    """The oracle's key and value encode of n tokens, split over host threads."""
+    n = k.shape[0]
+    cuts = np.linspace(0, n, threads + 1).astype(int)
+
+    def part(i):
+        a, b = cuts[i], cuts[i + 1]
+        bits, nc = oracle.key_encode(orot, k[a:b])
+        codes, sz = oracle.value_encode(v[a:b], D, Gv)
+        return bits, nc, codes, sz
+
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(part, range(threads)))
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))
+
+
+def test_batched_paged_full_size():
+    """32 sequences x 32 heads, lengths uniform in [1024, 32768], shuffled 256-token pages,
+    value group 64, full softmax: sampled (sequence, head) units against the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_kv_cache_compress_amd as kvc
+
+    wl = W.CONFIGS[3]
+    dev = torch.device("cuda")
+    lens = W.draw_seq_lens(wl)
+    Lm = int(lens.max())
+    _say(f"[full] {wl.name}: drawing inputs, lengths {lens.min()}..{Lm}")
+    K, V, q = W.draw_device(wl, dev, L=Lm)
+    pt_np, npages = W.page_layout(wl, lens)
+    kind, R16 = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, wl.Hkv, R16, rot_kind=kind, page_size=wl.P, value_group=wl.Gv, device=dev)
+    pt = torch.from_numpy(pt_np).to(dev)
+    seq = torch.from_numpy(lens).to(dev)
+    for b in range(wl.B):
+        n = int(lens[b])
+        kvc.append(cache, K[b:b + 1, :n].contiguous(), V[b:b + 1, :n].contiguous(),
+                   torch.zeros(1, dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+    out = kvc.decode_attend(cache, q, seq, pt, top_p=1.0, max_seq_len=Lm)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    _say("[full] library decode done")
+    orot = oracle.Rotation(oracle.ROT_DENSE, wl.D, R16=R16)
+    kb = cache.key_bits.cpu().numpy().view(np.uint32)
+    kn = cache.key_nc.cpu().numpy().view(np.uint32)
+    vc = cache.val_codes.cpu().numpy()
+    vs = cache.val_sz.cpu().numpy().view(np.uint32)
+    o = out.cpu().numpy()
+    qn = q.cpu().numpy()
+    for b, h in [(int(np.argmax(lens)), 0), (int(np.argmin(lens)), 31), (7, 13)]:
+        n = int(lens[b])
+        k = K[b, :n, h].float().cpu().numpy()
+        v = V[b, :n, h].float().cpu().numpy()
+        bits, nc, codes, sz = _oracle_encode(orot, k, v, wl.D, wl.Gv)
+        t = np.arange(n)
+        pg, sl = pt_np[b, t // wl.P], t % wl.P
+        _check_unit_cache(kb, kn, vc, vs, pg, sl, h, bits, nc, codes, sz)
+        qe = oracle.query_encode(orot, qn[b, h][None, :])
+        _, _, s = oracle.scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], wl.D)
+        ref = oracle.attend(s, codes, sz, wl.D, wl.Gv)
+        assert rel_err(o[b, h], ref) <= 2e-3
+        _say(f"[full] unit {(b, h)} ok over {n} tokens")
+
+
+def test_append32k_and_decode1m_full_size():
+    """The prefill append of 32768 tokens x 32 KV heads (randomized Hadamard rotation), then
+    a decode over one 1,048,576-token sequence with 32 query / 8 KV heads and Top-p 0.95, its
+    cache built by 32 appends of 32768 tokens: sampled heads against the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_kv_cache_compress_amd as kvc
+
+    wl = W.CONFIGS[4]
+    dev = torch.device("cuda")
+    D, P, Gv = wl.D, wl.P, wl.Gv
+    kind, signs = W.draw_rotation(wl)
+    orot = oracle.Rotation(oracle.ROT_HADAMARD, D, signs=signs)
+
+    # ---- prefill append, one call
+    n_new, Ha = wl.append_tokens, wl.append_heads
+    Ka, Va, _ = W.draw_device(wl, dev, L=n_new, Hkv=Ha)
+    pta_np, npa = W.page_layout(wl.scaled(Hkv=Ha), np.array([n_new], np.int32))
+    ca = kvc.KVCache(npa, Ha, signs, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    kvc.append(ca, Ka, Va, torch.zeros(1, dtype=torch.int32, device=dev), torch.from_numpy(pta_np).to(dev))
+    torch.cuda.synchronize()
+    kb = ca.key_bits.cpu().numpy().view(np.uint32)
+    kn = ca.key_nc.cpu().numpy().view(np.uint32)
+    vc = ca.val_codes.cpu().numpy()
+    vs = ca.val_sz.cpu().numpy().view(np.uint32)
+    t = np.arange(n_new)
+    pg, sl = pta_np[0, t // P], t % P
+    for h in (0, 31):
+        enc = _oracle_encode(orot, Ka[0, :, h].float().cpu().numpy(), Va[0, :, h].float().cpu().numpy(), D, Gv)
+        _check_unit_cache(kb, kn, vc, vs, pg, sl, h, *enc)
+    _say(f"[full] append of {n_new} x {Ha} token-heads ok on sampled heads")
+    del Ka, Va, ca, kb, kn, vc, vs
+
+    # ---- 1M-token decode over 8 KV heads
+    L, B, Hq, Hkv, G = wl.L, wl.B, wl.Hq, wl.Hkv, wl.Hq // wl.Hkv
+    K, V, q = W.draw_device(wl, dev)
+    lens = np.full(B, L, np.int32)
+    pt_np, npages = W.page_layout(wl, lens)
+    cache = kvc.KVCache(npages, Hkv, signs, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    pt = torch.from_numpy(pt_np).to(dev)
+    for i in range(L // n_new):
+        a = i * n_new
+        kvc.append(cache, K[:, a:a + n_new].contiguous(), V[:, a:a + n_new].contiguous(),
+                   torch.full((B,), a, dtype=torch.int32, device=dev), pt)
+    seq = torch.from_numpy(lens).to(dev)
+    dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev)
+    out = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    _say("[full] 1M-token decode done")
+    cnt = dbg.sel_count.cpu().numpy()
+    assert np.all(cnt >= 1) and np.all(cnt <= L)
+    h = 5
+    k = K[0, :, h].float().cpu().numpy()
+    v = V[0, :, h].float().cpu().numpy()
+    del K, V
+    bits, nc, codes, sz = _oracle_encode(orot, k, v, D, Gv)
+    kb = cache.key_bits[:, h].cpu().numpy().view(np.uint32)
+    kn = cache.key_nc[:, h].cpu().numpy().view(np.uint32)
+    t = np.arange(L)
+    pg, sl = pt_np[0, t // P], t % P
+    np.testing.assert_array_equal(kb[pg, sl], bits)
+    same = np.array_equal(kn[pg, sl] >> 16, nc[:, 1])
+    qn = q.cpu().numpy()
+    o = out.cpu().numpy()
+    for hh in range(h * G, (h + 1) * G):
+        qe = oracle.query_encode(orot, qn[0, hh][None, :])
+        _, _, s = oracle.scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], D)
+        tp = oracle.topp(s, wl.top_p, D)
+        if same:
+            assert cnt[0, hh] == len(tp["idx"])
+            np.testing.assert_array_equal(dbg.sel_idx[0, hh, :cnt[0, hh]].cpu().numpy(), tp["idx"])
+        assert rel_err(o[0, hh], oracle.attend(s, codes, sz, D, Gv, tp["idx"])) <= 2e-3
+        _say(f"[full] head {hh}: kept {cnt[0, hh]} of {L}")
