@@ -189,7 +189,7 @@ def main():
     # ---- selection statistics (one untimed debug decode)
     sel_union = sel_entries = None
     if wl.top_p < 1.0:
-        dbg = kvc.DecodeDebug.allocate(B, Hq, Lmax, True, dev)
+        dbg = kvc.DecodeDebug.allocate(B, Hq, Lmax, True, dev, scores=False)
         kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, debug=dbg)
         torch.cuda.synchronize()
         G = Hq // Hkv

@@ -131,17 +131,20 @@ class DecodeDebug:
     q_codes: torch.Tensor
     q_params: torch.Tensor
     q_sumu: torch.Tensor
-    iscores: torch.Tensor
-    scores: torch.Tensor
+    iscores: Optional[torch.Tensor]
+    scores: Optional[torch.Tensor]
     sel_count: Optional[torch.Tensor] = None
     sel_idx: Optional[torch.Tensor] = None
     sel_bins: Optional[torch.Tensor] = None
 
     @staticmethod
-    def allocate(B, Hq, ld, topp: bool, device) -> "DecodeDebug":
+    def allocate(B, Hq, ld, topp: bool, device, scores: bool = True) -> "DecodeDebug":
+        """Debug outputs of one decode.  scores=False leaves out the per-token scores, so the
+        decode runs the same score kernels as without debug output."""
         z = lambda *s, dt=torch.int32: torch.zeros(s, dtype=dt, device=device)
         return DecodeDebug(q_codes=z(B, Hq, HEAD_DIM, dt=torch.uint8), q_params=z(B, Hq, 4, dt=torch.float32),
-                           q_sumu=z(B, Hq), iscores=z(B, Hq, ld), scores=z(B, Hq, ld, dt=torch.float32),
+                           q_sumu=z(B, Hq), iscores=z(B, Hq, ld) if scores else None,
+                           scores=z(B, Hq, ld, dt=torch.float32) if scores else None,
                            sel_count=z(B, Hq) if topp else None, sel_idx=z(B, Hq, ld) - 1 if topp else None,
                            sel_bins=z(B, Hq, 2) if topp else None)
 

@@ -44,7 +44,7 @@ struct Plan {
     kvc::DecodeGeom g;
     bool topp;
     int nsplit, cps;
-    size_t off_qpl, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po;
+    size_t off_qpl, off_qa, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po;
     size_t total;
 };
 
@@ -92,20 +92,21 @@ void plan_layout(Plan &pl, int BH)
     };
     const size_t NC = (size_t)pl.g.NC, NCA = (size_t)pl.g.NCA;
     pl.off_qpl = take((size_t)BH * 16 * 4);
+    pl.off_qa = take((size_t)BH * 128);
     pl.off_qpar = take((size_t)BH * 16);
     pl.off_pm = take((size_t)BH * NCA * 4);
     pl.off_pl = take((size_t)BH * NCA * 4);
     pl.off_po = take((size_t)BH * NCA * 128 * 4);
     if (pl.topp) {
         // histogram splits: >= 512 blocks over (split, head, sequence); a split holds fewer
-        // than 65536 tokens (16-bit partial counts) and at most 1024 chunks
+        // than 65536 tokens (16-bit partial counts) and at most 256 chunks (one per thread)
         int nsplit = (512 + BH - 1) / BH;
         const int min_split = (int)(((long)pl.g.Lpad + 32767) / 32768);
         if (nsplit < min_split) nsplit = min_split;
         if (nsplit > pl.g.NC) nsplit = pl.g.NC;
         if (nsplit < 1) nsplit = 1;
         int cps = (pl.g.NC + nsplit - 1) / nsplit;
-        while (cps > 1024 || (long)cps * pl.g.CH > 65535) {
+        while (cps > 256 || (long)cps * pl.g.CH > 65535) {  // one chunk per histogram thread; u16 counts
             ++nsplit;
             cps = (pl.g.NC + nsplit - 1) / nsplit;
         }
@@ -278,6 +279,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     const int BH = B * Hq;
     uint32_t *qnib = at<uint32_t>(workspace, pl.off_qpl);
     float4 *qpar = at<float4>(workspace, pl.off_qpar);
+    uint8_t *qa = at<uint8_t>(workspace, pl.off_qa);
 
     kvc::QprepParams qp;
     qp.rot_kind = c->rot_kind;
@@ -285,6 +287,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     qp.q = q;
     qp.BH = BH;
     qp.qnib = qnib;
+    qp.qa = qa;
     qp.qpar = qpar;
     qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
@@ -298,6 +301,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     sp.g = pl.g;
     sp.c = cv;
     sp.qnib = qnib;
+    sp.qa = qa;
     sp.qpar = qpar;
     sp.kbin = kbin;
     sp.dl = pl.topp ? at<uint16_t>(workspace, pl.off_dl) : nullptr;

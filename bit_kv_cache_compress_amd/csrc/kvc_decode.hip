@@ -153,6 +153,17 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
         for (int m = 0; m < 8; ++m) word |= (uint32_t)us[32 * w + 4 * m + k] << (4 * m);
         p.qnib[(size_t)bh * 16 + r] = word;
     }
+    {
+        // the codes as the fp8 A operand of k_score_topp_mf, byte r = 32 group + index: it
+        // meets K = 16 group + index (index < 16) or 64 + 16 group + index - 16 of the fp4 key
+        // operand, where K = 32 j + 8 v + m carries bit 4m + v of key word j with the factor
+        // 1/2, 1, 2, 2 for v = 0..3; the code is scaled by 4, 2, 1, 1 to match
+        const int ga = r >> 5, pa = r & 31;
+        const int K = pa < 16 ? 16 * ga + pa : 64 + 16 * ga + (pa - 16);
+        const int j = K >> 5, v = (K >> 3) & 3, m = K & 7;
+        const int x = us[32 * j + 4 * m + v] << (v == 0 ? 2 : v == 1 ? 1 : 0);
+        p.qa[(size_t)bh * kD + r] = (uint8_t)fp8_e4m3_small(x);
+    }
     su = redi[0] + redi[1];
     if (r == 0) p.qpar[bh] = make_float4(vl * isd, delta * isd, __int_as_float(su), 0.0f);
     if (p.dbg_codes) p.dbg_codes[(size_t)bh * kD + r] = (uint8_t)u;
@@ -265,8 +276,10 @@ __global__ __launch_bounds__(64) void k_score(ScoreParams p)
 // max, each lane stores its tokens' 16-bit distances (128-byte coalesced stores), and every
 // position of the chunk is written (kBins past the end).
 // ---------------------------------------------------------------------------------------
+// At most 128 VGPRs (4 waves per SIMD requested); the compiler then fits the kernel in 70,
+// 7 waves per SIMD, which the key-load latency needs.
 template <int GB>
-__global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
+__global__ __launch_bounds__(64, 4) void k_score_topp(ScoreParams p)
 {
     constexpr int CH = kTopPChunk;
     constexpr int U = CH / 64;  // tokens per lane
@@ -350,6 +363,144 @@ __global__ __launch_bounds__(64) void k_score_topp(ScoreParams p)
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Top-p score pass on the matrix cores, for blocks of 4 query heads (GQA groups of 4 or
+// more).  Same work split, loads and outputs as k_score_topp; the binary x INT4 products
+// run as v_mfma_scale_f32_16x16x128_f8f6f4 with the query codes as the fp8 (e4m3) A
+// operand and the key sign bits as the fp4 (e2m1) B operand (16 columns: tokens), four
+// tiles of 16 tokens per 64-token group:
+//  - lane l holds token 64u + l of group u.  A 4 x 4 block transpose of its four key words
+//    over the 16-lane rows (two permlane32 and two permlane16 swaps) leaves, in register t,
+//    word j of token 64u + 16t + n in lane 16j + n: the B operand of tile t.
+//  - bit 4m + v of a word goes to nibble m of B register v, as 0x1 (0.5), 0x2 (1), 0x4 (2)
+//    for v = 0, 1, 2 and 0x4 after a shift for v = 3 (2).  The query codes carry the
+//    factors 4, 2, 1, 1, so each product is 2 * bit * u.
+//  - the A operand of tile t holds head h in row 4t + h and zeros in the other rows, and
+//    the four tiles accumulate into one result, which starts at -sumu of head h in
+//    register h.  Rows 4t' .. 4t' + 3 of the result (registers 0..3 of lanes 16t' + n)
+//    then hold A of the 4 heads for token 64u + 16t' + n: lane l ends with its own token.
+// Products and sums are integers below 2^12, exact in binary32: A = 2 ip - sumu and the
+// score are bit-identical to the dot8 form.
+// ---------------------------------------------------------------------------------------
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);  // a.hi <-> b.lo
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);  // odd rows of a <-> even rows of b
+    a = r[0];
+    b = r[1];
+}
+
+__global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
+{
+    constexpr int GB = 4;
+    constexpr int CH = kTopPChunk;
+    constexpr int U = CH / 64;  // 64-token groups
+    constexpr int kNone = -2 * kBinClamp;
+    __shared__ uint32_t pbase[CH / 16 + 1];
+    const DecodeGeom &g = p.g;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    int kvh, hq0;
+    block_heads(g, blockIdx.y, kvh, hq0);
+    const int L = g.seq_lens[b];
+    const int t0 = chunk * CH;
+    if (t0 >= L) return;
+    const int n = min(CH, L - t0);
+    const int lane = threadIdx.x;
+    const int bh0 = b * g.Hq + hq0;
+    const int logP = p.c.logP;
+    const int p0 = t0 >> logP;
+    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
+    for (int i = lane; i < np; i += 64)
+        pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
+                   << logP;
+    __syncthreads();
+    // A operand of tile t: the query rows 4t .. 4t + 3 (this lane's row is lane & 15), zero
+    // elsewhere, so that the four tiles of a group accumulate into one result
+    v8i_t qa[4];
+    {
+        const uint4 *src =
+            reinterpret_cast<const uint4 *>(p.qa + (size_t)(bh0 + (lane & 3)) * kD + 32 * (lane >> 4));
+        const uint4 a0 = src[0], a1 = src[1];
+        const v8i_t q8 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const int rt = (lane & 15) >> 2;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qa[t] = rt == t ? q8 : v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    float c0[GB], c1[GB];  // wave-uniform
+    v4f_t msu;             // -sumu of head h in row h (mod 4): the accumulator input
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        const float4 pq = p.qpar[bh0 + h];
+        c0[h] = pq.x;
+        c1[h] = pq.y;
+        msu[h] = (float)-__float_as_int(pq.z);
+    }
+    uint32_t slot[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int t = t0 + min(lane + 64 * u, n - 1);
+        slot[u] = pbase[(t >> logP) - p0] + (uint32_t)(t & ((1 << logP) - 1));
+    }
+    uint4 kb[U];
+    uint32_t nc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_key(p.c, slot[u], kb[u], nc[u]);
+    __builtin_amdgcn_sched_barrier(0);
+    int e[U][GB];
+    int lm[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) lm[h] = kNone;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        uint32_t w[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
+        const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
+                       __builtin_popcount(w[3]);
+        const float fP = (float)(2 * pc - kD);
+        const float r = half_bits_to_float(nc[u] & 0xFFFFu) / half_bits_to_float(nc[u] >> 16);
+        swap32(w[0], w[2]);
+        swap32(w[1], w[3]);
+        swap16(w[0], w[1]);
+        swap16(w[2], w[3]);
+        v4f_t d = msu;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const v8i_t bt = {(int)(w[t] & 0x11111111u), (int)(w[t] & 0x22222222u), (int)(w[t] & 0x44444444u),
+                              (int)((w[t] >> 1) & 0x44444444u), 0, 0, 0, 0};
+            d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[t], bt, d, 0, 4, 0, 127, 0, 127);
+        }
+        const int lim = lane + 64 * u < n ? INT_MAX : kNone;
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+            const float a = d[h];
+            const float cp = c0[h] * fP;
+            const float s = fmaf(c1[h], a, cp) * r;
+            const int ev = min(score_bin(s, p.kbin), lim);
+            e[u][h] = ev;
+            lm[h] = max(lm[h], ev);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h) lm[h] = wave_max_i(lm[h]);
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GB; ++h) p.lmax[(size_t)(bh0 + h) * g.NC + chunk] = lm[h];
+    }
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        uint16_t *row = p.dl + (size_t)(bh0 + h) * g.Lpad + t0 + lane;
+#pragma unroll
+        for (int u = 0; u < U; ++u) row[64 * u] = (uint16_t)min(lm[h] - e[u][h], kBins);
+    }
+}
+
 // Bins of caller-supplied scores (kv_topp_select): one block per (chunk, query head, seq).
 __global__ __launch_bounds__(256) void k_bin_scores(BinScoresParams p)
 {
@@ -393,7 +544,7 @@ __device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t
 __global__ __launch_bounds__(256) void k_hist(HistParams p)
 {
     __shared__ uint32_t hist[kBins + 1];  // + a bin for tokens that are not counted
-    __shared__ int delta[1024];
+    __shared__ int delta[kBlock];
     __shared__ int red[4];
     __shared__ int top[1];
     const DecodeGeom &g = p.g;
@@ -405,34 +556,44 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
     const int c0 = split * p.cps;
     if (c0 >= nch) return;  // the threshold pass reads only the splits that hold tokens
     const int c1 = min(nch, c0 + p.cps);
+    const int tb = c0 << g.logCH;
+    const int te = min(L, c1 << g.logCH);
+    const uint16_t *row = p.dl + bh * g.Lpad;
+    // 8 tokens per 16-byte load, 16 loads in flight (tb is a multiple of CH >= 256).  The
+    // first batch is issued before the top-bin reduction, whose reads then overlap it.
+    constexpr int U = 16;
+    constexpr int kStep = 8 * kBlock * U;
+    uint4 raw[U];
+    int t = tb + 8 * tid;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (t + 8 * kBlock * u < te) raw[u] = *reinterpret_cast<const uint4 *>(row + t + 8 * kBlock * u);
+    // the split's chunk top bins, one per thread (the plan keeps cps * CH <= 65535 with
+    // CH >= 256, so cps < kBlock), also read before the reduction
+    const int lmc = tid < c1 - c0 ? p.lmax[bh * g.NC + c0 + tid] : 0;
     for (int i = tid; i <= kBins; i += kBlock) hist[i] = 0u;
     const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
-    for (int c = c0 + tid; c < c1; c += kBlock) delta[c - c0] = emax - p.lmax[bh * g.NC + c];
+    if (tid < c1 - c0) delta[tid] = emax - lmc;
     __syncthreads();
-    {
-        const int tb = c0 << g.logCH;
-        const int te = min(L, c1 << g.logCH);
-        const uint16_t *row = p.dl + bh * g.Lpad;
-        // 8 tokens per 16-byte load, 16 loads in flight (tb is a multiple of CH >= 256)
-        constexpr int U = 16;
-        for (int t = tb + 8 * tid; t < te; t += 8 * kBlock * U) {
-            uint4 raw[U];
+    for (; t < te; t += kStep) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (t + 8 * kBlock * u < te) raw[u] = *reinterpret_cast<const uint4 *>(row + t + 8 * kBlock * u);
+        for (int u = 0; u < U; ++u) {
+            const int tu = t + 8 * kBlock * u;
+            if (tu < te) {
+                const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                const int dc = delta[(tu >> g.logCH) - c0];  // 8 tokens share a chunk
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tu = t + 8 * kBlock * u;
-                if (tu < te) {
-                    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-                    const int dc = delta[(tu >> g.logCH) - c0];  // 8 tokens share a chunk
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int d = dc + (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                        atomicAdd(&hist[(tu + e < te && d < kBins) ? d : kBins], 1u);
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    const int d = dc + (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                    atomicAdd(&hist[(tu + e < te && d < kBins) ? d : kBins], 1u);
                 }
             }
+        }
+        if (t + kStep < te) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (t + kStep + 8 * kBlock * u < te)
+                    raw[u] = *reinterpret_cast<const uint4 *>(row + t + kStep + 8 * kBlock * u);
         }
     }
     __syncthreads();
@@ -480,6 +641,8 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     const int nch = (L + g.CH - 1) >> g.logCH;
     const int nsu = (nch + p.cps - 1) / p.cps;  // splits that hold tokens
     // counts of bins 8 tid .. 8 tid + 7 summed over the splits (8 splits' loads in flight)
+    // the top bin of the first 1024 chunks is read together with the split counts
+    int m = tid < nch ? p.lmax[bh * g.NC + tid] : -kBinClamp;
     uint32_t cnt[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) cnt[k] = 0u;
@@ -498,8 +661,7 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
             }
         }
     }
-    int m = -kBinClamp;
-    for (int c = tid; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
+    for (int c = tid + kT; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
     m = wave_max_i(m);
     if (lane == 0) imax[wave] = m;
     if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
@@ -1117,7 +1279,7 @@ hipError_t launch_score(const ScoreParams &p, hipStream_t s)
         switch (p.g.GB) {
         case 1: hipLaunchKernelGGL((k_score_topp<1>), grid, blk, 0, s, p); break;
         case 2: hipLaunchKernelGGL((k_score_topp<2>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_score_topp<4>), grid, blk, 0, s, p); break;
+        default: hipLaunchKernelGGL(k_score_topp_mf, grid, blk, 0, s, p); break;
         }
     } else {
         // debug scores: the Top-p chunks, or the larger chunks of a full-softmax decode

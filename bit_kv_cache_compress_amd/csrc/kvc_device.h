@@ -177,6 +177,15 @@ __device__ __forceinline__ void read_query(QueryState<GB> &qs, const uint32_t *q
     }
 }
 
+// An integer 0 <= x < 256 with at most 4 significant bits as its fp8 (OCP e4m3) code:
+// exponent field floor(log2 x) + 7, the three bits below the leading one as the mantissa.
+__device__ __forceinline__ uint32_t fp8_e4m3_small(int x)
+{
+    if (x == 0) return 0u;
+    const int e = 31 - __builtin_clz((uint32_t)x);
+    return (uint32_t)(((e + 7) << 3) | (((x << 3) >> e) & 7));
+}
+
 // Key word w spread for the dot8 products: nibble m of spread_key(w, k) is 2 * bit (4m + k)
 // of w.  With the query word nib[4w + k] this gives 2 * sum_r bit_r u_r.
 __device__ __forceinline__ uint32_t spread_key(uint32_t w, int k)

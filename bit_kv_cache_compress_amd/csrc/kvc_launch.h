@@ -52,6 +52,7 @@ struct QprepParams {
     const float *q;        // [B*Hq][128]
     int BH;
     uint32_t *qnib;        // [B*Hq][16] int4 codes in dot8 order
+    uint8_t *qa;           // [B*Hq][128] codes as the fp8 A operand of the matrix-core score
     float4 *qpar;          // [B*Hq]
     uint8_t *dbg_codes;    // nullable [B*Hq][128]
     float *dbg_params;     // nullable [B*Hq][4]
@@ -80,6 +81,7 @@ struct ScoreParams {
     DecodeGeom g;
     CacheView c;
     const uint32_t *qnib;
+    const uint8_t *qa;
     const float4 *qpar;
     float kbin;
     uint16_t *dl;          // nullable [B*Hq][Lpad]: bin distance to the chunk's top bin

@@ -10,7 +10,9 @@ seeded generator:
 
 The oracle checks sampled (sequence, KV head) units one by one: the unit's cache bytes,
 then the library's scores, Top-p sets and outputs for the unit's query heads.  Properties
-that hold at any size are checked on every head."""
+that hold at any size are checked on every head.  The decode without score output (the
+kernels the benchmark times) must give the same Top-p sets and bit-identical outputs as the
+decode with score output."""
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
@@ -52,8 +54,16 @@ def test_gqa_128k_topp_full_size():
     dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev)
     out = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg)
     out_full = kvc.decode_attend(cache, q, seq, pt, top_p=1.0, max_seq_len=L)
+    # the decode as the benchmark runs it (no score output: the matrix-core score pass)
+    dbg_fast = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False)
+    out_fast = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg_fast)
     torch.cuda.synchronize()
     _say("[full] library decode done")
+    np.testing.assert_array_equal(dbg_fast.sel_count.cpu().numpy(), dbg.sel_count.cpu().numpy())
+    np.testing.assert_array_equal(dbg_fast.sel_bins.cpu().numpy(), dbg.sel_bins.cpu().numpy())
+    assert torch.equal(dbg_fast.sel_idx, dbg.sel_idx)
+    assert torch.equal(out_fast.view(torch.int32), out.view(torch.int32))
+    del dbg_fast, out_fast
 
     # properties on every (sequence, query head)
     cnt = dbg.sel_count.cpu().numpy()
@@ -233,7 +243,7 @@ def test_append32k_and_decode1m_full_size():
         kvc.append(cache, K[:, a:a + n_new].contiguous(), V[:, a:a + n_new].contiguous(),
                    torch.full((B,), a, dtype=torch.int32, device=dev), pt)
     seq = torch.from_numpy(lens).to(dev)
-    dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev)
+    dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False)
     out = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()

@@ -71,14 +71,16 @@ def test_append_parity(name):
     _say(f"[append] {name} ok {stats}")
 
 
-def _decode_with_debug(c, cache, top_p):
+def _decode_with_debug(c, cache, top_p, scores=True):
+    """Decode with debug outputs; scores=False runs the kernels of a decode without debug
+    output (the per-token scores are not written) and still returns the Top-p sets."""
     from bit_kv_cache_compress_amd import DecodeDebug, decode_attend
 
     dev = torch.device("cuda")
     q = torch.from_numpy(c.q).to(dev)
     lens = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
     pt = torch.from_numpy(c.pt).to(dev)
-    dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev)
+    dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev, scores=scores)
     out = decode_attend(cache, q, lens, pt, top_p=top_p, max_seq_len=c.max_len, debug=dbg)
     torch.cuda.synchronize()
     return out.cpu().numpy(), dbg
@@ -128,7 +130,7 @@ def test_end_to_end(name):
     _say(f"[e2e] {name}")
     g = gpu_append(c)
     same = all(np.array_equal(v, getattr(c.ocache, k)) for k, v in download(g).items())
-    out, dbg = _decode_with_debug(c, g, c.wl.top_p)
+    out, dbg = _decode_with_debug(c, g, c.wl.top_p, scores=False)
     ref = c.oracle_decode(c.ocache, c.wl.top_p)
     worst = max(float(rel_err(out[b, h], r["out"])) if int(c.lens[b]) else 0.0 for (b, h), r in ref.items())
     assert worst <= TOL
@@ -137,6 +139,23 @@ def test_end_to_end(name):
             cnt = int(dbg.sel_count[b, h])
             np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
     _say(f"[e2e] {name} ok, caches identical={same}, worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if CASES[n]["wl"].top_p < 1.0])
+def test_score_kernels_agree(name):
+    """The Top-p score pass of a decode without score output (the matrix-core kernel for
+    GQA groups of 4 or more) against the debug score pass (dot8): identical top bins,
+    thresholds, Top-p sets and bit-identical outputs on the oracle's cache."""
+    c = _case(name)
+    _say(f"[kernels] {name}")
+    g = upload(c.ocache, c)
+    o_dbg, d_dbg = _decode_with_debug(c, g, c.wl.top_p)
+    o_fast, d_fast = _decode_with_debug(c, g, c.wl.top_p, scores=False)
+    np.testing.assert_array_equal(d_fast.sel_count.cpu().numpy(), d_dbg.sel_count.cpu().numpy())
+    np.testing.assert_array_equal(d_fast.sel_bins.cpu().numpy(), d_dbg.sel_bins.cpu().numpy())
+    np.testing.assert_array_equal(d_fast.sel_idx.cpu().numpy(), d_dbg.sel_idx.cpu().numpy())
+    assert np.array_equal(o_fast.view(np.uint32), o_dbg.view(np.uint32))
+    _say(f"[kernels] {name} ok")
 
 
 def test_chunked_append_and_determinism():
