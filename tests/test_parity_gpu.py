@@ -158,6 +158,23 @@ def test_score_kernels_agree(name):
     _say(f"[kernels] {name} ok")
 
 
+def test_topp_sweep():
+    """Top-p from 0.3 to 0.999 on one cache (from a few dozen to almost every token of a
+    1024-token attention chunk kept): sets and outputs against the oracle."""
+    c = _case("c5-hadamard-topp")
+    for top_p in (0.3, 0.45, 0.6, 0.8, 0.95, 0.999):
+        _say(f"[sweep] top_p={top_p}")
+        g = upload(c.ocache, c)
+        out, dbg = _decode_with_debug(c, g, top_p, scores=False)
+        ref = c.oracle_decode(c.ocache, top_p)
+        for (b, h), r in ref.items():
+            cnt = int(dbg.sel_count[b, h])
+            assert cnt == len(r["idx"]), (top_p, b, h, cnt, len(r["idx"]))
+            np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            assert rel_err(out[b, h], r["out"]) <= TOL, (top_p, b, h)
+    _say("[sweep] ok")
+
+
 def test_chunked_append_and_determinism():
     c = _case("c3-gqa4-spikes-topp")
     _say("[chunks] chunked append 1/7/300-token pieces and repeated decode")
