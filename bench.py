@@ -222,7 +222,8 @@ def main():
         # the distances once
         "hist": DIST_BYTES * G * tokens_heads,
         "append": (2 * D * kv_in + KEY_BYTES + value_bytes(Gv)) * B * Hkv}
-    kernel_names = {"score": "k_score_topp" if wl.top_p < 1.0 else "k_score", "append": "k_append",
+    score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if wl.top_p < 1.0 else "k_score"
+    kernel_names = {"score": score_kernel, "append": "k_append",
                     "attend": "k_attend_topp" if wl.top_p < 1.0 else "k_attend", "hist": "k_hist",
                     "query": "k_qprep", "merge": "k_merge"}
     dominant = max((k for k in stage_ms if k in per_launch), key=lambda k: stage_ms[k])
