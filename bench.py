@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index 0..4 (default 2: GQA 128k Top-p)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--exact-keys", action="store_true",
+                    help="also keep binary16 keys; Top-p attends the selected tokens with exact scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -94,7 +96,8 @@ def main():
     K, V, q = W.draw_device(wl, dev, L=Lmax)
     pt_np, npages = W.page_layout(wl, lens)
     kind, rot = W.draw_rotation(wl)
-    cache = kvc.KVCache(npages, Hkv, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    cache = kvc.KVCache(npages, Hkv, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev,
+                        exact_keys=args.exact_keys)
     pt = torch.from_numpy(pt_np).to(dev)
     seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
     # prefill tokens 0 .. len-2 of every sequence
@@ -211,17 +214,19 @@ def main():
     # ---- roofline of the dominant kernel
     G = Hq // Hkv
     kv_in = 2 if wl.kv_dtype == "f16" else 4
+    kept_key_bytes = 2 * D if args.exact_keys and wl.top_p < 1.0 else KEY_BYTES
     per_launch = {
         # every key of the context, each scored for the G query heads of its KV head, and
         # the bin distances written
         "score": (KEY_BYTES + DIST_BYTES * G) * tokens_heads if wl.top_p < 1.0 else KEY_BYTES * tokens_heads,
         # Top-p: the distances, then key and value of every kept (token, query head);
         # full softmax: every key and value once per KV head
-        "attend": (DIST_BYTES * G * tokens_heads + (KEY_BYTES + value_bytes(Gv)) * sel_entries)
+        # (with binary16 keys, the 2 D bytes of the key instead of its 20-byte record)
+        "attend": (DIST_BYTES * G * tokens_heads + (kept_key_bytes + value_bytes(Gv)) * sel_entries)
         if sel_entries is not None else (KEY_BYTES + value_bytes(Gv)) * tokens_heads,
         # the distances once
         "hist": DIST_BYTES * G * tokens_heads,
-        "append": (2 * D * kv_in + KEY_BYTES + value_bytes(Gv)) * B * Hkv}
+        "append": (2 * D * kv_in + KEY_BYTES + value_bytes(Gv) + (2 * D if args.exact_keys else 0)) * B * Hkv}
     score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if wl.top_p < 1.0 else "k_score"
     kernel_names = {"score": score_kernel, "append": "k_append",
                     "attend": "k_attend_topp" if wl.top_p < 1.0 else "k_attend", "hist": "k_hist",
@@ -230,13 +235,17 @@ def main():
     ach = per_launch[dominant] / (stage_ms[dominant] / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(kernel_names[dominant], wl.name),
+                "traffic": None if args.exact_keys else measured_traffic(kernel_names[dominant], wl.name),
                 "algorithmic_bytes_per_launch": per_launch[dominant],
                 "avg_launch_us": round(stage_ms[dominant] * 1e3, 2)}
-    # whole step, algorithmic minimum: every key once, the values of the kept tokens once per
-    # KV head (the union over its query heads), the appended token
-    step_alg = per_launch["append"] + (KEY_BYTES * tokens_heads + value_bytes(Gv) * sel_union
-                                       if sel_union is not None else (KEY_BYTES + value_bytes(Gv)) * tokens_heads)
+    # whole step, algorithmic minimum: every key once, the values (with binary16 keys, also
+    # those keys) of the kept tokens once per KV head (the union over its query heads), and
+    # the appended token
+    if sel_union is not None:
+        kept = value_bytes(Gv) + (2 * D if args.exact_keys else 0)
+        step_alg = per_launch["append"] + KEY_BYTES * tokens_heads + kept * sel_union
+    else:
+        step_alg = per_launch["append"] + (KEY_BYTES + value_bytes(Gv)) * tokens_heads
     log(f"[bench] dominant {dominant}: {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
 
     result = {
@@ -246,7 +255,7 @@ def main():
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": Lmax,
                    "head_dim": D, "top_p": wl.top_p, "value_group": Gv, "page_size": P, "rotation": wl.rot,
                    "kv_dtype": wl.kv_dtype, "step": "append 1 token per sequence + decode attention",
-                   "cache_flushed_between_steps": not args.no_flush},
+                   "cache_flushed_between_steps": not args.no_flush, "exact_keys": args.exact_keys},
         "roofline": roofline,
         "step_hbm_frac_algorithmic": round(step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "query_head_tokens_per_s": value * (Hq // Hkv),
@@ -258,7 +267,9 @@ def main():
         result["topp_selected_union_token_kv_heads"] = sel_union
         result["topp_selected_token_query_heads"] = sel_entries
 
-    if not args.no_cpu_baseline:
+    if args.exact_keys and not args.no_cpu_baseline:
+        log("[cpu] no oracle baseline for the binary16-key mode (the default run has it)")
+    elif not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, wl, K, V, q, lens, pt_np, kind, rot,
                                                                       out, value)
     print(json.dumps(result), flush=True)

@@ -30,6 +30,7 @@ class KVCacheDesc(ctypes.Structure):
         ("rot", ctypes.c_void_p),
         ("keys", ctypes.c_void_p),
         ("vals", ctypes.c_void_p),
+        ("keys_f16", ctypes.c_void_p),
     ]
 
 

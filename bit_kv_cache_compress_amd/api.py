@@ -48,10 +48,14 @@ class KVCache:
 
     ``rotation``: dense -> float16 [128, 128] orthogonal matrix; hadamard -> 4 uint32 sign
     words (given as an int32 or uint32 array/tensor).
+
+    ``exact_keys``: also keep the keys in binary16 (``keys_f16`` [..., 128]); appends fill
+    it, and a Top-p decode then scores the selected tokens exactly with it.  ``proxy_desc``
+    is the descriptor without it (proxy scores throughout).
     """
 
     def __init__(self, num_pages: int, num_kv_heads: int, rotation, rot_kind: str = "dense",
-                 page_size: int = 256, value_group: int = 32, device="cuda"):
+                 page_size: int = 256, value_group: int = 32, device="cuda", exact_keys: bool = False):
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:
             device = torch.device("cuda", torch.cuda.current_device())
@@ -75,8 +79,13 @@ class KVCache:
         shp = (self.num_pages, self.num_kv_heads, self.page_size)
         self.keys = torch.zeros(shp + (D // 32 + 1,), dtype=torch.int32, device=device)
         self.vals = torch.zeros(shp + (D // 2 + 4 * (D // self.value_group),), dtype=torch.uint8, device=device)
+        self.keys_f16 = torch.zeros(shp + (D,), dtype=torch.float16, device=device) if exact_keys else None
         self.desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
-                                  self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(), self.vals.data_ptr())
+                                  self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(), self.vals.data_ptr(),
+                                  self.keys_f16.data_ptr() if exact_keys else None)
+        self.proxy_desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
+                                        self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(),
+                                        self.vals.data_ptr(), None)
 
     @property
     def key_bits(self) -> torch.Tensor:
@@ -95,7 +104,7 @@ class KVCache:
         return self.vals[..., HEAD_DIM // 2:].view(torch.int32)
 
     def nbytes(self) -> int:
-        return self.keys.numel() * 4 + self.vals.numel()
+        return self.keys.numel() * 4 + self.vals.numel() + (0 if self.keys_f16 is None else self.keys_f16.numel() * 2)
 
 
 def append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, start_pos: torch.Tensor,
@@ -207,8 +216,9 @@ class StageTimer:
 def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
                   top_p: float = 1.0, max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
-                  debug_struct: Optional[L.KVDebug] = None) -> torch.Tensor:
-    """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32."""
+                  debug_struct: Optional[L.KVDebug] = None, proxy: bool = False) -> torch.Tensor:
+    """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32.  Under Top-p, a
+    cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set."""
     dev = cache.device
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
@@ -231,7 +241,8 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
     if debug is not None:
         debug_struct = debug.struct()
     dbg = ctypes.byref(debug_struct) if debug_struct is not None else None
-    L.check(L.lib().kv_decode_attend(ctypes.byref(cache.desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
+    desc = cache.proxy_desc if proxy else cache.desc
+    L.check(L.lib().kv_decode_attend(ctypes.byref(desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
                                      _ptr(page_table), max_pages, float(top_p), _ptr(out), dbg, _ptr(workspace),
                                      workspace.numel(), _stream(dev)))
     return out

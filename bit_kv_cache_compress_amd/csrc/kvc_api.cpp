@@ -173,6 +173,8 @@ int check_cache(const kv_cache *c)
         return fail(KV_ERR_ARG, "rot_kind %d is not KV_ROT_DENSE or KV_ROT_HADAMARD", c->rot_kind);
     if (!c->rot || !c->keys || !c->vals)
         return fail(KV_ERR_ARG, "cache descriptor has a NULL array");
+    if (c->keys_f16 && ((uintptr_t)c->keys_f16 & 15u) != 0)
+        return fail(KV_ERR_ARG, "keys_f16 must be 16-byte aligned");
     return KV_OK;
 }
 
@@ -186,6 +188,7 @@ kvc::CacheView view_of(const kv_cache *c)
     v.lngrp = ilog2(c->head_dim / c->value_group);
     v.keys = c->keys;
     v.vals = c->vals;
+    v.kf16 = c->keys_f16;
     return v;
 }
 
@@ -354,6 +357,7 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
         ap.g.nsub = ap.g.G;
     }
     ap.c = cv;
+    ap.q = q;
     ap.qnib = qnib;
     ap.qpar = qpar;
     ap.klog = klog;

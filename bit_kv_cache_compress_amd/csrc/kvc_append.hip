@@ -88,6 +88,16 @@ __device__ __forceinline__ void encode_values(const float x[8], int i, int Gv, u
     if ((i & (gl - 1)) == 0) sz[(8 * i) / Gv] = s16 | (z16 << 16);
 }
 
+// The binary16 copy of key dims 8i .. 8i+7 of a slot (one 16-byte store), for caches that
+// keep one: x is the input key widened to binary32, rounded to nearest even.
+__device__ __forceinline__ void store_key16(const CacheView &c, size_t slot, int i, const float (&x)[8])
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = float_to_half_bits(x[2 * q]) | (float_to_half_bits(x[2 * q + 1]) << 16);
+    reinterpret_cast<uint4 *>(c.kf16 + slot * kD)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Sum over the 16 lanes of a token-head group.
 __device__ __forceinline__ double sum16(double v)
 {
@@ -118,6 +128,7 @@ __global__ __launch_bounds__(256) void k_append_hadamard(AppendParams p, long N)
     load8(p.k, p.dtype, row, xk);
     load8(p.v, p.dtype, row, xv);
     const size_t slot = slot_of(p, n);
+    if (p.c.kf16) store_key16(p.c, slot, i, xk);
 
     // sigma, then the 7 butterfly levels (h = 1, 2, 4 inside the lane, 8..64 across lanes)
     const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[i >> 2];
@@ -202,6 +213,7 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
             float x[8];
             if (n < N) {
                 load8(p.k, p.dtype, (size_t)n * kD + 8 * i, x);
+                if (p.c.kf16) store_key16(p.c, slot_of(p, n), i, x);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = 0.0f;
@@ -309,6 +321,7 @@ __global__ __launch_bounds__(256) void k_append_dense_small(AppendParams p, long
     if (t < 16) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) kd[8 * t + e] = (double)xk[e];
+        if (p.c.kf16) store_key16(p.c, slot, t, xk);
     }
     __syncthreads();
     double y = 0.0;

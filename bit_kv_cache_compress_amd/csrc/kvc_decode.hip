@@ -983,11 +983,12 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
     return __int_as_float(r);
 }
 
+template <bool EXACT>
 __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 {
     constexpr int CHA = kTopPAttendChunk;  // tokens of the attention chunk
     constexpr int NJ = CHA / 512;          // 16-byte distance loads per lane
-    constexpr int NB = 64;                 // entries per batch
+    constexpr int NB = EXACT ? 32 : 64;    // entries per batch
     constexpr int VU = NB / 16;            // value entries per 4-lane group and batch
     __shared__ union {
         uint16_t list[CHA];                // chunk offsets of the kept tokens
@@ -1085,6 +1086,19 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     const int eg = lane >> 2;  // entries eg + 16 u of a batch
     const int grp = (32 * q4) / p.c.Gv;
     const uint32_t tmask = (1u << logP) - 1u;
+    // exact scores: this lane's 32 query dims (binary32)
+    float qx[EXACT ? 32 : 1];
+    if constexpr (EXACT) {
+        const float4 *qs4 = reinterpret_cast<const float4 *>(p.q + bh * kD + 32 * q4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float4 v = qs4[k];
+            qx[4 * k] = v.x;
+            qx[4 * k + 1] = v.y;
+            qx[4 * k + 2] = v.z;
+            qx[4 * k + 3] = v.w;
+        }
+    }
     float acc[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
@@ -1102,7 +1116,18 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         }
         uint4 kb;
         uint32_t nc;
-        load_key(p.c, sl[VU], kb, nc);
+        if constexpr (!EXACT) load_key(p.c, sl[VU], kb, nc);
+        uint4 kx[EXACT ? VU : 1][4];  // exact scores: binary16 key dims 32 q4 .. 32 q4 + 31
+        if constexpr (EXACT) {
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                if (u < nu) {
+                    const uint4 *kr = reinterpret_cast<const uint4 *>(p.c.kf16 + (size_t)sl[u] * kD + 32 * q4);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) kx[u][k] = kr[k];
+                }
+            }
+        }
         uint4 cw[VU];
         uint32_t szw[VU];
 #pragma unroll
@@ -1114,11 +1139,31 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
             }
         }
         float s;
-        {
+        float sx[EXACT ? VU : 1];  // exact scores of entries eg + 16 u (in all 4 lanes of the group)
+        if constexpr (EXACT) {
+            s = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                sx[u] = -INFINITY;
+                if (u < nu) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t w4[4] = {kx[u][k].x, kx[u][k].y, kx[u][k].z, kx[u][k].w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            a = fmaf(qx[8 * k + e], half_bits_to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+                    }
+                    a = quad_sum(a);
+                    sx[u] = eg + 16 * u < nb ? a : -INFINITY;
+                }
+                s = fmaxf(s, sx[u]);
+            }
+        } else {
             int A;
             score_key<1>(kb, nc, qs, &s, &A);
+            if (lane >= nb) s = -INFINITY;
         }
-        if (lane >= nb) s = -INFINITY;
         const float mnew = fmaxf(mrun, wave_max(s));
         const float scale = (mrun == -INFINITY) ? 0.0f : exp2f((mrun - mnew) * p.klog);
         if (scale != 1.0f) {
@@ -1128,14 +1173,25 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
             for (int j = 0; j < 32; ++j) acc[j] *= scale;
         }
         mrun = mnew;
-        const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
-        lloc += w;
-        wbuf[lane] = w;
-        __syncthreads();
+        float wx[EXACT ? VU : 1];
+        if constexpr (EXACT) {
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                wx[u] = (sx[u] == -INFINITY) ? 0.0f : exp2f((sx[u] - mnew) * p.klog);
+                if (q4 == 0) lloc += wx[u];  // each entry once
+            }
+        } else {
+            const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
+            lloc += w;
+            wbuf[lane] = w;
+            __syncthreads();
+        }
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             if (u < nu) {
-                const float we = wbuf[eg + 16 * u];  // 0 past nb
+                float we;  // 0 past nb
+                if constexpr (EXACT) we = wx[u];
+                else we = wbuf[eg + 16 * u];
                 const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
                 const float zf = half_bits_to_float(szw[u] >> 16);
                 const float ws = we * sf;
@@ -1151,7 +1207,7 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
                 }
             }
         }
-        __syncthreads();  // wbuf is rewritten by the next batch
+        if constexpr (!EXACT) __syncthreads();  // wbuf is rewritten by the next batch
     }
 
     // ---- weight sum, then the value sums over the 16 entry groups: the 4 groups of a
@@ -1323,7 +1379,8 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         // one wave per (attention chunk, query head, sequence)
         const dim3 grid(p.g.NCA, p.g.Hq, p.g.B);
         if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_attend_topp, grid, dim3(64), 0, s, p);
+        if (p.c.kf16) hipLaunchKernelGGL(k_attend_topp<true>, grid, dim3(64), 0, s, p);
+        else hipLaunchKernelGGL(k_attend_topp<false>, grid, dim3(64), 0, s, p);
     } else {
         // one wave per (chunk, KV-head group, sequence)
         const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);

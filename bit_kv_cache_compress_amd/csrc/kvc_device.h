@@ -109,6 +109,14 @@ __device__ __forceinline__ void unpack_codes(uint32_t w, float c[8])
     c[7] = ubyte_to_float<3>(hi);
 }
 
+// Sum over the 4 lanes of a quad (DPP quad_perm 1,0,3,2 then 2,3,0,1); every lane gets it.
+__device__ __forceinline__ float quad_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    return v;
+}
+
 // Wave-wide max, uniform result: DPP within each 16-lane row, then the four row maxima.
 __device__ __forceinline__ float wave_max_u(float v)
 {

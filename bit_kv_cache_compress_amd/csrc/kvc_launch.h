@@ -23,6 +23,7 @@ struct CacheView {
     int lngrp;   // log2(128 / Gv)
     uint32_t *keys;  // [pages][Hkv][P][5]: 4 sign words, norm/corr word
     uint8_t *vals;   // [pages][Hkv][P][64 + 4 * 128/Gv]: codes, scale/zero words
+    uint16_t *kf16;  // nullable [pages][Hkv][P][128]: binary16 keys (unrotated)
 };
 
 // Key record of a slot (20 bytes: 4 sign words, then the norm/corr word).
@@ -125,6 +126,7 @@ struct SelectParams {
 struct AttendParams {
     DecodeGeom g;
     CacheView c;
+    const float *q;        // [B*Hq][128] the queries (exact scores from c.kf16)
     const uint32_t *qnib;
     const float4 *qpar;
     float klog;            // log2(e) / sqrt(D)

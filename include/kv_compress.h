@@ -73,6 +73,12 @@ enum { KV_F16 = 0, KV_F32 = 1 };
  * A key and a value are each one contiguous record (20 and 80 or 72 bytes), so that a
  * decode that gathers a few selected tokens touches one or two 128-byte lines per record
  * rather than one per field.
+ * keys_f16 (nullable): binary16 [num_pages][Hkv][page_size][D], the keys themselves (not
+ *   rotated), rounded to nearest even from binary32 input; 16-byte aligned.  When present,
+ *   appends fill it, and a Top-p decode scores the selected tokens exactly with it (the
+ *   proxy scores still choose them): RaBitQCache's abstract, proxy scores that estimate the
+ *   attention weights to retrieve a token set for sparse attention.  A caller that wants the
+ *   proxy scores for a cache that has the array passes a copy of the struct with it NULL.
  * rot: KV_ROT_DENSE -> binary16 [D][D] row-major orthogonal matrix R (k' = R k);
  *      KV_ROT_HADAMARD -> uint32 [D/32] random signs (bit j set: sigma_j = -1), and
  *      R = H diag(sigma) / sqrt(D) with H the Sylvester-order Hadamard matrix.
@@ -88,6 +94,7 @@ typedef struct kv_cache {
     const void *rot;       /* device: see above */
     uint32_t *keys;        /* device, 4-byte aligned: see above */
     uint8_t *vals;         /* device, 4-byte aligned: see above */
+    uint16_t *keys_f16;    /* device, nullable, 16-byte aligned: see above */
 } kv_cache;
 
 /* Optional intermediate outputs of kv_decode_attend ([host] struct; every member is a
@@ -150,6 +157,8 @@ int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const vo
  *   max_seq_len [host] upper bound of seq_lens (sizes the grid and the workspace)
  *   top_p       [host] >= 1: softmax over all tokens; in (0, 1): adaptive Top-p, then the
  *               softmax renormalised over the selected tokens.  <= 0 or NaN is an error.
+ *               Under Top-p with c->keys_f16 set, the softmax over the selected tokens uses
+ *               the exact scores <q, k> of their binary16 keys instead of the proxy scores.
  *   out         float [B][Hq][D]
  *   dbg         [host] nullable, see kv_debug
  *   workspace   device scratch of at least kv_decode_workspace_bytes(...) bytes; its

@@ -11,7 +11,10 @@ keys are stored as the sign bits of a random rotation with a binary16 norm and c
 ("RaBitQCache" abstract; "H1B-KV" key design), values as per-group 4-bit linear codes
 ("H1B-KV" key design), scores come from binary x INT4 dot products ("RaBitQCache" key
 design), an adaptive Top-p selects tokens ("RaBitQCache" abstract), and the output is the
-softmax-weighted sum of the decoded 4-bit values ("H1B-KV" technical framework).
+softmax-weighted sum of the decoded 4-bit values ("H1B-KV" technical framework).  With the
+keys also kept in binary16, the selected tokens are attended with exact scores <q, k>
+("RaBitQCache" abstract: proxy scores that estimate the attention weights retrieve the set
+for sparse attention); that path is plain numpy in binary64.
 
 Parity pins: every function here is checked against something other than itself in
 ``tests/test_oracle_*.py`` (brute force, closed forms, library routines, statistics).
@@ -213,6 +216,39 @@ def attend(s, codes, sz, D: int, Gv: int, idx=None) -> np.ndarray:
     return out
 
 
+def value_decode(codes, sz, D: int, Gv: int) -> np.ndarray:
+    """The 4-bit values of n tokens in binary64: code * scale + zero with the group's binary16
+    scale and zero point ("H1B-KV" key design, 4-bit linear values).  codes (n, D/2) uint8 with
+    the even dim in the low nibble; sz (n, D/Gv, 2) uint16 (scale, zero)."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1, D // 2)
+    sz = np.asarray(sz, dtype=np.uint16).reshape(-1, D // Gv, 2)
+    c = np.empty((codes.shape[0], D), dtype=np.float64)
+    c[:, 0::2] = codes & 15
+    c[:, 1::2] = codes >> 4
+    scale = sz[..., 0].view(np.float16).astype(np.float64)
+    zero = sz[..., 1].view(np.float16).astype(np.float64)
+    return c * np.repeat(scale, Gv, axis=1) + np.repeat(zero, Gv, axis=1)
+
+
+def exact_scores(q, k16) -> np.ndarray:
+    """<q, k> in binary64 for a binary32 query q (D,) and binary16 keys k16 (n, D)."""
+    k = np.asarray(k16, dtype=np.float16).astype(np.float64)
+    return k @ np.asarray(q, dtype=np.float32).astype(np.float64)
+
+
+def attend_exact(q, k16, codes, sz, D: int, Gv: int, idx) -> np.ndarray:
+    """Attention over a retrieved token set with exact scores ("RaBitQCache" abstract: the
+    proxy scores estimate the attention weights so as to retrieve the tokens that sparse
+    attention then runs over): softmax(<q, k_i> / sqrt(D)) over i in idx, times the decoded
+    4-bit values, in binary64.  An empty set gives zeros."""
+    idx = np.asarray(idx, dtype=np.int64)
+    if idx.size == 0:
+        return np.zeros(D)
+    s = exact_scores(q, np.asarray(k16)[idx])
+    w = np.exp((s - s.max()) / np.sqrt(D))
+    return (w @ value_decode(np.asarray(codes)[idx], np.asarray(sz)[idx], D, Gv)) / w.sum()
+
+
 # ----------------------------------------------------------------------------------------
 # Paged cache: per (physical page, KV head) structure-of-arrays
 # ----------------------------------------------------------------------------------------
@@ -223,10 +259,12 @@ class PagedCache:
       key_nc    uint32 [P]           binary16 norm (low half) | binary16 corr (high half)
       val_codes uint8  [P][D/2]      4-bit value codes, even dim in the low nibble
       val_sz    uint32 [P][D/Gv]     binary16 scale (low half) | binary16 zero (high half)
+      key_f16   float16 [P][D]       with exact_keys: the keys rounded to binary16 (nearest even)
     """
 
-    def __init__(self, num_pages, Hkv, P, D, Gv):
+    def __init__(self, num_pages, Hkv, P, D, Gv, exact_keys=False):
         self.num_pages, self.Hkv, self.P, self.D, self.Gv = num_pages, Hkv, P, D, Gv
+        self.key_f16 = np.zeros((num_pages, Hkv, P, D), dtype=np.float16) if exact_keys else None
         self.key_bits = np.zeros((num_pages, Hkv, P, D // 32), dtype=np.uint32)
         self.key_nc = np.zeros((num_pages, Hkv, P), dtype=np.uint32)
         self.val_codes = np.zeros((num_pages, Hkv, P, D // 2), dtype=np.uint8)
@@ -263,10 +301,14 @@ def append(cache: PagedCache, rot: Rotation, k, v, start_pos, page_table):
             cache.key_nc[pg, h, sl] = nc[:, 0].astype(np.uint32) | (nc[:, 1].astype(np.uint32) << 16)
             cache.val_codes[pg, h, sl] = codes
             cache.val_sz[pg, h, sl] = sz[..., 0].astype(np.uint32) | (sz[..., 1].astype(np.uint32) << 16)
+            if cache.key_f16 is not None:
+                cache.key_f16[pg, h, sl] = k[b, :, h, :].astype(np.float16)
 
 
-def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p):
-    """One (sequence, query head) decode step.  Query head h reads KV head h*Hkv//Hq."""
+def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy=False):
+    """One (sequence, query head) decode step.  Query head h reads KV head h*Hkv//Hq.  Under
+    Top-p, a cache with binary16 keys attends the selected set with exact scores (out), and
+    the proxy-score output is kept as out_proxy; proxy=True ignores the binary16 keys."""
     D, Gv = cache.D, cache.Gv
     kvh = h * cache.Hkv // Hq
     qe = query_encode(rot, q_h)
@@ -283,18 +325,22 @@ def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, 
         tp = topp(s, top_p, D)
         res.update(idx=tp["idx"], emax=tp["emax"], bstar=tp["bstar"], Z=tp["Z"], Tp=tp["Tp"])
         res["out"] = attend(s, codes, sz, D, Gv, tp["idx"])
+        if cache.key_f16 is not None and not proxy:
+            pg, sl = cache.locate(b, np.arange(L), page_table)
+            res["out_proxy"] = res["out"]
+            res["out"] = attend_exact(q_h, cache.key_f16[pg, kvh, sl], codes, sz, D, Gv, tp["idx"])
     else:
         res["idx"] = None
         res["out"] = attend(s, codes, sz, D, Gv)
     return res
 
 
-def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None):
+def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None, proxy=False):
     """Decode step for q (B, Hq, D).  Returns {(b, h): decode_head(...)} for the requested
     (b, h) pairs (all by default)."""
     q = np.asarray(q, dtype=np.float32)
     B, Hq, D = q.shape
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Hq)]
-    return {(b, h): decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p)
+    return {(b, h): decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy)
             for (b, h) in heads}

@@ -29,8 +29,8 @@ class Case:
     def max_len(self):
         return int(max(1, self.lens.max()))
 
-    def oracle_cache(self):
-        c = oracle.PagedCache(self.npages, self.wl.Hkv, self.wl.P, self.wl.D, self.wl.Gv)
+    def oracle_cache(self, exact_keys=False):
+        c = oracle.PagedCache(self.npages, self.wl.Hkv, self.wl.P, self.wl.D, self.wl.Gv, exact_keys=exact_keys)
         for b in range(self.wl.B):
             n = int(self.lens[b])
             if n:
@@ -42,21 +42,21 @@ class Case:
         return oracle.decode(cache, self.orot, self.q, self.lens, self.pt, top_p, heads=heads)
 
 
-def gpu_empty_cache(case: Case, device="cuda"):
+def gpu_empty_cache(case: Case, device="cuda", exact_keys=False):
     from bit_kv_cache_compress_amd import KVCache
 
     rot = case.rot_raw
     return KVCache(case.npages, case.wl.Hkv, rot, rot_kind=case.rot_kind, page_size=case.wl.P,
-                   value_group=case.wl.Gv, device=device)
+                   value_group=case.wl.Gv, device=device, exact_keys=exact_keys)
 
 
-def gpu_append(case: Case, chunk=None, device="cuda"):
+def gpu_append(case: Case, chunk=None, device="cuda", exact_keys=False):
     """The library's append of every sequence (optionally in chunks of `chunk` tokens)."""
     import torch
 
     from bit_kv_cache_compress_amd import append
 
-    cache = gpu_empty_cache(case, device)
+    cache = gpu_empty_cache(case, device, exact_keys=exact_keys)
     for b in range(case.wl.B):
         n = int(case.lens[b])
         step = n if chunk is None else chunk
@@ -75,7 +75,9 @@ def upload(cache_o: oracle.PagedCache, case: Case, device="cuda"):
     """A library cache holding the oracle's bytes."""
     import torch
 
-    g = gpu_empty_cache(case, device)
+    g = gpu_empty_cache(case, device, exact_keys=cache_o.key_f16 is not None)
+    if cache_o.key_f16 is not None:
+        g.keys_f16.copy_(torch.from_numpy(cache_o.key_f16))
     g.key_bits.copy_(torch.from_numpy(cache_o.key_bits.view(np.int32)))
     g.key_nc.copy_(torch.from_numpy(cache_o.key_nc.view(np.int32)))
     g.val_codes.copy_(torch.from_numpy(cache_o.val_codes))

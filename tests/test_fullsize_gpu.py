@@ -272,3 +272,49 @@ def test_append32k_and_decode1m_full_size():
             np.testing.assert_array_equal(dbg.sel_idx[0, hh, :cnt[0, hh]].cpu().numpy(), tp["idx"])
         assert rel_err(o[0, hh], oracle.attend(s, codes, sz, D, Gv, tp["idx"])) <= 2e-3
         _say(f"[full] head {hh}: kept {cnt[0, hh]} of {L}")
+
+
+def test_gqa_128k_exact_keys_full_size():
+    """The 128k-context GQA Top-p workload with binary16 keys kept next to the compressed
+    cache: the proxy scores select, the selected tokens are attended with exact scores.
+    Sampled units: the binary16 keys and the outputs against the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_kv_cache_compress_amd as kvc
+
+    wl = W.CONFIGS[2]
+    dev = torch.device("cuda")
+    B, Hq, Hkv, L, G = wl.B, wl.Hq, wl.Hkv, wl.L, wl.Hq // wl.Hkv
+    _say(f"[full] {wl.name} with binary16 keys")
+    K, V, q = W.draw_device(wl, dev)
+    lens = np.full(B, L, np.int32)
+    pt_np, npages = W.page_layout(wl, lens)
+    kind, R16 = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, Hkv, R16, rot_kind=kind, page_size=wl.P, value_group=wl.Gv, device=dev,
+                        exact_keys=True)
+    pt = torch.from_numpy(pt_np).to(dev)
+    seq = torch.from_numpy(lens).to(dev)
+    kvc.append(cache, K, V, torch.zeros(B, dtype=torch.int32, device=dev), pt)
+    dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False)
+    out = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    _say("[full] library decode done")
+    cnt = dbg.sel_count.cpu().numpy()
+    o = out.cpu().numpy()
+    qn = q.cpu().numpy()
+    vc = cache.val_codes.cpu().numpy()
+    vs = cache.val_sz.cpu().numpy().view(np.uint32)
+    for b, h in [(1, 2), (2, 5)]:
+        t = np.arange(L)
+        pg, sl = pt_np[b, t // wl.P], t % wl.P
+        k16 = cache.keys_f16[:, h].cpu().numpy()[pg, sl]
+        np.testing.assert_array_equal(k16.view(np.uint16), K[b, :, h].cpu().numpy().view(np.uint16))
+        codes = vc[pg, h, sl]
+        szw = vs[pg, h, sl]
+        sz = np.stack([(szw & 0xFFFF).astype(np.uint16), (szw >> 16).astype(np.uint16)], axis=-1)
+        for hh in range(h * G, (h + 1) * G):
+            idx = dbg.sel_idx[b, hh, :cnt[b, hh]].cpu().numpy()
+            ref = oracle.attend_exact(qn[b, hh], k16, codes, sz, wl.D, wl.Gv, idx)
+            assert rel_err(o[b, hh], ref) <= 2e-3
+        _say(f"[full] unit {(b, h)} ok, kept {cnt[b, h * G:(h + 1) * G].tolist()}")

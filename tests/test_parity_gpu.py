@@ -71,7 +71,7 @@ def test_append_parity(name):
     _say(f"[append] {name} ok {stats}")
 
 
-def _decode_with_debug(c, cache, top_p, scores=True):
+def _decode_with_debug(c, cache, top_p, scores=True, proxy=False):
     """Decode with debug outputs; scores=False runs the kernels of a decode without debug
     output (the per-token scores are not written) and still returns the Top-p sets."""
     from bit_kv_cache_compress_amd import DecodeDebug, decode_attend
@@ -81,7 +81,7 @@ def _decode_with_debug(c, cache, top_p, scores=True):
     lens = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
     pt = torch.from_numpy(c.pt).to(dev)
     dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev, scores=scores)
-    out = decode_attend(cache, q, lens, pt, top_p=top_p, max_seq_len=c.max_len, debug=dbg)
+    out = decode_attend(cache, q, lens, pt, top_p=top_p, max_seq_len=c.max_len, debug=dbg, proxy=proxy)
     torch.cuda.synchronize()
     return out.cpu().numpy(), dbg
 
@@ -156,6 +156,34 @@ def test_score_kernels_agree(name):
     np.testing.assert_array_equal(d_fast.sel_idx.cpu().numpy(), d_dbg.sel_idx.cpu().numpy())
     assert np.array_equal(o_fast.view(np.uint32), o_dbg.view(np.uint32))
     _say(f"[kernels] {name} ok")
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if CASES[n]["wl"].top_p < 1.0])
+def test_exact_keys(name):
+    """Binary16 keys next to the compressed cache: the appended bytes equal the oracle's
+    (nearest-even rounding of the input); a Top-p decode keeps the proxy sets and attends them
+    with the exact scores <q, k>; proxy=True gives the proxy-score output."""
+    c = _case(name)
+    _say(f"[exact] {name}")
+    oc = c.oracle_cache(exact_keys=True)
+    g = gpu_append(c, exact_keys=True)
+    np.testing.assert_array_equal(g.keys_f16.cpu().numpy().view(np.uint16), oc.key_f16.view(np.uint16))
+    g = upload(oc, c)
+    ref = c.oracle_decode(oc, c.wl.top_p)
+    out, dbg = _decode_with_debug(c, g, c.wl.top_p, scores=False)
+    out_p, _ = _decode_with_debug(c, g, c.wl.top_p, scores=False, proxy=True)
+    worst = 0.0
+    for (b, h), r in ref.items():
+        if int(c.lens[b]) == 0:
+            assert np.abs(out[b, h]).max() == 0.0
+            continue
+        cnt = int(dbg.sel_count[b, h])
+        np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+        e = float(rel_err(out[b, h], r["out"]))
+        worst = max(worst, e)
+        assert e <= TOL, (b, h, e)
+        assert rel_err(out_p[b, h], r["out_proxy"]) <= TOL
+    _say(f"[exact] {name} ok, worst rel err {worst:.2e}")
 
 
 def test_topp_sweep():
