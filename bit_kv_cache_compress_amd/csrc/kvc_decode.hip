@@ -526,31 +526,25 @@ __global__ __launch_bounds__(256) void k_bin_scores(BinScoresParams p)
         p.dl[bh * g.Lpad + t0 + tl] = (uint16_t)min(emax_s[0] - ebuf[tl], kBins);
 }
 
-// Top bin of (b, h): max over the chunk top bins.
-__device__ __forceinline__ int global_top_bin(const DecodeGeom &g, const int32_t *lmax, size_t bh, int nch,
-                                              int *red /* [4] */, int *out /* [1] */)
-{
-    int m[1] = {-kBinClamp};
-    for (int c = threadIdx.x; c < nch; c += kBlock) m[0] = max(m[0], lmax[bh * g.NC + c]);
-    block_reduce<1>(m, red, out, MaxI());
-    return out[0];
-}
-
 // ---------------------------------------------------------------------------------------
 // Histogram pass: per (split, query head, sequence) block, counts of tokens per bin
-// distance d = (e_max - chunk top) + distance-to-chunk-top, d < 8192.  The last block of a
-// (b, h) to finish (arrival counter) computes the Top-p threshold from all splits.
+// distance d = (e_max - chunk top) + distance-to-chunk-top, d < 8192, in LDS (atomics), then
+// written as 16-bit counts.  1024 threads (16 waves) per block: the pass is latency-bound,
+// and more waves per SIMD hide the distance loads.  The threshold pass follows.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_hist(HistParams p)
+constexpr int kHistThreads = 1024;
+
+__global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
 {
+    constexpr int kT = kHistThreads;
+    constexpr int U = 32768 / (8 * kT);    // 16-byte loads per thread: 32768 tokens per round
     __shared__ uint32_t hist[kBins + 1];  // + a bin for tokens that are not counted
-    __shared__ int delta[kBlock];
-    __shared__ int red[4];
-    __shared__ int top[1];
+    __shared__ int delta[kT];
+    __shared__ int red[kT / 64];
     const DecodeGeom &g = p.g;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t bh = (size_t)b * g.Hq + h;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = g.seq_lens[b];
     const int nch = L > 0 ? (L + g.CH - 1) >> g.logCH : 0;
     const int c0 = split * p.cps;
@@ -559,26 +553,32 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
     const int tb = c0 << g.logCH;
     const int te = min(L, c1 << g.logCH);
     const uint16_t *row = p.dl + bh * g.Lpad;
-    // 8 tokens per 16-byte load, 16 loads in flight (tb is a multiple of CH >= 256).  The
-    // first batch is issued before the top-bin reduction, whose reads then overlap it.
-    constexpr int U = 16;
-    constexpr int kStep = 8 * kBlock * U;
+    // 8 tokens per 16-byte load, U loads in flight (tb is a multiple of CH >= 256).  The
+    // first round is issued before the top-bin reduction, whose reads then overlap it.
+    constexpr int kStep = 8 * kT * U;
     uint4 raw[U];
     int t = tb + 8 * tid;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (t + 8 * kBlock * u < te) raw[u] = *reinterpret_cast<const uint4 *>(row + t + 8 * kBlock * u);
+        if (t + 8 * kT * u < te) raw[u] = *reinterpret_cast<const uint4 *>(row + t + 8 * kT * u);
     // the split's chunk top bins, one per thread (the plan keeps cps * CH <= 65535 with
-    // CH >= 256, so cps < kBlock), also read before the reduction
+    // CH >= 256, so cps < 256 <= kT), and the chunk top bins of the whole sequence for e_max
     const int lmc = tid < c1 - c0 ? p.lmax[bh * g.NC + c0 + tid] : 0;
-    for (int i = tid; i <= kBins; i += kBlock) hist[i] = 0u;
-    const int emax = global_top_bin(g, p.lmax, bh, nch, red, top);
+    int m = -kBinClamp;
+    for (int c = tid; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
+    for (int i = tid; i <= kBins; i += kT) hist[i] = 0u;
+    m = wave_max_i(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    int emax = red[0];
+#pragma unroll
+    for (int w = 1; w < kT / 64; ++w) emax = max(emax, red[w]);
     if (tid < c1 - c0) delta[tid] = emax - lmc;
     __syncthreads();
     for (; t < te; t += kStep) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tu = t + 8 * kBlock * u;
+            const int tu = t + 8 * kT * u;
             if (tu < te) {
                 const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
                 const int dc = delta[(tu >> g.logCH) - c0];  // 8 tokens share a chunk
@@ -592,13 +592,13 @@ __global__ __launch_bounds__(256) void k_hist(HistParams p)
         if (t + kStep < te) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (t + kStep + 8 * kBlock * u < te)
-                    raw[u] = *reinterpret_cast<const uint4 *>(row + t + kStep + 8 * kBlock * u);
+                if (t + kStep + 8 * kT * u < te)
+                    raw[u] = *reinterpret_cast<const uint4 *>(row + t + kStep + 8 * kT * u);
         }
     }
     __syncthreads();
     uint4 *dst = reinterpret_cast<uint4 *>(p.hist + (bh * p.nsplit + split) * kBins);
-    for (int i = tid; i < kBins / 8; i += kBlock) {
+    for (int i = tid; i < kBins / 8; i += kT) {
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) w[q] = hist[8 * i + 2 * q] | (hist[8 * i + 2 * q + 1] << 16);
@@ -1276,8 +1276,11 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
         const int c = sl + NS * i;
         v[i] = c < nch ? po[(size_t)c * kD] : 0.0f;
     }
-    float m = -INFINITY;
-    for (int c = tid; c < nch; c += kT) m = fmaxf(m, p.pm[bh * g.NCA + c]);
+    // the first kT chunks' max and weight sum are read once, with the value sums in flight
+    const float mc0 = tid < nch ? p.pm[bh * g.NCA + tid] : -INFINITY;
+    const float lc0 = tid < nch ? p.pl[bh * g.NCA + tid] : 0.0f;
+    float m = mc0;
+    for (int c = tid + kT; c < nch; c += kT) m = fmaxf(m, p.pm[bh * g.NCA + c]);
     m = wave_max(m);
     if (lane == 0) redf[0][wave] = m;
     __syncthreads();
@@ -1285,7 +1288,12 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 #pragma unroll
     for (int w = 1; w < kT / 64; ++w) M = fmaxf(M, redf[0][w]);
     float den = 0.0f;
-    for (int c = tid; c < nch; c += kT) {
+    if (tid < nch) {
+        const float a = (mc0 == -INFINITY) ? 0.0f : exp2f((mc0 - M) * p.klog);
+        alpha[tid] = a;
+        den = a * lc0;
+    }
+    for (int c = tid + kT; c < nch; c += kT) {
         const float mc = p.pm[bh * g.NCA + c];
         const float a = (mc == -INFINITY) ? 0.0f : exp2f((mc - M) * p.klog);
         alpha[c] = a;
@@ -1303,7 +1311,19 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
         const int c = sl + NS * i;
         if (c < nch) num = fmaf(alpha[c], v[i], num);
     }
-    for (int c = sl + NS * PF; c < nch; c += NS) num = fmaf(alpha[c], po[(size_t)c * kD], num);
+    for (int c0 = sl + NS * PF; c0 < nch; c0 += NS * PF) {
+        // the rest in rounds of PF loads in flight
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int c = c0 + NS * i;
+            v[i] = c < nch ? po[(size_t)c * kD] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int c = c0 + NS * i;
+            if (c < nch) num = fmaf(alpha[c], v[i], num);
+        }
+    }
     part[sl][d] = num;
     __syncthreads();
     if (tid < kD) {
@@ -1356,7 +1376,7 @@ hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s)
 
 hipError_t launch_hist(const HistParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kHistThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_thresh, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
