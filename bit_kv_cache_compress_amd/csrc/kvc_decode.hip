@@ -455,9 +455,6 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
     for (int u = 0; u < U; ++u) load_key(p.c, slot[u], kb[u], nc[u]);
     __builtin_amdgcn_sched_barrier(0);
     int e[U][GB];
-    int lm[GB];
-#pragma unroll
-    for (int h = 0; h < GB; ++h) lm[h] = kNone;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         uint32_t w[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
@@ -476,19 +473,29 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
                               (int)((w[t] >> 1) & 0x44444444u), 0, 0, 0, 0};
             d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[t], bt, d, 0, 4, 0, 127, 0, 127);
         }
-        const int lim = lane + 64 * u < n ? INT_MAX : kNone;
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             const float a = d[h];
             const float cp = c0[h] * fP;
             const float s = fmaf(c1[h], a, cp) * r;
-            const int ev = min(score_bin(s, p.kbin), lim);
-            e[u][h] = ev;
-            lm[h] = max(lm[h], ev);
+            e[u][h] = score_bin(s, p.kbin);
         }
     }
+    if (n < CH) {  // uniform: the last chunk of a sequence; positions past the end sit below all
 #pragma unroll
-    for (int h = 0; h < GB; ++h) lm[h] = wave_max_i(lm[h]);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int h = 0; h < GB; ++h)
+                if (lane + 64 * u >= n) e[u][h] = kNone;
+    }
+    int lm[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        int m = e[0][h];
+#pragma unroll
+        for (int u = 1; u < U; ++u) m = max(m, e[u][h]);
+        lm[h] = wave_max_iu(m);
+    }
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < GB; ++h) p.lmax[(size_t)(bh0 + h) * g.NC + chunk] = lm[h];

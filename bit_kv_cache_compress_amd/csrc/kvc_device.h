@@ -118,6 +118,17 @@ __device__ __forceinline__ float quad_sum(float v)
 }
 
 // Wave-wide max, uniform result: DPP within each 16-lane row, then the four row maxima.
+// Wave max of an int, returned in a scalar register: DPP within rows, then the 4 row maxima.
+__device__ __forceinline__ int wave_max_iu(int v)
+{
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));  // row_ror 4
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));  // row_ror 8
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 __device__ __forceinline__ float wave_max_u(float v)
 {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));   // quad_perm 1,0,3,2
