@@ -15,8 +15,9 @@ KV_OK, KV_ERR_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP = 0, -1, -2,
 KV_ROT_DENSE, KV_ROT_HADAMARD = 0, 1
 KV_F16, KV_F32 = 0, 1
 
-EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_workspace_bytes", "kv_topp_select",
-           "kv_topp_workspace_bytes", "kv_last_error", "kv_version")
+EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_tail", "kv_decode_workspace_bytes",
+           "kv_tail_append", "kv_tail_retire", "kv_topp_select", "kv_topp_workspace_bytes", "kv_last_error",
+           "kv_version")
 
 
 class KVCacheDesc(ctypes.Structure):
@@ -45,6 +46,15 @@ class KVDebug(ctypes.Structure):
         ("sel_idx", ctypes.c_void_p),
         ("sel_bins", ctypes.c_void_p),
         ("stage_events", ctypes.c_void_p),
+    ]
+
+
+class KVTailDesc(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("len", ctypes.c_void_p),
+        ("capacity", ctypes.c_int32),
     ]
 
 
@@ -79,6 +89,13 @@ def lib():
     L.kv_decode_attend.argtypes = [ctypes.POINTER(KVCacheDesc), P, i32, i32, P, i32, P, i32, f32, P,
                                    ctypes.POINTER(KVDebug), P, sz, P]
     L.kv_decode_attend.restype = ctypes.c_int
+    L.kv_decode_attend_tail.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVTailDesc), P, i32, i32, P, i32,
+                                        P, i32, f32, P, ctypes.POINTER(KVDebug), P, sz, P]
+    L.kv_decode_attend_tail.restype = ctypes.c_int
+    L.kv_tail_append.argtypes = [ctypes.POINTER(KVTailDesc), i32, i32, i32, P, P, i32, i32, P]
+    L.kv_tail_append.restype = ctypes.c_int
+    L.kv_tail_retire.argtypes = [ctypes.POINTER(KVTailDesc), i32, i32, i32, i32, P, P]
+    L.kv_tail_retire.restype = ctypes.c_int
     L.kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, f32]
     L.kv_decode_workspace_bytes.restype = sz
     L.kv_topp_select.argtypes = [P, i32, P, i32, i32, i32, f32, P, P, P, sz, P]

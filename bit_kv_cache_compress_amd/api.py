@@ -216,9 +216,11 @@ class StageTimer:
 def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
                   top_p: float = 1.0, max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
-                  debug_struct: Optional[L.KVDebug] = None, proxy: bool = False) -> torch.Tensor:
+                  debug_struct: Optional[L.KVDebug] = None, proxy: bool = False,
+                  tail: Optional["Tail"] = None) -> torch.Tensor:
     """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32.  Under Top-p, a
-    cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set."""
+    cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set.
+    With ``tail``, each sequence's binary16 tail tokens follow its seq_lens compressed ones."""
     dev = cache.device
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
@@ -242,10 +244,61 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
         debug_struct = debug.struct()
     dbg = ctypes.byref(debug_struct) if debug_struct is not None else None
     desc = cache.proxy_desc if proxy else cache.desc
-    L.check(L.lib().kv_decode_attend(ctypes.byref(desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
-                                     _ptr(page_table), max_pages, float(top_p), _ptr(out), dbg, _ptr(workspace),
-                                     workspace.numel(), _stream(dev)))
+    if tail is None:
+        L.check(L.lib().kv_decode_attend(ctypes.byref(desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
+                                         _ptr(page_table), max_pages, float(top_p), _ptr(out), dbg,
+                                         _ptr(workspace), workspace.numel(), _stream(dev)))
+    else:
+        if tail.k.shape[0] != B or tail.k.shape[2] != cache.num_kv_heads:
+            raise ValueError(f"tail must be [{B}, capacity, {cache.num_kv_heads}, {HEAD_DIM}]")
+        L.check(L.lib().kv_decode_attend_tail(ctypes.byref(desc), ctypes.byref(tail.desc), _ptr(q), B, Hq,
+                                              _ptr(seq_lens), int(max_seq_len), _ptr(page_table), max_pages,
+                                              float(top_p), _ptr(out), dbg, _ptr(workspace), workspace.numel(),
+                                              _stream(dev)))
     return out
+
+
+class Tail:
+    """Binary16 tail of uncompressed recent tokens (device memory owned by torch tensors):
+    ``k``, ``v`` float16 [B, capacity, Hkv, 128] (token j of sequence b's tail at [b, j]),
+    ``len`` int32 [B].  ``page(b, j, n)`` views tokens j .. j+n-1 of sequence b's tail as the
+    [1, n, Hkv, 128] input of ``append`` (to compress them into the cache)."""
+
+    def __init__(self, B: int, capacity: int, num_kv_heads: int, device="cuda"):
+        device = torch.device(device)
+        if device.type == "cuda" and device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = device
+        self.B, self.num_kv_heads = int(B), int(num_kv_heads)
+        self.k = torch.zeros((B, capacity, num_kv_heads, HEAD_DIM), dtype=torch.float16, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.len = torch.zeros(B, dtype=torch.int32, device=device)
+        self.capacity = int(capacity)
+        self.desc = L.KVTailDesc(self.k.data_ptr(), self.v.data_ptr(), self.len.data_ptr(), self.capacity)
+
+    def page(self, b: int, j: int, n: int):
+        return self.k[b:b + 1, j:j + n], self.v[b:b + 1, j:j + n]
+
+    def append(self, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Writes k, v [B, n_new, Hkv, 128] (float16 or float32) after each sequence's tail."""
+        if k.dim() != 4 or k.shape[0] != self.B or k.shape[2] != self.num_kv_heads or k.shape[3] != HEAD_DIM:
+            raise ValueError(f"k must be [{self.B}, n_new, {self.num_kv_heads}, {HEAD_DIM}]")
+        dtype = {torch.float16: L.KV_F16, torch.float32: L.KV_F32}.get(k.dtype)
+        if dtype is None:
+            raise TypeError("k, v must be float16 or float32")
+        _need(k, "k", k.dtype, self.device)
+        _need(v, "v", k.dtype, self.device, k.shape)
+        L.check(L.lib().kv_tail_append(ctypes.byref(self.desc), self.num_kv_heads, HEAD_DIM, dtype, _ptr(k), _ptr(v),
+                                       self.B, int(k.shape[1]), _stream(self.device)))
+
+    def retire(self, n: int, seq_lens: Optional[torch.Tensor] = None) -> None:
+        """Drops the first n tokens of every tail (after they were compressed into the cache)
+        and adds n to seq_lens when given."""
+        if seq_lens is not None:
+            _need(seq_lens, "seq_lens", torch.int32, self.device, (self.B,))
+        L.check(L.lib().kv_tail_retire(ctypes.byref(self.desc), self.num_kv_heads, HEAD_DIM, self.B, int(n),
+                                       _ptr(seq_lens) if seq_lens is not None else None,
+                                       _stream(self.device)))
 
 
 def topp_workspace_bytes(B: int, Hq: int, ld: int) -> int:

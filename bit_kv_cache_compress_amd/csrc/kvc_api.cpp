@@ -44,7 +44,7 @@ struct Plan {
     kvc::DecodeGeom g;
     bool topp;
     int nsplit, cps;
-    size_t off_qpl, off_qa, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po;
+    size_t off_qpl, off_qa, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po, off_tm, off_tl, off_to;
     size_t total;
 };
 
@@ -97,6 +97,10 @@ void plan_layout(Plan &pl, int BH)
     pl.off_pm = take((size_t)BH * NCA * 4);
     pl.off_pl = take((size_t)BH * NCA * 4);
     pl.off_po = take((size_t)BH * NCA * 128 * 4);
+    // the binary16 tail's partial per (sequence, query head) (kv_decode_attend_tail)
+    pl.off_tm = take((size_t)BH * 4);
+    pl.off_tl = take((size_t)BH * 4);
+    pl.off_to = take((size_t)BH * 128 * 4);
     if (pl.topp) {
         // histogram splits: >= 512 blocks over (split, head, sequence); a split holds fewer
         // than 65536 tokens (16-bit partial counts) and at most 256 chunks (one per thread)
@@ -178,6 +182,17 @@ int check_cache(const kv_cache *c)
     return KV_OK;
 }
 
+int check_tail(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t B)
+{
+    if (!t) return fail(KV_ERR_ARG, "tail descriptor is NULL");
+    if (!t->k || !t->v || !t->len) return fail(KV_ERR_ARG, "tail has a NULL array");
+    if (t->capacity <= 0) return fail(KV_ERR_ARG, "tail capacity must be positive (got %d)", t->capacity);
+    if ((((uintptr_t)t->k | (uintptr_t)t->v) & 15u) != 0) return fail(KV_ERR_ARG, "tail k and v must be 16-byte aligned");
+    if (head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", head_dim);
+    if (num_kv_heads <= 0 || B <= 0) return fail(KV_ERR_ARG, "num_kv_heads and B must be positive");
+    return KV_OK;
+}
+
 kvc::CacheView view_of(const kv_cache *c)
 {
     kvc::CacheView v;
@@ -251,12 +266,13 @@ size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max
     return pl.total;
 }
 
-int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, const int32_t *seq_lens,
-                     int32_t max_seq_len, const int32_t *page_table, int32_t max_pages, float top_p,
-                     float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
-                     hipStream_t stream)
+namespace {
+
+int decode_impl(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
+                const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
+                float top_p, float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
+                hipStream_t stream)
 {
-    g_err[0] = 0;
     int rc = check_cache(c);
     if (rc) return rc;
     rc = check_decode_shapes(B, Hq, c->num_kv_heads, max_seq_len, c->head_dim, top_p);
@@ -378,12 +394,110 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
     mp.pm = ap.pm;
     mp.pl = ap.pl;
     mp.po = ap.po;
+    mp.tm = mp.tl = mp.to = nullptr;
     mp.out = out;
+    if (tail) {
+        kvc::TailParams tp;
+        tp.B = B;
+        tp.Hq = Hq;
+        tp.G = Hq / c->num_kv_heads;
+        tp.Hkv = c->num_kv_heads;
+        tp.klog = klog;
+        tp.q = q;
+        tp.k = tail->k;
+        tp.v = tail->v;
+        tp.len = tail->len;
+        tp.cap = tail->capacity;
+        tp.tm = at<float>(workspace, pl.off_tm);
+        tp.tl = at<float>(workspace, pl.off_tl);
+        tp.to = at<float>(workspace, pl.off_to);
+        stage_mark(dbg, KV_STAGE_ATTEND, true, stream);
+        e = kvc::launch_tail(tp, stream);
+        if (e != hipSuccess) return hip_fail(e, "tail attention launch");
+        stage_mark(dbg, KV_STAGE_ATTEND, false, stream);
+        mp.tm = tp.tm;
+        mp.tl = tp.tl;
+        mp.to = tp.to;
+    }
     stage_mark(dbg, KV_STAGE_MERGE, true, stream);
     e = kvc::launch_merge(mp, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     stage_mark(dbg, KV_STAGE_MERGE, false, stream);
     return KV_OK;
+}
+
+}  // namespace
+
+int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, const int32_t *seq_lens,
+                     int32_t max_seq_len, const int32_t *page_table, int32_t max_pages, float top_p,
+                     float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream)
+{
+    g_err[0] = 0;
+    return decode_impl(c, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
+                       workspace, workspace_bytes, stream);
+}
+
+int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
+                          const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                          int32_t max_pages, float top_p, float *out, const kv_debug *dbg, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
+    int rc = check_tail(tail, c->num_kv_heads, c->head_dim, B);
+    if (rc) return rc;
+    return decode_impl(c, tail, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
+                       workspace, workspace_bytes, stream);
+}
+
+int kv_tail_append(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t dtype, const void *k,
+                   const void *v, int32_t B, int32_t n_new, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_tail(t, num_kv_heads, head_dim, B);
+    if (rc) return rc;
+    if (dtype != KV_F16 && dtype != KV_F32) return fail(KV_ERR_ARG, "dtype %d is not KV_F16 or KV_F32", dtype);
+    if (n_new < 0) return fail(KV_ERR_ARG, "n_new must be >= 0 (got %d)", n_new);
+    if (n_new == 0) return KV_OK;
+    if (!k || !v) return fail(KV_ERR_ARG, "NULL k or v");
+    kvc::TailEditParams p;
+    p.k = t->k;
+    p.v = t->v;
+    p.len = t->len;
+    p.cap = t->capacity;
+    p.Hkv = num_kv_heads;
+    p.B = B;
+    p.dtype = dtype;
+    p.nk = k;
+    p.nv = v;
+    p.n = n_new;
+    p.seq_lens = nullptr;
+    hipError_t e = kvc::launch_tail_append(p, stream);
+    return e == hipSuccess ? KV_OK : hip_fail(e, "tail append launch");
+}
+
+int kv_tail_retire(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t B, int32_t n,
+                   int32_t *seq_lens, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_tail(t, num_kv_heads, head_dim, B);
+    if (rc) return rc;
+    if (n < 0) return fail(KV_ERR_ARG, "n must be >= 0 (got %d)", n);
+    if (n == 0) return KV_OK;
+    kvc::TailEditParams p;
+    p.k = t->k;
+    p.v = t->v;
+    p.len = t->len;
+    p.cap = t->capacity;
+    p.Hkv = num_kv_heads;
+    p.B = B;
+    p.dtype = 0;
+    p.nk = p.nv = nullptr;
+    p.n = n;
+    p.seq_lens = seq_lens;
+    hipError_t e = kvc::launch_tail_retire(p, stream);
+    return e == hipSuccess ? KV_OK : hip_fail(e, "tail retire launch");
 }
 
 size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld)

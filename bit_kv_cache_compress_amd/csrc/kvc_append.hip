@@ -376,4 +376,81 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Tail of uncompressed recent tokens (lazy updates).  One 256-thread block per sequence,
+// so that the block that moves a sequence's tokens also updates its length afterwards.
+// A row is one (token, KV head): 128 binary16 = 16 lanes x 16 bytes.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+__global__ __launch_bounds__(256) void k_tail_append(TailEditParams p)
+{
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int l0 = p.len[b];
+    const int rows = p.n * p.Hkv;
+    for (int r = tid >> 4; r < rows; r += 16) {
+        const int i = r / p.Hkv, h = r - i * p.Hkv, j = l0 + i;
+        if (j >= p.cap) continue;  // past the capacity: dropped
+        const int c = tid & 15;    // dims 8c .. 8c + 7
+        float x[8];
+        const size_t src = (((size_t)b * p.n + i) * p.Hkv + h) * kD + 8 * c;
+        const size_t dst = (((size_t)b * p.cap + j) * p.Hkv + h) * kD;
+        load8(p.nk, p.dtype, src, x);
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = float_to_half_bits(x[2 * q]) | (float_to_half_bits(x[2 * q + 1]) << 16);
+        reinterpret_cast<uint4 *>(p.k + dst)[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        load8(p.nv, p.dtype, src, x);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = float_to_half_bits(x[2 * q]) | (float_to_half_bits(x[2 * q + 1]) << 16);
+        reinterpret_cast<uint4 *>(p.v + dst)[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __syncthreads();  // every thread has read len[b]
+    if (tid == 0) p.len[b] = min(l0 + p.n, p.cap);
+}
+
+// Tokens n .. len-1 move to 0 .. len-n-1, in ascending steps of at most n tokens: a step's
+// destinations lie below its sources and below every later step's sources, and the barrier
+// between steps orders them.
+__global__ __launch_bounds__(256) void k_tail_retire(TailEditParams p)
+{
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int l0 = p.len[b];
+    const int n = min(p.n, max(l0, 0));
+    const int keep = max(l0, 0) - n;
+    const size_t row = (size_t)p.Hkv * kD / 8;  // uint4 per token
+    uint4 *k4 = reinterpret_cast<uint4 *>(p.k + (size_t)b * p.cap * p.Hkv * kD);
+    uint4 *v4 = reinterpret_cast<uint4 *>(p.v + (size_t)b * p.cap * p.Hkv * kD);
+    if (n > 0) {
+        for (int j0 = 0; j0 < keep; j0 += n) {
+            const int cnt = min(n, keep - j0);
+            for (size_t e = tid; e < (size_t)cnt * row; e += 256) {
+                const size_t d = (size_t)j0 * row + e;
+                k4[d] = k4[d + (size_t)n * row];
+                v4[d] = v4[d + (size_t)n * row];
+            }
+            __syncthreads();
+        }
+    }
+    __syncthreads();  // every thread has read len[b]
+    if (tid == 0) {
+        p.len[b] = keep;
+        if (p.seq_lens) p.seq_lens[b] += n;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_tail_append(const TailEditParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tail_append, dim3(p.B), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_tail_retire(const TailEditParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tail_retire, dim3(p.B), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace kvc

@@ -1256,6 +1256,70 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
+// Exact attention over the binary16 tail (lazy updates): one 256-thread block per (query
+// head, sequence).  A pass of 256 tail tokens: thread t scores token t (<q, k> as a binary32
+// fma chain over the 128 dims), the block takes the max and the weights exp2((s - m) log2e /
+// sqrt(D)) with a running max over passes, then thread (d, half) sums the weighted binary16
+// values of dim d over half of the pass's tokens.  Writes the partial (m, l, o[128]) that the
+// merge adds to the chunk partials (m = -inf and zeros for an empty tail).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tail_attend(TailParams p)
+{
+    __shared__ float qs[kD];
+    __shared__ float ws[256];
+    __shared__ float part[2][kD];
+    __shared__ float red[4];
+    __shared__ float bc[1];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const size_t bh = (size_t)b * p.Hq + h;
+    const int kvh = h / p.G;
+    const int n = min(max(p.len[b], 0), p.cap);
+    if (tid < kD) qs[tid] = p.q[bh * kD + tid];
+    __syncthreads();
+    const int d = tid & (kD - 1), half = tid >> 7;
+    float m = -INFINITY, l = 0.0f, o = 0.0f;
+    for (int t0 = 0; t0 < n; t0 += 256) {
+        const int t = t0 + tid;
+        float s = -INFINITY;
+        if (t < n) {
+            const uint4 *kr = reinterpret_cast<const uint4 *>(p.k + (((size_t)b * p.cap + t) * p.Hkv + kvh) * kD);
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < kD / 8; ++c) {
+                const uint4 raw = kr[c];
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    a = fmaf(qs[8 * c + e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+            }
+            s = a;
+        }
+        float mx[1] = {s};
+        block_reduce<1>(mx, red, bc, MaxF());
+        const float mnew = fmaxf(m, bc[0]);
+        const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
+        const float w = (t < n) ? exp2f((s - mnew) * p.klog) : 0.0f;
+        ws[tid] = w;
+        float sw[1] = {w};
+        block_reduce<1>(sw, red, bc, SumF());  // its barriers also publish ws
+        l = l * scale + bc[0];
+        o *= scale;
+        m = mnew;
+        const int np = min(256, n - t0);
+        for (int j = half; j < np; j += 2)
+            o = fmaf(ws[j], half_bits_to_float(p.v[(((size_t)b * p.cap + t0 + j) * p.Hkv + kvh) * kD + d]), o);
+        __syncthreads();  // ws is rewritten by the next pass
+    }
+    part[half][d] = o;
+    __syncthreads();
+    if (tid < kD) p.to[bh * kD + tid] = part[0][tid] + part[1][tid];
+    if (tid == 0) {
+        p.tm[bh] = m;
+        p.tl[bh] = l;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Split-K merge, one 1024-thread block per (query head, sequence):
 //   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
 // Thread (d, slice) sums the chunks c = slice (mod 8) for dim d.  The value sums of the
@@ -1291,9 +1355,11 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     m = wave_max(m);
     if (lane == 0) redf[0][wave] = m;
     __syncthreads();
-    float M = redf[0][0];
+    const float tm = p.tm ? p.tm[bh] : -INFINITY;  // the binary16 tail's partial, if any
+    float M = fmaxf(redf[0][0], tm);
 #pragma unroll
     for (int w = 1; w < kT / 64; ++w) M = fmaxf(M, redf[0][w]);
+    const float at = (tm == -INFINITY) ? 0.0f : exp2f((tm - M) * p.klog);
     float den = 0.0f;
     if (tid < nch) {
         const float a = (mc0 == -INFINITY) ? 0.0f : exp2f((mc0 - M) * p.klog);
@@ -1309,7 +1375,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     den = wave_sum(den);
     if (lane == 0) redf[1][wave] = den;
     __syncthreads();  // also publishes alpha
-    float D = 0.0f;
+    float D = (at != 0.0f) ? at * p.tl[bh] : 0.0f;
 #pragma unroll
     for (int w = 0; w < kT / 64; ++w) D += redf[1][w];
     float num = 0.0f;
@@ -1334,7 +1400,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     part[sl][d] = num;
     __syncthreads();
     if (tid < kD) {
-        float t = 0.0f;
+        float t = (at != 0.0f) ? at * p.to[bh * kD + d] : 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < NS; ++s2) t += part[s2][d];
         p.out[bh * kD + d] = D > 0.0f ? t / D : 0.0f;
@@ -1428,6 +1494,12 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
             break;
         }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_tail(const TailParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tail_attend, dim3(p.Hq, p.B), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -144,7 +144,19 @@ struct MergeParams {
     DecodeGeom g;
     float klog;
     const float *pm, *pl, *po;
+    const float *tm, *tl, *to;  // nullable: the tail's partial (max score, weight sum, value sums)
     float *out;            // [B*Hq][128]
+};
+
+// Exact attention over the binary16 tail: one partial (m, l, o) per (sequence, query head).
+struct TailParams {
+    int B, Hq, G, Hkv;
+    float klog;
+    const float *q;        // [B*Hq][128]
+    const uint16_t *k, *v; // [B][cap][Hkv][128] binary16
+    const int32_t *len;    // [B]
+    int cap;
+    float *tm, *tl, *to;   // [B*Hq], [B*Hq], [B*Hq][128]
 };
 
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
@@ -155,5 +167,19 @@ hipError_t launch_hist(const HistParams &p, hipStream_t s);
 hipError_t launch_select(const SelectParams &p, hipStream_t s);
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, hipStream_t s);
+hipError_t launch_tail(const TailParams &p, hipStream_t s);
+
+// Tail maintenance: append new tokens (binary16) / retire the first n tokens.
+struct TailEditParams {
+    uint16_t *k, *v;       // [B][cap][Hkv][128]
+    int32_t *len;          // [B]
+    int cap, Hkv, B;
+    int dtype;             // append: 0 f16, 1 f32
+    const void *nk, *nv;   // append: [B][n][Hkv][128]
+    int n;                 // append: n_new; retire: n
+    int32_t *seq_lens;     // retire: nullable
+};
+hipError_t launch_tail_append(const TailEditParams &p, hipStream_t s);
+hipError_t launch_tail_retire(const TailEditParams &p, hipStream_t s);
 
 }  // namespace kvc

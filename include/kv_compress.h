@@ -169,6 +169,52 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq,
                      int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Uncompressed recent tokens ([host] struct describing device arrays), for lazy updates:
+ * RaBitQCache's abstract names asynchronous pipelining and lazy updates that hide the
+ * system's overhead.  The newest tokens of each sequence stay in binary16 until a whole
+ * page of them is compressed with kv_compress_append (for instance on a second stream,
+ * while decodes go on), so a decode step appends nothing to the compressed cache.
+ *   k, v      binary16 [B][capacity][Hkv][D], 16-byte aligned: token j of sequence b's
+ *             tail at [b][j]; the layout of kv_compress_append's input, so a full page
+ *             of the tail is compressed in place (k = tail k + b * capacity * Hkv * D)
+ *   len       int32 [B]: tokens in the tail of each sequence, 0 <= len[b] <= capacity
+ *   capacity  tokens per sequence in k and v (>= 1) */
+typedef struct kv_tail {
+    uint16_t *k;
+    uint16_t *v;
+    int32_t *len;
+    int32_t capacity;
+} kv_tail;
+
+/* kv_tail_append -- write n_new new tokens per sequence into the tail (lazy update).
+ *   dtype  KV_F16 or KV_F32 (rounded to binary16, nearest even)
+ *   k, v   [B][n_new][Hkv][D] row-major, Hkv = c->num_kv_heads of the cache they belong to
+ * Token i of sequence b goes to tail position len[b] + i, then len[b] += n_new.  Device-side
+ * precondition: len[b] + n_new <= capacity (tokens past the capacity are dropped). */
+int kv_tail_append(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t dtype, const void *k,
+                   const void *v, int32_t B, int32_t n_new, hipStream_t stream);
+
+/* kv_tail_retire -- drop the first n tokens of every sequence's tail once they have been
+ * compressed into the cache (kv_compress_append on tail positions 0..n-1, which may run on
+ * another stream; the caller orders the two).  The remaining tokens move to the front,
+ * len[b] -= n, and seq_lens[b] += n when seq_lens (int32 [B], nullable) is given.
+ * Device-side precondition: len[b] >= n. */
+int kv_tail_retire(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t B, int32_t n,
+                   int32_t *seq_lens, hipStream_t stream);
+
+/* kv_decode_attend_tail -- kv_decode_attend over a compressed cache plus a binary16 tail.
+ * Defines: RaBitQCache abstract (lazy updates); H1B-KV technical framework.
+ * Sequence b's context is its seq_lens[b] compressed tokens followed by its tail->len[b]
+ * tail tokens.  The compressed tokens are handled exactly as by kv_decode_attend (all of
+ * them, or the Top-p set chosen among them; with c->keys_f16, exact scores for that set);
+ * every tail token is attended with its exact score <q, k> and its binary16 value.  One
+ * softmax spans both.  Arguments and errors as kv_decode_attend, plus a NULL or invalid
+ * tail (KV_ERR_ARG); the workspace is kv_decode_workspace_bytes(...) bytes. */
+int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
+                          const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                          int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace size for kv_decode_attend with these arguments (0 on invalid arguments). */
 size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
                                  int32_t head_dim, float top_p);

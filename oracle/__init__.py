@@ -249,6 +249,20 @@ def attend_exact(q, k16, codes, sz, D: int, Gv: int, idx) -> np.ndarray:
     return (w @ value_decode(np.asarray(codes)[idx], np.asarray(sz)[idx], D, Gv)) / w.sum()
 
 
+def attend_with_tail(s_sel, vals_sel, q, tk, tv, D: int) -> np.ndarray:
+    """One softmax over the attended compressed tokens (scores s_sel, decoded values vals_sel)
+    and the binary16 tail tokens (exact scores <q, k>, their binary16 values), in binary64:
+    the lazy updates of "RaBitQCache" (abstract) leave the newest tokens uncompressed, and a
+    decode attends them next to the cache.  No tokens at all gives zeros."""
+    s = np.concatenate([np.asarray(s_sel, dtype=np.float64).ravel(), exact_scores(q, np.asarray(tk).reshape(-1, D))])
+    if s.size == 0:
+        return np.zeros(D)
+    vals = np.concatenate([np.asarray(vals_sel, dtype=np.float64).reshape(-1, D),
+                           np.asarray(tv, dtype=np.float16).astype(np.float64).reshape(-1, D)])
+    w = np.exp((s - s.max()) / np.sqrt(D))
+    return (w @ vals) / w.sum()
+
+
 # ----------------------------------------------------------------------------------------
 # Paged cache: per (physical page, KV head) structure-of-arrays
 # ----------------------------------------------------------------------------------------
@@ -305,10 +319,34 @@ def append(cache: PagedCache, rot: Rotation, k, v, start_pos, page_table):
                 cache.key_f16[pg, h, sl] = k[b, :, h, :].astype(np.float16)
 
 
-def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy=False):
+def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy=False, tail=None):
     """One (sequence, query head) decode step.  Query head h reads KV head h*Hkv//Hq.  Under
     Top-p, a cache with binary16 keys attends the selected set with exact scores (out), and
-    the proxy-score output is kept as out_proxy; proxy=True ignores the binary16 keys."""
+    the proxy-score output is kept as out_proxy; proxy=True ignores the binary16 keys.
+    tail = (binary16 keys, binary16 values) of the uncompressed tokens that follow the L
+    compressed ones: out is then the one softmax over both (the cache-only output stays as
+    out_cache)."""
+    res = _decode_head_cache(cache, rot, q_h, b, h, Hq, L, page_table, top_p, proxy)
+    if tail is None:
+        return res
+    D, Gv = cache.D, cache.Gv
+    if L <= 0:
+        s_sel, vals_sel = np.zeros(0), np.zeros((0, D))
+    else:
+        sel = np.arange(L) if res["idx"] is None else res["idx"]
+        bits, nc, codes, sz = cache.gather(b, res["kvh"], L, page_table)
+        if cache.key_f16 is not None and top_p < 1.0 and not proxy:
+            pg, sl = cache.locate(b, np.arange(L), page_table)
+            s_sel = exact_scores(q_h, cache.key_f16[pg, res["kvh"], sl][sel])
+        else:
+            s_sel = res["score"][sel]
+        vals_sel = value_decode(codes[sel], sz[sel], D, Gv)
+    res["out_cache"] = res["out"]
+    res["out"] = attend_with_tail(s_sel, vals_sel, q_h, tail[0], tail[1], D)
+    return res
+
+
+def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy):
     D, Gv = cache.D, cache.Gv
     kvh = h * cache.Hkv // Hq
     qe = query_encode(rot, q_h)
@@ -335,12 +373,20 @@ def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, 
     return res
 
 
-def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None, proxy=False):
+def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None, proxy=False,
+           tail=None):
     """Decode step for q (B, Hq, D).  Returns {(b, h): decode_head(...)} for the requested
-    (b, h) pairs (all by default)."""
+    (b, h) pairs (all by default).  tail = (tail_k, tail_v, tail_len): binary16 [B][cap][Hkv][D]
+    keys and values and int [B] lengths of the uncompressed tokens after seq_lens[b]."""
     q = np.asarray(q, dtype=np.float32)
     B, Hq, D = q.shape
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Hq)]
-    return {(b, h): decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy)
-            for (b, h) in heads}
+    out = {}
+    for (b, h) in heads:
+        th = None
+        if tail is not None:
+            n, kvh = int(tail[2][b]), h * cache.Hkv // Hq
+            th = (np.asarray(tail[0])[b, :n, kvh], np.asarray(tail[1])[b, :n, kvh])
+        out[(b, h)] = decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy, th)
+    return out

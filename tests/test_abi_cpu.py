@@ -120,3 +120,26 @@ def test_append_argument_errors():
     # zero new tokens is a no-op
     assert lib.kv_compress_append(ctypes.byref(d), 0, None, None, 1, 0, None, None, 1, None) == L.KV_OK
     assert lib.kv_compress_append(None, 0, FAKE, FAKE, 1, 4, FAKE, FAKE, 1, None) == L.KV_ERR_ARG
+
+
+def _decode_tail(tail, desc=None, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p=1.0):
+    desc = desc or _desc()
+    ws = L.lib().kv_decode_workspace_bytes(B, Hq, desc.num_kv_heads, max_seq_len, 128, top_p)
+    return L.lib().kv_decode_attend_tail(ctypes.byref(desc), ctypes.byref(tail) if tail is not None else None,
+                                         FAKE, B, Hq, FAKE, max_seq_len, FAKE, max_pages, top_p, FAKE, None, FAKE,
+                                         ws, None)
+
+
+@pytest.mark.parametrize("kw", [dict(k=None), dict(v=None), dict(len=None), dict(capacity=0),
+                                dict(k=0x10008)])
+def test_bad_tail_descriptor(kw):
+    d = dict(k=0x10000, v=0x10000, len=0x10000, capacity=256)
+    d.update(kw)
+    tail = L.KVTailDesc(*[d[f] for f, _ in L.KVTailDesc._fields_])
+    assert _decode_tail(tail) == L.KV_ERR_ARG
+    assert L.last_error()
+
+
+def test_null_tail_descriptor():
+    assert _decode_tail(None) == L.KV_ERR_ARG
+

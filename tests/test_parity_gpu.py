@@ -186,6 +186,151 @@ def test_exact_keys(name):
     _say(f"[exact] {name} ok, worst rel err {worst:.2e}")
 
 
+@pytest.mark.parametrize("name", ["c2-outliers-ragged", "c3-gqa4-spikes-topp", "c4-paged-g64-ragged",
+                                  "c5-hadamard-topp"])
+def test_tail(name):
+    """The compressed cache plus a binary16 tail of uncompressed recent tokens (lazy updates):
+    tail lengths 0, 1, 100 and a whole 256-token page, one softmax over both, at the case's
+    Top-p and with full softmax, against the oracle."""
+    import oracle
+    from bit_kv_cache_compress_amd import Tail, decode_attend
+
+    c = _case(name)
+    dev = torch.device("cuda")
+    B, Hkv, D, cap = c.wl.B, c.wl.Hkv, c.wl.D, 256
+    ntail = np.minimum(np.array([[0, 1, 100, 256][b % 4] for b in range(B)], np.int32), c.lens)
+    lc = (c.lens - ntail).astype(np.int32)
+    tk = np.zeros((B, cap, Hkv, D), np.float16)
+    tv = np.zeros_like(tk)
+    for b in range(B):
+        tk[b, :ntail[b]] = c.K[b, lc[b]:lc[b] + ntail[b]].astype(np.float16)
+        tv[b, :ntail[b]] = c.V[b, lc[b]:lc[b] + ntail[b]].astype(np.float16)
+    tail = Tail(B, cap, Hkv, dev)
+    tail.k.copy_(torch.from_numpy(tk))
+    tail.v.copy_(torch.from_numpy(tv))
+    tail.len.copy_(torch.from_numpy(ntail))
+    g = upload(c.ocache, c)
+    q = torch.from_numpy(c.q).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    lcd = torch.from_numpy(lc).to(dev)
+    for top_p in sorted({c.wl.top_p, 1.0}):
+        _say(f"[tail] {name} top_p={top_p} tails {ntail.tolist()}")
+        out = decode_attend(g, q, lcd, pt, top_p=top_p, max_seq_len=c.max_len, tail=tail)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        ref = oracle.decode(c.ocache, c.orot, c.q, lc, c.pt, top_p, tail=(tk, tv, ntail))
+        worst = 0.0
+        for (b, h), r in ref.items():
+            if lc[b] + ntail[b] == 0:
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (top_p, b, h, e)
+        _say(f"[tail] {name} top_p={top_p} ok, worst rel err {worst:.2e}")
+
+
+def test_tail_append_and_retire():
+    """Tail maintenance: appended tokens are the binary16 roundings of the input (float32 and
+    float16), past-capacity tokens are dropped, and retiring moves the rest to the front
+    (including moves whose source and destination ranges overlap) and advances seq_lens."""
+    from bit_kv_cache_compress_amd import Tail
+
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(7)
+    B, Hkv, D, cap = 3, 2, 128, 40
+    tail = Tail(B, cap, Hkv, dev)
+    want_k = np.zeros((B, cap, Hkv, D), np.float16)
+    want_v = np.zeros_like(want_k)
+    lens = np.zeros(B, np.int64)
+    for n, dt in [(5, np.float32), (1, np.float16), (30, np.float32), (7, np.float16)]:
+        k = (3 * rng.standard_normal((B, n, Hkv, D))).astype(dt)
+        v = rng.standard_normal((B, n, Hkv, D)).astype(dt)
+        tail.append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev))
+        for b in range(B):
+            m = min(n, cap - lens[b])
+            want_k[b, lens[b]:lens[b] + m] = k[b, :m].astype(np.float16)
+            want_v[b, lens[b]:lens[b] + m] = v[b, :m].astype(np.float16)
+            lens[b] += m
+    torch.cuda.synchronize()
+    assert tail.len.cpu().numpy().tolist() == lens.tolist() == [cap] * B
+    np.testing.assert_array_equal(tail.k.cpu().numpy().view(np.uint16), want_k.view(np.uint16))
+    np.testing.assert_array_equal(tail.v.cpu().numpy().view(np.uint16), want_v.view(np.uint16))
+    seq = torch.tensor([100, 0, 7], dtype=torch.int32, device=dev)
+    for n in (3, 16):  # 37 kept after 3 (overlapping move), then 21 after 16
+        tail.retire(n, seq)
+        torch.cuda.synchronize()
+        want_k = np.concatenate([want_k[:, n:], np.zeros_like(want_k[:, :n])], axis=1)
+        want_v = np.concatenate([want_v[:, n:], np.zeros_like(want_v[:, :n])], axis=1)
+        lens -= n
+        assert tail.len.cpu().numpy().tolist() == lens.tolist()
+        got_k, got_v = tail.k.cpu().numpy(), tail.v.cpu().numpy()
+        for b in range(B):
+            np.testing.assert_array_equal(got_k[b, :lens[b]].view(np.uint16), want_k[b, :lens[b]].view(np.uint16))
+            np.testing.assert_array_equal(got_v[b, :lens[b]].view(np.uint16), want_v[b, :lens[b]].view(np.uint16))
+    assert seq.cpu().numpy().tolist() == [119, 19, 26]
+
+
+def test_lazy_pipeline():
+    """Lazy updates end to end: tokens go to the binary16 tail one step at a time, a whole page
+    of the tail is compressed on a second stream while decodes go on, then retired; every
+    step's output (cache plus tail) against the oracle holding the same state."""
+    import oracle
+    from bit_kv_cache_compress_amd import Tail, append, decode_attend
+
+    c = _case("c3-gqa4-spikes-topp")  # binary16 inputs: the tail keeps them exactly
+    dev = torch.device("cuda")
+    B, Hkv, D, P = c.wl.B, c.wl.Hkv, c.wl.D, c.wl.P
+    L0 = 2 * P + 5                     # compressed at the start
+    steps = P + 9                      # one page fills and is compressed on the way
+    assert L0 + steps <= c.L
+    ocache = oracle.PagedCache(c.npages, Hkv, P, D, c.wl.Gv)
+    oracle.append(ocache, c.orot, c.K[:, :L0], c.V[:, :L0], np.zeros(B, np.int32), c.pt)
+    g = upload(ocache, c)
+    tail = Tail(B, 2 * P, Hkv, dev)
+    seq = torch.full((B,), L0, dtype=torch.int32, device=dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    q = torch.from_numpy(c.q).to(dev)
+    side = torch.cuda.Stream()
+    lc, nt, pending = L0, 0, None
+    for s in range(steps):
+        t = L0 + s
+        tail.append(torch.from_numpy(np.ascontiguousarray(c.K[:, t:t + 1])).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(c.V[:, t:t + 1])).to(dev))
+        nt += 1
+        if nt == P + 1 and pending is None:
+            # the tail's first page (positions lc .. lc+P-1) is compressed on the side stream
+            ev = torch.cuda.Event()
+            ev.record()
+            side.wait_event(ev)
+            with torch.cuda.stream(side):
+                for b in range(B):
+                    kb, vb = tail.page(b, 0, P)
+                    append(g, kb, vb, torch.tensor([lc], dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+                done = torch.cuda.Event()
+                done.record()
+            pending = (done, s + 4)
+        if pending is not None and s == pending[1]:
+            torch.cuda.current_stream().wait_event(pending[0])
+            tail.retire(P, seq)
+            oracle.append(ocache, c.orot, c.K[:, lc:lc + P], c.V[:, lc:lc + P], np.full(B, lc, np.int32), c.pt)
+            lc, nt, pending = lc + P, nt - P, None
+        out = decode_attend(g, q, seq, pt, top_p=c.wl.top_p, max_seq_len=c.L, tail=tail)
+        if s % 40 == 0 or s == steps - 1:
+            torch.cuda.synchronize()
+            tk = np.zeros((B, 2 * P, Hkv, D), np.float16)
+            tv = np.zeros_like(tk)
+            tk[:, :nt] = c.K[:, lc:lc + nt].astype(np.float16)
+            tv[:, :nt] = c.V[:, lc:lc + nt].astype(np.float16)
+            ref = oracle.decode(ocache, c.orot, c.q, np.full(B, lc, np.int32), c.pt, c.wl.top_p,
+                                tail=(tk, tv, np.full(B, nt, np.int32)))
+            o = out.cpu().numpy()
+            for (b, h), r in ref.items():
+                assert rel_err(o[b, h], r["out"]) <= TOL, (s, b, h)
+            _say(f"[lazy] step {s}: {lc} compressed + {nt} tail tokens ok")
+    assert lc == L0 + P and int(seq[0]) == lc
+
+
 def test_topp_sweep():
     """Top-p from 0.3 to 0.999 on one cache (from a few dozen to almost every token of a
     1024-token attention chunk kept): sets and outputs against the oracle."""
