@@ -45,10 +45,13 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index 0..4 (default 2: GQA 128k Top-p)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--lazy", action="store_true",
+                    help="lazy updates: new tokens go to a binary16 tail, whole pages are compressed on a "
+                         "second stream; times one page cycle (steps default to the page size)")
     ap.add_argument("--exact-keys", action="store_true",
                     help="also keep binary16 keys; Top-p attends the selected tokens with exact scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,7 +61,126 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (a known-size kernel that "
                          "calibrates the FETCH_SIZE/WRITE_SIZE counters), no JSON")
-    return ap.parse_args()
+    a = ap.parse_args()
+    a.steps_given = a.steps is not None
+    if a.steps is None:
+        a.steps = 50
+    return a
+
+
+def run_lazy(args):
+    """Decode steps with lazy updates: each step writes the new token of every sequence into
+    the binary16 tail and decodes over cache plus tail; when a tail holds more than a page, its
+    first page is compressed into the cache on a second stream and retired 4 steps later.
+    The timed region is one page cycle (page_size steps, one compression per sequence)."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_compress_amd as kvc
+    import workloads as W
+
+    wl = W.CONFIGS[args.config]
+    if wl.len_range is not None:
+        raise SystemExit("--lazy needs a workload with equal sequence lengths")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    D, Hq, Hkv, B, P, Gv, L = wl.D, wl.Hq, wl.Hkv, wl.B, wl.P, wl.Gv, wl.L
+    steps = args.steps if args.steps_given else P
+    total = args.warmup + steps
+    # compressed tokens before the first step: whole pages, the rest (1 .. P tokens) in the tail;
+    # the tail then passes P tokens at steps 0, P, 2P, ... so every window of P steps after the
+    # first compresses one page per sequence
+    Lc0 = (L - 1) // P * P
+    T0 = L - Lc0
+    log(f"[bench] lazy updates on {wl.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} top_p={wl.top_p}; "
+        f"{Lc0} compressed + {T0} tail tokens, {total} steps of one token")
+    K, V, q = W.draw_device(wl, dev, L=L)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed(99))
+    kvt = torch.float16 if wl.kv_dtype == "f16" else torch.float32
+    KN = torch.randn((total, B, 1, Hkv, D), generator=g, device=dev).to(kvt)
+    VN = torch.randn((total, B, 1, Hkv, D), generator=g, device=dev).to(kvt)
+    pt_np, npages = W.page_layout(wl, np.full(B, L, np.int32), reserve=total + P)
+    kind, rot = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, Hkv, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    pt = torch.from_numpy(pt_np).to(dev)
+    kvc.append(cache, K[:, :Lc0].to(kvt).contiguous(), V[:, :Lc0].to(kvt).contiguous(),
+               torch.zeros(B, dtype=torch.int32, device=dev), pt)
+    tail = kvc.Tail(B, 2 * P, Hkv, dev)
+    tail.append(K[:, Lc0:].to(kvt).contiguous(), V[:, Lc0:].to(kvt).contiguous())
+    del K, V
+    seq = torch.full((B,), Lc0, dtype=torch.int32, device=dev)
+    Lmax = L + total
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvc.decode_workspace_bytes(B, Hq, Hkv, Lmax, wl.top_p), dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    st = dict(lc=Lc0, nt=T0, pending=None, compressions=0)
+    starts = [torch.tensor([0], dtype=torch.int32, device=dev) for _ in range(B)]
+    pts = [pt[b:b + 1].contiguous() for b in range(B)]
+
+    def step(i):
+        tail.append(KN[i], VN[i])
+        st["nt"] += 1
+        if st["nt"] == P + 1 and st["pending"] is None:
+            ev = torch.cuda.Event()
+            ev.record()
+            side.wait_event(ev)
+            with torch.cuda.stream(side):
+                for b in range(B):
+                    starts[b].fill_(st["lc"])
+                    kb, vb = tail.page(b, 0, P)
+                    kvc.append(cache, kb, vb, starts[b], pts[b])
+                done = torch.cuda.Event()
+                done.record()
+            st["pending"] = (done, i + 4)
+            st["compressions"] += 1
+        if st["pending"] is not None and i == st["pending"][1]:
+            torch.cuda.current_stream().wait_event(st["pending"][0])
+            tail.retire(P, seq)
+            st["lc"] += P
+            st["nt"] -= P
+            st["pending"] = None
+        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=st["lc"], out=out, workspace=ws, tail=tail)
+
+    for i in range(args.warmup):
+        flush_buf.sum()
+        step(i)
+    torch.cuda.synchronize()
+    c0 = st["compressions"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    toks = []
+    wall0 = time.perf_counter()
+    for j in range(steps):
+        flush_buf.sum()
+        ev[j][0].record()
+        step(args.warmup + j)
+        ev[j][1].record()
+        toks.append(st["lc"] + st["nt"])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = statistics.mean(step_ms)
+    value = statistics.mean(t * B * Hkv for t in toks) / (ms / 1e3)
+    log(f"[bench] lazy step {ms * 1e3:.1f} us (median {statistics.median(step_ms) * 1e3:.1f}, "
+        f"max {max(step_ms) * 1e3:.1f}); {value:.3e} KV token-heads/s; "
+        f"{st['compressions'] - c0} page compressions on the second stream")
+    result = {
+        "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i32 (1-bit x int4 popcount) + f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": L,
+                   "head_dim": D, "top_p": wl.top_p, "value_group": Gv, "page_size": P, "rotation": wl.rot,
+                   "kv_dtype": wl.kv_dtype, "lazy": True, "tail_tokens_at_start": T0,
+                   "step": "append 1 token per sequence to the binary16 tail + decode over cache and tail; "
+                           "a full page compressed on a second stream",
+                   "cache_flushed_between_steps": True},
+        "roofline": None, "cpu_baseline": None,
+        "page_compressions_timed": st["compressions"] - c0,
+        "step_us_median": round(statistics.median(step_ms) * 1e3, 2),
+        "wall_ms_per_step_incl_flush": round(wall / steps * 1e3, 3),
+    }
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -80,6 +202,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copied {args.copy_calibration} MiB five times")
         return
+
+    if args.lazy:
+        return run_lazy(args)
 
     import bit_kv_cache_compress_amd as kvc
     import workloads as W

@@ -311,6 +311,23 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *q, int32_t 
     qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
+    qp.has_tail = tail != nullptr;
+    if (tail) {
+        kvc::TailParams &tp = qp.tail;
+        tp.B = B;
+        tp.Hq = Hq;
+        tp.G = Hq / c->num_kv_heads;
+        tp.Hkv = c->num_kv_heads;
+        tp.klog = klog;
+        tp.q = q;
+        tp.k = tail->k;
+        tp.v = tail->v;
+        tp.len = tail->len;
+        tp.cap = tail->capacity;
+        tp.tm = at<float>(workspace, pl.off_tm);
+        tp.tl = at<float>(workspace, pl.off_tl);
+        tp.to = at<float>(workspace, pl.off_to);
+    }
     stage_mark(dbg, KV_STAGE_QUERY, true, stream);
     hipError_t e = kvc::launch_qprep(qp, stream);
     if (e != hipSuccess) return hip_fail(e, "query launch");
@@ -397,27 +414,9 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *q, int32_t 
     mp.tm = mp.tl = mp.to = nullptr;
     mp.out = out;
     if (tail) {
-        kvc::TailParams tp;
-        tp.B = B;
-        tp.Hq = Hq;
-        tp.G = Hq / c->num_kv_heads;
-        tp.Hkv = c->num_kv_heads;
-        tp.klog = klog;
-        tp.q = q;
-        tp.k = tail->k;
-        tp.v = tail->v;
-        tp.len = tail->len;
-        tp.cap = tail->capacity;
-        tp.tm = at<float>(workspace, pl.off_tm);
-        tp.tl = at<float>(workspace, pl.off_tl);
-        tp.to = at<float>(workspace, pl.off_to);
-        stage_mark(dbg, KV_STAGE_ATTEND, true, stream);
-        e = kvc::launch_tail(tp, stream);
-        if (e != hipSuccess) return hip_fail(e, "tail attention launch");
-        stage_mark(dbg, KV_STAGE_ATTEND, false, stream);
-        mp.tm = tp.tm;
-        mp.tl = tp.tl;
-        mp.to = tp.to;
+        mp.tm = qp.tail.tm;
+        mp.tl = qp.tail.tl;
+        mp.to = qp.tail.to;
     }
     stage_mark(dbg, KV_STAGE_MERGE, true, stream);
     e = kvc::launch_merge(mp, stream);

@@ -69,7 +69,99 @@ struct SumF { __device__ float operator()(float a, float b) const { return a + b
 struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 
 // ---------------------------------------------------------------------------------------
-// Query preparation (one 128-thread block per (sequence, query head), one thread per dim):
+// Exact attention over the binary16 tail (lazy updates) for query head h of sequence b, by
+// a 128-thread block.  A pass covers 128 tail tokens: thread t scores token t (<q, k> as a
+// binary32 fma chain over the 128 dims) while thread (dg, ts) = (t mod 16, t / 16) already
+// holds the values of dims 8 dg .. 8 dg + 7 of tokens ts + 8 i, i < 16, so that every load
+// of the pass is in flight at once.  The block takes the max and the weights
+// exp2((s - m) log2e / sqrt(D)) with a running max over passes; thread (dg, ts) sums its 16
+// weighted values, and the 8 token slices are added at the end.  Writes the partial
+// (m, l, o[128]) that the merge adds to the chunk partials (m = -inf and zeros for an
+// empty tail).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
+{
+    constexpr int T = 128, NS = T / 16, NV = T / NS;  // tokens per pass, token slices, values per thread
+    __shared__ float qs[kD];
+    __shared__ float ws[T];
+    __shared__ float part[NS][kD];
+    __shared__ float red[2][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = bh / p.Hq, h = bh - b * p.Hq, kvh = h / p.G;
+    const int n = min(max(p.len[b], 0), p.cap);
+    qs[tid] = p.q[(size_t)bh * kD + tid];
+    const int dg = tid & 15, ts = tid >> 4;
+    const size_t row = (size_t)p.Hkv * kD;  // binary16 elements from one token to the next
+    const uint16_t *kb = p.k + ((size_t)b * p.cap * p.Hkv + kvh) * kD;
+    const uint16_t *vb = p.v + ((size_t)b * p.cap * p.Hkv + kvh) * kD + 8 * dg;
+    float m = -INFINITY, l = 0.0f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+    __syncthreads();
+    for (int t0 = 0; t0 < n; t0 += T) {
+        uint4 vr[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int t = t0 + ts + NS * i;
+            vr[i] = t < n ? *reinterpret_cast<const uint4 *>(vb + t * row) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const int t = t0 + tid;
+        float s = -INFINITY;
+        if (t < n) {
+            const uint4 *kr = reinterpret_cast<const uint4 *>(kb + t * row);
+            uint4 kk[kD / 8];
+#pragma unroll
+            for (int c = 0; c < kD / 8; ++c) kk[c] = kr[c];
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < kD / 8; ++c) {
+                const uint32_t w[4] = {kk[c].x, kk[c].y, kk[c].z, kk[c].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    a = fmaf(qs[8 * c + e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+            }
+            s = a;
+        }
+        const float wm = wave_max(s);
+        if (lane == 0) red[0][wave] = wm;
+        __syncthreads();
+        const float mnew = fmaxf(m, fmaxf(red[0][0], red[0][1]));
+        const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
+        const float w = (t < n) ? exp2f((s - mnew) * p.klog) : 0.0f;
+        ws[tid] = w;
+        const float wsum = wave_sum(w);
+        if (lane == 0) red[1][wave] = wsum;
+        __syncthreads();
+        l = l * scale + (red[1][0] + red[1][1]);
+        m = mnew;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= scale;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float wi = ws[ts + NS * i];
+            const uint32_t x[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e] = fmaf(wi, half_bits_to_float((x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), o[e]);
+        }
+        __syncthreads();  // ws and red are rewritten by the next pass
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[ts][8 * dg + e] = o[e];
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc += part[j][tid];
+    p.to[(size_t)bh * kD + tid] = acc;
+    if (tid == 0) {
+        p.tm[bh] = m;
+        p.tl[bh] = l;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Query preparation (one 128-thread block per (sequence, query head), one thread per dim;
+// with a tail, blocks BH .. 2 BH - 1 run the tail attention of the same heads alongside):
 //   dense:    q'_r = fmaf chain over j ascending of R[r][j] * q_j (binary32)
 //   hadamard: x = sigma * q, in-place fast Walsh-Hadamard butterflies h = 1..64 (binary32),
 //             q' = x * fp32(1/sqrt(D))
@@ -82,6 +174,10 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
     __shared__ int us[kD];
     __shared__ float redf[4];
     __shared__ int redi[2];
+    if ((int)blockIdx.x >= p.BH) {
+        tail_attend(p.tail, (int)blockIdx.x - p.BH);
+        return;
+    }
     const int bh = blockIdx.x, r = threadIdx.x;
     const int lane = r & 63, wave = r >> 6;
     const float *q = p.q + (size_t)bh * kD;
@@ -1256,70 +1352,6 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Exact attention over the binary16 tail (lazy updates): one 256-thread block per (query
-// head, sequence).  A pass of 256 tail tokens: thread t scores token t (<q, k> as a binary32
-// fma chain over the 128 dims), the block takes the max and the weights exp2((s - m) log2e /
-// sqrt(D)) with a running max over passes, then thread (d, half) sums the weighted binary16
-// values of dim d over half of the pass's tokens.  Writes the partial (m, l, o[128]) that the
-// merge adds to the chunk partials (m = -inf and zeros for an empty tail).
-// ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_tail_attend(TailParams p)
-{
-    __shared__ float qs[kD];
-    __shared__ float ws[256];
-    __shared__ float part[2][kD];
-    __shared__ float red[4];
-    __shared__ float bc[1];
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const size_t bh = (size_t)b * p.Hq + h;
-    const int kvh = h / p.G;
-    const int n = min(max(p.len[b], 0), p.cap);
-    if (tid < kD) qs[tid] = p.q[bh * kD + tid];
-    __syncthreads();
-    const int d = tid & (kD - 1), half = tid >> 7;
-    float m = -INFINITY, l = 0.0f, o = 0.0f;
-    for (int t0 = 0; t0 < n; t0 += 256) {
-        const int t = t0 + tid;
-        float s = -INFINITY;
-        if (t < n) {
-            const uint4 *kr = reinterpret_cast<const uint4 *>(p.k + (((size_t)b * p.cap + t) * p.Hkv + kvh) * kD);
-            float a = 0.0f;
-#pragma unroll
-            for (int c = 0; c < kD / 8; ++c) {
-                const uint4 raw = kr[c];
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    a = fmaf(qs[8 * c + e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
-            }
-            s = a;
-        }
-        float mx[1] = {s};
-        block_reduce<1>(mx, red, bc, MaxF());
-        const float mnew = fmaxf(m, bc[0]);
-        const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
-        const float w = (t < n) ? exp2f((s - mnew) * p.klog) : 0.0f;
-        ws[tid] = w;
-        float sw[1] = {w};
-        block_reduce<1>(sw, red, bc, SumF());  // its barriers also publish ws
-        l = l * scale + bc[0];
-        o *= scale;
-        m = mnew;
-        const int np = min(256, n - t0);
-        for (int j = half; j < np; j += 2)
-            o = fmaf(ws[j], half_bits_to_float(p.v[(((size_t)b * p.cap + t0 + j) * p.Hkv + kvh) * kD + d]), o);
-        __syncthreads();  // ws is rewritten by the next pass
-    }
-    part[half][d] = o;
-    __syncthreads();
-    if (tid < kD) p.to[bh * kD + tid] = part[0][tid] + part[1][tid];
-    if (tid == 0) {
-        p.tm[bh] = m;
-        p.tl[bh] = l;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
 // Split-K merge, one 1024-thread block per (query head, sequence):
 //   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
 // Thread (d, slice) sums the chunks c = slice (mod 8) for dim d.  The value sums of the
@@ -1415,7 +1447,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
 {
     const float isd = (float)(1.0 / sqrt((double)kD));
-    hipLaunchKernelGGL(k_qprep, dim3(p.BH), dim3(128), 0, s, p, isd);
+    hipLaunchKernelGGL(k_qprep, dim3(p.has_tail ? 2 * p.BH : p.BH), dim3(128), 0, s, p, isd);
     return hipGetLastError();
 }
 
@@ -1494,12 +1526,6 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
             break;
         }
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_tail(const TailParams &p, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_tail_attend, dim3(p.Hq, p.B), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -46,6 +46,18 @@ struct AppendParams {
     int max_pages;
 };
 
+// Attention over the binary16 tail of recent tokens: per query head, the running max m,
+// weight sum l and weighted value sum o of its tail tokens.
+struct TailParams {
+    int B, Hq, G, Hkv;
+    float klog;
+    const float *q;        // [B*Hq][128]
+    const uint16_t *k, *v; // [B][cap][Hkv][128] binary16
+    const int32_t *len;    // [B]
+    int cap;
+    float *tm, *tl, *to;   // [B*Hq], [B*Hq], [B*Hq][128]
+};
+
 // Query preparation: rotate, quantize, bit-planes.
 struct QprepParams {
     int rot_kind;
@@ -58,6 +70,8 @@ struct QprepParams {
     uint8_t *dbg_codes;    // nullable [B*Hq][128]
     float *dbg_params;     // nullable [B*Hq][4]
     int32_t *dbg_sumu;     // nullable [B*Hq]
+    int has_tail;          // blocks BH .. 2 BH - 1 attend over the binary16 tail
+    TailParams tail;
 };
 
 // Chunked decode geometry shared by the decode kernels.
@@ -149,15 +163,6 @@ struct MergeParams {
 };
 
 // Exact attention over the binary16 tail: one partial (m, l, o) per (sequence, query head).
-struct TailParams {
-    int B, Hq, G, Hkv;
-    float klog;
-    const float *q;        // [B*Hq][128]
-    const uint16_t *k, *v; // [B][cap][Hkv][128] binary16
-    const int32_t *len;    // [B]
-    int cap;
-    float *tm, *tl, *to;   // [B*Hq], [B*Hq], [B*Hq][128]
-};
 
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 hipError_t launch_qprep(const QprepParams &p, hipStream_t s);
@@ -167,7 +172,6 @@ hipError_t launch_hist(const HistParams &p, hipStream_t s);
 hipError_t launch_select(const SelectParams &p, hipStream_t s);
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s);
 hipError_t launch_merge(const MergeParams &p, hipStream_t s);
-hipError_t launch_tail(const TailParams &p, hipStream_t s);
 
 // Tail maintenance: append new tokens (binary16) / retire the first n tokens.
 struct TailEditParams {
