@@ -15,7 +15,8 @@ KV_OK, KV_ERR_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP = 0, -1, -2,
 KV_ROT_DENSE, KV_ROT_HADAMARD = 0, 1
 KV_F16, KV_F32 = 0, 1
 
-EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_tail", "kv_decode_workspace_bytes",
+EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_ex", "kv_decode_attend_tail",
+           "kv_decode_workspace_bytes",
            "kv_tail_append", "kv_tail_retire", "kv_topp_select", "kv_topp_workspace_bytes", "kv_last_error",
            "kv_version")
 
@@ -32,6 +33,7 @@ class KVCacheDesc(ctypes.Structure):
         ("keys", ctypes.c_void_p),
         ("vals", ctypes.c_void_p),
         ("keys_f16", ctypes.c_void_p),
+        ("key_center", ctypes.c_void_p),
     ]
 
 
@@ -55,6 +57,13 @@ class KVTailDesc(ctypes.Structure):
         ("v", ctypes.c_void_p),
         ("len", ctypes.c_void_p),
         ("capacity", ctypes.c_int32),
+    ]
+
+
+class KVDecodeOpts(ctypes.Structure):
+    _fields_ = [
+        ("tail", ctypes.POINTER(KVTailDesc)),
+        ("q_dither", ctypes.c_void_p),
     ]
 
 
@@ -92,6 +101,9 @@ def lib():
     L.kv_decode_attend_tail.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVTailDesc), P, i32, i32, P, i32,
                                         P, i32, f32, P, ctypes.POINTER(KVDebug), P, sz, P]
     L.kv_decode_attend_tail.restype = ctypes.c_int
+    L.kv_decode_attend_ex.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVDecodeOpts), P, i32, i32, P, i32,
+                                      P, i32, f32, P, ctypes.POINTER(KVDebug), P, sz, P]
+    L.kv_decode_attend_ex.restype = ctypes.c_int
     L.kv_tail_append.argtypes = [ctypes.POINTER(KVTailDesc), i32, i32, i32, P, P, i32, i32, P]
     L.kv_tail_append.restype = ctypes.c_int
     L.kv_tail_retire.argtypes = [ctypes.POINTER(KVTailDesc), i32, i32, i32, i32, P, P]

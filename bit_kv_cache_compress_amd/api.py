@@ -52,10 +52,15 @@ class KVCache:
     ``exact_keys``: also keep the keys in binary16 (``keys_f16`` [..., 128]); appends fill
     it, and a Top-p decode then scores the selected tokens exactly with it.  ``proxy_desc``
     is the descriptor without it (proxy scores throughout).
+
+    ``key_center``: optional float32 [Hkv, 128] per-head key centers (kept on the device as
+    ``key_center``).  Appends encode k - c_h instead of k; the proxy scores then estimate
+    <q, k - c_h>, a per-head shift that the softmax ignores (tails are moved to that frame).
     """
 
     def __init__(self, num_pages: int, num_kv_heads: int, rotation, rot_kind: str = "dense",
-                 page_size: int = 256, value_group: int = 32, device="cuda", exact_keys: bool = False):
+                 page_size: int = 256, value_group: int = 32, device="cuda", exact_keys: bool = False,
+                 key_center=None):
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:
             device = torch.device("cuda", torch.cuda.current_device())
@@ -80,12 +85,19 @@ class KVCache:
         self.keys = torch.zeros(shp + (D // 32 + 1,), dtype=torch.int32, device=device)
         self.vals = torch.zeros(shp + (D // 2 + 4 * (D // self.value_group),), dtype=torch.uint8, device=device)
         self.keys_f16 = torch.zeros(shp + (D,), dtype=torch.float16, device=device) if exact_keys else None
+        self.key_center = None
+        if key_center is not None:
+            kc = torch.as_tensor(key_center)
+            if kc.dtype != torch.float32 or tuple(kc.shape) != (self.num_kv_heads, D):
+                raise ValueError(f"key_center must be a float32 [{self.num_kv_heads}, {D}] array")
+            self.key_center = kc.to(device).contiguous()
+        kcp = self.key_center.data_ptr() if self.key_center is not None else None
         self.desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
                                   self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(), self.vals.data_ptr(),
-                                  self.keys_f16.data_ptr() if exact_keys else None)
+                                  self.keys_f16.data_ptr() if exact_keys else None, kcp)
         self.proxy_desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
                                         self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(),
-                                        self.vals.data_ptr(), None)
+                                        self.vals.data_ptr(), None, kcp)
 
     @property
     def key_bits(self) -> torch.Tensor:
@@ -217,10 +229,12 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
                   top_p: float = 1.0, max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
                   debug_struct: Optional[L.KVDebug] = None, proxy: bool = False,
-                  tail: Optional["Tail"] = None) -> torch.Tensor:
+                  tail: Optional["Tail"] = None, q_dither: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32.  Under Top-p, a
     cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set.
-    With ``tail``, each sequence's binary16 tail tokens follow its seq_lens compressed ones."""
+    With ``tail``, each sequence's binary16 tail tokens follow its seq_lens compressed ones.
+    ``q_dither`` (float32 [B, Hq, 128], uniforms in [0, 1)): stochastic rounding of the int4
+    query codes, floor(t + U) instead of rint(t)."""
     dev = cache.device
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
@@ -244,13 +258,19 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
         debug_struct = debug.struct()
     dbg = ctypes.byref(debug_struct) if debug_struct is not None else None
     desc = cache.proxy_desc if proxy else cache.desc
-    if tail is None:
+    if tail is not None and (tail.k.shape[0] != B or tail.k.shape[2] != cache.num_kv_heads):
+        raise ValueError(f"tail must be [{B}, capacity, {cache.num_kv_heads}, {HEAD_DIM}]")
+    if q_dither is not None:
+        _need(q_dither, "q_dither", torch.float32, dev, (B, Hq, HEAD_DIM))
+        opts = L.KVDecodeOpts(ctypes.pointer(tail.desc) if tail is not None else None, _ptr(q_dither))
+        L.check(L.lib().kv_decode_attend_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), B, Hq, _ptr(seq_lens),
+                                            int(max_seq_len), _ptr(page_table), max_pages, float(top_p), _ptr(out),
+                                            dbg, _ptr(workspace), workspace.numel(), _stream(dev)))
+    elif tail is None:
         L.check(L.lib().kv_decode_attend(ctypes.byref(desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
                                          _ptr(page_table), max_pages, float(top_p), _ptr(out), dbg,
                                          _ptr(workspace), workspace.numel(), _stream(dev)))
     else:
-        if tail.k.shape[0] != B or tail.k.shape[2] != cache.num_kv_heads:
-            raise ValueError(f"tail must be [{B}, capacity, {cache.num_kv_heads}, {HEAD_DIM}]")
         L.check(L.lib().kv_decode_attend_tail(ctypes.byref(desc), ctypes.byref(tail.desc), _ptr(q), B, Hq,
                                               _ptr(seq_lens), int(max_seq_len), _ptr(page_table), max_pages,
                                               float(top_p), _ptr(out), dbg, _ptr(workspace), workspace.numel(),

@@ -179,6 +179,8 @@ int check_cache(const kv_cache *c)
         return fail(KV_ERR_ARG, "cache descriptor has a NULL array");
     if (c->keys_f16 && ((uintptr_t)c->keys_f16 & 15u) != 0)
         return fail(KV_ERR_ARG, "keys_f16 must be 16-byte aligned");
+    if (c->key_center && ((uintptr_t)c->key_center & 15u) != 0)
+        return fail(KV_ERR_ARG, "key_center must be 16-byte aligned");
     return KV_OK;
 }
 
@@ -204,6 +206,7 @@ kvc::CacheView view_of(const kv_cache *c)
     v.keys = c->keys;
     v.vals = c->vals;
     v.kf16 = c->keys_f16;
+    v.kc = c->key_center;
     return v;
 }
 
@@ -268,7 +271,7 @@ size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max
 
 namespace {
 
-int decode_impl(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
+int decode_impl(const kv_cache *c, const kv_tail *tail, const float *dither, const float *q, int32_t B, int32_t Hq,
                 const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
                 float top_p, float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
                 hipStream_t stream)
@@ -311,6 +314,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *q, int32_t 
     qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
+    qp.dither = dither;
     qp.has_tail = tail != nullptr;
     if (tail) {
         kvc::TailParams &tp = qp.tail;
@@ -327,6 +331,8 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *q, int32_t 
         tp.tm = at<float>(workspace, pl.off_tm);
         tp.tl = at<float>(workspace, pl.off_tl);
         tp.to = at<float>(workspace, pl.off_to);
+        // exact scores of the compressed tokens (binary16 keys under Top-p) are uncentered
+        tp.center = (c->keys_f16 && pl.topp) ? nullptr : c->key_center;
     }
     stage_mark(dbg, KV_STAGE_QUERY, true, stream);
     hipError_t e = kvc::launch_qprep(qp, stream);
@@ -433,8 +439,8 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
                      hipStream_t stream)
 {
     g_err[0] = 0;
-    return decode_impl(c, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
-                       workspace, workspace_bytes, stream);
+    return decode_impl(c, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out,
+                       dbg, workspace, workspace_bytes, stream);
 }
 
 int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
@@ -446,7 +452,25 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
     if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
     int rc = check_tail(tail, c->num_kv_heads, c->head_dim, B);
     if (rc) return rc;
-    return decode_impl(c, tail, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
+    return decode_impl(c, tail, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
+                       workspace, workspace_bytes, stream);
+}
+
+int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
+                        const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                        int32_t max_pages, float top_p, float *out, const kv_debug *dbg, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
+    const kv_tail *tail = opts ? opts->tail : nullptr;
+    const float *dither = opts ? opts->q_dither : nullptr;
+    if (tail) {
+        int rc = check_tail(tail, c->num_kv_heads, c->head_dim, B);
+        if (rc) return rc;
+    }
+    if (dither && ((uintptr_t)dither & 3u) != 0) return fail(KV_ERR_ARG, "q_dither must be 4-byte aligned");
+    return decode_impl(c, tail, dither, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
                        workspace, workspace_bytes, stream);
 }
 

@@ -98,6 +98,17 @@ __device__ __forceinline__ void store_key16(const CacheView &c, size_t slot, int
     reinterpret_cast<uint4 *>(c.kf16 + slot * kD)[i] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Key centering: x -= c (binary32) for dims 8i .. 8i+7 of KV head h, when the cache has
+// centers; the sign bits, norm and correction are then those of k - c.
+__device__ __forceinline__ void center8(const CacheView &c, int h, int i, float (&x)[8])
+{
+    if (!c.kc) return;
+    const float4 *cr = reinterpret_cast<const float4 *>(c.kc + (size_t)h * kD + 8 * i);
+    const float4 a = cr[0], b = cr[1];
+    x[0] -= a.x; x[1] -= a.y; x[2] -= a.z; x[3] -= a.w;
+    x[4] -= b.x; x[5] -= b.y; x[6] -= b.z; x[7] -= b.w;
+}
+
 // Sum over the 16 lanes of a token-head group.
 __device__ __forceinline__ double sum16(double v)
 {
@@ -129,6 +140,7 @@ __global__ __launch_bounds__(256) void k_append_hadamard(AppendParams p, long N)
     load8(p.v, p.dtype, row, xv);
     const size_t slot = slot_of(p, n);
     if (p.c.kf16) store_key16(p.c, slot, i, xk);
+    center8(p.c, (int)(n % p.c.Hkv), i, xk);
 
     // sigma, then the 7 butterfly levels (h = 1, 2, 4 inside the lane, 8..64 across lanes)
     const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[i >> 2];
@@ -214,6 +226,7 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
             if (n < N) {
                 load8(p.k, p.dtype, (size_t)n * kD + 8 * i, x);
                 if (p.c.kf16) store_key16(p.c, slot_of(p, n), i, x);
+                center8(p.c, (int)(n % p.c.Hkv), i, x);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = 0.0f;
@@ -319,9 +332,10 @@ __global__ __launch_bounds__(256) void k_append_dense_small(AppendParams p, long
     if (t >= 64 && t < 80) load8(p.v, p.dtype, (size_t)n * kD + 8 * (t - 64), xv);
     const size_t slot = slot_of(p, n);
     if (t < 16) {
+        if (p.c.kf16) store_key16(p.c, slot, t, xk);
+        center8(p.c, (int)(n % p.c.Hkv), t, xk);
 #pragma unroll
         for (int e = 0; e < 8; ++e) kd[8 * t + e] = (double)xk[e];
-        if (p.c.kf16) store_key16(p.c, slot, t, xk);
     }
     __syncthreads();
     double y = 0.0;

@@ -75,7 +75,8 @@ struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 // holds the values of dims 8 dg .. 8 dg + 7 of tokens ts + 8 i, i < 16, so that every load
 // of the pass is in flight at once.  The block takes the max and the weights
 // exp2((s - m) log2e / sqrt(D)) with a running max over passes; thread (dg, ts) sums its 16
-// weighted values, and the 8 token slices are added at the end.  Writes the partial
+// weighted values, and the 8 token slices are added at the end.  With key centers the
+// scores are <q, k> - <q, c> (the frame of the centered proxy scores).  Writes the partial
 // (m, l, o[128]) that the merge adds to the chunk partials (m = -inf and zeros for an
 // empty tail).
 // ---------------------------------------------------------------------------------------
@@ -89,7 +90,17 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = bh / p.Hq, h = bh - b * p.Hq, kvh = h / p.G;
     const int n = min(max(p.len[b], 0), p.cap);
-    qs[tid] = p.q[(size_t)bh * kD + tid];
+    const float qv = p.q[(size_t)bh * kD + tid];
+    qs[tid] = qv;
+    // centered cache: tail scores move to the same frame, <q, k> - <q, c>
+    float qc = 0.0f;
+    if (p.center) {
+        const float cs = wave_sum(qv * p.center[(size_t)kvh * kD + tid]);
+        if (lane == 0) red[0][wave] = cs;
+        __syncthreads();
+        qc = red[0][0] + red[0][1];
+        __syncthreads();  // red is reused by the passes
+    }
     const int dg = tid & 15, ts = tid >> 4;
     const size_t row = (size_t)p.Hkv * kD;  // binary16 elements from one token to the next
     const uint16_t *kb = p.k + ((size_t)b * p.cap * p.Hkv + kvh) * kD;
@@ -120,7 +131,7 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
                 for (int e = 0; e < 8; ++e)
                     a = fmaf(qs[8 * c + e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
             }
-            s = a;
+            s = a - qc;
         }
         const float wm = wave_max(s);
         if (lane == 0) red[0][wave] = wm;
@@ -166,7 +177,9 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 //   hadamard: x = sigma * q, in-place fast Walsh-Hadamard butterflies h = 1..64 (binary32),
 //             q' = x * fp32(1/sqrt(D))
 //   v_l = min q', delta = (max q' - v_l) / 15, u = clamp(rint((q' - v_l) / delta), 0, 15)
-//   (u = 0 when delta == 0); the codes in dot8 order; c0 = v_l/sqrt(D), c1 = delta/sqrt(D).
+//   (u = 0 when delta == 0), or clamp(floor((q' - v_l) / delta + U), 0, 15) with the
+//   caller's uniform U under stochastic rounding; the codes in dot8 order; c0 = v_l/sqrt(D),
+//   c1 = delta/sqrt(D).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
 {
@@ -232,7 +245,8 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
     const float delta = (vr - vl) / 15.0f;
     int u = 0;
     if (delta != 0.0f) {
-        float t = rintf((x - vl) / delta);
+        const float tq = (x - vl) / delta;
+        float t = p.dither ? floorf(tq + p.dither[(size_t)bh * kD + r]) : rintf(tq);
         t = fminf(fmaxf(t, 0.0f), 15.0f);
         u = (int)t;
     }

@@ -24,6 +24,7 @@ struct CacheView {
     uint32_t *keys;  // [pages][Hkv][P][5]: 4 sign words, norm/corr word
     uint8_t *vals;   // [pages][Hkv][P][64 + 4 * 128/Gv]: codes, scale/zero words
     uint16_t *kf16;  // nullable [pages][Hkv][P][128]: binary16 keys (unrotated)
+    const float *kc; // nullable [Hkv][128]: key centers subtracted before the rotation
 };
 
 // Key record of a slot (20 bytes: 4 sign words, then the norm/corr word).
@@ -56,6 +57,7 @@ struct TailParams {
     const int32_t *len;    // [B]
     int cap;
     float *tm, *tl, *to;   // [B*Hq], [B*Hq], [B*Hq][128]
+    const float *center;   // nullable [Hkv][128]: scores are <q, k> - <q, center> (centered frame)
 };
 
 // Query preparation: rotate, quantize, bit-planes.
@@ -70,6 +72,7 @@ struct QprepParams {
     uint8_t *dbg_codes;    // nullable [B*Hq][128]
     float *dbg_params;     // nullable [B*Hq][4]
     int32_t *dbg_sumu;     // nullable [B*Hq]
+    const float *dither;   // nullable [B*Hq][128]: uniforms of the stochastic rounding
     int has_tail;          // blocks BH .. 2 BH - 1 attend over the binary16 tail
     TailParams tail;
 };

@@ -79,6 +79,17 @@ enum { KV_F16 = 0, KV_F32 = 1 };
  *   proxy scores still choose them): RaBitQCache's abstract, proxy scores that estimate the
  *   attention weights to retrieve a token set for sparse attention.  A caller that wants the
  *   proxy scores for a cache that has the array passes a copy of the struct with it NULL.
+ * key_center (nullable): binary32 [Hkv][D], 16-byte aligned, one center c_h per KV head (for
+ *   instance the mean of the head's keys): per-head key centering before the rotation, an
+ *   estimator variant outside the pages.  Appends encode k - c_h (the input widened to
+ *   binary32, then one binary32 subtraction per dim) in place of k: the sign bits, the norm
+ *   and the correction are those of k - c_h, and keys_f16 still holds k.  The proxy scores
+ *   then estimate <q, k - c_h> = <q, k> - <q, c_h>, which differs from <q, k> by one
+ *   constant per (sequence, query head); softmax weights do not see such a shift, so the
+ *   decode uses the centered scores as they are (Top-p bins included).  Only tail tokens
+ *   (kv_decode_attend_tail), scored exactly, are moved into the same frame: <q, k> - <q, c_h>
+ *   (unless the cache's exact scores are in use, which are uncentered).  The same centers
+ *   must be used for every append and decode of one cache.
  * rot: KV_ROT_DENSE -> binary16 [D][D] row-major orthogonal matrix R (k' = R k);
  *      KV_ROT_HADAMARD -> uint32 [D/32] random signs (bit j set: sigma_j = -1), and
  *      R = H diag(sigma) / sqrt(D) with H the Sylvester-order Hadamard matrix.
@@ -95,6 +106,7 @@ typedef struct kv_cache {
     uint32_t *keys;        /* device, 4-byte aligned: see above */
     uint8_t *vals;         /* device, 4-byte aligned: see above */
     uint16_t *keys_f16;    /* device, nullable, 16-byte aligned: see above */
+    const float *key_center; /* device, nullable, 16-byte aligned: see above */
 } kv_cache;
 
 /* Optional intermediate outputs of kv_decode_attend ([host] struct; every member is a
@@ -214,6 +226,28 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
                           const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
                           int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Optional inputs of a decode step ([host] struct; every member is nullable).
+ *   tail      as for kv_decode_attend_tail
+ *   q_dither  device float [B][Hq][D]: uniforms U in [0, 1) drawn by the caller, one per
+ *             query dim.  The int4 query codes become u_j = clamp(floor(t_j + U_j), 0, 15)
+ *             with t_j = (q'_j - v_l) / delta and a binary32 add, in place of rint(t_j):
+ *             seeded stochastic rounding, so that E[u_j] = t_j and the query quantization
+ *             adds no bias to the proxy score (an estimator variant outside the pages, the
+ *             randomized query quantization of RaBitQ).  Values outside [0, 1) are the
+ *             caller's error; the codes stay clamped to 0..15. */
+typedef struct kv_decode_opts {
+    const kv_tail *tail;
+    const float *q_dither;
+} kv_decode_opts;
+
+/* kv_decode_attend_ex -- kv_decode_attend with the options of kv_decode_opts (opts NULL or
+ * all members NULL: the same as kv_decode_attend).  Arguments, errors and workspace as
+ * kv_decode_attend_tail when a tail is given, else as kv_decode_attend. */
+int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
+                        const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                        int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace size for kv_decode_attend with these arguments (0 on invalid arguments). */
 size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,

@@ -52,7 +52,7 @@ def _load():
     lib.orc_rotate_f64.argtypes = [i32, i32, P, P, P, i64, P]
     lib.orc_key_encode.argtypes = [i32, i32, P, P, P, i64, P, P]
     lib.orc_value_encode.argtypes = [i32, i32, P, i64, P, P]
-    lib.orc_query_encode.argtypes = [i32, i32, P, P, P, i64, P, P, P, P]
+    lib.orc_query_encode.argtypes = [i32, i32, P, P, P, i64, P, P, P, P, P]
     lib.orc_scores.argtypes = [i32, P, P, i64, P, f32, f32, P, P, P]
     lib.orc_kbin.argtypes = [i32]
     lib.orc_kbin.restype = f32
@@ -144,17 +144,20 @@ def value_encode(v, D: int, Gv: int):
     return codes, sz
 
 
-def query_encode(rot: Rotation, q):
-    """q: (m, D) float32 -> dict(u (m, D) uint8, vl, delta, c0, c1 (m,) f32, sumu (m,), qrot)."""
+def query_encode(rot: Rotation, q, dither=None):
+    """q: (m, D) float32 -> dict(u (m, D) uint8, vl, delta, c0, c1 (m,) f32, sumu (m,), qrot).
+    dither: optional (m, D) float32 uniforms in [0, 1) for stochastic rounding of the codes."""
     D = rot.D
     q = _c(np.asarray(q, dtype=np.float32).reshape(-1, D), np.float32)
     m = q.shape[0]
+    if dither is not None:
+        dither = _c(np.asarray(dither, dtype=np.float32).reshape(m, D), np.float32)
     u = np.empty((m, D), dtype=np.uint8)
     par = np.empty((m, 4), dtype=np.float32)
     sumu = np.empty(m, dtype=np.int32)
     qrot = np.empty((m, D), dtype=np.float32)
-    _load().orc_query_encode(D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(q), m, _p(u), _p(par),
-                             _p(sumu), _p(qrot))
+    _load().orc_query_encode(D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(q), m,
+                             _p(dither) if dither is not None else None, _p(u), _p(par), _p(sumu), _p(qrot))
     return dict(u=u, vl=par[:, 0].copy(), delta=par[:, 1].copy(), c0=par[:, 2].copy(),
                 c1=par[:, 3].copy(), sumu=sumu, qrot=qrot)
 
@@ -249,12 +252,14 @@ def attend_exact(q, k16, codes, sz, D: int, Gv: int, idx) -> np.ndarray:
     return (w @ value_decode(np.asarray(codes)[idx], np.asarray(sz)[idx], D, Gv)) / w.sum()
 
 
-def attend_with_tail(s_sel, vals_sel, q, tk, tv, D: int) -> np.ndarray:
+def attend_with_tail(s_sel, vals_sel, q, tk, tv, D: int, shift: float = 0.0) -> np.ndarray:
     """One softmax over the attended compressed tokens (scores s_sel, decoded values vals_sel)
-    and the binary16 tail tokens (exact scores <q, k>, their binary16 values), in binary64:
-    the lazy updates of "RaBitQCache" (abstract) leave the newest tokens uncompressed, and a
-    decode attends them next to the cache.  No tokens at all gives zeros."""
-    s = np.concatenate([np.asarray(s_sel, dtype=np.float64).ravel(), exact_scores(q, np.asarray(tk).reshape(-1, D))])
+    and the binary16 tail tokens (exact scores <q, k> - shift, their binary16 values), in
+    binary64: the lazy updates of "RaBitQCache" (abstract) leave the newest tokens
+    uncompressed, and a decode attends them next to the cache.  shift = <q, c> puts the tail
+    in the frame of proxy scores of keys centered at c.  No tokens at all gives zeros."""
+    s = np.concatenate([np.asarray(s_sel, dtype=np.float64).ravel(),
+                        exact_scores(q, np.asarray(tk).reshape(-1, D)) - float(shift)])
     if s.size == 0:
         return np.zeros(D)
     vals = np.concatenate([np.asarray(vals_sel, dtype=np.float64).reshape(-1, D),
@@ -274,10 +279,14 @@ class PagedCache:
       val_codes uint8  [P][D/2]      4-bit value codes, even dim in the low nibble
       val_sz    uint32 [P][D/Gv]     binary16 scale (low half) | binary16 zero (high half)
       key_f16   float16 [P][D]       with exact_keys: the keys rounded to binary16 (nearest even)
+    key_center (optional, float32 [Hkv][D]): per-head key centers.  Appends encode the
+    binary32 difference k - c_h instead of k (key_f16 keeps k); the proxy scores then
+    estimate <q, k - c_h>, which differs from <q, k> by a constant per query head.
     """
 
-    def __init__(self, num_pages, Hkv, P, D, Gv, exact_keys=False):
+    def __init__(self, num_pages, Hkv, P, D, Gv, exact_keys=False, key_center=None):
         self.num_pages, self.Hkv, self.P, self.D, self.Gv = num_pages, Hkv, P, D, Gv
+        self.key_center = None if key_center is None else np.asarray(key_center, dtype=np.float32).reshape(Hkv, D)
         self.key_f16 = np.zeros((num_pages, Hkv, P, D), dtype=np.float16) if exact_keys else None
         self.key_bits = np.zeros((num_pages, Hkv, P, D // 32), dtype=np.uint32)
         self.key_nc = np.zeros((num_pages, Hkv, P), dtype=np.uint32)
@@ -309,7 +318,11 @@ def append(cache: PagedCache, rot: Rotation, k, v, start_pos, page_table):
         t = int(start_pos[b]) + np.arange(n_new)
         pg, sl = cache.locate(b, t, page_table)
         for h in range(Hkv):
-            bits, nc = key_encode(rot, k[b, :, h, :])
+            kh = k[b, :, h, :]
+            if cache.key_center is not None:
+                # centering before the rotation: one binary32 subtraction per dim
+                kh = kh.astype(np.float32) - cache.key_center[h]
+            bits, nc = key_encode(rot, kh)
             codes, sz = value_encode(v[b, :, h, :], D, cache.Gv)
             cache.key_bits[pg, h, sl] = bits
             cache.key_nc[pg, h, sl] = nc[:, 0].astype(np.uint32) | (nc[:, 1].astype(np.uint32) << 16)
@@ -319,14 +332,17 @@ def append(cache: PagedCache, rot: Rotation, k, v, start_pos, page_table):
                 cache.key_f16[pg, h, sl] = k[b, :, h, :].astype(np.float16)
 
 
-def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy=False, tail=None):
+def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy=False, tail=None,
+                dither=None):
     """One (sequence, query head) decode step.  Query head h reads KV head h*Hkv//Hq.  Under
     Top-p, a cache with binary16 keys attends the selected set with exact scores (out), and
     the proxy-score output is kept as out_proxy; proxy=True ignores the binary16 keys.
     tail = (binary16 keys, binary16 values) of the uncompressed tokens that follow the L
     compressed ones: out is then the one softmax over both (the cache-only output stays as
-    out_cache)."""
-    res = _decode_head_cache(cache, rot, q_h, b, h, Hq, L, page_table, top_p, proxy)
+    out_cache).  With key centers, the proxy scores are those of the centered keys and the
+    tail's exact scores are moved by <q, c> into their frame (not when exact scores of the
+    compressed tokens are in use).  dither: uniforms of the stochastic query rounding."""
+    res = _decode_head_cache(cache, rot, q_h, b, h, Hq, L, page_table, top_p, proxy, dither)
     if tail is None:
         return res
     D, Gv = cache.D, cache.Gv
@@ -342,14 +358,18 @@ def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, 
             s_sel = res["score"][sel]
         vals_sel = value_decode(codes[sel], sz[sel], D, Gv)
     res["out_cache"] = res["out"]
-    res["out"] = attend_with_tail(s_sel, vals_sel, q_h, tail[0], tail[1], D)
+    exact = cache.key_f16 is not None and top_p < 1.0 and not proxy
+    shift = 0.0
+    if cache.key_center is not None and not exact:
+        shift = float(np.dot(np.asarray(q_h, np.float64), cache.key_center[res["kvh"]].astype(np.float64)))
+    res["out"] = attend_with_tail(s_sel, vals_sel, q_h, tail[0], tail[1], D, shift)
     return res
 
 
-def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy):
+def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy, dither=None):
     D, Gv = cache.D, cache.Gv
     kvh = h * cache.Hkv // Hq
-    qe = query_encode(rot, q_h)
+    qe = query_encode(rot, q_h, dither)
     res = dict(u=qe["u"][0], vl=qe["vl"][0], delta=qe["delta"][0], c0=qe["c0"][0],
                c1=qe["c1"][0], sumu=int(qe["sumu"][0]), kvh=kvh)
     if L <= 0:
@@ -374,10 +394,11 @@ def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_
 
 
 def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None, proxy=False,
-           tail=None):
+           tail=None, dither=None):
     """Decode step for q (B, Hq, D).  Returns {(b, h): decode_head(...)} for the requested
     (b, h) pairs (all by default).  tail = (tail_k, tail_v, tail_len): binary16 [B][cap][Hkv][D]
-    keys and values and int [B] lengths of the uncompressed tokens after seq_lens[b]."""
+    keys and values and int [B] lengths of the uncompressed tokens after seq_lens[b].
+    dither: optional (B, Hq, D) uniforms in [0, 1) for stochastic rounding of the query codes."""
     q = np.asarray(q, dtype=np.float32)
     B, Hq, D = q.shape
     if heads is None:
@@ -388,5 +409,6 @@ def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, hea
         if tail is not None:
             n, kvh = int(tail[2][b]), h * cache.Hkv // Hq
             th = (np.asarray(tail[0])[b, :n, kvh], np.asarray(tail[1])[b, :n, kvh])
-        out[(b, h)] = decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy, th)
+        dh = None if dither is None else np.asarray(dither, dtype=np.float32)[b, h]
+        out[(b, h)] = decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy, th, dh)
     return out

@@ -227,14 +227,18 @@ static float inv_sqrt_d(int D) { return (float)(1.0 / sqrt((double)D)); }
  *             Walsh-Hadamard transform, Sylvester order); q'_j = x_j * fp32(1/sqrt(D))
  *   v_l = min q', v_r = max q', delta = (v_r - v_l) / 15
  *   u_j = 0 if delta == 0, else clamp(rint((q'_j - v_l) / delta), 0, 15)   (ties to even)
+ *         or, with dither (uniforms U in [0, 1), one per query dim, nullable):
+ *         clamp(floor((q'_j - v_l) / delta + U_j), 0, 15)  (stochastic rounding: the
+ *         expected code is (q'_j - v_l) / delta; RaBitQ's randomized query quantization,
+ *         outside the pages; binary32 divide, then binary32 add)
  *   c0 = v_l * fp32(1/sqrt(D)),  c1 = delta * fp32(1/sqrt(D)),  sumu = sum_j u_j
  * The dequantized query is q'_j ~ v_l + delta u_j, and x = sign(k')/sqrt(D) gives
  * <x, q> ~ c1 * A + c0 * P with A = sum_j s_j u_j, P = sum_j s_j, s_j = +-1.
  * Output: u[m][D] (one code per byte), par[m][4] = (v_l, delta, c0, c1), sumu[m],
  * qrot[m][D] (optional, the rotated query before quantization). */
 void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs,
-                      const float *q, int64_t m, uint8_t *u, float *par, int32_t *sumu,
-                      float *qrot)
+                      const float *q, int64_t m, const float *dither, uint8_t *u, float *par,
+                      int32_t *sumu, float *qrot)
 {
     float *x = (float *)malloc(sizeof(float) * (size_t)D);
     float isd = inv_sqrt_d(D);
@@ -268,7 +272,8 @@ void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs
         for (int j = 0; j < D; ++j) {
             int c = 0;
             if (delta != 0.0f) {
-                float t = rintf((x[j] - vl) / delta);
+                float tq = (x[j] - vl) / delta;
+                float t = dither ? floorf(tq + dither[i * D + j]) : rintf(tq);
                 if (t < 0.0f) t = 0.0f;
                 if (t > 15.0f) t = 15.0f;
                 c = (int)t;

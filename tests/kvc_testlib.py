@@ -29,8 +29,9 @@ class Case:
     def max_len(self):
         return int(max(1, self.lens.max()))
 
-    def oracle_cache(self, exact_keys=False):
-        c = oracle.PagedCache(self.npages, self.wl.Hkv, self.wl.P, self.wl.D, self.wl.Gv, exact_keys=exact_keys)
+    def oracle_cache(self, exact_keys=False, key_center=None):
+        c = oracle.PagedCache(self.npages, self.wl.Hkv, self.wl.P, self.wl.D, self.wl.Gv, exact_keys=exact_keys,
+                              key_center=key_center)
         for b in range(self.wl.B):
             n = int(self.lens[b])
             if n:
@@ -42,21 +43,21 @@ class Case:
         return oracle.decode(cache, self.orot, self.q, self.lens, self.pt, top_p, heads=heads)
 
 
-def gpu_empty_cache(case: Case, device="cuda", exact_keys=False):
+def gpu_empty_cache(case: Case, device="cuda", exact_keys=False, key_center=None):
     from bit_kv_cache_compress_amd import KVCache
 
     rot = case.rot_raw
     return KVCache(case.npages, case.wl.Hkv, rot, rot_kind=case.rot_kind, page_size=case.wl.P,
-                   value_group=case.wl.Gv, device=device, exact_keys=exact_keys)
+                   value_group=case.wl.Gv, device=device, exact_keys=exact_keys, key_center=key_center)
 
 
-def gpu_append(case: Case, chunk=None, device="cuda", exact_keys=False):
+def gpu_append(case: Case, chunk=None, device="cuda", exact_keys=False, key_center=None):
     """The library's append of every sequence (optionally in chunks of `chunk` tokens)."""
     import torch
 
     from bit_kv_cache_compress_amd import append
 
-    cache = gpu_empty_cache(case, device, exact_keys=exact_keys)
+    cache = gpu_empty_cache(case, device, exact_keys=exact_keys, key_center=key_center)
     for b in range(case.wl.B):
         n = int(case.lens[b])
         step = n if chunk is None else chunk
@@ -75,7 +76,7 @@ def upload(cache_o: oracle.PagedCache, case: Case, device="cuda"):
     """A library cache holding the oracle's bytes."""
     import torch
 
-    g = gpu_empty_cache(case, device, exact_keys=cache_o.key_f16 is not None)
+    g = gpu_empty_cache(case, device, exact_keys=cache_o.key_f16 is not None, key_center=cache_o.key_center)
     if cache_o.key_f16 is not None:
         g.keys_f16.copy_(torch.from_numpy(cache_o.key_f16))
     g.key_bits.copy_(torch.from_numpy(cache_o.key_bits.view(np.int32)))

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def _desc(**kw):
     d = dict(head_dim=128, num_kv_heads=8, value_group=32, page_size=256, num_pages=16, rot_kind=0,
-             rot=0x10000, keys=0x10000, vals=0x10000, keys_f16=None)
+             rot=0x10000, keys=0x10000, vals=0x10000, keys_f16=None, key_center=None)
     d.update(kw)
     return L.KVCacheDesc(*[d[f] for f, _ in L.KVCacheDesc._fields_])
 
@@ -53,6 +53,7 @@ def _decode(desc, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p=1.0, ws_bytes
     (dict(rot_kind=7), L.KV_ERR_ARG),
     (dict(keys=0), L.KV_ERR_ARG),
     (dict(keys_f16=0x10008), L.KV_ERR_ARG),  # binary16 keys not 16-byte aligned
+    (dict(key_center=0x10004), L.KV_ERR_ARG),  # key centers not 16-byte aligned
     (dict(vals=0), L.KV_ERR_ARG),
     (dict(rot=0), L.KV_ERR_ARG),
 ])
@@ -142,4 +143,26 @@ def test_bad_tail_descriptor(kw):
 
 def test_null_tail_descriptor():
     assert _decode_tail(None) == L.KV_ERR_ARG
+
+
+def _decode_ex(opts, desc=None, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p=1.0):
+    desc = desc or _desc()
+    ws = L.lib().kv_decode_workspace_bytes(B, Hq, desc.num_kv_heads, max_seq_len, 128, top_p)
+    return L.lib().kv_decode_attend_ex(ctypes.byref(desc) if desc is not None else None,
+                                       ctypes.byref(opts) if opts is not None else None, FAKE, B, Hq, FAKE,
+                                       max_seq_len, FAKE, max_pages, top_p, FAKE, None, FAKE, ws, None)
+
+
+def test_decode_ex_rejects_bad_options():
+    """kv_decode_attend_ex: a misaligned dither, an invalid tail in the options and a bad
+    cache descriptor are errors caught on the host."""
+    assert _decode_ex(L.KVDecodeOpts(None, 0x10002)) == L.KV_ERR_ARG
+    assert "q_dither" in L.last_error()
+    bad_tail = L.KVTailDesc(0x10000, 0x10000, None, 256)
+    assert _decode_ex(L.KVDecodeOpts(ctypes.pointer(bad_tail), None)) == L.KV_ERR_ARG
+    assert _decode_ex(L.KVDecodeOpts(None, None), desc=_desc(head_dim=64)) == L.KV_ERR_UNSUPPORTED
+    assert _decode_ex(L.KVDecodeOpts(None, None), B=0) == L.KV_ERR_ARG
+    rc = L.lib().kv_decode_attend_ex(None, None, FAKE, 2, 32, FAKE, 1000, FAKE, 4, 1.0, FAKE, None, FAKE, 1 << 30,
+                                     None)
+    assert rc == L.KV_ERR_ARG
 

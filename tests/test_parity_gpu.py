@@ -12,6 +12,7 @@ import sys
 import numpy as np
 import pytest
 
+import oracle
 import workloads as W
 from tests.kvc_testlib import Case, compare_caches, download, gpu_append, rel_err, upload
 
@@ -385,3 +386,157 @@ def test_topp_select_standalone():
                 np.testing.assert_array_equal(idx[b, h, :cnt[b, h]], r["idx"])
                 assert np.all(idx[b, h, cnt[b, h]:] == -1)
     _say("[topp] ok")
+
+
+def _centers(c):
+    """Per-KV-head key centers: the mean of the case's keys (binary32), as a caller would
+    take it from the prefill."""
+    m = np.zeros((c.wl.Hkv, c.wl.D), np.float64)
+    n = 0
+    for b in range(c.wl.B):
+        L = int(c.lens[b])
+        m += c.K[b, :L].astype(np.float64).sum(axis=0)
+        n += L
+    return (m / max(n, 1)).astype(np.float32)
+
+
+def _tail_of(c, ntail, cap, dev):
+    """A binary16 tail holding tokens lens-ntail .. lens-1 of each sequence (the compressed
+    length becomes lens - ntail)."""
+    from bit_kv_cache_compress_amd import Tail
+
+    B, Hkv, D = c.wl.B, c.wl.Hkv, c.wl.D
+    lc = (c.lens - ntail).astype(np.int32)
+    tk = np.zeros((B, cap, Hkv, D), np.float16)
+    tv = np.zeros_like(tk)
+    for b in range(B):
+        tk[b, :ntail[b]] = c.K[b, lc[b]:lc[b] + ntail[b]].astype(np.float16)
+        tv[b, :ntail[b]] = c.V[b, lc[b]:lc[b] + ntail[b]].astype(np.float16)
+    tail = Tail(B, cap, Hkv, dev)
+    tail.k.copy_(torch.from_numpy(tk))
+    tail.v.copy_(torch.from_numpy(tv))
+    tail.len.copy_(torch.from_numpy(ntail.astype(np.int32)))
+    return tail, (tk, tv, ntail), lc
+
+
+@pytest.mark.parametrize("name", ["c1-full-fp32-dense", "c2-outliers-ragged", "c3-gqa4-spikes-topp",
+                                  "c4-paged-g64-ragged", "c5-hadamard-topp"])
+def test_key_centering(name):
+    """Per-head key centering: the appended cache bytes bit-exact against the oracle's
+    centered cache, the decode's codes, proxy scores and Top-p sets bit-exact, outputs
+    within the bar, also with a binary16 tail (scores moved into the centered frame) and,
+    under Top-p, with exact scores."""
+    from bit_kv_cache_compress_amd import decode_attend
+
+    c = _case(name)
+    dev = torch.device("cuda")
+    kc = _centers(c)
+    _say(f"[center] {name} |c| max {np.abs(kc).max():.3f}")
+    ocen = c.oracle_cache(key_center=kc)
+    g = gpu_append(c, key_center=torch.from_numpy(kc))
+    stats = compare_caches(download(g), ocen, c)
+    _say(f"[center] {name} append ok {stats}")
+    gu = upload(ocen, c)
+    for top_p in sorted({c.wl.top_p, 1.0}):
+        out, dbg = _decode_with_debug(c, gu, top_p)
+        ref = oracle.decode(ocen, c.orot, c.q, c.lens, c.pt, top_p)
+        S = dbg.scores.cpu().numpy()
+        worst = 0.0
+        for (b, h), r in ref.items():
+            n = int(c.lens[b])
+            np.testing.assert_array_equal(S[b, h, :n].view(np.uint32), r["score"].view(np.uint32))
+            if top_p < 1.0 and n > 0:
+                cnt = int(dbg.sel_count[b, h])
+                np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            if n == 0:
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (top_p, b, h, e)
+        _say(f"[center] {name} top_p={top_p} ok, worst rel err {worst:.2e}")
+    # with a tail, proxy and (under Top-p) exact scores
+    ntail = np.minimum(np.array([[0, 1, 100, 256][b % 4] for b in range(c.wl.B)], np.int32), c.lens)
+    tail, otail, lc = _tail_of(c, ntail, 256, dev)
+    lcd = torch.from_numpy(lc).to(dev)
+    q = torch.from_numpy(c.q).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    variants = [(False, top_p) for top_p in sorted({c.wl.top_p, 1.0})]
+    if c.wl.top_p < 1.0:
+        variants.append((True, c.wl.top_p))
+    for exact, top_p in variants:
+        oc = c.oracle_cache(exact_keys=True, key_center=kc) if exact else ocen
+        gc = upload(oc, c) if exact else gu
+        out = decode_attend(gc, q, lcd, pt, top_p=top_p, max_seq_len=c.max_len, tail=tail)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        ref = oracle.decode(oc, c.orot, c.q, lc, c.pt, top_p, tail=otail)
+        worst = 0.0
+        for (b, h), r in ref.items():
+            if lc[b] + ntail[b] == 0:
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (exact, top_p, b, h, e)
+        _say(f"[center] {name} tail exact={exact} top_p={top_p} ok, worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", ["c2-outliers-ragged", "c3-gqa4-spikes-topp", "c4-paged-g64-ragged",
+                                  "c5-hadamard-topp", "gqa8-topp"])
+def test_stochastic_query_rounding(name):
+    """Seeded stochastic rounding of the int4 query (uniforms passed in): codes, parameters,
+    scores and Top-p sets bit-exact against the oracle given the same uniforms, outputs
+    within the bar; with a tail too."""
+    from bit_kv_cache_compress_amd import DecodeDebug, decode_attend
+
+    c = _case(name)
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(1234)
+    U = rng.random((c.wl.B, c.wl.Hq, c.wl.D), dtype=np.float32)
+    Ud = torch.from_numpy(U).to(dev)
+    g = upload(c.ocache, c)
+    q = torch.from_numpy(c.q).to(dev)
+    lens = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    for top_p in sorted({c.wl.top_p, 1.0}):
+        _say(f"[dither] {name} top_p={top_p}")
+        dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev)
+        out = decode_attend(g, q, lens, pt, top_p=top_p, max_seq_len=c.max_len, debug=dbg, q_dither=Ud)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        ref = oracle.decode(c.ocache, c.orot, c.q, c.lens, c.pt, top_p, dither=U)
+        plain = c.oracle_decode(c.ocache, top_p)
+        qc = dbg.q_codes.cpu().numpy()
+        qp = dbg.q_params.cpu().numpy()
+        S = dbg.scores.cpu().numpy()
+        worst, differ = 0.0, 0
+        for (b, h), r in ref.items():
+            np.testing.assert_array_equal(qc[b, h], r["u"])
+            np.testing.assert_array_equal(qp[b, h], np.array([r["vl"], r["delta"], r["c0"], r["c1"]], np.float32))
+            differ += int(np.any(r["u"] != plain[(b, h)]["u"]))
+            n = int(c.lens[b])
+            np.testing.assert_array_equal(S[b, h, :n].view(np.uint32), r["score"].view(np.uint32))
+            if top_p < 1.0 and n > 0:
+                cnt = int(dbg.sel_count[b, h])
+                np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            if n == 0:
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (top_p, b, h, e)
+        assert differ > 0  # the dither changed the codes
+        _say(f"[dither] {name} top_p={top_p} ok, worst rel err {worst:.2e}")
+    ntail = np.minimum(np.array([[0, 1, 100, 256][b % 4] for b in range(c.wl.B)], np.int32), c.lens)
+    tail, otail, lc = _tail_of(c, ntail, 256, dev)
+    out = decode_attend(g, q, torch.from_numpy(lc).to(dev), pt, top_p=c.wl.top_p, max_seq_len=c.max_len,
+                        tail=tail, q_dither=Ud)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = oracle.decode(c.ocache, c.orot, c.q, lc, c.pt, c.wl.top_p, tail=otail, dither=U)
+    for (b, h), r in ref.items():
+        if lc[b] + ntail[b] == 0:
+            continue
+        assert rel_err(out[b, h], r["out"]) <= TOL, (b, h)
+    _say(f"[dither] {name} tail ok")
