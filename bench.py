@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--lazy", action="store_true",
                     help="lazy updates: new tokens go to a binary16 tail, whole pages are compressed on a "
                          "second stream; times one page cycle (steps default to the page size)")
+    ap.add_argument("--center-keys", action="store_true",
+                    help="estimator variant: per-head key centers (the mean of the prefill keys)")
+    ap.add_argument("--stochastic-query", action="store_true",
+                    help="estimator variant: seeded stochastic rounding of the int4 query")
     ap.add_argument("--exact-keys", action="store_true",
                     help="also keep binary16 keys; Top-p attends the selected tokens with exact scores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -221,8 +225,19 @@ def main():
     K, V, q = W.draw_device(wl, dev, L=Lmax)
     pt_np, npages = W.page_layout(wl, lens)
     kind, rot = W.draw_rotation(wl)
+    center = None
+    if args.center_keys:
+        center = torch.zeros((Hkv, D), dtype=torch.float64, device=dev)
+        for b in range(B):
+            center += K[b, :int(lens[b]) - 1].double().sum(dim=0)
+        center = (center / float(max(int(lens.sum()) - B, 1))).float()
     cache = kvc.KVCache(npages, Hkv, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev,
-                        exact_keys=args.exact_keys)
+                        exact_keys=args.exact_keys, key_center=center)
+    dither = None
+    if args.stochastic_query:
+        gd = torch.Generator(device=dev)
+        gd.manual_seed(wl.seed(77))
+        dither = torch.rand((B, Hq, D), generator=gd, device=dev, dtype=torch.float32)
     pt = torch.from_numpy(pt_np).to(dev)
     seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
     # prefill tokens 0 .. len-2 of every sequence
@@ -255,7 +270,7 @@ def main():
     def step(dbg=None):
         kvc.append(cache, k_new, v_new, start, pt)
         kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
-                          debug_struct=dbg)
+                          debug_struct=dbg, q_dither=dither)
 
     if args.profile_steps:
         for _ in range(args.profile_steps):
@@ -303,7 +318,7 @@ def main():
         kvc.append(cache, k_new, v_new, start, pt)
         aev[i][1].record()
         kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
-                          debug_struct=timers[i].struct())
+                          debug_struct=timers[i].struct(), q_dither=dither)
     torch.cuda.synchronize()
     stage_ms = {}
     ran = ("query", "score", "hist", "attend", "merge") if wl.top_p < 1.0 else ("query", "attend", "merge")
@@ -318,7 +333,7 @@ def main():
     sel_union = sel_entries = None
     if wl.top_p < 1.0:
         dbg = kvc.DecodeDebug.allocate(B, Hq, Lmax, True, dev, scores=False)
-        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, debug=dbg)
+        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, debug=dbg, q_dither=dither)
         torch.cuda.synchronize()
         G = Hq // Hkv
         mask = torch.zeros((B, Hkv, Lmax), dtype=torch.bool, device=dev)
@@ -360,7 +375,8 @@ def main():
     ach = per_launch[dominant] / (stage_ms[dominant] / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": None if args.exact_keys else measured_traffic(kernel_names[dominant], wl.name),
+                "traffic": None if (args.exact_keys or args.center_keys or args.stochastic_query)
+                else measured_traffic(kernel_names[dominant], wl.name),
                 "algorithmic_bytes_per_launch": per_launch[dominant],
                 "avg_launch_us": round(stage_ms[dominant] * 1e3, 2)}
     # whole step, algorithmic minimum: every key once, the values (with binary16 keys, also
@@ -380,7 +396,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": Lmax,
                    "head_dim": D, "top_p": wl.top_p, "value_group": Gv, "page_size": P, "rotation": wl.rot,
                    "kv_dtype": wl.kv_dtype, "step": "append 1 token per sequence + decode attention",
-                   "cache_flushed_between_steps": not args.no_flush, "exact_keys": args.exact_keys},
+                   "cache_flushed_between_steps": not args.no_flush, "exact_keys": args.exact_keys,
+                   "key_center": args.center_keys, "stochastic_query": args.stochastic_query},
         "roofline": roofline,
         "step_hbm_frac_algorithmic": round(step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "query_head_tokens_per_s": value * (Hq // Hkv),
@@ -392,8 +409,9 @@ def main():
         result["topp_selected_union_token_kv_heads"] = sel_union
         result["topp_selected_token_query_heads"] = sel_entries
 
-    if args.exact_keys and not args.no_cpu_baseline:
-        log("[cpu] no oracle baseline for the binary16-key mode (the default run has it)")
+    variant = args.exact_keys or args.center_keys or args.stochastic_query
+    if variant and not args.no_cpu_baseline:
+        log("[cpu] no oracle baseline for the variant modes (the default run has it)")
     elif not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, wl, K, V, q, lens, pt_np, kind, rot,
                                                                       out, value)

@@ -190,3 +190,30 @@ def test_centering_changes_the_encoding_per_head():
         np.testing.assert_array_equal(cen.key_bits[0, h, :40], bits)
         other, _ = oracle.key_encode(rot, k[0, :, h] - c[(h + 1) % 3])
         assert not np.array_equal(cen.key_bits[0, h, :40], other)
+
+
+def test_centering_lowers_the_score_error_of_offset_keys():
+    """Keys with a common offset (k = mu + noise, |mu| = 3 |noise|): the centered proxy score
+    plus <q, c> (c = the keys' mean) misses <q, k> by far less than the plain proxy score,
+    since the estimator's spread scales with |k - c| instead of |k|."""
+    rot = _rotation("dense", 13)
+    rng = np.random.default_rng(14)
+    n = 2000
+    mu = rng.standard_normal(D)
+    mu *= 3 * np.sqrt(D) / np.linalg.norm(mu)
+    k = (mu[None] + rng.standard_normal((1, n, 1, D))).astype(np.float32)
+    v = np.zeros_like(k)
+    c = k[0, :, 0].astype(np.float64).mean(axis=0).astype(np.float32)[None]
+    pt = np.arange((n + 255) // 256, dtype=np.int32)[None]
+    plain = oracle.PagedCache(pt.size, 1, 256, D, 32)
+    cen = oracle.PagedCache(pt.size, 1, 256, D, 32, key_center=c)
+    oracle.append(plain, rot, k, v, np.zeros(1, np.int32), pt)
+    oracle.append(cen, rot, k, v, np.zeros(1, np.int32), pt)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    exact = k[0, :, 0].astype(np.float64) @ q[0, 0].astype(np.float64)
+    sp = oracle.decode(plain, rot, q, [n], pt, 1.0)[(0, 0)]["score"].astype(np.float64)
+    sc = oracle.decode(cen, rot, q, [n], pt, 1.0)[(0, 0)]["score"].astype(np.float64)
+    sc += float(q[0, 0].astype(np.float64) @ c[0].astype(np.float64))
+    e_plain = np.sqrt(np.mean((sp - exact) ** 2))
+    e_cen = np.sqrt(np.mean((sc - exact) ** 2))
+    assert e_cen < 0.5 * e_plain, (e_cen, e_plain)
