@@ -16,7 +16,7 @@ KV_ROT_DENSE, KV_ROT_HADAMARD = 0, 1
 KV_F16, KV_F32 = 0, 1
 
 EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_ex", "kv_decode_attend_tail",
-           "kv_decode_workspace_bytes",
+           "kv_decode_workspace_bytes", "kv_hp_update",
            "kv_tail_append", "kv_tail_retire", "kv_topp_select", "kv_topp_workspace_bytes", "kv_last_error",
            "kv_version")
 
@@ -57,6 +57,18 @@ class KVTailDesc(ctypes.Structure):
         ("v", ctypes.c_void_p),
         ("len", ctypes.c_void_p),
         ("capacity", ctypes.c_int32),
+        ("mass", ctypes.c_void_p),
+    ]
+
+
+class KVHpDesc(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("pos", ctypes.c_void_p),
+        ("saved", ctypes.c_void_p),
+        ("mass", ctypes.c_void_p),
+        ("capacity", ctypes.c_int32),
     ]
 
 
@@ -64,6 +76,7 @@ class KVDecodeOpts(ctypes.Structure):
     _fields_ = [
         ("tail", ctypes.POINTER(KVTailDesc)),
         ("q_dither", ctypes.c_void_p),
+        ("hp", ctypes.POINTER(KVHpDesc)),
     ]
 
 
@@ -104,6 +117,9 @@ def lib():
     L.kv_decode_attend_ex.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVDecodeOpts), P, i32, i32, P, i32,
                                       P, i32, f32, P, ctypes.POINTER(KVDebug), P, sz, P]
     L.kv_decode_attend_ex.restype = ctypes.c_int
+    L.kv_hp_update.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVHpDesc), ctypes.POINTER(KVTailDesc), i32,
+                               i32, P, P, i32, P]
+    L.kv_hp_update.restype = ctypes.c_int
     L.kv_tail_append.argtypes = [ctypes.POINTER(KVTailDesc), i32, i32, i32, P, P, i32, i32, P]
     L.kv_tail_append.restype = ctypes.c_int
     L.kv_tail_retire.argtypes = [ctypes.POINTER(KVTailDesc), i32, i32, i32, i32, P, P]

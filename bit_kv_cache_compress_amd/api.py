@@ -229,12 +229,14 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
                   top_p: float = 1.0, max_seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
                   debug_struct: Optional[L.KVDebug] = None, proxy: bool = False,
-                  tail: Optional["Tail"] = None, q_dither: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  tail: Optional["Tail"] = None, q_dither: Optional[torch.Tensor] = None,
+                  hp: Optional["HPTier"] = None) -> torch.Tensor:
     """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32.  Under Top-p, a
     cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set.
     With ``tail``, each sequence's binary16 tail tokens follow its seq_lens compressed ones.
     ``q_dither`` (float32 [B, Hq, 128], uniforms in [0, 1)): stochastic rounding of the int4
-    query codes, floor(t + U) instead of rint(t)."""
+    query codes, floor(t + U) instead of rint(t).  ``hp``: the high-precision tier, attended
+    exactly next to the tail; the tail (created with mass=True) and the tier accumulate mass."""
     dev = cache.device
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
@@ -260,9 +262,14 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
     desc = cache.proxy_desc if proxy else cache.desc
     if tail is not None and (tail.k.shape[0] != B or tail.k.shape[2] != cache.num_kv_heads):
         raise ValueError(f"tail must be [{B}, capacity, {cache.num_kv_heads}, {HEAD_DIM}]")
-    if q_dither is not None:
-        _need(q_dither, "q_dither", torch.float32, dev, (B, Hq, HEAD_DIM))
-        opts = L.KVDecodeOpts(ctypes.pointer(tail.desc) if tail is not None else None, _ptr(q_dither))
+    if hp is not None and (hp.B != B or hp.num_kv_heads != cache.num_kv_heads):
+        raise ValueError(f"tier must be [{B}, {cache.num_kv_heads}, capacity]")
+    if q_dither is not None or hp is not None:
+        if q_dither is not None:
+            _need(q_dither, "q_dither", torch.float32, dev, (B, Hq, HEAD_DIM))
+        opts = L.KVDecodeOpts(ctypes.pointer(tail.desc) if tail is not None else None,
+                              _ptr(q_dither) if q_dither is not None else None,
+                              ctypes.pointer(hp.desc) if hp is not None else None)
         L.check(L.lib().kv_decode_attend_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), B, Hq, _ptr(seq_lens),
                                             int(max_seq_len), _ptr(page_table), max_pages, float(top_p), _ptr(out),
                                             dbg, _ptr(workspace), workspace.numel(), _stream(dev)))
@@ -284,7 +291,7 @@ class Tail:
     ``len`` int32 [B].  ``page(b, j, n)`` views tokens j .. j+n-1 of sequence b's tail as the
     [1, n, Hkv, 128] input of ``append`` (to compress them into the cache)."""
 
-    def __init__(self, B: int, capacity: int, num_kv_heads: int, device="cuda"):
+    def __init__(self, B: int, capacity: int, num_kv_heads: int, device="cuda", mass: bool = False):
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:
             device = torch.device("cuda", torch.cuda.current_device())
@@ -294,7 +301,10 @@ class Tail:
         self.v = torch.zeros_like(self.k)
         self.len = torch.zeros(B, dtype=torch.int32, device=device)
         self.capacity = int(capacity)
-        self.desc = L.KVTailDesc(self.k.data_ptr(), self.v.data_ptr(), self.len.data_ptr(), self.capacity)
+        # attention mass per (sequence, tail token, KV head), for the high-precision tier
+        self.mass = torch.zeros((B, capacity, num_kv_heads), dtype=torch.float32, device=device) if mass else None
+        self.desc = L.KVTailDesc(self.k.data_ptr(), self.v.data_ptr(), self.len.data_ptr(), self.capacity,
+                                 self.mass.data_ptr() if mass else None)
 
     def page(self, b: int, j: int, n: int):
         return self.k[b:b + 1, j:j + n], self.v[b:b + 1, j:j + n]
@@ -319,6 +329,39 @@ class Tail:
         L.check(L.lib().kv_tail_retire(ctypes.byref(self.desc), self.num_kv_heads, HEAD_DIM, self.B, int(n),
                                        _ptr(seq_lens) if seq_lens is not None else None,
                                        _stream(self.device)))
+
+
+class HPTier:
+    """High-precision tier: per (sequence, KV head) up to ``capacity`` tokens kept in binary16
+    (``k``, ``v`` float16 [B, Hkv, capacity, 128]), with their positions ``pos`` (int32, -1 =
+    empty), the saved norm/correction words of their marked compressed records ``saved``
+    and their accumulated attention mass ``mass`` (float32)."""
+
+    def __init__(self, B: int, capacity: int, num_kv_heads: int, device="cuda"):
+        device = torch.device(device)
+        if device.type == "cuda" and device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = device
+        self.B, self.num_kv_heads, self.capacity = int(B), int(num_kv_heads), int(capacity)
+        shp = (B, num_kv_heads, capacity)
+        self.k = torch.zeros(shp + (HEAD_DIM,), dtype=torch.float16, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.pos = torch.full(shp, -1, dtype=torch.int32, device=device)
+        self.saved = torch.zeros(shp, dtype=torch.int32, device=device)
+        self.mass = torch.zeros(shp, dtype=torch.float32, device=device)
+        self.desc = L.KVHpDesc(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(), self.saved.data_ptr(),
+                               self.mass.data_ptr(), self.capacity)
+
+    def update(self, cache: "KVCache", tail: "Tail", n: int, seq_lens: torch.Tensor, page_table: torch.Tensor) -> None:
+        """Promotion step after tail tokens 0..n-1 were compressed into ``cache`` (at positions
+        seq_lens[b] + j) and before ``tail.retire(n)``."""
+        if tail.mass is None:
+            raise ValueError("the tail needs mass=True")
+        _need(seq_lens, "seq_lens", torch.int32, self.device, (self.B,))
+        _need(page_table, "page_table", torch.int32, self.device)
+        L.check(L.lib().kv_hp_update(ctypes.byref(cache.desc), ctypes.byref(self.desc), ctypes.byref(tail.desc),
+                                     self.B, int(n), _ptr(seq_lens), _ptr(page_table), int(page_table.shape[1]),
+                                     _stream(self.device)))
 
 
 def topp_workspace_bytes(B: int, Hq: int, ld: int) -> int:

@@ -195,6 +195,17 @@ int check_tail(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t
     return KV_OK;
 }
 
+int check_hp(const kv_hp *hp)
+{
+    if (!hp->k || !hp->v || !hp->pos || !hp->saved || !hp->mass) return fail(KV_ERR_ARG, "tier has a NULL array");
+    if (hp->capacity <= 0 || hp->capacity > 1024)
+        return fail(KV_ERR_ARG, "tier capacity must be in 1..1024 (got %d)", hp->capacity);
+    if ((((uintptr_t)hp->k | (uintptr_t)hp->v) & 15u) != 0) return fail(KV_ERR_ARG, "tier k and v must be 16-byte aligned");
+    if ((((uintptr_t)hp->pos | (uintptr_t)hp->saved | (uintptr_t)hp->mass) & 3u) != 0)
+        return fail(KV_ERR_ARG, "tier pos, saved and mass must be 4-byte aligned");
+    return KV_OK;
+}
+
 kvc::CacheView view_of(const kv_cache *c)
 {
     kvc::CacheView v;
@@ -271,7 +282,8 @@ size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max
 
 namespace {
 
-int decode_impl(const kv_cache *c, const kv_tail *tail, const float *dither, const float *q, int32_t B, int32_t Hq,
+int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const float *dither, const float *q,
+                int32_t B, int32_t Hq,
                 const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
                 float top_p, float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
                 hipStream_t stream)
@@ -315,8 +327,8 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *dither, con
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
     qp.dither = dither;
-    qp.has_tail = tail != nullptr;
-    if (tail) {
+    qp.has_tail = tail != nullptr || hp != nullptr;
+    if (qp.has_tail) {
         kvc::TailParams &tp = qp.tail;
         tp.B = B;
         tp.Hq = Hq;
@@ -324,10 +336,14 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *dither, con
         tp.Hkv = c->num_kv_heads;
         tp.klog = klog;
         tp.q = q;
-        tp.k = tail->k;
-        tp.v = tail->v;
-        tp.len = tail->len;
-        tp.cap = tail->capacity;
+        tp.k = tail ? tail->k : nullptr;
+        tp.v = tail ? tail->v : nullptr;
+        tp.len = tail ? tail->len : nullptr;
+        tp.cap = tail ? tail->capacity : 0;
+        tp.hk = hp ? hp->k : nullptr;
+        tp.hv = hp ? hp->v : nullptr;
+        tp.hpos = hp ? hp->pos : nullptr;
+        tp.hcap = hp ? hp->capacity : 0;
         tp.tm = at<float>(workspace, pl.off_tm);
         tp.tl = at<float>(workspace, pl.off_tl);
         tp.to = at<float>(workspace, pl.off_to);
@@ -419,10 +435,25 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const float *dither, con
     mp.po = ap.po;
     mp.tm = mp.tl = mp.to = nullptr;
     mp.out = out;
-    if (tail) {
+    mp.has_mass = 0;
+    if (qp.has_tail) {
         mp.tm = qp.tail.tm;
         mp.tl = qp.tail.tl;
         mp.to = qp.tail.to;
+    }
+    if (hp) {
+        kvc::MassParams &ms = mp.mass;
+        mp.has_mass = 1;
+        ms.q = q;
+        ms.center = qp.tail.center;
+        ms.tk = tail ? tail->k : nullptr;
+        ms.tlen = tail ? tail->len : nullptr;
+        ms.tcap = tail ? tail->capacity : 0;
+        ms.tmass = tail ? tail->mass : nullptr;
+        ms.hk = hp->k;
+        ms.hpos = hp->pos;
+        ms.hmass = hp->mass;
+        ms.hcap = hp->capacity;
     }
     stage_mark(dbg, KV_STAGE_MERGE, true, stream);
     e = kvc::launch_merge(mp, stream);
@@ -439,8 +470,8 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
                      hipStream_t stream)
 {
     g_err[0] = 0;
-    return decode_impl(c, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out,
-                       dbg, workspace, workspace_bytes, stream);
+    return decode_impl(c, nullptr, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p,
+                       out, dbg, workspace, workspace_bytes, stream);
 }
 
 int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
@@ -452,8 +483,8 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
     if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
     int rc = check_tail(tail, c->num_kv_heads, c->head_dim, B);
     if (rc) return rc;
-    return decode_impl(c, tail, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
-                       workspace, workspace_bytes, stream);
+    return decode_impl(c, tail, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out,
+                       dbg, workspace, workspace_bytes, stream);
 }
 
 int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
@@ -465,13 +496,57 @@ int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const flo
     if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
     const kv_tail *tail = opts ? opts->tail : nullptr;
     const float *dither = opts ? opts->q_dither : nullptr;
+    const kv_hp *hp = opts ? opts->hp : nullptr;
     if (tail) {
         int rc = check_tail(tail, c->num_kv_heads, c->head_dim, B);
         if (rc) return rc;
     }
+    if (hp) {
+        int rc = check_hp(hp);
+        if (rc) return rc;
+        if (tail && !tail->mass) return fail(KV_ERR_ARG, "a tier with a tail needs the tail's mass array");
+    }
     if (dither && ((uintptr_t)dither & 3u) != 0) return fail(KV_ERR_ARG, "q_dither must be 4-byte aligned");
-    return decode_impl(c, tail, dither, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
+    return decode_impl(c, tail, hp, dither, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
                        workspace, workspace_bytes, stream);
+}
+
+int kv_hp_update(const kv_cache *c, const kv_hp *hp, const kv_tail *t, int32_t B, int32_t n,
+                 const int32_t *seq_lens, const int32_t *page_table, int32_t max_pages, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_cache(c);
+    if (rc) return rc;
+    if (!hp) return fail(KV_ERR_ARG, "tier descriptor is NULL");
+    rc = check_hp(hp);
+    if (rc) return rc;
+    rc = check_tail(t, c->num_kv_heads, c->head_dim, B);
+    if (rc) return rc;
+    if (!t->mass) return fail(KV_ERR_ARG, "the tail has no mass array");
+    if (n < 0 || n > t->capacity) return fail(KV_ERR_ARG, "n must be in 0..tail capacity (got %d)", n);
+    if (hp->capacity + n > 1024) return fail(KV_ERR_ARG, "tier capacity + n must be <= 1024");
+    if (!seq_lens || !page_table) return fail(KV_ERR_ARG, "NULL seq_lens or page_table");
+    if (max_pages <= 0) return fail(KV_ERR_ARG, "max_pages must be positive");
+    if (n == 0) return KV_OK;
+    kvc::HpUpdateParams p;
+    p.c = view_of(c);
+    p.hk = hp->k;
+    p.hv = hp->v;
+    p.hpos = hp->pos;
+    p.hsaved = hp->saved;
+    p.hmass = hp->mass;
+    p.hcap = hp->capacity;
+    p.tk = t->k;
+    p.tv = t->v;
+    p.tmass = t->mass;
+    p.tcap = t->capacity;
+    p.B = B;
+    p.n = n;
+    p.seq_lens = seq_lens;
+    p.page_table = page_table;
+    p.max_pages = max_pages;
+    hipError_t e = kvc::launch_hp_update(p, stream);
+    return e == hipSuccess ? KV_OK : hip_fail(e, "tier update launch");
 }
 
 int kv_tail_append(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int32_t dtype, const void *k,
@@ -496,6 +571,7 @@ int kv_tail_append(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int
     p.nv = v;
     p.n = n_new;
     p.seq_lens = nullptr;
+    p.mass = t->mass;
     hipError_t e = kvc::launch_tail_append(p, stream);
     return e == hipSuccess ? KV_OK : hip_fail(e, "tail append launch");
 }
@@ -519,6 +595,7 @@ int kv_tail_retire(const kv_tail *t, int32_t num_kv_heads, int32_t head_dim, int
     p.nk = p.nv = nullptr;
     p.n = n;
     p.seq_lens = seq_lens;
+    p.mass = t->mass;
     hipError_t e = kvc::launch_tail_retire(p, stream);
     return e == hipSuccess ? KV_OK : hip_fail(e, "tail retire launch");
 }

@@ -418,6 +418,7 @@ __global__ __launch_bounds__(256) void k_tail_append(TailEditParams p)
 #pragma unroll
         for (int q = 0; q < 4; ++q) w[q] = float_to_half_bits(x[2 * q]) | (float_to_half_bits(x[2 * q + 1]) << 16);
         reinterpret_cast<uint4 *>(p.v + dst)[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        if (p.mass && c == 0) p.mass[((size_t)b * p.cap + j) * p.Hkv + h] = 0.0f;
     }
     __syncthreads();  // every thread has read len[b]
     if (tid == 0) p.len[b] = min(l0 + p.n, p.cap);
@@ -443,6 +444,10 @@ __global__ __launch_bounds__(256) void k_tail_retire(TailEditParams p)
                 k4[d] = k4[d + (size_t)n * row];
                 v4[d] = v4[d + (size_t)n * row];
             }
+            if (p.mass) {
+                float *mb = p.mass + (size_t)b * p.cap * p.Hkv;
+                for (int e = tid; e < cnt * p.Hkv; e += 256) mb[j0 * p.Hkv + e] = mb[(j0 + n) * p.Hkv + e];
+            }
             __syncthreads();
         }
     }
@@ -453,7 +458,107 @@ __global__ __launch_bounds__(256) void k_tail_retire(TailEditParams p)
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Promotion step of the high-precision tier, one 256-thread block per (KV head, sequence).
+// Candidates: the tier's C entries and the n tail tokens just compressed (positions
+// seq_lens[b] + j).  Rank = number of candidates ahead (larger mass; equal mass: lower
+// position; empty entries last, by index); the C first ranks hold the tier afterwards.
+// Leaving entries get their key record's norm/correction word back; entering tokens are
+// copied from the tail and their record word is replaced by the marker.  The free-slot list
+// and the order of entering tokens are ascending, so the result does not depend on timing.
+// ---------------------------------------------------------------------------------------
+constexpr uint32_t kHpMarker = 0x7E007E00u;  // binary16 NaN norm and correction
+constexpr int kHpMaxCand = 1024;
+
+__device__ __forceinline__ uint32_t *norm_word(const HpUpdateParams &p, int b, int kvh, int pos)
+{
+    const int page = p.page_table[(size_t)b * p.max_pages + (pos >> p.c.logP)];
+    const size_t slot = ((size_t)page * p.c.Hkv + kvh) * p.c.P + (pos & (p.c.P - 1));
+    return key_rec(p.c, slot) + kKeyWords;
+}
+
+__global__ __launch_bounds__(256) void k_hp_update(HpUpdateParams p)
+{
+    __shared__ float cm[kHpMaxCand];
+    __shared__ int cp[kHpMaxCand];
+    __shared__ int rk[kHpMaxCand];
+    __shared__ int slot_of_entering[kHpMaxCand];
+    const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int Hkv = p.c.Hkv, C = p.hcap, n = p.n, m = C + n;
+    const size_t e0 = ((size_t)b * Hkv + kvh) * C;
+    const int L0 = p.seq_lens[b];
+    constexpr int kEmpty = 0x7FFFFFFF;
+    for (int i = tid; i < m; i += 256) {
+        if (i < C) {
+            const int pos = p.hpos[e0 + i];
+            cm[i] = pos >= 0 ? p.hmass[e0 + i] : -INFINITY;
+            cp[i] = pos >= 0 ? pos : kEmpty;
+        } else {
+            const int j = i - C;
+            cm[i] = p.tmass[((size_t)b * p.tcap + j) * Hkv + kvh];
+            cp[i] = L0 + j;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += 256) {
+        const float mi = cm[i];
+        const int pi = cp[i];
+        int r = 0;
+        for (int k = 0; k < m; ++k) {
+            const float mk = cm[k];
+            const int pk = cp[k];
+            r += (mk > mi || (mk == mi && (pk < pi || (pk == pi && k < i)))) ? 1 : 0;
+        }
+        rk[i] = r;
+    }
+    __syncthreads();
+    // leaving entries: record word restored, entry emptied
+    for (int i = tid; i < C; i += 256) {
+        if (cp[i] != kEmpty && rk[i] >= C) {
+            *norm_word(p, b, kvh, cp[i]) = p.hsaved[e0 + i];
+            p.hpos[e0 + i] = -1;
+        }
+    }
+    // free slots (ascending) matched with entering tokens (ascending j), by one thread
+    if (tid == 0) {
+        int f = 0;
+        for (int j = 0; j < n; ++j) {
+            if (rk[C + j] < C) {
+                while (f < C && cp[f] != kEmpty && rk[f] < C) ++f;  // occupied and staying
+                slot_of_entering[j] = f++;
+            } else {
+                slot_of_entering[j] = -1;
+            }
+        }
+    }
+    __syncthreads();
+    // entering tokens: 16 threads copy a token's key and value rows, one sets the entry
+    for (int r = tid >> 4; r < n; r += 16) {
+        const int f = slot_of_entering[r];
+        if (f < 0) continue;
+        const int c = tid & 15;
+        const size_t src = (((size_t)b * p.tcap + r) * Hkv + kvh) * kD;
+        const size_t dst = (e0 + f) * kD;
+        reinterpret_cast<uint4 *>(p.hk + dst)[c] = reinterpret_cast<const uint4 *>(p.tk + src)[c];
+        reinterpret_cast<uint4 *>(p.hv + dst)[c] = reinterpret_cast<const uint4 *>(p.tv + src)[c];
+        if (c == 0) {
+            const int pos = L0 + r;
+            uint32_t *nw = norm_word(p, b, kvh, pos);
+            p.hsaved[e0 + f] = *nw;
+            *nw = kHpMarker;
+            p.hpos[e0 + f] = pos;
+            p.hmass[e0 + f] = cm[C + r];
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_hp_update(const HpUpdateParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_hp_update, dim3(p.c.Hkv, p.B), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_tail_append(const TailEditParams &p, hipStream_t s)
 {

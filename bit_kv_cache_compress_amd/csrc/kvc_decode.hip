@@ -75,11 +75,45 @@ struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 // holds the values of dims 8 dg .. 8 dg + 7 of tokens ts + 8 i, i < 16, so that every load
 // of the pass is in flight at once.  The block takes the max and the weights
 // exp2((s - m) log2e / sqrt(D)) with a running max over passes; thread (dg, ts) sums its 16
-// weighted values, and the 8 token slices are added at the end.  With key centers the
-// scores are <q, k> - <q, c> (the frame of the centered proxy scores).  Writes the partial
+// weighted values, and the 8 token slices are added at the end.  The entries of the
+// high-precision tier (KV head of h) follow the tail as a second segment, empty entries
+// with weight 0.  With key centers the scores are <q, k> - <q, c> (the frame of the
+// centered proxy scores).  Writes the partial
 // (m, l, o[128]) that the merge adds to the chunk partials (m = -inf and zeros for an
 // empty tail).
 // ---------------------------------------------------------------------------------------
+// Exact score <q, k> of one binary16 key against the binary32 query in LDS: a binary32 fma
+// chain over the 128 dims (dim 0 first).
+__device__ __forceinline__ float exact_dot(const uint16_t *k, const float *qs)
+{
+    const uint4 *kr = reinterpret_cast<const uint4 *>(k);
+    uint4 kk[kD / 8];
+#pragma unroll
+    for (int c = 0; c < kD / 8; ++c) kk[c] = kr[c];
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kD / 8; ++c) {
+        const uint32_t w[4] = {kk[c].x, kk[c].y, kk[c].z, kk[c].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(qs[8 * c + e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+    }
+    return a;
+}
+
+// <q, c> of the KV head's key center, by the first two waves of the block (q in qs); every
+// thread of the block gets the sum.  red2 is two floats of LDS.
+__device__ __forceinline__ float center_dot(const float *center, int kvh, const float *qs, float *red2)
+{
+    const int tid = threadIdx.x;
+    const float x = tid < kD ? qs[tid] * center[(size_t)kvh * kD + tid] : 0.0f;
+    const float cs = wave_sum(x);
+    if (tid == 0 || tid == 64) red2[tid >> 6] = cs;
+    __syncthreads();
+    const float qc = red2[0] + red2[1];
+    __syncthreads();  // red2 may be reused
+    return qc;
+}
+
 __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 {
     constexpr int T = 128, NS = T / 16, NV = T / NS;  // tokens per pass, token slices, values per thread
@@ -89,73 +123,60 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
     __shared__ float red[2][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = bh / p.Hq, h = bh - b * p.Hq, kvh = h / p.G;
-    const int n = min(max(p.len[b], 0), p.cap);
-    const float qv = p.q[(size_t)bh * kD + tid];
-    qs[tid] = qv;
-    // centered cache: tail scores move to the same frame, <q, k> - <q, c>
-    float qc = 0.0f;
-    if (p.center) {
-        const float cs = wave_sum(qv * p.center[(size_t)kvh * kD + tid]);
-        if (lane == 0) red[0][wave] = cs;
-        __syncthreads();
-        qc = red[0][0] + red[0][1];
-        __syncthreads();  // red is reused by the passes
-    }
+    qs[tid] = p.q[(size_t)bh * kD + tid];
+    __syncthreads();
+    // centered cache: exact scores move to the same frame, <q, k> - <q, c>
+    const float qc = p.center ? center_dot(p.center, kvh, qs, red[0]) : 0.0f;
     const int dg = tid & 15, ts = tid >> 4;
-    const size_t row = (size_t)p.Hkv * kD;  // binary16 elements from one token to the next
-    const uint16_t *kb = p.k + ((size_t)b * p.cap * p.Hkv + kvh) * kD;
-    const uint16_t *vb = p.v + ((size_t)b * p.cap * p.Hkv + kvh) * kD + 8 * dg;
     float m = -INFINITY, l = 0.0f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.0f;
-    __syncthreads();
-    for (int t0 = 0; t0 < n; t0 += T) {
-        uint4 vr[NV];
+
+    // one segment of n binary16 tokens, row elements apart (pos: nullable, < 0 = empty entry)
+    auto segment = [&](const uint16_t *kb, const uint16_t *vb, size_t row, int n, const int32_t *pos) {
+        for (int t0 = 0; t0 < n; t0 += T) {
+            uint4 vr[NV];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int t = t0 + ts + NS * i;
-            vr[i] = t < n ? *reinterpret_cast<const uint4 *>(vb + t * row) : make_uint4(0u, 0u, 0u, 0u);
-        }
-        const int t = t0 + tid;
-        float s = -INFINITY;
-        if (t < n) {
-            const uint4 *kr = reinterpret_cast<const uint4 *>(kb + t * row);
-            uint4 kk[kD / 8];
+            for (int i = 0; i < NV; ++i) {
+                const int t = t0 + ts + NS * i;
+                vr[i] = t < n ? *reinterpret_cast<const uint4 *>(vb + t * row + 8 * dg) : make_uint4(0u, 0u, 0u, 0u);
+            }
+            const int t = t0 + tid;
+            const bool valid = t < n && (!pos || pos[t] >= 0);
+            const float s = valid ? exact_dot(kb + t * row, qs) - qc : -INFINITY;
+            const float wm = wave_max(s);
+            if (lane == 0) red[0][wave] = wm;
+            __syncthreads();
+            const float mnew = fmaxf(m, fmaxf(red[0][0], red[0][1]));
+            const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
+            const float w = valid ? exp2f((s - mnew) * p.klog) : 0.0f;
+            ws[tid] = w;
+            const float wsum = wave_sum(w);
+            if (lane == 0) red[1][wave] = wsum;
+            __syncthreads();
+            l = l * scale + (red[1][0] + red[1][1]);
+            m = mnew;
 #pragma unroll
-            for (int c = 0; c < kD / 8; ++c) kk[c] = kr[c];
-            float a = 0.0f;
+            for (int e = 0; e < 8; ++e) o[e] *= scale;
 #pragma unroll
-            for (int c = 0; c < kD / 8; ++c) {
-                const uint32_t w[4] = {kk[c].x, kk[c].y, kk[c].z, kk[c].w};
+            for (int i = 0; i < NV; ++i) {
+                const float wi = ws[ts + NS * i];
+                const uint32_t keep = wi != 0.0f ? 0xFFFFFFFFu : 0u;  // empty entries hold anything
+                const uint32_t x[4] = {vr[i].x & keep, vr[i].y & keep, vr[i].z & keep, vr[i].w & keep};
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    a = fmaf(qs[8 * c + e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+                    o[e] = fmaf(wi, half_bits_to_float((x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), o[e]);
             }
-            s = a - qc;
+            __syncthreads();  // ws and red are rewritten by the next pass
         }
-        const float wm = wave_max(s);
-        if (lane == 0) red[0][wave] = wm;
-        __syncthreads();
-        const float mnew = fmaxf(m, fmaxf(red[0][0], red[0][1]));
-        const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
-        const float w = (t < n) ? exp2f((s - mnew) * p.klog) : 0.0f;
-        ws[tid] = w;
-        const float wsum = wave_sum(w);
-        if (lane == 0) red[1][wave] = wsum;
-        __syncthreads();
-        l = l * scale + (red[1][0] + red[1][1]);
-        m = mnew;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= scale;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const float wi = ws[ts + NS * i];
-            const uint32_t x[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[e] = fmaf(wi, half_bits_to_float((x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), o[e]);
-        }
-        __syncthreads();  // ws and red are rewritten by the next pass
+    };
+    if (p.k) {
+        const size_t base = ((size_t)b * p.cap * p.Hkv + kvh) * kD;
+        segment(p.k + base, p.v + base, (size_t)p.Hkv * kD, min(max(p.len[b], 0), p.cap), nullptr);
+    }
+    if (p.hk) {
+        const size_t e0 = ((size_t)b * p.Hkv + kvh) * p.hcap;
+        segment(p.hk + e0 * kD, p.hv + e0 * kD, (size_t)kD, p.hcap, p.hpos + e0);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[ts][8 * dg + e] = o[e];
@@ -824,7 +845,7 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     const uint64_t lo2 = lo + ((1ull << 24) - 1);
     hi += (lo2 < lo) ? 1 : 0;
     const uint64_t Tp = (hi << 40) | (lo2 >> 24);
-    int bstar = -1, count = 0;
+    int bstar = -2, count = 0;  // -2: this thread writes nothing
     if (Tp == 0) {
         if (tid == 0) {
             bstar = 0;
@@ -844,7 +865,13 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
             }
         }
     }
-    if (bstar >= 0) {
+    if (emax == -kBinClamp) {
+        // every score NaN or at the bottom clamp (for instance records of tokens held in the
+        // high-precision tier): no token has weight, the set is empty
+        bstar = tid == 0 ? -1 : -2;
+        count = 0;
+    }
+    if (bstar >= -1) {
         p.sel[bh * 4 + 0] = emax;
         p.sel[bh * 4 + 1] = bstar;
         p.sel[bh * 4 + 2] = count;
@@ -1018,7 +1045,8 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         }
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-            if (lane >= nb) s[h] = -INFINITY;
+            // past the batch, or a marked record (a token held in the high-precision tier)
+            if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
             const float mnew = fmaxf(mrun[h], wave_max_u(s[h]));
             const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
             if (scale != 1.0f) {
@@ -1366,6 +1394,60 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
+// Attention mass of the tail tokens and the high-precision tier, once the query head's
+// softmax is known (max score M, weight sum D): every such token adds its weight
+// exp2((s - M) log2e / sqrt(D)) / D, with its exact score s recomputed (16 lanes per token,
+// 8 dims each, so the rounding may differ from the tail pass in the last bits), to its
+// mass; the query heads of a KV head add atomically.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void merge_mass(const MassParams &p, int b, int h, int G, int Hkv, float M, float D,
+                                           float klog)
+{
+    __shared__ float qs[kD];
+    __shared__ float red2[2];
+    const int tid = threadIdx.x, kvh = h / G;
+    const size_t bh = (size_t)b * (G * Hkv) + h;
+    __syncthreads();
+    if (tid < kD) qs[tid] = p.q[bh * kD + tid];
+    __syncthreads();
+    const float qc = p.center ? center_dot(p.center, kvh, qs, red2) : 0.0f;
+    if (!(D > 0.0f)) return;
+    const float inv = 1.0f / D;
+    const int nt = p.tk ? min(max(p.tlen[b], 0), p.tcap) : 0;
+    const int nh = p.hk ? p.hcap : 0;
+    const size_t e0 = ((size_t)b * Hkv + kvh) * p.hcap;
+    // 16 lanes per token, lane sub holding dims 8 sub .. 8 sub + 7
+    const int sub = tid & 15;
+    float qx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qx[e] = qs[8 * sub + e];
+    const int step = (int)blockDim.x >> 4;
+    const int ntot = nt + nh;
+    for (int j0 = 0; j0 < ntot; j0 += step) {  // the same trip count for every lane
+        const int j = j0 + (tid >> 4);
+        const uint16_t *k = nullptr;
+        float *dst = nullptr;
+        if (j < nt) {
+            k = p.tk + (((size_t)b * p.tcap + j) * Hkv + kvh) * kD;
+            dst = p.tmass + ((size_t)b * p.tcap + j) * Hkv + kvh;
+        } else if (j < ntot && p.hpos[e0 + (j - nt)] >= 0) {
+            k = p.hk + (e0 + (j - nt)) * kD;
+            dst = p.hmass + e0 + (j - nt);
+        }
+        float a = 0.0f;
+        if (k) {
+            const uint4 kw = reinterpret_cast<const uint4 *>(k)[sub];
+            const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaf(qx[e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o);
+        if (k && sub == 0) atomicAdd(dst, exp2f((a - qc - M) * klog) * inv);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Split-K merge, one 1024-thread block per (query head, sequence):
 //   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
 // Thread (d, slice) sums the chunks c = slice (mod 8) for dim d.  The value sums of the
@@ -1451,6 +1533,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
         for (int s2 = 0; s2 < NS; ++s2) t += part[s2][d];
         p.out[bh * kD + d] = D > 0.0f ? t / D : 0.0f;
     }
+    if (p.has_mass) merge_mass(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog);
 }
 
 }  // namespace

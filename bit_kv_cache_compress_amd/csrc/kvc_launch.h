@@ -58,6 +58,24 @@ struct TailParams {
     int cap;
     float *tm, *tl, *to;   // [B*Hq], [B*Hq], [B*Hq][128]
     const float *center;   // nullable [Hkv][128]: scores are <q, k> - <q, center> (centered frame)
+    const uint16_t *hk, *hv;  // nullable: high-precision tier [B][Hkv][hcap][128] binary16
+    const int32_t *hpos;   // [B][Hkv][hcap], -1 = empty
+    int hcap;
+};
+
+// Accumulation of attention mass into the tail and the high-precision tier, done by the
+// merge once the softmax normalizer of each query head is known.
+struct MassParams {
+    const float *q;        // [B*Hq][128]
+    const float *center;   // nullable, as TailParams
+    const uint16_t *tk;    // tail keys [B][tcap][Hkv][128]
+    const int32_t *tlen;   // [B]
+    int tcap;
+    float *tmass;          // [B][tcap][Hkv]
+    const uint16_t *hk;    // tier keys [B][Hkv][hcap][128]
+    const int32_t *hpos;   // [B][Hkv][hcap]
+    float *hmass;          // [B][Hkv][hcap]
+    int hcap;
 };
 
 // Query preparation: rotate, quantize, bit-planes.
@@ -163,6 +181,8 @@ struct MergeParams {
     const float *pm, *pl, *po;
     const float *tm, *tl, *to;  // nullable: the tail's partial (max score, weight sum, value sums)
     float *out;            // [B*Hq][128]
+    int has_mass;          // accumulate attention mass (high-precision tier)
+    MassParams mass;
 };
 
 // Exact attention over the binary16 tail: one partial (m, l, o) per (sequence, query head).
@@ -185,8 +205,27 @@ struct TailEditParams {
     const void *nk, *nv;   // append: [B][n][Hkv][128]
     int n;                 // append: n_new; retire: n
     int32_t *seq_lens;     // retire: nullable
+    float *mass;           // nullable [B][cap][Hkv]: zeroed for appended tokens, moved on retire
 };
 hipError_t launch_tail_append(const TailEditParams &p, hipStream_t s);
 hipError_t launch_tail_retire(const TailEditParams &p, hipStream_t s);
+
+// Promotion step of the high-precision tier (one block per (KV head, sequence)).
+struct HpUpdateParams {
+    CacheView c;
+    uint16_t *hk, *hv;     // [B][Hkv][hcap][128]
+    int32_t *hpos;         // [B][Hkv][hcap]
+    uint32_t *hsaved;      // [B][Hkv][hcap]
+    float *hmass;          // [B][Hkv][hcap]
+    int hcap;
+    const uint16_t *tk, *tv;  // tail [B][tcap][Hkv][128]
+    const float *tmass;    // [B][tcap][Hkv]
+    int tcap;
+    int B, n;
+    const int32_t *seq_lens;
+    const int32_t *page_table;
+    int max_pages;
+};
+hipError_t launch_hp_update(const HpUpdateParams &p, hipStream_t s);
 
 }  // namespace kvc

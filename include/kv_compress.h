@@ -196,7 +196,33 @@ typedef struct kv_tail {
     uint16_t *v;
     int32_t *len;
     int32_t capacity;
+    float *mass;           /* nullable float [B][capacity][Hkv]: attention mass accumulated by the
+                              decodes of kv_decode_attend_ex with a high-precision tier (the sum
+                              over the KV head's query heads of each step's softmax weight);
+                              kv_tail_append zeroes it for new tokens, kv_tail_retire moves it */
 } kv_tail;
+
+/* High-precision tier ([host] struct describing device arrays): H1IB-KV's high-precision
+ * layer, which keeps the most important key-value pairs in binary16 while the rest go to
+ * the one-bit layer.  Importance is read here as accumulated attention mass, and a token
+ * can enter the tier only while it is still in binary16, i.e. when its page of the tail is
+ * compressed (kv_hp_update).  Per (sequence b, KV head h) up to `capacity` entries:
+ *   k, v   binary16 [B][Hkv][capacity][D], 16-byte aligned
+ *   pos    int32 [B][Hkv][capacity]: the token position of the entry, -1 for an empty one
+ *   saved  uint32 [B][Hkv][capacity]: the norm/correction word of the token's compressed
+ *          key record, which holds the marker 0x7E007E00 (binary16 NaN norm) while the
+ *          token is in the tier; a decode gives a marked record no weight, so the token is
+ *          attended once, exactly, from the tier.  Eviction restores the word.
+ *   mass   float [B][Hkv][capacity]: accumulated attention mass of the entry
+ * All-empty is pos = -1 everywhere (mass and saved are then ignored). */
+typedef struct kv_hp {
+    uint16_t *k;
+    uint16_t *v;
+    int32_t *pos;
+    uint32_t *saved;
+    float *mass;
+    int32_t capacity;
+} kv_hp;
 
 /* kv_tail_append -- write n_new new tokens per sequence into the tail (lazy update).
  *   dtype  KV_F16 or KV_F32 (rounded to binary16, nearest even)
@@ -239,6 +265,12 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
 typedef struct kv_decode_opts {
     const kv_tail *tail;
     const float *q_dither;
+    const kv_hp *hp;       /* nullable: the high-precision tier.  Its entries of KV head h are
+                              attended with exact scores and binary16 values in the same softmax
+                              as the cache and the tail (scores in the centered frame when the
+                              cache has key centers and is scored by proxy); afterwards every
+                              tail token and tier entry adds its softmax weight, summed over the
+                              KV head's query heads, to its mass (tail->mass must then be set). */
 } kv_decode_opts;
 
 /* kv_decode_attend_ex -- kv_decode_attend with the options of kv_decode_opts (opts NULL or
@@ -248,6 +280,19 @@ int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const flo
                         const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
                         int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* kv_hp_update -- the tier's promotion step, when the first n tokens of every tail (positions
+ * seq_lens[b] .. seq_lens[b] + n - 1) have been compressed into the cache and before
+ * kv_tail_retire(n) drops them.  For each (sequence, KV head), among the tier's entries and
+ * those n tokens, the `capacity` with the largest mass stay or enter (ties: the lower
+ * position first; empty entries last).  An entering token's binary16 key and value are
+ * copied from the tail, its mass carried over, and its compressed key record marked (the
+ * old word kept in saved); a leaving entry's record word is restored and the entry emptied.
+ *   c          the cache the tokens were compressed into (page_table as for the append)
+ *   seq_lens   int32 [B]: compressed tokens before the n, as kv_tail_retire will advance them
+ * Requires t->mass, n <= t->capacity and capacity + n <= 1024. */
+int kv_hp_update(const kv_cache *c, const kv_hp *hp, const kv_tail *t, int32_t B, int32_t n,
+                 const int32_t *seq_lens, const int32_t *page_table, int32_t max_pages, hipStream_t stream);
 
 /* Workspace size for kv_decode_attend with these arguments (0 on invalid arguments). */
 size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
@@ -260,7 +305,8 @@ size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max
  *   [-2^29, 2^29]; d_i = max_j e_j - e_i; weight W(d) = T[d mod 256] >> (d / 256) for
  *   d < 8192 and 0 beyond, T[j] = round(2^(32 - j/256)); Z = sum_i W(d_i);
  *   T_p = ceil(Z * rint(p * 2^24) / 2^24); b* = min { b : sum_{d_i <= b} W(d_i) >= T_p };
- *   selected set S = { i : d_i <= b* }.
+ *   selected set S = { i : d_i <= b* }.  When e_max itself is the bottom bin -2^29 (every
+ *   score NaN or below -2^29 / kbin: no token has weight), S is empty.
  *   scores    float [B][Hq][ld]; tokens 0..seq_lens[b]-1 are used (seq_lens <= ld)
  *   top_p     [host] in (0, 1)
  *   sel_idx   int32 [B][Hq][ld]: S in ascending order; entries past the count are untouched

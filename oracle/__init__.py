@@ -252,20 +252,23 @@ def attend_exact(q, k16, codes, sz, D: int, Gv: int, idx) -> np.ndarray:
     return (w @ value_decode(np.asarray(codes)[idx], np.asarray(sz)[idx], D, Gv)) / w.sum()
 
 
-def attend_with_tail(s_sel, vals_sel, q, tk, tv, D: int, shift: float = 0.0) -> np.ndarray:
+def attend_with_tail(s_sel, vals_sel, q, tk, tv, D: int, shift: float = 0.0, weights: bool = False):
     """One softmax over the attended compressed tokens (scores s_sel, decoded values vals_sel)
     and the binary16 tail tokens (exact scores <q, k> - shift, their binary16 values), in
     binary64: the lazy updates of "RaBitQCache" (abstract) leave the newest tokens
     uncompressed, and a decode attends them next to the cache.  shift = <q, c> puts the tail
-    in the frame of proxy scores of keys centered at c.  No tokens at all gives zeros."""
+    in the frame of proxy scores of keys centered at c.  No tokens at all gives zeros.
+    weights=True also returns the tail tokens' softmax weights (normalized over everything)."""
+    ntk = np.asarray(tk).reshape(-1, D).shape[0]
     s = np.concatenate([np.asarray(s_sel, dtype=np.float64).ravel(),
                         exact_scores(q, np.asarray(tk).reshape(-1, D)) - float(shift)])
     if s.size == 0:
-        return np.zeros(D)
+        return (np.zeros(D), np.zeros(ntk)) if weights else np.zeros(D)
     vals = np.concatenate([np.asarray(vals_sel, dtype=np.float64).reshape(-1, D),
                            np.asarray(tv, dtype=np.float16).astype(np.float64).reshape(-1, D)])
     w = np.exp((s - s.max()) / np.sqrt(D))
-    return (w @ vals) / w.sum()
+    out = (w @ vals) / w.sum()
+    return (out, w[s.size - ntk:] / w.sum()) if weights else out
 
 
 # ----------------------------------------------------------------------------------------
@@ -349,7 +352,9 @@ def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, 
     if L <= 0:
         s_sel, vals_sel = np.zeros(0), np.zeros((0, D))
     else:
-        sel = np.arange(L) if res["idx"] is None else res["idx"]
+        # all live tokens (marked records of the high-precision tier have NaN scores) or the
+        # Top-p set
+        sel = np.nonzero(~np.isnan(res["score"]))[0] if res["idx"] is None else res["idx"]
         bits, nc, codes, sz = cache.gather(b, res["kvh"], L, page_table)
         if cache.key_f16 is not None and top_p < 1.0 and not proxy:
             pg, sl = cache.locate(b, np.arange(L), page_table)
@@ -362,7 +367,7 @@ def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, 
     shift = 0.0
     if cache.key_center is not None and not exact:
         shift = float(np.dot(np.asarray(q_h, np.float64), cache.key_center[res["kvh"]].astype(np.float64)))
-    res["out"] = attend_with_tail(s_sel, vals_sel, q_h, tail[0], tail[1], D, shift)
+    res["out"], res["w_tail"] = attend_with_tail(s_sel, vals_sel, q_h, tail[0], tail[1], D, shift, weights=True)
     return res
 
 
@@ -389,16 +394,90 @@ def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_
             res["out"] = attend_exact(q_h, cache.key_f16[pg, kvh, sl], codes, sz, D, Gv, tp["idx"])
     else:
         res["idx"] = None
-        res["out"] = attend(s, codes, sz, D, Gv)
+        live = ~np.isnan(s)  # a NaN score marks a record held in the high-precision tier
+        res["out"] = attend(s, codes, sz, D, Gv) if live.all() else attend(s, codes, sz, D, Gv, np.nonzero(live)[0])
     return res
 
 
+class HPTier:
+    """High-precision tier ("H1IB-KV" high-precision layer): per (sequence, KV head) up to C
+    tokens kept in binary16, read here as the ones with the largest accumulated attention
+    mass.  k16, v16 float16 [B][Hkv][C][D]; pos int [B][Hkv][C] (-1 empty); saved uint32
+    [B][Hkv][C]: the norm/correction word of the token's compressed key record, which holds
+    MARKER while the token is in the tier; mass float64 [B][Hkv][C]."""
+
+    MARKER = 0x7E007E00  # binary16 NaN norm and correction
+
+    def __init__(self, B, Hkv, C, D):
+        self.B, self.Hkv, self.C, self.D = B, Hkv, C, D
+        self.k16 = np.zeros((B, Hkv, C, D), np.float16)
+        self.v16 = np.zeros((B, Hkv, C, D), np.float16)
+        self.pos = np.full((B, Hkv, C), -1, np.int64)
+        self.saved = np.zeros((B, Hkv, C), np.uint32)
+        self.mass = np.zeros((B, Hkv, C), np.float64)
+
+
+def hp_update(cache: PagedCache, hp: HPTier, tail_k, tail_v, tail_mass, n, seq_lens, page_table):
+    """Promotion step, once tail tokens 0..n-1 of every sequence (positions seq_lens[b] + j)
+    are compressed into the cache: per (sequence, KV head) the C candidates with the largest
+    mass among the tier's entries and those n tokens hold the tier afterwards (equal mass:
+    lower position first; empty entries last).  Leaving entries get their record word back;
+    entering tokens take the free entries in ascending order (in ascending j), with their
+    binary16 key and value, their mass, and their record word saved and replaced by MARKER."""
+    C = hp.C
+    for b in range(hp.B):
+        L0 = int(seq_lens[b])
+        for h in range(hp.Hkv):
+            cand = []  # (sort key, kind, index)
+            for i in range(C):
+                if hp.pos[b, h, i] >= 0:
+                    cand.append(((-hp.mass[b, h, i], int(hp.pos[b, h, i]), i), "entry", i))
+                else:
+                    cand.append(((np.inf, 2**62, i), "entry", i))
+            for j in range(n):
+                cand.append(((-float(tail_mass[b, j, h]), L0 + j, C + j), "tail", j))
+            cand.sort(key=lambda c: c[0])
+            chosen = cand[:C]
+            stay = {i for _, kind, i in chosen if kind == "entry" and hp.pos[b, h, i] >= 0}
+            enter = sorted(j for _, kind, j in chosen if kind == "tail")
+            for i in range(C):
+                if hp.pos[b, h, i] >= 0 and i not in stay:
+                    pg, sl = cache.locate(b, int(hp.pos[b, h, i]), page_table)
+                    cache.key_nc[pg, h, sl] = hp.saved[b, h, i]
+                    hp.pos[b, h, i] = -1
+            free = [i for i in range(C) if hp.pos[b, h, i] < 0]
+            for f, j in zip(free, enter):
+                pos = L0 + j
+                pg, sl = cache.locate(b, pos, page_table)
+                hp.k16[b, h, f] = np.asarray(tail_k)[b, j, h]
+                hp.v16[b, h, f] = np.asarray(tail_v)[b, j, h]
+                hp.saved[b, h, f] = cache.key_nc[pg, h, sl]
+                cache.key_nc[pg, h, sl] = HPTier.MARKER
+                hp.pos[b, h, f] = pos
+                hp.mass[b, h, f] = float(tail_mass[b, j, h])
+
+
+def add_mass(res, tail_mass, hp: HPTier, Hq):
+    """Adds each query head's softmax weights of its tail tokens and tier entries (from
+    decode(..., hp=...)) to tail_mass [B][cap][Hkv] and hp.mass: the mass accumulates the
+    weights of the KV head's query heads, step after step."""
+    for (b, h), r in res.items():
+        kvh = h * hp.Hkv // Hq
+        wt, wh = r["w_tail_only"], r["w_hp"]
+        if tail_mass is not None and wt.size:
+            tail_mass[b, :wt.size, kvh] += wt
+        hp.mass[b, kvh] += wh
+
+
 def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, heads=None, proxy=False,
-           tail=None, dither=None):
+           tail=None, dither=None, hp: HPTier = None):
     """Decode step for q (B, Hq, D).  Returns {(b, h): decode_head(...)} for the requested
     (b, h) pairs (all by default).  tail = (tail_k, tail_v, tail_len): binary16 [B][cap][Hkv][D]
     keys and values and int [B] lengths of the uncompressed tokens after seq_lens[b].
-    dither: optional (B, Hq, D) uniforms in [0, 1) for stochastic rounding of the query codes."""
+    dither: optional (B, Hq, D) uniforms in [0, 1) for stochastic rounding of the query codes.
+    hp: the high-precision tier, whose valid entries of the head's KV head are attended like
+    tail tokens after them; each result then holds w_tail_only (the tail tokens' weights) and
+    w_hp [C] (the entries' weights, 0 for empty entries)."""
     q = np.asarray(q, dtype=np.float32)
     B, Hq, D = q.shape
     if heads is None:
@@ -406,9 +485,22 @@ def decode(cache: PagedCache, rot: Rotation, q, seq_lens, page_table, top_p, hea
     out = {}
     for (b, h) in heads:
         th = None
+        kvh = h * cache.Hkv // Hq
+        nt = 0
         if tail is not None:
-            n, kvh = int(tail[2][b]), h * cache.Hkv // Hq
-            th = (np.asarray(tail[0])[b, :n, kvh], np.asarray(tail[1])[b, :n, kvh])
+            nt = int(tail[2][b])
+            th = (np.asarray(tail[0])[b, :nt, kvh], np.asarray(tail[1])[b, :nt, kvh])
+        if hp is not None:
+            live = np.nonzero(hp.pos[b, kvh] >= 0)[0]
+            tk_ = np.zeros((0, D), np.float16) if th is None else th[0]
+            tv_ = np.zeros((0, D), np.float16) if th is None else th[1]
+            th = (np.concatenate([tk_, hp.k16[b, kvh, live]]), np.concatenate([tv_, hp.v16[b, kvh, live]]))
         dh = None if dither is None else np.asarray(dither, dtype=np.float32)[b, h]
-        out[(b, h)] = decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy, th, dh)
+        r = decode_head(cache, rot, q[b, h], b, h, Hq, int(seq_lens[b]), page_table, top_p, proxy, th, dh)
+        if hp is not None:
+            w = r["w_tail"]
+            r["w_tail_only"] = w[:nt]
+            r["w_hp"] = np.zeros(hp.C)
+            r["w_hp"][live] = w[nt:]
+        out[(b, h)] = r
     return out

@@ -367,7 +367,10 @@ static uint64_t bin_weight(const uint64_t *T, int64_t d)
  *   S   = { i : d_i <= b* }, returned as ascending indices.
  * S is the smallest prefix of bins, heaviest first, whose weight reaches the fraction p of
  * the total: the textbook nucleus, at a resolution of 2^(1/256) in weight.  Whole bins are
- * kept, so equal scores are kept or dropped together.  Returns |S|; sel_idx may be NULL. */
+ * kept, so equal scores are kept or dropped together.  When e_max is the bottom bin itself
+ * (every score NaN, or below -2^29 / kbin), no token has weight and S is empty (b* = -1):
+ * NaN scores mark records that the cache holds elsewhere.  Returns |S|; sel_idx may be
+ * NULL. */
 int64_t orc_topp(int D, const float *s, int64_t L, float p, int32_t *sel_idx,
                  int32_t *emax_out, int32_t *bstar_out, uint64_t *Z_out, uint64_t *Tp_out)
 {
@@ -379,6 +382,13 @@ int64_t orc_topp(int D, const float *s, int64_t L, float p, int32_t *sel_idx,
     for (int64_t i = 1; i < L; ++i) {
         int32_t e = orc_bin(s[i], kb);
         if (e > emax) emax = e;
+    }
+    if (emax == -ORC_BIN_CLAMP) {
+        if (emax_out) *emax_out = emax;
+        if (bstar_out) *bstar_out = -1;
+        if (Z_out) *Z_out = 0;
+        if (Tp_out) *Tp_out = 0;
+        return 0;
     }
     /* count of tokens per bin distance d < 8192 */
     uint64_t *cnt = (uint64_t *)calloc(ORC_NBINS, sizeof(uint64_t));

@@ -134,7 +134,7 @@ def _decode_tail(tail, desc=None, B=2, Hq=32, max_seq_len=1000, max_pages=4, top
 @pytest.mark.parametrize("kw", [dict(k=None), dict(v=None), dict(len=None), dict(capacity=0),
                                 dict(k=0x10008)])
 def test_bad_tail_descriptor(kw):
-    d = dict(k=0x10000, v=0x10000, len=0x10000, capacity=256)
+    d = dict(k=0x10000, v=0x10000, len=0x10000, capacity=256, mass=None)
     d.update(kw)
     tail = L.KVTailDesc(*[d[f] for f, _ in L.KVTailDesc._fields_])
     assert _decode_tail(tail) == L.KV_ERR_ARG
@@ -156,13 +156,53 @@ def _decode_ex(opts, desc=None, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p
 def test_decode_ex_rejects_bad_options():
     """kv_decode_attend_ex: a misaligned dither, an invalid tail in the options and a bad
     cache descriptor are errors caught on the host."""
-    assert _decode_ex(L.KVDecodeOpts(None, 0x10002)) == L.KV_ERR_ARG
+    assert _decode_ex(L.KVDecodeOpts(None, 0x10002, None)) == L.KV_ERR_ARG
     assert "q_dither" in L.last_error()
-    bad_tail = L.KVTailDesc(0x10000, 0x10000, None, 256)
-    assert _decode_ex(L.KVDecodeOpts(ctypes.pointer(bad_tail), None)) == L.KV_ERR_ARG
-    assert _decode_ex(L.KVDecodeOpts(None, None), desc=_desc(head_dim=64)) == L.KV_ERR_UNSUPPORTED
-    assert _decode_ex(L.KVDecodeOpts(None, None), B=0) == L.KV_ERR_ARG
+    bad_tail = L.KVTailDesc(0x10000, 0x10000, None, 256, None)
+    assert _decode_ex(L.KVDecodeOpts(ctypes.pointer(bad_tail), None, None)) == L.KV_ERR_ARG
+    assert _decode_ex(L.KVDecodeOpts(None, None, None), desc=_desc(head_dim=64)) == L.KV_ERR_UNSUPPORTED
+    assert _decode_ex(L.KVDecodeOpts(None, None, None), B=0) == L.KV_ERR_ARG
     rc = L.lib().kv_decode_attend_ex(None, None, FAKE, 2, 32, FAKE, 1000, FAKE, 4, 1.0, FAKE, None, FAKE, 1 << 30,
                                      None)
     assert rc == L.KV_ERR_ARG
+
+
+def _hp(**kw):
+    d = dict(k=0x10000, v=0x10000, pos=0x10000, saved=0x10000, mass=0x10000, capacity=64)
+    d.update(kw)
+    return L.KVHpDesc(*[d[f] for f, _ in L.KVHpDesc._fields_])
+
+
+@pytest.mark.parametrize("kw", [dict(k=None), dict(pos=None), dict(saved=None), dict(mass=None),
+                                dict(capacity=0), dict(capacity=1025), dict(v=0x10008), dict(mass=0x10002)])
+def test_bad_tier_descriptor(kw):
+    assert _decode_ex(L.KVDecodeOpts(None, None, ctypes.pointer(_hp(**kw)))) == L.KV_ERR_ARG
+    assert L.last_error()
+
+
+def test_tier_with_tail_needs_the_tail_mass():
+    tail = L.KVTailDesc(0x10000, 0x10000, 0x10000, 256, None)
+    assert _decode_ex(L.KVDecodeOpts(ctypes.pointer(tail), None, ctypes.pointer(_hp()))) == L.KV_ERR_ARG
+    assert "mass" in L.last_error()
+
+
+def test_hp_update_rejects_bad_arguments():
+    lib = L.lib()
+    tail = L.KVTailDesc(0x10000, 0x10000, 0x10000, 256, 0x10000)
+    nomass = L.KVTailDesc(0x10000, 0x10000, 0x10000, 256, None)
+    d, hp = _desc(), _hp()
+
+    def upd(desc=d, h=hp, t=tail, B=2, n=256, seq=FAKE, pt=FAKE, mp=4):
+        return lib.kv_hp_update(ctypes.byref(desc) if desc is not None else None,
+                                ctypes.byref(h) if h is not None else None, ctypes.byref(t) if t is not None else None,
+                                B, n, seq, pt, mp, None)
+    assert upd(h=None) == L.KV_ERR_ARG
+    assert upd(t=None) == L.KV_ERR_ARG
+    assert upd(t=nomass) == L.KV_ERR_ARG
+    assert upd(n=257) == L.KV_ERR_ARG                      # more than the tail holds
+    assert upd(h=_hp(capacity=900), n=200) == L.KV_ERR_ARG  # more than 1024 candidates
+    assert upd(seq=None) == L.KV_ERR_ARG
+    assert upd(mp=0) == L.KV_ERR_ARG
+    assert upd(desc=_desc(value_group=16)) == L.KV_ERR_UNSUPPORTED
+    assert upd(n=0) == L.KV_OK
 
