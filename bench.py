@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--lazy", action="store_true",
                     help="lazy updates: new tokens go to a binary16 tail, whole pages are compressed on a "
                          "second stream; times one page cycle (steps default to the page size)")
+    ap.add_argument("--hp-capacity", type=int, default=0, metavar="C",
+                    help="with --lazy: a high-precision tier of C binary16 entries per (sequence, KV head), "
+                         "filled at each page compression by accumulated attention mass")
     ap.add_argument("--center-keys", action="store_true",
                     help="estimator variant: per-head key centers (the mean of the prefill keys)")
     ap.add_argument("--stochastic-query", action="store_true",
@@ -110,8 +113,10 @@ def run_lazy(args):
     pt = torch.from_numpy(pt_np).to(dev)
     kvc.append(cache, K[:, :Lc0].to(kvt).contiguous(), V[:, :Lc0].to(kvt).contiguous(),
                torch.zeros(B, dtype=torch.int32, device=dev), pt)
-    tail = kvc.Tail(B, 2 * P, Hkv, dev)
+    C = args.hp_capacity
+    tail = kvc.Tail(B, 2 * P, Hkv, dev, mass=C > 0)
     tail.append(K[:, Lc0:].to(kvt).contiguous(), V[:, Lc0:].to(kvt).contiguous())
+    hp = kvc.HPTier(B, C, Hkv, dev) if C > 0 else None
     del K, V
     seq = torch.full((B,), Lc0, dtype=torch.int32, device=dev)
     Lmax = L + total
@@ -141,11 +146,14 @@ def run_lazy(args):
             st["compressions"] += 1
         if st["pending"] is not None and i == st["pending"][1]:
             torch.cuda.current_stream().wait_event(st["pending"][0])
+            if hp is not None:
+                hp.update(cache, tail, P, seq, pt)
             tail.retire(P, seq)
             st["lc"] += P
             st["nt"] -= P
             st["pending"] = None
-        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=st["lc"], out=out, workspace=ws, tail=tail)
+        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=st["lc"], out=out, workspace=ws, tail=tail,
+                          hp=hp)
 
     for i in range(args.warmup):
         flush_buf.sum()
@@ -166,6 +174,8 @@ def run_lazy(args):
     step_ms = [a.elapsed_time(b) for a, b in ev]
     ms = statistics.mean(step_ms)
     value = statistics.mean(t * B * Hkv for t in toks) / (ms / 1e3)
+    if hp is not None:
+        log(f"[bench] tier: {int((hp.pos >= 0).sum())} entries filled, mass {float(hp.mass.sum()):.2f}")
     log(f"[bench] lazy step {ms * 1e3:.1f} us (median {statistics.median(step_ms) * 1e3:.1f}, "
         f"max {max(step_ms) * 1e3:.1f}); {value:.3e} KV token-heads/s; "
         f"{st['compressions'] - c0} page compressions on the second stream")
@@ -175,7 +185,7 @@ def run_lazy(args):
         "vs_baseline": None, "dtype": "i32 (1-bit x int4 popcount) + f32", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": L,
                    "head_dim": D, "top_p": wl.top_p, "value_group": Gv, "page_size": P, "rotation": wl.rot,
-                   "kv_dtype": wl.kv_dtype, "lazy": True, "tail_tokens_at_start": T0,
+                   "kv_dtype": wl.kv_dtype, "lazy": True, "tail_tokens_at_start": T0, "hp_capacity": C,
                    "step": "append 1 token per sequence to the binary16 tail + decode over cache and tail; "
                            "a full page compressed on a second stream",
                    "cache_flushed_between_steps": True},

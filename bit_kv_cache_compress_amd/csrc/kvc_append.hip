@@ -504,6 +504,7 @@ __global__ __launch_bounds__(256) void k_hp_update(HpUpdateParams p)
         const float mi = cm[i];
         const int pi = cp[i];
         int r = 0;
+#pragma unroll 8
         for (int k = 0; k < m; ++k) {
             const float mk = cm[k];
             const int pk = cp[k];

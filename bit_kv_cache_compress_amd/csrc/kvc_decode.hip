@@ -70,14 +70,13 @@ struct SumI { __device__ int operator()(int a, int b) const { return a + b; } };
 
 // ---------------------------------------------------------------------------------------
 // Exact attention over the binary16 tail (lazy updates) for query head h of sequence b, by
-// a 128-thread block.  A pass covers 128 tail tokens: thread t scores token t (<q, k> as a
-// binary32 fma chain over the 128 dims) while thread (dg, ts) = (t mod 16, t / 16) already
-// holds the values of dims 8 dg .. 8 dg + 7 of tokens ts + 8 i, i < 16, so that every load
-// of the pass is in flight at once.  The block takes the max and the weights
-// exp2((s - m) log2e / sqrt(D)) with a running max over passes; thread (dg, ts) sums its 16
-// weighted values, and the 8 token slices are added at the end.  The entries of the
-// high-precision tier (KV head of h) follow the tail as a second segment, empty entries
-// with weight 0.  With key centers the scores are <q, k> - <q, c> (the frame of the
+// a 256-thread block.  The tail tokens and then the entries of the high-precision tier (KV
+// head of h; empty entries with weight 0) form one index space.  A pass covers 256 of them:
+// thread t scores token t (<q, k> as a binary32 fma chain over the 128 dims) while thread
+// (dg, ts) = (t mod 16, t / 16) already holds the values of dims 8 dg .. 8 dg + 7 of tokens
+// ts + 16 i, i < 16, so that every load of the pass is in flight at once.  The block takes
+// the max and the weights exp2((s - m) log2e / sqrt(D)) with a running max over passes;
+// thread (dg, ts) sums its 16 weighted values, and the 16 token slices are added at the end.  With key centers the scores are <q, k> - <q, c> (the frame of the
 // centered proxy scores).  Writes the partial
 // (m, l, o[128]) that the merge adds to the chunk partials (m = -inf and zeros for an
 // empty tail).
@@ -116,75 +115,85 @@ __device__ __forceinline__ float center_dot(const float *center, int kvh, const 
 
 __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 {
-    constexpr int T = 128, NS = T / 16, NV = T / NS;  // tokens per pass, token slices, values per thread
+    constexpr int T = 256, NS = T / 16, NV = T / NS;  // tokens per pass, token slices, values per thread
+    constexpr int NW = T / 64;
     __shared__ float qs[kD];
     __shared__ float ws[T];
     __shared__ float part[NS][kD];
-    __shared__ float red[2][2];
+    __shared__ float red[2][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = bh / p.Hq, h = bh - b * p.Hq, kvh = h / p.G;
-    qs[tid] = p.q[(size_t)bh * kD + tid];
+    if (tid < kD) qs[tid] = p.q[(size_t)bh * kD + tid];
     __syncthreads();
     // centered cache: exact scores move to the same frame, <q, k> - <q, c>
     const float qc = p.center ? center_dot(p.center, kvh, qs, red[0]) : 0.0f;
     const int dg = tid & 15, ts = tid >> 4;
+    // one index space: tail tokens 0 .. nt-1, then the tier entries of this KV head
+    const int nt = p.k ? min(max(p.len[b], 0), p.cap) : 0;
+    const int nh = p.hk ? p.hcap : 0;
+    const int ntot = nt + nh;
+    const size_t trow = (size_t)p.Hkv * kD;
+    const uint16_t *tk = p.k ? p.k + ((size_t)b * p.cap * p.Hkv + kvh) * kD : nullptr;
+    const uint16_t *tv = p.v ? p.v + ((size_t)b * p.cap * p.Hkv + kvh) * kD : nullptr;
+    const size_t e0 = ((size_t)b * p.Hkv + kvh) * p.hcap;
+    const uint16_t *hk = p.hk ? p.hk + e0 * kD : nullptr;
+    const uint16_t *hv = p.hv ? p.hv + e0 * kD : nullptr;
     float m = -INFINITY, l = 0.0f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.0f;
-
-    // one segment of n binary16 tokens, row elements apart (pos: nullable, < 0 = empty entry)
-    auto segment = [&](const uint16_t *kb, const uint16_t *vb, size_t row, int n, const int32_t *pos) {
-        for (int t0 = 0; t0 < n; t0 += T) {
-            uint4 vr[NV];
+    for (int t0 = 0; t0 < ntot; t0 += T) {
+        uint4 vr[NV];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int t = t0 + ts + NS * i;
-                vr[i] = t < n ? *reinterpret_cast<const uint4 *>(vb + t * row + 8 * dg) : make_uint4(0u, 0u, 0u, 0u);
-            }
-            const int t = t0 + tid;
-            const bool valid = t < n && (!pos || pos[t] >= 0);
-            const float s = valid ? exact_dot(kb + t * row, qs) - qc : -INFINITY;
-            const float wm = wave_max(s);
-            if (lane == 0) red[0][wave] = wm;
-            __syncthreads();
-            const float mnew = fmaxf(m, fmaxf(red[0][0], red[0][1]));
-            const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
-            const float w = valid ? exp2f((s - mnew) * p.klog) : 0.0f;
-            ws[tid] = w;
-            const float wsum = wave_sum(w);
-            if (lane == 0) red[1][wave] = wsum;
-            __syncthreads();
-            l = l * scale + (red[1][0] + red[1][1]);
-            m = mnew;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= scale;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const float wi = ws[ts + NS * i];
-                const uint32_t keep = wi != 0.0f ? 0xFFFFFFFFu : 0u;  // empty entries hold anything
-                const uint32_t x[4] = {vr[i].x & keep, vr[i].y & keep, vr[i].z & keep, vr[i].w & keep};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    o[e] = fmaf(wi, half_bits_to_float((x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), o[e]);
-            }
-            __syncthreads();  // ws and red are rewritten by the next pass
+        for (int i = 0; i < NV; ++i) {
+            const int u = t0 + ts + NS * i;
+            const uint16_t *vp = u < nt ? tv + u * trow : hv + (size_t)(u - nt) * kD;
+            vr[i] = u < ntot ? *reinterpret_cast<const uint4 *>(vp + 8 * dg) : make_uint4(0u, 0u, 0u, 0u);
         }
-    };
-    if (p.k) {
-        const size_t base = ((size_t)b * p.cap * p.Hkv + kvh) * kD;
-        segment(p.k + base, p.v + base, (size_t)p.Hkv * kD, min(max(p.len[b], 0), p.cap), nullptr);
-    }
-    if (p.hk) {
-        const size_t e0 = ((size_t)b * p.Hkv + kvh) * p.hcap;
-        segment(p.hk + e0 * kD, p.hv + e0 * kD, (size_t)kD, p.hcap, p.hpos + e0);
+        const int u = t0 + tid;
+        // empty tier entries are read like the others (the arrays are whole) and masked after,
+        // so that the key loads do not wait for the position load
+        float s = -INFINITY;
+        if (u < ntot) s = exact_dot(u < nt ? tk + u * trow : hk + (size_t)(u - nt) * kD, qs) - qc;
+        if (u >= nt && (u >= ntot || p.hpos[e0 + (u - nt)] < 0)) s = -INFINITY;
+        const float wm = wave_max(s);
+        if (lane == 0) red[0][wave] = wm;
+        __syncthreads();
+        float mnew = m;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mnew = fmaxf(mnew, red[0][w]);
+        const float scale = (m == -INFINITY) ? 0.0f : exp2f((m - mnew) * p.klog);
+        const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
+        ws[tid] = w;
+        const float wsum = wave_sum(w);
+        if (lane == 0) red[1][wave] = wsum;
+        __syncthreads();
+        float lsum = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) lsum += red[1][w2];
+        l = l * scale + lsum;
+        m = mnew;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= scale;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float wi = ws[ts + NS * i];
+            const uint32_t keep = wi != 0.0f ? 0xFFFFFFFFu : 0u;  // empty entries hold anything
+            const uint32_t x[4] = {vr[i].x & keep, vr[i].y & keep, vr[i].z & keep, vr[i].w & keep};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e] = fmaf(wi, half_bits_to_float((x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), o[e]);
+        }
+        __syncthreads();  // ws and red are rewritten by the next pass
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[ts][8 * dg + e] = o[e];
     __syncthreads();
-    float acc = 0.0f;
+    if (tid < kD) {
+        float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) acc += part[j][tid];
-    p.to[(size_t)bh * kD + tid] = acc;
+        for (int j = 0; j < NS; ++j) acc += part[j][tid];
+        p.to[(size_t)bh * kD + tid] = acc;
+    }
     if (tid == 0) {
         p.tm[bh] = m;
         p.tl[bh] = l;
@@ -192,8 +201,9 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 }
 
 // ---------------------------------------------------------------------------------------
-// Query preparation (one 128-thread block per (sequence, query head), one thread per dim;
-// with a tail, blocks BH .. 2 BH - 1 run the tail attention of the same heads alongside):
+// Query preparation (one block per (sequence, query head), one thread per dim; with a tail,
+// blocks BH .. 2 BH - 1 run the tail attention of the same heads alongside, and all blocks
+// have 256 threads, of which the query preparation uses the first 128):
 //   dense:    q'_r = fmaf chain over j ascending of R[r][j] * q_j (binary32)
 //   hadamard: x = sigma * q, in-place fast Walsh-Hadamard butterflies h = 1..64 (binary32),
 //             q' = x * fp32(1/sqrt(D))
@@ -202,7 +212,7 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 //   caller's uniform U under stochastic rounding; the codes in dot8 order; c0 = v_l/sqrt(D),
 //   c1 = delta/sqrt(D).
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
+__global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
 {
     __shared__ float xs[kD];
     __shared__ int us[kD];
@@ -212,6 +222,7 @@ __global__ __launch_bounds__(128) void k_qprep(QprepParams p, float isd)
         tail_attend(p.tail, (int)blockIdx.x - p.BH);
         return;
     }
+    if (threadIdx.x >= kD) return;  // whole waves: blocks of 256 threads when a tail runs alongside
     const int bh = blockIdx.x, r = threadIdx.x;
     const int lane = r & 63, wave = r >> 6;
     const float *q = p.q + (size_t)bh * kD;
@@ -1396,54 +1407,83 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 // ---------------------------------------------------------------------------------------
 // Attention mass of the tail tokens and the high-precision tier, once the query head's
 // softmax is known (max score M, weight sum D): every such token adds its weight
-// exp2((s - M) log2e / sqrt(D)) / D, with its exact score s recomputed (16 lanes per token,
-// 8 dims each, so the rounding may differ from the tail pass in the last bits), to its
-// mass; the query heads of a KV head add atomically.
+// exp2((s - M) log2e / sqrt(D)) / D to its mass, with its exact score s recomputed by a
+// group of 16 lanes (8 dims each, so the rounding may differ from the tail pass in the last
+// bits); the query heads of a KV head add atomically.  The first round's loads (query,
+// center, key words, entry positions) are issued when the merge starts, so that they are
+// done by the time M and D are.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void merge_mass(const MassParams &p, int b, int h, int G, int Hkv, float M, float D,
-                                           float klog)
+constexpr int kMassNU = 4;  // tokens per 16-lane group and round
+
+struct MassPrefetch {
+    float qx[8], cx[8];
+    uint4 kw[kMassNU];
+    bool ok[kMassNU];
+    int nt, ntot;
+};
+
+__device__ __forceinline__ const uint16_t *mass_key(const MassParams &p, int b, int kvh, int Hkv, int nt, int j)
 {
-    __shared__ float qs[kD];
-    __shared__ float red2[2];
-    const int tid = threadIdx.x, kvh = h / G;
+    return j < nt ? p.tk + (((size_t)b * p.tcap + j) * Hkv + kvh) * kD
+                  : p.hk + (((size_t)b * Hkv + kvh) * p.hcap + (j - nt)) * kD;
+}
+
+__device__ __forceinline__ void mass_round_load(const MassParams &p, int b, int kvh, int Hkv, int j0, MassPrefetch &f)
+{
+    const int tid = threadIdx.x, step = (int)blockDim.x >> 4, sub = tid & 15;
+#pragma unroll
+    for (int u = 0; u < kMassNU; ++u) {
+        const int j = j0 + u * step + (tid >> 4);
+        f.ok[u] = j < f.ntot && (j < f.nt || p.hpos[((size_t)b * Hkv + kvh) * p.hcap + (j - f.nt)] >= 0);
+        f.kw[u] = j < f.ntot ? reinterpret_cast<const uint4 *>(mass_key(p, b, kvh, Hkv, f.nt, j))[sub]
+                             : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+__device__ __forceinline__ void mass_prefetch(const MassParams &p, int b, int h, int G, int Hkv, MassPrefetch &f)
+{
+    const int kvh = h / G, sub = threadIdx.x & 15;
     const size_t bh = (size_t)b * (G * Hkv) + h;
-    __syncthreads();
-    if (tid < kD) qs[tid] = p.q[bh * kD + tid];
-    __syncthreads();
-    const float qc = p.center ? center_dot(p.center, kvh, qs, red2) : 0.0f;
-    if (!(D > 0.0f)) return;
-    const float inv = 1.0f / D;
-    const int nt = p.tk ? min(max(p.tlen[b], 0), p.tcap) : 0;
-    const int nh = p.hk ? p.hcap : 0;
-    const size_t e0 = ((size_t)b * Hkv + kvh) * p.hcap;
-    // 16 lanes per token, lane sub holding dims 8 sub .. 8 sub + 7
-    const int sub = tid & 15;
-    float qx[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qx[e] = qs[8 * sub + e];
-    const int step = (int)blockDim.x >> 4;
-    const int ntot = nt + nh;
-    for (int j0 = 0; j0 < ntot; j0 += step) {  // the same trip count for every lane
-        const int j = j0 + (tid >> 4);
-        const uint16_t *k = nullptr;
-        float *dst = nullptr;
-        if (j < nt) {
-            k = p.tk + (((size_t)b * p.tcap + j) * Hkv + kvh) * kD;
-            dst = p.tmass + ((size_t)b * p.tcap + j) * Hkv + kvh;
-        } else if (j < ntot && p.hpos[e0 + (j - nt)] >= 0) {
-            k = p.hk + (e0 + (j - nt)) * kD;
-            dst = p.hmass + e0 + (j - nt);
+    for (int e = 0; e < 8; ++e) {
+        f.qx[e] = p.q[bh * kD + 8 * sub + e];  // q is only 4-byte aligned
+        f.cx[e] = p.center ? p.center[(size_t)kvh * kD + 8 * sub + e] : 0.0f;
+    }
+    f.nt = p.tk ? min(max(p.tlen[b], 0), p.tcap) : 0;
+    f.ntot = f.nt + (p.hk ? p.hcap : 0);
+    mass_round_load(p, b, kvh, Hkv, 0, f);
+}
+
+__device__ __forceinline__ void mass_finish(const MassParams &p, int b, int h, int G, int Hkv, float M, float D,
+                                            float klog, MassPrefetch &f)
+{
+    const int kvh = h / G, tid = threadIdx.x, sub = tid & 15, step = (int)blockDim.x >> 4;
+    // <q, c>: the 16-lane group's own sum over the 128 dims
+    float qc = 0.0f;
+    if (p.center) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qc = fmaf(f.qx[e], f.cx[e], qc);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) qc += __shfl_xor(qc, o);
+    }
+    const float inv = D > 0.0f ? 1.0f / D : 0.0f;
+    for (int j0 = 0; j0 < f.ntot; j0 += kMassNU * step) {  // the same trip count for every lane
+        if (j0 > 0) mass_round_load(p, b, kvh, Hkv, j0, f);
+#pragma unroll
+        for (int u = 0; u < kMassNU; ++u) {
+            const int j = j0 + u * step + (tid >> 4);
+            const uint32_t w[4] = {f.kw[u].x, f.kw[u].y, f.kw[u].z, f.kw[u].w};
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaf(f.qx[e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o);
+            if (f.ok[u] && sub == 0 && D > 0.0f) {
+                float *dst = j < f.nt ? p.tmass + ((size_t)b * p.tcap + j) * Hkv + kvh
+                                      : p.hmass + ((size_t)b * Hkv + kvh) * p.hcap + (j - f.nt);
+                atomicAdd(dst, exp2f((a - qc - M) * klog) * inv);
+            }
         }
-        float a = 0.0f;
-        if (k) {
-            const uint4 kw = reinterpret_cast<const uint4 *>(k)[sub];
-            const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = fmaf(qx[e], half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) a += __shfl_xor(a, o);
-        if (k && sub == 0) atomicAdd(dst, exp2f((a - qc - M) * klog) * inv);
     }
 }
 
@@ -1468,6 +1508,8 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     const int CHa = g.CH * g.KA;
     const int nch = L > 0 ? (L + CHa - 1) / CHa : 0;
     const int d = tid & (kD - 1), sl = tid >> 7;
+    MassPrefetch mf;
+    if (p.has_mass) mass_prefetch(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, mf);
     const float *po = p.po + bh * g.NCA * kD + d;
     float v[PF];
 #pragma unroll
@@ -1533,7 +1575,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
         for (int s2 = 0; s2 < NS; ++s2) t += part[s2][d];
         p.out[bh * kD + d] = D > 0.0f ? t / D : 0.0f;
     }
-    if (p.has_mass) merge_mass(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog);
+    if (p.has_mass) mass_finish(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog, mf);
 }
 
 }  // namespace
@@ -1544,7 +1586,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
 {
     const float isd = (float)(1.0 / sqrt((double)kD));
-    hipLaunchKernelGGL(k_qprep, dim3(p.has_tail ? 2 * p.BH : p.BH), dim3(128), 0, s, p, isd);
+    hipLaunchKernelGGL(k_qprep, dim3(p.has_tail ? 2 * p.BH : p.BH), dim3(p.has_tail ? 256 : 128), 0, s, p, isd);
     return hipGetLastError();
 }
 

@@ -540,3 +540,219 @@ def test_stochastic_query_rounding(name):
             continue
         assert rel_err(out[b, h], r["out"]) <= TOL, (b, h)
     _say(f"[dither] {name} tail ok")
+
+
+def _tier_case(c, lc, C, seed):
+    """An oracle cache copy with, per (sequence, KV head), up to 5 of its compressed tokens moved
+    into a high-precision tier of C entries (scattered slots), and the same state on the GPU."""
+    import copy
+
+    from bit_kv_cache_compress_amd import HPTier
+
+    rng = np.random.default_rng(seed)
+    B, Hkv, D = c.wl.B, c.wl.Hkv, c.wl.D
+    oc = copy.deepcopy(c.ocache)
+    hp = oracle.HPTier(B, Hkv, C, D)
+    slots = [1, 3, 4, 6, 7]
+    for b in range(B):
+        for h in range(Hkv):
+            n = min(5, int(lc[b]))
+            for i, t in enumerate(sorted(rng.choice(int(lc[b]), n, replace=False).tolist()) if n else []):
+                pg, sl = oc.locate(b, t, c.pt)
+                f = slots[i]
+                hp.saved[b, h, f] = oc.key_nc[pg, h, sl]
+                oc.key_nc[pg, h, sl] = oracle.HPTier.MARKER
+                hp.pos[b, h, f] = t
+                hp.k16[b, h, f] = c.K[b, t, h].astype(np.float16)
+                hp.v16[b, h, f] = c.V[b, t, h].astype(np.float16)
+    dev = torch.device("cuda")
+    g = upload(oc, c)
+    hg = HPTier(B, C, Hkv, dev)
+    hg.k.copy_(torch.from_numpy(hp.k16))
+    hg.v.copy_(torch.from_numpy(hp.v16))
+    hg.pos.copy_(torch.from_numpy(hp.pos.astype(np.int32)))
+    hg.saved.copy_(torch.from_numpy(hp.saved.view(np.int32)))
+    return oc, hp, g, hg
+
+
+@pytest.mark.parametrize("name", ["c2-outliers-ragged", "c3-gqa4-spikes-topp", "c4-paged-g64-ragged",
+                                  "c5-hadamard-topp"])
+def test_hp_tier_decode(name):
+    """Decode with the high-precision tier and a tail: outputs within the bar against the
+    oracle, and the masses the decode adds to tail tokens and tier entries within 1e-3
+    (relative) of the oracle's binary64 weights, summed over each KV head's query heads."""
+    from bit_kv_cache_compress_amd import decode_attend
+
+    c = _case(name)
+    dev = torch.device("cuda")
+    B, Hkv = c.wl.B, c.wl.Hkv
+    ntail = np.minimum(np.array([[0, 1, 100, 256][b % 4] for b in range(B)], np.int32), c.lens)
+    lc = (c.lens - ntail).astype(np.int32)
+    oc, hp, g, hg = _tier_case(c, lc, 8, 31)
+    tail, otail, _ = _tail_of(c, ntail, 256, dev)
+    from bit_kv_cache_compress_amd import Tail
+    tailm = Tail(B, 256, Hkv, dev, mass=True)
+    tailm.k.copy_(tail.k)
+    tailm.v.copy_(tail.v)
+    tailm.len.copy_(tail.len)
+    q = torch.from_numpy(c.q).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    lcd = torch.from_numpy(lc).to(dev)
+    for top_p in sorted({c.wl.top_p, 1.0}):
+        tailm.mass.zero_()
+        hg.mass.zero_()
+        hp.mass[:] = 0.0
+        _say(f"[tier] {name} top_p={top_p}")
+        out = decode_attend(g, q, lcd, pt, top_p=top_p, max_seq_len=c.max_len, tail=tailm, hp=hg)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        ref = oracle.decode(oc, c.orot, c.q, lc, c.pt, top_p, tail=otail, hp=hp)
+        worst = 0.0
+        for (b, h), r in ref.items():
+            if lc[b] + ntail[b] == 0 and not np.any(hp.pos[b] >= 0):
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (top_p, b, h, e)
+        tm = np.zeros((B, 256, Hkv))
+        oracle.add_mass(ref, tm, hp, c.wl.Hq)
+        gm = tailm.mass.cpu().numpy().astype(np.float64)
+        hm = hg.mass.cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(gm, tm, rtol=1e-3, atol=1e-7)
+        np.testing.assert_allclose(hm, hp.mass, rtol=1e-3, atol=1e-7)
+        assert hp.mass.sum() > 0
+        _say(f"[tier] {name} top_p={top_p} ok, worst rel err {worst:.2e}, tier mass {hp.mass.sum():.3f}")
+
+
+@pytest.mark.parametrize("name", ["c3-gqa4-spikes-topp", "c5-hadamard-topp"])
+def test_hp_tier_update(name):
+    """The promotion step against the oracle on caller-set masses (distinct values plus ties):
+    tier positions, saved words, masses, binary16 rows and every key record bit-exact."""
+    from bit_kv_cache_compress_amd import Tail
+
+    c = _case(name)
+    dev = torch.device("cuda")
+    B, Hkv, D, P = c.wl.B, c.wl.Hkv, c.wl.D, c.wl.P
+    n = min(P, 128)
+    lc = (c.lens - n).astype(np.int32)  # the last n tokens are the tail page just compressed
+    oc, hp, g, hg = _tier_case(c, lc, 16, 41)
+    rng = np.random.default_rng(42)
+    hp.mass[:] = np.where(hp.pos >= 0, rng.random(hp.pos.shape).astype(np.float32), 0.0)
+    tmass = rng.random((B, n, Hkv)).astype(np.float32) * 1.2
+    tmass[:, 5:9] = tmass[:, 4:5]  # ties at one mass
+    hg.mass.copy_(torch.from_numpy(hp.mass.astype(np.float32)))
+    tail = Tail(B, n, Hkv, dev, mass=True)
+    tk = np.stack([c.K[b, lc[b]:lc[b] + n] for b in range(B)]).astype(np.float16)
+    tv = np.stack([c.V[b, lc[b]:lc[b] + n] for b in range(B)]).astype(np.float16)
+    tail.k.copy_(torch.from_numpy(tk))
+    tail.v.copy_(torch.from_numpy(tv))
+    tail.len.fill_(n)
+    tail.mass.copy_(torch.from_numpy(tmass))
+    seq = torch.from_numpy(lc).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    hg.update(g, tail, n, seq, pt)
+    torch.cuda.synchronize()
+    oracle.hp_update(oc, hp, tk, tv, tmass, n, lc, c.pt)
+    np.testing.assert_array_equal(hg.pos.cpu().numpy(), hp.pos.astype(np.int32))
+    live = hp.pos >= 0
+    np.testing.assert_array_equal(hg.saved.cpu().numpy().view(np.uint32)[live], hp.saved[live])
+    np.testing.assert_array_equal(hg.mass.cpu().numpy()[live], hp.mass[live].astype(np.float32))
+    np.testing.assert_array_equal(hg.k.cpu().numpy()[live].view(np.uint16), hp.k16[live].view(np.uint16))
+    np.testing.assert_array_equal(hg.v.cpu().numpy()[live].view(np.uint16), hp.v16[live].view(np.uint16))
+    np.testing.assert_array_equal(g.key_nc.cpu().numpy().view(np.uint32), oc.key_nc)
+    np.testing.assert_array_equal(g.key_bits.cpu().numpy().view(np.uint32), oc.key_bits)
+    entered = int(((hp.pos >= lc[:, None, None]) & live).sum())
+    _say(f"[tier-update] {name} ok: {int(live.sum())} entries, {entered} entered from the tail")
+    assert entered > 0
+
+
+def test_hp_tier_pipeline():
+    """Lazy updates with the high-precision tier: one token per step into the tail, a page
+    compressed on a second stream, then the promotion and the retire; every 16th step's output
+    against the oracle holding the same state (its own binary64 masses).  After each
+    promotion the tier sets are compared; a different choice must still be valid under the
+    oracle's masses (a near-tie decided by binary32 atomics), and ends the output checks."""
+    from bit_kv_cache_compress_amd import HPTier, Tail, append, decode_attend
+
+    c = _case("c3-gqa4-spikes-topp")
+    dev = torch.device("cuda")
+    B, Hkv, D, P, Hq = c.wl.B, c.wl.Hkv, c.wl.D, c.wl.P, c.wl.Hq
+    C = 16
+    L0 = 2 * P + 5
+    steps = 2 * P + 9
+    assert L0 + steps <= c.L
+    ocache = oracle.PagedCache(c.npages, Hkv, P, D, c.wl.Gv)
+    oracle.append(ocache, c.orot, c.K[:, :L0], c.V[:, :L0], np.zeros(B, np.int32), c.pt)
+    g = upload(ocache, c)
+    tail = Tail(B, 2 * P, Hkv, dev, mass=True)
+    hg = HPTier(B, C, Hkv, dev)
+    hp = oracle.HPTier(B, Hkv, C, D)
+    tmass = np.zeros((B, 2 * P, Hkv))
+    seq = torch.full((B,), L0, dtype=torch.int32, device=dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    q = torch.from_numpy(c.q).to(dev)
+    side = torch.cuda.Stream()
+    lc, nt, pending, comparing, promotions = L0, 0, None, True, 0
+    for s in range(steps):
+        t = L0 + s
+        tail.append(torch.from_numpy(np.ascontiguousarray(c.K[:, t:t + 1])).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(c.V[:, t:t + 1])).to(dev))
+        tmass[:, nt] = 0.0
+        nt += 1
+        if nt == P + 1 and pending is None:
+            ev = torch.cuda.Event()
+            ev.record()
+            side.wait_event(ev)
+            with torch.cuda.stream(side):
+                for b in range(B):
+                    kb, vb = tail.page(b, 0, P)
+                    append(g, kb, vb, torch.tensor([lc], dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+                done = torch.cuda.Event()
+                done.record()
+            pending = (done, s + 4)
+        if pending is not None and s == pending[1]:
+            torch.cuda.current_stream().wait_event(pending[0])
+            hg.update(g, tail, P, seq, pt)
+            tail.retire(P, seq)
+            if comparing:
+                oracle.append(ocache, c.orot, c.K[:, lc:lc + P], c.V[:, lc:lc + P], np.full(B, lc, np.int32), c.pt)
+                tk = c.K[:, lc:lc + P].astype(np.float16)
+                tv = c.V[:, lc:lc + P].astype(np.float16)
+                before = {(b, h): ({int(p): hp.mass[b, h, i] for i, p in enumerate(hp.pos[b, h]) if p >= 0},
+                                   {lc + j: tmass[b, j, h] for j in range(P)}) for b in range(B) for h in range(Hkv)}
+                oracle.hp_update(ocache, hp, tk, tv, tmass, P, np.full(B, lc, np.int32), c.pt)
+                torch.cuda.synchronize()
+                gpos = hg.pos.cpu().numpy()
+                for b in range(B):
+                    for h in range(Hkv):
+                        want = {int(p) for p in hp.pos[b, h] if p >= 0}
+                        got = {int(p) for p in gpos[b, h] if p >= 0}
+                        if got != want:
+                            allm = dict(before[(b, h)][0])
+                            allm.update(before[(b, h)][1])
+                            kth = sorted(allm.values(), reverse=True)[C - 1]
+                            tol = 1e-3 * max(allm.values())
+                            assert all(allm[p] >= kth - tol for p in got), (b, h)
+                            comparing = False
+                tmass = np.concatenate([tmass[:, P:], np.zeros_like(tmass[:, :P])], axis=1)
+                promotions += 1
+            lc, nt, pending = lc + P, nt - P, None
+        out = decode_attend(g, q, seq, pt, top_p=c.wl.top_p, max_seq_len=c.L, tail=tail, hp=hg)
+        if comparing:
+            tk = np.zeros((B, 2 * P, Hkv, D), np.float16)
+            tv = np.zeros_like(tk)
+            tk[:, :nt] = c.K[:, lc:lc + nt].astype(np.float16)
+            tv[:, :nt] = c.V[:, lc:lc + nt].astype(np.float16)
+            ref = oracle.decode(ocache, c.orot, c.q, np.full(B, lc, np.int32), c.pt, c.wl.top_p,
+                                tail=(tk, tv, np.full(B, nt, np.int32)), hp=hp)
+            oracle.add_mass(ref, tmass, hp, Hq)
+            if s % 16 == 0 or s == steps - 1:
+                o = out.cpu().numpy()
+                for (b, h), r in ref.items():
+                    assert rel_err(o[b, h], r["out"]) <= TOL, (s, b, h)
+                _say(f"[tier-lazy] step {s}: {lc} compressed + {nt} tail tokens, "
+                     f"{int((hp.pos >= 0).sum())} tier entries ok")
+    assert promotions >= 1
+    torch.cuda.synchronize()
+    _say(f"[tier-lazy] done, compared through the end: {comparing}")
