@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--hp-capacity", type=int, default=0, metavar="C",
                     help="with --lazy: a high-precision tier of C binary16 entries per (sequence, KV head), "
                          "filled at each page compression by accumulated attention mass")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append the step's new tokens with a call of their own instead of inside the decode")
     ap.add_argument("--center-keys", action="store_true",
                     help="estimator variant: per-head key centers (the mean of the prefill keys)")
     ap.add_argument("--stochastic-query", action="store_true",
@@ -278,9 +280,13 @@ def main():
         f"workspace {ws.numel() / 2**20:.1f} MiB")
 
     def step(dbg=None):
-        kvc.append(cache, k_new, v_new, start, pt)
-        kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
-                          debug_struct=dbg, q_dither=dither)
+        if args.separate_append:
+            kvc.append(cache, k_new, v_new, start, pt)
+            kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
+                              debug_struct=dbg, q_dither=dither)
+        else:  # the new tokens' encoding rides in the decode's first launch
+            kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
+                              debug_struct=dbg, q_dither=dither, append=(k_new, v_new, start))
 
     if args.profile_steps:
         for _ in range(args.profile_steps):
@@ -325,10 +331,12 @@ def main():
         if not args.no_flush:
             flush()
         aev[i][0].record()
-        kvc.append(cache, k_new, v_new, start, pt)
+        if args.separate_append:
+            kvc.append(cache, k_new, v_new, start, pt)
         aev[i][1].record()
         kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, out=out, workspace=ws,
-                          debug_struct=timers[i].struct(), q_dither=dither)
+                          debug_struct=timers[i].struct(), q_dither=dither,
+                          append=None if args.separate_append else (k_new, v_new, start))
     torch.cuda.synchronize()
     stage_ms = {}
     ran = ("query", "score", "hist", "attend", "merge") if wl.top_p < 1.0 else ("query", "attend", "merge")
@@ -336,7 +344,8 @@ def main():
         for k, v in t.elapsed_ms(ran).items():
             stage_ms.setdefault(k, []).append(v)
     stage_ms = {k: statistics.mean(v) for k, v in stage_ms.items()}
-    stage_ms["append"] = statistics.mean(a.elapsed_time(b) for a, b in aev)
+    if args.separate_append:
+        stage_ms["append"] = statistics.mean(a.elapsed_time(b) for a, b in aev)
     log("[bench] stages (us): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in stage_ms.items()))
 
     # ---- selection statistics (one untimed debug decode)
@@ -405,7 +414,9 @@ def main():
         "vs_baseline": None, "dtype": "i32 (1-bit x int4 popcount) + f32", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": Lmax,
                    "head_dim": D, "top_p": wl.top_p, "value_group": Gv, "page_size": P, "rotation": wl.rot,
-                   "kv_dtype": wl.kv_dtype, "step": "append 1 token per sequence + decode attention",
+                   "kv_dtype": wl.kv_dtype,
+                   "step": "append 1 token per sequence + decode attention"
+                           + (" (two calls)" if args.separate_append else " (one call, fused append)"),
                    "cache_flushed_between_steps": not args.no_flush, "exact_keys": args.exact_keys,
                    "key_center": args.center_keys, "stochastic_query": args.stochastic_query},
         "roofline": roofline,

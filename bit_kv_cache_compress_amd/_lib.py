@@ -72,11 +72,22 @@ class KVHpDesc(ctypes.Structure):
     ]
 
 
+class KVAppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("n_new", ctypes.c_int32),
+        ("start_pos", ctypes.c_void_p),
+    ]
+
+
 class KVDecodeOpts(ctypes.Structure):
     _fields_ = [
         ("tail", ctypes.POINTER(KVTailDesc)),
         ("q_dither", ctypes.c_void_p),
         ("hp", ctypes.POINTER(KVHpDesc)),
+        ("append", ctypes.POINTER(KVAppendArgs)),
     ]
 
 

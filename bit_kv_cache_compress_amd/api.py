@@ -119,19 +119,28 @@ class KVCache:
         return self.keys.numel() * 4 + self.vals.numel() + (0 if self.keys_f16 is None else self.keys_f16.numel() * 2)
 
 
-def append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, start_pos: torch.Tensor,
-           page_table: torch.Tensor) -> None:
-    """Encodes k, v [B, n_new, Hkv, 128] (float16 or float32) at positions start_pos[b] + i."""
+def _append_args(cache: KVCache, k: torch.Tensor, v: torch.Tensor, start_pos: torch.Tensor, B=None):
+    """Checks the new tokens of an append -> (dtype, k, v, n_new, start_pos) for the C ABI."""
     dev = cache.device
     if k.dim() != 4 or k.shape[2] != cache.num_kv_heads or k.shape[3] != HEAD_DIM:
         raise ValueError(f"k must be [B, n_new, {cache.num_kv_heads}, {HEAD_DIM}], got {tuple(k.shape)}")
+    if B is not None and k.shape[0] != B:
+        raise ValueError(f"k must have the decode's batch of {B}")
     dtype = {torch.float16: L.KV_F16, torch.float32: L.KV_F32}.get(k.dtype)
     if dtype is None:
         raise TypeError("k, v must be float16 or float32")
     _need(k, "k", k.dtype, dev)
     _need(v, "v", k.dtype, dev, k.shape)
-    B, n_new = int(k.shape[0]), int(k.shape[1])
-    _need(start_pos, "start_pos", torch.int32, dev, (B,))
+    _need(start_pos, "start_pos", torch.int32, dev, (int(k.shape[0]),))
+    return dtype, _ptr(k), _ptr(v), int(k.shape[1]), _ptr(start_pos)
+
+
+def append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, start_pos: torch.Tensor,
+           page_table: torch.Tensor) -> None:
+    """Encodes k, v [B, n_new, Hkv, 128] (float16 or float32) at positions start_pos[b] + i."""
+    dev = cache.device
+    dtype, _, _, n_new, _ = _append_args(cache, k, v, start_pos)
+    B = int(k.shape[0])
     _need(page_table, "page_table", torch.int32, dev)
     if page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError("page_table must be [B, max_pages]")
@@ -230,13 +239,15 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
                   workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
                   debug_struct: Optional[L.KVDebug] = None, proxy: bool = False,
                   tail: Optional["Tail"] = None, q_dither: Optional[torch.Tensor] = None,
-                  hp: Optional["HPTier"] = None) -> torch.Tensor:
+                  hp: Optional["HPTier"] = None, append: Optional[tuple] = None) -> torch.Tensor:
     """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32.  Under Top-p, a
     cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set.
     With ``tail``, each sequence's binary16 tail tokens follow its seq_lens compressed ones.
     ``q_dither`` (float32 [B, Hq, 128], uniforms in [0, 1)): stochastic rounding of the int4
     query codes, floor(t + U) instead of rint(t).  ``hp``: the high-precision tier, attended
-    exactly next to the tail; the tail (created with mass=True) and the tier accumulate mass."""
+    exactly next to the tail; the tail (created with mass=True) and the tier accumulate mass.
+    ``append`` = (k, v, start_pos): new tokens written into the cache first, as ``append``
+    would write them (seq_lens must count them), inside the decode's first launch."""
     dev = cache.device
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
@@ -264,12 +275,17 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
         raise ValueError(f"tail must be [{B}, capacity, {cache.num_kv_heads}, {HEAD_DIM}]")
     if hp is not None and (hp.B != B or hp.num_kv_heads != cache.num_kv_heads):
         raise ValueError(f"tier must be [{B}, {cache.num_kv_heads}, capacity]")
-    if q_dither is not None or hp is not None:
+    app = None
+    if append is not None:
+        ak, av, asp = append
+        app = L.KVAppendArgs(*_append_args(cache, ak, av, asp, B))
+    if q_dither is not None or hp is not None or app is not None:
         if q_dither is not None:
             _need(q_dither, "q_dither", torch.float32, dev, (B, Hq, HEAD_DIM))
         opts = L.KVDecodeOpts(ctypes.pointer(tail.desc) if tail is not None else None,
                               _ptr(q_dither) if q_dither is not None else None,
-                              ctypes.pointer(hp.desc) if hp is not None else None)
+                              ctypes.pointer(hp.desc) if hp is not None else None,
+                              ctypes.pointer(app) if app is not None else None)
         L.check(L.lib().kv_decode_attend_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), B, Hq, _ptr(seq_lens),
                                             int(max_seq_len), _ptr(page_table), max_pages, float(top_p), _ptr(out),
                                             dbg, _ptr(workspace), workspace.numel(), _stream(dev)))

@@ -241,20 +241,22 @@ const char *kv_last_error(void) { return g_err; }
 
 int kv_version(void) { return 10000; }
 
-int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const void *v, int32_t B,
-                       int32_t n_new, const int32_t *start_pos, const int32_t *page_table,
-                       int32_t max_pages, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments of an append (the cache already checked) and fills its parameters;
+// n_new == 0 gives KV_OK with p.n_new = 0.
+int make_append(const kv_cache *c, int32_t dtype, const void *k, const void *v, int32_t B, int32_t n_new,
+                const int32_t *start_pos, const int32_t *page_table, int32_t max_pages, kvc::AppendParams &p)
 {
-    g_err[0] = 0;
-    int rc = check_cache(c);
-    if (rc) return rc;
     if (dtype != KV_F16 && dtype != KV_F32) return fail(KV_ERR_ARG, "dtype %d is not KV_F16 or KV_F32", dtype);
     if (B <= 0 || n_new < 0 || max_pages <= 0)
         return fail(KV_ERR_ARG, "B and max_pages must be positive and n_new >= 0 (got %d, %d, %d)", B, n_new,
                     max_pages);
+    p.n_new = 0;
     if (n_new == 0) return KV_OK;
     if (!k || !v || !start_pos || !page_table) return fail(KV_ERR_ARG, "NULL k, v, start_pos or page_table");
-    kvc::AppendParams p;
     p.c = view_of(c);
     p.rot_kind = c->rot_kind;
     p.rot = c->rot;
@@ -266,6 +268,23 @@ int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const vo
     p.start_pos = start_pos;
     p.page_table = page_table;
     p.max_pages = max_pages;
+    return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const void *v, int32_t B,
+                       int32_t n_new, const int32_t *start_pos, const int32_t *page_table,
+                       int32_t max_pages, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_cache(c);
+    if (rc) return rc;
+    kvc::AppendParams p;
+    rc = make_append(c, dtype, k, v, B, n_new, start_pos, page_table, max_pages, p);
+    if (rc || p.n_new == 0) return rc;
     hipError_t e = kvc::launch_append(p, stream);
     if (e != hipSuccess) return hip_fail(e, "append launch");
     return KV_OK;
@@ -282,8 +301,8 @@ size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max
 
 namespace {
 
-int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const float *dither, const float *q,
-                int32_t B, int32_t Hq,
+int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const float *dither,
+                const kv_append_args *app, const float *q, int32_t B, int32_t Hq,
                 const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
                 float top_p, float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
                 hipStream_t stream)
@@ -327,6 +346,20 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
     qp.dither = dither;
+    qp.app_blocks = 0;
+    qp.app_N = 0;
+    if (app) {
+        rc = make_append(c, app->dtype, app->k, app->v, B, app->n_new, app->start_pos, page_table, max_pages, qp.app);
+        if (rc) return rc;
+        if (qp.app.n_new > 0) {
+            qp.app_blocks = kvc::fused_append_blocks(qp.app);
+            qp.app_N = (long)B * qp.app.n_new * c->num_kv_heads;
+            if (qp.app_blocks == 0) {  // too many tokens to ride along: an append launch first
+                hipError_t ea = kvc::launch_append(qp.app, stream);
+                if (ea != hipSuccess) return hip_fail(ea, "append launch");
+            }
+        }
+    }
     qp.has_tail = tail != nullptr || hp != nullptr;
     if (qp.has_tail) {
         kvc::TailParams &tp = qp.tail;
@@ -470,8 +503,8 @@ int kv_decode_attend(const kv_cache *c, const float *q, int32_t B, int32_t Hq, c
                      hipStream_t stream)
 {
     g_err[0] = 0;
-    return decode_impl(c, nullptr, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p,
-                       out, dbg, workspace, workspace_bytes, stream);
+    return decode_impl(c, nullptr, nullptr, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages,
+                       top_p, out, dbg, workspace, workspace_bytes, stream);
 }
 
 int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q, int32_t B, int32_t Hq,
@@ -483,8 +516,8 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
     if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
     int rc = check_tail(tail, c->num_kv_heads, c->head_dim, B);
     if (rc) return rc;
-    return decode_impl(c, tail, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out,
-                       dbg, workspace, workspace_bytes, stream);
+    return decode_impl(c, tail, nullptr, nullptr, nullptr, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages,
+                       top_p, out, dbg, workspace, workspace_bytes, stream);
 }
 
 int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
@@ -507,8 +540,9 @@ int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const flo
         if (tail && !tail->mass) return fail(KV_ERR_ARG, "a tier with a tail needs the tail's mass array");
     }
     if (dither && ((uintptr_t)dither & 3u) != 0) return fail(KV_ERR_ARG, "q_dither must be 4-byte aligned");
-    return decode_impl(c, tail, hp, dither, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg,
-                       workspace, workspace_bytes, stream);
+    const kv_append_args *app = opts ? opts->append : nullptr;
+    return decode_impl(c, tail, hp, dither, app, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out,
+                       dbg, workspace, workspace_bytes, stream);
 }
 
 int kv_hp_update(const kv_cache *c, const kv_hp *hp, const kv_tail *t, int32_t B, int32_t n,

@@ -13,6 +13,7 @@
 // each thread issues all of its loads of a pass before using any of them, so that a block
 // keeps several KB of HBM reads in flight.  Partial results (max score, weight sum, weighted
 // value sum) of all chunks are merged per (sequence, query head) at the end.
+#include "kvc_append_dev.h"
 #include "kvc_device.h"
 #include "kvc_launch.h"
 
@@ -202,8 +203,9 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 
 // ---------------------------------------------------------------------------------------
 // Query preparation (one block per (sequence, query head), one thread per dim; with a tail,
-// blocks BH .. 2 BH - 1 run the tail attention of the same heads alongside, and all blocks
-// have 256 threads, of which the query preparation uses the first 128):
+// blocks BH .. 2 BH - 1 run the tail attention of the same heads alongside, and the blocks
+// after those encode the new tokens of a fused append; with either, all blocks have 256
+// threads, of which the query preparation uses the first 128):
 //   dense:    q'_r = fmaf chain over j ascending of R[r][j] * q_j (binary32)
 //   hadamard: x = sigma * q, in-place fast Walsh-Hadamard butterflies h = 1..64 (binary32),
 //             q' = x * fp32(1/sqrt(D))
@@ -219,7 +221,15 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
     __shared__ float redf[4];
     __shared__ int redi[2];
     if ((int)blockIdx.x >= p.BH) {
-        tail_attend(p.tail, (int)blockIdx.x - p.BH);
+        const long tb = p.has_tail ? p.BH : 0;  // tail blocks
+        const long ab = (long)blockIdx.x - p.BH - tb;
+        if (ab < 0) {
+            tail_attend(p.tail, (int)blockIdx.x - p.BH);
+        } else if (p.app.rot_kind == 1) {
+            append_hadamard_block(p.app, p.app_N, ab);
+        } else {
+            append_small_block(p.app, p.app_N, ab);
+        }
         return;
     }
     if (threadIdx.x >= kD) return;  // whole waves: blocks of 256 threads when a tail runs alongside
@@ -1586,7 +1596,9 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
 {
     const float isd = (float)(1.0 / sqrt((double)kD));
-    hipLaunchKernelGGL(k_qprep, dim3(p.has_tail ? 2 * p.BH : p.BH), dim3(p.has_tail ? 256 : 128), 0, s, p, isd);
+    const long blocks = (long)p.BH * (p.has_tail ? 2 : 1) + p.app_blocks;
+    const bool wide = p.has_tail || p.app_blocks > 0;
+    hipLaunchKernelGGL(k_qprep, dim3((unsigned)blocks), dim3(wide ? 256 : 128), 0, s, p, isd);
     return hipGetLastError();
 }
 

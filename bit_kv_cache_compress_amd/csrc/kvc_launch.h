@@ -93,6 +93,9 @@ struct QprepParams {
     const float *dither;   // nullable [B*Hq][128]: uniforms of the stochastic rounding
     int has_tail;          // blocks BH .. 2 BH - 1 attend over the binary16 tail
     TailParams tail;
+    long app_blocks;       // 0, or the blocks after those that encode new tokens (fused append)
+    long app_N;            // token-heads to encode
+    AppendParams app;
 };
 
 // Chunked decode geometry shared by the decode kernels.
@@ -188,6 +191,9 @@ struct MergeParams {
 // Exact attention over the binary16 tail: one partial (m, l, o) per (sequence, query head).
 
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
+// Blocks of 256 threads with which the query-preparation launch can encode these new tokens
+// (the randomized Hadamard rotation, or the dense one for at most 8192 token-heads), else 0.
+long fused_append_blocks(const AppendParams &p);
 hipError_t launch_qprep(const QprepParams &p, hipStream_t s);
 hipError_t launch_score(const ScoreParams &p, hipStream_t s);
 hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s);

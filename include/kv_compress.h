@@ -262,6 +262,19 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
  *             adds no bias to the proxy score (an estimator variant outside the pages, the
  *             randomized query quantization of RaBitQ).  Values outside [0, 1) are the
  *             caller's error; the codes stay clamped to 0..15. */
+/* New tokens that a decode step appends to the cache itself (kv_decode_opts.append): the
+ * arguments of kv_compress_append for the decode's B, page_table and max_pages.  The
+ * tokens are written exactly as kv_compress_append would write them, before any of them
+ * is read, so seq_lens must already count them.  With the randomized Hadamard rotation, or
+ * the dense one and at most 8192 new token-heads, the encoding runs inside the decode's
+ * first launch, next to the query preparation; otherwise as its own launch first. */
+typedef struct kv_append_args {
+    int32_t dtype;               /* KV_F16 or KV_F32 */
+    const void *k, *v;           /* [B][n_new][Hkv][D] */
+    int32_t n_new;               /* >= 0 */
+    const int32_t *start_pos;    /* int32 [B] */
+} kv_append_args;
+
 typedef struct kv_decode_opts {
     const kv_tail *tail;
     const float *q_dither;
@@ -271,6 +284,7 @@ typedef struct kv_decode_opts {
                               cache has key centers and is scored by proxy); afterwards every
                               tail token and tier entry adds its softmax weight, summed over the
                               KV head's query heads, to its mass (tail->mass must then be set). */
+    const kv_append_args *append; /* nullable: new tokens appended first, see kv_append_args */
 } kv_decode_opts;
 
 /* kv_decode_attend_ex -- kv_decode_attend with the options of kv_decode_opts (opts NULL or

@@ -756,3 +756,93 @@ def test_hp_tier_pipeline():
     assert promotions >= 1
     torch.cuda.synchronize()
     _say(f"[tier-lazy] done, compared through the end: {comparing}")
+
+
+@pytest.mark.parametrize("name", ["c1-full-fp32-dense", "c2-outliers-ragged", "c3-gqa4-spikes-topp",
+                                  "c5-hadamard-topp", "gqa8-topp"])
+def test_decode_with_fused_append(name):
+    """A decode that appends the newest token of every sequence itself (its encoding rides in
+    the query-preparation launch): cache bytes bit-exact against the oracle's, outputs within
+    the bar, and both bit-identical to a separate append followed by a decode."""
+    from bit_kv_cache_compress_amd import append, decode_attend
+    from tests.kvc_testlib import gpu_empty_cache
+
+    c = _case(name)
+    assert np.all(c.lens >= 1)
+    dev = torch.device("cuda")
+    B = c.wl.B
+    pt = torch.from_numpy(c.pt).to(dev)
+    q = torch.from_numpy(c.q).to(dev)
+    lens = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
+    last = c.lens.astype(np.int64) - 1
+    k_new = torch.from_numpy(np.ascontiguousarray(c.K[np.arange(B), last][:, None])).to(dev)
+    v_new = torch.from_numpy(np.ascontiguousarray(c.V[np.arange(B), last][:, None])).to(dev)
+    start = torch.from_numpy(last.astype(np.int32)).to(dev)
+    outs, caches = [], []
+    for fused in (True, False):
+        g = gpu_empty_cache(c)
+        for b in range(B):
+            n = int(c.lens[b]) - 1
+            if n > 0:
+                append(g, torch.from_numpy(np.ascontiguousarray(c.K[b:b + 1, :n])).to(dev),
+                       torch.from_numpy(np.ascontiguousarray(c.V[b:b + 1, :n])).to(dev),
+                       torch.zeros(1, dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+        if fused:
+            out = decode_attend(g, q, lens, pt, top_p=c.wl.top_p, max_seq_len=c.max_len, append=(k_new, v_new, start))
+        else:
+            append(g, k_new, v_new, start, pt)
+            out = decode_attend(g, q, lens, pt, top_p=c.wl.top_p, max_seq_len=c.max_len)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        caches.append(download(g))
+    stats = compare_caches(caches[0], c.ocache, c)
+    for key in caches[0]:
+        np.testing.assert_array_equal(caches[0][key], caches[1][key])
+    np.testing.assert_array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    ref = c.oracle_decode(c.ocache, c.wl.top_p)
+    worst = max(float(rel_err(outs[0][b, h], r["out"])) for (b, h), r in ref.items())
+    assert worst <= TOL
+    _say(f"[fused-append] {name} ok {stats}, worst rel err {worst:.2e}")
+
+
+def test_decode_with_fused_append_fallback():
+    """More new token-heads than the fused launch takes (dense rotation, > 8192): the decode
+    appends them with a launch of its own first.  Three copies of one sequence, 3 x 3096 new
+    token-heads each step: bytes and outputs bit-identical to a separate append and decode,
+    outputs within the bar of the oracle's."""
+    from bit_kv_cache_compress_amd import KVCache, append, decode_attend
+
+    c = _case("c1-full-fp32-dense")  # B = 1, Hkv = 1, 4096 tokens
+    dev = torch.device("cuda")
+    n0, R = 1000, 3
+    n_new = int(c.lens[0]) - n0
+    assert R * n_new * c.wl.Hkv > 8192
+    pt3 = torch.from_numpy(np.stack([c.pt[0] + i * c.npages for i in range(R)]).astype(np.int32)).to(dev)
+    K3 = np.repeat(c.K, R, axis=0)
+    V3 = np.repeat(c.V, R, axis=0)
+    kn = torch.from_numpy(np.ascontiguousarray(K3[:, n0:])).to(dev)
+    vn = torch.from_numpy(np.ascontiguousarray(V3[:, n0:])).to(dev)
+    start = torch.full((R,), n0, dtype=torch.int32, device=dev)
+    q3 = torch.from_numpy(np.repeat(c.q, R, axis=0)).to(dev)
+    lens3 = torch.full((R,), int(c.lens[0]), dtype=torch.int32, device=dev)
+    outs, caches = [], []
+    for fused in (True, False):
+        g = KVCache(R * c.npages, 1, c.rot_raw, rot_kind=c.rot_kind, page_size=c.wl.P, value_group=c.wl.Gv, device=dev)
+        append(g, torch.from_numpy(np.ascontiguousarray(K3[:, :n0])).to(dev),
+               torch.from_numpy(np.ascontiguousarray(V3[:, :n0])).to(dev), torch.zeros(R, dtype=torch.int32, device=dev),
+               pt3)
+        if fused:
+            out = decode_attend(g, q3, lens3, pt3, top_p=1.0, max_seq_len=c.max_len, append=(kn, vn, start))
+        else:
+            append(g, kn, vn, start, pt3)
+            out = decode_attend(g, q3, lens3, pt3, top_p=1.0, max_seq_len=c.max_len)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        caches.append(download(g))
+    for key in caches[0]:
+        np.testing.assert_array_equal(caches[0][key], caches[1][key])
+    np.testing.assert_array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    ref = c.oracle_decode(c.ocache, 1.0)[(0, 0)]["out"]
+    for i in range(R):
+        assert rel_err(outs[0][i, 0], ref) <= TOL
+    _say("[fused-append] fallback ok")
