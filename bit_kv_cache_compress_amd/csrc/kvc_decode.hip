@@ -1504,6 +1504,7 @@ __device__ __forceinline__ void mass_finish(const MassParams &p, int b, int h, i
 // first 256 chunks are loaded first, so that their reads overlap the max and weight
 // reductions.
 // ---------------------------------------------------------------------------------------
+template <bool MASS>
 __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 {
     constexpr int kT = 1024, NS = kT / kD;  // threads, chunk slices
@@ -1519,7 +1520,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     const int nch = L > 0 ? (L + CHa - 1) / CHa : 0;
     const int d = tid & (kD - 1), sl = tid >> 7;
     MassPrefetch mf;
-    if (p.has_mass) mass_prefetch(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, mf);
+    if (MASS) mass_prefetch(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, mf);
     const float *po = p.po + bh * g.NCA * kD + d;
     float v[PF];
 #pragma unroll
@@ -1585,7 +1586,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
         for (int s2 = 0; s2 < NS; ++s2) t += part[s2][d];
         p.out[bh * kD + d] = D > 0.0f ? t / D : 0.0f;
     }
-    if (p.has_mass) mass_finish(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog, mf);
+    if (MASS) mass_finish(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog, mf);
 }
 
 }  // namespace
@@ -1682,7 +1683,8 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_merge, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
+    if (p.has_mass) hipLaunchKernelGGL(k_merge<true>, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
+    else hipLaunchKernelGGL(k_merge<false>, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 
