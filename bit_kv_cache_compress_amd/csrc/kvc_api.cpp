@@ -76,10 +76,11 @@ void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, bool topp)
     pl.g.logCH = ilog2(CH);
     pl.g.NC = (max_len + CH - 1) / CH;
     if (pl.g.NC < 1) pl.g.NC = 1;
-    pl.g.Lpad = pl.g.NC * CH;
     pl.g.ld = max_len;
     pl.g.KA = KA;
     pl.g.NCA = (pl.g.NC + KA - 1) / KA;
+    // rows of whole attention chunks, so that a chunk's distance loads need no bound
+    pl.g.Lpad = pl.g.NCA * KA * CH;
 }
 
 void plan_layout(Plan &pl, int BH)

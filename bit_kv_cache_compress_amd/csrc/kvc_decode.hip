@@ -1166,33 +1166,36 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     const DecodeGeom &g = p.g;
     const int achunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int kvh = h / g.G;
-    const int L = g.seq_lens[b];
     const int t0 = achunk * CHA;
-    if (t0 >= L) return;
-    const int n = min(CHA, L - t0);
     const int lane = threadIdx.x;
     const size_t bh = (size_t)b * g.Hq + h;
 
-    // ---- round 1: distances (tokens 8 lane + 512 j .. + 7), query, thresholds, page ids
+    // ---- round 1: distances (tokens 8 lane + 512 j .. + 7), thresholds, page ids and the
+    // sequence length, all issued together: the distance rows hold whole attention chunks
+    // and the page ids are read within the table, so none of these loads waits for the
+    // length (values past it are masked below)
     uint4 raw[NJ];
     const uint16_t *row = p.dl + bh * g.Lpad + t0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int tl = 8 * lane + 512 * j;
-        if (tl < n) raw[j] = *reinterpret_cast<const uint4 *>(row + tl);
-    }
+    for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const uint4 *>(row + 8 * lane + 512 * j);
     int thr[NJ];  // wave-uniform
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int chunk = achunk * NJ + j;
-        thr[j] = (chunk * kTopPChunk < L) ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
+        thr[j] = chunk < g.NC ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
     }
     const int logP = p.c.logP;
     const int p0 = t0 >> logP;
-    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
-    for (int i = lane; i < np; i += 64)
+    const int npmax = min(((t0 + CHA - 1) >> logP) - p0 + 1, g.max_pages - p0);
+    for (int i = lane; i < npmax; i += 64)
         pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
                    << logP;
+    const int L = g.seq_lens[b];
+    if (t0 >= L) return;
+    const int n = min(CHA, L - t0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        if (j * kTopPChunk >= n) thr[j] = -1;  // a 512-token chunk past the end keeps nothing
     QueryState<1> qs;  // wave-uniform: scalar loads into SGPRs
 #pragma unroll
     for (int i = 0; i < 16; ++i) qs.nib[0][i] = p.qnib[bh * 16 + i];
