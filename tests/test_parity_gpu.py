@@ -846,3 +846,59 @@ def test_decode_with_fused_append_fallback():
     for i in range(R):
         assert rel_err(outs[0][i, 0], ref) <= TOL
     _say("[fused-append] fallback ok")
+
+
+@pytest.mark.parametrize("rot", ["dense", "hadamard"])
+def test_degenerate_inputs(rot):
+    """The method's degenerate cases against the oracle: a zero query (delta = 0, every code
+    0, equal scores), zero keys (norm 0, correction 1), value groups of one value (scale 0),
+    a sequence whose keys are all equal (one bin: Top-p keeps all of it), one-token and
+    empty sequences, and Top-p at 1e-6 (the top bin only), 0.5, 0.999999 and 1."""
+    from bit_kv_cache_compress_amd import append, decode_attend
+    from tests.kvc_testlib import gpu_empty_cache
+
+    wl = W.CONFIGS[2].scaled(B=5, Hq=8, Hkv=2, P=64, rot=rot)
+    c = Case(wl, L=700, seq_lens=[700, 700, 1, 0, 333])
+    rng = np.random.default_rng(77)
+    c.q[0, 0] = 0.0                                    # zero query
+    c.q[1, 3] = 2.5                                    # constant query
+    c.K[0, rng.choice(700, 40, replace=False), 1] = 0  # zero keys
+    c.K[1] = c.K[1, :1]                                # all keys of sequence 1 equal
+    c.V[0, :, 0, 32:64] = 1.25                         # one value group constant
+    c.V[4, :, 1] = 0.0                                 # zero values
+    c.ocache = c.oracle_cache()
+    dev = torch.device("cuda")
+    g = gpu_empty_cache(c)
+    pt = torch.from_numpy(c.pt).to(dev)
+    for b in range(c.wl.B):
+        n = int(c.lens[b])
+        if n:
+            append(g, torch.from_numpy(np.ascontiguousarray(c.K[b:b + 1, :n])).to(dev),
+                   torch.from_numpy(np.ascontiguousarray(c.V[b:b + 1, :n])).to(dev),
+                   torch.zeros(1, dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+    torch.cuda.synchronize()
+    compare_caches(download(g), c.ocache, c)
+    from bit_kv_cache_compress_amd import DecodeDebug
+    q = torch.from_numpy(c.q).to(dev)
+    lens = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
+    for top_p in (1e-6, 0.5, 0.999999, 1.0):
+        dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev)
+        out = decode_attend(g, q, lens, pt, top_p=top_p, max_seq_len=c.max_len, debug=dbg)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        ref = c.oracle_decode(c.ocache, top_p)
+        for (b, h), r in ref.items():
+            n = int(c.lens[b])
+            np.testing.assert_array_equal(dbg.q_codes[b, h].cpu().numpy(), r["u"])
+            if n == 0:
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            if top_p < 1.0:
+                cnt = int(dbg.sel_count[b, h])
+                np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            assert rel_err(out[b, h], r["out"]) <= TOL, (top_p, b, h)
+        # equal keys: every token in one bin, so Top-p keeps them all
+        if top_p < 1.0:
+            assert int(dbg.sel_count[1, 0]) == 700
+        _say(f"[degenerate] {rot} top_p={top_p} ok")
+    assert np.all(ref[(0, 0)]["u"] == 0)
