@@ -783,6 +783,14 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     const DecodeGeom &g = p.g;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bh = (size_t)b * g.Hq + h;
+    // counts of bins 8 tid .. 8 tid + 7 summed over the splits (8 splits' loads in flight).
+    // The first 8 splits and the top bins of the first 1024 chunks are read within the
+    // planned bounds before the length is known; splits and chunks past it are masked below.
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + bh * p.nsplit * kBins) + tid;
+    uint4 v0[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v0[k] = k < p.nsplit ? src[(size_t)k * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
+    const int mfirst = tid < g.NC ? p.lmax[bh * g.NC + tid] : -kBinClamp;
     const int L = g.seq_lens[b];
     if (L <= 0) {
         if (tid == 0) {
@@ -799,17 +807,17 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     }
     const int nch = (L + g.CH - 1) >> g.logCH;
     const int nsu = (nch + p.cps - 1) / p.cps;  // splits that hold tokens
-    // counts of bins 8 tid .. 8 tid + 7 summed over the splits (8 splits' loads in flight)
-    // the top bin of the first 1024 chunks is read together with the split counts
-    int m = tid < nch ? p.lmax[bh * g.NC + tid] : -kBinClamp;
+    int m = tid < nch ? mfirst : -kBinClamp;
     uint32_t cnt[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) cnt[k] = 0u;
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + bh * p.nsplit * kBins) + tid;
     for (int s0 = 0; s0 < nsu; s0 += 8) {
         uint4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (s0 + k < nsu) ? src[(size_t)(s0 + k) * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
+        for (int k = 0; k < 8; ++k) {
+            if (s0 == 0) v[k] = k < nsu ? v0[k] : make_uint4(0u, 0u, 0u, 0u);
+            else v[k] = (s0 + k < nsu) ? src[(size_t)(s0 + k) * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
