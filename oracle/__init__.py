@@ -50,9 +50,9 @@ def _load():
     lib.orc_f64_from_f16.argtypes = [ctypes.c_uint16]
     lib.orc_f64_from_f16.restype = ctypes.c_double
     lib.orc_rotate_f64.argtypes = [i32, i32, P, P, P, i64, P]
-    lib.orc_key_encode.argtypes = [i32, i32, P, P, P, i64, P, P]
+    lib.orc_key_encode.argtypes = [i32, i32, i32, P, P, P, i64, P, P]
     lib.orc_value_encode.argtypes = [i32, i32, P, i64, P, P]
-    lib.orc_query_encode.argtypes = [i32, i32, P, P, P, i64, P, P, P, P, P]
+    lib.orc_query_encode.argtypes = [i32, i32, i32, P, P, P, i64, P, P, P, P, P]
     lib.orc_scores.argtypes = [i32, P, P, i64, P, f32, f32, P, P, P]
     lib.orc_kbin.argtypes = [i32]
     lib.orc_kbin.restype = f32
@@ -123,14 +123,16 @@ def rotate_f64(rot: Rotation, x) -> np.ndarray:
     return y
 
 
-def key_encode(rot: Rotation, k):
-    """k: (n, D) float -> bits (n, D/32) uint32, nc (n, 2) uint16 (norm, corr)."""
+def key_encode(rot: Rotation, k, sk=None):
+    """k: (n, D) float -> bits (n, sk/32) uint32, nc (n, 2) uint16 (norm, corr); sk is the
+    sketch width (the first sk rotated coordinates; default D)."""
     D = rot.D
+    sk = D if sk is None else int(sk)
     k = _c(np.asarray(k).astype(np.float32).reshape(-1, D), np.float32)
     n = k.shape[0]
-    bits = np.empty((n, D // 32), dtype=np.uint32)
+    bits = np.empty((n, sk // 32), dtype=np.uint32)
     nc = np.empty((n, 2), dtype=np.uint16)
-    _load().orc_key_encode(D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(k), n, _p(bits), _p(nc))
+    _load().orc_key_encode(D, sk, rot.kind, _p(rot.Rf), _p(rot.signs), _p(k), n, _p(bits), _p(nc))
     return bits, nc
 
 
@@ -144,10 +146,12 @@ def value_encode(v, D: int, Gv: int):
     return codes, sz
 
 
-def query_encode(rot: Rotation, q, dither=None):
+def query_encode(rot: Rotation, q, dither=None, sk=None):
     """q: (m, D) float32 -> dict(u (m, D) uint8, vl, delta, c0, c1 (m,) f32, sumu (m,), qrot).
-    dither: optional (m, D) float32 uniforms in [0, 1) for stochastic rounding of the codes."""
+    dither: optional (m, D) float32 uniforms in [0, 1) for stochastic rounding of the codes;
+    sk: the keys' sketch width (default D): codes past it are 0."""
     D = rot.D
+    sk = D if sk is None else int(sk)
     q = _c(np.asarray(q, dtype=np.float32).reshape(-1, D), np.float32)
     m = q.shape[0]
     if dither is not None:
@@ -156,22 +160,24 @@ def query_encode(rot: Rotation, q, dither=None):
     par = np.empty((m, 4), dtype=np.float32)
     sumu = np.empty(m, dtype=np.int32)
     qrot = np.empty((m, D), dtype=np.float32)
-    _load().orc_query_encode(D, rot.kind, _p(rot.Rf), _p(rot.signs), _p(q), m,
+    _load().orc_query_encode(D, sk, rot.kind, _p(rot.Rf), _p(rot.signs), _p(q), m,
                              _p(dither) if dither is not None else None, _p(u), _p(par), _p(sumu), _p(qrot))
     return dict(u=u, vl=par[:, 0].copy(), delta=par[:, 1].copy(), c0=par[:, 2].copy(),
                 c1=par[:, 3].copy(), sumu=sumu, qrot=qrot)
 
 
-def scores(bits, nc, u, c0, c1, D: int):
-    """One encoded query against L encoded keys -> (A, P, score) arrays of length L."""
-    bits = _c(bits, np.uint32).reshape(-1, D // 32)
+def scores(bits, nc, u, c0, c1, D: int, sk=None):
+    """One encoded query against L encoded keys (sketches of sk bits, default D) -> (A, P,
+    score) arrays of length L."""
+    sk = D if sk is None else int(sk)
+    bits = _c(bits, np.uint32).reshape(-1, sk // 32)
     nc = _c(nc, np.uint16).reshape(-1, 2)
     u = _c(u, np.uint8).reshape(D)
     L = bits.shape[0]
     A = np.empty(L, dtype=np.int32)
     P = np.empty(L, dtype=np.int32)
     s = np.empty(L, dtype=np.float32)
-    _load().orc_scores(D, _p(bits), _p(nc), L, _p(u), float(c0), float(c1), _p(A), _p(P), _p(s))
+    _load().orc_scores(sk, _p(bits), _p(nc), L, _p(u), float(c0), float(c1), _p(A), _p(P), _p(s))
     return A, P, s
 
 
@@ -277,7 +283,8 @@ def attend_with_tail(s_sel, vals_sel, q, tk, tv, D: int, shift: float = 0.0, wei
 class PagedCache:
     """The paged packed cache.  Token t of sequence b lives in physical page
     page_table[b][t // P], slot t % P.  Per (page, KV head):
-      key_bits  uint32 [P][D/32]     sign bits of the rotated key
+      key_bits  uint32 [P][sk/32]    sign bits of the first sk rotated coordinates (the
+                                     sketch; sk = D unless a narrower sketch is asked for)
       key_nc    uint32 [P]           binary16 norm (low half) | binary16 corr (high half)
       val_codes uint8  [P][D/2]      4-bit value codes, even dim in the low nibble
       val_sz    uint32 [P][D/Gv]     binary16 scale (low half) | binary16 zero (high half)
@@ -287,11 +294,12 @@ class PagedCache:
     estimate <q, k - c_h>, which differs from <q, k> by a constant per query head.
     """
 
-    def __init__(self, num_pages, Hkv, P, D, Gv, exact_keys=False, key_center=None):
+    def __init__(self, num_pages, Hkv, P, D, Gv, exact_keys=False, key_center=None, sketch=None):
         self.num_pages, self.Hkv, self.P, self.D, self.Gv = num_pages, Hkv, P, D, Gv
+        self.sk = D if sketch is None else int(sketch)  # sketch width: sign bits per key
         self.key_center = None if key_center is None else np.asarray(key_center, dtype=np.float32).reshape(Hkv, D)
         self.key_f16 = np.zeros((num_pages, Hkv, P, D), dtype=np.float16) if exact_keys else None
-        self.key_bits = np.zeros((num_pages, Hkv, P, D // 32), dtype=np.uint32)
+        self.key_bits = np.zeros((num_pages, Hkv, P, self.sk // 32), dtype=np.uint32)
         self.key_nc = np.zeros((num_pages, Hkv, P), dtype=np.uint32)
         self.val_codes = np.zeros((num_pages, Hkv, P, D // 2), dtype=np.uint8)
         self.val_sz = np.zeros((num_pages, Hkv, P, D // Gv), dtype=np.uint32)
@@ -325,7 +333,7 @@ def append(cache: PagedCache, rot: Rotation, k, v, start_pos, page_table):
             if cache.key_center is not None:
                 # centering before the rotation: one binary32 subtraction per dim
                 kh = kh.astype(np.float32) - cache.key_center[h]
-            bits, nc = key_encode(rot, kh)
+            bits, nc = key_encode(rot, kh, cache.sk)
             codes, sz = value_encode(v[b, :, h, :], D, cache.Gv)
             cache.key_bits[pg, h, sl] = bits
             cache.key_nc[pg, h, sl] = nc[:, 0].astype(np.uint32) | (nc[:, 1].astype(np.uint32) << 16)
@@ -374,7 +382,7 @@ def decode_head(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, 
 def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_table, top_p, proxy, dither=None):
     D, Gv = cache.D, cache.Gv
     kvh = h * cache.Hkv // Hq
-    qe = query_encode(rot, q_h, dither)
+    qe = query_encode(rot, q_h, dither, cache.sk)
     res = dict(u=qe["u"][0], vl=qe["vl"][0], delta=qe["delta"][0], c0=qe["c0"][0],
                c1=qe["c1"][0], sumu=int(qe["sumu"][0]), kvh=kvh)
     if L <= 0:
@@ -382,7 +390,7 @@ def _decode_head_cache(cache: PagedCache, rot: Rotation, q_h, b, h, Hq, L, page_
                    idx=None)
         return res
     bits, nc, codes, sz = cache.gather(b, kvh, L, page_table)
-    A, P, s = scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], D)
+    A, P, s = scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], D, cache.sk)
     res.update(A=A, P=P, score=s)
     if top_p < 1.0:
         tp = topp(s, top_p, D)

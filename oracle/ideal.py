@@ -7,6 +7,10 @@ rotation and an optional int4 query:
     k' = Q k, q' = Q q, x = sign(k') / sqrt(D)          (sign(0) = +1)
     corr = <x, k' / |k|>
     est  = |k| <x, q~> / corr,   q~ = q' or its int4 dequantization
+With a sketch of sk < D coordinates, k' and q' are the first sk rotated coordinates and
+x = sign(k')/sqrt(sk); the estimate stays unbiased (the part of q orthogonal to k has
+conditional mean zero given the rotated key) and its spread goes as sqrt(1 - corr^2)/corr,
+corr ~ sqrt(2 sk / (pi D)): about 1.9 times the full sketch's at sk = D/2.
 
 "RaBitQCache" (abstract; key design) states that its proxy score from randomized rotated
 binary quantization is an unbiased estimator of the attention score with a proven error
@@ -37,16 +41,19 @@ def int4_dequant(qp, mode="rne", uniforms=None):
     return vl + delta * u
 
 
-def estimate(Q, k, q, query="exact", uniforms=None):
-    """Estimator of <k, q> for a batch of rotations Q (n, D, D) or one rotation (D, D)."""
+def estimate(Q, k, q, query="exact", uniforms=None, sk=None):
+    """Estimator of <k, q> for a batch of rotations Q (n, D, D) or one rotation (D, D).
+    sk: sketch width, the first sk rotated coordinates only (default D): a non-square
+    projection whose rows are the first sk rows of Q."""
     Q = np.asarray(Q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
     D = k.shape[-1]
-    kp = Q @ k
-    qp = Q @ q
+    sk = D if sk is None else int(sk)
+    kp = (Q @ k)[..., :sk]
+    qp = (Q @ q)[..., :sk]
     nk = np.linalg.norm(k)
-    x = sign_pm1(kp) / np.sqrt(D)
+    x = sign_pm1(kp) / np.sqrt(sk)
     corr = np.sum(x * kp, axis=-1) / nk
     if query == "exact":
         qt = qp

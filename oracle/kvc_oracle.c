@@ -130,34 +130,38 @@ void orc_rotate_f64(int D, int rot_kind, const float *R, const uint32_t *signs,
 /* Key encode: sign bits of the rotated key + binary16 norm and correction.               */
 /* ------------------------------------------------------------------------------------- */
 
-/* For each of n keys k (D floats):
+/* For each of n keys k (D floats), with a sketch of the first sk rotated coordinates
+ * (sk = D: the whole rotation; sk < D, a multiple of 32: a non-square random projection,
+ * the rows 0..sk-1 of R, read from "H1B-KV" key design as a 1-bit sketch by random
+ * projection):
  *   k' = R k                                   (binary64, rotate_f64)
- *   bit_r = 1 if k'_r >= 0 else 0              ([H1IB] 二.1: sign gives +-1; a zero counts
+ *   bit_r = 1 if k'_r >= 0 else 0, r < sk      ([H1IB] 二.1: sign gives +-1; a zero counts
  *                                               as +1)
  *   bit r is stored in 32-bit word r/32 at bit position r%32; viewed as little-endian
  *   bytes this is byte r/8, bit r%8, exactly the bitmap order of [H1IB] 二.3.
- *   norm = fp16(|k|_2)
- *   corr = fp16( sum_r |k'_r| / (sqrt(D) |k|) ) = fp16(<x, k'/|k|>), x = sign(k')/sqrt(D)
- *          ([RaBitQ, outside the pages]: the estimator's normaliser); corr = 1 when k = 0.
- * Output: bits[n][D/32], nc[n][2] = (norm, corr) as binary16 bit patterns. */
-void orc_key_encode(int D, int rot_kind, const float *R, const uint32_t *signs,
+ *   norm = fp16(|k|_2)                         (the whole key)
+ *   corr = fp16( sum_{r<sk} |k'_r| / (sqrt(sk) |k|) ) = fp16(<x, k'/|k|>),
+ *          x = sign(k'_{<sk})/sqrt(sk) ([RaBitQ, outside the pages]: the estimator's
+ *          normaliser); corr = 1 when k = 0.
+ * Output: bits[n][sk/32], nc[n][2] = (norm, corr) as binary16 bit patterns. */
+void orc_key_encode(int D, int sk, int rot_kind, const float *R, const uint32_t *signs,
                     const float *k, int64_t n, uint32_t *bits, uint16_t *nc)
 {
     double *y = (double *)malloc(sizeof(double) * (size_t)D);
-    int W = D / 32;
+    int W = sk / 32;
     for (int64_t i = 0; i < n; ++i) {
         const float *ki = k + i * D;
         rotate_f64(D, rot_kind, R, signs, ki, y);
         uint32_t *bw = bits + i * W;
         for (int w = 0; w < W; ++w) bw[w] = 0u;
-        for (int r = 0; r < D; ++r)
+        for (int r = 0; r < sk; ++r)
             if (!(y[r] < 0.0)) bw[r >> 5] |= 1u << (r & 31);
         double ss = 0.0, sabs = 0.0;
         for (int j = 0; j < D; ++j) ss += (double)ki[j] * (double)ki[j];
-        for (int r = 0; r < D; ++r) sabs += fabs(y[r]);
+        for (int r = 0; r < sk; ++r) sabs += fabs(y[r]);
         double nrm = sqrt(ss);
         nc[2 * i + 0] = orc_f16_from_f64(nrm);
-        nc[2 * i + 1] = orc_f16_from_f64(nrm == 0.0 ? 1.0 : sabs / (sqrt((double)D) * nrm));
+        nc[2 * i + 1] = orc_f16_from_f64(nrm == 0.0 ? 1.0 : sabs / (sqrt((double)sk) * nrm));
     }
     free(y);
 }
@@ -220,29 +224,33 @@ void orc_value_encode(int D, int Gv, const float *v, int64_t n, uint8_t *codes, 
 /* 1/sqrt(D) rounded to binary32. */
 static float inv_sqrt_d(int D) { return (float)(1.0 / sqrt((double)D)); }
 
-/* For each of m queries q (D floats), in binary32 with this exact operation order:
+/* For each of nq queries q (D floats), in binary32 with this exact operation order (sk:
+ * the sketch width of the keys, as for orc_key_encode; only the first sk rotated
+ * coordinates are quantized, the codes of the others are 0):
  *   dense:    q'_r = fmaf chain over j ascending: a = R[r][0]*q_0; a = fmaf(R[r][j], q_j, a)
  *   hadamard: x_j = sigma_j q_j; for h = 1, 2, 4, ..., D/2 and every i with (i & h) == 0:
  *             (x_i, x_{i+h}) <- (x_i + x_{i+h}, x_i - x_{i+h})   (the textbook in-place fast
  *             Walsh-Hadamard transform, Sylvester order); q'_j = x_j * fp32(1/sqrt(D))
- *   v_l = min q', v_r = max q', delta = (v_r - v_l) / 15
- *   u_j = 0 if delta == 0, else clamp(rint((q'_j - v_l) / delta), 0, 15)   (ties to even)
+ *   v_l = min_{j<sk} q'_j, v_r = max_{j<sk} q'_j, delta = (v_r - v_l) / 15
+ *   u_j = 0 if delta == 0 or j >= sk, else clamp(rint((q'_j - v_l) / delta), 0, 15)
+ *         (ties to even)
  *         or, with dither (uniforms U in [0, 1), one per query dim, nullable):
  *         clamp(floor((q'_j - v_l) / delta + U_j), 0, 15)  (stochastic rounding: the
  *         expected code is (q'_j - v_l) / delta; RaBitQ's randomized query quantization,
  *         outside the pages; binary32 divide, then binary32 add)
- *   c0 = v_l * fp32(1/sqrt(D)),  c1 = delta * fp32(1/sqrt(D)),  sumu = sum_j u_j
- * The dequantized query is q'_j ~ v_l + delta u_j, and x = sign(k')/sqrt(D) gives
- * <x, q> ~ c1 * A + c0 * P with A = sum_j s_j u_j, P = sum_j s_j, s_j = +-1.
- * Output: u[m][D] (one code per byte), par[m][4] = (v_l, delta, c0, c1), sumu[m],
- * qrot[m][D] (optional, the rotated query before quantization). */
-void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs,
-                      const float *q, int64_t m, const float *dither, uint8_t *u, float *par,
+ *   c0 = v_l * fp32(1/sqrt(sk)),  c1 = delta * fp32(1/sqrt(sk)),  sumu = sum_j u_j
+ * The dequantized query is q'_j ~ v_l + delta u_j, and x = sign(k'_{<sk})/sqrt(sk) gives
+ * <x, q> ~ c1 * A + c0 * P with A = sum_{j<sk} s_j u_j, P = sum_{j<sk} s_j, s_j = +-1.
+ * Output: u[nq][D] (one code per byte), par[nq][4] = (v_l, delta, c0, c1), sumu[nq],
+ * qrot[nq][D] (optional, the rotated query before quantization). */
+void orc_query_encode(int D, int sk, int rot_kind, const float *R, const uint32_t *signs,
+                      const float *q, int64_t nq, const float *dither, uint8_t *u, float *par,
                       int32_t *sumu, float *qrot)
 {
     float *x = (float *)malloc(sizeof(float) * (size_t)D);
     float isd = inv_sqrt_d(D);
-    for (int64_t i = 0; i < m; ++i) {
+    float isk = inv_sqrt_d(sk);
+    for (int64_t i = 0; i < nq; ++i) {
         const float *qi = q + i * D;
         if (rot_kind == ORC_ROT_DENSE) {
             for (int r = 0; r < D; ++r) {
@@ -263,7 +271,7 @@ void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs
             for (int j = 0; j < D; ++j) x[j] = x[j] * isd;
         }
         float vl = x[0], vr = x[0];
-        for (int j = 1; j < D; ++j) {
+        for (int j = 1; j < sk; ++j) {
             if (x[j] < vl) vl = x[j];
             if (x[j] > vr) vr = x[j];
         }
@@ -271,7 +279,7 @@ void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs
         int32_t su = 0;
         for (int j = 0; j < D; ++j) {
             int c = 0;
-            if (delta != 0.0f) {
+            if (delta != 0.0f && j < sk) {
                 float tq = (x[j] - vl) / delta;
                 float t = dither ? floorf(tq + dither[i * D + j]) : rintf(tq);
                 if (t < 0.0f) t = 0.0f;
@@ -284,8 +292,8 @@ void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs
         }
         par[i * 4 + 0] = vl;
         par[i * 4 + 1] = delta;
-        par[i * 4 + 2] = vl * isd;
-        par[i * 4 + 3] = delta * isd;
+        par[i * 4 + 2] = vl * isk;
+        par[i * 4 + 3] = delta * isk;
         sumu[i] = su;
     }
     free(x);
@@ -295,20 +303,20 @@ void orc_query_encode(int D, int rot_kind, const float *R, const uint32_t *signs
 /* Proxy score ([RBQC]: binary x INT4 arithmetic; unbiased proxy score).                  */
 /* ------------------------------------------------------------------------------------- */
 
-/* For each of L encoded keys against one encoded query (u[D], c0, c1):
- *   s_j = +1 if bit j is set else -1            ([H1IB] 二.3 bit order)
- *   A = sum_j s_j u_j,   P = sum_j s_j            (integers, written as explicit +-1 dots)
+/* For each of L encoded keys (sketches of sk bits) against one encoded query (u[D], c0, c1):
+ *   s_j = +1 if bit j is set else -1, j < sk    ([H1IB] 二.3 bit order)
+ *   A = sum_{j<sk} s_j u_j,   P = sum_{j<sk} s_j  (integers, written as explicit +-1 dots)
  *   r = float(norm) / float(corr)                 (binary32 divide)
  *   score = fmaf(c1, float(A), c0 * float(P)) * r (binary32; c0*P rounded first)
  * score estimates <k, q>: |k| <x, q'> / <x, k'/|k|>, with <x, q'> ~ c1 A + c0 P. */
-void orc_scores(int D, const uint32_t *bits, const uint16_t *nc, int64_t L,
+void orc_scores(int sk, const uint32_t *bits, const uint16_t *nc, int64_t L,
                 const uint8_t *u, float c0, float c1, int32_t *A, int32_t *P, float *score)
 {
-    int W = D / 32;
+    int W = sk / 32;
     for (int64_t t = 0; t < L; ++t) {
         const uint32_t *bw = bits + t * W;
         int32_t a = 0, p = 0;
-        for (int j = 0; j < D; ++j) {
+        for (int j = 0; j < sk; ++j) {
             int s = ((bw[j >> 5] >> (j & 31)) & 1u) ? 1 : -1;
             a += s * (int32_t)u[j];
             p += s;
