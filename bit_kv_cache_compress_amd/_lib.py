@@ -34,6 +34,7 @@ class KVCacheDesc(ctypes.Structure):
         ("vals", ctypes.c_void_p),
         ("keys_f16", ctypes.c_void_p),
         ("key_center", ctypes.c_void_p),
+        ("sketch_dim", ctypes.c_int32),
     ]
 
 

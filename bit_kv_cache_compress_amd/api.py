@@ -53,6 +53,9 @@ class KVCache:
     it, and a Top-p decode then scores the selected tokens exactly with it.  ``proxy_desc``
     is the descriptor without it (proxy scores throughout).
 
+    ``sketch_dim``: sign bits per key, 128 (the whole rotation) or 64 (a narrow sketch of
+    the first 64 rotated coordinates, 12-byte key records).
+
     ``key_center``: optional float32 [Hkv, 128] per-head key centers (kept on the device as
     ``key_center``).  Appends encode k - c_h instead of k; the proxy scores then estimate
     <q, k - c_h>, a per-head shift that the softmax ignores (tails are moved to that frame).
@@ -60,7 +63,7 @@ class KVCache:
 
     def __init__(self, num_pages: int, num_kv_heads: int, rotation, rot_kind: str = "dense",
                  page_size: int = 256, value_group: int = 32, device="cuda", exact_keys: bool = False,
-                 key_center=None):
+                 key_center=None, sketch_dim: int = HEAD_DIM):
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:
             device = torch.device("cuda", torch.cuda.current_device())
@@ -81,8 +84,11 @@ class KVCache:
                 raise ValueError("hadamard rotation must hold 4 sign words")
             r = torch.where(r >= 2**31, r - 2**32, r).to(torch.int32)
             self.rot = r.to(device).contiguous()
+        if sketch_dim not in (HEAD_DIM, 64):
+            raise ValueError("sketch_dim must be 128 or 64")
+        self.sketch_dim = int(sketch_dim)
         shp = (self.num_pages, self.num_kv_heads, self.page_size)
-        self.keys = torch.zeros(shp + (D // 32 + 1,), dtype=torch.int32, device=device)
+        self.keys = torch.zeros(shp + (self.sketch_dim // 32 + 1,), dtype=torch.int32, device=device)
         self.vals = torch.zeros(shp + (D // 2 + 4 * (D // self.value_group),), dtype=torch.uint8, device=device)
         self.keys_f16 = torch.zeros(shp + (D,), dtype=torch.float16, device=device) if exact_keys else None
         self.key_center = None
@@ -94,18 +100,18 @@ class KVCache:
         kcp = self.key_center.data_ptr() if self.key_center is not None else None
         self.desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
                                   self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(), self.vals.data_ptr(),
-                                  self.keys_f16.data_ptr() if exact_keys else None, kcp)
+                                  self.keys_f16.data_ptr() if exact_keys else None, kcp, self.sketch_dim)
         self.proxy_desc = L.KVCacheDesc(D, self.num_kv_heads, self.value_group, self.page_size, self.num_pages,
                                         self.rot_kind, self.rot.data_ptr(), self.keys.data_ptr(),
-                                        self.vals.data_ptr(), None, kcp)
+                                        self.vals.data_ptr(), None, kcp, self.sketch_dim)
 
     @property
     def key_bits(self) -> torch.Tensor:
-        return self.keys[..., :HEAD_DIM // 32]
+        return self.keys[..., :self.sketch_dim // 32]
 
     @property
     def key_nc(self) -> torch.Tensor:
-        return self.keys[..., HEAD_DIM // 32]
+        return self.keys[..., self.sketch_dim // 32]
 
     @property
     def val_codes(self) -> torch.Tensor:

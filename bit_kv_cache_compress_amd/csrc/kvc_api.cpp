@@ -182,6 +182,8 @@ int check_cache(const kv_cache *c)
         return fail(KV_ERR_ARG, "keys_f16 must be 16-byte aligned");
     if (c->key_center && ((uintptr_t)c->key_center & 15u) != 0)
         return fail(KV_ERR_ARG, "key_center must be 16-byte aligned");
+    if (c->sketch_dim != 0 && c->sketch_dim != 128 && c->sketch_dim != 64)
+        return fail(KV_ERR_UNSUPPORTED, "sketch_dim %d: supported widths are 128 (or 0) and 64", c->sketch_dim);
     return KV_OK;
 }
 
@@ -219,6 +221,8 @@ kvc::CacheView view_of(const kv_cache *c)
     v.vals = c->vals;
     v.kf16 = c->keys_f16;
     v.kc = c->key_center;
+    v.sk = c->sketch_dim == 0 ? c->head_dim : c->sketch_dim;
+    v.kw = v.sk / 32;
     return v;
 }
 
@@ -346,6 +350,8 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     qp.dbg_codes = dbg ? dbg->q_codes : nullptr;
     qp.dbg_params = dbg ? dbg->q_params : nullptr;
     qp.dbg_sumu = dbg ? dbg->q_sumu : nullptr;
+    qp.sk = cv.sk;
+    qp.isk = (float)(1.0 / sqrt((double)cv.sk));
     qp.dither = dither;
     qp.app_blocks = 0;
     qp.app_N = 0;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
 #pragma unroll
             for (int rb = 0; rb < 8; ++rb) {
                 const double val = acc[rb][v];
-                sa += fabs(val);
+                if (rb < 2 * p.c.kw) sa += fabs(val);  // dims 16 rb .. 16 rb + 15 of the sketch
                 const uint64_t m = __ballot(!(val < 0.0));
                 const uint32_t bits16 = (uint32_t)((m >> (16 * q)) & 0xFFFFull);
                 words[v][rb >> 1] |= bits16 << (16 * (rb & 1));
@@ -112,8 +112,7 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
                 if (n < N) {
                     const size_t slot = slot_of(p, n);
                     uint32_t *kr = key_rec(p.c, slot);
-#pragma unroll
-                    for (int q2 = 0; q2 < kKeyWords; ++q2) kr[q2] = words[v][q2];
+                    for (int q2 = 0; q2 < p.c.kw; ++q2) kr[q2] = words[v][q2];
                 }
             }
         }
@@ -133,7 +132,7 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
                 }
                 ss = sum16(ss);
                 const size_t slot = slot_of(p, n);
-                if (i == 0) key_rec(p.c, slot)[kKeyWords] = norm_corr_word(ss, sabs_s[r]);
+                if (i == 0) key_rec(p.c, slot)[p.c.kw] = norm_corr_word(ss, sabs_s[r], p.c.sk);
                 float xv[8];
                 load8(p.v, p.dtype, (size_t)n * kD + 8 * i, xv);
                 encode_values(xv, i, p.c.Gv, val_rec(p.c, slot));
@@ -262,7 +261,7 @@ __device__ __forceinline__ uint32_t *norm_word(const HpUpdateParams &p, int b, i
 {
     const int page = p.page_table[(size_t)b * p.max_pages + (pos >> p.c.logP)];
     const size_t slot = ((size_t)page * p.c.Hkv + kvh) * p.c.P + (pos & (p.c.P - 1));
-    return key_rec(p.c, slot) + kKeyWords;
+    return key_rec(p.c, slot) + p.c.kw;
 }
 
 __global__ __launch_bounds__(256) void k_hp_update(HpUpdateParams p)

@@ -111,11 +111,12 @@ __device__ __forceinline__ double sum16(double v)
     return v;
 }
 
-// key_nc word: binary16 |k| (low) and binary16 sum|k'| / (sqrt(D) |k|) (high; 1 if k = 0).
-__device__ __forceinline__ uint32_t norm_corr_word(double ss, double sabs_rot)
+// key_nc word: binary16 |k| (low) and binary16 sum_{r<sk} |k'_r| / (sqrt(sk) |k|) (high;
+// 1 if k = 0), sk the sketch width (sign bits per key).
+__device__ __forceinline__ uint32_t norm_corr_word(double ss, double sabs_rot, int sk)
 {
     const double nrm = sqrt(ss);
-    const double corr = (nrm == 0.0) ? 1.0 : sabs_rot / (sqrt((double)kD) * nrm);
+    const double corr = (nrm == 0.0) ? 1.0 : sabs_rot / (sqrt((double)sk) * nrm);
     return double_to_half_bits(nrm) | (double_to_half_bits(corr) << 16);
 }
 
@@ -174,10 +175,11 @@ __device__ __forceinline__ void append_hadamard_block(const AppendParams &p, lon
     uint32_t word = byte << (8 * (i & 3));
     word |= __shfl_xor(word, 1);
     word |= __shfl_xor(word, 2);
-    if ((i & 3) == 0) key_rec(p.c, slot)[i >> 2] = word;
+    if ((i & 3) == 0 && (i >> 2) < p.c.kw) key_rec(p.c, slot)[i >> 2] = word;  // the sketch's words
+    if (8 * i >= p.c.sk) sabs = 0.0;        // dims past the sketch
     ss = sum16(ss);
     sabs = sum16(sabs) / sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
-    if (i == 0) key_rec(p.c, slot)[kKeyWords] = norm_corr_word(ss, sabs);
+    if (i == 0) key_rec(p.c, slot)[p.c.kw] = norm_corr_word(ss, sabs, p.c.sk);
     encode_values(xv, i, p.c.Gv, val_rec(p.c, slot));
 }
 
@@ -237,9 +239,9 @@ __device__ __forceinline__ void append_small_block(const AppendParams &p, long N
     __syncthreads();
     if (t == 0) {
         uint32_t *kr = key_rec(p.c, slot);
-#pragma unroll
-        for (int q = 0; q < kKeyWords; ++q) kr[q] = rows[q];
-        kr[kKeyWords] = norm_corr_word((red[4] + red[5]) + (red[6] + red[7]), (red[0] + red[1]) + (red[2] + red[3]));
+        for (int q = 0; q < p.c.kw; ++q) kr[q] = rows[q];  // wave w holds rows 32 w .. 32 w + 31
+        const double sabs = p.c.kw == 4 ? (red[0] + red[1]) + (red[2] + red[3]) : red[0] + red[1];
+        kr[p.c.kw] = norm_corr_word((red[4] + red[5]) + (red[6] + red[7]), sabs, p.c.sk);
     }
     if (t >= 64 && t < 80)
         encode_values(xv, t - 64, p.c.Gv, val_rec(p.c, slot));

@@ -34,13 +34,19 @@ __device__ __forceinline__ size_t chunk_slot(const CacheView &c, const int *page
     return ((size_t)pages[(t >> c.logP) - p0] * c.Hkv + kvh) * c.P + (t & (c.P - 1));
 }
 
-// Key record of a slot: the 16 sign bytes (one 16-byte load at 4-byte alignment) and the
-// norm/corr word.
+// Key record of a slot: the sign bytes (one 16- or 8-byte load at 4-byte alignment; a
+// 64-bit sketch leaves the upper two words zero) and the norm/corr word.
 __device__ __forceinline__ void load_key(const CacheView &c, size_t slot, uint4 &kb, uint32_t &nc)
 {
     const uint32_t *kr = key_rec(c, slot);
-    __builtin_memcpy(&kb, kr, 16);
-    nc = kr[kKeyWords];
+    if (c.kw == 4) {
+        __builtin_memcpy(&kb, kr, 16);
+    } else {
+        uint2 lo;
+        __builtin_memcpy(&lo, kr, 8);
+        kb = make_uint4(lo.x, lo.y, 0u, 0u);
+    }
+    nc = kr[c.kw];
 }
 
 // Block-wide reduction of GB values per thread (256 threads); result broadcast in LDS.
@@ -209,10 +215,11 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 //   dense:    q'_r = fmaf chain over j ascending of R[r][j] * q_j (binary32)
 //   hadamard: x = sigma * q, in-place fast Walsh-Hadamard butterflies h = 1..64 (binary32),
 //             q' = x * fp32(1/sqrt(D))
+//   over the sketch's dims r < sk (the others get code 0):
 //   v_l = min q', delta = (max q' - v_l) / 15, u = clamp(rint((q' - v_l) / delta), 0, 15)
 //   (u = 0 when delta == 0), or clamp(floor((q' - v_l) / delta + U), 0, 15) with the
-//   caller's uniform U under stochastic rounding; the codes in dot8 order; c0 = v_l/sqrt(D),
-//   c1 = delta/sqrt(D).
+//   caller's uniform U under stochastic rounding; the codes in dot8 order; c0 = v_l/sqrt(sk),
+//   c1 = delta/sqrt(sk).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
 {
@@ -271,7 +278,8 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
         __syncthreads();
         x = xs[r] * isd;
     }
-    float mn = x, mx = x;
+    // the range of the sketch's dims (the first sk rotated coordinates)
+    float mn = r < p.sk ? x : INFINITY, mx = r < p.sk ? x : -INFINITY;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         mn = fminf(mn, __shfl_xor(mn, o));
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
     const float vr = fmaxf(redf[2], redf[3]);
     const float delta = (vr - vl) / 15.0f;
     int u = 0;
-    if (delta != 0.0f) {
+    if (delta != 0.0f && r < p.sk) {  // dims past the sketch keep code 0
         const float tq = (x - vl) / delta;
         float t = p.dither ? floorf(tq + p.dither[(size_t)bh * kD + r]) : rintf(tq);
         t = fminf(fmaxf(t, 0.0f), 15.0f);
@@ -317,13 +325,13 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
         p.qa[(size_t)bh * kD + r] = (uint8_t)fp8_e4m3_small(x);
     }
     su = redi[0] + redi[1];
-    if (r == 0) p.qpar[bh] = make_float4(vl * isd, delta * isd, __int_as_float(su), 0.0f);
+    if (r == 0) p.qpar[bh] = make_float4(vl * p.isk, delta * p.isk, __int_as_float(su), 0.0f);
     if (p.dbg_codes) p.dbg_codes[(size_t)bh * kD + r] = (uint8_t)u;
     if (r == 0 && p.dbg_params) {
         p.dbg_params[bh * 4 + 0] = vl;
         p.dbg_params[bh * 4 + 1] = delta;
-        p.dbg_params[bh * 4 + 2] = vl * isd;
-        p.dbg_params[bh * 4 + 3] = delta * isd;
+        p.dbg_params[bh * 4 + 2] = vl * p.isk;
+        p.dbg_params[bh * 4 + 3] = delta * p.isk;
     }
     if (r == 0 && p.dbg_sumu) p.dbg_sumu[bh] = su;
 }
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(64) void k_score(ScoreParams p)
             if (tl < n) {
                 float s[GB];
                 int A[GB];
-                score_key<GB>(kb[u], nc[u], qs, s, A);
+                score_key<GB>(kb[u], nc[u], qs, s, A, p.c.sk);
 #pragma unroll
                 for (int h = 0; h < GB; ++h) {
                     const int e = score_bin(s[h], p.kbin);
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp(ScoreParams p)
     for (int u = 0; u < U; ++u) {
         float s[GB];
         int A[GB];
-        score_key<GB>(kb[u], nc[u], qs, s, A);
+        score_key<GB>(kb[u], nc[u], qs, s, A, p.c.sk);
         // min() rather than a select, so that the score is computed on every lane
         // instead of behind a branch
         const int lim = lane + 64 * u < n ? INT_MAX : kNone;
@@ -612,7 +620,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
         uint32_t w[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
         const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                        __builtin_popcount(w[3]);
-        const float fP = (float)(2 * pc - kD);
+        const float fP = (float)(2 * pc - p.c.sk);
         const float r = half_bits_to_float(nc[u] & 0xFFFFu) / half_bits_to_float(nc[u] >> 16);
         swap32(w[0], w[2]);
         swap32(w[1], w[3]);
@@ -1070,7 +1078,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         float s[GB];
         {
             int A[GB];
-            score_key<GB>(kb, nc, qs, s, A);
+            score_key<GB>(kb, nc, qs, s, A, p.c.sk);
         }
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
@@ -1338,7 +1346,7 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
             }
         } else {
             int A;
-            score_key<1>(kb, nc, qs, &s, &A);
+            score_key<1>(kb, nc, qs, &s, &A, p.c.sk);
             if (lane >= nb) s = -INFINITY;
         }
         const float mnew = fmaxf(mrun, wave_max(s));

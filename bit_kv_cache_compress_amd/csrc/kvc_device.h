@@ -6,7 +6,6 @@
 namespace kvc {
 
 constexpr int kD = 128;            // head_dim handled by the kernels
-constexpr int kKeyWords = kD / 32;  // 32-bit words of sign bits per key
 constexpr int kBins = 8192;        // Top-p bin distances with non-zero weight
 constexpr int kBinClamp = 1 << 29;
 constexpr int kBlock = 256;
@@ -214,11 +213,12 @@ __device__ __forceinline__ uint32_t spread_key(uint32_t w, int k)
 
 // Proxy score of one cached key against GB query heads (binary x INT4, then the binary32
 // combine):  A = 2 * sum_r bit_r u_r - sumu  (= sum_r s_r u_r, s_r = +-1; the dot8 chain
-// starts at -sumu and wraps modulo 2^32), P = 2 * popcount(bits) - D  (= sum_r s_r),
+// starts at -sumu and wraps modulo 2^32), P = 2 * popcount(bits) - sk  (= sum_r s_r over the
+// sk sketch bits; the words past them are zero, as are the query codes of those dims),
 // score = fmaf(c1, A, c0 * P) * (norm / corr).
 template <int GB>
 __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const QueryState<GB> &qs,
-                                          float *s, int *A)
+                                          float *s, int *A, int sk)
 {
     const uint32_t w[4] = {kb.x, kb.y, kb.z, kb.w};
     uint32_t x[16];
@@ -228,7 +228,7 @@ __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const Que
         for (int k = 0; k < 4; ++k) x[4 * i + k] = spread_key(w[i], k);
     const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                    __builtin_popcount(w[3]);
-    const float fP = (float)(2 * pc - kD);
+    const float fP = (float)(2 * pc - sk);
     const float r = half_bits_to_float(nc & 0xFFFFu) / half_bits_to_float(nc >> 16);
     // the GB accumulation chains are interleaved so that consecutive dot products are
     // independent

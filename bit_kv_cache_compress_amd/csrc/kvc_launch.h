@@ -25,10 +25,12 @@ struct CacheView {
     uint8_t *vals;   // [pages][Hkv][P][64 + 4 * 128/Gv]: codes, scale/zero words
     uint16_t *kf16;  // nullable [pages][Hkv][P][128]: binary16 keys (unrotated)
     const float *kc; // nullable [Hkv][128]: key centers subtracted before the rotation
+    int kw;          // sign words per key record: 4 (the whole rotation) or 2 (a 64-bit sketch)
+    int sk;          // sign bits per key: 32 kw
 };
 
-// Key record of a slot (20 bytes: 4 sign words, then the norm/corr word).
-__device__ __forceinline__ uint32_t *key_rec(const CacheView &c, size_t slot) { return c.keys + slot * 5; }
+// Key record of a slot (kw sign words, then the norm/corr word: 20 or 12 bytes).
+__device__ __forceinline__ uint32_t *key_rec(const CacheView &c, size_t slot) { return c.keys + slot * (c.kw + 1); }
 // Value record of a slot (64 bytes of codes, then 128/Gv scale/zero words).
 __device__ __forceinline__ uint8_t *val_rec(const CacheView &c, size_t slot)
 {
@@ -90,6 +92,8 @@ struct QprepParams {
     uint8_t *dbg_codes;    // nullable [B*Hq][128]
     float *dbg_params;     // nullable [B*Hq][4]
     int32_t *dbg_sumu;     // nullable [B*Hq]
+    int sk;                // sketch width of the keys: dims quantized (the rest code 0)
+    float isk;             // fp32(1/sqrt(sk)), the scale of c0, c1
     const float *dither;   // nullable [B*Hq][128]: uniforms of the stochastic rounding
     int has_tail;          // blocks BH .. 2 BH - 1 attend over the binary16 tail
     TailParams tail;

@@ -59,12 +59,17 @@ enum { KV_F16 = 0, KV_F32 = 1 };
  * Token t of sequence b lives in physical page page_table[b][t / page_size], slot
  * t % page_size; the record of (page p, KV head h, slot s) has index
  * i = (p * num_kv_heads + h) * page_size + s in each of the two arrays:
- *   keys  uint32 [num_pages][Hkv][page_size][D/32 + 1], a 20-byte record per key:
- *         words 0..D/32-1: bit r of the rotated key k' = R k is bit r%32 of word r/32, set
- *           when k'_r >= 0.  Read as little-endian bytes this is byte r/8, bit r%8, set = +1:
- *           the bitmap order of the H1IB-KV page, section 二.3.
- *         word D/32: binary16 |k| in the low half, binary16 correction
- *           sum_r |k'_r| / (sqrt(D) |k|) in the high half (1.0 for k = 0).
+ *   keys  uint32 [num_pages][Hkv][page_size][S/32 + 1], a 20-byte record per key (12 bytes
+ *         for S = 64), with S = sketch_dim (the sign bits per key, D unless set to 64):
+ *         words 0..S/32-1: bit r of the rotated key k' = R k is bit r%32 of word r/32, set
+ *           when k'_r >= 0, for r < S.  Read as little-endian bytes this is byte r/8, bit
+ *           r%8, set = +1: the bitmap order of the H1IB-KV page, section 二.3.
+ *         word S/32: binary16 |k| in the low half, binary16 correction
+ *           sum_{r<S} |k'_r| / (sqrt(S) |k|) in the high half (1.0 for k = 0).
+ *   S < D is a narrow sketch, the non-square random projection onto the first S rows of R
+ *   (H1B-KV key design: a 1-bit key sketch by random projection): the query is quantized
+ *   over the same S coordinates and the estimator keeps its form with S in place of D in
+ *   its sign part (x = sign(k'_{<S})/sqrt(S)); the softmax temperature stays 1/sqrt(D).
  *   vals  uint8 [num_pages][Hkv][page_size][D/2 + 4 D/value_group], a record per value:
  *         bytes 0..D/2-1: 4-bit codes, dim 2m in the low nibble of byte m and dim 2m+1 in
  *           the high nibble;
@@ -107,6 +112,7 @@ typedef struct kv_cache {
     uint8_t *vals;         /* device, 4-byte aligned: see above */
     uint16_t *keys_f16;    /* device, nullable, 16-byte aligned: see above */
     const float *key_center; /* device, nullable, 16-byte aligned: see above */
+    int32_t sketch_dim;    /* sign bits per key: 0 or D (the whole rotation), or 64 */
 } kv_cache;
 
 /* Optional intermediate outputs of kv_decode_attend ([host] struct; every member is a

@@ -29,9 +29,9 @@ class Case:
     def max_len(self):
         return int(max(1, self.lens.max()))
 
-    def oracle_cache(self, exact_keys=False, key_center=None):
+    def oracle_cache(self, exact_keys=False, key_center=None, sketch=None):
         c = oracle.PagedCache(self.npages, self.wl.Hkv, self.wl.P, self.wl.D, self.wl.Gv, exact_keys=exact_keys,
-                              key_center=key_center)
+                              key_center=key_center, sketch=sketch)
         for b in range(self.wl.B):
             n = int(self.lens[b])
             if n:
@@ -43,21 +43,22 @@ class Case:
         return oracle.decode(cache, self.orot, self.q, self.lens, self.pt, top_p, heads=heads)
 
 
-def gpu_empty_cache(case: Case, device="cuda", exact_keys=False, key_center=None):
+def gpu_empty_cache(case: Case, device="cuda", exact_keys=False, key_center=None, sketch=None):
     from bit_kv_cache_compress_amd import KVCache
 
     rot = case.rot_raw
     return KVCache(case.npages, case.wl.Hkv, rot, rot_kind=case.rot_kind, page_size=case.wl.P,
-                   value_group=case.wl.Gv, device=device, exact_keys=exact_keys, key_center=key_center)
+                   value_group=case.wl.Gv, device=device, exact_keys=exact_keys, key_center=key_center,
+                   sketch_dim=sketch or case.wl.D)
 
 
-def gpu_append(case: Case, chunk=None, device="cuda", exact_keys=False, key_center=None):
+def gpu_append(case: Case, chunk=None, device="cuda", exact_keys=False, key_center=None, sketch=None):
     """The library's append of every sequence (optionally in chunks of `chunk` tokens)."""
     import torch
 
     from bit_kv_cache_compress_amd import append
 
-    cache = gpu_empty_cache(case, device, exact_keys=exact_keys, key_center=key_center)
+    cache = gpu_empty_cache(case, device, exact_keys=exact_keys, key_center=key_center, sketch=sketch)
     for b in range(case.wl.B):
         n = int(case.lens[b])
         step = n if chunk is None else chunk
@@ -76,7 +77,8 @@ def upload(cache_o: oracle.PagedCache, case: Case, device="cuda"):
     """A library cache holding the oracle's bytes."""
     import torch
 
-    g = gpu_empty_cache(case, device, exact_keys=cache_o.key_f16 is not None, key_center=cache_o.key_center)
+    g = gpu_empty_cache(case, device, exact_keys=cache_o.key_f16 is not None, key_center=cache_o.key_center,
+                        sketch=cache_o.sk)
     if cache_o.key_f16 is not None:
         g.keys_f16.copy_(torch.from_numpy(cache_o.key_f16))
     g.key_bits.copy_(torch.from_numpy(cache_o.key_bits.view(np.int32)))
@@ -130,7 +132,7 @@ def compare_caches(gpu: dict, ocache: oracle.PagedCache, case: Case):
                 else:
                     mag = np.full(case.wl.D, np.abs(k.astype(np.float64)).sum() / np.sqrt(case.wl.D))
                 xb = np.bitwise_xor(gpu["key_bits"][pg[i], h, sl[i]], ocache.key_bits[pg[i], h, sl[i]])
-                for w in range(case.wl.D // 32):
+                for w in range(xb.shape[-1]):  # the record's sign words (a sketch may hold fewer)
                     for bit in range(32):
                         if (int(xb[w]) >> bit) & 1:
                             r = 32 * w + bit

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def _desc(**kw):
     d = dict(head_dim=128, num_kv_heads=8, value_group=32, page_size=256, num_pages=16, rot_kind=0,
-             rot=0x10000, keys=0x10000, vals=0x10000, keys_f16=None, key_center=None)
+             rot=0x10000, keys=0x10000, vals=0x10000, keys_f16=None, key_center=None, sketch_dim=0)
     d.update(kw)
     return L.KVCacheDesc(*[d[f] for f, _ in L.KVCacheDesc._fields_])
 
@@ -54,6 +54,7 @@ def _decode(desc, B=2, Hq=32, max_seq_len=1000, max_pages=4, top_p=1.0, ws_bytes
     (dict(keys=0), L.KV_ERR_ARG),
     (dict(keys_f16=0x10008), L.KV_ERR_ARG),  # binary16 keys not 16-byte aligned
     (dict(key_center=0x10004), L.KV_ERR_ARG),  # key centers not 16-byte aligned
+    (dict(sketch_dim=96), L.KV_ERR_UNSUPPORTED),  # sketch widths are 128 and 64
     (dict(vals=0), L.KV_ERR_ARG),
     (dict(rot=0), L.KV_ERR_ARG),
 ])

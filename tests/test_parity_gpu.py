@@ -902,3 +902,44 @@ def test_degenerate_inputs(rot):
             assert int(dbg.sel_count[1, 0]) == 700
         _say(f"[degenerate] {rot} top_p={top_p} ok")
     assert np.all(ref[(0, 0)]["u"] == 0)
+
+
+@pytest.mark.parametrize("name", ["c1-full-fp32-dense", "c2-outliers-ragged", "c3-gqa4-spikes-topp",
+                                  "c4-paged-g64-ragged", "c5-hadamard-topp", "gqa2-pages16-p0.5", "gqa8-topp"])
+def test_narrow_sketch(name):
+    """A 64-bit key sketch (the first 64 rotated coordinates, 12-byte key records) against the
+    oracle's: appended bytes bit-exact, the query codes and parameters, integer and binary32
+    scores and Top-p sets bit-exact, outputs within the bar, at the case's Top-p and with
+    full softmax (the matrix-core, dot8 and full-softmax score paths)."""
+    c = _case(name)
+    oc = c.oracle_cache(sketch=64)
+    _say(f"[sketch] {name} append")
+    g = gpu_append(c, sketch=64)
+    stats = compare_caches(download(g), oc, c)
+    assert g.keys.shape[-1] == 3
+    for top_p in sorted({c.wl.top_p, 1.0}):
+        out, dbg = _decode_with_debug(c, g, top_p)
+        ref = c.oracle_decode(oc, top_p)
+        qc, qp = dbg.q_codes.cpu().numpy(), dbg.q_params.cpu().numpy()
+        A, S = dbg.iscores.cpu().numpy(), dbg.scores.cpu().numpy()
+        worst = 0.0
+        for (b, h), r in ref.items():
+            np.testing.assert_array_equal(qc[b, h], r["u"])
+            assert np.all(r["u"][64:] == 0)
+            np.testing.assert_array_equal(qp[b, h], np.array([r["vl"], r["delta"], r["c0"], r["c1"]], np.float32))
+            n = int(c.lens[b])
+            np.testing.assert_array_equal(A[b, h, :n], r["A"])
+            np.testing.assert_array_equal(S[b, h, :n].view(np.uint32), r["score"].view(np.uint32))
+            if top_p < 1.0 and n > 0:
+                cnt = int(dbg.sel_count[b, h])
+                np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            if n == 0:
+                assert np.abs(out[b, h]).max() == 0.0
+                continue
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (top_p, b, h, e)
+        # the fast path (no debug outputs) gives the same result
+        out2, _ = _decode_with_debug(c, g, top_p, scores=False)
+        np.testing.assert_array_equal(out2.view(np.uint32), out.view(np.uint32))
+        _say(f"[sketch] {name} top_p={top_p} ok {stats}, worst rel err {worst:.2e}")
