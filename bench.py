@@ -30,7 +30,6 @@ HBM_PEAK_GBS = 8000.0
 # word per token-KV-head; a cached value is 64 B of 4-bit codes + a 4 B scale/zero word per
 # group.  Top-p adds a 2 B bin distance per (token, query head), written by the score pass
 # and read by the histogram and attention passes.
-KEY_BYTES = 20
 DIST_BYTES = 2
 
 
@@ -57,6 +56,8 @@ def parse():
                          "filled at each page compression by accumulated attention mass")
     ap.add_argument("--separate-append", action="store_true",
                     help="append the step's new tokens with a call of their own instead of inside the decode")
+    ap.add_argument("--sketch-dim", type=int, default=128, choices=(128, 64),
+                    help="sign bits per key: 128, or a narrow 64-bit sketch (12-byte key records)")
     ap.add_argument("--center-keys", action="store_true",
                     help="estimator variant: per-head key centers (the mean of the prefill keys)")
     ap.add_argument("--stochastic-query", action="store_true",
@@ -244,7 +245,7 @@ def main():
             center += K[b, :int(lens[b]) - 1].double().sum(dim=0)
         center = (center / float(max(int(lens.sum()) - B, 1))).float()
     cache = kvc.KVCache(npages, Hkv, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev,
-                        exact_keys=args.exact_keys, key_center=center)
+                        exact_keys=args.exact_keys, key_center=center, sketch_dim=args.sketch_dim)
     dither = None
     if args.stochastic_query:
         gd = torch.Generator(device=dev)
@@ -373,19 +374,20 @@ def main():
     # ---- roofline of the dominant kernel
     G = Hq // Hkv
     kv_in = 2 if wl.kv_dtype == "f16" else 4
-    kept_key_bytes = 2 * D if args.exact_keys and wl.top_p < 1.0 else KEY_BYTES
+    key_bytes = 4 * (args.sketch_dim // 32 + 1)  # the key record: sign words and the norm/corr word
+    kept_key_bytes = 2 * D if args.exact_keys and wl.top_p < 1.0 else key_bytes
     per_launch = {
         # every key of the context, each scored for the G query heads of its KV head, and
         # the bin distances written
-        "score": (KEY_BYTES + DIST_BYTES * G) * tokens_heads if wl.top_p < 1.0 else KEY_BYTES * tokens_heads,
+        "score": (key_bytes + DIST_BYTES * G) * tokens_heads if wl.top_p < 1.0 else key_bytes * tokens_heads,
         # Top-p: the distances, then key and value of every kept (token, query head);
         # full softmax: every key and value once per KV head
         # (with binary16 keys, the 2 D bytes of the key instead of its 20-byte record)
         "attend": (DIST_BYTES * G * tokens_heads + (kept_key_bytes + value_bytes(Gv)) * sel_entries)
-        if sel_entries is not None else (KEY_BYTES + value_bytes(Gv)) * tokens_heads,
+        if sel_entries is not None else (key_bytes + value_bytes(Gv)) * tokens_heads,
         # the distances once
         "hist": DIST_BYTES * G * tokens_heads,
-        "append": (2 * D * kv_in + KEY_BYTES + value_bytes(Gv) + (2 * D if args.exact_keys else 0)) * B * Hkv}
+        "append": (2 * D * kv_in + key_bytes + value_bytes(Gv) + (2 * D if args.exact_keys else 0)) * B * Hkv}
     score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if wl.top_p < 1.0 else "k_score"
     kernel_names = {"score": score_kernel, "append": "k_append",
                     "attend": "k_attend_topp" if wl.top_p < 1.0 else "k_attend", "hist": "k_hist",
@@ -394,7 +396,8 @@ def main():
     ach = per_launch[dominant] / (stage_ms[dominant] / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": None if (args.exact_keys or args.center_keys or args.stochastic_query)
+                "traffic": None if (args.exact_keys or args.center_keys or args.stochastic_query
+                                    or args.sketch_dim != D)
                 else measured_traffic(kernel_names[dominant], wl.name),
                 "algorithmic_bytes_per_launch": per_launch[dominant],
                 "avg_launch_us": round(stage_ms[dominant] * 1e3, 2)}
@@ -403,9 +406,9 @@ def main():
     # the appended token
     if sel_union is not None:
         kept = value_bytes(Gv) + (2 * D if args.exact_keys else 0)
-        step_alg = per_launch["append"] + KEY_BYTES * tokens_heads + kept * sel_union
+        step_alg = per_launch["append"] + key_bytes * tokens_heads + kept * sel_union
     else:
-        step_alg = per_launch["append"] + (KEY_BYTES + value_bytes(Gv)) * tokens_heads
+        step_alg = per_launch["append"] + (key_bytes + value_bytes(Gv)) * tokens_heads
     log(f"[bench] dominant {dominant}: {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
 
     result = {
@@ -418,7 +421,8 @@ def main():
                    "step": "append 1 token per sequence + decode attention"
                            + (" (two calls)" if args.separate_append else " (one call, fused append)"),
                    "cache_flushed_between_steps": not args.no_flush, "exact_keys": args.exact_keys,
-                   "key_center": args.center_keys, "stochastic_query": args.stochastic_query},
+                   "key_center": args.center_keys, "stochastic_query": args.stochastic_query,
+                   "sketch_dim": args.sketch_dim},
         "roofline": roofline,
         "step_hbm_frac_algorithmic": round(step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "query_head_tokens_per_s": value * (Hq // Hkv),
@@ -430,7 +434,7 @@ def main():
         result["topp_selected_union_token_kv_heads"] = sel_union
         result["topp_selected_token_query_heads"] = sel_entries
 
-    variant = args.exact_keys or args.center_keys or args.stochastic_query
+    variant = args.exact_keys or args.center_keys or args.stochastic_query or args.sketch_dim != D
     if variant and not args.no_cpu_baseline:
         log("[cpu] no oracle baseline for the variant modes (the default run has it)")
     elif not args.no_cpu_baseline:

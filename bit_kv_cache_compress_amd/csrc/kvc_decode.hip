@@ -49,6 +49,22 @@ __device__ __forceinline__ void load_key(const CacheView &c, size_t slot, uint4 
     nc = kr[c.kw];
 }
 
+// load_key for a record width known at compile time (KW sign words): the fast paths are
+// instantiated per width, so their unrolled key loads carry no width test.
+template <int KW>
+__device__ __forceinline__ void load_key_t(const CacheView &c, size_t slot, uint4 &kb, uint32_t &nc)
+{
+    const uint32_t *kr = c.keys + slot * (KW + 1);
+    if constexpr (KW == 4) {
+        __builtin_memcpy(&kb, kr, 16);
+    } else {
+        uint2 lo;
+        __builtin_memcpy(&lo, kr, 8);
+        kb = make_uint4(lo.x, lo.y, 0u, 0u);
+    }
+    nc = kr[KW];
+}
+
 // Block-wide reduction of GB values per thread (256 threads); result broadcast in LDS.
 template <int GB, typename T, typename Op>
 __device__ __forceinline__ void block_reduce(T (&v)[GB], T *red /* [4][GB] */, T *out /* [GB] */, Op op)
@@ -438,7 +454,7 @@ __global__ __launch_bounds__(64) void k_score(ScoreParams p)
 // ---------------------------------------------------------------------------------------
 // At most 128 VGPRs (4 waves per SIMD requested); the compiler then fits the kernel in 70,
 // 7 waves per SIMD, which the key-load latency needs.
-template <int GB>
+template <int GB, int KW>
 __global__ __launch_bounds__(64, 4) void k_score_topp(ScoreParams p)
 {
     constexpr int CH = kTopPChunk;
@@ -491,14 +507,14 @@ __global__ __launch_bounds__(64, 4) void k_score_topp(ScoreParams p)
     uint32_t nc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        load_key(p.c, slot[u], kb[u], nc[u]);
+        load_key_t<KW>(p.c, slot[u], kb[u], nc[u]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float s[GB];
         int A[GB];
-        score_key<GB>(kb[u], nc[u], qs, s, A, p.c.sk);
+        score_key<GB>(kb[u], nc[u], qs, s, A, 32 * KW);
         // min() rather than a select, so that the score is computed on every lane
         // instead of behind a branch
         const int lim = lane + 64 * u < n ? INT_MAX : kNone;
@@ -558,6 +574,7 @@ __device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
     b = r[1];
 }
 
+template <int KW>
 __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
 {
     constexpr int GB = 4;
@@ -612,7 +629,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
     uint4 kb[U];
     uint32_t nc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_key(p.c, slot[u], kb[u], nc[u]);
+    for (int u = 0; u < U; ++u) load_key_t<KW>(p.c, slot[u], kb[u], nc[u]);
     __builtin_amdgcn_sched_barrier(0);
     int e[U][GB];
 #pragma unroll
@@ -620,7 +637,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
         uint32_t w[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
         const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                        __builtin_popcount(w[3]);
-        const float fP = (float)(2 * pc - p.c.sk);
+        const float fP = (float)(2 * pc - 32 * KW);
         const float r = half_bits_to_float(nc[u] & 0xFFFFu) / half_bits_to_float(nc[u] >> 16);
         swap32(w[0], w[2]);
         swap32(w[1], w[3]);
@@ -705,7 +722,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
 {
     constexpr int kT = kHistThreads;
     constexpr int U = 32768 / (8 * kT);    // 16-byte loads per thread: 32768 tokens per round
-    __shared__ uint32_t hist[kBins + 1];  // + a bin for tokens that are not counted
+    __shared__ uint32_t hist[kBins];
     __shared__ int delta[kT];
     __shared__ int red[kT / 64];
     const DecodeGeom &g = p.g;
@@ -733,7 +750,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
     const int lmc = tid < c1 - c0 ? p.lmax[bh * g.NC + c0 + tid] : 0;
     int m = -kBinClamp;
     for (int c = tid; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
-    for (int i = tid; i <= kBins; i += kT) hist[i] = 0u;
+    for (int i = tid; i < kBins; i += kT) hist[i] = 0u;
     m = wave_max_i(m);
     if (lane == 0) red[wave] = m;
     __syncthreads();
@@ -751,8 +768,10 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
                 const int dc = delta[(tu >> g.logCH) - c0];  // 8 tokens share a chunk
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
+                    // tokens past the last bin have no weight and are not counted (sending them
+                    // all to one spare counter made it a hot spot when many fall there)
                     const int d = dc + (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                    atomicAdd(&hist[(tu + e < te && d < kBins) ? d : kBins], 1u);
+                    if (tu + e < te && d < kBins) atomicAdd(&hist[d], 1u);
                 }
             }
         }
@@ -994,7 +1013,7 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 // lane accumulates weight x decoded value for its 8 dims (the zero point once per token).
 // The wave writes (m, sum of weights, weighted value sums) per head for the merge.
 // ---------------------------------------------------------------------------------------
-template <int GB, int GV>
+template <int GB, int GV, int KW>
 __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 {
     constexpr int NB = 64;        // tokens per batch
@@ -1055,7 +1074,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
             // a whole batch inside one page: consecutive slots
             const uint32_t first = (uint32_t)(t0 + bs);
             const uint32_t s0 = pbase[(first >> logP) - p0] + (first & tmask);
-            load_key(p.c, s0 + lane, kb, nc);
+            load_key_t<KW>(p.c, s0 + lane, kb, nc);
             const uint8_t *vr = p.c.vals + (size_t)(s0 + eg) * VREC;
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
@@ -1065,7 +1084,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         } else {
             {
                 const uint32_t t = (uint32_t)(t0 + bs + min(lane, nb - 1));
-                load_key(p.c, pbase[(t >> logP) - p0] + (t & tmask), kb, nc);
+                load_key_t<KW>(p.c, pbase[(t >> logP) - p0] + (t & tmask), kb, nc);
             }
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
@@ -1078,7 +1097,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         float s[GB];
         {
             int A[GB];
-            score_key<GB>(kb, nc, qs, s, A, p.c.sk);
+            score_key<GB>(kb, nc, qs, s, A, 32 * KW);
         }
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
@@ -1165,7 +1184,7 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
     return __int_as_float(r);
 }
 
-template <bool EXACT>
+template <bool EXACT, int KW>
 __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
 {
     constexpr int CHA = kTopPAttendChunk;  // tokens of the attention chunk
@@ -1301,7 +1320,7 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
         }
         uint4 kb;
         uint32_t nc;
-        if constexpr (!EXACT) load_key(p.c, sl[VU], kb, nc);
+        if constexpr (!EXACT) load_key_t<KW>(p.c, sl[VU], kb, nc);
         uint4 kx[EXACT ? VU : 1][4];  // exact scores: binary16 key dims 32 q4 .. 32 q4 + 31
         if constexpr (EXACT) {
 #pragma unroll
@@ -1346,7 +1365,7 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
             }
         } else {
             int A;
-            score_key<1>(kb, nc, qs, &s, &A, p.c.sk);
+            score_key<1>(kb, nc, qs, &s, &A, 32 * KW);
             if (lane >= nb) s = -INFINITY;
         }
         const float mnew = fmaxf(mrun, wave_max(s));
@@ -1608,6 +1627,14 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     if (MASS) mass_finish(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog, mf);
 }
 
+// The full-softmax kernel for the cache's key record width.
+template <int GB, int GV>
+void launch_full(const AttendParams &p, dim3 grid, hipStream_t s)
+{
+    if (p.c.kw == 4) hipLaunchKernelGGL((k_attend_full<GB, GV, 4>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((k_attend_full<GB, GV, 2>), grid, dim3(64), 0, s, p);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -1629,9 +1656,18 @@ hipError_t launch_score(const ScoreParams &p, hipStream_t s)
     const bool dbg = p.dbg_scores || p.dbg_iscores;
     if (!dbg && p.dl && p.g.CH == kTopPChunk) {
         switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_score_topp<1>), grid, blk, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_score_topp<2>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL(k_score_topp_mf, grid, blk, 0, s, p); break;
+        case 1:
+            if (p.c.kw == 4) hipLaunchKernelGGL((k_score_topp<1, 4>), grid, blk, 0, s, p);
+            else hipLaunchKernelGGL((k_score_topp<1, 2>), grid, blk, 0, s, p);
+            break;
+        case 2:
+            if (p.c.kw == 4) hipLaunchKernelGGL((k_score_topp<2, 4>), grid, blk, 0, s, p);
+            else hipLaunchKernelGGL((k_score_topp<2, 2>), grid, blk, 0, s, p);
+            break;
+        default:
+            if (p.c.kw == 4) hipLaunchKernelGGL(k_score_topp_mf<4>, grid, blk, 0, s, p);
+            else hipLaunchKernelGGL(k_score_topp_mf<2>, grid, blk, 0, s, p);
+            break;
         }
     } else {
         // debug scores: the Top-p chunks, or the larger chunks of a full-softmax decode
@@ -1675,8 +1711,14 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         // one wave per (attention chunk, query head, sequence)
         const dim3 grid(p.g.NCA, p.g.Hq, p.g.B);
         if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
-        if (p.c.kf16) hipLaunchKernelGGL(k_attend_topp<true>, grid, dim3(64), 0, s, p);
-        else hipLaunchKernelGGL(k_attend_topp<false>, grid, dim3(64), 0, s, p);
+        const bool w4 = p.c.kw == 4;
+        if (p.c.kf16) {
+            if (w4) hipLaunchKernelGGL((k_attend_topp<true, 4>), grid, dim3(64), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_topp<true, 2>), grid, dim3(64), 0, s, p);
+        } else {
+            if (w4) hipLaunchKernelGGL((k_attend_topp<false, 4>), grid, dim3(64), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_topp<false, 2>), grid, dim3(64), 0, s, p);
+        }
     } else {
         // one wave per (chunk, KV-head group, sequence)
         const dim3 grid(p.g.NCA, p.g.Hkv * p.g.nsub, p.g.B);
@@ -1684,16 +1726,16 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         const bool g32 = p.c.Gv == 32;
         switch (p.g.GB) {
         case 1:
-            if (g32) hipLaunchKernelGGL((k_attend_full<1, 32>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_full<1, 64>), grid, dim3(64), 0, s, p);
+            if (g32) launch_full<1, 32>(p, grid, s);
+            else launch_full<1, 64>(p, grid, s);
             break;
         case 2:
-            if (g32) hipLaunchKernelGGL((k_attend_full<2, 32>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_full<2, 64>), grid, dim3(64), 0, s, p);
+            if (g32) launch_full<2, 32>(p, grid, s);
+            else launch_full<2, 64>(p, grid, s);
             break;
         default:
-            if (g32) hipLaunchKernelGGL((k_attend_full<4, 32>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_full<4, 64>), grid, dim3(64), 0, s, p);
+            if (g32) launch_full<4, 32>(p, grid, s);
+            else launch_full<4, 64>(p, grid, s);
             break;
         }
     }
