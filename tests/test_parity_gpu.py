@@ -542,7 +542,7 @@ def test_stochastic_query_rounding(name):
     _say(f"[dither] {name} tail ok")
 
 
-def _tier_case(c, lc, C, seed):
+def _tier_case(c, lc, C, seed, sketch=None):
     """An oracle cache copy with, per (sequence, KV head), up to 5 of its compressed tokens moved
     into a high-precision tier of C entries (scattered slots), and the same state on the GPU."""
     import copy
@@ -551,7 +551,7 @@ def _tier_case(c, lc, C, seed):
 
     rng = np.random.default_rng(seed)
     B, Hkv, D = c.wl.B, c.wl.Hkv, c.wl.D
-    oc = copy.deepcopy(c.ocache)
+    oc = copy.deepcopy(c.ocache) if sketch is None else c.oracle_cache(sketch=sketch)
     hp = oracle.HPTier(B, Hkv, C, D)
     slots = [1, 3, 4, 6, 7]
     for b in range(B):
@@ -625,10 +625,12 @@ def test_hp_tier_decode(name):
         _say(f"[tier] {name} top_p={top_p} ok, worst rel err {worst:.2e}, tier mass {hp.mass.sum():.3f}")
 
 
-@pytest.mark.parametrize("name", ["c3-gqa4-spikes-topp", "c5-hadamard-topp"])
-def test_hp_tier_update(name):
+@pytest.mark.parametrize("name,sketch", [("c3-gqa4-spikes-topp", None), ("c5-hadamard-topp", None),
+                                         ("c3-gqa4-spikes-topp", 64)])
+def test_hp_tier_update(name, sketch):
     """The promotion step against the oracle on caller-set masses (distinct values plus ties):
-    tier positions, saved words, masses, binary16 rows and every key record bit-exact."""
+    tier positions, saved words, masses, binary16 rows and every key record bit-exact (also
+    with 12-byte records of a 64-bit sketch, whose norm/correction word is word 2)."""
     from bit_kv_cache_compress_amd import Tail
 
     c = _case(name)
@@ -636,7 +638,7 @@ def test_hp_tier_update(name):
     B, Hkv, D, P = c.wl.B, c.wl.Hkv, c.wl.D, c.wl.P
     n = min(P, 128)
     lc = (c.lens - n).astype(np.int32)  # the last n tokens are the tail page just compressed
-    oc, hp, g, hg = _tier_case(c, lc, 16, 41)
+    oc, hp, g, hg = _tier_case(c, lc, 16, 41, sketch)
     rng = np.random.default_rng(42)
     hp.mass[:] = np.where(hp.pos >= 0, rng.random(hp.pos.shape).astype(np.float32), 0.0)
     tmass = rng.random((B, n, Hkv)).astype(np.float32) * 1.2
@@ -943,3 +945,14 @@ def test_narrow_sketch(name):
         out2, _ = _decode_with_debug(c, g, top_p, scores=False)
         np.testing.assert_array_equal(out2.view(np.uint32), out.view(np.uint32))
         _say(f"[sketch] {name} top_p={top_p} ok {stats}, worst rel err {worst:.2e}")
+    if c.wl.top_p < 1.0:
+        # binary16 keys: the sketch chooses the set, the softmax uses exact scores
+        oe = c.oracle_cache(exact_keys=True, sketch=64)
+        ge = upload(oe, c)
+        out, _ = _decode_with_debug(c, ge, c.wl.top_p, scores=False)
+        ref = c.oracle_decode(oe, c.wl.top_p)
+        for (b, h), r in ref.items():
+            if int(c.lens[b]) == 0:
+                continue
+            assert rel_err(out[b, h], r["out"]) <= TOL, ("exact", b, h)
+        _say(f"[sketch] {name} exact scores ok")
