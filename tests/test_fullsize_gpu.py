@@ -121,6 +121,25 @@ def test_gqa_128k_topp_full_size():
             assert rel_err(of[b, hh], r["out_full"]) <= 2e-3
         _say(f"[full] unit {(b, h)} ok: cache identical={same}, kept {cnt[b, h * G:(h + 1) * G].tolist()}")
 
+    # the step as the benchmark times it: tokens 0 .. L-2 appended, then one decode call that
+    # appends token L-1 itself (its encoding inside the query-preparation launch)
+    del cache, dbg
+    cache2 = kvc.KVCache(npages, Hkv, R16, rot_kind=kind, page_size=wl.P, value_group=wl.Gv, device=dev)
+    kvc.append(cache2, K[:, :L - 1].contiguous(), V[:, :L - 1].contiguous(), torch.zeros(B, dtype=torch.int32, device=dev),
+               pt)
+    out2 = kvc.decode_attend(cache2, q, seq, pt, top_p=wl.top_p, max_seq_len=L,
+                             append=(K[:, L - 1:].contiguous(), V[:, L - 1:].contiguous(),
+                                     torch.full((B,), L - 1, dtype=torch.int32, device=dev)))
+    torch.cuda.synchronize()
+    o2 = out2.cpu().numpy()
+    kb2 = cache2.key_bits.cpu().numpy().view(np.uint32)
+    for (b, h), (bits, nc, codes, sz, res) in zip(SAMPLED_UNITS, refs):
+        pg, sl = pt_np[b, (L - 1) // wl.P], (L - 1) % wl.P
+        np.testing.assert_array_equal(kb2[pg, h, sl], bits[L - 1])
+        for j, hh in enumerate(range(h * G, (h + 1) * G)):
+            assert rel_err(o2[b, hh], res[j]["out"]) <= 2e-3
+    _say("[full] the benchmark's step (append inside the decode) ok")
+
 
 def _check_unit_cache(kb, kn, vc, vs, pg, sl, h, bits, nc, codes, sz):
     """Cache bytes of one unit: sign words and norms exact, correction within one binary16
