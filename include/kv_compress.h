@@ -75,7 +75,7 @@ enum { KV_F16 = 0, KV_F32 = 1 };
  *           the high nibble;
  *         then one uint32 per group of value_group dims: binary16 scale in the low half,
  *           binary16 zero point in the high half; value = code * scale + zero.
- * A key and a value are each one contiguous record (20 and 80 or 72 bytes), so that a
+ * A key and a value are each one contiguous record (20 or 12 and 80 or 72 bytes), so that a
  * decode that gathers a few selected tokens touches one or two 128-byte lines per record
  * rather than one per field.
  * keys_f16 (nullable): binary16 [num_pages][Hkv][page_size][D], the keys themselves (not
