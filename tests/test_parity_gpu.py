@@ -956,3 +956,40 @@ def test_narrow_sketch(name):
                 continue
             assert rel_err(out[b, h], r["out"]) <= TOL, ("exact", b, h)
         _say(f"[sketch] {name} exact scores ok")
+
+
+@pytest.mark.parametrize("top_p", [0.9, 1.0])
+def test_chunk_boundary_lengths(top_p):
+    """Sequence lengths on both sides of the 512-token score chunks, the 1024-token attention
+    chunks and the 256-token pages (masking of the last chunk, of the last histogram split
+    and of the merge's chunk count), and a batch of empty sequences."""
+    from bit_kv_cache_compress_amd import decode_attend
+
+    lens = [1, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047, 2049]
+    wl = W.CONFIGS[2].scaled(B=len(lens), Hq=4, Hkv=1, P=256, top_p=top_p)
+    c = Case(wl, L=max(lens), seq_lens=lens)
+    c.ocache = c.oracle_cache()
+    dev = torch.device("cuda")
+    g = upload(c.ocache, c)
+    q = torch.from_numpy(c.q).to(dev)
+    lt = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
+    # four extra page-table columns (page 0, never reached) let a workspace be planned for
+    # sequences longer than any present
+    wide = np.concatenate([c.pt, np.zeros((c.pt.shape[0], 4), c.pt.dtype)], axis=1)
+    pt = torch.from_numpy(wide).to(dev)
+    for max_len in (c.max_len, wide.shape[1] * 256):
+        out = decode_attend(g, q, lt, pt, top_p=top_p, max_seq_len=max_len)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        ref = c.oracle_decode(c.ocache, top_p)
+        worst = 0.0
+        for (b, h), r in ref.items():
+            e = float(rel_err(out[b, h], r["out"]))
+            worst = max(worst, e)
+            assert e <= TOL, (max_len, lens[b], h, e)
+        _say(f"[boundary] top_p={top_p} max_len={max_len} ok, worst rel err {worst:.2e}")
+    # every sequence empty: zeros
+    zero = torch.zeros_like(lt)
+    out = decode_attend(g, q, zero, pt, top_p=top_p, max_seq_len=c.max_len)
+    torch.cuda.synchronize()
+    assert float(out.abs().max()) == 0.0
