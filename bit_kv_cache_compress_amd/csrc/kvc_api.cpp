@@ -44,7 +44,7 @@ struct Plan {
     kvc::DecodeGeom g;
     bool topp;
     int nsplit, cps;
-    size_t off_qpl, off_qa, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_pm, off_pl, off_po, off_tm, off_tl, off_to;
+    size_t off_qpl, off_qa, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_order, off_octr, off_pm, off_pl, off_po, off_tm, off_tl, off_to;
     size_t total;
 };
 
@@ -122,9 +122,11 @@ void plan_layout(Plan &pl, int BH)
         pl.off_hist = take((size_t)BH * nsplit * 8192 * 2);
         pl.off_sel = take((size_t)BH * 4 * 4);
         pl.off_cnt = take((size_t)BH * NC * 4);
+        pl.off_order = take((size_t)BH * 4);
+        pl.off_octr = take(2 * 4);
     } else {
         pl.nsplit = pl.cps = 0;
-        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = 0;
+        pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = pl.off_order = pl.off_octr = 0;
     }
     pl.total = o;
 }
@@ -423,6 +425,8 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
         hp.lmax = sp.lmax;
         hp.hist = at<uint16_t>(workspace, pl.off_hist);
         hp.sel = at<int32_t>(workspace, pl.off_sel);
+        hp.order = at<int32_t>(workspace, pl.off_order);
+        hp.order_ctr = at<int32_t>(workspace, pl.off_octr);
         hp.dbg_count = dbg ? dbg->sel_count : nullptr;
         hp.dbg_bins = dbg ? dbg->sel_bins : nullptr;
         stage_mark(dbg, KV_STAGE_HIST, true, stream);
@@ -459,6 +463,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     ap.dl = sp.dl;
     ap.lmax = sp.lmax;
     ap.sel = pl.topp ? at<int32_t>(workspace, pl.off_sel) : nullptr;
+    ap.order = pl.topp ? at<int32_t>(workspace, pl.off_order) : nullptr;
     ap.pm = at<float>(workspace, pl.off_pm);
     ap.pl = at<float>(workspace, pl.off_pl);
     ap.po = at<float>(workspace, pl.off_po);
@@ -703,6 +708,7 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     hp.lmax = bp.lmax;
     hp.hist = at<uint16_t>(workspace, pl.off_hist);
     hp.sel = at<int32_t>(workspace, pl.off_sel);
+    hp.order = hp.order_ctr = nullptr;
     hp.dbg_count = sel_count;
     hp.dbg_bins = nullptr;
     e = kvc::launch_hist(hp, stream);

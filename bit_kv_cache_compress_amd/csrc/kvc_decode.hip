@@ -729,6 +729,11 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const size_t bh = (size_t)b * g.Hq + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (p.order_ctr && (split | h | b | tid) == 0) {
+        // the threshold pass, which follows, takes the dispatch-order slots from these
+        p.order_ctr[0] = 0;
+        p.order_ctr[1] = 0;
+    }
     const int L = g.seq_lens[b];
     const int nch = L > 0 ? (L + g.CH - 1) >> g.logCH : 0;
     const int c0 = split * p.cps;
@@ -792,6 +797,20 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
     }
 }
 
+// Dispatch order of the Top-p attention pass: a head expected to keep more than one batch (64
+// entries) per attention chunk takes a slot from the front of `order`, any other head one from
+// the back.  The dense heads' waves, each of which works through several dependent batches,
+// then start first instead of after every head ahead of them in index order.  The slots of
+// equal-class heads follow the order of their atomics; each wave still writes the partial of
+// its own (head, chunk), so the results do not depend on it.
+__device__ __forceinline__ void order_head(const HistParams &p, size_t bh, bool dense)
+{
+    const int BH = p.g.B * p.g.Hq;
+    const int k = atomicAdd(&p.order_ctr[dense ? 0 : 1], 1);
+    const int slot = dense ? k : BH - 1 - k;
+    if (slot >= 0 && slot < BH) p.order[slot] = (int)bh;
+}
+
 // Top-p threshold of each (b, h) from the split counts: one 1024-thread block per (query
 // head, sequence), thread t owns bins 8t .. 8t+7.  A kernel of its own, so that the split
 // counts reach it through the kernel boundary rather than through device-scope fences in
@@ -821,6 +840,7 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     const int L = g.seq_lens[b];
     if (L <= 0) {
         if (tid == 0) {
+            if (p.order) order_head(p, bh, false);
             p.sel[bh * 4 + 0] = 0;
             p.sel[bh * 4 + 1] = -1;
             p.sel[bh * 4 + 2] = 0;
@@ -928,6 +948,7 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
         count = 0;
     }
     if (bstar >= -1) {
+        if (p.order) order_head(p, bh, (long)count * kTopPAttendChunk > 64L * L);
         p.sel[bh * 4 + 0] = emax;
         p.sel[bh * 4 + 1] = bstar;
         p.sel[bh * 4 + 2] = count;
@@ -1160,7 +1181,8 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention: one wave per (attention chunk of 1024 tokens, query head, sequence).
+// Top-p attention: one wave per (attention chunk of 1024 tokens, query head, sequence), the
+// heads taken in the dispatch order of the threshold pass (dense heads first).
 // Top-p keeps a small, head-specific set of tokens, so the wave first lists the kept tokens
 // of its chunk in ascending order (one pass over the 16-bit bin distances, 8 tokens per
 // 16-byte load, one wave scan of packed 16-bit counts), then works through the list in
@@ -1199,11 +1221,15 @@ __global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
     __shared__ uint32_t pbase[CHA / 16 + 1];
     uint16_t *list = sh.list;
     const DecodeGeom &g = p.g;
-    const int achunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int achunk = blockIdx.x;
+    // the head of this dispatch rank (dense heads first; the threshold pass wrote the order)
+    int bhr = p.order[blockIdx.z * g.Hq + blockIdx.y];
+    if ((unsigned)bhr >= (unsigned)(g.B * g.Hq)) bhr = blockIdx.z * g.Hq + blockIdx.y;
+    const int b = bhr / g.Hq, h = bhr - b * g.Hq;
     const int kvh = h / g.G;
     const int t0 = achunk * CHA;
     const int lane = threadIdx.x;
-    const size_t bh = (size_t)b * g.Hq + h;
+    const size_t bh = (size_t)bhr;
 
     // ---- round 1: distances (tokens 8 lane + 512 j .. + 7), thresholds, page ids and the
     // sequence length, all issued together: the distance rows hold whole attention chunks

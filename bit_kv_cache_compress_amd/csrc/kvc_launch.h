@@ -152,6 +152,8 @@ struct HistParams {
     uint16_t *hist;        // [B*Hq][nsplit][8192] per-split counts (a split has < 65536 tokens);
                            // splits past a sequence's end are neither written nor read
     int32_t *sel;          // [B*Hq][4] = (e_max, b*, count, 0)
+    int32_t *order;        // nullable [B*Hq]: the heads in the attention pass's dispatch order
+    int32_t *order_ctr;    // [2] slots taken from the front and from the back of `order`
     int32_t *dbg_count;    // nullable [B*Hq]
     int32_t *dbg_bins;     // nullable [B*Hq][2]
 };
@@ -176,6 +178,7 @@ struct AttendParams {
     const uint16_t *dl;
     const int32_t *lmax;
     const int32_t *sel;
+    const int32_t *order;  // [B*Hq] head (b * Hq + h) of each dispatch rank
     // partial results per (b, h, chunk)
     float *pm;             // [B*Hq][NCA] max score of the chunk's attended tokens
     float *pl;             // [B*Hq][NCA] sum of weights

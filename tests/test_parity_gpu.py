@@ -993,3 +993,32 @@ def test_chunk_boundary_lengths(top_p):
     out = decode_attend(g, q, zero, pt, top_p=top_p, max_seq_len=c.max_len)
     torch.cuda.synchronize()
     assert float(out.abs().max()) == 0.0
+
+
+def test_topp_dispatch_classes_poisoned_workspace():
+    """Top-p heads of both dispatch classes of the attention pass (more, and at most, 64 kept
+    tokens per 1024-token chunk), decoded on a workspace filled with 0xFF bytes (NaN as
+    binary32): every partial that the merge reads is written by this call, whatever order
+    the threshold pass gave the heads."""
+    from bit_kv_cache_compress_amd import decode_attend, decode_workspace_bytes
+
+    wl = W.CONFIGS[2].scaled(B=2, Hq=8, Hkv=2, P=256)
+    c = Case(wl, L=16384)
+    c.ocache = c.oracle_cache()
+    ref = c.oracle_decode(c.ocache, wl.top_p)
+    dense = {bh for bh, r in ref.items() if r["idx"].size * 1024 > 64 * int(c.lens[bh[0]])}
+    assert 0 < len(dense) < len(ref), f"need heads of both classes, got {len(dense)} dense of {len(ref)}"
+    dev = torch.device("cuda")
+    g = upload(c.ocache, c)
+    q = torch.from_numpy(c.q).to(dev)
+    lt = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    ws = torch.full((decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, c.max_len, wl.top_p),), 255, dtype=torch.uint8,
+                    device=dev)
+    for rep in range(2):  # the second call runs on the first call's leftovers
+        out = decode_attend(g, q, lt, pt, top_p=wl.top_p, max_seq_len=c.max_len, workspace=ws)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        for (b, h), r in ref.items():
+            assert rel_err(out[b, h], r["out"]) <= TOL, (rep, b, h, (b, h) in dense)
+    _say(f"[order] {len(dense)} dense heads of {len(ref)}: ok on a poisoned workspace")
