@@ -1207,7 +1207,7 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
 }
 
 template <bool EXACT, int KW>
-__global__ __launch_bounds__(64) void k_attend_topp(AttendParams p)
+__global__ __launch_bounds__(64, EXACT ? 1 : 5) void k_attend_topp(AttendParams p)
 {
     constexpr int CHA = kTopPAttendChunk;  // tokens of the attention chunk
     constexpr int NJ = CHA / 512;          // 16-byte distance loads per lane
