@@ -721,7 +721,10 @@ constexpr int kHistThreads = 1024;
 __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
 {
     constexpr int kT = kHistThreads;
-    constexpr int U = 32768 / (8 * kT);    // 16-byte loads per thread: 32768 tokens per round
+    // one 16-byte load per thread and round (8192 tokens), the next round's load in flight
+    // while this round is counted (more loads per round, counted after they all arrive,
+    // left the atomics and the stream to run one after the other)
+    constexpr int U = 1;
     __shared__ uint32_t hist[kBins];
     __shared__ int delta[kT];
     __shared__ int red[kT / 64];
@@ -742,8 +745,8 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
     const int tb = c0 << g.logCH;
     const int te = min(L, c1 << g.logCH);
     const uint16_t *row = p.dl + bh * g.Lpad;
-    // 8 tokens per 16-byte load, U loads in flight (tb is a multiple of CH >= 256).  The
-    // first round is issued before the top-bin reduction, whose reads then overlap it.
+    // 8 tokens per 16-byte load (tb is a multiple of CH >= 256).  The first round is issued
+    // before the top-bin reduction, whose reads then overlap it.
     constexpr int kStep = 8 * kT * U;
     uint4 raw[U];
     int t = tb + 8 * tid;
@@ -765,6 +768,11 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
     if (tid < c1 - c0) delta[tid] = emax - lmc;
     __syncthreads();
     for (; t < te; t += kStep) {
+        // the next round's loads go out before this round's counting
+        uint4 nxt[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (t + kStep + 8 * kT * u < te) nxt[u] = *reinterpret_cast<const uint4 *>(row + t + kStep + 8 * kT * u);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int tu = t + 8 * kT * u;
@@ -780,12 +788,8 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
                 }
             }
         }
-        if (t + kStep < te) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (t + kStep + 8 * kT * u < te)
-                    raw[u] = *reinterpret_cast<const uint4 *>(row + t + kStep + 8 * kT * u);
-        }
+        for (int u = 0; u < U; ++u) raw[u] = nxt[u];
     }
     __syncthreads();
     uint4 *dst = reinterpret_cast<uint4 *>(p.hist + (bh * p.nsplit + split) * kBins);
@@ -837,6 +841,8 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
 #pragma unroll
     for (int k = 0; k < 8; ++k) v0[k] = k < p.nsplit ? src[(size_t)k * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
     const int mfirst = tid < g.NC ? p.lmax[bh * g.NC + tid] : -kBinClamp;
+    // the weight table, while those loads are in flight (published by the barrier below)
+    if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
     const int L = g.seq_lens[b];
     if (L <= 0) {
         if (tid == 0) {
@@ -878,7 +884,6 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     for (int c = tid + kT; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
     m = wave_max_i(m);
     if (lane == 0) imax[wave] = m;
-    if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
     __syncthreads();
     // d >> 8 is the same for all 8 bins of a thread
     const int shift = tid >> 5;
