@@ -48,28 +48,44 @@ __device__ __forceinline__ uint32_t double_to_half_bits(double x)
 // ---------------------------------------------------------------------------------------
 // Wave / block reductions (wave64)
 // ---------------------------------------------------------------------------------------
+// Lane index within the wave (v_mbcnt).
+__device__ __forceinline__ int lane_id()
+{
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+// v of lane (this lane XOR m), m < 64: one ds_bpermute over the whole wave, without the
+// sub-width bound of __shfl_xor (whose wave-constant bound the compiler otherwise keeps
+// live, and spills, across long loops).
+__device__ __forceinline__ int xor_lane(int v, int m)
+{
+    return __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
+}
+__device__ __forceinline__ float xor_lane(float v, int m)
+{
+    return __int_as_float(xor_lane(__float_as_int(v), m));
+}
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, xor_lane(v, o));
     return v;
 }
 __device__ __forceinline__ int wave_max_i(int v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    for (int o = 32; o > 0; o >>= 1) v = max(v, xor_lane(v, o));
     return v;
 }
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    for (int o = 32; o > 0; o >>= 1) v += xor_lane(v, o);
     return v;
 }
 __device__ __forceinline__ int wave_sum_i(int v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    for (int o = 32; o > 0; o >>= 1) v += xor_lane(v, o);
     return v;
 }
 
