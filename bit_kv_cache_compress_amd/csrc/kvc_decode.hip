@@ -801,18 +801,31 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistParams p)
     }
 }
 
-// Dispatch order of the Top-p attention pass: a head expected to keep more than one batch (64
-// entries) per attention chunk takes a slot from the front of `order`, any other head one from
-// the back.  The dense heads' waves, each of which works through several dependent batches,
-// then start first instead of after every head ahead of them in index order.  The slots of
-// equal-class heads follow the order of their atomics; each wave still writes the partial of
-// its own (head, chunk), so the results do not depend on it.
-__device__ __forceinline__ void order_head(const HistParams &p, size_t bh, bool dense)
+// Attention chunks that one wave of a Top-p head covers (log2): 4 or 2 when the head's kept
+// count puts at most one batch (64 entries) in such a wave, else 1.  Most heads keep a few
+// tokens per chunk; one wave over several chunks then replaces waves whose fixed work (the
+// list, the scan, the final sums, the partial) would outweigh their few entries.
+__device__ __forceinline__ int attend_span_log2(int kept, int L)
+{
+    const long e = (long)kept * kTopPAttendChunk, cap = 64L * L;
+    return 4 * e <= cap ? 2 : (2 * e <= cap ? 1 : 0);
+}
+
+// Dispatch order of the Top-p attention pass: a head whose waves cover one chunk each (the
+// dense heads, whose waves work through several dependent batches) takes a slot from the
+// front of `order`, any other head one from the back, so that the dense heads' waves start
+// first instead of after every head ahead of them in index order.  An entry is the head
+// b * Hq + h with log2 of its span in bits 24 and up.  The slots of one class follow the
+// order of their atomics; every wave writes the partials of its own (head, chunks), so the
+// results do not depend on it.
+__device__ __forceinline__ void order_head(const HistParams &p, size_t bh, int kept, int L)
 {
     const int BH = p.g.B * p.g.Hq;
+    const int ls = attend_span_log2(kept, L);
+    const bool dense = ls == 0;
     const int k = atomicAdd(&p.order_ctr[dense ? 0 : 1], 1);
     const int slot = dense ? k : BH - 1 - k;
-    if (slot >= 0 && slot < BH) p.order[slot] = (int)bh;
+    if (slot >= 0 && slot < BH) p.order[slot] = (int)bh | (ls << 24);
 }
 
 // Top-p threshold of each (b, h) from the split counts: one 1024-thread block per (query
@@ -846,7 +859,7 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
     const int L = g.seq_lens[b];
     if (L <= 0) {
         if (tid == 0) {
-            if (p.order) order_head(p, bh, false);
+            if (p.order) order_head(p, bh, 0, 0);
             p.sel[bh * 4 + 0] = 0;
             p.sel[bh * 4 + 1] = -1;
             p.sel[bh * 4 + 2] = 0;
@@ -953,7 +966,7 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
         count = 0;
     }
     if (bstar >= -1) {
-        if (p.order) order_head(p, bh, (long)count * kTopPAttendChunk > 64L * L);
+        if (p.order) order_head(p, bh, count, L);
         p.sel[bh * 4 + 0] = emax;
         p.sel[bh * 4 + 1] = bstar;
         p.sel[bh * 4 + 2] = count;
@@ -1186,10 +1199,13 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention: one wave per (attention chunk of 1024 tokens, query head, sequence), the
-// heads taken in the dispatch order of the threshold pass (dense heads first).
+// Top-p attention: blocks of 4 waves over 4 attention chunks of 1024 tokens of one query
+// head, the heads taken in the dispatch order of the threshold pass (dense heads first, each
+// with its span).  A dense head's wave covers one chunk; a head that keeps few tokens has one
+// wave over 2 or 4 chunks, and the block's other waves end at once.  The waves of a block
+// share no data (each has its own LDS slices), so a block holds no barrier.
 // Top-p keeps a small, head-specific set of tokens, so the wave first lists the kept tokens
-// of its chunk in ascending order (one pass over the 16-bit bin distances, 8 tokens per
+// of its span in ascending order (one pass over the 16-bit bin distances, 8 tokens per
 // 16-byte load, one wave scan of packed 16-bit counts), then works through the list in
 // batches of 64 entries.  For a batch every load is issued up front: one key record per lane
 // and, per 4-lane group, the value records of up to 4 entries (16 bytes of codes, i.e. 32
@@ -1211,54 +1227,84 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
     return __int_as_float(r);
 }
 
-template <bool EXACT, int KW>
-__global__ __launch_bounds__(64, EXACT ? 1 : 5) void k_attend_topp(AttendParams p)
+// LDS ordering among the lanes of one wave (the attention waves of a block share no data):
+// a wave's LDS operations complete in order, so fences at wavefront scope, which keep the
+// compiler from moving LDS accesses across this point, are all that is needed.
+__device__ __forceinline__ void wave_lds_sync()
 {
-    constexpr int CHA = kTopPAttendChunk;  // tokens of the attention chunk
-    constexpr int NJ = CHA / 512;          // 16-byte distance loads per lane
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of one head
+
+template <bool EXACT, int KW>
+__global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 5) void k_attend_topp(AttendParams p)
+{
+    constexpr int CHA = kTopPAttendChunk;  // tokens of an attention chunk
+    constexpr int NW = kAttendWaves;
+    constexpr int NJ = CHA * NW / 512;     // 16-byte distance loads per lane, widest span
     constexpr int NB = EXACT ? 32 : 64;    // entries per batch
     constexpr int VU = NB / 16;            // value entries per 4-lane group and batch
-    __shared__ union {
-        uint16_t list[CHA];                // chunk offsets of the kept tokens
-        float4 red[4][4][9];               // final sums: [row][dim block][32 dims + zero term]
-    } sh;
-    __shared__ float wbuf[64];
-    __shared__ uint32_t pbase[CHA / 16 + 1];
-    uint16_t *list = sh.list;
+    // per-wave slices; a wave over s chunks uses the s slices of its group, contiguous.  A
+    // list slice is 2304 bytes so that the final sums (2304 bytes) fit in one.
+    constexpr int SL = 1152;               // list entries per slice
+    constexpr int PS = CHA / 16 + 1;       // page ids per slice (pages of >= 16 tokens)
+    __shared__ uint16_t lst[NW * SL];
+    __shared__ float wbs[NW][64];
+    __shared__ uint32_t pbs[NW * PS];
     const DecodeGeom &g = p.g;
-    const int achunk = blockIdx.x;
-    // the head of this dispatch rank (dense heads first; the threshold pass wrote the order)
-    int bhr = p.order[blockIdx.z * g.Hq + blockIdx.y];
-    if ((unsigned)bhr >= (unsigned)(g.B * g.Hq)) bhr = blockIdx.z * g.Hq + blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar
+    // the head of this dispatch rank and its span (dense heads first; the threshold pass
+    // wrote the order)
+    const int code = p.order[blockIdx.z * g.Hq + blockIdx.y];
+    int bhr = code & 0xFFFFFF;
+    const int ls = (code >> 24) & 3;
+    if (bhr >= g.B * g.Hq) bhr = blockIdx.z * g.Hq + blockIdx.y;
     const int b = bhr / g.Hq, h = bhr - b * g.Hq;
     const int kvh = h / g.G;
-    const int t0 = achunk * CHA;
-    const int lane = threadIdx.x;
     const size_t bh = (size_t)bhr;
+    // the block's waves cover chunks NW bx .. + NW - 1, in groups of span = 2^ls; one wave
+    // per group works, the one whose index within the group rotates with the block, so that
+    // the working waves spread over the SIMDs; the others have nothing to do
+    const int span = 1 << ls;
+    const int first = wave & ~(span - 1);  // first wave (and slice) of this wave's group
+    if (wave - first != ((int)blockIdx.x & (span - 1))) return;
+    const int c0 = (int)blockIdx.x * NW + first;  // first chunk of the span
+    if (c0 >= g.NCA) return;
+    const int t0 = c0 * CHA;
+    uint16_t *list = lst + first * SL;
+    float4(*red)[4][9] = reinterpret_cast<float4(*)[4][9]>(list);  // after the last batch
+    float *wbuf = wbs[wave];
+    uint32_t *pbase = pbs + first * PS;
 
-    // ---- round 1: distances (tokens 8 lane + 512 j .. + 7), thresholds, page ids and the
-    // sequence length, all issued together: the distance rows hold whole attention chunks
-    // and the page ids are read within the table, so none of these loads waits for the
-    // length (values past it are masked below)
+    // ---- round 1: the span's distances (tokens 8 lane + 512 j .. + 7), thresholds and page
+    // ids, and the sequence length, all issued together: the distance rows hold whole
+    // attention chunks and the page ids are read within the table, so none of these loads
+    // waits for the length (values past it are masked below)
     uint4 raw[NJ];
+    int thr[NJ];  // wave-uniform
     const uint16_t *row = p.dl + bh * g.Lpad + t0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) raw[j] = *reinterpret_cast<const uint4 *>(row + 8 * lane + 512 * j);
-    int thr[NJ];  // wave-uniform
-#pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int chunk = achunk * NJ + j;
-        thr[j] = chunk < g.NC ? chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk) : -1;
+        const int chunk = c0 * (CHA / 512) + j;
+        thr[j] = -1;
+        if (j < span * (CHA / 512) && chunk < g.NCA * (CHA / 512)) {
+            raw[j] = *reinterpret_cast<const uint4 *>(row + 8 * lane + 512 * j);
+            if (chunk < g.NC) thr[j] = chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk);
+        }
     }
     const int logP = p.c.logP;
     const int p0 = t0 >> logP;
-    const int npmax = min(((t0 + CHA - 1) >> logP) - p0 + 1, g.max_pages - p0);
+    const int npmax = min(((t0 + CHA * span - 1) >> logP) - p0 + 1, g.max_pages - p0);
     for (int i = lane; i < npmax; i += 64)
         pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
                    << logP;
     const int L = g.seq_lens[b];
     if (t0 >= L) return;
-    const int n = min(CHA, L - t0);
+    const int n = min(CHA * span, L - t0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
         if (j * kTopPChunk >= n) thr[j] = -1;  // a 512-token chunk past the end keeps nothing
@@ -1290,32 +1336,38 @@ __global__ __launch_bounds__(64, EXACT ? 1 : 5) void k_attend_topp(AttendParams 
         }
         keep[j] = m;
     }
-    uint64_t cnt4 = 0;
+    // wave-wide inclusive scans of the packed 16-bit counts, four 512-token groups per word
+    // (a field never exceeds 512); the second word only for a span of more than two chunks
+    uint64_t cnt4[2] = {0, 0}, before[2] = {0, 0}, total[2] = {0, 0};
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) cnt4 |= (uint64_t)__builtin_popcount(keep[j]) << (16 * j);
-    // wave-wide inclusive scan of the packed 16-bit counts (a field never exceeds 512)
-    uint64_t incl = cnt4;
+    for (int j = 0; j < NJ; ++j) cnt4[j >> 2] |= (uint64_t)__builtin_popcount(keep[j]) << (16 * (j & 3));
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+    for (int w = 0; w < 2; ++w) {
+        if (w == 0 || span > 2) {
+            uint64_t incl = cnt4[w];
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint64_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            total[w] = __shfl(incl, 63);
+            before[w] = incl - cnt4[w];
+        }
     }
-    const uint64_t total = __shfl(incl, 63);
-    const uint64_t before = incl - cnt4;
     int nlist = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        int off = nlist + (int)((before >> (16 * j)) & 0xFFFFu);
+        int off = nlist + (int)((before[j >> 2] >> (16 * (j & 3))) & 0xFFFFu);
         uint32_t m = keep[j];
         while (m) {
             const int e = __builtin_ctz(m);
             m &= m - 1u;
             list[off++] = (uint16_t)(8 * lane + 512 * j + e);
         }
-        nlist += (int)((total >> (16 * j)) & 0xFFFFu);
+        nlist += (int)((total[j >> 2] >> (16 * (j & 3))) & 0xFFFFu);
     }
     nlist = __builtin_amdgcn_readfirstlane(nlist);  // wave-uniform: scalar loop control
-    __syncthreads();
+    wave_lds_sync();
 
     const int q4 = lane & 3;   // dims 32*q4 .. 32*q4+31
     const int eg = lane >> 2;  // entries eg + 16 u of a batch
@@ -1419,7 +1471,7 @@ __global__ __launch_bounds__(64, EXACT ? 1 : 5) void k_attend_topp(AttendParams 
             const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
             lloc += w;
             wbuf[lane] = w;
-            __syncthreads();
+            wave_lds_sync();
         }
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
@@ -1442,13 +1494,14 @@ __global__ __launch_bounds__(64, EXACT ? 1 : 5) void k_attend_topp(AttendParams 
                 }
             }
         }
-        if constexpr (!EXACT) __syncthreads();  // wbuf is rewritten by the next batch
+        if constexpr (!EXACT) wave_lds_sync();  // wbuf is rewritten by the next batch
     }
 
     // ---- weight sum, then the value sums over the 16 entry groups: the 4 groups of a
-    // 16-lane row by DPP rotations, the 4 rows through LDS (the list's space: the last
-    // batch's barrier follows every read of the list)
+    // 16-lane row by DPP rotations, the 4 rows through LDS (the list's slice, which the
+    // fence below keeps from being overwritten before the last batch has read it)
     const float lsum = wave_sum(lloc);
+    wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
         acc[j] += dpp_ror(acc[j], 4);
@@ -1457,29 +1510,32 @@ __global__ __launch_bounds__(64, EXACT ? 1 : 5) void k_attend_topp(AttendParams 
     zacc += dpp_ror(zacc, 4);
     zacc += dpp_ror(zacc, 8);
     if ((lane & 15) < 4) {
-        float4 *dst = sh.red[lane >> 4][q4];
+        float4 *dst = red[lane >> 4][q4];
 #pragma unroll
         for (int k = 0; k < 8; ++k) dst[k] = make_float4(acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]);
         dst[8].x = zacc;
     }
-    __syncthreads();
-    const size_t pidx = bh * g.NCA + achunk;
+    wave_lds_sync();
+    const size_t pidx = bh * g.NCA + c0;
     {
         // lane l: dims 2l, 2l + 1 (dim block l / 16, float4 (l & 15) / 2, half l & 1)
         const int qb = lane >> 4, f4 = (lane & 15) >> 1, hf = lane & 1;
         float v0 = 0.0f, v1 = 0.0f, z = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float4 a = sh.red[r][qb][f4];
+            const float4 a = red[r][qb][f4];
             v0 += hf ? a.z : a.x;
             v1 += hf ? a.w : a.y;
-            z += sh.red[r][qb][8].x;
+            z += red[r][qb][8].x;
         }
         reinterpret_cast<float2 *>(p.po + pidx * kD)[lane] = make_float2(v0 + z, v1 + z);
     }
     if (lane == 0) {
         p.pm[pidx] = mrun;
         p.pl[pidx] = lsum;
+    } else if (lane < span && c0 + lane < g.NCA) {
+        p.pm[pidx + lane] = -INFINITY;  // the span's other chunks: empty partials
+        p.pl[pidx + lane] = 0.0f;
     }
 }
 
@@ -1569,7 +1625,9 @@ __device__ __forceinline__ void mass_finish(const MassParams &p, int b, int h, i
 // ---------------------------------------------------------------------------------------
 // Split-K merge, one 1024-thread block per (query head, sequence):
 //   out = sum_c a_c o_c / sum_c a_c l_c,  a_c = exp2((m_c - M) log2e/sqrt(D)),  M = max m_c.
-// Thread (d, slice) sums the chunks c = slice (mod 8) for dim d.  The value sums of the
+// Thread (d, slice) sums the chunks c = slice (mod 8) for dim d; a chunk of zero weight (no
+// attended token, or an empty partial of a Top-p span) adds nothing, and its value sums are
+// not read.  The value sums of the
 // first 256 chunks are loaded first, so that their reads overlap the max and weight
 // reductions.
 // ---------------------------------------------------------------------------------------
@@ -1632,7 +1690,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
         const int c = sl + NS * i;
-        if (c < nch) num = fmaf(alpha[c], v[i], num);
+        if (c < nch && alpha[c] != 0.0f) num = fmaf(alpha[c], v[i], num);
     }
     for (int c0 = sl + NS * PF; c0 < nch; c0 += NS * PF) {
         // the rest in rounds of PF loads in flight
@@ -1644,7 +1702,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             const int c = c0 + NS * i;
-            if (c < nch) num = fmaf(alpha[c], v[i], num);
+            if (c < nch && alpha[c] != 0.0f) num = fmaf(alpha[c], v[i], num);
         }
     }
     part[sl][d] = num;
@@ -1739,16 +1797,16 @@ hipError_t launch_select(const SelectParams &p, hipStream_t s)
 hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
 {
     if (select) {
-        // one wave per (attention chunk, query head, sequence)
-        const dim3 grid(p.g.NCA, p.g.Hq, p.g.B);
+        // blocks of kAttendWaves waves per (kAttendWaves attention chunks, dispatch rank)
+        const dim3 grid((p.g.NCA + kAttendWaves - 1) / kAttendWaves, p.g.Hq, p.g.B);
         if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
         const bool w4 = p.c.kw == 4;
         if (p.c.kf16) {
-            if (w4) hipLaunchKernelGGL((k_attend_topp<true, 4>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_topp<true, 2>), grid, dim3(64), 0, s, p);
+            if (w4) hipLaunchKernelGGL((k_attend_topp<true, 4>), grid, dim3(64 * kAttendWaves), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_topp<true, 2>), grid, dim3(64 * kAttendWaves), 0, s, p);
         } else {
-            if (w4) hipLaunchKernelGGL((k_attend_topp<false, 4>), grid, dim3(64), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_topp<false, 2>), grid, dim3(64), 0, s, p);
+            if (w4) hipLaunchKernelGGL((k_attend_topp<false, 4>), grid, dim3(64 * kAttendWaves), 0, s, p);
+            else hipLaunchKernelGGL((k_attend_topp<false, 2>), grid, dim3(64 * kAttendWaves), 0, s, p);
         }
     } else {
         // one wave per (chunk, KV-head group, sequence)
