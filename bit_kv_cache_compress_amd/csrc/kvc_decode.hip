@@ -1240,7 +1240,7 @@ __device__ __forceinline__ void wave_lds_sync()
 constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of one head
 
 template <bool EXACT, int KW>
-__global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 5) void k_attend_topp(AttendParams p)
+__global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_topp(AttendParams p)
 {
     constexpr int CHA = kTopPAttendChunk;  // tokens of an attention chunk
     constexpr int NW = kAttendWaves;
@@ -1284,17 +1284,19 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 5) void k_attend_top
     // ids, and the sequence length, all issued together: the distance rows hold whole
     // attention chunks and the page ids are read within the table, so none of these loads
     // waits for the length (values past it are masked below)
+    // Every load is issued without a branch (a load under a branch made the wave wait for it
+    // where the paths join): groups past the span or the padded row re-read the first group,
+    // and thresholds past the last score chunk read the last one; both are masked below.
     uint4 raw[NJ];
     int thr[NJ];  // wave-uniform
     const uint16_t *row = p.dl + bh * g.Lpad + t0;
+    const int nj = min(span * (CHA / 512), (g.NCA - c0) * (CHA / 512));  // groups in the row
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+        raw[j] = *reinterpret_cast<const uint4 *>(row + 8 * lane + 512 * (j < nj ? j : 0));
         const int chunk = c0 * (CHA / 512) + j;
-        thr[j] = -1;
-        if (j < span * (CHA / 512) && chunk < g.NCA * (CHA / 512)) {
-            raw[j] = *reinterpret_cast<const uint4 *>(row + 8 * lane + 512 * j);
-            if (chunk < g.NC) thr[j] = chunk_threshold(p.sel, p.lmax, bh, g.NC, chunk);
-        }
+        thr[j] = chunk_threshold(p.sel, p.lmax, bh, g.NC, min(chunk, g.NC - 1));
+        if (j >= nj || chunk >= g.NC) thr[j] = -1;
     }
     const int logP = p.c.logP;
     const int p0 = t0 >> logP;
@@ -1391,110 +1393,190 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 5) void k_attend_top
     for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
     float zacc = 0.0f, lloc = 0.0f, mrun = -INFINITY;
 
-    for (int bs = 0; bs < nlist; bs += NB) {
-        const int nb = min(NB, nlist - bs);
-        const int nu = (nb + 15) >> 4;  // value rounds of this batch (uniform)
-        // ---- round 2: the batch's key and value records (entries past nb re-read the last)
-        uint32_t sl[VU + 1];
-#pragma unroll
-        for (int u = 0; u <= VU; ++u) {
-            const uint32_t t = (uint32_t)(t0 + list[bs + min(u < VU ? eg + 16 * u : lane, nb - 1)]);
-            sl[u] = pbase[(t >> logP) - p0] + (t & tmask);
-        }
-        uint4 kb;
-        uint32_t nc;
-        if constexpr (!EXACT) load_key_t<KW>(p.c, sl[VU], kb, nc);
-        uint4 kx[EXACT ? VU : 1][4];  // exact scores: binary16 key dims 32 q4 .. 32 q4 + 31
-        if constexpr (EXACT) {
-#pragma unroll
-            for (int u = 0; u < VU; ++u) {
-                if (u < nu) {
-                    const uint4 *kr = reinterpret_cast<const uint4 *>(p.c.kf16 + (size_t)sl[u] * kD + 32 * q4);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) kx[u][k] = kr[k];
-                }
+    if constexpr (EXACT) {
+        for (int bs = 0; bs < nlist; bs += NB) {
+            const int nb = min(NB, nlist - bs);
+            const int nu = (nb + 15) >> 4;  // value rounds of this batch (uniform)
+            // ---- round 2: the batch's key and value records (entries past nb re-read the last)
+            uint32_t sl[VU + 1];
+    #pragma unroll
+            for (int u = 0; u <= VU; ++u) {
+                const uint32_t t = (uint32_t)(t0 + list[bs + min(u < VU ? eg + 16 * u : lane, nb - 1)]);
+                sl[u] = pbase[(t >> logP) - p0] + (t & tmask);
             }
-        }
-        uint4 cw[VU];
-        uint32_t szw[VU];
-#pragma unroll
-        for (int u = 0; u < VU; ++u) {
-            if (u < nu) {
-                const uint8_t *vr = val_rec(p.c, sl[u]);
-                __builtin_memcpy(&cw[u], vr + 16 * q4, 16);  // 8-byte aligned when Gv = 64
-                szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
-            }
-        }
-        float s;
-        float sx[EXACT ? VU : 1];  // exact scores of entries eg + 16 u (in all 4 lanes of the group)
-        if constexpr (EXACT) {
-            s = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < VU; ++u) {
-                sx[u] = -INFINITY;
-                if (u < nu) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t w4[4] = {kx[u][k].x, kx[u][k].y, kx[u][k].z, kx[u][k].w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            a = fmaf(qx[8 * k + e], half_bits_to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+            uint4 kb;
+            uint32_t nc;
+            if constexpr (!EXACT) load_key_t<KW>(p.c, sl[VU], kb, nc);
+            uint4 kx[EXACT ? VU : 1][4];  // exact scores: binary16 key dims 32 q4 .. 32 q4 + 31
+            if constexpr (EXACT) {
+    #pragma unroll
+                for (int u = 0; u < VU; ++u) {
+                    if (u < nu) {
+                        const uint4 *kr = reinterpret_cast<const uint4 *>(p.c.kf16 + (size_t)sl[u] * kD + 32 * q4);
+    #pragma unroll
+                        for (int k = 0; k < 4; ++k) kx[u][k] = kr[k];
                     }
-                    a = quad_sum(a);
-                    sx[u] = eg + 16 * u < nb ? a : -INFINITY;
                 }
-                s = fmaxf(s, sx[u]);
             }
-        } else {
-            int A;
-            score_key<1>(kb, nc, qs, &s, &A, 32 * KW);
-            if (lane >= nb) s = -INFINITY;
+            uint4 cw[VU];
+            uint32_t szw[VU];
+    #pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                if (u < nu) {
+                    const uint8_t *vr = val_rec(p.c, sl[u]);
+                    __builtin_memcpy(&cw[u], vr + 16 * q4, 16);  // 8-byte aligned when Gv = 64
+                    szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
+                }
+            }
+            float s;
+            float sx[EXACT ? VU : 1];  // exact scores of entries eg + 16 u (in all 4 lanes of the group)
+            if constexpr (EXACT) {
+                s = -INFINITY;
+    #pragma unroll
+                for (int u = 0; u < VU; ++u) {
+                    sx[u] = -INFINITY;
+                    if (u < nu) {
+                        float a = 0.0f;
+    #pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t w4[4] = {kx[u][k].x, kx[u][k].y, kx[u][k].z, kx[u][k].w};
+    #pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                a = fmaf(qx[8 * k + e], half_bits_to_float((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), a);
+                        }
+                        a = quad_sum(a);
+                        sx[u] = eg + 16 * u < nb ? a : -INFINITY;
+                    }
+                    s = fmaxf(s, sx[u]);
+                }
+            } else {
+                int A;
+                score_key<1>(kb, nc, qs, &s, &A, 32 * KW);
+                if (lane >= nb) s = -INFINITY;
+            }
+            const float mnew = fmaxf(mrun, wave_max(s));
+            const float scale = (mrun == -INFINITY) ? 0.0f : exp2f((mrun - mnew) * p.klog);
+            if (scale != 1.0f) {
+                zacc *= scale;
+                lloc *= scale;
+    #pragma unroll
+                for (int j = 0; j < 32; ++j) acc[j] *= scale;
+            }
+            mrun = mnew;
+            float wx[EXACT ? VU : 1];
+            if constexpr (EXACT) {
+    #pragma unroll
+                for (int u = 0; u < VU; ++u) {
+                    wx[u] = (sx[u] == -INFINITY) ? 0.0f : exp2f((sx[u] - mnew) * p.klog);
+                    if (q4 == 0) lloc += wx[u];  // each entry once
+                }
+            } else {
+                const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
+                lloc += w;
+                wbuf[lane] = w;
+                wave_lds_sync();
+            }
+    #pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                if (u < nu) {
+                    float we;  // 0 past nb
+                    if constexpr (EXACT) we = wx[u];
+                    else we = wbuf[eg + 16 * u];
+                    const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
+                    const float zf = half_bits_to_float(szw[u] >> 16);
+                    const float ws = we * sf;
+                    zacc = fmaf(we, zf, zacc);
+                    const uint32_t cwk[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+    #pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        // word k holds dims 32 q4 + 8k .. + 7
+                        float c[8];
+                        unpack_codes(cwk[k], c);
+    #pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[8 * k + j] = fmaf(ws, c[j], acc[8 * k + j]);
+                    }
+                }
+            }
+            if constexpr (!EXACT) wave_lds_sync();  // wbuf is rewritten by the next batch
         }
-        const float mnew = fmaxf(mrun, wave_max(s));
-        const float scale = (mrun == -INFINITY) ? 0.0f : exp2f((mrun - mnew) * p.klog);
-        if (scale != 1.0f) {
-            zacc *= scale;
-            lloc *= scale;
+    } else {
+        // Proxy scores: the batches are software-pipelined in two register sets, the next
+        // batch's key and value gathers in flight while this batch is scored and summed (a
+        // dense head's wave works through many batches, each otherwise paying a full gather
+        // latency).  Value rounds past the batch's entries re-read its last entry and are
+        // not summed.
+        struct Gather {
+            uint4 kb;
+            uint32_t nc;
+            uint4 cw[VU];
+            uint32_t szw[VU];
+        };
+        auto gather = [&](int bs, Gather &G) {
+            const int nb = min(NB, nlist - bs);
+            uint32_t sl[VU + 1];
 #pragma unroll
-            for (int j = 0; j < 32; ++j) acc[j] *= scale;
-        }
-        mrun = mnew;
-        float wx[EXACT ? VU : 1];
-        if constexpr (EXACT) {
+            for (int u = 0; u <= VU; ++u) {
+                const uint32_t t = (uint32_t)(t0 + list[bs + min(u < VU ? eg + 16 * u : lane, nb - 1)]);
+                sl[u] = pbase[(t >> logP) - p0] + (t & tmask);
+            }
+            load_key_t<KW>(p.c, sl[VU], G.kb, G.nc);
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
-                wx[u] = (sx[u] == -INFINITY) ? 0.0f : exp2f((sx[u] - mnew) * p.klog);
-                if (q4 == 0) lloc += wx[u];  // each entry once
+                const uint8_t *vr = val_rec(p.c, sl[u]);
+                __builtin_memcpy(&G.cw[u], vr + 16 * q4, 16);  // 8-byte aligned when Gv = 64
+                G.szw[u] = *reinterpret_cast<const uint32_t *>(vr + kD / 2 + 4 * grp);
             }
-        } else {
+        };
+        auto attend = [&](int bs, const Gather &G) {
+            const int nb = min(NB, nlist - bs);
+            const int nu = (nb + 15) >> 4;  // value rounds of this batch (uniform)
+            float s;
+            int A;
+            score_key<1>(G.kb, G.nc, qs, &s, &A, 32 * KW);
+            if (lane >= nb) s = -INFINITY;
+            const float mnew = fmaxf(mrun, wave_max(s));
+            const float scale = (mrun == -INFINITY) ? 0.0f : exp2f((mrun - mnew) * p.klog);
+            if (scale != 1.0f) {
+                zacc *= scale;
+                lloc *= scale;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) acc[j] *= scale;
+            }
+            mrun = mnew;
             const float w = (s == -INFINITY) ? 0.0f : exp2f((s - mnew) * p.klog);
             lloc += w;
             wbuf[lane] = w;
             wave_lds_sync();
-        }
 #pragma unroll
-        for (int u = 0; u < VU; ++u) {
-            if (u < nu) {
-                float we;  // 0 past nb
-                if constexpr (EXACT) we = wx[u];
-                else we = wbuf[eg + 16 * u];
-                const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
-                const float zf = half_bits_to_float(szw[u] >> 16);
-                const float ws = we * sf;
-                zacc = fmaf(we, zf, zacc);
-                const uint32_t cwk[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+            for (int u = 0; u < VU; ++u) {
+                if (u < nu) {
+                    const float we = wbuf[eg + 16 * u];  // 0 past nb
+                    const float sf = half_bits_to_float(G.szw[u] & 0xFFFFu);
+                    const float zf = half_bits_to_float(G.szw[u] >> 16);
+                    const float ws = we * sf;
+                    zacc = fmaf(we, zf, zacc);
+                    const uint32_t cwk[4] = {G.cw[u].x, G.cw[u].y, G.cw[u].z, G.cw[u].w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    // word k holds dims 32 q4 + 8k .. + 7
-                    float c[8];
-                    unpack_codes(cwk[k], c);
+                    for (int k = 0; k < 4; ++k) {
+                        // word k holds dims 32 q4 + 8k .. + 7
+                        float c[8];
+                        unpack_codes(cwk[k], c);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[8 * k + j] = fmaf(ws, c[j], acc[8 * k + j]);
+                        for (int j = 0; j < 8; ++j) acc[8 * k + j] = fmaf(ws, c[j], acc[8 * k + j]);
+                    }
                 }
             }
+            wave_lds_sync();  // wbuf is rewritten by the next batch
+        };
+        Gather ga, gb;
+        if (nlist > 0) gather(0, ga);
+        for (int bs = 0; bs < nlist; bs += 2 * NB) {
+            if (bs + NB < nlist) gather(bs + NB, gb);
+            attend(bs, ga);
+            if (bs + NB >= nlist) break;
+            if (bs + 2 * NB < nlist) gather(bs + 2 * NB, ga);
+            attend(bs + NB, gb);
         }
-        if constexpr (!EXACT) wave_lds_sync();  // wbuf is rewritten by the next batch
     }
 
     // ---- weight sum, then the value sums over the 16 entry groups: the 4 groups of a
