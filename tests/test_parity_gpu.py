@@ -1022,3 +1022,31 @@ def test_topp_dispatch_classes_poisoned_workspace():
         for (b, h), r in ref.items():
             assert rel_err(out[b, h], r["out"]) <= TOL, (rep, b, h, (b, h) in dense)
     _say(f"[order] {len(dense)} dense heads of {len(ref)}: ok on a poisoned workspace")
+
+
+@pytest.mark.parametrize("scores", [True, False])
+def test_topp_many_heads_ragged(scores):
+    """128 query heads (4 sequences of 32) with ragged lengths and an empty sequence: top bins,
+    thresholds, counts and index sets equal the oracle's bit for bit, outputs within the
+    tolerance, twice in a row on one workspace; scores=True runs the debug score kernel, the
+    other the matrix-core one."""
+    wl = W.CONFIGS[2].scaled(B=4, Hq=32, Hkv=8, P=256)
+    lens = [0, 1, 3001, 8192]
+    c = Case(wl, L=max(lens), seq_lens=lens)
+    c.ocache = c.oracle_cache()
+    g = upload(c.ocache, c)
+    ref = c.oracle_decode(c.ocache, wl.top_p)
+    for rep in range(2):
+        out, dbg = _decode_with_debug(c, g, wl.top_p, scores=scores)
+        for (b, h), r in ref.items():
+            n = int(c.lens[b])
+            if n == 0:
+                assert np.abs(out[b, h]).max() == 0.0 and int(dbg.sel_count[b, h]) == 0
+                continue
+            cnt = int(dbg.sel_count[b, h])
+            assert cnt == len(r["idx"]), (rep, b, h, cnt, len(r["idx"]))
+            np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            bins = dbg.sel_bins[b, h].cpu().numpy()
+            assert (int(bins[0]), int(bins[1])) == (r["emax"], r["bstar"]), (b, h)
+            assert rel_err(out[b, h], r["out"]) <= TOL, (rep, b, h)
+    _say(f"[many heads] scores={scores} ok")
