@@ -1050,3 +1050,23 @@ def test_topp_many_heads_ragged(scores):
             assert (int(bins[0]), int(bins[1])) == (r["emax"], r["bstar"]), (b, h)
             assert rel_err(out[b, h], r["out"]) <= TOL, (rep, b, h)
     _say(f"[many heads] scores={scores} ok")
+
+
+def test_topp_spans_small_pages():
+    """16-token pages under spans of 4 attention chunks (a light head's wave over 4096 tokens
+    reads 257 page ids, the most its LDS holds) and a ragged length that ends inside a span:
+    sets and outputs against the oracle."""
+    wl = W.CONFIGS[2].scaled(B=2, Hq=8, Hkv=2, P=16)
+    lens = [9000, 4097]
+    c = Case(wl, L=max(lens), seq_lens=lens)
+    c.ocache = c.oracle_cache()
+    g = upload(c.ocache, c)
+    ref = c.oracle_decode(c.ocache, wl.top_p)
+    light = sum(1 for (b, h), r in ref.items() if r["idx"].size * 4096 <= 64 * int(c.lens[b]))
+    assert light > 0, "no head takes spans of 4 chunks"
+    out, dbg = _decode_with_debug(c, g, wl.top_p, scores=False)
+    for (b, h), r in ref.items():
+        cnt = int(dbg.sel_count[b, h])
+        np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+        assert rel_err(out[b, h], r["out"]) <= TOL, (b, h)
+    _say(f"[small pages] {light} of {len(ref)} heads with spans of 4 chunks: ok")
