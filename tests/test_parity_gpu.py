@@ -1070,3 +1070,25 @@ def test_topp_spans_small_pages():
         np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
         assert rel_err(out[b, h], r["out"]) <= TOL, (b, h)
     _say(f"[small pages] {light} of {len(ref)} heads with spans of 4 chunks: ok")
+
+
+def test_topp_long_sequence():
+    """One 262144-token sequence at Top-p 0.95 (the ultra-long workload's rotation and page
+    size; 8 query / 2 KV heads): 64 histogram splits per head, dense heads keeping 60-70% of
+    their tokens (several batches per attention chunk) and 256 partial slots per head in the
+    merge.  Index sets equal the oracle's bit for bit, outputs within the tolerance."""
+    wl = W.CONFIGS[4].scaled(B=1, Hq=8, Hkv=2)
+    c = Case(wl, L=262144)
+    c.ocache = c.oracle_cache()
+    g = upload(c.ocache, c)
+    ref = c.oracle_decode(c.ocache, wl.top_p)
+    out, dbg = _decode_with_debug(c, g, wl.top_p, scores=False)
+    worst = 0.0
+    for (b, h), r in ref.items():
+        cnt = int(dbg.sel_count[b, h])
+        assert cnt == len(r["idx"]), (b, h, cnt, len(r["idx"]))
+        np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+        e = float(rel_err(out[b, h], r["out"]))
+        worst = max(worst, e)
+        assert e <= TOL, (b, h, e)
+    _say(f"[long] 262144 tokens, top_p={wl.top_p}: ok, worst rel err {worst:.2e}")
