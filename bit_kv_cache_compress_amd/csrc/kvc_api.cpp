@@ -145,6 +145,8 @@ int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, f
     const long limit = (long)chunk_cap(top_p < 1.0f) * kvc::kMaxChunks;  // merge weights fit in LDS
     if (max_seq_len > limit)
         return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld", max_seq_len, limit);
+    if (top_p < 1.0f && (long)B * Hq >= (1L << 24))  // the attention pass's dispatch-order entries
+        return fail(KV_ERR_UNSUPPORTED, "B * Hq = %ld: Top-p supports fewer than 2^24 query heads", (long)B * Hq);
     return KV_OK;
 }
 

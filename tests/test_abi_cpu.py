@@ -75,6 +75,7 @@ def test_bad_cache_descriptor(kw, code):
     (dict(top_p=0.0), L.KV_ERR_ARG),
     (dict(top_p=-0.5), L.KV_ERR_ARG),
     (dict(top_p=float("nan")), L.KV_ERR_ARG),
+    (dict(B=1 << 19, Hq=32, top_p=0.9), L.KV_ERR_UNSUPPORTED),  # 2^24 query heads under Top-p
     (dict(q=None), L.KV_ERR_ARG),
     (dict(out=None), L.KV_ERR_ARG),
 ])
