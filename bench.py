@@ -125,7 +125,7 @@ def run_lazy(args):
     Lmax = L + total
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = torch.empty(kvc.decode_workspace_bytes(B, Hq, Hkv, Lmax, wl.top_p), dtype=torch.uint8, device=dev)
-    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
+    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)  # summed in its own dtype: reads only
     side = torch.cuda.Stream()
     st = dict(lc=Lc0, nt=T0, pending=None, compressions=0)
     starts = [torch.tensor([0], dtype=torch.int32, device=dev) for _ in range(B)]
@@ -271,8 +271,9 @@ def main():
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = torch.empty(kvc.decode_workspace_bytes(B, Hq, Hkv, Lmax, wl.top_p), dtype=torch.uint8, device=dev)
     # read-only sweep of 512 MiB between steps: evicts L2 and the 256 MB Infinity Cache
-    # without leaving dirty lines behind (whose write-back would be charged to the next step)
-    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
+    # without leaving dirty lines behind (whose write-back would be charged to the next step).
+    # A float32 buffer is summed in its own dtype, with no widening copy.
+    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
 
     def flush():
         flush_buf.sum()

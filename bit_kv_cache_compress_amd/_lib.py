@@ -16,7 +16,7 @@ KV_ROT_DENSE, KV_ROT_HADAMARD = 0, 1
 KV_F16, KV_F32 = 0, 1
 
 EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_ex", "kv_decode_attend_tail",
-           "kv_decode_workspace_bytes", "kv_hp_update",
+           "kv_decode_workspace_bytes", "kv_workspace_bytes", "kv_hp_update",
            "kv_tail_append", "kv_tail_retire", "kv_topp_select", "kv_topp_workspace_bytes", "kv_last_error",
            "kv_version")
 
@@ -49,6 +49,8 @@ class KVDebug(ctypes.Structure):
         ("sel_idx", ctypes.c_void_p),
         ("sel_bins", ctypes.c_void_p),
         ("stage_events", ctypes.c_void_p),
+        ("bin_dist", ctypes.c_void_p),
+        ("chunk_top", ctypes.c_void_p),
     ]
 
 
@@ -138,6 +140,8 @@ def lib():
     L.kv_tail_retire.restype = ctypes.c_int
     L.kv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, f32]
     L.kv_decode_workspace_bytes.restype = sz
+    L.kv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, f32]
+    L.kv_workspace_bytes.restype = sz
     L.kv_topp_select.argtypes = [P, i32, P, i32, i32, i32, f32, P, P, P, sz, P]
     L.kv_topp_select.restype = ctypes.c_int
     L.kv_topp_workspace_bytes.argtypes = [i32, i32, i32]

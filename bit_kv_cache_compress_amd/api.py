@@ -172,22 +172,30 @@ class DecodeDebug:
     sel_count: Optional[torch.Tensor] = None
     sel_idx: Optional[torch.Tensor] = None
     sel_bins: Optional[torch.Tensor] = None
+    bin_dist: Optional[torch.Tensor] = None
+    chunk_top: Optional[torch.Tensor] = None
 
     @staticmethod
-    def allocate(B, Hq, ld, topp: bool, device, scores: bool = True) -> "DecodeDebug":
+    def allocate(B, Hq, ld, topp: bool, device, scores: bool = True, dist: bool = False) -> "DecodeDebug":
         """Debug outputs of one decode.  scores=False leaves out the per-token scores, so the
-        decode runs the same score kernels as without debug output."""
+        decode runs the same score kernels as without debug output.  dist=True (Top-p) also
+        returns what the score pass wrote: bin_dist uint16 [B, Hq, ld] (returned as int32
+        bits of an int16 tensor) and chunk_top int32 [B, Hq, ceil(ld / 512)]."""
         z = lambda *s, dt=torch.int32: torch.zeros(s, dtype=dt, device=device)
+        dist = dist and topp
         return DecodeDebug(q_codes=z(B, Hq, HEAD_DIM, dt=torch.uint8), q_params=z(B, Hq, 4, dt=torch.float32),
                            q_sumu=z(B, Hq), iscores=z(B, Hq, ld) if scores else None,
                            scores=z(B, Hq, ld, dt=torch.float32) if scores else None,
                            sel_count=z(B, Hq) if topp else None, sel_idx=z(B, Hq, ld) - 1 if topp else None,
-                           sel_bins=z(B, Hq, 2) if topp else None)
+                           sel_bins=z(B, Hq, 2) if topp else None,
+                           bin_dist=z(B, Hq, ld, dt=torch.int16) if dist else None,
+                           chunk_top=z(B, Hq, (ld + 511) // 512) if dist else None)
 
     def struct(self) -> L.KVDebug:
-        return L.KVDebug(*[None if t is None else t.data_ptr() for t in
-                           (self.q_codes, self.q_params, self.q_sumu, self.iscores, self.scores, self.sel_count,
-                            self.sel_idx, self.sel_bins)], None)
+        ptrs = [None if t is None else t.data_ptr() for t in
+                (self.q_codes, self.q_params, self.q_sumu, self.iscores, self.scores, self.sel_count, self.sel_idx,
+                 self.sel_bins)]
+        return L.KVDebug(*ptrs, None, *[None if t is None else t.data_ptr() for t in (self.bin_dist, self.chunk_top)])
 
 
 def _loaded_hip_runtime() -> str:

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "kv_compress.h"
@@ -242,6 +243,53 @@ T *at(void *ws, size_t off)
     return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
 }
 
+// KV_DEBUG=1 (read at every call): device-side argument checks before a call enqueues its
+// kernels.  The checker reads seq_lens / start_pos and the page table entries the call would
+// use, the stream is synchronized, and a failure becomes KV_ERR_ARG.
+bool debug_checks()
+{
+    const char *v = getenv("KV_DEBUG");
+    return v && v[0] == '1' && v[1] == 0;
+}
+
+int run_check(const kvc::CheckParams &p, hipStream_t stream)
+{
+    int32_t flag[4] = {0, 0, 0, 0};
+    hipError_t e = kvc::launch_check(p, flag, stream);
+    if (e != hipSuccess) return hip_fail(e, "argument checker");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "argument checker synchronize");
+    switch (flag[0]) {
+    case kvc::kCheckOk: return KV_OK;
+    case kvc::kCheckLen:
+        return fail(KV_ERR_ARG, "KV_DEBUG: seq_lens[%d] = %d is outside 0..max_seq_len (%d)", flag[1], flag[3],
+                    p.max_seq_len);
+    case kvc::kCheckStart:
+        return fail(KV_ERR_ARG, "KV_DEBUG: start_pos[%d] = %d: the %d new tokens leave the %d mapped pages", flag[1],
+                    flag[3], p.n_new, p.max_pages);
+    default:
+        return fail(KV_ERR_ARG, "KV_DEBUG: page_table[%d][%d] = %d is outside 0..num_pages-1 (%d pages)", flag[1],
+                    flag[2], flag[3], p.num_pages);
+    }
+}
+
+// Checks of a decode (seq_lens) or an append (start_pos, n_new) against the page table.
+int check_on_device(const kv_cache *c, const int32_t *seq_lens, int max_seq_len, const int32_t *start_pos,
+                    int n_new, const int32_t *page_table, int B, int max_pages, hipStream_t stream)
+{
+    kvc::CheckParams p;
+    p.seq_lens = seq_lens;
+    p.max_seq_len = max_seq_len;
+    p.start_pos = start_pos;
+    p.n_new = n_new;
+    p.page_table = page_table;
+    p.B = B;
+    p.max_pages = max_pages;
+    p.logP = ilog2(c->page_size);
+    p.num_pages = c->num_pages;
+    return run_check(p, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +342,10 @@ int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const vo
     kvc::AppendParams p;
     rc = make_append(c, dtype, k, v, B, n_new, start_pos, page_table, max_pages, p);
     if (rc || p.n_new == 0) return rc;
+    if (debug_checks()) {
+        rc = check_on_device(c, nullptr, 0, start_pos, n_new, page_table, B, max_pages, stream);
+        if (rc) return rc;
+    }
     hipError_t e = kvc::launch_append(p, stream);
     if (e != hipSuccess) return hip_fail(e, "append launch");
     return KV_OK;
@@ -306,6 +358,11 @@ size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max
     Plan pl;
     make_plan(pl, B, Hq, Hkv, max_seq_len, top_p);
     return pl.total;
+}
+
+size_t kv_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t head_dim, float top_p)
+{
+    return kv_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, head_dim, top_p);
 }
 
 namespace {
@@ -333,6 +390,14 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     pl.g.seq_lens = seq_lens;
     pl.g.page_table = page_table;
     pl.g.max_pages = max_pages;
+    if (debug_checks()) {
+        if (app && app->n_new > 0 && app->start_pos) {
+            rc = check_on_device(c, nullptr, 0, app->start_pos, app->n_new, page_table, B, max_pages, stream);
+            if (rc) return rc;
+        }
+        rc = check_on_device(c, seq_lens, max_seq_len, nullptr, 0, page_table, B, max_pages, stream);
+        if (rc) return rc;
+    }
     const kvc::CacheView cv = view_of(c);
     const float isd = (float)(1.0 / sqrt((double)c->head_dim));
     const float kbin = (float)(256.0 * 1.4426950408889634074 / sqrt((double)c->head_dim));
@@ -415,6 +480,15 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
         e = kvc::launch_score(sp, stream);
         if (e != hipSuccess) return hip_fail(e, "score launch");
         stage_mark(dbg, KV_STAGE_SCORE, false, stream);
+    }
+    if (pl.topp && dbg && dbg->bin_dist) {  // what the score pass wrote, row by row
+        e = hipMemcpy2DAsync(dbg->bin_dist, (size_t)pl.g.ld * 2, sp.dl, (size_t)pl.g.Lpad * 2, (size_t)pl.g.ld * 2,
+                             (size_t)BH, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "bin distance copy");
+    }
+    if (pl.topp && dbg && dbg->chunk_top) {
+        e = hipMemcpyAsync(dbg->chunk_top, sp.lmax, (size_t)BH * pl.g.NC * 4, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "chunk top copy");
     }
 
     if (pl.topp) {

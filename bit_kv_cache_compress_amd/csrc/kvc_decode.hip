@@ -19,6 +19,9 @@
 
 namespace kvc {
 
+// Result words of the argument checker (k_check), one copy per device.
+__device__ int32_t g_check_flag[4];
+
 namespace {
 
 // First query head of block (hb = kv head * nsub + sub) and its KV head.
@@ -1798,6 +1801,54 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     if (MASS) mass_finish(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, M, D, p.klog, mf);
 }
 
+// ---------------------------------------------------------------------------------------
+// Argument checker (KV_DEBUG=1): block b checks sequence b's token range and the page table
+// entries that cover it; every read stays inside seq_lens / start_pos [B] and the B x
+// max_pages table, so a bad entry is reported instead of dereferenced.  The first failing
+// thread (atomicCAS on the code word) records (code, b, page index or -1, value).
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_check_clear(int32_t *flag)
+{
+    if (threadIdx.x < 4) flag[threadIdx.x] = 0;
+}
+
+__device__ __forceinline__ void check_fail(int32_t *flag, int code, int b, int j, int v)
+{
+    if (atomicCAS(&flag[0], 0, code) == 0) {
+        flag[1] = b;
+        flag[2] = j;
+        flag[3] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_check(CheckParams p, int32_t *flag)
+{
+    const int b = blockIdx.x;
+    long lo = 0, hi = 0;  // token range [lo, hi)
+    if (p.seq_lens) {
+        const int L = p.seq_lens[b];
+        if (L < 0 || L > p.max_seq_len) {
+            if (threadIdx.x == 0) check_fail(flag, kCheckLen, b, -1, L);
+            return;
+        }
+        hi = L;
+    } else {
+        const int sp = p.start_pos[b];
+        if (sp < 0 || (long)sp + p.n_new > ((long)p.max_pages << p.logP)) {
+            if (threadIdx.x == 0) check_fail(flag, kCheckStart, b, -1, sp);
+            return;
+        }
+        lo = sp;
+        hi = (long)sp + p.n_new;
+    }
+    if (hi <= lo) return;
+    const long j0 = lo >> p.logP, j1 = (hi - 1) >> p.logP;  // j1 < max_pages by the checks above
+    for (long j = j0 + threadIdx.x; j <= j1; j += blockDim.x) {
+        const int id = p.page_table[(size_t)b * p.max_pages + j];
+        if (id < 0 || id >= p.num_pages) check_fail(flag, kCheckPage, b, (int)j, id);
+    }
+}
+
 // The full-softmax kernel for the cache's key record width.
 template <int GB, int GV>
 void launch_full(const AttendParams &p, dim3 grid, hipStream_t s)
@@ -1911,6 +1962,18 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         }
     }
     return hipGetLastError();
+}
+
+hipError_t launch_check(const CheckParams &p, int32_t *flag_host, hipStream_t s)
+{
+    int32_t *flag = nullptr;  // this device's copy of the flag
+    hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&flag), HIP_SYMBOL(g_check_flag));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_check_clear, dim3(1), dim3(64), 0, s, flag);
+    hipLaunchKernelGGL(k_check, dim3(p.B), dim3(256), 0, s, p, flag);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipMemcpyAsync(flag_host, flag, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
 }
 
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)

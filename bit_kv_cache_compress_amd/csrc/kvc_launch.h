@@ -241,4 +241,21 @@ struct HpUpdateParams {
 };
 hipError_t launch_hp_update(const HpUpdateParams &p, hipStream_t s);
 
+// Device-side argument checker (KV_DEBUG=1): one block per sequence checks the token range a
+// call would touch -- [0, seq_lens[b]) for a decode, [start_pos[b], start_pos[b] + n_new) for
+// an append -- against its bound and the page table entries covering it against num_pages.
+// The first failure is recorded in a 4-word flag (code, sequence, page index, value).
+struct CheckParams {
+    const int32_t *seq_lens;   // nullable: decode lengths [B]
+    int max_seq_len;
+    const int32_t *start_pos;  // nullable: append positions [B]
+    int n_new;
+    const int32_t *page_table; // [B][max_pages]
+    int B, max_pages, logP, num_pages;
+};
+enum { kCheckOk = 0, kCheckLen = 1, kCheckStart = 2, kCheckPage = 3 };
+// Clears the flag, runs the checker and copies the flag to flag_host (4 words) on stream s; the
+// caller synchronizes s before reading it.
+hipError_t launch_check(const CheckParams &p, int32_t *flag_host, hipStream_t s);
+
 }  // namespace kvc

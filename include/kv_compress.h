@@ -25,9 +25,14 @@
  *   - Each call validates its arguments on the host first.  On a bad argument it returns a
  *     negative code, records a message for kv_last_error(), and enqueues nothing.  A failed
  *     kernel launch returns KV_ERR_HIP with the HIP error string.
- *   - Device-side preconditions are not checked: sequence lengths within the pages the page
- *     table maps, page ids < num_pages, finite inputs, and (for append) positions that stay
- *     inside the mapped pages.
+ *   - Device-side preconditions are not checked by default: sequence lengths within the pages
+ *     the page table maps, page ids < num_pages, finite inputs, and (for append) positions
+ *     that stay inside the mapped pages.  With the environment variable KV_DEBUG set to 1 (read
+ *     at every call), kv_compress_append and the decode calls first run a checker kernel over
+ *     seq_lens, start_pos and the page table entries the call would use (it reads them within
+ *     their declared extents only), synchronize `stream`, and return KV_ERR_ARG with the first
+ *     offending (sequence, page index, value) in kv_last_error() before enqueuing any other
+ *     kernel; such calls are then synchronous and must not be captured into a graph.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null stream).
  *   - head_dim D must be 128; value_group must be 32 or 64; page_size must be a power of
  *     two >= 16; the GQA group Hq/Hkv must be 1, 2, 4 or 8.
@@ -129,7 +134,15 @@ typedef struct kv_cache {
  *   stage_events [host] array of 2 * KV_NUM_STAGES hipEvent_t (nullable): the call records
  *            stage_events[2s] on `stream` before the kernels of stage s and
  *            stage_events[2s+1] after them, for each stage s it runs (others are left
- *            alone), so a caller can time every stage with hipEventElapsedTime. */
+ *            alone), so a caller can time every stage with hipEventElapsedTime.
+ *   bin_dist uint16 [B][Hq][ld]     Top-p only: what the score pass wrote for token t, the
+ *            distance chunk_top - e_t of its score bin e_t = floor(s_t * kbin) (see
+ *            kv_topp_select) to the top bin of its 512-token chunk, saturated at 8192, and 8192
+ *            for positions past seq_lens[b] inside the sequence's last chunk (later chunks are
+ *            left undefined).  Copied from the workspace after the score pass, so a decode
+ *            without scores/iscores is checked on the very kernels it runs otherwise.
+ *   chunk_top int32 [B][Hq][ceil(ld / 512)]  Top-p only: the top bin of each 512-token chunk
+ *            (undefined for chunks past seq_lens[b]). */
 enum {
     KV_STAGE_QUERY = 0,   /* query rotation, int4 codes, bit-planes */
     KV_STAGE_SCORE = 1,   /* Top-p: proxy scores of all tokens -> bin distances */
@@ -149,6 +162,8 @@ typedef struct kv_debug {
     int32_t *sel_idx;
     int32_t *sel_bins;
     hipEvent_t *stage_events;
+    uint16_t *bin_dist;
+    int32_t *chunk_top;
 } kv_debug;
 
 /* kv_compress_append -- encode n_new new tokens per sequence into the cache.
@@ -315,9 +330,14 @@ int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const flo
 int kv_hp_update(const kv_cache *c, const kv_hp *hp, const kv_tail *t, int32_t B, int32_t n,
                  const int32_t *seq_lens, const int32_t *page_table, int32_t max_pages, hipStream_t stream);
 
-/* Workspace size for kv_decode_attend with these arguments (0 on invalid arguments). */
+/* Workspace size for kv_decode_attend, kv_decode_attend_tail and kv_decode_attend_ex with these
+ * arguments (0 on invalid arguments).  kv_workspace_bytes is the same function under the name
+ * the decode's statement of the problem uses; kv_topp_select has a sizer of its own
+ * (kv_topp_workspace_bytes), since it takes scores rather than a cache. */
 size_t kv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
                                  int32_t head_dim, float top_p);
+size_t kv_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len, int32_t head_dim,
+                          float top_p);
 
 /* kv_topp_select -- adaptive Top-p over caller-supplied proxy scores.
  * Defines: RaBitQCache abstract (adaptive Top-p retrieval whose token budget follows the

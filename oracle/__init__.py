@@ -58,6 +58,7 @@ def _load():
     lib.orc_kbin.restype = f32
     lib.orc_bin.argtypes = [f32, f32]
     lib.orc_bin.restype = i32
+    lib.orc_bins.argtypes = [i32, P, i64, P]
     lib.orc_weight_table.argtypes = [P]
     lib.orc_topp.argtypes = [i32, P, i64, f32, P, P, P, P, P]
     lib.orc_topp.restype = i64
@@ -188,6 +189,14 @@ def kbin(D: int) -> float:
 def score_bin(s: float, D: int) -> int:
     lib = _load()
     return int(lib.orc_bin(float(s), lib.orc_kbin(D)))
+
+
+def bins(s, D: int) -> np.ndarray:
+    """Top-p bins e_i = floor(s_i * kbin) (clamped; see score_bin) of an array of scores."""
+    s = _c(s, np.float32).ravel()
+    e = np.empty(s.shape[0], dtype=np.int32)
+    _load().orc_bins(D, _p(s), s.shape[0], _p(e))
+    return e
 
 
 def weight_table() -> np.ndarray:

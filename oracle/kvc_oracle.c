@@ -353,6 +353,13 @@ int32_t orc_bin(float s, float kbin)
     return (int32_t)floorf(x);
 }
 
+/* Bins of L scores: e[i] = orc_bin(s[i], kbin(D)). */
+void orc_bins(int D, const float *s, int64_t L, int32_t *e)
+{
+    float kb = orc_kbin(D);
+    for (int64_t i = 0; i < L; ++i) e[i] = orc_bin(s[i], kb);
+}
+
 /* Weight table T[j] = round(2^(32 - j/256)), j = 0..255. */
 void orc_weight_table(uint64_t *T)
 {

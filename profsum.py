@@ -1,9 +1,9 @@
 """Summaries of rocprofv3 output for the committed profiles (kernel times, HBM traffic).
 
-  python -m bit_kv_cache_compress_amd.profsum stats RUN_kernel_stats.csv OUT.txt --command "..."
+  python profsum.py stats RUN_kernel_stats.csv OUT.txt --command "..."
       per-kernel call count and duration table of a ``--kernel-trace --stats`` run
 
-  python -m bit_kv_cache_compress_amd.profsum traffic --kernel K --workload W --source FILE
+  python profsum.py traffic --kernel K --workload W --source FILE
          --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv --copy-mib N
          --out OUT.json [--command "..."]
       HBM bytes per launch of kernel K from two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE;
@@ -22,7 +22,7 @@ import os
 import re
 import statistics
 
-PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_kv_cache_compress_amd", "csrc")
 
 
 def short_name(name: str) -> str:
@@ -72,7 +72,7 @@ def traffic(a) -> dict:
     kib = a.copy_mib * 1024.0
     fs, ws = kib / statistics.median(cfetch), kib / statistics.median(cwrite)
     f_kib, w_kib = statistics.mean(fetch), statistics.mean(write)
-    src = os.path.join(PKG, "csrc", a.source)
+    src = os.path.join(CSRC, a.source)
     rec = {
         "kernel": a.kernel, "workload": a.workload, "source": a.source,
         "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),

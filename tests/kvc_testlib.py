@@ -94,6 +94,43 @@ def download(g):
                 val_codes=g.val_codes.cpu().numpy(), val_sz=g.val_sz.cpu().numpy().view(np.uint32))
 
 
+def oracle_cache_of(gpu: dict, case: Case, sketch=None):
+    """An oracle cache holding the bytes the library wrote (download()), so that the oracle's
+    query encode, scores, Top-p and attention run on exactly the GPU-built records."""
+    c = oracle.PagedCache(case.npages, case.wl.Hkv, case.wl.P, case.wl.D, case.wl.Gv, sketch=sketch)
+    c.key_bits[...] = gpu["key_bits"]
+    c.key_nc[...] = gpu["key_nc"]
+    c.val_codes[...] = gpu["val_codes"]
+    c.val_sz[...] = gpu["val_sz"]
+    return c
+
+
+def chunk_dists(s, D: int, chunk: int = 512):
+    """What the Top-p score pass writes for one query head's L scores, from the oracle's bins:
+    (bin distance of every token to the top bin of its chunk, saturated at 8192, and 8192 past
+    L in the last chunk; the chunks' top bins)."""
+    e = oracle.bins(s, D).astype(np.int64)
+    L = e.shape[0]
+    nch = (L + chunk - 1) // chunk
+    top = np.array([e[c * chunk:(c + 1) * chunk].max() for c in range(nch)], dtype=np.int64)
+    d = np.full(nch * chunk, 8192, dtype=np.int64)
+    d[:L] = np.minimum(np.repeat(top, chunk)[:L] - e, 8192)
+    return d.astype(np.uint16), top.astype(np.int32)
+
+
+def check_bins(dbg, b: int, h: int, s, D: int, ld: int):
+    """The score pass's bin distances and chunk top bins of (b, h) (DecodeDebug with
+    dist=True) against the oracle's bins of the scores s of its L tokens (bit-exact)."""
+    d, top = chunk_dists(s, D)
+    if top.size == 0:
+        return
+    got_d = dbg.bin_dist[b, h].cpu().numpy().view(np.uint16)
+    got_t = dbg.chunk_top[b, h].cpu().numpy()
+    n = min(d.shape[0], ld)
+    np.testing.assert_array_equal(got_d[:n], d[:n])
+    np.testing.assert_array_equal(got_t[:top.shape[0]], top)
+
+
 def written_slots(case: Case):
     """(page, slot) index arrays of every written token, per sequence."""
     pg, sl = [], []

@@ -95,8 +95,24 @@ def test_workspace_too_small():
     assert rc == L.KV_ERR_WORKSPACE
 
 
+def _struct_fields(name):
+    src = open(os.path.join(ROOT, "include", "kv_compress.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    body = re.search(r"typedef struct " + name + r"\s*\{(.*?)\}\s*" + name + ";", src, flags=re.S).group(1)
+    return [re.findall(r"(\w+)\s*(?:\[\w*\])?$", d.strip())[0] for d in body.split(";") if d.strip()]
+
+
+@pytest.mark.parametrize("name,cls", [("kv_cache", "KVCacheDesc"), ("kv_debug", "KVDebug"), ("kv_tail", "KVTailDesc"),
+                                      ("kv_hp", "KVHpDesc"), ("kv_decode_opts", "KVDecodeOpts")])
+def test_binding_structs_match_header(name, cls):
+    """The ctypes structures declare the header's members in the header's order."""
+    assert [f for f, _ in getattr(L, cls)._fields_] == _struct_fields(name)
+
+
 def test_workspace_sizes():
     lib = L.lib()
+    assert lib.kv_workspace_bytes(4, 32, 8, 131072, 128, 0.9) == lib.kv_decode_workspace_bytes(4, 32, 8, 131072, 128,
+                                                                                              0.9)
     full = lib.kv_decode_workspace_bytes(4, 32, 8, 131072, 128, 1.0)
     topp = lib.kv_decode_workspace_bytes(4, 32, 8, 131072, 128, 0.9)
     assert 0 < full < topp

@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.kvc_testlib import rel_err
+from tests.kvc_testlib import Case, check_bins, chunk_dists, compare_caches, download, gpu_append, oracle_cache_of, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,7 @@ def test_gqa_128k_topp_full_size():
     out = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg)
     out_full = kvc.decode_attend(cache, q, seq, pt, top_p=1.0, max_seq_len=L)
     # the decode as the benchmark runs it (no score output: the matrix-core score pass)
-    dbg_fast = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False)
+    dbg_fast = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False, dist=True)
     out_fast = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg_fast)
     torch.cuda.synchronize()
     _say("[full] library decode done")
@@ -63,6 +63,8 @@ def test_gqa_128k_topp_full_size():
     np.testing.assert_array_equal(dbg_fast.sel_bins.cpu().numpy(), dbg.sel_bins.cpu().numpy())
     assert torch.equal(dbg_fast.sel_idx, dbg.sel_idx)
     assert torch.equal(out_fast.view(torch.int32), out.view(torch.int32))
+    fast_dist = {u: (dbg_fast.bin_dist[u[0], u[1] * G:(u[1] + 1) * G].cpu().numpy().view(np.uint16),
+                     dbg_fast.chunk_top[u[0], u[1] * G:(u[1] + 1) * G].cpu().numpy()) for u in SAMPLED_UNITS}
     del dbg_fast, out_fast
 
     # properties on every (sequence, query head)
@@ -111,12 +113,23 @@ def test_gqa_128k_topp_full_size():
         np.testing.assert_array_equal(vc[pg, h, sl], codes)
         np.testing.assert_array_equal(vs[pg, h, sl], sz[..., 0].astype(np.uint32) | (sz[..., 1].astype(np.uint32) << 16))
         same = np.array_equal(kn[pg, h, sl] >> 16, nc[:, 1])
+        # the oracle's scores and Top-p on the records the library wrote: compared always
+        ncw = kn[pg, h, sl]
+        nc_g = np.stack([(ncw & 0xFFFF).astype(np.uint16), (ncw >> 16).astype(np.uint16)], axis=-1)
+        fd, ft = fast_dist[(b, h)]
         for j, hh in enumerate(range(h * G, (h + 1) * G)):
             r = res[j]
-            if same:
-                np.testing.assert_array_equal(scores[b, hh].cpu().numpy().view(np.uint32), r["s"].view(np.uint32))
-                assert cnt[b, hh] == len(r["tp"]["idx"])
-                np.testing.assert_array_equal(idx[b, hh, :cnt[b, hh]], r["tp"]["idx"])
+            qe = oracle.query_encode(orot, qn[b, hh][None, :])
+            _, _, s_g = oracle.scores(kb[pg, h, sl], nc_g, qe["u"][0], qe["c0"][0], qe["c1"][0], wl.D)
+            tp_g = oracle.topp(s_g, wl.top_p, wl.D)
+            np.testing.assert_array_equal(scores[b, hh].cpu().numpy().view(np.uint32), s_g.view(np.uint32))
+            assert cnt[b, hh] == len(tp_g["idx"])
+            np.testing.assert_array_equal(idx[b, hh, :cnt[b, hh]], tp_g["idx"])
+            d_ref, top_ref = chunk_dists(s_g, wl.D)
+            np.testing.assert_array_equal(fd[j], d_ref[:L])
+            np.testing.assert_array_equal(ft[j], top_ref)
+            assert rel_err(o[b, hh], oracle.attend(s_g, codes, sz, wl.D, wl.Gv, tp_g["idx"])) <= 2e-3
+            # end to end, from the oracle's own encoding
             assert rel_err(o[b, hh], r["out"]) <= 2e-3
             assert rel_err(of[b, hh], r["out_full"]) <= 2e-3
         _say(f"[full] unit {(b, h)} ok: cache identical={same}, kept {cnt[b, h * G:(h + 1) * G].tolist()}")
@@ -139,6 +152,50 @@ def test_gqa_128k_topp_full_size():
         for j, hh in enumerate(range(h * G, (h + 1) * G)):
             assert rel_err(o2[b, hh], res[j]["out"]) <= 2e-3
     _say("[full] the benchmark's step (append inside the decode) ok")
+
+
+def test_7b_layer_full_size():
+    """The 7B-shaped layer at its own shape: 32 heads x 8192 tokens, fp16 K/V with 4 outlier
+    channels per head scaled by 8, dense rotation, full softmax.  Every head: the cache bytes
+    against the oracle's encoding, the scores against the oracle on the library's records, and
+    the outputs against the oracle; then the same cache under Top-p 0.9 (sets and the score
+    pass's bins bit-exact)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_kv_cache_compress_amd as kvc
+
+    wl = W.CONFIGS[1]
+    c = Case(wl)
+    _say(f"[full] {wl.name}: oracle encode of {c.L} x {wl.Hkv} token-heads")
+    c.ocache = c.oracle_cache()
+    g = gpu_append(c)
+    gb = download(g)
+    stats = compare_caches(gb, c.ocache, c)
+    _say(f"[full] cache ok {stats}")
+    dev = torch.device("cuda")
+    q = torch.from_numpy(c.q).to(dev)
+    lens = torch.from_numpy(c.lens).to(dev)
+    pt = torch.from_numpy(c.pt).to(dev)
+    og = oracle_cache_of(gb, c)
+    for top_p in (1.0, 0.9):
+        dbg = kvc.DecodeDebug.allocate(wl.B, wl.Hq, c.L, top_p < 1.0, dev, scores=top_p >= 1.0, dist=True)
+        out = kvc.decode_attend(g, q, lens, pt, top_p=top_p, max_seq_len=c.L, debug=dbg).cpu().numpy()
+        ref = c.oracle_decode(c.ocache, top_p)
+        ref_g = c.oracle_decode(og, top_p)
+        worst = 0.0
+        for (b, h), r in ref_g.items():
+            if top_p >= 1.0:
+                np.testing.assert_array_equal(dbg.iscores[b, h].cpu().numpy(), r["A"])
+                np.testing.assert_array_equal(dbg.scores[b, h].cpu().numpy().view(np.uint32), r["score"].view(np.uint32))
+            else:
+                cnt = int(dbg.sel_count[b, h])
+                assert cnt == len(r["idx"]), (h, cnt, len(r["idx"]))
+                np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+                check_bins(dbg, b, h, r["score"], wl.D, c.L)
+            e = max(float(rel_err(out[b, h], r["out"])), float(rel_err(out[b, h], ref[(b, h)]["out"])))
+            worst = max(worst, e)
+            assert e <= 2e-3, (h, e)
+        _say(f"[full] top_p={top_p}: every head ok, worst rel err {worst:.2e}")
 
 
 def _check_unit_cache(kb, kn, vc, vs, pg, sl, h, bits, nc, codes, sz):
@@ -262,7 +319,7 @@ def test_append32k_and_decode1m_full_size():
         kvc.append(cache, K[:, a:a + n_new].contiguous(), V[:, a:a + n_new].contiguous(),
                    torch.full((B,), a, dtype=torch.int32, device=dev), pt)
     seq = torch.from_numpy(lens).to(dev)
-    dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False)
+    dbg = kvc.DecodeDebug.allocate(B, Hq, L, True, dev, scores=False, dist=True)
     out = kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=L, debug=dbg)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
@@ -279,16 +336,25 @@ def test_append32k_and_decode1m_full_size():
     t = np.arange(L)
     pg, sl = pt_np[0, t // P], t % P
     np.testing.assert_array_equal(kb[pg, sl], bits)
-    same = np.array_equal(kn[pg, sl] >> 16, nc[:, 1])
+    np.testing.assert_array_equal(kn[pg, sl] & 0xFFFF, nc[:, 0])
+    assert np.all(np.abs((kn[pg, sl] >> 16).astype(np.int64) - nc[:, 1].astype(np.int64)) <= 1)
+    ncw = kn[pg, sl]
+    nc_g = np.stack([(ncw & 0xFFFF).astype(np.uint16), (ncw >> 16).astype(np.uint16)], axis=-1)
     qn = q.cpu().numpy()
     o = out.cpu().numpy()
     for hh in range(h * G, (h + 1) * G):
         qe = oracle.query_encode(orot, qn[0, hh][None, :])
+        # Top-p sets and the score pass's bins from the oracle on the library's records
+        _, _, s_g = oracle.scores(kb[pg, sl], nc_g, qe["u"][0], qe["c0"][0], qe["c1"][0], D)
+        tp_g = oracle.topp(s_g, wl.top_p, D)
+        assert cnt[0, hh] == len(tp_g["idx"])
+        np.testing.assert_array_equal(dbg.sel_idx[0, hh, :cnt[0, hh]].cpu().numpy(), tp_g["idx"])
+        d_ref, top_ref = chunk_dists(s_g, D)
+        np.testing.assert_array_equal(dbg.bin_dist[0, hh].cpu().numpy().view(np.uint16), d_ref[:L])
+        np.testing.assert_array_equal(dbg.chunk_top[0, hh].cpu().numpy(), top_ref)
+        # end to end from the oracle's own encoding
         _, _, s = oracle.scores(bits, nc, qe["u"][0], qe["c0"][0], qe["c1"][0], D)
         tp = oracle.topp(s, wl.top_p, D)
-        if same:
-            assert cnt[0, hh] == len(tp["idx"])
-            np.testing.assert_array_equal(dbg.sel_idx[0, hh, :cnt[0, hh]].cpu().numpy(), tp["idx"])
         assert rel_err(o[0, hh], oracle.attend(s, codes, sz, D, Gv, tp["idx"])) <= 2e-3
         _say(f"[full] head {hh}: kept {cnt[0, hh]} of {L}")
 
@@ -324,6 +390,9 @@ def test_gqa_128k_exact_keys_full_size():
     qn = q.cpu().numpy()
     vc = cache.val_codes.cpu().numpy()
     vs = cache.val_sz.cpu().numpy().view(np.uint32)
+    kb = cache.key_bits.cpu().numpy().view(np.uint32)
+    kn = cache.key_nc.cpu().numpy().view(np.uint32)
+    orot = oracle.Rotation(oracle.ROT_DENSE, wl.D, R16=R16)
     for b, h in [(1, 2), (2, 5)]:
         t = np.arange(L)
         pg, sl = pt_np[b, t // wl.P], t % wl.P
@@ -332,8 +401,15 @@ def test_gqa_128k_exact_keys_full_size():
         codes = vc[pg, h, sl]
         szw = vs[pg, h, sl]
         sz = np.stack([(szw & 0xFFFF).astype(np.uint16), (szw >> 16).astype(np.uint16)], axis=-1)
+        ncw = kn[pg, h, sl]
+        nc_g = np.stack([(ncw & 0xFFFF).astype(np.uint16), (ncw >> 16).astype(np.uint16)], axis=-1)
         for hh in range(h * G, (h + 1) * G):
-            idx = dbg.sel_idx[b, hh, :cnt[b, hh]].cpu().numpy()
+            # the set the oracle's Top-p chooses on the library's records, not the library's own
+            qe = oracle.query_encode(orot, qn[b, hh][None, :])
+            _, _, s_g = oracle.scores(kb[pg, h, sl], nc_g, qe["u"][0], qe["c0"][0], qe["c1"][0], wl.D)
+            idx = oracle.topp(s_g, wl.top_p, wl.D)["idx"]
+            assert cnt[b, hh] == len(idx)
+            np.testing.assert_array_equal(dbg.sel_idx[b, hh, :cnt[b, hh]].cpu().numpy(), idx)
             ref = oracle.attend_exact(qn[b, hh], k16, codes, sz, wl.D, wl.Gv, idx)
             assert rel_err(o[b, hh], ref) <= 2e-3
         _say(f"[full] unit {(b, h)} ok, kept {cnt[b, h * G:(h + 1) * G].tolist()}")

@@ -20,7 +20,7 @@ from oracle import ideal
 from workloads import haar_orthogonal_batch
 
 D = 128
-S = 12000
+S = 20000
 
 
 def _pair(rng, cos=0.3):

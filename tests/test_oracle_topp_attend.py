@@ -49,6 +49,13 @@ def test_bin_is_floor_and_clamped():
     assert oracle.score_bin(float("nan"), D) == -(2**29)
 
 
+def test_bins_vector_matches_scalar():
+    """The array form of the bins agrees with the scalar bin, clamps and NaN included."""
+    rng = np.random.default_rng(7)
+    s = np.concatenate([rng.normal(0, 30, 500), [0.0, -0.0, 1e30, -1e30, np.nan, np.inf, -np.inf]]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.bins(s, D), [oracle.score_bin(float(x), D) for x in s])
+
+
 def _nucleus_masses(s, S, p):
     """Binary64 softmax masses of S and of S minus its lowest bin."""
     w = np.exp((s.astype(np.float64) - s.max()) / np.sqrt(D))

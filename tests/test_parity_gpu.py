@@ -14,7 +14,8 @@ import pytest
 
 import oracle
 import workloads as W
-from tests.kvc_testlib import Case, compare_caches, download, gpu_append, rel_err, upload
+from tests.kvc_testlib import (Case, check_bins, compare_caches, download, gpu_append, oracle_cache_of, rel_err,
+                               upload)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -72,16 +73,17 @@ def test_append_parity(name):
     _say(f"[append] {name} ok {stats}")
 
 
-def _decode_with_debug(c, cache, top_p, scores=True, proxy=False):
+def _decode_with_debug(c, cache, top_p, scores=True, proxy=False, dist=True):
     """Decode with debug outputs; scores=False runs the kernels of a decode without debug
-    output (the per-token scores are not written) and still returns the Top-p sets."""
+    output (the per-token scores are not written) and still returns the Top-p sets and what
+    the score pass wrote (bin distances, chunk top bins)."""
     from bit_kv_cache_compress_amd import DecodeDebug, decode_attend
 
     dev = torch.device("cuda")
     q = torch.from_numpy(c.q).to(dev)
     lens = torch.from_numpy(c.lens.astype(np.int32)).to(dev)
     pt = torch.from_numpy(c.pt).to(dev)
-    dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev, scores=scores)
+    dbg = DecodeDebug.allocate(c.wl.B, c.wl.Hq, c.max_len, top_p < 1.0, dev, scores=scores, dist=dist)
     out = decode_attend(cache, q, lens, pt, top_p=top_p, max_seq_len=c.max_len, debug=dbg, proxy=proxy)
     torch.cuda.synchronize()
     return out.cpu().numpy(), dbg
@@ -116,6 +118,7 @@ def test_decode_stagewise(name, mode):
             np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
             bins = dbg.sel_bins[b, h].cpu().numpy()
             assert (int(bins[0]), int(bins[1])) == (r["emax"], r["bstar"])
+            check_bins(dbg, b, h, r["score"], c.wl.D, c.max_len)
         e = float(rel_err(out[b, h], r["out"])) if n else float(np.abs(out[b, h]).max())
         if n == 0:
             assert e == 0.0
@@ -130,15 +133,26 @@ def test_end_to_end(name):
     c = _case(name)
     _say(f"[e2e] {name}")
     g = gpu_append(c)
-    same = all(np.array_equal(v, getattr(c.ocache, k)) for k, v in download(g).items())
+    gb = download(g)
+    same = all(np.array_equal(v, getattr(c.ocache, k)) for k, v in gb.items())
     out, dbg = _decode_with_debug(c, g, c.wl.top_p, scores=False)
     ref = c.oracle_decode(c.ocache, c.wl.top_p)
     worst = max(float(rel_err(out[b, h], r["out"])) if int(c.lens[b]) else 0.0 for (b, h), r in ref.items())
     assert worst <= TOL
-    if same and c.wl.top_p < 1.0:
-        for (b, h), r in ref.items():
+    # the oracle's query encode, scores, Top-p and attention on the bytes the library wrote:
+    # every set, bin and threshold bit-exact whatever the encoders' rounding did
+    ref_g = c.oracle_decode(oracle_cache_of(gb, c), c.wl.top_p)
+    for (b, h), r in ref_g.items():
+        n = int(c.lens[b])
+        if n:
+            assert rel_err(out[b, h], r["out"]) <= TOL
+        if c.wl.top_p < 1.0 and n:
             cnt = int(dbg.sel_count[b, h])
+            assert cnt == len(r["idx"]), (b, h, cnt, len(r["idx"]))
             np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            bins = dbg.sel_bins[b, h].cpu().numpy()
+            assert (int(bins[0]), int(bins[1])) == (r["emax"], r["bstar"])
+            check_bins(dbg, b, h, r["score"], c.wl.D, c.max_len)
     _say(f"[e2e] {name} ok, caches identical={same}, worst rel err {worst:.2e}")
 
 
@@ -156,6 +170,11 @@ def test_score_kernels_agree(name):
     np.testing.assert_array_equal(d_fast.sel_bins.cpu().numpy(), d_dbg.sel_bins.cpu().numpy())
     np.testing.assert_array_equal(d_fast.sel_idx.cpu().numpy(), d_dbg.sel_idx.cpu().numpy())
     assert np.array_equal(o_fast.view(np.uint32), o_dbg.view(np.uint32))
+    # the fast kernels' own output, per token: bins of every query head against the oracle's
+    ref = c.oracle_decode(c.ocache, c.wl.top_p)
+    for (b, h), r in ref.items():
+        if int(c.lens[b]):
+            check_bins(d_fast, b, h, r["score"], c.wl.D, c.max_len)
     _say(f"[kernels] {name} ok")
 
 
