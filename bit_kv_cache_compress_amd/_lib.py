@@ -15,7 +15,8 @@ KV_OK, KV_ERR_ARG, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_ERR_HIP = 0, -1, -2,
 KV_ROT_DENSE, KV_ROT_HADAMARD = 0, 1
 KV_F16, KV_F32 = 0, 1
 
-EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_ex", "kv_decode_attend_tail",
+EXPORTS = ("kv_compress_append", "kv_decode_attend", "kv_decode_attend_ex", "kv_decode_attend_noalloc",
+           "kv_decode_attend_tail",
            "kv_decode_workspace_bytes", "kv_workspace_bytes", "kv_hp_update",
            "kv_tail_append", "kv_tail_retire", "kv_topp_select", "kv_topp_workspace_bytes", "kv_last_error",
            "kv_version")
@@ -131,6 +132,9 @@ def lib():
     L.kv_decode_attend_ex.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVDecodeOpts), P, i32, i32, P, i32,
                                       P, i32, f32, P, ctypes.POINTER(KVDebug), P, sz, P]
     L.kv_decode_attend_ex.restype = ctypes.c_int
+    L.kv_decode_attend_noalloc.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVDecodeOpts), P, i32, i32, P,
+                                           i32, P, i32, f32, P, ctypes.POINTER(KVDebug), P]
+    L.kv_decode_attend_noalloc.restype = ctypes.c_int
     L.kv_hp_update.argtypes = [ctypes.POINTER(KVCacheDesc), ctypes.POINTER(KVHpDesc), ctypes.POINTER(KVTailDesc), i32,
                                i32, P, P, i32, P]
     L.kv_hp_update.restype = ctypes.c_int

@@ -253,7 +253,8 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
                   workspace: Optional[torch.Tensor] = None, debug: Optional[DecodeDebug] = None,
                   debug_struct: Optional[L.KVDebug] = None, proxy: bool = False,
                   tail: Optional["Tail"] = None, q_dither: Optional[torch.Tensor] = None,
-                  hp: Optional["HPTier"] = None, append: Optional[tuple] = None) -> torch.Tensor:
+                  hp: Optional["HPTier"] = None, append: Optional[tuple] = None,
+                  noalloc: bool = False) -> torch.Tensor:
     """One decode step: q [B, Hq, 128] float32 -> out [B, Hq, 128] float32.  Under Top-p, a
     cache with binary16 keys scores the selected tokens exactly unless ``proxy`` is set.
     With ``tail``, each sequence's binary16 tail tokens follow its seq_lens compressed ones.
@@ -261,7 +262,9 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
     query codes, floor(t + U) instead of rint(t).  ``hp``: the high-precision tier, attended
     exactly next to the tail; the tail (created with mass=True) and the tier accumulate mass.
     ``append`` = (k, v, start_pos): new tokens written into the cache first, as ``append``
-    would write them (seq_lens must count them), inside the decode's first launch."""
+    would write them (seq_lens must count them), inside the decode's first launch.
+    ``noalloc``: run kv_decode_attend_noalloc, whose workspace is the library's static
+    per-device array (``workspace`` must then be None; pass ``out`` to allocate nothing)."""
     dev = cache.device
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must be [B, Hq, {HEAD_DIM}]")
@@ -277,10 +280,14 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, (B, Hq, HEAD_DIM))
-    need = decode_workspace_bytes(B, Hq, cache.num_kv_heads, max_seq_len, top_p)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, dev)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc decodes use the library's static workspace")
+    else:
+        need = decode_workspace_bytes(B, Hq, cache.num_kv_heads, max_seq_len, top_p)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, dev)
     if debug is not None:
         debug_struct = debug.struct()
     dbg = ctypes.byref(debug_struct) if debug_struct is not None else None
@@ -293,16 +300,22 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, page_
     if append is not None:
         ak, av, asp = append
         app = L.KVAppendArgs(*_append_args(cache, ak, av, asp, B))
-    if q_dither is not None or hp is not None or app is not None:
+    if noalloc or q_dither is not None or hp is not None or app is not None:
         if q_dither is not None:
             _need(q_dither, "q_dither", torch.float32, dev, (B, Hq, HEAD_DIM))
         opts = L.KVDecodeOpts(ctypes.pointer(tail.desc) if tail is not None else None,
                               _ptr(q_dither) if q_dither is not None else None,
                               ctypes.pointer(hp.desc) if hp is not None else None,
                               ctypes.pointer(app) if app is not None else None)
-        L.check(L.lib().kv_decode_attend_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), B, Hq, _ptr(seq_lens),
-                                            int(max_seq_len), _ptr(page_table), max_pages, float(top_p), _ptr(out),
-                                            dbg, _ptr(workspace), workspace.numel(), _stream(dev)))
+        if noalloc:
+            L.check(L.lib().kv_decode_attend_noalloc(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), B, Hq,
+                                                     _ptr(seq_lens), int(max_seq_len), _ptr(page_table), max_pages,
+                                                     float(top_p), _ptr(out), dbg, _stream(dev)))
+        else:
+            L.check(L.lib().kv_decode_attend_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), B, Hq,
+                                                _ptr(seq_lens), int(max_seq_len), _ptr(page_table), max_pages,
+                                                float(top_p), _ptr(out), dbg, _ptr(workspace), workspace.numel(),
+                                                _stream(dev)))
     elif tail is None:
         L.check(L.lib().kv_decode_attend(ctypes.byref(desc), _ptr(q), B, Hq, _ptr(seq_lens), int(max_seq_len),
                                          _ptr(page_table), max_pages, float(top_p), _ptr(out), dbg,

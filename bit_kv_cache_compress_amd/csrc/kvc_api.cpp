@@ -608,12 +608,12 @@ int kv_decode_attend_tail(const kv_cache *c, const kv_tail *tail, const float *q
                        top_p, out, dbg, workspace, workspace_bytes, stream);
 }
 
-int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
-                        const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
-                        int32_t max_pages, float top_p, float *out, const kv_debug *dbg, void *workspace,
-                        size_t workspace_bytes, hipStream_t stream)
+namespace {
+
+int decode_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
+              const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table, int32_t max_pages, float top_p,
+              float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    g_err[0] = 0;
     if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
     const kv_tail *tail = opts ? opts->tail : nullptr;
     const float *dither = opts ? opts->q_dither : nullptr;
@@ -631,6 +631,40 @@ int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const flo
     const kv_append_args *app = opts ? opts->append : nullptr;
     return decode_impl(c, tail, hp, dither, app, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out,
                        dbg, workspace, workspace_bytes, stream);
+}
+
+}  // namespace
+
+int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
+                        const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                        int32_t max_pages, float top_p, float *out, const kv_debug *dbg, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream)
+{
+    g_err[0] = 0;
+    return decode_ex(c, opts, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg, workspace,
+                     workspace_bytes, stream);
+}
+
+int kv_decode_attend_noalloc(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
+                             const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                             int32_t max_pages, float top_p, float *out, const kv_debug *dbg, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!c) return fail(KV_ERR_ARG, "cache descriptor is NULL");
+    int rc = check_decode_shapes(B, Hq, c->num_kv_heads, max_seq_len, c->head_dim, top_p);
+    if (rc) return rc;
+    Plan pl;
+    make_plan(pl, B, Hq, c->num_kv_heads, max_seq_len, top_p);
+    if (pl.total > kvc::kStaticScratchBytes)
+        return fail(KV_ERR_WORKSPACE,
+                    "this decode needs %zu bytes of workspace, above the %zu bytes of the static workspace of "
+                    "kv_decode_attend_noalloc (use kv_decode_attend_ex with a caller workspace)",
+                    pl.total, kvc::kStaticScratchBytes);
+    void *ws = nullptr;
+    hipError_t e = kvc::static_scratch(stream, &ws);
+    if (e != hipSuccess) return hip_fail(e, "static workspace address");
+    return decode_ex(c, opts, q, B, Hq, seq_lens, max_seq_len, page_table, max_pages, top_p, out, dbg, ws, pl.total,
+                     stream);
 }
 
 int kv_hp_update(const kv_cache *c, const kv_hp *hp, const kv_tail *t, int32_t B, int32_t n,

@@ -13,6 +13,8 @@
 // each thread issues all of its loads of a pass before using any of them, so that a block
 // keeps several KB of HBM reads in flight.  Partial results (max score, weight sum, weighted
 // value sum) of all chunks are merged per (sequence, query head) at the end.
+#include <mutex>
+
 #include "kvc_append_dev.h"
 #include "kvc_device.h"
 #include "kvc_launch.h"
@@ -21,6 +23,12 @@ namespace kvc {
 
 // Result words of the argument checker (k_check), one copy per device.
 __device__ int32_t g_check_flag[4];
+
+// Workspace of kv_decode_attend_noalloc: every device the library runs on holds its own copy
+// until the process ends.  Host code reaches it only through the per-device address that
+// static_scratch() takes with hipGetSymbolAddress (the array's name in host code is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -1962,6 +1970,40 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         }
     }
     return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];  // the device address of each device's copy of `scratch`
+}  // namespace
+
+hipError_t static_scratch(hipStream_t s, void **ptr)
+{
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (s) {
+        e = hipStreamGetDevice(s, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        // once per device, with that device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_check(const CheckParams &p, int32_t *flag_host, hipStream_t s)

@@ -241,6 +241,11 @@ struct HpUpdateParams {
 };
 hipError_t launch_hp_update(const HpUpdateParams &p, hipStream_t s);
 
+// Bytes of the static workspace of kv_decode_attend_noalloc (per device).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+// Device address of the static workspace on the device of stream s (taken once per device).
+hipError_t static_scratch(hipStream_t s, void **ptr);
+
 // Device-side argument checker (KV_DEBUG=1): one block per sequence checks the token range a
 // call would touch -- [0, seq_lens[b]) for a decode, [start_pos[b], start_pos[b] + n_new) for
 // an append -- against its bound and the page table entries covering it against num_pages.

@@ -317,6 +317,22 @@ int kv_decode_attend_ex(const kv_cache *c, const kv_decode_opts *opts, const flo
                         int32_t max_pages, float top_p, float *out, const kv_debug *dbg,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kv_decode_attend_noalloc -- kv_decode_attend_ex without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a 64 MiB array in the library's device code, one
+ * copy per device, held from the library's load until the process ends; its address is taken
+ * once per device (hipGetSymbolAddress, with that device current) on the first call that runs
+ * on the device.  The call allocates nothing and frees nothing.
+ *   Arguments, results and errors as kv_decode_attend_ex; KV_ERR_WORKSPACE when the decode
+ *   needs more than 64 MiB of workspace (kv_decode_workspace_bytes(...) > 64 MiB; for example
+ *   the 128k-token, 4-sequence, 32-query-head Top-p decode needs about 49 MiB).
+ *   Every call on one device shares that device's array, and each call overwrites what it
+ *   needs (nothing has to start at zero): calls that may overlap on one device -- on two
+ *   streams, or from two threads -- race, and the caller must order them. */
+int kv_decode_attend_noalloc(const kv_cache *c, const kv_decode_opts *opts, const float *q, int32_t B, int32_t Hq,
+                             const int32_t *seq_lens, int32_t max_seq_len, const int32_t *page_table,
+                             int32_t max_pages, float top_p, float *out, const kv_debug *dbg, hipStream_t stream);
+
 /* kv_hp_update -- the tier's promotion step, when the first n tokens of every tail (positions
  * seq_lens[b] .. seq_lens[b] + n - 1) have been compressed into the cache and before
  * kv_tail_retire(n) drops them.  For each (sequence, KV head), among the tier's entries and

@@ -224,3 +224,17 @@ def test_hp_update_rejects_bad_arguments():
     assert upd(desc=_desc(value_group=16)) == L.KV_ERR_UNSUPPORTED
     assert upd(n=0) == L.KV_OK
 
+
+
+def test_noalloc_rejects_workspaces_above_its_static_array():
+    """kv_decode_attend_noalloc has a 64 MiB static workspace per device: a decode that needs
+    more is refused on the host (KV_ERR_WORKSPACE, nothing enqueued), as are bad shapes."""
+    lib = L.lib()
+    d = _desc(num_pages=4096)
+    need = lib.kv_decode_workspace_bytes(4, 32, 8, 262144, 128, 0.9)
+    assert need > 64 << 20
+    rc = lib.kv_decode_attend_noalloc(ctypes.byref(d), None, FAKE, 4, 32, FAKE, 262144, FAKE, 1024, 0.9, FAKE, None,
+                                      None)
+    assert rc == L.KV_ERR_WORKSPACE and "static workspace" in L.last_error()
+    rc = lib.kv_decode_attend_noalloc(ctypes.byref(d), None, FAKE, 4, 24, FAKE, 1000, FAKE, 4, 0.9, FAKE, None, None)
+    assert rc == L.KV_ERR_UNSUPPORTED
