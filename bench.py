@@ -25,11 +25,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "compressed-KV decode: KV tokens*heads attended/s and % of MI355X HBM peak"
+APPEND_METRIC = "compressed-KV append: token-heads compressed/s and % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
-# Algorithmic bytes per unit: a cached key is 16 B of sign words + a 4 B norm/correction
-# word per token-KV-head; a cached value is 64 B of 4-bit codes + a 4 B scale/zero word per
-# group.  Top-p adds a 2 B bin distance per (token, query head), written by the score pass
-# and read by the histogram and attention passes.
+# Algorithmic bytes (the least a step must move): a cached key is 16 B of sign words + a 4 B
+# norm/correction word per token-KV-head, read once per step; a cached value is 64 B of 4-bit
+# codes + a 4 B scale/zero word per group, read once per attended token-KV-head (under Top-p:
+# the union of the kept tokens of the KV head's query heads).  The design also moves a 2 B
+# bin distance per (token, query head) (written by the score pass, read by the histogram and
+# attention passes) and re-reads the key records of kept tokens; those count as design
+# bytes, not algorithmic ones.
 DIST_BYTES = 2
 
 
@@ -47,6 +51,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index 0..4 (default 2: GQA 128k Top-p)")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="override the workload's top_p (1 = full softmax, e.g. --config 2 --top-p 1: the "
+                         "128k streaming check)")
+    ap.add_argument("--append", action="store_true",
+                    help="time the prefill append of workload 4 (32768 tokens x 32 KV heads, randomized "
+                         "Hadamard rotation) instead of a decode step: token-heads compressed/s")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--lazy", action="store_true",
                     help="lazy updates: new tokens go to a binary16 tail, whole pages are compressed on a "
@@ -78,6 +88,17 @@ def parse():
     return a
 
 
+def workload(args):
+    """The workload of --config, with --top-p applied (and named after it)."""
+    import workloads as W
+
+    wl = W.CONFIGS[args.config]
+    if args.top_p is not None and args.top_p != wl.top_p:
+        base = wl.name.rsplit("-topp", 1)[0] if wl.top_p < 1.0 else wl.name
+        wl = wl.scaled(top_p=args.top_p, name=base + ("-full" if args.top_p >= 1.0 else f"-topp{args.top_p:g}"))
+    return wl
+
+
 def run_lazy(args):
     """Decode steps with lazy updates: each step writes the new token of every sequence into
     the binary16 tail and decodes over cache plus tail; when a tail holds more than a page, its
@@ -89,7 +110,7 @@ def run_lazy(args):
     import bit_kv_cache_compress_amd as kvc
     import workloads as W
 
-    wl = W.CONFIGS[args.config]
+    wl = workload(args)
     if wl.len_range is not None:
         raise SystemExit("--lazy needs a workload with equal sequence lengths")
     dev = torch.device("cuda:0")
@@ -200,6 +221,140 @@ def run_lazy(args):
     print(json.dumps(result), flush=True)
 
 
+def run_append(args):
+    """The prefill append of workload 4: 32768 new tokens x 32 KV heads of binary16 K/V
+    (N(0,1)) encoded with the randomized Hadamard rotation into the paged cache (sign bits,
+    norm and correction of every key; 4-bit codes with scale and zero point of every value).
+    One launch per step, timed with events on the stream it runs on; caches flushed between
+    steps.  Algorithmic bytes: the K and V read (512 B per token-head) and the 20 B key and
+    80 B value records written."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_compress_amd as kvc
+    import workloads as W
+
+    wl = W.CONFIGS[4]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    D, P, Gv = wl.D, wl.P, wl.Gv
+    n_new, Ha = wl.append_tokens, wl.append_heads
+    name = f"hadamard-append{n_new // 1024}k-{Ha}kvh-f16"
+    log(f"[bench] append workload {name}: {n_new} tokens x {Ha} KV heads, rotation {wl.rot}, value group {Gv}")
+    K, V, _ = W.draw_device(wl, dev, L=n_new, Hkv=Ha)
+    pt_np, npages = W.page_layout(wl.scaled(Hkv=Ha), np.array([n_new], np.int32))
+    kind, signs = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, Ha, signs, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    pt = torch.from_numpy(pt_np).to(dev)
+    start = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+
+    def step():
+        kvc.append(cache, K, V, start, pt)
+
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            flush_buf.sum()
+            step()
+        torch.cuda.synchronize()
+        log("[bench] profile steps done")
+        return
+    for _ in range(args.warmup):
+        flush_buf.sum()
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush_buf.sum()
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = statistics.mean(step_ms)
+    th = n_new * Ha
+    value = th / (ms / 1e3)
+    key_bytes, vb = 20, value_bytes(Gv)
+    alg = th * (2 * D * 2 + key_bytes + vb)
+    ach = alg / (ms / 1e3) / 1e9
+    kern = "k_append_hadamard" if kind != "dense" else "k_append_dense"
+    log(f"[bench] append {ms * 1e3:.1f} us (median {statistics.median(step_ms) * 1e3:.1f}); {value:.3e} "
+        f"token-heads/s; {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
+    result = {
+        "metric": APPEND_METRIC, "value": value, "unit": "token-heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 in, f32 arithmetic, u8/u32 records out", "data": "synthetic",
+        "config": {"workload": name, "new_tokens": n_new, "kv_heads": Ha, "head_dim": D, "value_group": Gv,
+                   "page_size": P, "rotation": wl.rot, "kv_dtype": wl.kv_dtype,
+                   "cache_flushed_between_steps": not args.no_flush},
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kern, name),
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_us": round(ms * 1e3, 2)},
+        "step_us_median": round(statistics.median(step_ms) * 1e3, 2),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity_sample"] = cpu_append_baseline(args, wl, K, V, cache, pt_np, signs)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_append_baseline(args, wl, K, V, cache, pt_np, signs):
+    """The oracle's key and value encode, untuned, on a bounded sample of the same append:
+    the first tokens of every KV head, split over the host cores by (head, token block)."""
+    import numpy as np
+
+    import oracle
+
+    D, P, Gv = wl.D, wl.P, wl.Gv
+    Ha = K.shape[2]
+    cores = len(os.sched_getaffinity(0))
+    n = 2048  # tokens per head in the sample
+    orot = oracle.Rotation(oracle.ROT_HADAMARD, D, signs=signs)
+    k = K[0, :n].float().cpu().numpy()
+    v = V[0, :n].float().cpu().numpy()
+    units = [(h, t0) for h in range(Ha) for t0 in range(0, n, 256)]
+
+    def enc(u):
+        h, t0 = u
+        bits, nc = oracle.key_encode(orot, k[t0:t0 + 256, h])
+        codes, sz = oracle.value_encode(v[t0:t0 + 256, h], D, Gv)
+        return bits, nc, codes, sz
+
+    reps = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        while True:
+            res = list(ex.map(enc, units))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el * (reps + 1) / reps > args.cpu_seconds or reps >= 200:
+                break
+    cpu_value = reps * n * Ha / el
+    # parity of the sample against the bytes the library wrote
+    kb = cache.key_bits.cpu().numpy().view(np.uint32)
+    kn = cache.key_nc.cpu().numpy().view(np.uint32)
+    vc = cache.val_codes.cpu().numpy()
+    vs = cache.val_sz.cpu().numpy().view(np.uint32)
+    bad = 0
+    for (h, t0_), (bits, nc, codes, sz) in zip(units, res):
+        t = np.arange(t0_, t0_ + 256)
+        pg, sl = pt_np[0, t // P], t % P
+        ok = (np.array_equal(kb[pg, h, sl], bits) and np.array_equal(kn[pg, h, sl] & 0xFFFF, nc[:, 0])
+              and np.all(np.abs((kn[pg, h, sl] >> 16).astype(np.int64) - nc[:, 1].astype(np.int64)) <= 1)
+              and np.array_equal(vc[pg, h, sl], codes)
+              and np.array_equal(vs[pg, h, sl], sz[..., 0].astype(np.uint32) | (sz[..., 1].astype(np.uint32) << 16)))
+        bad += 0 if ok else 1
+    log(f"[cpu] oracle append {cpu_value:.3e} token-heads/s on {cores} threads; sample units differing: {bad}")
+    base = {"value": cpu_value, "unit": "token-heads/s", "cores": min(cores, len(units)), "kind": "oracle",
+            "sample": f"first {n} tokens of each of {Ha} KV heads x {reps} repetition(s): the oracle's key and "
+                      f"value encode in {len(units)} (head, 256-token) units", "seconds": round(el, 2)}
+    return base, {"units": len(units), "units_differing": bad,
+                  "bar": "sign bits, norms, codes, scale/zero bit-exact; correction within one binary16 ulp"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -222,11 +377,13 @@ def main():
 
     if args.lazy:
         return run_lazy(args)
+    if args.append:
+        return run_append(args)
 
     import bit_kv_cache_compress_amd as kvc
     import workloads as W
 
-    wl = W.CONFIGS[args.config]
+    wl = workload(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     D, Hq, Hkv, B, P, Gv = wl.D, wl.Hq, wl.Hkv, wl.B, wl.P, wl.Gv
@@ -372,45 +529,58 @@ def main():
             f"union over GQA groups {sel_union} token-KV-heads")
         del dbg, mask
 
-    # ---- roofline of the dominant kernel
+    # ---- roofline of the dominant kernel (the stage with the longest average duration)
     G = Hq // Hkv
     kv_in = 2 if wl.kv_dtype == "f16" else 4
     key_bytes = 4 * (args.sketch_dim // 32 + 1)  # the key record: sign words and the norm/corr word
-    kept_key_bytes = 2 * D if args.exact_keys and wl.top_p < 1.0 else key_bytes
-    per_launch = {
-        # every key of the context, each scored for the G query heads of its KV head, and
-        # the bin distances written
-        "score": (key_bytes + DIST_BYTES * G) * tokens_heads if wl.top_p < 1.0 else key_bytes * tokens_heads,
-        # Top-p: the distances, then key and value of every kept (token, query head);
-        # full softmax: every key and value once per KV head
-        # (with binary16 keys, the 2 D bytes of the key instead of its 20-byte record)
-        "attend": (DIST_BYTES * G * tokens_heads + (kept_key_bytes + value_bytes(Gv)) * sel_entries)
-        if sel_entries is not None else (key_bytes + value_bytes(Gv)) * tokens_heads,
-        # the distances once
-        "hist": DIST_BYTES * G * tokens_heads,
-        "append": (2 * D * kv_in + key_bytes + value_bytes(Gv) + (2 * D if args.exact_keys else 0)) * B * Hkv}
-    score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if wl.top_p < 1.0 else "k_score"
+    topp = wl.top_p < 1.0
+    exact = args.exact_keys and topp
+    vb = value_bytes(Gv)
+    new_tokens = B * Hkv  # the step appends one token per sequence and KV head
+    append_alg = (2 * D * kv_in + key_bytes + vb + (2 * D if args.exact_keys else 0)) * new_tokens
+    # algorithmic bytes per launch: every key record once (score pass; the full-softmax
+    # attention pass reads keys itself), the value record of every attended token-KV-head once
+    # (Top-p: the union over the KV head's query heads; with binary16 keys, also those keys)
+    alg = {
+        "score": key_bytes * tokens_heads,
+        "attend": (vb + (2 * D if exact else 0)) * sel_union if topp else (key_bytes + vb) * tokens_heads,
+        "hist": 0, "query": 0, "merge": 0, "append": append_alg}
+    # what the design moves on top: 16-bit bin distances (written once, read by the histogram
+    # and the attention pass), the kept tokens' key records re-read for their scores, and one
+    # value record per kept (token, query head) rather than per KV head
+    design = {
+        "score": (key_bytes + DIST_BYTES * G) * tokens_heads if topp else key_bytes * tokens_heads,
+        "attend": (DIST_BYTES * G * tokens_heads + ((2 * D if exact else key_bytes) + vb) * sel_entries)
+        if topp else (key_bytes + vb) * tokens_heads,
+        "hist": DIST_BYTES * G * tokens_heads, "query": 0, "merge": 0, "append": append_alg}
+    score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if topp else "k_score"
     kernel_names = {"score": score_kernel, "append": "k_append",
-                    "attend": "k_attend_topp" if wl.top_p < 1.0 else "k_attend", "hist": "k_hist",
+                    "attend": "k_attend_topp" if topp else "k_attend_full", "hist": "k_hist",
                     "query": "k_qprep", "merge": "k_merge"}
-    dominant = max((k for k in stage_ms if k in per_launch), key=lambda k: stage_ms[k])
-    ach = per_launch[dominant] / (stage_ms[dominant] / 1e3) / 1e9
+    dominant = max((k for k in stage_ms if k in alg), key=lambda k: stage_ms[k])
+    t_dom = stage_ms[dominant] / 1e3
+    ach = alg[dominant] / t_dom / 1e9
+    variant = args.exact_keys or args.center_keys or args.stochastic_query or args.sketch_dim != D
     roofline = {"bound": "hbm", "kernel": kernel_names[dominant], "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": None if (args.exact_keys or args.center_keys or args.stochastic_query
-                                    or args.sketch_dim != D)
-                else measured_traffic(kernel_names[dominant], wl.name),
-                "algorithmic_bytes_per_launch": per_launch[dominant],
-                "avg_launch_us": round(stage_ms[dominant] * 1e3, 2)}
-    # whole step, algorithmic minimum: every key once, the values (with binary16 keys, also
-    # those keys) of the kept tokens once per KV head (the union over its query heads), and
-    # the appended token
-    if sel_union is not None:
-        kept = value_bytes(Gv) + (2 * D if args.exact_keys else 0)
-        step_alg = per_launch["append"] + key_bytes * tokens_heads + kept * sel_union
+                "traffic": None if variant else measured_traffic(kernel_names[dominant], wl.name),
+                "algorithmic_bytes_per_launch": alg[dominant],
+                "avg_launch_us": round(stage_ms[dominant] * 1e3, 2),
+                "design_bytes_per_launch": design[dominant],
+                "design_frac": round(design[dominant] / t_dom / 1e9 / HBM_PEAK_GBS, 4)}
+    # whole step, algorithmic minimum: every key once, the attended values once per KV head,
+    # the appended tokens, the queries and the outputs
+    qo = 2 * B * Hq * D * 4
+    if topp:
+        step_alg = append_alg + key_bytes * tokens_heads + (vb + (2 * D if exact else 0)) * sel_union + qo
     else:
-        step_alg = per_launch["append"] + (key_bytes + value_bytes(Gv)) * tokens_heads
-    log(f"[bench] dominant {dominant}: {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
+        step_alg = append_alg + (key_bytes + vb) * tokens_heads + qo
+    log(f"[bench] dominant {dominant}: {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak "
+        f"({design[dominant] / t_dom / 1e9:.0f} GB/s counting the design's bytes); whole step "
+        f"{100 * step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS:.1f}% of peak")
+    stage_alg = {k: {"us": round(stage_ms[k] * 1e3, 2), "algorithmic_bytes": alg[k], "design_bytes": design[k],
+                     "frac": round(alg[k] / (stage_ms[k] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                 for k in stage_ms if k in alg}
 
     result = {
         "metric": METRIC, "value": value, "unit": "KV token-heads/s", "n_gpus": 1, "steps": args.steps,
@@ -426,8 +596,10 @@ def main():
                    "sketch_dim": args.sketch_dim},
         "roofline": roofline,
         "step_hbm_frac_algorithmic": round(step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": step_alg,
         "query_head_tokens_per_s": value * (Hq // Hkv),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "stages": stage_alg,
         "step_us_median": round(statistics.median(step_ms) * 1e3, 2),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
     }
@@ -435,7 +607,6 @@ def main():
         result["topp_selected_union_token_kv_heads"] = sel_union
         result["topp_selected_token_query_heads"] = sel_entries
 
-    variant = args.exact_keys or args.center_keys or args.stochastic_query or args.sketch_dim != D
     if variant and not args.no_cpu_baseline:
         log("[cpu] no oracle baseline for the variant modes (the default run has it)")
     elif not args.no_cpu_baseline:

@@ -231,10 +231,13 @@ kvc::CacheView view_of(const kv_cache *c)
     return v;
 }
 
-// Records the stage's start (begin = true) or end event when the caller asked for them.
-void stage_mark(const kv_debug *dbg, int stage, bool begin, hipStream_t s)
+// Stage events, when the caller asked for them: the stage's kernels record them as they
+// begin and end (hipExtLaunchKernel, see kvc::StageTiming).
+void stage_mark(const kv_debug *dbg, int stage, bool begin, hipStream_t)
 {
-    if (dbg && dbg->stage_events) (void)hipEventRecord(dbg->stage_events[2 * stage + (begin ? 0 : 1)], s);
+    if (!dbg || !dbg->stage_events) return;
+    if (begin) kvc::g_stage_timing = {dbg->stage_events[2 * stage], dbg->stage_events[2 * stage + 1]};
+    else kvc::g_stage_timing = {nullptr, nullptr};
 }
 
 template <typename T>
@@ -373,6 +376,9 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
                 float top_p, float *out, const kv_debug *dbg, void *workspace, size_t workspace_bytes,
                 hipStream_t stream)
 {
+    struct TimingGuard {  // no stage timing outlives the call, whatever path it returns by
+        ~TimingGuard() { kvc::g_stage_timing = {nullptr, nullptr}; }
+    } timing_guard;
     int rc = check_cache(c);
     if (rc) return rc;
     rc = check_decode_shapes(B, Hq, c->num_kv_heads, max_seq_len, c->head_dim, top_p);

@@ -166,13 +166,13 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
     if (N == 0) return hipSuccess;
     if (p.rot_kind == 1) {
         const long blocks = (N + 15) / 16;
-        hipLaunchKernelGGL(k_append_hadamard, dim3((unsigned)blocks), dim3(256), 0, s, p, N);
+        KVC_LAUNCH(k_append_hadamard, dim3((unsigned)blocks), dim3(256), s, p, N);
     } else if (N <= 8192) {
-        hipLaunchKernelGGL(k_append_dense_small, dim3((unsigned)N), dim3(256), 0, s, p, N);
+        KVC_LAUNCH(k_append_dense_small, dim3((unsigned)N), dim3(256), s, p, N);
     } else {
         const long tiles = (N + 31) / 32;
         const long blocks = tiles < 2048 ? tiles : 2048;
-        hipLaunchKernelGGL(k_append_dense, dim3((unsigned)blocks), dim3(128), 0, s, p, N);
+        KVC_LAUNCH(k_append_dense, dim3((unsigned)blocks), dim3(128), s, p, N);
     }
     return hipGetLastError();
 }
@@ -344,19 +344,19 @@ __global__ __launch_bounds__(256) void k_hp_update(HpUpdateParams p)
 
 hipError_t launch_hp_update(const HpUpdateParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_hp_update, dim3(p.c.Hkv, p.B), dim3(256), 0, s, p);
+    KVC_LAUNCH(k_hp_update, dim3(p.c.Hkv, p.B), dim3(256), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_tail_append(const TailEditParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_tail_append, dim3(p.B), dim3(256), 0, s, p);
+    KVC_LAUNCH(k_tail_append, dim3(p.B), dim3(256), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_tail_retire(const TailEditParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_tail_retire, dim3(p.B), dim3(256), 0, s, p);
+    KVC_LAUNCH(k_tail_retire, dim3(p.B), dim3(256), s, p);
     return hipGetLastError();
 }
 

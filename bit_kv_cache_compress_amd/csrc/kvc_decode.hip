@@ -21,6 +21,8 @@
 
 namespace kvc {
 
+thread_local StageTiming g_stage_timing = {nullptr, nullptr};
+
 // Result words of the argument checker (k_check), one copy per device.
 __device__ int32_t g_check_flag[4];
 
@@ -1861,8 +1863,8 @@ __global__ __launch_bounds__(256) void k_check(CheckParams p, int32_t *flag)
 template <int GB, int GV>
 void launch_full(const AttendParams &p, dim3 grid, hipStream_t s)
 {
-    if (p.c.kw == 4) hipLaunchKernelGGL((k_attend_full<GB, GV, 4>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((k_attend_full<GB, GV, 2>), grid, dim3(64), 0, s, p);
+    if (p.c.kw == 4) KVC_LAUNCH((k_attend_full<GB, GV, 4>), grid, dim3(64), s, p);
+    else KVC_LAUNCH((k_attend_full<GB, GV, 2>), grid, dim3(64), s, p);
 }
 
 }  // namespace
@@ -1875,7 +1877,7 @@ hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
     const float isd = (float)(1.0 / sqrt((double)kD));
     const long blocks = (long)p.BH * (p.has_tail ? 2 : 1) + p.app_blocks;
     const bool wide = p.has_tail || p.app_blocks > 0;
-    hipLaunchKernelGGL(k_qprep, dim3((unsigned)blocks), dim3(wide ? 256 : 128), 0, s, p, isd);
+    KVC_LAUNCH(k_qprep, dim3((unsigned)blocks), dim3(wide ? 256 : 128), s, p, isd);
     return hipGetLastError();
 }
 
@@ -1887,24 +1889,24 @@ hipError_t launch_score(const ScoreParams &p, hipStream_t s)
     if (!dbg && p.dl && p.g.CH == kTopPChunk) {
         switch (p.g.GB) {
         case 1:
-            if (p.c.kw == 4) hipLaunchKernelGGL((k_score_topp<1, 4>), grid, blk, 0, s, p);
-            else hipLaunchKernelGGL((k_score_topp<1, 2>), grid, blk, 0, s, p);
+            if (p.c.kw == 4) KVC_LAUNCH((k_score_topp<1, 4>), grid, blk, s, p);
+            else KVC_LAUNCH((k_score_topp<1, 2>), grid, blk, s, p);
             break;
         case 2:
-            if (p.c.kw == 4) hipLaunchKernelGGL((k_score_topp<2, 4>), grid, blk, 0, s, p);
-            else hipLaunchKernelGGL((k_score_topp<2, 2>), grid, blk, 0, s, p);
+            if (p.c.kw == 4) KVC_LAUNCH((k_score_topp<2, 4>), grid, blk, s, p);
+            else KVC_LAUNCH((k_score_topp<2, 2>), grid, blk, s, p);
             break;
         default:
-            if (p.c.kw == 4) hipLaunchKernelGGL(k_score_topp_mf<4>, grid, blk, 0, s, p);
-            else hipLaunchKernelGGL(k_score_topp_mf<2>, grid, blk, 0, s, p);
+            if (p.c.kw == 4) KVC_LAUNCH(k_score_topp_mf<4>, grid, blk, s, p);
+            else KVC_LAUNCH(k_score_topp_mf<2>, grid, blk, s, p);
             break;
         }
     } else {
         // debug scores: the Top-p chunks, or the larger chunks of a full-softmax decode
         switch (p.g.GB) {
-        case 1: hipLaunchKernelGGL((k_score<1, true, 8192>), grid, blk, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((k_score<2, true, 4096>), grid, blk, 0, s, p); break;
-        default: hipLaunchKernelGGL((k_score<4, true, 2048>), grid, blk, 0, s, p); break;
+        case 1: KVC_LAUNCH((k_score<1, true, 8192>), grid, blk, s, p); break;
+        case 2: KVC_LAUNCH((k_score<2, true, 4096>), grid, blk, s, p); break;
+        default: KVC_LAUNCH((k_score<4, true, 2048>), grid, blk, s, p); break;
         }
     }
     return hipGetLastError();
@@ -1912,26 +1914,26 @@ hipError_t launch_score(const ScoreParams &p, hipStream_t s)
 
 hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_bin_scores, dim3(p.g.NC, p.g.Hq, p.g.B), dim3(kBlock), 0, s, p);
+    KVC_LAUNCH(k_bin_scores, dim3(p.g.NC, p.g.Hq, p.g.B), dim3(kBlock), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_hist(const HistParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kHistThreads), 0, s, p);
+    KVC_LAUNCH(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kHistThreads), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_thresh, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
+    KVC_LAUNCH(k_thresh, dim3(p.g.Hq, p.g.B), dim3(1024), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectParams &p, hipStream_t s)
 {
     const dim3 grid(p.g.NC, p.g.Hq, p.g.B);
-    hipLaunchKernelGGL(k_sel_count, grid, dim3(kBlock), 0, s, p);
+    KVC_LAUNCH(k_sel_count, grid, dim3(kBlock), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sel_write, grid, dim3(kBlock), 0, s, p);
+    KVC_LAUNCH(k_sel_write, grid, dim3(kBlock), s, p);
     return hipGetLastError();
 }
 
@@ -1943,11 +1945,11 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
         const bool w4 = p.c.kw == 4;
         if (p.c.kf16) {
-            if (w4) hipLaunchKernelGGL((k_attend_topp<true, 4>), grid, dim3(64 * kAttendWaves), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_topp<true, 2>), grid, dim3(64 * kAttendWaves), 0, s, p);
+            if (w4) KVC_LAUNCH((k_attend_topp<true, 4>), grid, dim3(64 * kAttendWaves), s, p);
+            else KVC_LAUNCH((k_attend_topp<true, 2>), grid, dim3(64 * kAttendWaves), s, p);
         } else {
-            if (w4) hipLaunchKernelGGL((k_attend_topp<false, 4>), grid, dim3(64 * kAttendWaves), 0, s, p);
-            else hipLaunchKernelGGL((k_attend_topp<false, 2>), grid, dim3(64 * kAttendWaves), 0, s, p);
+            if (w4) KVC_LAUNCH((k_attend_topp<false, 4>), grid, dim3(64 * kAttendWaves), s, p);
+            else KVC_LAUNCH((k_attend_topp<false, 2>), grid, dim3(64 * kAttendWaves), s, p);
         }
     } else {
         // one wave per (chunk, KV-head group, sequence)
@@ -2020,8 +2022,8 @@ hipError_t launch_check(const CheckParams &p, int32_t *flag_host, hipStream_t s)
 
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)
 {
-    if (p.has_mass) hipLaunchKernelGGL(k_merge<true>, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
-    else hipLaunchKernelGGL(k_merge<false>, dim3(p.g.Hq, p.g.B), dim3(1024), 0, s, p);
+    if (p.has_mass) KVC_LAUNCH(k_merge<true>, dim3(p.g.Hq, p.g.B), dim3(1024), s, p);
+    else KVC_LAUNCH(k_merge<false>, dim3(p.g.Hq, p.g.B), dim3(1024), s, p);
     return hipGetLastError();
 }
 

@@ -1,9 +1,30 @@
 // Kernel parameter blocks and launchers of libkvcompress (host <-> kernels interface).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace kvc {
+
+// Stage timing (kv_debug.stage_events): while set, the next kernel this thread launches
+// records `start` when it begins, and every kernel it launches records `stop` when it ends
+// (hipExtLaunchKernel), so the pair brackets a stage's kernels as a kernel trace does, without
+// the dispatch latency of event packets between them.
+struct StageTiming {
+    hipEvent_t start, stop;
+};
+extern thread_local StageTiming g_stage_timing;
+
+#define KVC_LAUNCH(kern, grid, block, s, ...)                                                               \
+    do {                                                                                                  \
+        if (::kvc::g_stage_timing.stop) {                                                                 \
+            hipExtLaunchKernelGGL(kern, grid, block, 0, s, ::kvc::g_stage_timing.start,                   \
+                                  ::kvc::g_stage_timing.stop, 0, __VA_ARGS__);                            \
+            ::kvc::g_stage_timing.start = nullptr;                                                        \
+        } else {                                                                                          \
+            hipLaunchKernelGGL(kern, grid, block, 0, s, __VA_ARGS__);                                     \
+        }                                                                                                 \
+    } while (0)
 
 // Tokens per Top-p score chunk (one wave of the score kernel, 8 tokens per lane).
 constexpr int kTopPChunk = 512;
