@@ -146,8 +146,8 @@ int check_decode_shapes(int B, int Hq, int Hkv, int max_seq_len, int head_dim, f
     const long limit = (long)chunk_cap(top_p < 1.0f) * kvc::kMaxChunks;  // merge weights fit in LDS
     if (max_seq_len > limit)
         return fail(KV_ERR_UNSUPPORTED, "max_seq_len %d above %ld", max_seq_len, limit);
-    if (top_p < 1.0f && (long)B * Hq >= (1L << 24))  // the attention pass's dispatch-order entries
-        return fail(KV_ERR_UNSUPPORTED, "B * Hq = %ld: Top-p supports fewer than 2^24 query heads", (long)B * Hq);
+    if (B > 65535 || Hq > 65535)  // grid dimensions: sequences in z, query heads (or KV groups) in y
+        return fail(KV_ERR_UNSUPPORTED, "B = %d, Hq = %d: at most 65535 sequences and query heads", B, Hq);
     return KV_OK;
 }
 
@@ -532,11 +532,6 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
 
     kvc::AttendParams ap;
     ap.g = pl.g;
-    if (pl.topp) {
-        // Top-p keeps a different small set of tokens per query head: one head per block
-        ap.g.GB = 1;
-        ap.g.nsub = ap.g.G;
-    }
     ap.c = cv;
     ap.q = q;
     ap.qnib = qnib;
@@ -546,6 +541,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     ap.lmax = sp.lmax;
     ap.sel = pl.topp ? at<int32_t>(workspace, pl.off_sel) : nullptr;
     ap.order = pl.topp ? at<int32_t>(workspace, pl.off_order) : nullptr;
+    ap.order_ctr = pl.topp ? at<int32_t>(workspace, pl.off_octr) : nullptr;
     ap.pm = at<float>(workspace, pl.off_pm);
     ap.pl = at<float>(workspace, pl.off_pl);
     ap.po = at<float>(workspace, pl.off_po);

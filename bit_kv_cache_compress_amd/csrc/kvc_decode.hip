@@ -1270,22 +1270,45 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
     const DecodeGeom &g = p.g;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar
-    // the head of this dispatch rank and its span (dense heads first; the threshold pass
-    // wrote the order)
-    const int code = p.order[blockIdx.z * g.Hq + blockIdx.y];
-    int bhr = code & 0xFFFFFF;
-    const int ls = (code >> 24) & 3;
-    if (bhr >= g.B * g.Hq) bhr = blockIdx.z * g.Hq + blockIdx.y;
+    int bhr, ls, c0, first;
+    if (p.order_ctr[0] == g.B * g.Hq) {
+        // every head covers its chunks one by one (each keeps many tokens): the blocks are
+        // renumbered so that a block holds the GB query heads of one KV head for NW / GB
+        // consecutive chunks (wave w: head w mod GB, chunk w / GB).  Those waves run on one
+        // compute unit at the same time, so a record that several of the heads keep crosses
+        // HBM once and reaches the others from the caches.
+        const int GB = g.GB, cpb = NW / GB;
+        const int nxf = (g.NCA + cpb - 1) / cpb;
+        const int L0 = (int)blockIdx.x + (int)gridDim.x * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
+        const int grp = L0 / nxf, xf = L0 - grp * nxf;
+        const int ngrp = g.B * g.Hkv * g.nsub;
+        if (grp >= ngrp) return;
+        const int bq = grp / (g.Hkv * g.nsub);
+        int kvg, hq0;
+        block_heads(g, grp - bq * g.Hkv * g.nsub, kvg, hq0);
+        bhr = bq * g.Hq + hq0 + (wave & (GB - 1));
+        ls = 0;
+        first = wave;
+        c0 = xf * cpb + wave / GB;
+    } else {
+        // the head of this dispatch rank and its span (dense heads first; the threshold pass
+        // wrote the order)
+        const int code = p.order[blockIdx.z * g.Hq + blockIdx.y];
+        bhr = code & 0xFFFFFF;
+        ls = (code >> 24) & 3;
+        if (bhr >= g.B * g.Hq) bhr = blockIdx.z * g.Hq + blockIdx.y;
+        // the block's waves cover chunks NW bx .. + NW - 1, in groups of span = 2^ls; one
+        // wave per group works, the one whose index within the group rotates with the block,
+        // so that the working waves spread over the SIMDs; the others have nothing to do
+        const int sp = 1 << ls;
+        first = wave & ~(sp - 1);  // first wave (and slice) of this wave's group
+        if (wave - first != ((int)blockIdx.x & (sp - 1))) return;
+        c0 = (int)blockIdx.x * NW + first;  // first chunk of the span
+    }
     const int b = bhr / g.Hq, h = bhr - b * g.Hq;
     const int kvh = h / g.G;
     const size_t bh = (size_t)bhr;
-    // the block's waves cover chunks NW bx .. + NW - 1, in groups of span = 2^ls; one wave
-    // per group works, the one whose index within the group rotates with the block, so that
-    // the working waves spread over the SIMDs; the others have nothing to do
     const int span = 1 << ls;
-    const int first = wave & ~(span - 1);  // first wave (and slice) of this wave's group
-    if (wave - first != ((int)blockIdx.x & (span - 1))) return;
-    const int c0 = (int)blockIdx.x * NW + first;  // first chunk of the span
     if (c0 >= g.NCA) return;
     const int t0 = c0 * CHA;
     uint16_t *list = lst + first * SL;

@@ -200,6 +200,7 @@ struct AttendParams {
     const int32_t *lmax;
     const int32_t *sel;
     const int32_t *order;  // [B*Hq] head (b * Hq + h) of each dispatch rank
+    const int32_t *order_ctr;  // [2]: order_ctr[0] heads were classed dense (attention chunk by chunk)
     // partial results per (b, h, chunk)
     float *pm;             // [B*Hq][NCA] max score of the chunk's attended tokens
     float *pl;             // [B*Hq][NCA] sum of weights

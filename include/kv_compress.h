@@ -192,7 +192,7 @@ int kv_compress_append(const kv_cache *c, int32_t dtype, const void *k, const vo
  *               softmax renormalised over the selected tokens.  <= 0 or NaN is an error.
  *               Under Top-p with c->keys_f16 set, the softmax over the selected tokens uses
  *               the exact scores <q, k> of their binary16 keys instead of the proxy scores.
- *               Top-p needs B * Hq < 2^24 (else KV_ERR_UNSUPPORTED).
+ *               B and Hq must be at most 65535 (else KV_ERR_UNSUPPORTED).
  *   out         float [B][Hq][D]
  *   dbg         [host] nullable, see kv_debug
  *   workspace   device scratch of at least kv_decode_workspace_bytes(...) bytes; its

@@ -75,7 +75,8 @@ def test_bad_cache_descriptor(kw, code):
     (dict(top_p=0.0), L.KV_ERR_ARG),
     (dict(top_p=-0.5), L.KV_ERR_ARG),
     (dict(top_p=float("nan")), L.KV_ERR_ARG),
-    (dict(B=1 << 19, Hq=32, top_p=0.9), L.KV_ERR_UNSUPPORTED),  # 2^24 query heads under Top-p
+    (dict(B=1 << 19, Hq=32, top_p=0.9), L.KV_ERR_UNSUPPORTED),  # more sequences than the grid holds
+    (dict(B=70000, Hq=32, top_p=1.0), L.KV_ERR_UNSUPPORTED),
     (dict(q=None), L.KV_ERR_ARG),
     (dict(out=None), L.KV_ERR_ARG),
 ])
