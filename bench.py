@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--append", action="store_true",
                     help="time the prefill append of workload 4 (32768 tokens x 32 KV heads, randomized "
                          "Hadamard rotation) instead of a decode step: token-heads compressed/s")
+    ap.add_argument("--append-rotation", choices=("hadamard", "dense"), default="hadamard",
+                    help="with --append: the rotation (dense: a seeded Haar rotation in binary16)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--lazy", action="store_true",
                     help="lazy updates: new tokens go to a binary16 tail, whole pages are compressed on a "
@@ -235,16 +237,18 @@ def run_append(args):
     import workloads as W
 
     wl = W.CONFIGS[4]
+    if args.append_rotation == "dense":
+        wl = wl.scaled(rot="dense")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     D, P, Gv = wl.D, wl.P, wl.Gv
     n_new, Ha = wl.append_tokens, wl.append_heads
-    name = f"hadamard-append{n_new // 1024}k-{Ha}kvh-f16"
+    name = f"{wl.rot}-append{n_new // 1024}k-{Ha}kvh-f16"
     log(f"[bench] append workload {name}: {n_new} tokens x {Ha} KV heads, rotation {wl.rot}, value group {Gv}")
     K, V, _ = W.draw_device(wl, dev, L=n_new, Hkv=Ha)
     pt_np, npages = W.page_layout(wl.scaled(Hkv=Ha), np.array([n_new], np.int32))
-    kind, signs = W.draw_rotation(wl)
-    cache = kvc.KVCache(npages, Ha, signs, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
+    kind, rot = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, Ha, rot, rot_kind=kind, page_size=P, value_group=Gv, device=dev)
     pt = torch.from_numpy(pt_np).to(dev)
     start = torch.zeros(1, dtype=torch.int32, device=dev)
     flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
@@ -280,7 +284,7 @@ def run_append(args):
     key_bytes, vb = 20, value_bytes(Gv)
     alg = th * (2 * D * 2 + key_bytes + vb)
     ach = alg / (ms / 1e3) / 1e9
-    kern = "k_append_hadamard" if kind != "dense" else "k_append_dense"
+    kern = "k_append_hadamard" if kind != "dense" else "k_append_mfma<true>"
     log(f"[bench] append {ms * 1e3:.1f} us (median {statistics.median(step_ms) * 1e3:.1f}); {value:.3e} "
         f"token-heads/s; {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
     result = {
@@ -297,7 +301,7 @@ def run_append(args):
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], result["parity_sample"] = cpu_append_baseline(args, wl, K, V, cache, pt_np, signs)
+        result["cpu_baseline"], result["parity_sample"] = cpu_append_baseline(args, wl, K, V, cache, pt_np, rot)
     print(json.dumps(result), flush=True)
 
 
@@ -312,7 +316,8 @@ def cpu_append_baseline(args, wl, K, V, cache, pt_np, signs):
     Ha = K.shape[2]
     cores = len(os.sched_getaffinity(0))
     n = 2048  # tokens per head in the sample
-    orot = oracle.Rotation(oracle.ROT_HADAMARD, D, signs=signs)
+    orot = (oracle.Rotation(oracle.ROT_HADAMARD, D, signs=signs) if wl.rot == "hadamard"
+            else oracle.Rotation(oracle.ROT_DENSE, D, R16=signs))
     k = K[0, :n].float().cpu().numpy()
     v = V[0, :n].float().cpu().numpy()
     units = [(h, t0) for h in range(Ha) for t0 in range(0, n, 256)]

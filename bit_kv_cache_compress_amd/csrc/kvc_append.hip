@@ -16,7 +16,7 @@ namespace {
 typedef double double4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------------------
-// Randomized Hadamard rotation (append_hadamard_block): 16 token-heads per 256-thread block.
+// Randomized Hadamard rotation (append_hadamard_block): 64 token-heads per 256-thread block.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_append_hadamard(AppendParams p, long N)
 {
@@ -142,6 +142,255 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
 }
 
 // ---------------------------------------------------------------------------------------
+// Rotation on the matrix cores, for binary16 keys without key centers: 16 token-heads per
+// wave, k' = R k as v_mfma_f32_16x16x32_f16 with the keys as A (16 tokens x 128 dims) and the
+// rotation as B (B[j][o] = R[o][j]; for the randomized Hadamard rotation H[o][j] sigma_j = +-1,
+// and k' = (H sigma k) / sqrt(D) has the signs of the product).  Binary16 products are exact
+// in binary32, so the only error of an output is that of its binary32 sums: at most
+// gamma_128 = 128 u / (1 - 128 u) < 7.7e-6 (u = 2^-24) times sum_j |R_oj k_j|, whatever order
+// the matrix core adds in.  A coordinate whose |k'_o| exceeds 1e-5 times that sum has the
+// sign of the exact product; the others (rare) take the exact sign from a binary64 sum of the
+// 128 products over the wave's lanes.  sum_j |R_oj k_j| is |k|_1 for the Hadamard rotation,
+// and the product of |R| and |k| on the matrix cores for the dense one.
+// The token-heads are taken head by head (n = (b Hkv + h) n_new + t), so that a wave's 16
+// records are consecutive slots of a page, written whole.  sum |k'| (for the correction) is
+// the binary32 sum of the matrix-core outputs, within 1e-5 relative of the binary64 one.
+// ---------------------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBS = kD + 8;  // LDS row stride of the rotation (halves): 16-byte aligned rows
+
+__device__ __forceinline__ half8_t as_half8(uint4 v)
+{
+    half8_t h;
+    __builtin_memcpy(&h, &v, 16);
+    return h;
+}
+
+// v (64-bit) of lane src
+__device__ __forceinline__ size_t from_lane64(size_t v, int src)
+{
+    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)v);
+    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(v >> 32));
+    return ((size_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ double xor_lane_d(double v, int m)
+{
+    const long long x = __double_as_longlong(v);
+    const int lo = xor_lane((int)x, m), hi = xor_lane((int)(x >> 32), m);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Input row and slot of token-head n in head-major order.
+__device__ __forceinline__ void token_at(const AppendParams &p, uint32_t n, size_t &row, size_t &slot)
+{
+    const uint32_t nn = (uint32_t)p.n_new, hk = (uint32_t)p.c.Hkv;
+    const uint32_t t = n % nn, bh = n / nn;
+    const uint32_t h = bh % hk, b = bh / hk;
+    row = ((size_t)(b * nn + t) * hk + h) * kD;
+    const int pos = p.start_pos[b] + (int)t;
+    const int page = p.page_table[(size_t)b * p.max_pages + (pos >> p.c.logP)];
+    slot = ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
+}
+
+template <bool DENSE>
+__global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
+{
+    __shared__ __align__(16) uint16_t Bt[kD * kBS];  // Bt[o][j] = B[j][o]
+    __shared__ uint64_t sgn_s[4][32];                // per wave: sign ballots [4 nt + i]
+    __shared__ uint64_t unc_s[4][32];                // per wave: uncertain ballots
+    __shared__ float sab_s[4][16];                   // per wave: sum |k'| of the tile's tokens
+    __shared__ double ss_s[4][16];                   // per wave: |k|^2 of the tile's tokens
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int c = tid; c < kD * kD / 8; c += 256) {
+        const int o = c >> 4, q = c & 15;  // row o, halves 8 q .. 8 q + 7
+        uint4 v;
+        if constexpr (DENSE) {
+            v = reinterpret_cast<const uint4 *>(p.rot)[c];
+        } else {
+            const uint32_t sg = reinterpret_cast<const uint32_t *>(p.rot)[q >> 2];
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j0 = 8 * q + 2 * e, j1 = j0 + 1;
+                const uint32_t n0 = (__builtin_popcount(o & j0) + (sg >> (j0 & 31))) & 1u;
+                const uint32_t n1 = (__builtin_popcount(o & j1) + (sg >> (j1 & 31))) & 1u;
+                w[e] = (0x3C00u | (n0 << 15)) | ((0x3C00u | (n1 << 15)) << 16);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        *reinterpret_cast<uint4 *>(&Bt[o * kBS + 8 * q]) = v;
+    }
+    __syncthreads();
+    const uint16_t *K = reinterpret_cast<const uint16_t *>(p.k);
+    const uint16_t *V = reinterpret_cast<const uint16_t *>(p.v);
+    const int m = lane & 15, kb = lane >> 4;  // A layout: token m, dims 8 kb + 32 ks
+    const int tv = lane >> 2, jv = lane & 3;  // value layout: token tv, dims 32 jv .. + 31
+    const uint32_t ntiles = ((uint32_t)N + 15u) / 16u;
+    for (uint32_t tile = blockIdx.x * 4u + (uint32_t)wave; tile < ntiles; tile += gridDim.x * 4u) {
+        const int nvalid = min(16, N - (int)(tile * 16u));
+        size_t row = 0, slot = 0;
+        if (lane < 16) token_at(p, tile * 16u + (uint32_t)min(lane, nvalid - 1), row, slot);
+        const size_t rowA = from_lane64(row, m), rowV = from_lane64(row, tv);
+        const size_t slotA = from_lane64(slot, m), slotV = from_lane64(slot, tv);
+        uint4 a[4], vr[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const uint4 *>(K + rowA + 32 * ks + 8 * kb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vr[q] = *reinterpret_cast<const uint4 *>(V + rowV + 32 * jv + 8 * q);
+        if (p.c.kf16 && m < nvalid) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4 *>(p.c.kf16 + slotA * kD + 32 * ks + 8 * kb) = a[ks];
+        }
+        // |k|_1 (binary32) and |k|^2 (binary64) of token m: this lane's 32 dims, then lanes
+        // m, m + 16, m + 32, m + 48
+        float l1 = 0.0f;
+        double ss = 0.0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t w[4] = {a[ks].x, a[ks].y, a[ks].z, a[ks].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                l1 += fabsf(x);
+                ss = fma((double)x, (double)x, ss);
+            }
+        }
+        l1 += xor_lane(l1, 16);
+        l1 += xor_lane(l1, 32);
+        ss += xor_lane_d(ss, 16);
+        ss += xor_lane_d(ss, 32);
+        if (kb == 0) ss_s[wave][m] = ss;
+        // the products: acc[nt] holds out dim 16 nt + m of tokens 4 kb + i in element i
+        f32x4_t acc[8], aab[DENSE ? 8 : 1];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            acc[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (DENSE) aab[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        uint4 aabs[DENSE ? 4 : 1];
+        if constexpr (DENSE) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                aabs[ks] = make_uint4(a[ks].x & 0x7FFF7FFFu, a[ks].y & 0x7FFF7FFFu, a[ks].z & 0x7FFF7FFFu,
+                                      a[ks].w & 0x7FFF7FFFu);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            uint4 bw[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                bw[ks] = *reinterpret_cast<const uint4 *>(&Bt[(16 * nt + m) * kBS + 32 * ks + 8 * kb]);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ks]), as_half8(bw[ks]), acc[nt], 0, 0, 0);
+                if constexpr (DENSE) {
+                    const uint4 babs = make_uint4(bw[ks].x & 0x7FFF7FFFu, bw[ks].y & 0x7FFF7FFFu,
+                                                  bw[ks].z & 0x7FFF7FFFu, bw[ks].w & 0x7FFF7FFFu);
+                    aab[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(aabs[ks]), as_half8(babs), aab[nt], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one output tile's operands at a time
+        }
+        // signs, certified against the bound; sum |k'| over the sketch's dims
+        float bnd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bnd[i] = 1e-5f * __int_as_float(__builtin_amdgcn_ds_bpermute((4 * kb + i) << 2, __float_as_int(l1)));
+        // the 32 sign ballots (and, when some coordinate is uncertain, the 32 uncertainty
+        // ballots) go to LDS from lanes 0..31, ballot k = 4 nt + i in lane k
+        uint64_t any = 0;
+        float sa[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        int sg_lo = 0, sg_hi = 0, un_lo = 0, un_hi = 0;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = acc[nt][i];
+                const float b = DENSE ? 1e-5f * aab[DENSE ? nt : 0][i] : bnd[i];
+                const uint64_t sg = __builtin_amdgcn_ballot_w64(!(v < 0.0f));
+                const uint64_t un = __builtin_amdgcn_ballot_w64(!(fabsf(v) > b));
+                const bool mine = lane == 4 * nt + i;
+                sg_lo = mine ? (int)(uint32_t)sg : sg_lo;
+                sg_hi = mine ? (int)(uint32_t)(sg >> 32) : sg_hi;
+                un_lo = mine ? (int)(uint32_t)un : un_lo;
+                un_hi = mine ? (int)(uint32_t)(un >> 32) : un_hi;
+                any |= un;
+                if (nt < 2 * p.c.kw) sa[i] += fabsf(v);
+            }
+        }
+        if (lane < 32) {
+            sgn_s[wave][lane] = ((uint64_t)(uint32_t)sg_hi << 32) | (uint32_t)sg_lo;
+            if (any) unc_s[wave][lane] = ((uint64_t)(uint32_t)un_hi << 32) | (uint32_t)un_lo;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) sa[i] += xor_lane(sa[i], o);
+            if (m == 0) sab_s[wave][4 * kb + i] = sa[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (any) {
+            // exact signs of the uncertain coordinates: lane l adds the products of dims
+            // 2 l, 2 l + 1 in binary64 (exact for binary16 operands), summed over the wave
+            for (int k = 0; k < 32; ++k) {
+                uint64_t u = unc_s[wave][k];
+                const int nt = k >> 2, i = k & 3;
+                while (u) {
+                    const int bit = __builtin_ctzll(u);
+                    u &= u - 1;
+                    const int tok = 4 * (bit >> 4) + i, o = 16 * nt + (bit & 15);
+                    const size_t r = from_lane64(row, tok);
+                    const uint32_t xw = *reinterpret_cast<const uint32_t *>(K + r + 2 * lane);
+                    const uint32_t bw = *reinterpret_cast<const uint32_t *>(&Bt[o * kBS + 2 * lane]);
+                    double s = (double)half_bits_to_float(xw & 0xFFFFu) * (double)half_bits_to_float(bw & 0xFFFFu);
+                    s += (double)half_bits_to_float(xw >> 16) * (double)half_bits_to_float(bw >> 16);
+#pragma unroll
+                    for (int q = 32; q > 0; q >>= 1) s += xor_lane_d(s, q);
+                    if (lane == 0) {
+                        const uint64_t b1 = 1ull << bit;
+                        sgn_s[wave][k] = (s < 0.0) ? (sgn_s[wave][k] & ~b1) : (sgn_s[wave][k] | b1);
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        // key record of token tv: word jv (dims 32 jv .. 32 jv + 31: out tiles 2 jv, 2 jv + 1),
+        // and the norm/correction word
+        if (tv < nvalid) {
+            const int g = tv >> 2, i = tv & 3;
+            const uint32_t lo = (uint32_t)(sgn_s[wave][4 * (2 * jv) + i] >> (16 * g)) & 0xFFFFu;
+            const uint32_t hi = (uint32_t)(sgn_s[wave][4 * (2 * jv + 1) + i] >> (16 * g)) & 0xFFFFu;
+            uint32_t *kr = key_rec(p.c, slotV);
+            if (jv < p.c.kw) kr[jv] = lo | (hi << 16);
+            if (jv == 0) {
+                const double sabs = (double)sab_s[wave][tv] / (DENSE ? 1.0 : sqrt((double)kD));
+                kr[p.c.kw] = norm_corr_word(ss_s[wave][tv], sabs, p.c.sk);
+            }
+            float x[32];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w[4] = {vr[q].x, vr[q].y, vr[q].z, vr[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[8 * q + 2 * e] = half_bits_to_float(w[e] & 0xFFFFu);
+                    x[8 * q + 2 * e + 1] = half_bits_to_float(w[e] >> 16);
+                }
+            }
+            encode_values32(x, jv, p.c.Gv, val_rec(p.c, slotV));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the LDS slices are rewritten
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Dense rotation for few token-heads (append_small_block): one 256-thread block per
 // token-head.
 // ---------------------------------------------------------------------------------------
@@ -156,7 +405,7 @@ long fused_append_blocks(const AppendParams &p)
 {
     const long N = (long)p.B * p.n_new * p.c.Hkv;
     if (N == 0) return 0;
-    if (p.rot_kind == 1) return (N + 15) / 16;
+    if (p.rot_kind == 1) return (N + 63) / 64;
     return N <= 8192 ? N : 0;
 }
 
@@ -164,8 +413,16 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
 {
     const long N = (long)p.B * p.n_new * p.c.Hkv;
     if (N == 0) return hipSuccess;
-    if (p.rot_kind == 1) {
-        const long blocks = (N + 15) / 16;
+    // dense rotation, binary16 keys without centers: the rotation on the matrix cores (16
+    // token-heads per wave); the randomized Hadamard rotation's butterflies cost less than its
+    // 128 x 128 product
+    const bool mfma = p.rot_kind == 0 && p.dtype == 0 && !p.c.kc && N > 8192 && N < (1L << 31);
+    if (mfma) {
+        const long mblocks = ((N + 15) / 16 + 3) / 4;
+        const unsigned blocks = (unsigned)(mblocks < 1024 ? mblocks : 1024);
+        KVC_LAUNCH(k_append_mfma<true>, dim3(blocks), dim3(256), s, p, (int)N);
+    } else if (p.rot_kind == 1) {
+        const long blocks = (N + 63) / 64;
         KVC_LAUNCH(k_append_hadamard, dim3((unsigned)blocks), dim3(256), s, p, N);
     } else if (N <= 8192) {
         KVC_LAUNCH(k_append_dense_small, dim3((unsigned)N), dim3(256), s, p, N);

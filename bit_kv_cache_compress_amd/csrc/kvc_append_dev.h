@@ -41,12 +41,51 @@ __device__ __forceinline__ size_t slot_of(const AppendParams &p, long n)
     return ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
 }
 
+// Codes c_e = clamp(rint((x_e - zf) / sf), 0, 15) of NE elements (sf != 0), with the quotient
+// correctly rounded as an IEEE binary32 division gives it, packed 8 to a word (element e in
+// nibble e mod 8 of word e / 8).  The quotient is first taken as (x - zf) * rcp(sf), within a
+// few ulp of the correctly rounded one; rint of the two can only differ when the approximation
+// lies within 2^-16 of a half-integer (an ulp near 16 is 2^-20), and then the elements take the
+// IEEE division.  x - zf is the binary32 difference either way.  Two codes are packed as one
+// float c_even + 16 c_odd (exact), converted to an integer once.
+template <int NE>
+__device__ __forceinline__ void value_codes(const float (&x)[NE], float zf, float sf, uint32_t (&w)[NE / 8])
+{
+    const float r = __builtin_amdgcn_rcpf(sf);
+    bool near = false;
+#pragma unroll
+    for (int q = 0; q < NE / 8; ++q) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float q0 = (x[8 * q + e] - zf) * r, q1 = (x[8 * q + e + 1] - zf) * r;
+            const float t0 = rintf(q0), t1 = rintf(q1);
+            near |= (fabsf(fabsf(q0 - t0) - 0.5f) <= 0x1p-16f) | (fabsf(fabsf(q1 - t1) - 0.5f) <= 0x1p-16f);
+            const float pair = fmaf(16.0f, __builtin_amdgcn_fmed3f(t1, 0.0f, 15.0f), __builtin_amdgcn_fmed3f(t0, 0.0f, 15.0f));
+            word |= (uint32_t)pair << (4 * e);
+        }
+        w[q] = word;
+    }
+    if (near) {
+#pragma unroll
+        for (int q = 0; q < NE / 8; ++q) {
+            uint32_t word = 0u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = rintf((x[8 * q + e] - zf) / sf);
+                word |= (uint32_t)fminf(fmaxf(t, 0.0f), 15.0f) << (4 * e);
+            }
+            w[q] = word;
+        }
+    }
+}
+
 // Value encode of one token-head by 16 lanes (lane i holds dims 8i..8i+7) into its record:
 //   scale = fp16((max - min) / 15), zero = fp16(min) per group of Gv dims (binary32 ops),
 //   code  = clamp(rint((x - zero) / scale), 0, 15), 0 when scale == 0;
 //   byte m of the 64 code bytes holds dim 2m in its low nibble, dim 2m+1 in its high nibble;
 //   the scale/zero words follow the codes.
-__device__ __forceinline__ void encode_values(const float x[8], int i, int Gv, uint8_t *rec)
+__device__ __forceinline__ void encode_values(const float (&x)[8], int i, int Gv, uint8_t *rec)
 {
     uint8_t *codes = rec;
     uint32_t *sz = reinterpret_cast<uint32_t *>(rec + kD / 2);
@@ -67,18 +106,9 @@ __device__ __forceinline__ void encode_values(const float x[8], int i, int Gv, u
     const uint32_t z16 = float_to_half_bits(mn);
     const float sf = half_bits_to_float(s16);
     const float zf = half_bits_to_float(z16);
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        int c = 0;
-        if (sf != 0.0f) {
-            float t = rintf((x[e] - zf) / sf);
-            t = fminf(fmaxf(t, 0.0f), 15.0f);
-            c = (int)t;
-        }
-        word |= (uint32_t)c << (4 * e);
-    }
-    reinterpret_cast<uint32_t *>(codes)[i] = word;
+    uint32_t word[1] = {0u};
+    if (sf != 0.0f) value_codes<8>(x, zf, sf, word);
+    reinterpret_cast<uint32_t *>(codes)[i] = word[0];
     if ((i & (gl - 1)) == 0) sz[(8 * i) / Gv] = s16 | (z16 << 16);
 }
 
@@ -122,65 +152,149 @@ __device__ __forceinline__ uint32_t norm_corr_word(double ss, double sabs_rot, i
 
 // ---------------------------------------------------------------------------------------
 // Randomized Hadamard rotation: k' = H diag(sigma) k / sqrt(D), in binary64 butterflies.
-// 16 lanes per token-head, 16 token-heads per 256-thread block.
+// 4 lanes per token-head (lane j holds dims 32 j .. 32 j + 31), 64 token-heads per 256-thread
+// block.  The token-heads are taken head by head: n = (b * Hkv + h) * n_new + t, so that the
+// 16 token-heads of a wave are consecutive tokens of one head, whose records are consecutive
+// slots of a page: every record is written whole, by full 16-byte stores where it allows.
 // ---------------------------------------------------------------------------------------
+// v of lane (this lane XOR 1) and (this lane XOR 2) within the quad (DPP quad_perm), for a
+// binary64 value.
+__device__ __forceinline__ double quad_xor1(double v)
+{
+    const long long x = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(x >> 32), 0xB1, 0xF, 0xF, true);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double quad_xor2(double v)
+{
+    const long long x = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(x >> 32), 0x4E, 0xF, 0xF, true);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ float quad_xor1f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// Value encode of one token-head by 4 lanes (lane j holds dims 32 j .. 32 j + 31), with the
+// arithmetic of encode_values: per group of Gv dims, scale = fp16((max - min) / 15) and
+// zero = fp16(min) (binary32 ops), code = clamp(rint((x - zero) / scale), 0, 15) (0 when
+// scale == 0); lane j writes bytes 16 j .. 16 j + 15 of the codes and its group's word.
+__device__ __forceinline__ void encode_values32(const float (&x)[32], int j, int Gv, uint8_t *rec)
+{
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+    }
+    if (Gv == 64) {  // two lanes per group
+        mn = fminf(mn, quad_xor1f(mn));
+        mx = fmaxf(mx, quad_xor1f(mx));
+    }
+    const float step = (mx - mn) / 15.0f;
+    const uint32_t s16 = float_to_half_bits(step);
+    const uint32_t z16 = float_to_half_bits(mn);
+    const float sf = half_bits_to_float(s16);
+    const float zf = half_bits_to_float(z16);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (sf != 0.0f) value_codes<32>(x, zf, sf, w);
+    __builtin_memcpy(rec + 16 * j, w, 16);  // 16-byte aligned for Gv 32, 8-byte for Gv 64
+    if (Gv == 32 || (j & 1) == 0) reinterpret_cast<uint32_t *>(rec + kD / 2)[(32 * j) / Gv] = s16 | (z16 << 16);
+}
+
 __device__ __forceinline__ void append_hadamard_block(const AppendParams &p, long N, long blk)
 {
-    const int i = threadIdx.x & 15;
-    const long n = blk * 16 + (threadIdx.x >> 4);
-    if (n >= N) return;  // whole 16-lane groups exit together
-    const size_t row = (size_t)n * kD + 8 * i;
-    float xk[8], xv[8];
-    load8(p.k, p.dtype, row, xk);
-    load8(p.v, p.dtype, row, xv);
-    const size_t slot = slot_of(p, n);
-    if (p.c.kf16) store_key16(p.c, slot, i, xk);
-    center8(p.c, (int)(n % p.c.Hkv), i, xk);
-
-    // sigma, then the 7 butterfly levels (h = 1, 2, 4 inside the lane, 8..64 across lanes)
-    const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[i >> 2];
-    double y[8];
+    const int j = threadIdx.x & 3;
+    const long n = blk * 64 + (threadIdx.x >> 2);
+    if (n >= N) return;  // whole quads exit together: the DPP partners are in the quad
+    const int t = (int)(n % p.n_new);
+    const long bh = n / p.n_new;
+    const int h = (int)(bh % p.c.Hkv), b = (int)(bh / p.c.Hkv);
+    const size_t row = ((size_t)((long)b * p.n_new + t) * p.c.Hkv + h) * kD + 32 * j;
+    const int pos = p.start_pos[b] + t;
+    const int page = p.page_table[(size_t)b * p.max_pages + (pos >> p.c.logP)];
+    const size_t slot = ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
+    // the value's raw input is loaded with the key, so that the token-head costs one round of
+    // memory latency (binary16: 64 bytes per lane; binary32 values are loaded after the key)
+    uint4 vraw[4];
+    if (p.dtype == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vraw[q] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.v) + row + 8 * q);
+    }
+    float x[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float x8[8];
+        load8(p.k, p.dtype, row + 8 * q, x8);
+        if (p.c.kf16) store_key16(p.c, slot, 4 * j + q, x8);
+        center8(p.c, h, 4 * j + q, x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * q + e] = x8[e];
+    }
+    // sigma, then the 7 butterfly levels (h = 1 .. 16 inside the lane, 32 and 64 across the quad)
+    const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[j];
+    double y[32];
     double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const double xe = (double)xk[e];
-        ss += xe * xe;
-        const int d = 8 * i + e;
-        y[e] = ((sgw >> (d & 31)) & 1u) ? -xe : xe;
+    for (int e = 0; e < 32; ++e) {
+        const double xe = (double)x[e];
+        ss = fma(xe, xe, ss);
+        y[e] = ((sgw >> e) & 1u) ? -xe : xe;
     }
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
+    for (int m = 1; m < 32; m <<= 1)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if ((e & h) == 0) {
-                const double a = y[e], b = y[e + h];
-                y[e] = a + b;
-                y[e + h] = a - b;
+        for (int e = 0; e < 32; ++e)
+            if ((e & m) == 0) {
+                const double a = y[e], c = y[e + m];
+                y[e] = a + c;
+                y[e + m] = a - c;
             }
+    // across the quad: the lane holding the upper index keeps o - y, the other y + o, as one
+    // fma with a factor of -1 or +1 (exact)
+    const double f1 = (j & 1) ? -1.0 : 1.0, f2 = (j & 2) ? -1.0 : 1.0;
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
+    for (int e = 0; e < 32; ++e) y[e] = fma(f1, y[e], quad_xor1(y[e]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double o = __shfl_xor(y[e], m);
-            y[e] = (i & m) ? (o - y[e]) : (y[e] + o);
-        }
-    // sign bits: byte i of the 16-byte key word vector
-    uint32_t byte = 0;
+    for (int e = 0; e < 32; ++e) y[e] = fma(f2, y[e], quad_xor2(y[e]));
+    // sign bits: word j of the key record; sum |k'| over the sketch's dims
+    uint32_t word = 0;
     double sabs = 0.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        byte |= (y[e] < 0.0 ? 0u : 1u) << e;
+    for (int e = 0; e < 32; ++e) {
+        word |= (y[e] < 0.0 ? 0u : 1u) << e;
         sabs += fabs(y[e]);
     }
-    uint32_t word = byte << (8 * (i & 3));
-    word |= __shfl_xor(word, 1);
-    word |= __shfl_xor(word, 2);
-    if ((i & 3) == 0 && (i >> 2) < p.c.kw) key_rec(p.c, slot)[i >> 2] = word;  // the sketch's words
-    if (8 * i >= p.c.sk) sabs = 0.0;        // dims past the sketch
-    ss = sum16(ss);
-    sabs = sum16(sabs) / sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
-    if (i == 0) key_rec(p.c, slot)[p.c.kw] = norm_corr_word(ss, sabs, p.c.sk);
-    encode_values(xv, i, p.c.Gv, val_rec(p.c, slot));
+    if (32 * j >= p.c.sk) sabs = 0.0;  // dims past the sketch
+    ss += quad_xor1(ss);
+    ss += quad_xor2(ss);
+    sabs += quad_xor1(sabs);
+    sabs += quad_xor2(sabs);
+    sabs /= sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
+    uint32_t *kr = key_rec(p.c, slot);
+    if (j < p.c.kw) kr[j] = word;  // the sketch's words
+    if (j == 0) kr[p.c.kw] = norm_corr_word(ss, sabs, p.c.sk);
+    // values
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (p.dtype == 0) {
+            const uint32_t w[4] = {vraw[q].x, vraw[q].y, vraw[q].z, vraw[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[8 * q + 2 * e] = half_bits_to_float(w[e] & 0xFFFFu);
+                x[8 * q + 2 * e + 1] = half_bits_to_float(w[e] >> 16);
+            }
+        } else {
+            float x8[8];
+            load8(p.v, p.dtype, row + 8 * q, x8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[8 * q + e] = x8[e];
+        }
+    }
+    encode_values32(x, j, p.c.Gv, val_rec(p.c, slot));
 }
 
 // ---------------------------------------------------------------------------------------
