@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
     __shared__ float xs[kD];
     __shared__ int us[kD];
     __shared__ float redf[4];
-    __shared__ int redi[2];
+    __shared__ int redi[4];
     if ((int)blockIdx.x >= p.BH) {
         const long tb = p.has_tail ? p.BH : 0;  // tail blocks
         const long ab = (long)blockIdx.x - p.BH - tb;
@@ -330,7 +330,11 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
         u = (int)t;
     }
     int su = wave_sum_i(u);
-    if (lane == 0) redi[wave] = su;
+    int s3 = wave_sum_i((r & 3) == 3 ? u : 0);  // the codes of dims 3 mod 4 (k_score_topp_mf)
+    if (lane == 0) {
+        redi[wave] = su;
+        redi[2 + wave] = s3;
+    }
     __syncthreads();  // everyone has read xs
     us[r] = u;
     __syncthreads();
@@ -345,16 +349,19 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
     {
         // the codes as the fp8 A operand of k_score_topp_mf, byte r = 32 group + index: it
         // meets K = 16 group + index (index < 16) or 64 + 16 group + index - 16 of the fp4 key
-        // operand, where K = 32 j + 8 v + m carries bit 4m + v of key word j with the factor
-        // 1/2, 1, 2, 2 for v = 0..3; the code is scaled by 4, 2, 1, 1 to match
+        // operand, where K = 32 j + 8 v + m carries bit 4m + v of key word j as 1/2, 1, 2 times
+        // the bit for v = 0..2 (the code is scaled by 4, 2, 1 to match) and as 1 - 2 bit for
+        // v = 3 (the code is negated)
         const int ga = r >> 5, pa = r & 31;
         const int K = pa < 16 ? 16 * ga + pa : 64 + 16 * ga + (pa - 16);
         const int j = K >> 5, v = (K >> 3) & 3, m = K & 7;
-        const int x = us[32 * j + 4 * m + v] << (v == 0 ? 2 : v == 1 ? 1 : 0);
-        p.qa[(size_t)bh * kD + r] = (uint8_t)fp8_e4m3_small(x);
+        const int uc = us[32 * j + 4 * m + v];
+        const uint32_t f8 = fp8_e4m3_small(uc << (v == 0 ? 2 : v == 1 ? 1 : 0));
+        p.qa[(size_t)bh * kD + r] = (uint8_t)(v == 3 && uc ? f8 | 0x80u : f8);  // -u for v = 3
     }
     su = redi[0] + redi[1];
-    if (r == 0) p.qpar[bh] = make_float4(vl * p.isk, delta * p.isk, __int_as_float(su), 0.0f);
+    s3 = redi[2] + redi[3];
+    if (r == 0) p.qpar[bh] = make_float4(vl * p.isk, delta * p.isk, __int_as_float(su), __int_as_float(s3));
     if (p.dbg_codes) p.dbg_codes[(size_t)bh * kD + r] = (uint8_t)u;
     if (r == 0 && p.dbg_params) {
         p.dbg_params[bh * 4 + 0] = vl;
@@ -562,17 +569,28 @@ __global__ __launch_bounds__(64, 4) void k_score_topp(ScoreParams p)
 //    over the 16-lane rows (two permlane32 and two permlane16 swaps) leaves, in register t,
 //    word j of token 64u + 16t + n in lane 16j + n: the B operand of tile t.
 //  - bit 4m + v of a word goes to nibble m of B register v, as 0x1 (0.5), 0x2 (1), 0x4 (2)
-//    for v = 0, 1, 2 and 0x4 after a shift for v = 3 (2).  The query codes carry the
-//    factors 4, 2, 1, 1, so each product is 2 * bit * u.
+//    for v = 0, 1, 2, with the query codes scaled by 4, 2, 1: each product is 2 * bit * u.
+//    For v = 3 the bit stays in place, as the sign of the nibble 0x2 (+1 or -1 for a clear
+//    or set bit: one and-or), against the code -u: the product is 2 * bit * u - u, and the
+//    sum of those u (the codes of dims 3 mod 4) is added back through the accumulator.
 //  - the A operand of tile t holds head h in row 4t + h and zeros in the other rows, and
 //    the four tiles accumulate into one result, which starts at -sumu of head h in
-//    register h.  Rows 4t' .. 4t' + 3 of the result (registers 0..3 of lanes 16t' + n)
+//    register h (plus the dims 3 mod 4 sum).  Rows 4t' .. 4t' + 3 of the result (registers 0..3 of lanes 16t' + n)
 //    then hold A of the 4 heads for token 64u + 16t' + n: lane l ends with its own token.
 // Products and sums are integers below 2^12, exact in binary32: A = 2 ip - sumu and the
 // score are bit-identical to the dot8 form.
 // ---------------------------------------------------------------------------------------
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+// (a & m) | c in one instruction (VOP3 takes no literal here, and the compiler splits the
+// two-constant form in two): m from a scalar register, c from a vector register
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
 
 __device__ __forceinline__ void swap32(uint32_t &a, uint32_t &b)
 {
@@ -631,7 +649,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
         const float4 pq = p.qpar[bh0 + h];
         c0[h] = pq.x;
         c1[h] = pq.y;
-        msu[h] = (float)-__float_as_int(pq.z);
+        msu[h] = (float)(__float_as_int(pq.w) - __float_as_int(pq.z));
     }
     uint32_t slot[U];
 #pragma unroll
@@ -645,13 +663,14 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
     for (int u = 0; u < U; ++u) load_key_t<KW>(p.c, slot[u], kb[u], nc[u]);
     __builtin_amdgcn_sched_barrier(0);
     int e[U][GB];
+    const uint32_t plus1 = 0x22222222u;  // every nibble +1 (fp4 e2m1 0x2)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         uint32_t w[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
         const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                        __builtin_popcount(w[3]);
         const float fP = (float)(2 * pc - 32 * KW);
-        const float r = half_bits_to_float(nc[u] & 0xFFFFu) / half_bits_to_float(nc[u] >> 16);
+        const float r = norm_over_corr(nc[u]);
         swap32(w[0], w[2]);
         swap32(w[1], w[3]);
         swap16(w[0], w[1]);
@@ -660,7 +679,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const v8i_t bt = {(int)(w[t] & 0x11111111u), (int)(w[t] & 0x22222222u), (int)(w[t] & 0x44444444u),
-                              (int)((w[t] >> 1) & 0x44444444u), 0, 0, 0, 0};
+                              (int)and_or(w[t], 0x88888888u, plus1), 0, 0, 0, 0};
             d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[t], bt, d, 0, 4, 0, 127, 0, 127);
         }
 #pragma unroll

@@ -158,6 +158,26 @@ __device__ __forceinline__ float wave_max_u(float v)
 }
 
 // ---------------------------------------------------------------------------------------
+// norm / corr of a key record's binary16 pair, rounded to nearest binary32: the same value
+// as IEEE division, in fewer instructions.  y = rcp(c) is within one ulp of 1/c, so
+// q0 = n * y is within three ulps of q = n / c and the remainder n - c * q0 is exact in one
+// fma; q1 = q0 + (n - c q0) * y then differs from q by less than 2^-20 ulp.  A quotient of
+// two binary16 numbers lies more than 2^-12 ulp from every rounding midpoint of binary32
+// (such a midpoint has an odd 25-bit significand, and its distance to n / c is a nonzero
+// multiple of a power of two that c's 11-bit significand bounds), so q1 is rounded as q.
+// Where q1 is NaN (a zero, infinite or NaN operand) or zero (n = 0, where the sum with the
+// zero remainder can lose the sign of q0), q0 is the IEEE quotient and is taken instead.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float norm_over_corr(uint32_t nc)
+{
+    const float n = half_bits_to_float(nc & 0xFFFFu), c = half_bits_to_float(nc >> 16);
+    const float y = __builtin_amdgcn_rcpf(c);
+    const float q0 = n * y;
+    const float q1 = fmaf(fmaf(-c, q0, n), y, q0);
+    return __builtin_amdgcn_class(q1, 0x63) ? q0 : q1;  // classes sNaN, qNaN, -0, +0
+}
+
+// ---------------------------------------------------------------------------------------
 // Top-p bin of a proxy score: floor(s * kbin) in binary32, clamped to [-2^29, 2^29];
 // a NaN goes to the bottom.
 // ---------------------------------------------------------------------------------------
@@ -245,7 +265,7 @@ __device__ __forceinline__ void score_key(const uint4 kb, uint32_t nc, const Que
     const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
                    __builtin_popcount(w[3]);
     const float fP = (float)(2 * pc - sk);
-    const float r = half_bits_to_float(nc & 0xFFFFu) / half_bits_to_float(nc >> 16);
+    const float r = norm_over_corr(nc);
     // the GB accumulation chains are interleaved so that consecutive dot products are
     // independent
     uint32_t ip[GB];
