@@ -535,6 +535,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     ap.c = cv;
     ap.q = q;
     ap.qnib = qnib;
+    ap.qa = qa;
     ap.qpar = qpar;
     ap.klog = klog;
     ap.dl = sp.dl;

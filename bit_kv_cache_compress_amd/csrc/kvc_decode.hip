@@ -605,6 +605,29 @@ __device__ __forceinline__ void swap16(uint32_t &a, uint32_t &b)
     b = r[1];
 }
 
+// The binary x INT4 products of this lane's key with 4 query heads on the matrix cores (the
+// transpose, operands and tiles described above): register h of the result is
+// A = 2 sum_r bit_r u_r - sumu of head h for the lane's own token.  qa(t) gives the A
+// operand of tile t; msu holds the accumulator start of each head.
+template <typename QA>
+__device__ __forceinline__ v4f_t key_products4(const uint4 &kb, const v4f_t &msu, QA qa)
+{
+    uint32_t w[4] = {kb.x, kb.y, kb.z, kb.w};
+    swap32(w[0], w[2]);
+    swap32(w[1], w[3]);
+    swap16(w[0], w[1]);
+    swap16(w[2], w[3]);
+    const uint32_t plus1 = 0x22222222u;  // every nibble +1 (fp4 e2m1 0x2)
+    v4f_t d = msu;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const v8i_t bt = {(int)(w[t] & 0x11111111u), (int)(w[t] & 0x22222222u), (int)(w[t] & 0x44444444u),
+                          (int)and_or(w[t], 0x88888888u, plus1), 0, 0, 0, 0};
+        d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa(t), bt, d, 0, 4, 0, 127, 0, 127);
+    }
+    return d;
+}
+
 template <int KW>
 __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
 {
@@ -663,25 +686,13 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
     for (int u = 0; u < U; ++u) load_key_t<KW>(p.c, slot[u], kb[u], nc[u]);
     __builtin_amdgcn_sched_barrier(0);
     int e[U][GB];
-    const uint32_t plus1 = 0x22222222u;  // every nibble +1 (fp4 e2m1 0x2)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        uint32_t w[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
-        const int pc = __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) +
-                       __builtin_popcount(w[3]);
+        const int pc = __builtin_popcount(kb[u].x) + __builtin_popcount(kb[u].y) + __builtin_popcount(kb[u].z) +
+                       __builtin_popcount(kb[u].w);
         const float fP = (float)(2 * pc - 32 * KW);
         const float r = norm_over_corr(nc[u]);
-        swap32(w[0], w[2]);
-        swap32(w[1], w[3]);
-        swap16(w[0], w[1]);
-        swap16(w[2], w[3]);
-        v4f_t d = msu;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const v8i_t bt = {(int)(w[t] & 0x11111111u), (int)(w[t] & 0x22222222u), (int)(w[t] & 0x44444444u),
-                              (int)and_or(w[t], 0x88888888u, plus1), 0, 0, 0, 0};
-            d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[t], bt, d, 0, 4, 0, 127, 0, 127);
-        }
+        const v4f_t d = key_products4(kb[u], msu, [&](int t) { return qa[t]; });
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             const float a = d[h];
@@ -1226,6 +1237,307 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         if (lane == 0) {
             p.pm[pidx + (size_t)h * g.NCA] = mrun[h];
             p.pl[pidx + (size_t)h * g.NCA] = l;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Full-softmax attention with the weighted value sums on the matrix cores.  One wave per
+// (chunk of CH tokens, KV head, sequence) and GB <= 4 query heads of that KV head, batches of
+// 64 tokens as two steps of 32 through v_mfma_f32_16x16x32_bf16:
+//   O[(h, g)][d] = sum_t A[(h, g)][t] B[t][d],  A = w_h(t) * scale_g(t),  B = code_d(t),
+// with the A rows (h, g) = NG h + g (NG = 128 / GV groups; rows past GB heads are zero) and
+// the dims in 8 tiles of 16 columns (tile j, column n: dim 8n + j); a row keeps the dims of
+// its own group.
+//  - A goes in as a bfloat16 pair hi + lo (A - hi - lo within 2^-18 A), both through the
+//    MFMA against the same B.
+//  - B holds the 4-bit code c as the bfloat16 128 + c (bits 0x4300 | c, exact): one byte
+//    permute and one and-or per two codes.  A ninth tile with B = 128 gives 128 * sum_t A per
+//    row, subtracted at the end; fp32 accumulation keeps the sum to about 2^-19 relative.
+//  - the zero points add sum_t w_h(t) zero_g(t) per row, in fp32 on the vector unit.
+// Lane l scores token l of the batch (binary x INT4; for four heads on the matrix cores as in
+// k_score_topp_mf, with the query operand read from LDS per tile).  As an A row it is
+// (h, g) = l mod 16, as a B column the dims 8 (l mod 16) .. + 7, and in both roles it covers
+// tokens 8 (l / 16) .. + 7 of each 32-token step; so per token of that K block it loads the
+// 4 code bytes of its dims and the scale/zero word of its row's group, and reads the weights
+// of its row's head from LDS.  Output rows 4 (l / 16) + i, columns l mod 16 (the MFMA's
+// accumulator layout): lane l ends with 8 dims of the heads whose group matches its dims.
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// x0, x1 rounded to bfloat16 (hi) and the rounded remainders (lo), two per word, x0 low
+__device__ __forceinline__ void bf16_split2(float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    const bf16x2_t h = __builtin_convertvector((f2_t){x0, x1}, bf16x2_t);
+    __builtin_memcpy(&hi, &h, 4);
+    const f2_t r = {x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u)};
+    const bf16x2_t l = __builtin_convertvector(r, bf16x2_t);
+    __builtin_memcpy(&lo, &l, 4);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    const uint4 v = make_uint4(a, b, c, d);
+    bf16x8_t r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ __forceinline__ float pick4(const v4f_t &v, int i)
+{
+    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+template <int GB, int GV, int KW, bool PAGE64>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_full_mf(AttendParams p)
+{
+    constexpr int NB = 64;                // tokens per batch
+    constexpr int NG = kD / GV;           // value groups per token
+    constexpr int HR = 16 / NG;           // heads that the 16 A rows span
+    constexpr int VREC = kD / 2 + 4 * NG;  // bytes of a value record
+    static_assert(GB <= HR, "A rows");
+    constexpr bool MF4 = GB == 4;  // four heads: the key products on the matrix cores as well
+    __shared__ float wbuf[HR][NB];  // weights by head; rows past GB stay zero
+    __shared__ uint4 qa_s[MF4 ? 34 : 1];  // the 4 heads' fp8 query codes, then 32 zero bytes
+    __shared__ uint32_t pbase[kMaxFullChunk / 16 + 1];
+    const DecodeGeom &g = p.g;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    int kvh, hq0;
+    block_heads(g, blockIdx.y, kvh, hq0);
+    const int L = g.seq_lens[b];
+    const int t0 = chunk * g.CH;
+    if (t0 >= L) return;
+    const int n = min(g.CH, L - t0);
+    const int lane = threadIdx.x;
+    const int bh0 = b * g.Hq + hq0;
+    const int logP = p.c.logP;
+    const int p0 = t0 >> logP;
+    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
+    for (int i = lane; i < np; i += 64)
+        pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
+                   << logP;
+    for (int i = lane; i < (HR - GB) * NB; i += 64) wbuf[GB + i / NB][i % NB] = 0.0f;
+    QueryState<MF4 ? 1 : GB> qs;  // wave-uniform: scalar loads into SGPRs (dot8 products)
+    float c0[GB], c1[GB];
+    v4f_t msu = {0.0f, 0.0f, 0.0f, 0.0f};  // the matrix-core products' accumulator start
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        const float4 pq = p.qpar[bh0 + h];
+        c0[h] = pq.x;
+        c1[h] = pq.y;
+        if constexpr (MF4) {
+            msu[h] = (float)(__float_as_int(pq.w) - __float_as_int(pq.z));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) qs.nib[h][i] = p.qnib[(size_t)(bh0 + h) * 16 + i];
+            qs.c0[h] = pq.x;
+            qs.c1[h] = pq.y;
+            qs.sumu[h] = __float_as_int(pq.z);
+        }
+    }
+    if constexpr (MF4) {
+        if (lane < 32) qa_s[lane] = reinterpret_cast<const uint4 *>(p.qa + (size_t)bh0 * kD)[lane];
+        else if (lane < 34) qa_s[lane] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    // A operand of key-product tile t: query head lane & 3 in row lane & 15 of tile
+    // (lane & 15) >> 2, its 32 codes of K block lane >> 4; zeros in the other tiles
+    const int qrow = 8 * (lane & 3) + 2 * (lane >> 4), qtile = (lane & 15) >> 2;
+
+    const int r16 = lane & 15, kb = lane >> 4;
+    const int ha = r16 / NG, ga = r16 % NG;  // the lane's A row
+    const int vw = 4 * r16;                  // its code word: dims 8 r16 .. 8 r16 + 7
+    const int vz = kD / 2 + 4 * ga;          // the scale/zero word of its A row's group
+    const uint32_t tmask = (1u << logP) - 1u;
+    const uint32_t c128 = 0x43004300u;       // two bfloat16 128s
+    const bf16x8_t b128 = as_bf16x8(c128, c128, c128, c128);
+    v4f_t acc[9];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) acc[j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float zacc = 0.0f, lsum[GB], mrun[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        lsum[h] = 0.0f;
+        mrun[h] = -INFINITY;
+    }
+
+    for (int bs = 0; bs < n; bs += NB) {
+        const int nb = min(NB, n - bs);
+        // ---- the batch's key and value records
+        uint4 kbw;
+        uint32_t nc;
+        uint32_t cw[16], szw[16];  // entry 8 kt + i: token 32 kt + 8 kb + i of the batch
+        if constexpr (PAGE64) {
+            // pages of 64 tokens or more hold a whole batch (it starts at a multiple of 64):
+            // consecutive slots, one address per lane and fixed offsets.  Slots past the
+            // sequence's end are read but get no weight, and their scale/zero words are
+            // cleared below, so that whatever they hold stays out of the sums.
+            const uint32_t first = (uint32_t)(t0 + bs);
+            const uint32_t s0 = pbase[(first >> logP) - p0] + (first & tmask);
+            load_key_t<KW>(p.c, s0 + lane, kbw, nc);
+            const uint8_t *vr = p.c.vals + (size_t)(s0 + 8 * kb) * VREC;
+            const uint32_t *cwp = reinterpret_cast<const uint32_t *>(vr + vw);
+            const uint32_t *szp = reinterpret_cast<const uint32_t *>(vr + vz);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    cw[8 * kt + i] = cwp[(32 * kt + i) * (VREC / 4)];
+                    szw[8 * kt + i] = szp[(32 * kt + i) * (VREC / 4)];
+                }
+            if (nb < NB) {  // uniform: the sequence's last batch
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (32 * kt + 8 * kb + i >= nb) szw[8 * kt + i] = 0u;
+            }
+        } else {
+            // tokens past nb re-read the last one
+            {
+                const uint32_t t = (uint32_t)(t0 + bs + min(lane, nb - 1));
+                load_key_t<KW>(p.c, pbase[(t >> logP) - p0] + (t & tmask), kbw, nc);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t t = (uint32_t)(t0 + bs + min(32 * kt + 8 * kb + i, nb - 1));
+                    const uint8_t *vr = p.c.vals + (size_t)(pbase[(t >> logP) - p0] + (t & tmask)) * VREC;
+                    cw[8 * kt + i] = *reinterpret_cast<const uint32_t *>(vr + vw);
+                    szw[8 * kt + i] = *reinterpret_cast<const uint32_t *>(vr + vz);
+                }
+        }
+        float s[GB];
+        if constexpr (MF4) {
+            const int pc = __builtin_popcount(kbw.x) + __builtin_popcount(kbw.y) + __builtin_popcount(kbw.z) +
+                           __builtin_popcount(kbw.w);
+            const float fP = (float)(2 * pc - 32 * KW);
+            const float r = norm_over_corr(nc);
+            const v4f_t d = key_products4(kbw, msu, [&](int t) {
+                const uint4 *q = &qa_s[qtile == t ? qrow : 32];
+                const uint4 a0 = q[0], a1 = q[1];
+                return v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            });
+#pragma unroll
+            for (int h = 0; h < GB; ++h) s[h] = fmaf(c1[h], d[h], c0[h] * fP) * r;
+        } else {
+            int A[GB];
+            score_key<GB>(kbw, nc, qs, s, A, 32 * KW);
+        }
+        // ---- running max per head; the partial sums are rescaled when it grows
+        float scl[GB];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+            // past the batch, or a marked record (a token held in the high-precision tier)
+            if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
+            const float mnew = fmaxf(mrun[h], wave_max_u(s[h]));
+            scl[h] = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
+            grow |= scl[h] != 1.0f;
+            mrun[h] = mnew;
+        }
+        if (grow) {  // wave-uniform
+            float f[4];  // accumulator register i holds row 4 kb + i, of head (4 kb + i) / NG
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hr = (4 * kb + i) / NG;
+                float v = 1.0f;
+#pragma unroll
+                for (int h = 0; h < GB; ++h) v = hr == h ? scl[h] : v;
+                f[i] = v;
+            }
+#pragma unroll
+            for (int j = 0; j < 9; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[j][i] *= f[i];
+            float fz = 1.0f;
+#pragma unroll
+            for (int h = 0; h < GB; ++h) fz = ha == h ? scl[h] : fz;
+            zacc *= fz;
+#pragma unroll
+            for (int h = 0; h < GB; ++h) lsum[h] *= scl[h];
+        }
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+            const float w = (s[h] == -INFINITY) ? 0.0f : exp2f((s[h] - mrun[h]) * p.klog);
+            lsum[h] += w;
+            wbuf[h][lane] = w;
+        }
+        __syncthreads();
+        // ---- two 32-token steps on the matrix cores
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const float4 wa = *reinterpret_cast<const float4 *>(&wbuf[ha][32 * kt + 8 * kb]);
+            const float4 wb = *reinterpret_cast<const float4 *>(&wbuf[ha][32 * kt + 8 * kb + 4]);
+            const float w8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t sz = szw[8 * kt + i];
+                x[i] = w8[i] * half_bits_to_float(sz & 0xFFFFu);
+                zacc = fmaf(w8[i], half_bits_to_float(sz >> 16), zacc);
+            }
+            uint32_t ah[4], al[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) bf16_split2(x[2 * m], x[2 * m + 1], ah[m], al[m]);
+            const bf16x8_t Ahi = as_bf16x8(ah[0], ah[1], ah[2], ah[3]);
+            const bf16x8_t Alo = as_bf16x8(al[0], al[1], al[2], al[3]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // byte k of the code words: dims 8 r16 + 2k (low nibble) and + 2k + 1 (high)
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    // byte k of tokens 2m and 2m + 1 into bytes 0 and 2, zeros between
+                    const uint32_t q = __builtin_amdgcn_perm(cw[8 * kt + 2 * m + 1], cw[8 * kt + 2 * m],
+                                                             0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
+                    lo[m] = and_or(q, 0x000F000Fu, c128);
+                    hi[m] = and_or(q >> 4, 0x000F000Fu, c128);
+                }
+                const bf16x8_t Blo = as_bf16x8(lo[0], lo[1], lo[2], lo[3]);
+                const bf16x8_t Bhi = as_bf16x8(hi[0], hi[1], hi[2], hi[3]);
+                acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Blo, acc[2 * k], 0, 0, 0);
+                acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bhi, acc[2 * k + 1], 0, 0, 0);
+                acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Blo, acc[2 * k], 0, 0, 0);
+                acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bhi, acc[2 * k + 1], 0, 0, 0);
+            }
+            acc[8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, b128, acc[8], 0, 0, 0);
+            acc[8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, b128, acc[8], 0, 0, 0);
+        }
+        __syncthreads();  // wbuf is rewritten by the next batch
+    }
+
+    // ---- weight sums; zero-point sums of each A row over its 4 token blocks (lanes r16 + 16 k)
+    const size_t pidx = (size_t)bh0 * g.NCA + chunk;  // partial of head bh0 (+ h * NCA)
+    zacc += __shfl_xor(zacc, 16);
+    zacc += __shfl_xor(zacc, 32);
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        const float l = wave_sum(lsum[h]);
+        if (lane == 0) {
+            p.pm[pidx + (size_t)h * g.NCA] = mrun[h];
+            p.pl[pidx + (size_t)h * g.NCA] = l;
+        }
+    }
+    // lane l holds columns r16 (dims 8 r16 + j of tile j) of rows 4 kb + i; the rows of the
+    // dims' own group are i = gd (NG = 4) or i = gd, gd + 2 (NG = 2)
+    const int gd = (8 * r16) / GV;
+#pragma unroll
+    for (int q = 0; q < 4 / NG; ++q) {
+        const int i = gd + NG * q;
+        const int row = 4 * kb + i, h = row / NG;
+        const float z = __shfl(zacc, row);  // lanes row, row + 16, ... hold the row's sum
+        if (h < GB) {
+            const float c = pick4(acc[8], i);
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = (pick4(acc[j], i) - c) + z;
+            float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + 8 * r16);
+            dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_float4(o[4], o[5], o[6], o[7]);
         }
     }
 }
@@ -1901,12 +2213,25 @@ __global__ __launch_bounds__(256) void k_check(CheckParams p, int32_t *flag)
     }
 }
 
-// The full-softmax kernel for the cache's key record width.
+// The full-softmax kernel for the cache's key record width.  The matrix-core form when its
+// A operand has at least 4 rows in use (heads x value groups); one head over 64-dim groups
+// (2 rows) stays on the vector units, which measured faster there.
 template <int GB, int GV>
 void launch_full(const AttendParams &p, dim3 grid, hipStream_t s)
 {
-    if (p.c.kw == 4) KVC_LAUNCH((k_attend_full<GB, GV, 4>), grid, dim3(64), s, p);
-    else KVC_LAUNCH((k_attend_full<GB, GV, 2>), grid, dim3(64), s, p);
+    if constexpr (GB * (kD / GV) < 4) {
+        if (p.c.kw == 4) KVC_LAUNCH((k_attend_full<GB, GV, 4>), grid, dim3(64), s, p);
+        else KVC_LAUNCH((k_attend_full<GB, GV, 2>), grid, dim3(64), s, p);
+    } else {
+        const bool big = p.c.logP >= 6;
+        if (p.c.kw == 4) {
+            if (big) KVC_LAUNCH((k_attend_full_mf<GB, GV, 4, true>), grid, dim3(64), s, p);
+            else KVC_LAUNCH((k_attend_full_mf<GB, GV, 4, false>), grid, dim3(64), s, p);
+        } else {
+            if (big) KVC_LAUNCH((k_attend_full_mf<GB, GV, 2, true>), grid, dim3(64), s, p);
+            else KVC_LAUNCH((k_attend_full_mf<GB, GV, 2, false>), grid, dim3(64), s, p);
+        }
+    }
 }
 
 }  // namespace

@@ -193,6 +193,7 @@ struct AttendParams {
     CacheView c;
     const float *q;        // [B*Hq][128] the queries (exact scores from c.kf16)
     const uint32_t *qnib;
+    const uint8_t *qa;     // [B*Hq][128] the codes as the fp8 operand of the matrix-core key products
     const float4 *qpar;
     float klog;            // log2(e) / sqrt(D)
     // Top-p selection (select mode only)
