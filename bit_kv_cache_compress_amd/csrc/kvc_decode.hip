@@ -1362,6 +1362,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
         lsum[h] = 0.0f;
         mrun[h] = -INFINITY;
     }
+    const float lazy = 8.0f / p.klog;  // score units of a factor 2^8 in weight
 
     for (int bs = 0; bs < n; bs += NB) {
         const int nb = min(NB, n - bs);
@@ -1427,17 +1428,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
             int A[GB];
             score_key<GB>(kbw, nc, qs, s, A, 32 * KW);
         }
-        // ---- running max per head; the partial sums are rescaled when it grows
+        // ---- reference score per head (wave-uniform): the weights are exp2((s - m) klog) <= 2^8.
+        // m moves only when a score passes m + 8 / klog, then to the batch max, and the partial
+        // sums are rescaled; most batches cost one compare per head instead of a wave max.
         float scl[GB];
         bool grow = false;
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             // past the batch, or a marked record (a token held in the high-precision tier)
             if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
-            const float mnew = fmaxf(mrun[h], wave_max_u(s[h]));
-            scl[h] = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
-            grow |= scl[h] != 1.0f;
-            mrun[h] = mnew;
+            scl[h] = 1.0f;
+            if (__any(s[h] > mrun[h] + lazy)) {  // the first finite score always moves it
+                const float mnew = wave_max_u(s[h]);
+                scl[h] = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
+                mrun[h] = mnew;
+                grow = true;
+            }
         }
         if (grow) {  // wave-uniform
             float f[4];  // accumulator register i holds row 4 kb + i, of head (4 kb + i) / NG
@@ -1462,7 +1468,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
         }
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-            const float w = (s[h] == -INFINITY) ? 0.0f : exp2f((s[h] - mrun[h]) * p.klog);
+            // v_exp_f32 (exp2(-inf) = 0); no weight while the head has no finite score
+            const float w = (mrun[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s[h] - mrun[h]) * p.klog);
             lsum[h] += w;
             wbuf[h][lane] = w;
         }

@@ -203,7 +203,8 @@ struct AttendParams {
     const int32_t *order;  // [B*Hq] head (b * Hq + h) of each dispatch rank
     const int32_t *order_ctr;  // [2]: order_ctr[0] heads were classed dense (attention chunk by chunk)
     // partial results per (b, h, chunk)
-    float *pm;             // [B*Hq][NCA] max score of the chunk's attended tokens
+    float *pm;             // [B*Hq][NCA] the chunk's reference score: the max of its attended
+                           // tokens, or (full softmax) up to 8 / klog below it
     float *pl;             // [B*Hq][NCA] sum of weights
     float *po;             // [B*Hq][NCA][128] weighted value sums
 };
