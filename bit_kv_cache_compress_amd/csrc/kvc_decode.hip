@@ -1089,13 +1089,15 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 // query heads of that KV head.  The chunk is walked in batches of 64 tokens.  For a batch
 // every load is issued up front: one key record per lane (the lane's token) and, per 16-lane
 // group, the value words of 16 tokens (4 bytes of codes, i.e. 8 dims, and the group's
-// scale/zero word per lane).  The lane scores its token for the GB heads (binary x INT4),
-// the running max of each head is updated with a wave reduction (earlier batches are
-// rescaled when it grows), the weights exp2((s - m) log2e/sqrt(D)) go through LDS, and each
-// lane accumulates weight x decoded value for its 8 dims (the zero point once per token).
-// The wave writes (m, sum of weights, weighted value sums) per head for the merge.
+// scale/zero word per lane).  The lane scores its token for the GB heads (binary x INT4).
+// Each head keeps a reference score m, which moves (a wave max, the earlier batches
+// rescaled) only when a score passes it by 8 / (log2e/sqrt(D)); the weights
+// exp2((s - m) log2e/sqrt(D)) <= 2^8 go through LDS, and each lane accumulates weight x
+// decoded value for its 8 dims (the zero point once per token).  The wave writes (m, sum of
+// weights, weighted value sums) per head for the merge.  Used where the matrix-core form
+// below would fill fewer than 4 of its 16 rows (one head over 64-dim groups).
 // ---------------------------------------------------------------------------------------
-template <int GB, int GV, int KW>
+template <int GB, int GV, int KW, bool PAGE64>
 __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 {
     constexpr int NB = 64;        // tokens per batch
@@ -1146,22 +1148,33 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
     }
 
+    const float lazy = 8.0f / p.klog;  // score units of a factor 2^8 in weight
     for (int bs = 0; bs < n; bs += NB) {
         const int nb = min(NB, n - bs);
-        // ---- the batch's key and value records (tokens past nb re-read the last one)
+        // ---- the batch's key and value records (the slow path re-reads the last token for
+        // those past nb)
         uint4 kb;
         uint32_t nc;
         uint32_t cw[VU], szw[VU];
-        if (nb == NB && logP >= 6) {
-            // a whole batch inside one page: consecutive slots
+        if constexpr (PAGE64) {
+            // pages of 64 tokens or more hold a whole batch: consecutive slots, one address per
+            // lane and fixed offsets; slots past the sequence's end get no weight, and their
+            // scale/zero words are cleared so that whatever they hold stays out of the sums
             const uint32_t first = (uint32_t)(t0 + bs);
             const uint32_t s0 = pbase[(first >> logP) - p0] + (first & tmask);
             load_key_t<KW>(p.c, s0 + lane, kb, nc);
             const uint8_t *vr = p.c.vals + (size_t)(s0 + eg) * VREC;
+            const uint32_t *cwp = reinterpret_cast<const uint32_t *>(vr + vw);
+            const uint32_t *szp = reinterpret_cast<const uint32_t *>(vr + vz);
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
-                cw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * u * VREC + vw);
-                szw[u] = *reinterpret_cast<const uint32_t *>(vr + 4 * u * VREC + vz);
+                cw[u] = cwp[u * VREC];  // 4 tokens further per u
+                szw[u] = szp[u * VREC];
+            }
+            if (nb < NB) {  // uniform: the sequence's last batch
+#pragma unroll
+                for (int u = 0; u < VU; ++u)
+                    if (eg + 4 * u >= nb) szw[u] = 0u;
             }
         } else {
             {
@@ -1185,16 +1198,18 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         for (int h = 0; h < GB; ++h) {
             // past the batch, or a marked record (a token held in the high-precision tier)
             if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
-            const float mnew = fmaxf(mrun[h], wave_max_u(s[h]));
-            const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
-            if (scale != 1.0f) {
+            // the reference score moves only when a score passes it by 8 / klog (weights stay
+            // <= 2^8), then to the batch max with the partial sums rescaled
+            if (__any(s[h] > mrun[h] + lazy)) {
+                const float mnew = wave_max_u(s[h]);
+                const float scale = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
                 zacc[h] *= scale;
                 lsum[h] *= scale;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[h][j] *= scale;
+                mrun[h] = mnew;
             }
-            mrun[h] = mnew;
-            const float w = (s[h] == -INFINITY) ? 0.0f : exp2f((s[h] - mnew) * p.klog);
+            const float w = (mrun[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s[h] - mrun[h]) * p.klog);
             lsum[h] += w;
             wbuf[lane][h] = w;
         }
@@ -1262,6 +1277,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 // 4 code bytes of its dims and the scale/zero word of its row's group, and reads the weights
 // of its row's head from LDS.  Output rows 4 (l / 16) + i, columns l mod 16 (the MFMA's
 // accumulator layout): lane l ends with 8 dims of the heads whose group matches its dims.
+// The softmax keeps a reference score per head as k_attend_full does.
 // ---------------------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
@@ -2226,11 +2242,16 @@ __global__ __launch_bounds__(256) void k_check(CheckParams p, int32_t *flag)
 template <int GB, int GV>
 void launch_full(const AttendParams &p, dim3 grid, hipStream_t s)
 {
+    const bool big = p.c.logP >= 6;
     if constexpr (GB * (kD / GV) < 4) {
-        if (p.c.kw == 4) KVC_LAUNCH((k_attend_full<GB, GV, 4>), grid, dim3(64), s, p);
-        else KVC_LAUNCH((k_attend_full<GB, GV, 2>), grid, dim3(64), s, p);
+        if (p.c.kw == 4) {
+            if (big) KVC_LAUNCH((k_attend_full<GB, GV, 4, true>), grid, dim3(64), s, p);
+            else KVC_LAUNCH((k_attend_full<GB, GV, 4, false>), grid, dim3(64), s, p);
+        } else {
+            if (big) KVC_LAUNCH((k_attend_full<GB, GV, 2, true>), grid, dim3(64), s, p);
+            else KVC_LAUNCH((k_attend_full<GB, GV, 2, false>), grid, dim3(64), s, p);
+        }
     } else {
-        const bool big = p.c.logP >= 6;
         if (p.c.kw == 4) {
             if (big) KVC_LAUNCH((k_attend_full_mf<GB, GV, 4, true>), grid, dim3(64), s, p);
             else KVC_LAUNCH((k_attend_full_mf<GB, GV, 4, false>), grid, dim3(64), s, p);
