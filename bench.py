@@ -559,8 +559,10 @@ def main():
         if topp else (key_bytes + vb) * tokens_heads,
         "hist": DIST_BYTES * G * tokens_heads, "query": 0, "merge": 0, "append": append_alg}
     score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if topp else "k_score"
+    # full softmax: the matrix-core kernel unless its A operand would fill fewer than 4 rows
+    full_kernel = "k_attend_full_mf" if G * (D // Gv) >= 4 else "k_attend_full"
     kernel_names = {"score": score_kernel, "append": "k_append",
-                    "attend": "k_attend_topp" if topp else "k_attend_full", "hist": "k_hist",
+                    "attend": "k_attend_topp" if topp else full_kernel, "hist": "k_hist",
                     "query": "k_qprep", "merge": "k_merge"}
     dominant = max((k for k in stage_ms if k in alg), key=lambda k: stage_ms[k])
     t_dom = stage_ms[dominant] / 1e3

@@ -1306,35 +1306,55 @@ __device__ __forceinline__ float pick4(const v4f_t &v, int i)
     return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
-template <int GB, int GV, int KW, bool PAGE64>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_full_mf(AttendParams p)
+// LDS ordering among the lanes of one wave (for data no other wave touches): a wave's LDS
+// operations complete in order, so fences at wavefront scope, which keep the compiler from
+// moving LDS accesses across this point, are all that is needed.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave's state of the matrix-core pass: the 9 accumulator tiles, the zero-point sum of the
+// lane's A row, and per head the lane's weight sum and the (wave-uniform) reference score.
+template <int GB>
+struct MfState {
+    v4f_t acc[9];
+    float zacc, lsum[GB], mrun[GB];
+};
+
+// LDS of one wave of the pass: the batch's weights by head (row GB stays zero: the A rows of
+// heads past GB read it), the 4 heads' fp8 query codes and 32 zero bytes, the page ids of the
+// pass's tokens (NPB entries: tokens / 16 + 1 for pages of >= 16 tokens).
+template <int GB, int NPB>
+struct MfShared {
+    float wbuf[GB + 1][64];
+    uint4 qa[34];
+    uint32_t pbase[NPB];
+};
+
+// The matrix-core pass of one wave over tokens tb .. tb + n - 1 of sequence b for the GB query
+// heads bh0 .. of KV head kvh (the scheme above).  Leaves the sums in st; mf_outputs gives
+// the value sums.
+template <int GB, int GV, int KW, bool PAGE64, int NPB>
+__device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, int bh0, int tb, int n,
+                                        MfShared<GB, NPB> &sh, MfState<GB> &st)
 {
     constexpr int NB = 64;                // tokens per batch
     constexpr int NG = kD / GV;           // value groups per token
-    constexpr int HR = 16 / NG;           // heads that the 16 A rows span
     constexpr int VREC = kD / 2 + 4 * NG;  // bytes of a value record
-    static_assert(GB <= HR, "A rows");
+    static_assert(GB * NG <= 16, "A rows");
     constexpr bool MF4 = GB == 4;  // four heads: the key products on the matrix cores as well
-    __shared__ float wbuf[HR][NB];  // weights by head; rows past GB stay zero
-    __shared__ uint4 qa_s[MF4 ? 34 : 1];  // the 4 heads' fp8 query codes, then 32 zero bytes
-    __shared__ uint32_t pbase[kMaxFullChunk / 16 + 1];
     const DecodeGeom &g = p.g;
-    const int chunk = blockIdx.x, b = blockIdx.z;
-    int kvh, hq0;
-    block_heads(g, blockIdx.y, kvh, hq0);
-    const int L = g.seq_lens[b];
-    const int t0 = chunk * g.CH;
-    if (t0 >= L) return;
-    const int n = min(g.CH, L - t0);
-    const int lane = threadIdx.x;
-    const int bh0 = b * g.Hq + hq0;
+    const int lane = threadIdx.x & 63;
     const int logP = p.c.logP;
-    const int p0 = t0 >> logP;
-    const int np = ((t0 + n - 1) >> logP) - p0 + 1;
+    const int p0 = tb >> logP;
+    const int np = ((tb + n - 1) >> logP) - p0 + 1;
     for (int i = lane; i < np; i += 64)
-        pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
-                   << logP;
-    for (int i = lane; i < (HR - GB) * NB; i += 64) wbuf[GB + i / NB][i % NB] = 0.0f;
+        sh.pbase[i] = ((uint32_t)g.page_table[(size_t)b * g.max_pages + p0 + i] * (uint32_t)p.c.Hkv + (uint32_t)kvh)
+                      << logP;
+    sh.wbuf[GB][lane] = 0.0f;
     QueryState<MF4 ? 1 : GB> qs;  // wave-uniform: scalar loads into SGPRs (dot8 products)
     float c0[GB], c1[GB];
     v4f_t msu = {0.0f, 0.0f, 0.0f, 0.0f};  // the matrix-core products' accumulator start
@@ -1354,29 +1374,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
         }
     }
     if constexpr (MF4) {
-        if (lane < 32) qa_s[lane] = reinterpret_cast<const uint4 *>(p.qa + (size_t)bh0 * kD)[lane];
-        else if (lane < 34) qa_s[lane] = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < 32) sh.qa[lane] = reinterpret_cast<const uint4 *>(p.qa + (size_t)bh0 * kD)[lane];
+        else if (lane < 34) sh.qa[lane] = make_uint4(0u, 0u, 0u, 0u);
     }
-    __syncthreads();
+    wave_lds_sync();
     // A operand of key-product tile t: query head lane & 3 in row lane & 15 of tile
     // (lane & 15) >> 2, its 32 codes of K block lane >> 4; zeros in the other tiles
     const int qrow = 8 * (lane & 3) + 2 * (lane >> 4), qtile = (lane & 15) >> 2;
 
     const int r16 = lane & 15, kb = lane >> 4;
     const int ha = r16 / NG, ga = r16 % NG;  // the lane's A row
+    const int hw = ha < GB ? ha : GB;        // its weight row (the zero row past GB)
     const int vw = 4 * r16;                  // its code word: dims 8 r16 .. 8 r16 + 7
     const int vz = kD / 2 + 4 * ga;          // the scale/zero word of its A row's group
     const uint32_t tmask = (1u << logP) - 1u;
     const uint32_t c128 = 0x43004300u;       // two bfloat16 128s
     const bf16x8_t b128 = as_bf16x8(c128, c128, c128, c128);
-    v4f_t acc[9];
 #pragma unroll
-    for (int j = 0; j < 9; ++j) acc[j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float zacc = 0.0f, lsum[GB], mrun[GB];
+    for (int j = 0; j < 9; ++j) st.acc[j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    st.zacc = 0.0f;
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
-        lsum[h] = 0.0f;
-        mrun[h] = -INFINITY;
+        st.lsum[h] = 0.0f;
+        st.mrun[h] = -INFINITY;
     }
     const float lazy = 8.0f / p.klog;  // score units of a factor 2^8 in weight
 
@@ -1391,8 +1411,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
             // consecutive slots, one address per lane and fixed offsets.  Slots past the
             // sequence's end are read but get no weight, and their scale/zero words are
             // cleared below, so that whatever they hold stays out of the sums.
-            const uint32_t first = (uint32_t)(t0 + bs);
-            const uint32_t s0 = pbase[(first >> logP) - p0] + (first & tmask);
+            const uint32_t first = (uint32_t)(tb + bs);
+            const uint32_t s0 = sh.pbase[(first >> logP) - p0] + (first & tmask);
             load_key_t<KW>(p.c, s0 + lane, kbw, nc);
             const uint8_t *vr = p.c.vals + (size_t)(s0 + 8 * kb) * VREC;
             const uint32_t *cwp = reinterpret_cast<const uint32_t *>(vr + vw);
@@ -1414,15 +1434,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
         } else {
             // tokens past nb re-read the last one
             {
-                const uint32_t t = (uint32_t)(t0 + bs + min(lane, nb - 1));
-                load_key_t<KW>(p.c, pbase[(t >> logP) - p0] + (t & tmask), kbw, nc);
+                const uint32_t t = (uint32_t)(tb + bs + min(lane, nb - 1));
+                load_key_t<KW>(p.c, sh.pbase[(t >> logP) - p0] + (t & tmask), kbw, nc);
             }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const uint32_t t = (uint32_t)(t0 + bs + min(32 * kt + 8 * kb + i, nb - 1));
-                    const uint8_t *vr = p.c.vals + (size_t)(pbase[(t >> logP) - p0] + (t & tmask)) * VREC;
+                    const uint32_t t = (uint32_t)(tb + bs + min(32 * kt + 8 * kb + i, nb - 1));
+                    const uint8_t *vr = p.c.vals + (size_t)(sh.pbase[(t >> logP) - p0] + (t & tmask)) * VREC;
                     cw[8 * kt + i] = *reinterpret_cast<const uint32_t *>(vr + vw);
                     szw[8 * kt + i] = *reinterpret_cast<const uint32_t *>(vr + vz);
                 }
@@ -1434,7 +1454,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const float fP = (float)(2 * pc - 32 * KW);
             const float r = norm_over_corr(nc);
             const v4f_t d = key_products4(kbw, msu, [&](int t) {
-                const uint4 *q = &qa_s[qtile == t ? qrow : 32];
+                const uint4 *q = &sh.qa[qtile == t ? qrow : 32];
                 const uint4 a0 = q[0], a1 = q[1];
                 return v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             });
@@ -1454,10 +1474,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
             // past the batch, or a marked record (a token held in the high-precision tier)
             if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
             scl[h] = 1.0f;
-            if (__any(s[h] > mrun[h] + lazy)) {  // the first finite score always moves it
+            if (__any(s[h] > st.mrun[h] + lazy)) {  // the first finite score always moves it
                 const float mnew = wave_max_u(s[h]);
-                scl[h] = (mrun[h] == -INFINITY) ? 0.0f : exp2f((mrun[h] - mnew) * p.klog);
-                mrun[h] = mnew;
+                scl[h] = (st.mrun[h] == -INFINITY) ? 0.0f : exp2f((st.mrun[h] - mnew) * p.klog);
+                st.mrun[h] = mnew;
                 grow = true;
             }
         }
@@ -1474,34 +1494,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
 #pragma unroll
             for (int j = 0; j < 9; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[j][i] *= f[i];
+                for (int i = 0; i < 4; ++i) st.acc[j][i] *= f[i];
             float fz = 1.0f;
 #pragma unroll
             for (int h = 0; h < GB; ++h) fz = ha == h ? scl[h] : fz;
-            zacc *= fz;
+            st.zacc *= fz;
 #pragma unroll
-            for (int h = 0; h < GB; ++h) lsum[h] *= scl[h];
+            for (int h = 0; h < GB; ++h) st.lsum[h] *= scl[h];
         }
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             // v_exp_f32 (exp2(-inf) = 0); no weight while the head has no finite score
-            const float w = (mrun[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s[h] - mrun[h]) * p.klog);
-            lsum[h] += w;
-            wbuf[h][lane] = w;
+            const float w = (st.mrun[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s[h] - st.mrun[h]) * p.klog);
+            st.lsum[h] += w;
+            sh.wbuf[h][lane] = w;
         }
-        __syncthreads();
+        wave_lds_sync();
         // ---- two 32-token steps on the matrix cores
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const float4 wa = *reinterpret_cast<const float4 *>(&wbuf[ha][32 * kt + 8 * kb]);
-            const float4 wb = *reinterpret_cast<const float4 *>(&wbuf[ha][32 * kt + 8 * kb + 4]);
+            const float4 wa = *reinterpret_cast<const float4 *>(&sh.wbuf[hw][32 * kt + 8 * kb]);
+            const float4 wb = *reinterpret_cast<const float4 *>(&sh.wbuf[hw][32 * kt + 8 * kb + 4]);
             const float w8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t sz = szw[8 * kt + i];
                 x[i] = w8[i] * half_bits_to_float(sz & 0xFFFFu);
-                zacc = fmaf(w8[i], half_bits_to_float(sz >> 16), zacc);
+                st.zacc = fmaf(w8[i], half_bits_to_float(sz >> 16), st.zacc);
             }
             uint32_t ah[4], al[4];
 #pragma unroll
@@ -1522,47 +1542,76 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 }
                 const bf16x8_t Blo = as_bf16x8(lo[0], lo[1], lo[2], lo[3]);
                 const bf16x8_t Bhi = as_bf16x8(hi[0], hi[1], hi[2], hi[3]);
-                acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Blo, acc[2 * k], 0, 0, 0);
-                acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bhi, acc[2 * k + 1], 0, 0, 0);
-                acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Blo, acc[2 * k], 0, 0, 0);
-                acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bhi, acc[2 * k + 1], 0, 0, 0);
+                st.acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Blo, st.acc[2 * k], 0, 0, 0);
+                st.acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, Bhi, st.acc[2 * k + 1], 0, 0, 0);
+                st.acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Blo, st.acc[2 * k], 0, 0, 0);
+                st.acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, Bhi, st.acc[2 * k + 1], 0, 0, 0);
             }
-            acc[8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, b128, acc[8], 0, 0, 0);
-            acc[8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, b128, acc[8], 0, 0, 0);
+            st.acc[8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, b128, st.acc[8], 0, 0, 0);
+            st.acc[8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, b128, st.acc[8], 0, 0, 0);
         }
-        __syncthreads();  // wbuf is rewritten by the next batch
+        wave_lds_sync();  // wbuf is rewritten by the next batch
     }
+}
 
-    // ---- weight sums; zero-point sums of each A row over its 4 token blocks (lanes r16 + 16 k)
-    const size_t pidx = (size_t)bh0 * g.NCA + chunk;  // partial of head bh0 (+ h * NCA)
-    zacc += __shfl_xor(zacc, 16);
-    zacc += __shfl_xor(zacc, 32);
-#pragma unroll
-    for (int h = 0; h < GB; ++h) {
-        const float l = wave_sum(lsum[h]);
-        if (lane == 0) {
-            p.pm[pidx + (size_t)h * g.NCA] = mrun[h];
-            p.pl[pidx + (size_t)h * g.NCA] = l;
-        }
-    }
-    // lane l holds columns r16 (dims 8 r16 + j of tile j) of rows 4 kb + i; the rows of the
-    // dims' own group are i = gd (NG = 4) or i = gd, gd + 2 (NG = 2)
+// The value sums of a finished pass: out(h, d0, o) receives o[j] = sum_t w_h(t) v_t[d0 + j],
+// j < 8, for every head and 8-dim block the lane holds (each (head, block) once in the wave).
+// Lane l holds columns l mod 16 (dims 8 (l mod 16) + j of tile j) of rows 4 (l / 16) + i; the
+// rows of the dims' own group are i = gd (NG = 4) or i = gd, gd + 2 (NG = 2).
+template <int GB, int GV, typename Out>
+__device__ __forceinline__ void mf_outputs(MfState<GB> &st, Out out)
+{
+    constexpr int NG = kD / GV;
+    const int lane = threadIdx.x & 63, r16 = lane & 15, kb = lane >> 4;
+    // zero-point sums of each A row over its 4 token blocks (lanes r16 + 16 k)
+    float z = st.zacc;
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
     const int gd = (8 * r16) / GV;
 #pragma unroll
     for (int q = 0; q < 4 / NG; ++q) {
         const int i = gd + NG * q;
         const int row = 4 * kb + i, h = row / NG;
-        const float z = __shfl(zacc, row);  // lanes row, row + 16, ... hold the row's sum
+        const float zr = __shfl(z, row);  // lanes row, row + 16, ... hold the row's sum
         if (h < GB) {
-            const float c = pick4(acc[8], i);
+            const float c = pick4(st.acc[8], i);
             float o[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = (pick4(acc[j], i) - c) + z;
-            float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + 8 * r16);
-            dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+            for (int j = 0; j < 8; ++j) o[j] = (pick4(st.acc[j], i) - c) + zr;
+            out(h, 8 * r16, o);
         }
     }
+}
+
+template <int GB, int GV, int KW, bool PAGE64>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_full_mf(AttendParams p)
+{
+    __shared__ MfShared<GB, kMaxFullChunk / 16 + 1> sh;
+    const DecodeGeom &g = p.g;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    int kvh, hq0;
+    block_heads(g, blockIdx.y, kvh, hq0);
+    const int L = g.seq_lens[b];
+    const int t0 = chunk * g.CH;
+    if (t0 >= L) return;
+    const int n = min(g.CH, L - t0);
+    const int bh0 = b * g.Hq + hq0;
+    MfState<GB> st;
+    mf_pass<GB, GV, KW, PAGE64>(p, b, kvh, bh0, t0, n, sh, st);
+    const size_t pidx = (size_t)bh0 * g.NCA + chunk;  // partial of head bh0 (+ h * NCA)
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        const float l = wave_sum(st.lsum[h]);
+        if (threadIdx.x == 0) {
+            p.pm[pidx + (size_t)h * g.NCA] = st.mrun[h];
+            p.pl[pidx + (size_t)h * g.NCA] = l;
+        }
+    }
+    mf_outputs<GB, GV>(st, [&](int h, int d0, const float (&o)[8]) {
+        float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + d0);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1592,16 +1641,6 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
     const int r = k == 4 ? __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true)
                          : __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true);
     return __int_as_float(r);
-}
-
-// LDS ordering among the lanes of one wave (the attention waves of a block share no data):
-// a wave's LDS operations complete in order, so fences at wavefront scope, which keep the
-// compiler from moving LDS accesses across this point, are all that is needed.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of one head
