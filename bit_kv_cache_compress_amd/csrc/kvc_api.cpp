@@ -45,6 +45,7 @@ struct Plan {
     kvc::DecodeGeom g;
     bool topp;
     int nsplit, cps;
+    int hist_fused;  // the histogram and threshold passes in one kernel (k_hist_thresh)
     size_t off_qpl, off_qa, off_qpar, off_lmax, off_dl, off_hist, off_sel, off_cnt, off_order, off_octr, off_pm, off_pl, off_po, off_tm, off_tl, off_to;
     size_t total;
 };
@@ -118,6 +119,9 @@ void plan_layout(Plan &pl, int BH)
         }
         pl.nsplit = nsplit;
         pl.cps = cps;
+        // one block per head counts all its tokens and thresholds them: when the heads alone
+        // give at least 128 blocks and a head's score chunks fit one per thread
+        pl.hist_fused = BH >= 128 && pl.g.NC <= 1024;
         pl.off_lmax = take((size_t)BH * NC * 4);
         pl.off_dl = take((size_t)BH * pl.g.Lpad * 2);
         pl.off_hist = take((size_t)BH * nsplit * 8192 * 2);
@@ -126,7 +130,7 @@ void plan_layout(Plan &pl, int BH)
         pl.off_order = take((size_t)BH * 4);
         pl.off_octr = take(2 * 4);
     } else {
-        pl.nsplit = pl.cps = 0;
+        pl.nsplit = pl.cps = pl.hist_fused = 0;
         pl.off_lmax = pl.off_dl = pl.off_hist = pl.off_sel = pl.off_cnt = pl.off_order = pl.off_octr = 0;
     }
     pl.total = o;
@@ -430,6 +434,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     qp.dither = dither;
     qp.app_blocks = 0;
     qp.app_N = 0;
+    qp.order_ctr = pl.topp ? at<int32_t>(workspace, pl.off_octr) : nullptr;
     if (app) {
         rc = make_append(c, app->dtype, app->k, app->v, B, app->n_new, app->start_pos, page_table, max_pages, qp.app);
         if (rc) return rc;
@@ -502,6 +507,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
         hp.g = pl.g;
         hp.nsplit = pl.nsplit;
         hp.cps = pl.cps;
+        hp.fused = pl.hist_fused;
         hp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
         hp.dl = sp.dl;
         hp.lmax = sp.lmax;
@@ -816,6 +822,7 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     hp.g = pl.g;
     hp.nsplit = pl.nsplit;
     hp.cps = pl.cps;
+    hp.fused = pl.hist_fused;
     hp.pfx = (uint32_t)rint((double)top_p * 16777216.0);
     hp.dl = bp.dl;
     hp.lmax = bp.lmax;

@@ -270,6 +270,10 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
     }
     if (threadIdx.x >= kD) return;  // whole waves: blocks of 256 threads when a tail runs alongside
     const int bh = blockIdx.x, r = threadIdx.x;
+    if (p.order_ctr && (bh | r) == 0) {  // the dispatch slots of the threshold pass, two kernels on
+        p.order_ctr[0] = 0;
+        p.order_ctr[1] = 0;
+    }
     const int lane = r & 63, wave = r >> 6;
     const float *q = p.q + (size_t)bh * kD;
     float x;
@@ -871,76 +875,15 @@ __device__ __forceinline__ void order_head(const HistParams &p, size_t bh, int k
     if (slot >= 0 && slot < BH) p.order[slot] = (int)bh | (ls << 24);
 }
 
-// Top-p threshold of each (b, h) from the split counts: one 1024-thread block per (query
-// head, sequence), thread t owns bins 8t .. 8t+7.  A kernel of its own, so that the split
-// counts reach it through the kernel boundary rather than through device-scope fences in
-// every histogram block.  With W(d) = T[d mod 256] >> (d / 256), T[j] = round(2^(32 - j/256)):
-//   Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
-//   b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p },  count = sum_{d <= b*} cnt[d].
-// One block scan carries both the weighted sums and the counts, so the thread whose bins
-// hold b* writes the result without a further pass.
-__global__ __launch_bounds__(1024) void k_thresh(HistParams p)
+// The threshold of head bh from its bin counts (thread t: bins 8t .. 8t + 7), e_max and the
+// sequence length L > 0, in a 1024-thread block: the weighted block scan and the writes
+// described at k_thresh.  T holds the 256 weights (published by a barrier before the call);
+// wsum, csum and imax are block scratch, imax already holding each wave's top bin.
+__device__ __forceinline__ void thresh_finish(const HistParams &p, size_t bh, int L, const uint32_t (&cnt)[8],
+                                              const uint64_t *T, uint64_t *wsum, int *csum, const int *imax)
 {
     constexpr int kT = 1024;
-    __shared__ uint64_t T[256];
-    __shared__ uint64_t wsum[kT / 64];
-    __shared__ int csum[kT / 64];
-    __shared__ int imax[kT / 64];
-    const DecodeGeom &g = p.g;
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t bh = (size_t)b * g.Hq + h;
-    // counts of bins 8 tid .. 8 tid + 7 summed over the splits (8 splits' loads in flight).
-    // The first 8 splits and the top bins of the first 1024 chunks are read within the
-    // planned bounds before the length is known; splits and chunks past it are masked below.
-    const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + bh * p.nsplit * kBins) + tid;
-    uint4 v0[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v0[k] = k < p.nsplit ? src[(size_t)k * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
-    const int mfirst = tid < g.NC ? p.lmax[bh * g.NC + tid] : -kBinClamp;
-    // the weight table, while those loads are in flight (published by the barrier below)
-    if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
-    const int L = g.seq_lens[b];
-    if (L <= 0) {
-        if (tid == 0) {
-            if (p.order) order_head(p, bh, 0, 0);
-            p.sel[bh * 4 + 0] = 0;
-            p.sel[bh * 4 + 1] = -1;
-            p.sel[bh * 4 + 2] = 0;
-            if (p.dbg_count) p.dbg_count[bh] = 0;
-            if (p.dbg_bins) {
-                p.dbg_bins[bh * 2] = 0;
-                p.dbg_bins[bh * 2 + 1] = -1;
-            }
-        }
-        return;
-    }
-    const int nch = (L + g.CH - 1) >> g.logCH;
-    const int nsu = (nch + p.cps - 1) / p.cps;  // splits that hold tokens
-    int m = tid < nch ? mfirst : -kBinClamp;
-    uint32_t cnt[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) cnt[k] = 0u;
-    for (int s0 = 0; s0 < nsu; s0 += 8) {
-        uint4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (s0 == 0) v[k] = k < nsu ? v0[k] : make_uint4(0u, 0u, 0u, 0u);
-            else v[k] = (s0 + k < nsu) ? src[(size_t)(s0 + k) * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                cnt[2 * q] += w[q] & 0xFFFFu;
-                cnt[2 * q + 1] += w[q] >> 16;
-            }
-        }
-    }
-    for (int c = tid + kT; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
-    m = wave_max_i(m);
-    if (lane == 0) imax[wave] = m;
-    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // d >> 8 is the same for all 8 bins of a thread
     const int shift = tid >> 5;
     uint64_t mine = 0;
@@ -1019,6 +962,166 @@ __global__ __launch_bounds__(1024) void k_thresh(HistParams p)
             p.dbg_bins[bh * 2 + 1] = bstar;
         }
     }
+}
+
+// Top-p threshold of each (b, h) from the split counts: one 1024-thread block per (query
+// head, sequence), thread t owns bins 8t .. 8t+7.  A kernel of its own, so that the split
+// counts reach it through the kernel boundary rather than through device-scope fences in
+// every histogram block.  With W(d) = T[d mod 256] >> (d / 256), T[j] = round(2^(32 - j/256)):
+//   Z = sum_d cnt[d] W(d),  T_p = ceil(Z * pfx / 2^24),
+//   b* = min { b : sum_{d <= b} cnt[d] W(d) >= T_p },  count = sum_{d <= b*} cnt[d].
+// One block scan carries both the weighted sums and the counts, so the thread whose bins
+// hold b* writes the result without a further pass.
+__global__ __launch_bounds__(1024) void k_thresh(HistParams p)
+{
+    constexpr int kT = 1024;
+    __shared__ uint64_t T[256];
+    __shared__ uint64_t wsum[kT / 64];
+    __shared__ int csum[kT / 64];
+    __shared__ int imax[kT / 64];
+    const DecodeGeom &g = p.g;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t bh = (size_t)b * g.Hq + h;
+    // counts of bins 8 tid .. 8 tid + 7 summed over the splits (8 splits' loads in flight).
+    // The first 8 splits and the top bins of the first 1024 chunks are read within the
+    // planned bounds before the length is known; splits and chunks past it are masked below.
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.hist + bh * p.nsplit * kBins) + tid;
+    uint4 v0[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v0[k] = k < p.nsplit ? src[(size_t)k * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
+    const int mfirst = tid < g.NC ? p.lmax[bh * g.NC + tid] : -kBinClamp;
+    // the weight table, while those loads are in flight (published by the barrier below)
+    if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
+    const int L = g.seq_lens[b];
+    if (L <= 0) {
+        if (tid == 0) {
+            if (p.order) order_head(p, bh, 0, 0);
+            p.sel[bh * 4 + 0] = 0;
+            p.sel[bh * 4 + 1] = -1;
+            p.sel[bh * 4 + 2] = 0;
+            if (p.dbg_count) p.dbg_count[bh] = 0;
+            if (p.dbg_bins) {
+                p.dbg_bins[bh * 2] = 0;
+                p.dbg_bins[bh * 2 + 1] = -1;
+            }
+        }
+        return;
+    }
+    const int nch = (L + g.CH - 1) >> g.logCH;
+    const int nsu = (nch + p.cps - 1) / p.cps;  // splits that hold tokens
+    int m = tid < nch ? mfirst : -kBinClamp;
+    uint32_t cnt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cnt[k] = 0u;
+    for (int s0 = 0; s0 < nsu; s0 += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (s0 == 0) v[k] = k < nsu ? v0[k] : make_uint4(0u, 0u, 0u, 0u);
+            else v[k] = (s0 + k < nsu) ? src[(size_t)(s0 + k) * (kBins / 8)] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cnt[2 * q] += w[q] & 0xFFFFu;
+                cnt[2 * q + 1] += w[q] >> 16;
+            }
+        }
+    }
+    for (int c = tid + kT; c < nch; c += kT) m = max(m, p.lmax[bh * g.NC + c]);
+    m = wave_max_i(m);
+    if (lane == 0) imax[wave] = m;
+    __syncthreads();
+    thresh_finish(p, bh, L, cnt, T, wsum, csum, imax);
+}
+
+// ---------------------------------------------------------------------------------------
+// Histogram and threshold in one kernel, for heads whose sequence has at most 1024 score
+// chunks when there are enough heads to give each a block: the block counts every token of
+// its head in LDS (four 16-byte loads per thread and round, the next round's in flight) and
+// runs the threshold scan of k_thresh on those counts, so that no split counts go through
+// HBM and no second launch is needed.  The dispatch slots were cleared by the query pass.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kHistThreads) void k_hist_thresh(HistParams p)
+{
+    constexpr int kT = kHistThreads, U = 4;
+    constexpr int kStep = 8 * kT * U;  // tokens per round
+    __shared__ uint32_t hist[kBins];
+    __shared__ int delta[kT];
+    __shared__ uint64_t T[256];
+    __shared__ uint64_t wsum[kT / 64];
+    __shared__ int csum[kT / 64];
+    __shared__ int imax[kT / 64];
+    const DecodeGeom &g = p.g;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const size_t bh = (size_t)b * g.Hq + h;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int L = g.seq_lens[b];
+    const uint16_t *row = p.dl + bh * g.Lpad;
+    // the first round's distances (the row holds whole chunks: reads up to Lpad stay in it;
+    // tokens past L are not counted) and the chunk top bins, issued together
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int t = 8 * tid + 8 * kT * u;
+        raw[u] = t < g.Lpad ? *reinterpret_cast<const uint4 *>(row + t) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int nch = L > 0 ? (L + g.CH - 1) >> g.logCH : 0;  // <= kT (the plan's condition)
+    const int lmc = tid < nch ? p.lmax[bh * g.NC + tid] : -kBinClamp;
+    if (tid < 256) T[tid] = (uint64_t)rint(ldexp(exp2(-(double)tid / 256.0), 32));
+    for (int i = tid; i < kBins; i += kT) hist[i] = 0u;
+    const int m = wave_max_i(lmc);
+    if (lane == 0) imax[wave] = m;
+    __syncthreads();
+    if (L <= 0) {  // uniform
+        if (tid == 0) {
+            if (p.order) order_head(p, bh, 0, 0);
+            p.sel[bh * 4 + 0] = 0;
+            p.sel[bh * 4 + 1] = -1;
+            p.sel[bh * 4 + 2] = 0;
+            if (p.dbg_count) p.dbg_count[bh] = 0;
+            if (p.dbg_bins) {
+                p.dbg_bins[bh * 2] = 0;
+                p.dbg_bins[bh * 2 + 1] = -1;
+            }
+        }
+        return;
+    }
+    int emax = imax[0];
+#pragma unroll
+    for (int w = 1; w < kT / 64; ++w) emax = max(emax, imax[w]);
+    if (tid < nch) delta[tid] = emax - lmc;
+    __syncthreads();
+    for (int t = 8 * tid; t < L; t += kStep) {
+        uint4 nxt[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tn = t + kStep + 8 * kT * u;
+            if (tn < L) nxt[u] = *reinterpret_cast<const uint4 *>(row + tn);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tu = t + 8 * kT * u;
+            if (tu < L) {
+                const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                const int dc = delta[tu >> g.logCH];  // 8 tokens share a chunk
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int d = dc + (int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                    if (tu + e < L && d < kBins) atomicAdd(&hist[d], 1u);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = nxt[u];
+    }
+    __syncthreads();
+    uint32_t cnt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cnt[k] = hist[8 * tid + k];
+    thresh_finish(p, bh, L, cnt, T, wsum, csum, imax);
 }
 
 // Bin-distance threshold of a chunk: token kept when its distance to the chunk top bin is
@@ -2354,6 +2457,10 @@ hipError_t launch_bin_scores(const BinScoresParams &p, hipStream_t s)
 
 hipError_t launch_hist(const HistParams &p, hipStream_t s)
 {
+    if (p.fused) {
+        KVC_LAUNCH(k_hist_thresh, dim3(p.g.Hq, p.g.B), dim3(kHistThreads), s, p);
+        return hipGetLastError();
+    }
     KVC_LAUNCH(k_hist, dim3(p.nsplit, p.g.Hq, p.g.B), dim3(kHistThreads), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -118,6 +118,7 @@ struct QprepParams {
     const float *dither;   // nullable [B*Hq][128]: uniforms of the stochastic rounding
     int has_tail;          // blocks BH .. 2 BH - 1 attend over the binary16 tail
     TailParams tail;
+    int32_t *order_ctr;    // nullable [2]: cleared for the threshold pass's dispatch slots
     long app_blocks;       // 0, or the blocks after those that encode new tokens (fused append)
     long app_N;            // token-heads to encode
     AppendParams app;
@@ -167,6 +168,7 @@ struct BinScoresParams {
 struct HistParams {
     DecodeGeom g;
     int nsplit, cps;       // splits per (b,h), chunks per split
+    int fused;             // one block per head counts and thresholds (k_hist_thresh)
     uint32_t pfx;          // rint(p * 2^24)
     const uint16_t *dl;
     const int32_t *lmax;

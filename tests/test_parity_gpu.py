@@ -1045,10 +1045,10 @@ def test_topp_dispatch_classes_poisoned_workspace():
 
 @pytest.mark.parametrize("scores", [True, False])
 def test_topp_many_heads_ragged(scores):
-    """128 query heads (4 sequences of 32) with ragged lengths and an empty sequence: top bins,
-    thresholds, counts and index sets equal the oracle's bit for bit, outputs within the
-    tolerance, twice in a row on one workspace; scores=True runs the debug score kernel, the
-    other the matrix-core one."""
+    """128 query heads (4 sequences of 32, enough heads for the one-kernel histogram and
+    threshold pass) with ragged lengths and an empty sequence: top bins, thresholds, counts and
+    index sets equal the oracle's bit for bit, outputs within the tolerance, twice in a row on
+    one workspace; scores=True runs the debug score kernel, the other the matrix-core one."""
     wl = W.CONFIGS[2].scaled(B=4, Hq=32, Hkv=8, P=256)
     lens = [0, 1, 3001, 8192]
     c = Case(wl, L=max(lens), seq_lens=lens)
