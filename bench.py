@@ -284,7 +284,7 @@ def run_append(args):
     key_bytes, vb = 20, value_bytes(Gv)
     alg = th * (2 * D * 2 + key_bytes + vb)
     ach = alg / (ms / 1e3) / 1e9
-    kern = "k_append_hadamard" if kind != "dense" else "k_append_mfma<true>"
+    kern = "k_append_hadamard" if kind != "dense" else "k_append_mfma"
     log(f"[bench] append {ms * 1e3:.1f} us (median {statistics.median(step_ms) * 1e3:.1f}); {value:.3e} "
         f"token-heads/s; {ach:.0f} GB/s algorithmic = {100 * ach / HBM_PEAK_GBS:.1f}% of peak")
     result = {

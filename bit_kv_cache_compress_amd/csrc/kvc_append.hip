@@ -3,10 +3,12 @@
 //
 // Method: "H1B-KV" (key design: 1-bit key sketch by random projection, 4-bit linear value
 // quantization) with the randomized rotation of "RaBitQCache" (abstract).  The sign of each
-// rotated coordinate is decided on the exact product: for binary16 (and, in practice,
-// binary32) inputs every partial sum of R k is exact in binary64, so the kernels rotate in
-// binary64 -- a butterfly for the randomized Hadamard rotation and binary64 MFMA for the
-// dense one -- and their sign bits do not depend on the summation order.
+// rotated coordinate is the sign of the exact product: for binary16 (and, in practice,
+// binary32) inputs every partial sum of R k is exact in binary64.  The randomized Hadamard
+// rotation runs its butterflies in binary64; the dense rotation of large appends of binary16
+// keys runs on the fp16 matrix cores with a rigorous error bound per coordinate and a
+// binary64 sum for the few coordinates inside it (k_append_mfma); the other dense appends
+// rotate in binary64 (MFMA f64, or fp64 fma chains for a few keys).
 #include "kvc_append_dev.h"
 
 namespace kvc {
@@ -142,16 +144,14 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
 }
 
 // ---------------------------------------------------------------------------------------
-// Rotation on the matrix cores, for binary16 keys without key centers: 16 token-heads per
-// wave, k' = R k as v_mfma_f32_16x16x32_f16 with the keys as A (16 tokens x 128 dims) and the
-// rotation as B (B[j][o] = R[o][j]; for the randomized Hadamard rotation H[o][j] sigma_j = +-1,
-// and k' = (H sigma k) / sqrt(D) has the signs of the product).  Binary16 products are exact
-// in binary32, so the only error of an output is that of its binary32 sums: at most
-// gamma_128 = 128 u / (1 - 128 u) < 7.7e-6 (u = 2^-24) times sum_j |R_oj k_j|, whatever order
-// the matrix core adds in.  A coordinate whose |k'_o| exceeds 1e-5 times that sum has the
-// sign of the exact product; the others (rare) take the exact sign from a binary64 sum of the
-// 128 products over the wave's lanes.  sum_j |R_oj k_j| is |k|_1 for the Hadamard rotation,
-// and the product of |R| and |k| on the matrix cores for the dense one.
+// Dense rotation on the matrix cores, for binary16 keys without key centers: 16 token-heads
+// per wave, k' = R k as v_mfma_f32_16x16x32_f16 with the keys as A (16 tokens x 128 dims) and
+// the rotation as B (B[j][o] = R[o][j]).  Binary16 products are exact in binary32, so the only
+// error of an output is that of its binary32 sums: at most gamma_128 = 128 u / (1 - 128 u)
+// < 7.7e-6 (u = 2^-24) times sum_j |R_oj k_j|, whatever order the matrix core adds in.  A
+// coordinate whose |k'_o| exceeds 1e-5 times that sum (the product of |R| and |k|, a second
+// MFMA chain on the magnitudes) has the sign of the exact product; the others (rare) take the
+// exact sign from a binary64 sum of the 128 products over the wave's lanes.
 // The token-heads are taken head by head (n = (b Hkv + h) n_new + t), so that a wave's 16
 // records are consecutive slots of a page, written whole.  sum |k'| (for the correction) is
 // the binary32 sum of the matrix-core outputs, within 1e-5 relative of the binary64 one.
@@ -195,7 +195,6 @@ __device__ __forceinline__ void token_at(const AppendParams &p, uint32_t n, size
     slot = ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
 }
 
-template <bool DENSE>
 __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
 {
     __shared__ __align__(16) uint16_t Bt[kD * kBS];  // Bt[o][j] = B[j][o]
@@ -206,22 +205,7 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int c = tid; c < kD * kD / 8; c += 256) {
         const int o = c >> 4, q = c & 15;  // row o, halves 8 q .. 8 q + 7
-        uint4 v;
-        if constexpr (DENSE) {
-            v = reinterpret_cast<const uint4 *>(p.rot)[c];
-        } else {
-            const uint32_t sg = reinterpret_cast<const uint32_t *>(p.rot)[q >> 2];
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j0 = 8 * q + 2 * e, j1 = j0 + 1;
-                const uint32_t n0 = (__builtin_popcount(o & j0) + (sg >> (j0 & 31))) & 1u;
-                const uint32_t n1 = (__builtin_popcount(o & j1) + (sg >> (j1 & 31))) & 1u;
-                w[e] = (0x3C00u | (n0 << 15)) | ((0x3C00u | (n1 << 15)) << 16);
-            }
-            v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        *reinterpret_cast<uint4 *>(&Bt[o * kBS + 8 * q]) = v;
+        *reinterpret_cast<uint4 *>(&Bt[o * kBS + 8 * q]) = reinterpret_cast<const uint4 *>(p.rot)[c];
     }
     __syncthreads();
     const uint16_t *K = reinterpret_cast<const uint16_t *>(p.k);
@@ -244,9 +228,7 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4 *>(p.c.kf16 + slotA * kD + 32 * ks + 8 * kb) = a[ks];
         }
-        // |k|_1 (binary32) and |k|^2 (binary64) of token m: this lane's 32 dims, then lanes
-        // m, m + 16, m + 32, m + 48
-        float l1 = 0.0f;
+        // |k|^2 (binary64) of token m: this lane's 32 dims, then lanes m, m + 16, m + 32, m + 48
         double ss = 0.0;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -254,29 +236,25 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                l1 += fabsf(x);
                 ss = fma((double)x, (double)x, ss);
             }
         }
-        l1 += xor_lane(l1, 16);
-        l1 += xor_lane(l1, 32);
         ss += xor_lane_d(ss, 16);
         ss += xor_lane_d(ss, 32);
         if (kb == 0) ss_s[wave][m] = ss;
         // the products: acc[nt] holds out dim 16 nt + m of tokens 4 kb + i in element i
-        f32x4_t acc[8], aab[DENSE ? 8 : 1];
+        // (and in aab[nt] the bound's sum of |R_oj k_j|)
+        f32x4_t acc[8], aab[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             acc[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (DENSE) aab[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+            aab[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
         }
-        uint4 aabs[DENSE ? 4 : 1];
-        if constexpr (DENSE) {
+        uint4 aabs[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                aabs[ks] = make_uint4(a[ks].x & 0x7FFF7FFFu, a[ks].y & 0x7FFF7FFFu, a[ks].z & 0x7FFF7FFFu,
-                                      a[ks].w & 0x7FFF7FFFu);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            aabs[ks] = make_uint4(a[ks].x & 0x7FFF7FFFu, a[ks].y & 0x7FFF7FFFu, a[ks].z & 0x7FFF7FFFu,
+                                  a[ks].w & 0x7FFF7FFFu);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             uint4 bw[4];
@@ -286,18 +264,13 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ks]), as_half8(bw[ks]), acc[nt], 0, 0, 0);
-                if constexpr (DENSE) {
-                    const uint4 babs = make_uint4(bw[ks].x & 0x7FFF7FFFu, bw[ks].y & 0x7FFF7FFFu,
-                                                  bw[ks].z & 0x7FFF7FFFu, bw[ks].w & 0x7FFF7FFFu);
-                    aab[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(aabs[ks]), as_half8(babs), aab[nt], 0, 0, 0);
-                }
+                const uint4 babs = make_uint4(bw[ks].x & 0x7FFF7FFFu, bw[ks].y & 0x7FFF7FFFu,
+                                              bw[ks].z & 0x7FFF7FFFu, bw[ks].w & 0x7FFF7FFFu);
+                aab[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(aabs[ks]), as_half8(babs), aab[nt], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);  // one output tile's operands at a time
         }
         // signs, certified against the bound; sum |k'| over the sketch's dims
-        float bnd[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bnd[i] = 1e-5f * __int_as_float(__builtin_amdgcn_ds_bpermute((4 * kb + i) << 2, __float_as_int(l1)));
         // the 32 sign ballots (and, when some coordinate is uncertain, the 32 uncertainty
         // ballots) go to LDS from lanes 0..31, ballot k = 4 nt + i in lane k
         uint64_t any = 0;
@@ -308,7 +281,7 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float v = acc[nt][i];
-                const float b = DENSE ? 1e-5f * aab[DENSE ? nt : 0][i] : bnd[i];
+                const float b = 1e-5f * aab[nt][i];
                 const uint64_t sg = __builtin_amdgcn_ballot_w64(!(v < 0.0f));
                 const uint64_t un = __builtin_amdgcn_ballot_w64(!(fabsf(v) > b));
                 const bool mine = lane == 4 * nt + i;
@@ -369,7 +342,7 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
             uint32_t *kr = key_rec(p.c, slotV);
             if (jv < p.c.kw) kr[jv] = lo | (hi << 16);
             if (jv == 0) {
-                const double sabs = (double)sab_s[wave][tv] / (DENSE ? 1.0 : sqrt((double)kD));
+                const double sabs = (double)sab_s[wave][tv];
                 kr[p.c.kw] = norm_corr_word(ss_s[wave][tv], sabs, p.c.sk);
             }
             float x[32];
@@ -420,7 +393,7 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s)
     if (mfma) {
         const long mblocks = ((N + 15) / 16 + 3) / 4;
         const unsigned blocks = (unsigned)(mblocks < 1024 ? mblocks : 1024);
-        KVC_LAUNCH(k_append_mfma<true>, dim3(blocks), dim3(256), s, p, (int)N);
+        KVC_LAUNCH(k_append_mfma, dim3(blocks), dim3(256), s, p, (int)N);
     } else if (p.rot_kind == 1) {
         const long blocks = (N + 63) / 64;
         KVC_LAUNCH(k_append_hadamard, dim3((unsigned)blocks), dim3(256), s, p, N);
