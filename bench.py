@@ -514,6 +514,7 @@ def main():
 
     # ---- selection statistics (one untimed debug decode)
     sel_union = sel_entries = None
+    masked_tokens = masked_entries = 0
     if wl.top_p < 1.0:
         dbg = kvc.DecodeDebug.allocate(B, Hq, Lmax, True, dev, scores=False)
         kvc.decode_attend(cache, q, seq, pt, top_p=wl.top_p, max_seq_len=Lmax, debug=dbg, q_dither=dither)
@@ -529,6 +530,18 @@ def main():
             mask[:, h // G] |= m
         sel_union = int(mask.sum())
         sel_entries = int(cnt.sum())
+        # groups that the attention pass reads whole (the masked matrix-core chunk pass): every
+        # head dense (more than 64 kept per 2048 tokens), groups of 4 heads over pages of >= 64
+        # tokens, each head keeping more than a quarter of its sequence
+        L_b = seq.long()[:, None]
+        masked_tokens = 0
+        masked_entries = 0
+        if G == 4 and P >= 64 and not args.exact_keys and bool((cnt.long() * 2048 > 64 * L_b).all()):
+            grp = (cnt.long() * 4 > L_b).view(B, Hkv, G).all(dim=2)
+            masked_tokens = int((grp.long() * L_b).sum())
+            masked_entries = int((cnt.long().view(B, Hkv, G).sum(dim=2) * grp.long()).sum())
+        if masked_tokens:
+            log(f"[bench] the masked chunk pass reads {masked_tokens} token-KV-heads whole")
         sel_frac = float(cnt.sum()) / float(tokens_heads * G)
         log(f"[bench] Top-p kept {sel_frac * 100:.2f}% of (token, query head) pairs; "
             f"union over GQA groups {sel_union} token-KV-heads")
@@ -555,7 +568,8 @@ def main():
     # value record per kept (token, query head) rather than per KV head
     design = {
         "score": (key_bytes + DIST_BYTES * G) * tokens_heads if topp else key_bytes * tokens_heads,
-        "attend": (DIST_BYTES * G * tokens_heads + ((2 * D if exact else key_bytes) + vb) * sel_entries)
+        "attend": (DIST_BYTES * G * tokens_heads + ((2 * D if exact else key_bytes) + vb) * (sel_entries - masked_entries)
+                   + (key_bytes + vb) * masked_tokens)
         if topp else (key_bytes + vb) * tokens_heads,
         "hist": DIST_BYTES * G * tokens_heads, "query": 0, "merge": 0, "append": append_alg}
     score_kernel = ("k_score_topp_mf" if G >= 4 else "k_score_topp") if topp else "k_score"

@@ -365,7 +365,8 @@ __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
     }
     su = redi[0] + redi[1];
     s3 = redi[2] + redi[3];
-    if (r == 0) p.qpar[bh] = make_float4(vl * p.isk, delta * p.isk, __int_as_float(su), __int_as_float(s3));
+    // (c0, c1, sumu as integer bits, s3 - sumu as a float: the matrix-core products' offset)
+    if (r == 0) p.qpar[bh] = make_float4(vl * p.isk, delta * p.isk, __int_as_float(su), (float)(s3 - su));
     if (p.dbg_codes) p.dbg_codes[(size_t)bh * kD + r] = (uint8_t)u;
     if (r == 0 && p.dbg_params) {
         p.dbg_params[bh * 4 + 0] = vl;
@@ -676,7 +677,7 @@ __global__ __launch_bounds__(64, 4) void k_score_topp_mf(ScoreParams p)
         const float4 pq = p.qpar[bh0 + h];
         c0[h] = pq.x;
         c1[h] = pq.y;
-        msu[h] = (float)(__float_as_int(pq.w) - __float_as_int(pq.z));
+        msu[h] = pq.w;
     }
     uint32_t slot[U];
 #pragma unroll
@@ -1409,6 +1410,12 @@ __device__ __forceinline__ float pick4(const v4f_t &v, int i)
     return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
+// A wave-uniform value (loaded by every lane from one address) moved to a scalar register.
+__device__ __forceinline__ float uniform_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 // LDS ordering among the lanes of one wave (for data no other wave touches): a wave's LDS
 // operations complete in order, so fences at wavefront scope, which keep the compiler from
 // moving LDS accesses across this point, are all that is needed.
@@ -1438,11 +1445,12 @@ struct MfShared {
 };
 
 // The matrix-core pass of one wave over tokens tb .. tb + n - 1 of sequence b for the GB query
-// heads bh0 .. of KV head kvh (the scheme above).  Leaves the sums in st; mf_outputs gives
-// the value sums.
-template <int GB, int GV, int KW, bool PAGE64, int NPB>
+// heads bh0 .. of KV head kvh (the scheme above).  MASKED (Top-p): a token counts for head h
+// only if bit 8 h + (i mod 8) of LDS word msk[i / 8] is set, i = t - tb (the caller's keep
+// bits, written before the call).  Leaves the sums in st; mf_outputs gives the value sums.
+template <int GB, int GV, int KW, bool PAGE64, bool MASKED, int NPB>
 __device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, int bh0, int tb, int n,
-                                        MfShared<GB, NPB> &sh, MfState<GB> &st)
+                                        MfShared<GB, NPB> &sh, MfState<GB> &st, const uint32_t *msk = nullptr)
 {
     constexpr int NB = 64;                // tokens per batch
     constexpr int NG = kD / GV;           // value groups per token
@@ -1459,15 +1467,17 @@ __device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, i
                       << logP;
     sh.wbuf[GB][lane] = 0.0f;
     QueryState<MF4 ? 1 : GB> qs;  // wave-uniform: scalar loads into SGPRs (dot8 products)
-    float c0[GB], c1[GB];
-    v4f_t msu = {0.0f, 0.0f, 0.0f, 0.0f};  // the matrix-core products' accumulator start
+    // per head (wave-uniform, held in scalar registers): the score coefficients and -sumu,
+    // which is added to the matrix-core products (integers below 2^24: exact either way)
+    float c0[GB], c1[GB], msu[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
         const float4 pq = p.qpar[bh0 + h];
-        c0[h] = pq.x;
-        c1[h] = pq.y;
+        c0[h] = uniform_f(pq.x);
+        c1[h] = uniform_f(pq.y);
+        msu[h] = 0.0f;
         if constexpr (MF4) {
-            msu[h] = (float)(__float_as_int(pq.w) - __float_as_int(pq.z));
+            msu[h] = uniform_f(pq.w);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) qs.nib[h][i] = p.qnib[(size_t)(bh0 + h) * 16 + i];
@@ -1556,13 +1566,13 @@ __device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, i
                            __builtin_popcount(kbw.w);
             const float fP = (float)(2 * pc - 32 * KW);
             const float r = norm_over_corr(nc);
-            const v4f_t d = key_products4(kbw, msu, [&](int t) {
+            const v4f_t d = key_products4(kbw, v4f_t{0.0f, 0.0f, 0.0f, 0.0f}, [&](int t) {
                 const uint4 *q = &sh.qa[qtile == t ? qrow : 32];
                 const uint4 a0 = q[0], a1 = q[1];
                 return v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             });
 #pragma unroll
-            for (int h = 0; h < GB; ++h) s[h] = fmaf(c1[h], d[h], c0[h] * fP) * r;
+            for (int h = 0; h < GB; ++h) s[h] = fmaf(c1[h], d[h] + msu[h], c0[h] * fP) * r;
         } else {
             int A[GB];
             score_key<GB>(kbw, nc, qs, s, A, 32 * KW);
@@ -1572,10 +1582,16 @@ __device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, i
         // sums are rescaled; most batches cost one compare per head instead of a wave max.
         float scl[GB];
         bool grow = false;
+        // the token's keep bits: bit 8 h for head h
+        const uint32_t kw8 = MASKED ? msk[(bs + lane) >> 3] >> (lane & 7) : 0u;
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
-            // past the batch, or a marked record (a token held in the high-precision tier)
+            // past the batch, a marked record (a token held in the high-precision tier), or
+            // (masked) a token outside the head's Top-p set
             if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
+            if constexpr (MASKED) {
+                if (!(kw8 & (1u << (8 * h)))) s[h] = -INFINITY;
+            }
             scl[h] = 1.0f;
             if (__any(s[h] > st.mrun[h] + lazy)) {  // the first finite score always moves it
                 const float mnew = wave_max_u(s[h]);
@@ -1700,7 +1716,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void k_
     const int n = min(g.CH, L - t0);
     const int bh0 = b * g.Hq + hq0;
     MfState<GB> st;
-    mf_pass<GB, GV, KW, PAGE64>(p, b, kvh, bh0, t0, n, sh, st);
+    mf_pass<GB, GV, KW, PAGE64, false>(p, b, kvh, bh0, t0, n, sh, st);
     const size_t pidx = (size_t)bh0 * g.NCA + chunk;  // partial of head bh0 (+ h * NCA)
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
@@ -1748,7 +1764,90 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
 
 constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of one head
 
-template <bool EXACT, int KW>
+// ---------------------------------------------------------------------------------------
+// Top-p attention of one attention chunk for a KV head's 4 query heads that each keep more
+// than 1 / kMaskedDense of their sequence, by one wave.  Gathering the kept records per head
+// then reads most records several times over (through the caches) and lists every kept
+// token; instead the wave runs the full-softmax matrix-core pass over the chunk with a mask (a
+// token counts for a head when its bin distance is within the head's threshold for the
+// token's score chunk), reading every key and value record of the chunk once for the 4 heads,
+// and writes each head's partial: the quantities the gather pass writes, up to rounding.
+// slice: kMaskedSlice bytes of LDS, 16-byte aligned, the wave's own.
+// ---------------------------------------------------------------------------------------
+constexpr int kMaskedDense = 4;
+constexpr int kMaskedPages = kTopPAttendChunk / 64 + 1;  // page ids of a chunk (pages >= 64)
+constexpr int kMaskedSlice = (int)sizeof(MfShared<4, kMaskedPages>) + kTopPAttendChunk / 2;  // + keep bits
+static_assert(sizeof(MfShared<4, kMaskedPages>) % 16 == 0, "slices stay 16-byte aligned");
+
+template <int GV, int KW>
+__device__ __forceinline__ void topp_masked_chunk(const AttendParams &p, int b, int kvh, int hq0, int c, int L,
+                                                  uint8_t *slice)
+{
+    constexpr int GB = 4, CHA = kTopPAttendChunk;
+    using Sh = MfShared<GB, kMaskedPages>;
+    const DecodeGeom &g = p.g;
+    const int lane = threadIdx.x & 63;
+    const int bh0 = b * g.Hq + hq0;
+    const int tb = c * CHA;
+    // keep bits: byte 4 o + h = head h's bits for tokens tb + 8 o .. + 7 (bit e: token
+    // tb + 8 o + e within the head's threshold for its score chunk).  Lane l reads 8 distances
+    // of head l / 16 per 16-byte load; the rows are padded to whole attention chunks, so reads
+    // past the end stay inside them (and those tokens get no weight in the pass).
+    {
+        constexpr int NL = CHA / 128;  // loads per lane
+        constexpr int LPS = kTopPChunk / 128;  // loads per score chunk
+        const int hh = lane >> 4, o16 = lane & 15;
+        const size_t bh = (size_t)(bh0 + hh);
+        const int sc0 = tb / kTopPChunk;
+        int thr[CHA / kTopPChunk];
+#pragma unroll
+        for (int k = 0; k < CHA / kTopPChunk; ++k) thr[k] = chunk_threshold(p.sel, p.lmax, bh, g.NC, min(sc0 + k, g.NC - 1));
+        uint4 raw[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) raw[j] = *reinterpret_cast<const uint4 *>(p.dl + bh * g.Lpad + tb + 128 * j + 8 * o16);
+        uint8_t *bits = slice + sizeof(Sh);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+            const int t = thr[j / LPS];
+            uint32_t m = 0u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m |= ((int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) <= t) ? (1u << e) : 0u;
+            bits[4 * (16 * j + o16) + hh] = (uint8_t)m;
+        }
+    }
+    MfState<GB> st;
+    mf_pass<GB, GV, KW, true, true>(p, b, kvh, bh0, tb, min(CHA, L - tb), *reinterpret_cast<Sh *>(slice), st,
+                                    reinterpret_cast<const uint32_t *>(slice + sizeof(Sh)));
+    const size_t pidx = (size_t)bh0 * g.NCA + c;  // partial of head bh0 (+ h * NCA)
+#pragma unroll
+    for (int h = 0; h < GB; ++h) {
+        const float l = wave_sum(st.lsum[h]);
+        if (lane == 0) {
+            p.pm[pidx + (size_t)h * g.NCA] = st.mrun[h];
+            p.pl[pidx + (size_t)h * g.NCA] = l;
+        }
+    }
+    mf_outputs<GB, GV>(st, [&](int h, int d0, const float (&o)[8]) {
+        float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + d0);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    });
+}
+
+// Whether the query heads hq0 .. hq0 + 3 of sequence b (a KV head's group) each keep more
+// than 1 / kMaskedDense of the sequence's L tokens (the threshold pass's counts).
+__device__ __forceinline__ bool masked_group(const AttendParams &p, int b, int hq0, int L)
+{
+    bool many = true;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) many &= (long)kMaskedDense * p.sel[(size_t)(b * p.g.Hq + hq0 + h) * 4 + 2] > L;
+    return many;
+}
+
+// MG: 0, or the value group size (32 or 64) when the masked chunk pass is compiled in (groups
+// of 4 query heads, pages of 64 tokens or more, compressed keys).
+template <bool EXACT, int KW, int MG>
 __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_topp(AttendParams p)
 {
     constexpr int CHA = kTopPAttendChunk;  // tokens of an attention chunk
@@ -1760,10 +1859,39 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
     // list slice is 2304 bytes so that the final sums (2304 bytes) fit in one.
     constexpr int SL = 1152;               // list entries per slice
     constexpr int PS = CHA / 16 + 1;       // page ids per slice (pages of >= 16 tokens)
-    __shared__ uint16_t lst[NW * SL];
+    // the list slices; with the masked chunk pass, also the waves' slices of that pass
+    constexpr int LST = MG != 0 && NW * kMaskedSlice > NW * SL * 2 ? NW * kMaskedSlice / 2 : NW * SL;
+    __shared__ __align__(16) uint16_t lst[LST];
     __shared__ float wbs[NW][64];
     __shared__ uint32_t pbs[NW * PS];
     const DecodeGeom &g = p.g;
+    if constexpr (MG != 0) {
+        // every head dense, and the block's group of 4 heads each keeping a large share: one
+        // read of every record of a chunk for the 4 heads, one chunk per wave.  The block
+        // numbering is the dense case's below (block xf of the group's NCA); blocks
+        // xf < nq = NCA / 4 take chunks xf + nq w (wave w), the others end at once, so that the
+        // working blocks are consecutive and spread over the XCDs as blocks are dealt out.
+        static_assert(NW == 4, "masked chunk pass: 4 waves per block");
+        if (p.order_ctr[0] == g.B * g.Hq && g.GB == 4) {
+            const int L0 = (int)blockIdx.x + (int)gridDim.x * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
+            const int grp = L0 / g.NCA, xf = L0 - grp * g.NCA;
+            if (grp < g.B * g.Hkv * g.nsub) {
+                const int bq = grp / (g.Hkv * g.nsub);
+                int kvg, hq0;
+                block_heads(g, grp - bq * g.Hkv * g.nsub, kvg, hq0);
+                const int Lq = g.seq_lens[bq];
+                if (masked_group(p, bq, hq0, Lq)) {  // block-uniform
+                    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                    const int nq = (g.NCA + 3) >> 2;
+                    const int c = xf + nq * w;
+                    if (xf < nq && c * kTopPAttendChunk < Lq)
+                        topp_masked_chunk<MG, KW>(p, bq, kvg, hq0, c, Lq,
+                                                  reinterpret_cast<uint8_t *>(lst) + kMaskedSlice * w);
+                    return;
+                }
+            }
+        }
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar
     int bhr, ls, c0, first;
@@ -2485,12 +2613,22 @@ hipError_t launch_attend(const AttendParams &p, bool select, hipStream_t s)
         const dim3 grid((p.g.NCA + kAttendWaves - 1) / kAttendWaves, p.g.Hq, p.g.B);
         if (p.g.CH * p.g.KA != kTopPAttendChunk) return hipErrorInvalidValue;
         const bool w4 = p.c.kw == 4;
+        const dim3 blk(64 * kAttendWaves);
         if (p.c.kf16) {
-            if (w4) KVC_LAUNCH((k_attend_topp<true, 4>), grid, dim3(64 * kAttendWaves), s, p);
-            else KVC_LAUNCH((k_attend_topp<true, 2>), grid, dim3(64 * kAttendWaves), s, p);
+            if (w4) KVC_LAUNCH((k_attend_topp<true, 4, 0>), grid, blk, s, p);
+            else KVC_LAUNCH((k_attend_topp<true, 2, 0>), grid, blk, s, p);
+        } else if (p.g.GB == 4 && p.c.logP >= 6) {
+            // groups of 4 heads over pages of >= 64 tokens: with the masked chunk pass
+            if (p.c.Gv == 32) {
+                if (w4) KVC_LAUNCH((k_attend_topp<false, 4, 32>), grid, blk, s, p);
+                else KVC_LAUNCH((k_attend_topp<false, 2, 32>), grid, blk, s, p);
+            } else {
+                if (w4) KVC_LAUNCH((k_attend_topp<false, 4, 64>), grid, blk, s, p);
+                else KVC_LAUNCH((k_attend_topp<false, 2, 64>), grid, blk, s, p);
+            }
         } else {
-            if (w4) KVC_LAUNCH((k_attend_topp<false, 4>), grid, dim3(64 * kAttendWaves), s, p);
-            else KVC_LAUNCH((k_attend_topp<false, 2>), grid, dim3(64 * kAttendWaves), s, p);
+            if (w4) KVC_LAUNCH((k_attend_topp<false, 4, 0>), grid, blk, s, p);
+            else KVC_LAUNCH((k_attend_topp<false, 2, 0>), grid, blk, s, p);
         }
     } else {
         // one wave per (chunk, KV-head group, sequence)

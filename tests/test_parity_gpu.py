@@ -1111,3 +1111,33 @@ def test_topp_long_sequence():
         worst = max(worst, e)
         assert e <= TOL, (b, h, e)
     _say(f"[long] 262144 tokens, top_p={wl.top_p}: ok, worst rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("lens", [[5000, 2300], [1, 777]])
+def test_topp_masked_groups(lens):
+    """Every head dense (the attention pass's block-per-KV-head numbering), the 4 query heads
+    of KV head 0 each keeping about 90% of their tokens (the masked matrix-core pass over every
+    record of a chunk) and those of KV head 1 some 15-25% (the per-head gather), in one call:
+    ragged lengths whose last chunk ends inside a wave's quarter, and quarters past the end.
+    Index sets equal the oracle's bit for bit, outputs within the tolerance, twice in a row on
+    one workspace."""
+    wl = W.CONFIGS[4].scaled(B=2, Hq=8, Hkv=2)
+    c = Case(wl, L=max(lens), seq_lens=lens)
+    c.q[:, 0:4] *= 0.3  # flat softmax: most tokens kept
+    c.q[:, 4:8] *= 2.0  # sharper: a minority kept
+    c.ocache = c.oracle_cache()
+    g = upload(c.ocache, c)
+    ref = c.oracle_decode(c.ocache, wl.top_p)
+    frac = {bh: r["idx"].size / int(c.lens[bh[0]]) for bh, r in ref.items()}
+    if lens[0] > 1000:
+        assert all(f * 1024 * 2 > 64 for f in frac.values()), frac  # every head dense
+        assert all(frac[(b, h)] > 0.25 for b in range(2) for h in range(4)), frac
+        assert all(min(frac[(b, h)] for h in range(4, 8)) <= 0.25 for b in range(2)), frac
+    for rep in range(2):
+        out, dbg = _decode_with_debug(c, g, wl.top_p, scores=False)
+        for (b, h), r in ref.items():
+            cnt = int(dbg.sel_count[b, h])
+            assert cnt == len(r["idx"]), (rep, b, h, cnt, len(r["idx"]))
+            np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+            assert rel_err(out[b, h], r["out"]) <= TOL, (rep, b, h, frac[(b, h)])
+    _say(f"[masked] lens={lens}: ok")
