@@ -1765,74 +1765,119 @@ __device__ __forceinline__ float dpp_ror(float v, int k)
 constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of one head
 
 // ---------------------------------------------------------------------------------------
-// Top-p attention of one attention chunk for a KV head's 4 query heads that each keep more
-// than 1 / kMaskedDense of their sequence, by one wave.  Gathering the kept records per head
-// then reads most records several times over (through the caches) and lists every kept
-// token; instead the wave runs the full-softmax matrix-core pass over the chunk with a mask (a
-// token counts for a head when its bin distance is within the head's threshold for the
-// token's score chunk), reading every key and value record of the chunk once for the 4 heads,
-// and writes each head's partial: the quantities the gather pass writes, up to rounding.
-// slice: kMaskedSlice bytes of LDS, 16-byte aligned, the wave's own.
+// Top-p attention of 4 attention chunks (one per wave) for a KV head's 4 query heads that
+// each keep more than 1 / kMaskedDense of their sequence.  Gathering the kept records per
+// head then reads most records several times over (through the caches) and lists every kept
+// token; instead each wave runs the full-softmax matrix-core pass over its chunk with a mask
+// (a token counts for a head when its bin distance is within the head's threshold for the
+// token's score chunk), reading every key and value record of the chunk once for the 4
+// heads.  The waves' (reference score, weight sum, value sums) per head are combined through
+// LDS into one partial per head, written to slot `slot`: the quantities the gather pass
+// writes for its chunks, up to rounding.  Chunks past the sequence's end contribute nothing.
+// smem: kMaskedSmem bytes, 16-byte aligned; every thread of the block calls it (it holds
+// block barriers).
 // ---------------------------------------------------------------------------------------
 constexpr int kMaskedDense = 4;
 constexpr int kMaskedPages = kTopPAttendChunk / 64 + 1;  // page ids of a chunk (pages >= 64)
 constexpr int kMaskedSlice = (int)sizeof(MfShared<4, kMaskedPages>) + kTopPAttendChunk / 2;  // + keep bits
+constexpr int kMaskedCombine = (4 * 4 * kD + 2 * 4 * 4) * 4;  // [wave][head][128] sums, then m and l
+constexpr int kMaskedSmem = 4 * kMaskedSlice > kMaskedCombine ? 4 * kMaskedSlice : kMaskedCombine;
 static_assert(sizeof(MfShared<4, kMaskedPages>) % 16 == 0, "slices stay 16-byte aligned");
 
 template <int GV, int KW>
-__device__ __forceinline__ void topp_masked_chunk(const AttendParams &p, int b, int kvh, int hq0, int c, int L,
-                                                  uint8_t *slice)
+__device__ __forceinline__ void topp_masked_chunks(const AttendParams &p, int b, int kvh, int hq0, int c, int slot,
+                                                   int L, uint8_t *smem)
 {
-    constexpr int GB = 4, CHA = kTopPAttendChunk;
+    constexpr int GB = 4, NW = 4, CHA = kTopPAttendChunk;
     using Sh = MfShared<GB, kMaskedPages>;
     const DecodeGeom &g = p.g;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int bh0 = b * g.Hq + hq0;
     const int tb = c * CHA;
-    // keep bits: byte 4 o + h = head h's bits for tokens tb + 8 o .. + 7 (bit e: token
-    // tb + 8 o + e within the head's threshold for its score chunk).  Lane l reads 8 distances
-    // of head l / 16 per 16-byte load; the rows are padded to whole attention chunks, so reads
-    // past the end stay inside them (and those tokens get no weight in the pass).
-    {
-        constexpr int NL = CHA / 128;  // loads per lane
-        constexpr int LPS = kTopPChunk / 128;  // loads per score chunk
-        const int hh = lane >> 4, o16 = lane & 15;
-        const size_t bh = (size_t)(bh0 + hh);
-        const int sc0 = tb / kTopPChunk;
-        int thr[CHA / kTopPChunk];
-#pragma unroll
-        for (int k = 0; k < CHA / kTopPChunk; ++k) thr[k] = chunk_threshold(p.sel, p.lmax, bh, g.NC, min(sc0 + k, g.NC - 1));
-        uint4 raw[NL];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) raw[j] = *reinterpret_cast<const uint4 *>(p.dl + bh * g.Lpad + tb + 128 * j + 8 * o16);
-        uint8_t *bits = slice + sizeof(Sh);
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-            const int t = thr[j / LPS];
-            uint32_t m = 0u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m |= ((int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) <= t) ? (1u << e) : 0u;
-            bits[4 * (16 * j + o16) + hh] = (uint8_t)m;
-        }
-    }
     MfState<GB> st;
-    mf_pass<GB, GV, KW, true, true>(p, b, kvh, bh0, tb, min(CHA, L - tb), *reinterpret_cast<Sh *>(slice), st,
-                                    reinterpret_cast<const uint32_t *>(slice + sizeof(Sh)));
-    const size_t pidx = (size_t)bh0 * g.NCA + c;  // partial of head bh0 (+ h * NCA)
+    if (tb < L) {  // wave-uniform
+        uint8_t *slice = smem + kMaskedSlice * wave;
+        // keep bits: byte 4 o + h = head h's bits for tokens tb + 8 o .. + 7 (bit e: token
+        // tb + 8 o + e within the head's threshold for its score chunk).  Lane l reads 8
+        // distances of head l / 16 per 16-byte load; the rows are padded to whole attention
+        // chunks, so reads past the end stay inside them (and those tokens get no weight).
+        {
+            constexpr int NL = CHA / 128;          // loads per lane
+            constexpr int LPS = kTopPChunk / 128;  // loads per score chunk
+            const int hh = lane >> 4, o16 = lane & 15;
+            const size_t bh = (size_t)(bh0 + hh);
+            const int sc0 = tb / kTopPChunk;
+            int thr[CHA / kTopPChunk];
 #pragma unroll
-    for (int h = 0; h < GB; ++h) {
-        const float l = wave_sum(st.lsum[h]);
-        if (lane == 0) {
-            p.pm[pidx + (size_t)h * g.NCA] = st.mrun[h];
-            p.pl[pidx + (size_t)h * g.NCA] = l;
+            for (int k = 0; k < CHA / kTopPChunk; ++k)
+                thr[k] = chunk_threshold(p.sel, p.lmax, bh, g.NC, min(sc0 + k, g.NC - 1));
+            uint4 raw[NL];
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                raw[j] = *reinterpret_cast<const uint4 *>(p.dl + bh * g.Lpad + tb + 128 * j + 8 * o16);
+            uint8_t *bits = slice + sizeof(Sh);
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+                const int t = thr[j / LPS];
+                uint32_t m = 0u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    m |= ((int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) <= t) ? (1u << e) : 0u;
+                bits[4 * (16 * j + o16) + hh] = (uint8_t)m;
+            }
+        }
+        mf_pass<GB, GV, KW, true, true>(p, b, kvh, bh0, tb, min(CHA, L - tb), *reinterpret_cast<Sh *>(slice), st,
+                                        reinterpret_cast<const uint32_t *>(slice + sizeof(Sh)));
+    } else {  // past the sequence's end: nothing
+#pragma unroll
+        for (int j = 0; j < 9; ++j) st.acc[j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+        st.zacc = 0.0f;
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+            st.lsum[h] = 0.0f;
+            st.mrun[h] = -INFINITY;
         }
     }
+    float l[GB];
+#pragma unroll
+    for (int h = 0; h < GB; ++h) l[h] = wave_sum(st.lsum[h]);
+    __syncthreads();  // every wave is done with its LDS slice
+    float *cmb = reinterpret_cast<float *>(smem);  // [NW][GB][128] value sums, then [NW][GB] m and l
+    float *cm = cmb + NW * GB * kD, *cl = cm + NW * GB;
     mf_outputs<GB, GV>(st, [&](int h, int d0, const float (&o)[8]) {
-        float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + d0);
+        float4 *dst = reinterpret_cast<float4 *>(cmb + (wave * GB + h) * kD + d0);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
     });
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GB; ++h) {
+            cm[wave * GB + h] = st.mrun[h];
+            cl[wave * GB + h] = l[h];
+        }
+    }
+    __syncthreads();
+    // wave h: head h, lane l: dims 2 l and 2 l + 1
+    const int h = wave, d = 2 * lane;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, cm[w * GB + h]);
+    float o0 = 0.0f, o1 = 0.0f, lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float mw = cm[w * GB + h];
+        const float a = (mw == -INFINITY) ? 0.0f : exp2f((mw - M) * p.klog);
+        o0 = fmaf(a, cmb[(w * GB + h) * kD + d], o0);
+        o1 = fmaf(a, cmb[(w * GB + h) * kD + d + 1], o1);
+        lt = fmaf(a, cl[w * GB + h], lt);
+    }
+    const size_t pidx = (size_t)(bh0 + h) * g.NCA + slot;
+    reinterpret_cast<float2 *>(p.po + pidx * kD)[lane] = make_float2(o0, o1);
+    if (lane == 0) {
+        p.pm[pidx] = M;
+        p.pl[pidx] = lt;
+    }
 }
 
 // Whether the query heads hq0 .. hq0 + 3 of sequence b (a KV head's group) each keep more
@@ -1860,7 +1905,7 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
     constexpr int SL = 1152;               // list entries per slice
     constexpr int PS = CHA / 16 + 1;       // page ids per slice (pages of >= 16 tokens)
     // the list slices; with the masked chunk pass, also the waves' slices of that pass
-    constexpr int LST = MG != 0 && NW * kMaskedSlice > NW * SL * 2 ? NW * kMaskedSlice / 2 : NW * SL;
+    constexpr int LST = MG != 0 && kMaskedSmem > NW * SL * 2 ? kMaskedSmem / 2 : NW * SL;
     __shared__ __align__(16) uint16_t lst[LST];
     __shared__ float wbs[NW][64];
     __shared__ uint32_t pbs[NW * PS];
@@ -1868,9 +1913,11 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
     if constexpr (MG != 0) {
         // every head dense, and the block's group of 4 heads each keeping a large share: one
         // read of every record of a chunk for the 4 heads, one chunk per wave.  The block
-        // numbering is the dense case's below (block xf of the group's NCA); blocks
-        // xf < nq = NCA / 4 take chunks xf + nq w (wave w), the others end at once, so that the
-        // working blocks are consecutive and spread over the XCDs as blocks are dealt out.
+        // numbering is the dense case's below (block xf of the group's NCA).  Blocks
+        // xf < nq = NCA / 4 take chunks xf + nq w (wave w) and write their combined partial to
+        // slot xf; the others mark slot xf empty and end, so that the working blocks are
+        // consecutive (spread over the XCDs as blocks are dealt out) and the merge finds the
+        // partials in the first nq slots.
         static_assert(NW == 4, "masked chunk pass: 4 waves per block");
         if (p.order_ctr[0] == g.B * g.Hq && g.GB == 4) {
             const int L0 = (int)blockIdx.x + (int)gridDim.x * ((int)blockIdx.y + (int)gridDim.y * (int)blockIdx.z);
@@ -1883,10 +1930,14 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
                 if (masked_group(p, bq, hq0, Lq)) {  // block-uniform
                     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
                     const int nq = (g.NCA + 3) >> 2;
-                    const int c = xf + nq * w;
-                    if (xf < nq && c * kTopPAttendChunk < Lq)
-                        topp_masked_chunk<MG, KW>(p, bq, kvg, hq0, c, Lq,
-                                                  reinterpret_cast<uint8_t *>(lst) + kMaskedSlice * w);
+                    if (xf < nq) {
+                        topp_masked_chunks<MG, KW>(p, bq, kvg, hq0, xf + nq * w, xf, Lq,
+                                                   reinterpret_cast<uint8_t *>(lst));
+                    } else if (threadIdx.x < 4) {
+                        const size_t pidx = (size_t)(bq * g.Hq + hq0 + threadIdx.x) * g.NCA + xf;
+                        p.pm[pidx] = -INFINITY;
+                        p.pl[pidx] = 0.0f;
+                    }
                     return;
                 }
             }
@@ -2377,7 +2428,7 @@ template <bool MASS>
 __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 {
     constexpr int kT = 1024, NS = kT / kD;  // threads, chunk slices
-    constexpr int PF = 32;                  // chunks per thread loaded ahead
+    constexpr int PF = MASS ? 16 : 32;      // chunks per thread loaded ahead (fewer beside the mass prefetch)
     __shared__ float alpha[kMaxChunks];
     __shared__ float redf[2][kT / 64];
     __shared__ float part[NS][kD];
@@ -2390,12 +2441,14 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
     const int d = tid & (kD - 1), sl = tid >> 7;
     MassPrefetch mf;
     if (MASS) mass_prefetch(p.mass, b, h, g.Hq / g.Hkv, g.Hkv, mf);
+    // Loads and sums below are branch-free (so that a round's loads are all in flight at
+    // once): a chunk past the end, or one without weight, re-reads chunk 0 and is not added.
     const float *po = p.po + bh * g.NCA * kD + d;
     float v[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
         const int c = sl + NS * i;
-        v[i] = c < nch ? po[(size_t)c * kD] : 0.0f;
+        v[i] = po[(size_t)(c < nch ? c : 0) * kD];
     }
     // the first kT chunks' max and weight sum are read once, with the value sums in flight
     const float mc0 = tid < nch ? p.pm[bh * g.NCA + tid] : -INFINITY;
@@ -2432,20 +2485,25 @@ __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
         const int c = sl + NS * i;
-        if (c < nch && alpha[c] != 0.0f) num = fmaf(alpha[c], v[i], num);
+        const float a = alpha[c < nch ? c : 0];
+        num = (c < nch && a != 0.0f) ? fmaf(a, v[i], num) : num;
     }
     for (int c0 = sl + NS * PF; c0 < nch; c0 += NS * PF) {
-        // the rest in rounds of PF loads in flight
+        // the rest in rounds of PF loads in flight; the weights are known by now, so empty
+        // partials (chunks that a wave covering several wrote as such) are not fetched
+        float a[PF];
+        bool any = false;
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             const int c = c0 + NS * i;
-            v[i] = c < nch ? po[(size_t)c * kD] : 0.0f;
+            a[i] = c < nch ? alpha[c] : 0.0f;
+            any |= a[i] != 0.0f;
         }
+        if (!__any(any)) continue;  // wave-uniform: a round of empty partials only
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int c = c0 + NS * i;
-            if (c < nch && alpha[c] != 0.0f) num = fmaf(alpha[c], v[i], num);
-        }
+        for (int i = 0; i < PF; ++i) v[i] = po[(size_t)(a[i] != 0.0f ? c0 + NS * i : 0) * kD];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) num = a[i] != 0.0f ? fmaf(a[i], v[i], num) : num;
     }
     part[sl][d] = num;
     __syncthreads();
