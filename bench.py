@@ -76,6 +76,9 @@ def parse():
                     help="estimator variant: seeded stochastic rounding of the int4 query")
     ap.add_argument("--exact-keys", action="store_true",
                     help="also keep binary16 keys; Top-p attends the selected tokens with exact scores")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step (its kernels, on one stream) in a HIP graph once and time its "
+                         "replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -466,6 +469,19 @@ def main():
             flush()
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # the step allocates nothing and synchronizes nowhere, so it can be captured as it is
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            if not args.no_flush:
+                flush()
+            run()
+        torch.cuda.synchronize()
 
     # ---- timed region: K steps, per-step HIP events (flush outside the events)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -475,7 +491,7 @@ def main():
         if not args.no_flush:
             flush()
         ev[i][0].record()
-        step()
+        run()
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -614,7 +630,7 @@ def main():
                            + (" (two calls)" if args.separate_append else " (one call, fused append)"),
                    "cache_flushed_between_steps": not args.no_flush, "exact_keys": args.exact_keys,
                    "key_center": args.center_keys, "stochastic_query": args.stochastic_query,
-                   "sketch_dim": args.sketch_dim},
+                   "sketch_dim": args.sketch_dim, "hip_graph": args.graph},
         "roofline": roofline,
         "step_hbm_frac_algorithmic": round(step_alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": step_alg,
