@@ -1114,28 +1114,33 @@ def test_topp_long_sequence():
 
 
 @pytest.mark.parametrize("lens,variant", [([5000, 2300], "g32-p256"), ([1, 777], "g32-p256"),
-                                          ([5000, 2300], "g64-p64"), ([4100, 3000], "sketch64")])
+                                          ([5000, 2300], "g64-p64"), ([4100, 3000], "sketch64"),
+                                          ([3000, 2500, 1, 4100], "128heads")])
 def test_topp_masked_groups(lens, variant):
     """Every head dense (the attention pass's block-per-KV-head numbering), the 4 query heads
     of KV head 0 each keeping about 90% of their tokens (the masked matrix-core pass over every
     record of a chunk) and those of KV head 1 some 15-25% (the per-head gather), in one call:
     ragged lengths that end inside a chunk, and blocks whose chunks lie past the end.  The
     variants cover the pass's builds: value groups of 32 and 64, pages of 256 and 64 tokens,
-    the full and the 64-bit key sketch.  Index sets equal the oracle's bit for bit, outputs
-    within the tolerance, twice in a row on one workspace."""
-    spec = {"g32-p256": dict(), "g64-p64": dict(Gv=64, P=64), "sketch64": dict()}[variant]
-    wl = W.CONFIGS[4].scaled(B=2, Hq=8, Hkv=2, **spec)
+    the full and the 64-bit key sketch; and 128 heads over 4 sequences (the one-block histogram
+    and threshold pass, an alternation of masked and gathered groups, a one-token sequence).
+    Index sets equal the oracle's bit for bit, outputs within the tolerance, twice in a row on
+    one workspace."""
+    spec = {"g32-p256": dict(), "g64-p64": dict(Gv=64, P=64), "sketch64": dict(),
+            "128heads": dict(B=4, Hq=32, Hkv=8)}[variant]
+    wl = W.CONFIGS[4].scaled(**{**dict(B=2, Hq=8, Hkv=2), **spec})
     c = Case(wl, L=max(lens), seq_lens=lens)
-    c.q[:, 0:4] *= 0.3  # flat softmax: most tokens kept
-    c.q[:, 4:8] *= 1.4 if variant == "sketch64" else 2.0  # sharper: a minority kept
+    G = wl.Hq // wl.Hkv
+    for kvh in range(wl.Hkv):  # even KV heads: flat softmax, most tokens kept; odd: a minority
+        c.q[:, G * kvh:G * (kvh + 1)] *= 0.3 if kvh % 2 == 0 else (1.4 if variant == "sketch64" else 2.0)
     c.ocache = c.oracle_cache(sketch=64 if variant == "sketch64" else None)
     g = upload(c.ocache, c)
     ref = c.oracle_decode(c.ocache, wl.top_p)
     frac = {bh: r["idx"].size / int(c.lens[bh[0]]) for bh, r in ref.items()}
     if lens[0] > 1000:
         assert all(f * 1024 * 2 > 64 for f in frac.values()), frac  # every head dense
-        assert all(frac[(b, h)] > 0.25 for b in range(2) for h in range(4)), frac
-        assert any(min(frac[(b, h)] for h in range(4, 8)) <= 0.25 for b in range(2)), frac
+        assert all(frac[(b, h)] > 0.25 for b in range(wl.B) for h in range(4) if c.lens[b] > 0), frac
+        assert any(min(frac[(b, h)] for h in range(4, 8)) <= 0.25 for b in range(wl.B) if c.lens[b] > 1), frac
     for rep in range(2):
         out, dbg = _decode_with_debug(c, g, wl.top_p, scores=False)
         for (b, h), r in ref.items():
