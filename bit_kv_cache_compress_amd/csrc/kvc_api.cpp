@@ -57,7 +57,7 @@ int chunk_cap(bool topp)
 }
 
 // Geometry.
-//  Full softmax: chunks of CH tokens, the largest power of two in [256, 2048] that still
+//  Full softmax: chunks of CH tokens, the largest power of two in [64, 2048] that still
 //  gives at least 4096 waves (16 per compute unit) over (chunk, KV-head group, sequence)
 //  and no more than kMaxChunks chunks; one attention wave per chunk (KA = 1).
 //  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention wave
@@ -71,7 +71,7 @@ void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, bool topp)
     } else {
         CH = chunk_cap(false);
         const long units = (long)B * rows_per_seq;
-        while (CH > 256 && units * ((max_len + CH - 1) / CH) < 4096 && (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
+        while (CH > 64 && units * ((max_len + CH - 1) / CH) < 4096 && (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
             CH >>= 1;
     }
     pl.g.CH = CH;
