@@ -108,7 +108,7 @@ void plan_layout(Plan &pl, int BH)
         // histogram splits: >= 512 blocks over (split, head, sequence); a split holds fewer
         // than 65536 tokens (16-bit partial counts) and at most 256 chunks (one per thread)
         int nsplit = (512 + BH - 1) / BH;
-        const int min_split = (int)(((long)pl.g.Lpad + 32767) / 32768);
+        const int min_split = (int)(((long)pl.g.Lpad + 65535) / 65536);
         if (nsplit < min_split) nsplit = min_split;
         if (nsplit > pl.g.NC) nsplit = pl.g.NC;
         if (nsplit < 1) nsplit = 1;
