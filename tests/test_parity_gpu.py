@@ -1149,3 +1149,63 @@ def test_topp_masked_groups(lens, variant):
             np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
             assert rel_err(out[b, h], r["out"]) <= TOL, (rep, b, h, frac[(b, h)])
     _say(f"[masked] lens={lens} {variant}: ok")
+
+
+def _random_case(i):
+    """Seeded random geometry (its own input streams: workload index 100 + i)."""
+    rng = np.random.default_rng(4242 + i)
+    if i % 4 == 3:  # 128 query heads: the one-block histogram and threshold pass
+        G, Hkv, B = 4, 8, 4
+        L = int(rng.integers(300, 4000))
+    else:
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]) if G == 8 else rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 4))
+        L = int(rng.integers(300, 12000))
+    P = int(rng.choice([16, 64, 128, 256]))
+    Gv = int(rng.choice([32, 64]))
+    rot = str(rng.choice(["dense", "hadamard"]))
+    top_p = float(rng.choice([0.5, 0.8, 0.95, 1.0]))
+    spike = float(rng.choice([0.0, 0.01]))
+    sketch = int(rng.choice([128, 64]))
+    lens = [int(x) for x in rng.integers(0, L + 1, size=B)]
+    lens[0] = L
+    if B > 1 and i % 3 == 0:
+        lens[-1] = int(rng.choice([0, 1]))  # an empty or one-token sequence
+    wl = W.CONFIGS[2].scaled(name=f"random-{i}", index=100 + i, B=B, Hq=G * Hkv, Hkv=Hkv, L=L, P=P, Gv=Gv, rot=rot,
+                             top_p=top_p, spike_frac=spike, shuffle_pages=bool(rng.integers(0, 2)))
+    return wl, lens, sketch
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_geometry(i):
+    """Seeded random geometries (GQA groups 1-8, 1-4 sequences of up to 12000 tokens with
+    random lengths including empty and one-token ones, 128 query heads in every fourth case,
+    pages of 16-256 tokens, value groups 32/64, both rotations, Top-p 0.5-0.95 or
+    full softmax, with or without spikes, 128- or 64-bit sketches, shuffled pages): the append's
+    bytes against the oracle's encoding, then the decode over the oracle's cache bytes (sets
+    bit-exact, outputs within the tolerance)."""
+    wl, lens, sketch = _random_case(i)
+    sk = None if sketch == 128 else sketch
+    c = Case(wl, L=max(lens), seq_lens=lens)
+    c.ocache = c.oracle_cache(sketch=sk)
+    g_app = gpu_append(c, sketch=sk)
+    stats = compare_caches(download(g_app), c.ocache, c)
+    g = upload(c.ocache, c)
+    ref = c.oracle_decode(c.ocache, wl.top_p)
+    out, dbg = _decode_with_debug(c, g, wl.top_p, scores=False, dist=False)
+    worst = 0.0
+    for (b, h), r in ref.items():
+        n = int(c.lens[b])
+        if n == 0:
+            assert np.abs(out[b, h]).max() == 0.0, (b, h)
+            continue
+        if wl.top_p < 1.0:
+            cnt = int(dbg.sel_count[b, h])
+            assert cnt == len(r["idx"]), (i, b, h, cnt, len(r["idx"]))
+            np.testing.assert_array_equal(dbg.sel_idx[b, h, :cnt].cpu().numpy(), r["idx"])
+        e = float(rel_err(out[b, h], r["out"]))
+        worst = max(worst, e)
+        assert e <= TOL, (i, b, h, e)
+    _say(f"[random {i}] G={wl.Hq // wl.Hkv} Hkv={wl.Hkv} B={wl.B} lens={lens} P={wl.P} Gv={wl.Gv} {wl.rot} "
+         f"top_p={wl.top_p} sketch={sketch}: ok {stats}, worst {worst:.1e}")
