@@ -546,9 +546,9 @@ def main():
             mask[:, h // G] |= m
         sel_union = int(mask.sum())
         sel_entries = int(cnt.sum())
-        # groups that the attention pass reads whole (the masked matrix-core chunk pass): every
-        # head dense (more than 64 kept per 2048 tokens), groups of 4 heads over pages of >= 64
-        # tokens, each head keeping more than a quarter of its sequence
+        # groups that the attention pass reads whole (the masked matrix-core chunk pass, which
+        # reads no distances): every head dense (more than 64 kept per 2048 tokens), groups of 4
+        # heads over pages of >= 64 tokens, each head keeping more than a quarter of its sequence
         L_b = seq.long()[:, None]
         masked_tokens = 0
         masked_entries = 0
@@ -584,7 +584,8 @@ def main():
     # value record per kept (token, query head) rather than per KV head
     design = {
         "score": (key_bytes + DIST_BYTES * G) * tokens_heads if topp else key_bytes * tokens_heads,
-        "attend": (DIST_BYTES * G * tokens_heads + ((2 * D if exact else key_bytes) + vb) * (sel_entries - masked_entries)
+        "attend": (DIST_BYTES * G * (tokens_heads - masked_tokens)
+                   + ((2 * D if exact else key_bytes) + vb) * (sel_entries - masked_entries)
                    + (key_bytes + vb) * masked_tokens)
         if topp else (key_bytes + vb) * tokens_heads,
         "hist": DIST_BYTES * G * tokens_heads, "query": 0, "merge": 0, "append": append_alg}

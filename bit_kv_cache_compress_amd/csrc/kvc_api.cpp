@@ -544,6 +544,7 @@ int decode_impl(const kv_cache *c, const kv_tail *tail, const kv_hp *hp, const f
     ap.qa = qa;
     ap.qpar = qpar;
     ap.klog = klog;
+    ap.kbin = kbin;
     ap.dl = sp.dl;
     ap.lmax = sp.lmax;
     ap.sel = pl.topp ? at<int32_t>(workspace, pl.off_sel) : nullptr;

@@ -1446,11 +1446,12 @@ struct MfShared {
 
 // The matrix-core pass of one wave over tokens tb .. tb + n - 1 of sequence b for the GB query
 // heads bh0 .. of KV head kvh (the scheme above).  MASKED (Top-p): a token counts for head h
-// only if bit 8 h + (i mod 8) of LDS word msk[i / 8] is set, i = t - tb (the caller's keep
-// bits, written before the call).  Leaves the sums in st; mf_outputs gives the value sums.
+// only if the Top-p bin of its score is at least ebin[h] = e_max - b* of the head (the score
+// is the score pass's, bit for bit, so this is the set the threshold pass counted).  Leaves
+// the sums in st; mf_outputs gives the value sums.
 template <int GB, int GV, int KW, bool PAGE64, bool MASKED, int NPB>
 __device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, int bh0, int tb, int n,
-                                        MfShared<GB, NPB> &sh, MfState<GB> &st, const uint32_t *msk = nullptr)
+                                        MfShared<GB, NPB> &sh, MfState<GB> &st, const int *ebin = nullptr)
 {
     constexpr int NB = 64;                // tokens per batch
     constexpr int NG = kD / GV;           // value groups per token
@@ -1582,16 +1583,14 @@ __device__ __forceinline__ void mf_pass(const AttendParams &p, int b, int kvh, i
         // sums are rescaled; most batches cost one compare per head instead of a wave max.
         float scl[GB];
         bool grow = false;
-        // the token's keep bits: bit 8 h for head h
-        const uint32_t kw8 = MASKED ? msk[(bs + lane) >> 3] >> (lane & 7) : 0u;
 #pragma unroll
         for (int h = 0; h < GB; ++h) {
             // past the batch, a marked record (a token held in the high-precision tier), or
             // (masked) a token outside the head's Top-p set
-            if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
             if constexpr (MASKED) {
-                if (!(kw8 & (1u << (8 * h)))) s[h] = -INFINITY;
+                if (score_bin(s[h], p.kbin) < ebin[h]) s[h] = -INFINITY;  // NaN: the bottom bin
             }
+            if (lane >= nb || s[h] != s[h]) s[h] = -INFINITY;
             scl[h] = 1.0f;
             if (__any(s[h] > st.mrun[h] + lazy)) {  // the first finite score always moves it
                 const float mnew = wave_max_u(s[h]);
@@ -1769,9 +1768,9 @@ constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of
 // each keep more than 1 / kMaskedDense of their sequence.  Gathering the kept records per
 // head then reads most records several times over (through the caches) and lists every kept
 // token; instead each wave runs the full-softmax matrix-core pass over its chunk with a mask
-// (a token counts for a head when its bin distance is within the head's threshold for the
-// token's score chunk), reading every key and value record of the chunk once for the 4
-// heads.  The waves' (reference score, weight sum, value sums) per head are combined through
+// (a token counts for a head when the Top-p bin of its score, which the pass recomputes bit
+// for bit, is at least the head's e_max - b*), reading every key and value record of the
+// chunk once for the 4 heads and none of the bin distances.  The waves' (reference score, weight sum, value sums) per head are combined through
 // LDS into one partial per head, written to slot `slot`: the quantities the gather pass
 // writes for its chunks, up to rounding.  Chunks past the sequence's end contribute nothing.
 // smem: kMaskedSmem bytes, 16-byte aligned; every thread of the block calls it (it holds
@@ -1779,7 +1778,7 @@ constexpr int kAttendWaves = 4;  // waves per Top-p attention block: 4 chunks of
 // ---------------------------------------------------------------------------------------
 constexpr int kMaskedDense = 4;
 constexpr int kMaskedPages = kTopPAttendChunk / 64 + 1;  // page ids of a chunk (pages >= 64)
-constexpr int kMaskedSlice = (int)sizeof(MfShared<4, kMaskedPages>) + kTopPAttendChunk / 2;  // + keep bits
+constexpr int kMaskedSlice = (int)sizeof(MfShared<4, kMaskedPages>);
 constexpr int kMaskedCombine = (4 * 4 * kD + 2 * 4 * 4) * 4;  // [wave][head][128] sums, then m and l
 constexpr int kMaskedSmem = 4 * kMaskedSlice > kMaskedCombine ? 4 * kMaskedSlice : kMaskedCombine;
 static_assert(sizeof(MfShared<4, kMaskedPages>) % 16 == 0, "slices stay 16-byte aligned");
@@ -1797,38 +1796,15 @@ __device__ __forceinline__ void topp_masked_chunks(const AttendParams &p, int b,
     MfState<GB> st;
     if (tb < L) {  // wave-uniform
         uint8_t *slice = smem + kMaskedSlice * wave;
-        // keep bits: byte 4 o + h = head h's bits for tokens tb + 8 o .. + 7 (bit e: token
-        // tb + 8 o + e within the head's threshold for its score chunk).  Lane l reads 8
-        // distances of head l / 16 per 16-byte load; the rows are padded to whole attention
-        // chunks, so reads past the end stay inside them (and those tokens get no weight).
-        {
-            constexpr int NL = CHA / 128;          // loads per lane
-            constexpr int LPS = kTopPChunk / 128;  // loads per score chunk
-            const int hh = lane >> 4, o16 = lane & 15;
-            const size_t bh = (size_t)(bh0 + hh);
-            const int sc0 = tb / kTopPChunk;
-            int thr[CHA / kTopPChunk];
+        // the heads' lowest kept bin, e_max - b* (wave-uniform)
+        int ebin[GB];
 #pragma unroll
-            for (int k = 0; k < CHA / kTopPChunk; ++k)
-                thr[k] = chunk_threshold(p.sel, p.lmax, bh, g.NC, min(sc0 + k, g.NC - 1));
-            uint4 raw[NL];
-#pragma unroll
-            for (int j = 0; j < NL; ++j)
-                raw[j] = *reinterpret_cast<const uint4 *>(p.dl + bh * g.Lpad + tb + 128 * j + 8 * o16);
-            uint8_t *bits = slice + sizeof(Sh);
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-                const int t = thr[j / LPS];
-                uint32_t m = 0u;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    m |= ((int)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) <= t) ? (1u << e) : 0u;
-                bits[4 * (16 * j + o16) + hh] = (uint8_t)m;
-            }
+        for (int h = 0; h < GB; ++h) {
+            const int *sl = p.sel + (size_t)(bh0 + h) * 4;
+            ebin[h] = __builtin_amdgcn_readfirstlane(sl[0] - sl[1]);
         }
         mf_pass<GB, GV, KW, true, true>(p, b, kvh, bh0, tb, min(CHA, L - tb), *reinterpret_cast<Sh *>(slice), st,
-                                        reinterpret_cast<const uint32_t *>(slice + sizeof(Sh)));
+                                        ebin);
     } else {  // past the sequence's end: nothing
 #pragma unroll
         for (int j = 0; j < 9; ++j) st.acc[j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};

@@ -198,6 +198,7 @@ struct AttendParams {
     const uint8_t *qa;     // [B*Hq][128] the codes as the fp8 operand of the matrix-core key products
     const float4 *qpar;
     float klog;            // log2(e) / sqrt(D)
+    float kbin;            // Top-p bins per score unit (the score pass's)
     // Top-p selection (select mode only)
     const uint16_t *dl;
     const int32_t *lmax;
