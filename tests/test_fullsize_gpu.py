@@ -154,6 +154,66 @@ def test_gqa_128k_topp_full_size():
     _say("[full] the benchmark's step (append inside the decode) ok")
 
 
+def test_gqa_128k_topp_ragged_full_size():
+    """The 128k GQA Top-p workload's shape (batch 4, 32 query / 8 KV heads, Top-p 0.9) with
+    ragged lengths 131072, 130772, 70001 and 513, decoded as the benchmark runs it (no score
+    output): enough 512-token chunks that a score wave covers two consecutive chunks, here
+    with a sequence ending inside the first chunk of a pair and one inside the second.  The
+    score pass's distances and chunk top bins, the Top-p counts, sets and outputs of sampled
+    (sequence, KV head) units against the oracle run on the records the library wrote."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_kv_cache_compress_amd as kvc
+
+    wl = W.CONFIGS[2]
+    dev = torch.device("cuda")
+    B, Hq, Hkv, G = wl.B, wl.Hq, wl.Hkv, wl.Hq // wl.Hkv
+    lens = np.array([131072, 131072 - 300, 70001, 513], np.int32)
+    Lm = int(lens.max())
+    _say(f"[full] {wl.name} ragged {lens.tolist()}: drawing inputs")
+    K, V, q = W.draw_device(wl, dev, L=Lm)
+    pt_np, npages = W.page_layout(wl, lens)
+    kind, R16 = W.draw_rotation(wl)
+    cache = kvc.KVCache(npages, Hkv, R16, rot_kind=kind, page_size=wl.P, value_group=wl.Gv, device=dev)
+    pt = torch.from_numpy(pt_np).to(dev)
+    for b in range(B):
+        n = int(lens[b])
+        kvc.append(cache, K[b:b + 1, :n].contiguous(), V[b:b + 1, :n].contiguous(),
+                   torch.zeros(1, dtype=torch.int32, device=dev), pt[b:b + 1].contiguous())
+    dbg = kvc.DecodeDebug.allocate(B, Hq, Lm, True, dev, scores=False, dist=True)
+    out = kvc.decode_attend(cache, q, torch.from_numpy(lens).to(dev), pt, top_p=wl.top_p, max_seq_len=Lm,
+                            debug=dbg)
+    torch.cuda.synchronize()
+    _say("[full] library decode done")
+    assert torch.isfinite(out).all()
+    orot = oracle.Rotation(oracle.ROT_DENSE, wl.D, R16=R16)
+    kb = cache.key_bits.cpu().numpy().view(np.uint32)
+    kn = cache.key_nc.cpu().numpy().view(np.uint32)
+    vc = cache.val_codes.cpu().numpy()
+    vs = cache.val_sz.cpu().numpy().view(np.uint32)
+    o = out.cpu().numpy()
+    qn = q.cpu().numpy()
+    cnt = dbg.sel_count.cpu().numpy()
+    for b, h in [(1, 2), (2, 5), (3, 7)]:
+        n = int(lens[b])
+        t = np.arange(n)
+        pg, sl = pt_np[b, t // wl.P], t % wl.P
+        ncw = kn[pg, h, sl]
+        nc_g = np.stack([(ncw & 0xFFFF).astype(np.uint16), (ncw >> 16).astype(np.uint16)], axis=-1)
+        codes = vc[pg, h, sl]
+        szw = vs[pg, h, sl]
+        sz = np.stack([(szw & 0xFFFF).astype(np.uint16), (szw >> 16).astype(np.uint16)], axis=-1)
+        for hh in range(h * G, (h + 1) * G):
+            qe = oracle.query_encode(orot, qn[b, hh][None, :])
+            _, _, s_g = oracle.scores(kb[pg, h, sl], nc_g, qe["u"][0], qe["c0"][0], qe["c1"][0], wl.D)
+            tp = oracle.topp(s_g, wl.top_p, wl.D)
+            check_bins(dbg, b, hh, s_g, wl.D, Lm)
+            assert cnt[b, hh] == len(tp["idx"]), (b, hh)
+            np.testing.assert_array_equal(dbg.sel_idx[b, hh, :cnt[b, hh]].cpu().numpy(), tp["idx"])
+            assert rel_err(o[b, hh], oracle.attend(s_g, codes, sz, wl.D, wl.Gv, tp["idx"])) <= 2e-3
+        _say(f"[full] unit {(b, h)} over {n} tokens ok, kept {cnt[b, h * G:(h + 1) * G].tolist()}")
+
+
 def test_7b_layer_full_size():
     """The 7B-shaped layer at its own shape: 32 heads x 8192 tokens, fp16 K/V with 4 outlier
     channels per head scaled by 8, dense rotation, full softmax.  Every head: the cache bytes
