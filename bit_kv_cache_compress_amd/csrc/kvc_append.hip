@@ -20,7 +20,7 @@ typedef double double4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------------------
 // Randomized Hadamard rotation (append_hadamard_block): 64 token-heads per 256-thread block.
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_append_hadamard(AppendParams p, long N)
+__global__ __launch_bounds__(256, 4) void k_append_hadamard(AppendParams p, long N)
 {
     append_hadamard_block(p, N, blockIdx.x);
 }

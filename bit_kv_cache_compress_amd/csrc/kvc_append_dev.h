@@ -217,67 +217,19 @@ __device__ __forceinline__ void append_hadamard_block(const AppendParams &p, lon
     const int pos = p.start_pos[b] + t;
     const int page = p.page_table[(size_t)b * p.max_pages + (pos >> p.c.logP)];
     const size_t slot = ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
-    // the value's raw input is loaded with the key, so that the token-head costs one round of
-    // memory latency (binary16: 64 bytes per lane; binary32 values are loaded after the key)
-    uint4 vraw[4];
+    // the key's and the value's raw inputs are loaded together, so that the token-head costs
+    // one round of memory latency (binary16: 64 bytes of each per lane; binary32 inputs are
+    // loaded where they are used).  The value is encoded first, so that its raw words are not
+    // held through the key's rotation.
+    uint4 kraw[4], vraw[4];
     if (p.dtype == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) vraw[q] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.v) + row + 8 * q);
+        for (int q = 0; q < 4; ++q) {
+            kraw[q] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.k) + row + 8 * q);
+            vraw[q] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(p.v) + row + 8 * q);
+        }
     }
     float x[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float x8[8];
-        load8(p.k, p.dtype, row + 8 * q, x8);
-        if (p.c.kf16) store_key16(p.c, slot, 4 * j + q, x8);
-        center8(p.c, h, 4 * j + q, x8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * q + e] = x8[e];
-    }
-    // sigma, then the 7 butterfly levels (h = 1 .. 16 inside the lane, 32 and 64 across the quad)
-    const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[j];
-    double y[32];
-    double ss = 0.0;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const double xe = (double)x[e];
-        ss = fma(xe, xe, ss);
-        y[e] = ((sgw >> e) & 1u) ? -xe : xe;
-    }
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1)
-#pragma unroll
-        for (int e = 0; e < 32; ++e)
-            if ((e & m) == 0) {
-                const double a = y[e], c = y[e + m];
-                y[e] = a + c;
-                y[e + m] = a - c;
-            }
-    // across the quad: the lane holding the upper index keeps o - y, the other y + o, as one
-    // fma with a factor of -1 or +1 (exact)
-    const double f1 = (j & 1) ? -1.0 : 1.0, f2 = (j & 2) ? -1.0 : 1.0;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) y[e] = fma(f1, y[e], quad_xor1(y[e]));
-#pragma unroll
-    for (int e = 0; e < 32; ++e) y[e] = fma(f2, y[e], quad_xor2(y[e]));
-    // sign bits: word j of the key record; sum |k'| over the sketch's dims
-    uint32_t word = 0;
-    double sabs = 0.0;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        word |= (y[e] < 0.0 ? 0u : 1u) << e;
-        sabs += fabs(y[e]);
-    }
-    if (32 * j >= p.c.sk) sabs = 0.0;  // dims past the sketch
-    ss += quad_xor1(ss);
-    ss += quad_xor2(ss);
-    sabs += quad_xor1(sabs);
-    sabs += quad_xor2(sabs);
-    sabs /= sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
-    uint32_t *kr = key_rec(p.c, slot);
-    if (j < p.c.kw) kr[j] = word;  // the sketch's words
-    if (j == 0) kr[p.c.kw] = norm_corr_word(ss, sabs, p.c.sk);
-    // values
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (p.dtype == 0) {
@@ -295,6 +247,80 @@ __device__ __forceinline__ void append_hadamard_block(const AppendParams &p, lon
         }
     }
     encode_values32(x, j, p.c.Gv, val_rec(p.c, slot));
+    __builtin_amdgcn_sched_barrier(0);  // the value's registers are free before the key's rotation
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float x8[8];
+        if (p.dtype == 0) {
+            const uint32_t w[4] = {kraw[q].x, kraw[q].y, kraw[q].z, kraw[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x8[2 * e] = half_bits_to_float(w[e] & 0xFFFFu);
+                x8[2 * e + 1] = half_bits_to_float(w[e] >> 16);
+            }
+        } else {
+            load8(p.k, p.dtype, row + 8 * q, x8);
+        }
+        if (p.c.kf16) store_key16(p.c, slot, 4 * j + q, x8);
+        center8(p.c, h, 4 * j + q, x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * q + e] = x8[e];
+    }
+    // sigma, then the 7 butterfly levels (h = 1 .. 16 inside the lane, 32 and 64 across the quad)
+    const uint32_t sgw = reinterpret_cast<const uint32_t *>(p.rot)[j];
+    double y[32];
+    double ss = 0.0;
+    // (|k|^2 from the signed copies, y^2 = x^2, so that the binary32 inputs are dead once
+    // converted; the chain completes before the butterflies overwrite y)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const double xe = (double)x[e];
+        y[e] = ((sgw >> e) & 1u) ? -xe : xe;
+        ss = fma(y[e], y[e], ss);
+    }
+    ss += quad_xor1(ss);
+    ss += quad_xor2(ss);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            if ((e & m) == 0) {
+                const double a = y[e], c = y[e + m];
+                y[e] = a + c;
+                y[e + m] = a - c;
+            }
+        __builtin_amdgcn_sched_barrier(0);  // one level at a time: its inputs die as it goes
+    }
+    // across the quad: the lane holding the upper index keeps o - y, the other y + o, as one
+    // fma with a factor of -1 or +1 (exact)
+    const double f1 = (j & 1) ? -1.0 : 1.0, f2 = (j & 2) ? -1.0 : 1.0;
+    // (in groups of 8 values, so that the partners' copies do not all live at once)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        y[e] = fma(f1, y[e], quad_xor1(y[e]));
+        if ((e & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        y[e] = fma(f2, y[e], quad_xor2(y[e]));
+        if ((e & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    // sign bits: word j of the key record; sum |k'| over the sketch's dims
+    uint32_t word = 0;
+    double sabs = 0.0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        word |= (y[e] < 0.0 ? 0u : 1u) << e;
+        sabs += fabs(y[e]);
+    }
+    if (32 * j >= p.c.sk) sabs = 0.0;  // dims past the sketch
+    sabs += quad_xor1(sabs);
+    sabs += quad_xor2(sabs);
+    sabs /= sqrt((double)kD);  // sum |k'| with k' = y / sqrt(D)
+    uint32_t *kr = key_rec(p.c, slot);
+    if (j < p.c.kw) kr[j] = word;  // the sketch's words
+    if (j == 0) kr[p.c.kw] = norm_corr_word(ss, sabs, p.c.sk);
 }
 
 // ---------------------------------------------------------------------------------------
