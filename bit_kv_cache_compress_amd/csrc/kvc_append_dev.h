@@ -46,13 +46,14 @@ __device__ __forceinline__ size_t slot_of(const AppendParams &p, long n)
 // nibble e mod 8 of word e / 8).  The quotient is first taken as (x - zf) * rcp(sf), within a
 // few ulp of the correctly rounded one; rint of the two can only differ when the approximation
 // lies within 2^-16 of a half-integer (an ulp near 16 is 2^-20), and then the elements take the
-// IEEE division.  x - zf is the binary32 difference either way.  Two codes are packed as one
-// float c_even + 16 c_odd (exact), converted to an integer once.
+// IEEE division.  x - zf is the binary32 difference either way.  Since |q - rint(q)| <= 1/2,
+// that test is max |q - rint(q)| >= 1/2 - 2^-16 over the elements, one compare in all.  Two
+// codes are packed as one float c_even + 16 c_odd (exact), converted to an integer once.
 template <int NE>
 __device__ __forceinline__ void value_codes(const float (&x)[NE], float zf, float sf, uint32_t (&w)[NE / 8])
 {
     const float r = __builtin_amdgcn_rcpf(sf);
-    bool near = false;
+    float dmax = 0.0f;
 #pragma unroll
     for (int q = 0; q < NE / 8; ++q) {
         uint32_t word = 0u;
@@ -60,13 +61,13 @@ __device__ __forceinline__ void value_codes(const float (&x)[NE], float zf, floa
         for (int e = 0; e < 8; e += 2) {
             const float q0 = (x[8 * q + e] - zf) * r, q1 = (x[8 * q + e + 1] - zf) * r;
             const float t0 = rintf(q0), t1 = rintf(q1);
-            near |= (fabsf(fabsf(q0 - t0) - 0.5f) <= 0x1p-16f) | (fabsf(fabsf(q1 - t1) - 0.5f) <= 0x1p-16f);
+            dmax = fmaxf(dmax, fmaxf(fabsf(q0 - t0), fabsf(q1 - t1)));
             const float pair = fmaf(16.0f, __builtin_amdgcn_fmed3f(t1, 0.0f, 15.0f), __builtin_amdgcn_fmed3f(t0, 0.0f, 15.0f));
             word |= (uint32_t)pair << (4 * e);
         }
         w[q] = word;
     }
-    if (near) {
+    if (dmax >= 0.5f - 0x1p-16f) {
 #pragma unroll
         for (int q = 0; q < NE / 8; ++q) {
             uint32_t word = 0u;
