@@ -661,8 +661,11 @@ def measured_traffic(kernel, workload):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "bit_kv_cache_compress_amd", "csrc", rec["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        srcs = rec["source"] if isinstance(rec["source"], list) else [rec["source"]]
+        h = hashlib.sha256()
+        for f in srcs:  # the kernel's file and the headers listed with it, in order
+            h.update(open(os.path.join(ROOT, "bit_kv_cache_compress_amd", "csrc", f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
             return None
         return rec["bytes_per_launch"]
     except Exception:

@@ -3,13 +3,14 @@
   python profsum.py stats RUN_kernel_stats.csv OUT.txt --command "..."
       per-kernel call count and duration table of a ``--kernel-trace --stats`` run
 
-  python profsum.py traffic --kernel K --workload W --source FILE
+  python profsum.py traffic --kernel K --workload W --source FILE[,FILE...]
          --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv --copy-mib N
          --out OUT.json [--command "..."]
       HBM bytes per launch of kernel K from two ``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE;
       KiB per dispatch), each scaled by what the same counter reads for a device copy of N
       MiB (which reads and writes exactly N MiB).  The JSON records the SHA-256 of the
-      kernel's source so that a reader can tell whether the kernel changed since.
+      kernel's source files (concatenated in the order given) so that a reader can tell
+      whether the kernel changed since.
 """
 from __future__ import annotations
 
@@ -72,10 +73,14 @@ def traffic(a) -> dict:
     kib = a.copy_mib * 1024.0
     fs, ws = kib / statistics.median(cfetch), kib / statistics.median(cwrite)
     f_kib, w_kib = statistics.mean(fetch), statistics.mean(write)
-    src = os.path.join(CSRC, a.source)
+    # one file, or several (the kernel's file and the headers it includes), hashed in order
+    srcs = a.source.split(",")
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     rec = {
-        "kernel": a.kernel, "workload": a.workload, "source": a.source,
-        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "kernel": a.kernel, "workload": a.workload, "source": srcs[0] if len(srcs) == 1 else srcs,
+        "source_sha256": h.hexdigest(),
         "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
         "dispatches": [len(fetch), len(write)],
         "copy_calibration": {"mib": a.copy_mib, "kernel": a.copy_kernel,
