@@ -1204,8 +1204,9 @@ __global__ __launch_bounds__(256) void k_sel_write(SelectParams p)
 template <int GB, int GV, int KW, bool PAGE64>
 __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 {
+    static_assert(GB == 1, "the vector-unit pass serves one query head per KV head");
     constexpr int NB = 64;        // tokens per batch
-    constexpr int VU = NB / 4;    // value tokens per 16-lane group and batch
+    constexpr int VU = NB / 16;   // value tokens per 4-lane group and batch
     constexpr int VREC = kD / 2 + 4 * (kD / GV);  // bytes of a value record
     __shared__ float wbuf[NB][GB];
     __shared__ uint32_t pbase[kMaxFullChunk / 16 + 1];
@@ -1237,19 +1238,22 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
     }
     __syncthreads();
 
-    const int sub = lane & 15;  // dims 8*sub .. 8*sub+7
-    const int eg = lane >> 4;   // value tokens eg + 4 u of a batch
-    const int grp = (8 * sub) / GV;
+    // values: 4 lanes per token, 32 dims each (one 16-byte load of codes and the group's
+    // scale/zero word), so that the per-token scale work is shared by 32 dims and a batch
+    // takes 8 value loads per lane
+    const int q4 = lane & 3;   // dims 32*q4 .. 32*q4+31
+    const int eg = lane >> 2;  // value tokens eg + 16 u of a batch
+    const int grp = (32 * q4) / GV;
     const uint32_t tmask = (1u << logP) - 1u;
-    const int vw = 4 * sub, vz = kD / 2 + 4 * grp;  // offsets of the lane's code and scale/zero words
-    float acc[GB][8], zacc[GB], lsum[GB], mrun[GB];
+    const int vw = 16 * q4, vz = kD / 2 + 4 * grp;  // offsets of the lane's codes and scale/zero word
+    float acc[GB][32], zacc[GB], lsum[GB], mrun[GB];
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
         zacc[h] = 0.0f;
         lsum[h] = 0.0f;
         mrun[h] = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] = 0.0f;
+        for (int j = 0; j < 32; ++j) acc[h][j] = 0.0f;
     }
 
     const float lazy = 8.0f / p.klog;  // score units of a factor 2^8 in weight
@@ -1259,7 +1263,8 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         // those past nb)
         uint4 kb;
         uint32_t nc;
-        uint32_t cw[VU], szw[VU];
+        uint4 cw[VU];
+        uint32_t szw[VU];
         if constexpr (PAGE64) {
             // pages of 64 tokens or more hold a whole batch: consecutive slots, one address per
             // lane and fixed offsets; slots past the sequence's end get no weight, and their
@@ -1268,17 +1273,15 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
             const uint32_t s0 = pbase[(first >> logP) - p0] + (first & tmask);
             load_key_t<KW>(p.c, s0 + lane, kb, nc);
             const uint8_t *vr = p.c.vals + (size_t)(s0 + eg) * VREC;
-            const uint32_t *cwp = reinterpret_cast<const uint32_t *>(vr + vw);
-            const uint32_t *szp = reinterpret_cast<const uint32_t *>(vr + vz);
 #pragma unroll
-            for (int u = 0; u < VU; ++u) {
-                cw[u] = cwp[u * VREC];  // 4 tokens further per u
-                szw[u] = szp[u * VREC];
+            for (int u = 0; u < VU; ++u) {  // 16 tokens further per u
+                __builtin_memcpy(&cw[u], vr + (size_t)u * 16 * VREC + vw, 16);  // 8-byte aligned when Gv = 64
+                szw[u] = *reinterpret_cast<const uint32_t *>(vr + (size_t)u * 16 * VREC + vz);
             }
             if (nb < NB) {  // uniform: the sequence's last batch
 #pragma unroll
                 for (int u = 0; u < VU; ++u)
-                    if (eg + 4 * u >= nb) szw[u] = 0u;
+                    if (eg + 16 * u >= nb) szw[u] = 0u;
             }
         } else {
             {
@@ -1287,9 +1290,9 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
             }
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
-                const uint32_t t = (uint32_t)(t0 + bs + min(eg + 4 * u, nb - 1));
+                const uint32_t t = (uint32_t)(t0 + bs + min(eg + 16 * u, nb - 1));
                 const uint8_t *vr = p.c.vals + (size_t)(pbase[(t >> logP) - p0] + (t & tmask)) * VREC;
-                cw[u] = *reinterpret_cast<const uint32_t *>(vr + vw);
+                __builtin_memcpy(&cw[u], vr + vw, 16);
                 szw[u] = *reinterpret_cast<const uint32_t *>(vr + vz);
             }
         }
@@ -1310,7 +1313,7 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
                 zacc[h] *= scale;
                 lsum[h] *= scale;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] *= scale;
+                for (int j = 0; j < 32; ++j) acc[h][j] *= scale;
                 mrun[h] = mnew;
             }
             const float w = (mrun[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s[h] - mrun[h]) * p.klog);
@@ -1320,38 +1323,44 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
-            const int e = eg + 4 * u;  // weight 0 past nb
+            const int e = eg + 16 * u;  // weight 0 past nb
             const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
             const float zf = half_bits_to_float(szw[u] >> 16);
-            float c[8];
-            unpack_codes(cw[u], c);
+            const uint32_t cwk[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
             for (int h = 0; h < GB; ++h) {
                 const float w = wbuf[e][h];
                 const float ws = w * sf;
                 zacc[h] = fmaf(w, zf, zacc[h]);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(ws, c[j], acc[h][j]);
+                for (int k = 0; k < 4; ++k) {  // word k: dims 32 q4 + 8k .. + 7
+                    float c[8];
+                    unpack_codes(cwk[k], c);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[h][8 * k + j] = fmaf(ws, c[j], acc[h][8 * k + j]);
+                }
             }
         }
         __syncthreads();  // wbuf is rewritten by the next batch
     }
 
-    // ---- weight sums, then the value sums over the 4 token groups (lanes sub, sub + 16, ...)
+    // ---- weight sums, then the value sums over the 16 token groups (lanes q4, q4 + 4, ...)
     const size_t pidx = (size_t)bh0 * g.NCA + chunk;  // partial of head bh0 (+ h * NCA)
 #pragma unroll
     for (int h = 0; h < GB; ++h) {
         const float l = wave_sum(lsum[h]);
 #pragma unroll
-        for (int o = 16; o < 64; o <<= 1) {
-            zacc[h] += __shfl_xor(zacc[h], o);
+        for (int o = 4; o < 64; o <<= 1) {
+            zacc[h] += xor_lane(zacc[h], o);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] += __shfl_xor(acc[h][j], o);
+            for (int j = 0; j < 32; ++j) acc[h][j] += xor_lane(acc[h][j], o);
         }
-        if (lane < 16) {
-            float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + 8 * lane);
-            dst[0] = make_float4(acc[h][0] + zacc[h], acc[h][1] + zacc[h], acc[h][2] + zacc[h], acc[h][3] + zacc[h]);
-            dst[1] = make_float4(acc[h][4] + zacc[h], acc[h][5] + zacc[h], acc[h][6] + zacc[h], acc[h][7] + zacc[h]);
+        if (lane < 4) {
+            float4 *dst = reinterpret_cast<float4 *>(p.po + (pidx + (size_t)h * g.NCA) * kD + 32 * lane);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                dst[k] = make_float4(acc[h][4 * k] + zacc[h], acc[h][4 * k + 1] + zacc[h], acc[h][4 * k + 2] + zacc[h],
+                                     acc[h][4 * k + 3] + zacc[h]);
         }
         if (lane == 0) {
             p.pm[pidx + (size_t)h * g.NCA] = mrun[h];
