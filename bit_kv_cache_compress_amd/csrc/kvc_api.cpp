@@ -58,11 +58,13 @@ int chunk_cap(bool topp)
 
 // Geometry.
 //  Full softmax: chunks of CH tokens, the largest power of two in [64, 2048] that still
-//  gives at least 4096 waves (16 per compute unit) over (chunk, KV-head group, sequence)
-//  and no more than kMaxChunks chunks; one attention wave per chunk (KA = 1).
+//  gives at least 4096 waves (16 per compute unit) over (chunk, KV-head group, sequence),
+//  and at most 512 when each KV head has one query head (GB = 1: the vector-unit pass for
+//  64-dim value groups, whose waves then carry at most 8 batches), as long as no more than
+//  kMaxChunks chunks result; one attention wave per chunk (KA = 1).
 //  Top-p: score chunks of 512 tokens (one wave, 8 tokens per lane); an attention wave
 //  (one query head: Top-p keeps a few, head-specific tokens) covers KA = 2 score chunks.
-void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, bool topp)
+void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, bool topp, int GB)
 {
     int CH, KA = 1;
     if (topp) {
@@ -71,7 +73,9 @@ void plan_geometry(Plan &pl, int B, int rows_per_seq, int max_len, bool topp)
     } else {
         CH = chunk_cap(false);
         const long units = (long)B * rows_per_seq;
-        while (CH > 64 && units * ((max_len + CH - 1) / CH) < 4096 && (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
+        const int cap = GB == 1 ? 512 : CH;
+        while (CH > 64 && (CH > cap || units * ((max_len + CH - 1) / CH) < 4096) &&
+               (long)(CH >> 1) * kvc::kMaxChunks >= max_len)
             CH >>= 1;
     }
     pl.g.CH = CH;
@@ -167,7 +171,7 @@ void make_plan(Plan &pl, int B, int Hq, int Hkv, int max_seq_len, float top_p)
     pl.g.G = G;
     pl.g.GB = GB;
     pl.g.nsub = G / GB;
-    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, pl.topp);
+    plan_geometry(pl, B, Hkv * pl.g.nsub, max_seq_len, pl.topp, GB);
     plan_layout(pl, B * Hq);
 }
 
@@ -776,7 +780,7 @@ size_t kv_topp_workspace_bytes(int32_t B, int32_t Hq, int32_t ld)
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, true);
+    plan_geometry(pl, B, Hq, ld, true, 1);
     plan_layout(pl, B * Hq);
     return pl.total;
 }
@@ -804,7 +808,7 @@ int kv_topp_select(const float *scores, int32_t ld, const int32_t *seq_lens, int
     pl.g.Hq = Hq;
     pl.g.Hkv = Hq;
     pl.g.G = pl.g.GB = pl.g.nsub = 1;
-    plan_geometry(pl, B, Hq, ld, true);
+    plan_geometry(pl, B, Hq, ld, true, 1);
     plan_layout(pl, B * Hq);
     pl.g.seq_lens = seq_lens;
     pl.g.page_table = nullptr;
