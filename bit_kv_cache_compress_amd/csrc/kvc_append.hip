@@ -148,10 +148,11 @@ __global__ __launch_bounds__(128) void k_append_dense(AppendParams p, long N)
 // per wave, k' = R k as v_mfma_f32_16x16x32_f16 with the keys as A (16 tokens x 128 dims) and
 // the rotation as B (B[j][o] = R[o][j]).  Binary16 products are exact in binary32, so the only
 // error of an output is that of its binary32 sums: at most gamma_128 = 128 u / (1 - 128 u)
-// < 7.7e-6 (u = 2^-24) times sum_j |R_oj k_j|, whatever order the matrix core adds in.  A
-// coordinate whose |k'_o| exceeds 1e-5 times that sum (the product of |R| and |k|, a second
-// MFMA chain on the magnitudes) has the sign of the exact product; the others (rare) take the
-// exact sign from a binary64 sum of the 128 products over the wave's lanes.
+// < 7.7e-6 (u = 2^-24) times sum_j |R_oj k_j|, whatever order the matrix core adds in, and by
+// Cauchy-Schwarz that sum is at most |R_o| |k| (Euclidean norms: of the row, computed once per
+// block in binary64, and of the key, from its binary64 |k|^2).  A coordinate whose |k'_o|
+// exceeds 1e-5 |R_o| |k| has the sign of the exact product; the others (rare) take the exact
+// sign from a binary64 sum of the 128 products over the wave's lanes.
 // The token-heads are taken head by head (n = (b Hkv + h) n_new + t), so that a wave's 16
 // records are consecutive slots of a page, written whole.  sum |k'| (for the correction) is
 // the binary32 sum of the matrix-core outputs, within 1e-5 relative of the binary64 one.
@@ -195,23 +196,36 @@ __device__ __forceinline__ void token_at(const AppendParams &p, uint32_t n, size
     slot = ((size_t)page * p.c.Hkv + h) * p.c.P + (pos & (p.c.P - 1));
 }
 
-__global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
+__global__ __launch_bounds__(256, 4) void k_append_mfma(AppendParams p, int N)
 {
     __shared__ __align__(16) uint16_t Bt[kD * kBS];  // Bt[o][j] = B[j][o]
     __shared__ uint64_t sgn_s[4][32];                // per wave: sign ballots [4 nt + i]
     __shared__ uint64_t unc_s[4][32];                // per wave: uncertain ballots
     __shared__ float sab_s[4][16];                   // per wave: sum |k'| of the tile's tokens
     __shared__ double ss_s[4][16];                   // per wave: |k|^2 of the tile's tokens
+    __shared__ float rn_s[kD];                       // |R_o|, rounded up
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int c = tid; c < kD * kD / 8; c += 256) {
         const int o = c >> 4, q = c & 15;  // row o, halves 8 q .. 8 q + 7
         *reinterpret_cast<uint4 *>(&Bt[o * kBS + 8 * q]) = reinterpret_cast<const uint4 *>(p.rot)[c];
     }
     __syncthreads();
+    if (tid < kD) {
+        double r2 = 0.0;
+        for (int j = 0; j < kD; ++j) {
+            const double r = (double)half_bits_to_float(Bt[tid * kBS + j]);
+            r2 = fma(r, r, r2);
+        }
+        rn_s[tid] = (float)(sqrt(r2) * (1.0 + 0x1p-20));
+    }
+    __syncthreads();
     const uint16_t *K = reinterpret_cast<const uint16_t *>(p.k);
     const uint16_t *V = reinterpret_cast<const uint16_t *>(p.v);
     const int m = lane & 15, kb = lane >> 4;  // A layout: token m, dims 8 kb + 32 ks
     const int tv = lane >> 2, jv = lane & 3;  // value layout: token tv, dims 32 jv .. + 31
+    float rb[8];  // 1e-5 |R_o| of out dims o = 16 nt + m
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) rb[nt] = 1e-5f * rn_s[16 * nt + m];
     const uint32_t ntiles = ((uint32_t)N + 15u) / 16u;
     for (uint32_t tile = blockIdx.x * 4u + (uint32_t)wave; tile < ntiles; tile += gridDim.x * 4u) {
         const int nvalid = min(16, N - (int)(tile * 16u));
@@ -242,19 +256,18 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
         ss += xor_lane_d(ss, 16);
         ss += xor_lane_d(ss, 32);
         if (kb == 0) ss_s[wave][m] = ss;
-        // the products: acc[nt] holds out dim 16 nt + m of tokens 4 kb + i in element i
-        // (and in aab[nt] the bound's sum of |R_oj k_j|)
-        f32x4_t acc[8], aab[8];
+        // |k| of tokens 4 kb + i (the bound's key factor), from lanes 4 kb + i
+        float kn[4];
+        {
+            const float knm = sqrtf((float)ss);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            acc[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
-            aab[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+            for (int i = 0; i < 4; ++i)
+                kn[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * kb + i) << 2, __float_as_int(knm)));
         }
-        uint4 aabs[4];
+        // the products: acc[nt] holds out dim 16 nt + m of tokens 4 kb + i in element i
+        f32x4_t acc[8];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            aabs[ks] = make_uint4(a[ks].x & 0x7FFF7FFFu, a[ks].y & 0x7FFF7FFFu, a[ks].z & 0x7FFF7FFFu,
-                                  a[ks].w & 0x7FFF7FFFu);
+        for (int nt = 0; nt < 8; ++nt) acc[nt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             uint4 bw[4];
@@ -262,12 +275,8 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
             for (int ks = 0; ks < 4; ++ks)
                 bw[ks] = *reinterpret_cast<const uint4 *>(&Bt[(16 * nt + m) * kBS + 32 * ks + 8 * kb]);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 4; ++ks)
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a[ks]), as_half8(bw[ks]), acc[nt], 0, 0, 0);
-                const uint4 babs = make_uint4(bw[ks].x & 0x7FFF7FFFu, bw[ks].y & 0x7FFF7FFFu,
-                                              bw[ks].z & 0x7FFF7FFFu, bw[ks].w & 0x7FFF7FFFu);
-                aab[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(aabs[ks]), as_half8(babs), aab[nt], 0, 0, 0);
-            }
             __builtin_amdgcn_sched_barrier(0);  // one output tile's operands at a time
         }
         // signs, certified against the bound; sum |k'| over the sketch's dims
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(256) void k_append_mfma(AppendParams p, int N)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float v = acc[nt][i];
-                const float b = 1e-5f * aab[nt][i];
+                const float b = rb[nt] * kn[i];  // >= 1e-5 sum_j |R_oj k_j|
                 const uint64_t sg = __builtin_amdgcn_ballot_w64(!(v < 0.0f));
                 const uint64_t un = __builtin_amdgcn_ballot_w64(!(fabsf(v) > b));
                 const bool mine = lane == 4 * nt + i;
