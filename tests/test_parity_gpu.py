@@ -73,6 +73,44 @@ def test_append_parity(name):
     _say(f"[append] {name} ok {stats}")
 
 
+def test_dense_append_certified_signs():
+    """The dense rotation on the matrix cores (more than 8192 binary16 token-heads) with keys
+    built so that many rotated coordinates sit at or near zero, where the binary32 sums cannot
+    certify a sign and the binary64 sum decides: zero keys (every coordinate uncertain, each
+    sign +1), one-hot keys (k' is a column of R), the columns of R themselves (k' = R R^T e_i,
+    which is e_i up to the binary16 rounding of R) and their negatives, beside random keys.
+    Every record against the oracle's encoding (sign bits exact outside the 2^-40 band)."""
+    wl = W.CONFIGS[2].scaled(B=1, Hq=8, Hkv=8, P=256)
+    c = Case(wl, L=2048)  # 16384 token-heads: the matrix-core append
+    assert c.rot_kind == "dense"
+    R = c.rot_raw.astype(np.float16)
+    K = c.K
+    for t in range(c.L):
+        for h in range(wl.Hkv):
+            kind, i = (t + h) % 5, (7 * t + 3 * h) % wl.D
+            if kind == 0:
+                K[0, t, h] = 0.0
+            elif kind == 1:
+                K[0, t, h] = 0.0
+                K[0, t, h, i] = np.float16(1.5 + (t % 7))
+            elif kind == 2:
+                K[0, t, h] = R[:, i]
+            elif kind == 3:
+                K[0, t, h] = -R[:, i]
+    c.ocache = c.oracle_cache()
+    g = gpu_append(c)
+    d = download(g)
+    stats = compare_caches(d, c.ocache, c)
+    # zero keys exactly: every sign +1 (a zero counts as positive), norm 0, correction 1
+    for t in range(c.L):
+        for h in range(wl.Hkv):
+            if (t + h) % 5 == 0:
+                pg, sl = c.pt[0, t // wl.P], t % wl.P
+                assert np.all(d["key_bits"][pg, h, sl] == 0xFFFFFFFF), (t, h)
+                assert int(d["key_nc"][pg, h, sl]) == 0x3C000000, (t, h, hex(int(d["key_nc"][pg, h, sl])))
+    _say(f"[append] certified signs ok {stats}")
+
+
 def _decode_with_debug(c, cache, top_p, scores=True, proxy=False, dist=True):
     """Decode with debug outputs; scores=False runs the kernels of a decode without debug
     output (the per-token scores are not written) and still returns the Top-p sets and what
