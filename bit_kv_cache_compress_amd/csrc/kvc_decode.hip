@@ -1330,12 +1330,12 @@ __global__ __launch_bounds__(64) void k_attend_full(AttendParams p)
 #pragma unroll
             for (int h = 0; h < GB; ++h) {
                 const float w = wbuf[e][h];
-                const float ws = w * sf;
+                const float ws = w * sf * kCodeUnscale;  // exact: by 2^9
                 zacc[h] = fmaf(w, zf, zacc[h]);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {  // word k: dims 32 q4 + 8k .. + 7
                     float c[8];
-                    unpack_codes(cwk[k], c);
+                    unpack_codes_e4m3(cwk[k], c);  // c * 2^-9
 #pragma unroll
                     for (int j = 0; j < 8; ++j) acc[h][8 * k + j] = fmaf(ws, c[j], acc[h][8 * k + j]);
                 }
@@ -2180,14 +2180,14 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
                     else we = wbuf[eg + 16 * u];
                     const float sf = half_bits_to_float(szw[u] & 0xFFFFu);
                     const float zf = half_bits_to_float(szw[u] >> 16);
-                    const float ws = we * sf;
+                    const float ws = we * sf * kCodeUnscale;  // exact: by 2^9
                     zacc = fmaf(we, zf, zacc);
                     const uint32_t cwk[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
     #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         // word k holds dims 32 q4 + 8k .. + 7
                         float c[8];
-                        unpack_codes(cwk[k], c);
+                        unpack_codes_e4m3(cwk[k], c);  // c * 2^-9
     #pragma unroll
                         for (int j = 0; j < 8; ++j) acc[8 * k + j] = fmaf(ws, c[j], acc[8 * k + j]);
                     }
@@ -2249,14 +2249,14 @@ __global__ __launch_bounds__(64 * kAttendWaves, EXACT ? 1 : 4) void k_attend_top
                     const float we = wbuf[eg + 16 * u];  // 0 past nb
                     const float sf = half_bits_to_float(G.szw[u] & 0xFFFFu);
                     const float zf = half_bits_to_float(G.szw[u] >> 16);
-                    const float ws = we * sf;
+                    const float ws = we * sf * kCodeUnscale;  // exact: by 2^9
                     zacc = fmaf(we, zf, zacc);
                     const uint32_t cwk[4] = {G.cw[u].x, G.cw[u].y, G.cw[u].z, G.cw[u].w};
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         // word k holds dims 32 q4 + 8k .. + 7
                         float c[8];
-                        unpack_codes(cwk[k], c);
+                        unpack_codes_e4m3(cwk[k], c);  // c * 2^-9
 #pragma unroll
                         for (int j = 0; j < 8; ++j) acc[8 * k + j] = fmaf(ws, c[j], acc[8 * k + j]);
                     }

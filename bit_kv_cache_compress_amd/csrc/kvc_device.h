@@ -109,6 +109,28 @@ __device__ __forceinline__ float ubyte_to_float(uint32_t x)
     return f;
 }
 
+// The 8 codes of a code word as c * 2^-9, two per instruction: a byte holding a code c < 16,
+// read as an OCP E4M3 number (gfx950's fp8), is exactly c * 2^-9 (a subnormal for c < 8, the
+// exponent's lowest normal binade for c >= 8), so v_cvt_pk_f32_fp8 converts two codes at once.
+// A caller multiplies its weight by 2^9 (exact): w 2^9 * c 2^-9 rounds as w * c does.
+constexpr float kCodeUnscale = 512.0f;
+__device__ __forceinline__ void unpack_codes_e4m3(uint32_t w, float c[8])
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // dims 0,2,4,6 / 1,3,5,7
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);  // bytes 0, 1: dims 0, 2
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);   // bytes 2, 3: dims 4, 6
+    const auto x = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);  // dims 1, 3
+    const auto y = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);   // dims 5, 7
+    c[0] = a[0];
+    c[1] = x[0];
+    c[2] = a[1];
+    c[3] = x[1];
+    c[4] = b[0];
+    c[5] = y[0];
+    c[6] = b[1];
+    c[7] = y[1];
+}
+
 // The 8 codes of a 32-bit code word (dims 2m in the low, 2m+1 in the high nibble of byte m)
 // as floats, c[0..7] in dim order.
 __device__ __forceinline__ void unpack_codes(uint32_t w, float c[8])
