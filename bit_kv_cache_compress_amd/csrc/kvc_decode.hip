@@ -2406,14 +2406,15 @@ __device__ __forceinline__ void mass_finish(const MassParams &p, int b, int h, i
 // Thread (d, slice) sums the chunks c = slice (mod 8) for dim d; a chunk of zero weight (no
 // attended token, or an empty partial of a Top-p span) adds nothing, and its value sums are
 // not read.  The value sums of the
-// first 256 chunks are loaded first, so that their reads overlap the max and weight
+// first 8 PF chunks are loaded first, so that their reads overlap the max and weight
 // reductions.
 // ---------------------------------------------------------------------------------------
-template <bool MASS>
+// PF: chunks per thread loaded ahead, at most what the plan's NCA chunks give a thread (8
+// slices), so that no load is spent on a slot past the last; fewer beside the mass prefetch.
+template <bool MASS, int PF>
 __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
 {
     constexpr int kT = 1024, NS = kT / kD;  // threads, chunk slices
-    constexpr int PF = MASS ? 16 : 32;      // chunks per thread loaded ahead (fewer beside the mass prefetch)
     __shared__ float alpha[kMaxChunks];
     __shared__ float redf[2][kT / 64];
     __shared__ float part[NS][kD];
@@ -2744,8 +2745,16 @@ hipError_t launch_check(const CheckParams &p, int32_t *flag_host, hipStream_t s)
 
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)
 {
-    if (p.has_mass) KVC_LAUNCH(k_merge<true>, dim3(p.g.Hq, p.g.B), dim3(1024), s, p);
-    else KVC_LAUNCH(k_merge<false>, dim3(p.g.Hq, p.g.B), dim3(1024), s, p);
+    const dim3 grid(p.g.Hq, p.g.B);
+    const int per = (p.g.NCA + 7) / 8;  // chunks per thread (8 slices of 128 dims)
+    if (p.has_mass) {
+        if (per <= 8) KVC_LAUNCH((k_merge<true, 8>), grid, dim3(1024), s, p);
+        else KVC_LAUNCH((k_merge<true, 16>), grid, dim3(1024), s, p);
+    } else {
+        if (per <= 8) KVC_LAUNCH((k_merge<false, 8>), grid, dim3(1024), s, p);
+        else if (per <= 16) KVC_LAUNCH((k_merge<false, 16>), grid, dim3(1024), s, p);
+        else KVC_LAUNCH((k_merge<false, 32>), grid, dim3(1024), s, p);
+    }
     return hipGetLastError();
 }
 
