@@ -250,20 +250,30 @@ __device__ __forceinline__ void tail_attend(const TailParams &p, int bh)
 //   caller's uniform U under stochastic rounding; the codes in dot8 order; c0 = v_l/sqrt(sk),
 //   c1 = delta/sqrt(sk).
 // ---------------------------------------------------------------------------------------
+// EXTRA: the blocks the launch carries past the query heads' -- 0 none, 1 the binary16 tail
+// and any appends, 2 randomized-Hadamard appends only, 3 dense appends only -- so that a
+// launch compiles in (and holds registers for) only the paths it runs.
+template <int EXTRA>
 __global__ __launch_bounds__(256) void k_qprep(QprepParams p, float isd)
 {
     __shared__ float xs[kD];
     __shared__ int us[kD];
     __shared__ float redf[4];
     __shared__ int redi[4];
-    if ((int)blockIdx.x >= p.BH) {
+    if (EXTRA != 0 && (int)blockIdx.x >= p.BH) {
         const long tb = p.has_tail ? p.BH : 0;  // tail blocks
         const long ab = (long)blockIdx.x - p.BH - tb;
-        if (ab < 0) {
-            tail_attend(p.tail, (int)blockIdx.x - p.BH);
-        } else if (p.app.rot_kind == 1) {
+        if constexpr (EXTRA == 1) {
+            if (ab < 0) {
+                tail_attend(p.tail, (int)blockIdx.x - p.BH);
+            } else if (p.app.rot_kind == 1) {
+                append_hadamard_block(p.app, p.app_N, ab);
+            } else {
+                append_small_block(p.app, p.app_N, ab);
+            }
+        } else if constexpr (EXTRA == 2) {
             append_hadamard_block(p.app, p.app_N, ab);
-        } else {
+        } else if constexpr (EXTRA == 3) {
             append_small_block(p.app, p.app_N, ab);
         }
         return;
@@ -2586,7 +2596,11 @@ hipError_t launch_qprep(const QprepParams &p, hipStream_t s)
     const float isd = (float)(1.0 / sqrt((double)kD));
     const long blocks = (long)p.BH * (p.has_tail ? 2 : 1) + p.app_blocks;
     const bool wide = p.has_tail || p.app_blocks > 0;
-    KVC_LAUNCH(k_qprep, dim3((unsigned)blocks), dim3(wide ? 256 : 128), s, p, isd);
+    const dim3 grid((unsigned)blocks), blk(wide ? 256 : 128);
+    if (p.has_tail) KVC_LAUNCH(k_qprep<1>, grid, blk, s, p, isd);
+    else if (p.app_blocks > 0 && p.app.rot_kind == 1) KVC_LAUNCH(k_qprep<2>, grid, blk, s, p, isd);
+    else if (p.app_blocks > 0) KVC_LAUNCH(k_qprep<3>, grid, blk, s, p, isd);
+    else KVC_LAUNCH(k_qprep<0>, grid, blk, s, p, isd);
     return hipGetLastError();
 }
 
