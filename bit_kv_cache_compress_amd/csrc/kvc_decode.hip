@@ -2419,7 +2419,7 @@ __device__ __forceinline__ void mass_finish(const MassParams &p, int b, int h, i
 // first 8 PF chunks are loaded first, so that their reads overlap the max and weight
 // reductions.
 // ---------------------------------------------------------------------------------------
-// PF: chunks per thread loaded ahead, at most what the plan's NCA chunks give a thread (8
+// PF: chunks per thread loaded ahead, no more than the plan's NCA chunks give a thread (8
 // slices), so that no load is spent on a slot past the last; fewer beside the mass prefetch.
 template <bool MASS, int PF>
 __global__ __launch_bounds__(1024) void k_merge(MergeParams p)
@@ -2760,13 +2760,15 @@ hipError_t launch_check(const CheckParams &p, int32_t *flag_host, hipStream_t s)
 hipError_t launch_merge(const MergeParams &p, hipStream_t s)
 {
     const dim3 grid(p.g.Hq, p.g.B);
-    const int per = (p.g.NCA + 7) / 8;  // chunks per thread (8 slices of 128 dims)
+    // chunks per thread (8 slices of 128 dims); up to 16 of them, 8 loaded ahead and the rest
+    // after the weights are known (Top-p partials of spans are often empty and then skipped)
+    const int per = (p.g.NCA + 7) / 8;
     if (p.has_mass) {
-        if (per <= 8) KVC_LAUNCH((k_merge<true, 8>), grid, dim3(1024), s, p);
+        if (per <= 16) KVC_LAUNCH((k_merge<true, 8>), grid, dim3(1024), s, p);
         else KVC_LAUNCH((k_merge<true, 16>), grid, dim3(1024), s, p);
     } else {
-        if (per <= 8) KVC_LAUNCH((k_merge<false, 8>), grid, dim3(1024), s, p);
-        else if (per <= 16) KVC_LAUNCH((k_merge<false, 16>), grid, dim3(1024), s, p);
+        if (per <= 16) KVC_LAUNCH((k_merge<false, 8>), grid, dim3(1024), s, p);
+        else if (per <= 32) KVC_LAUNCH((k_merge<false, 16>), grid, dim3(1024), s, p);
         else KVC_LAUNCH((k_merge<false, 32>), grid, dim3(1024), s, p);
     }
     return hipGetLastError();
